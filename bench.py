@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Batch-1 greedy decode through the Qwen3.5-4B-shaped int8 hybrid stack on one MI355X.
+
+One step = one token through the whole path: 32 layers (24 GDN, 8 gated full
+attention over a bf16 KV cache at ~8192 tokens), final RMSNorm, int8 lm_head over
+248 320 tokens, greedy argmax and the next token's embedding, all on the device
+from one replayed HIP graph.  Prints one JSON line (rank 0).
+
+    python bench.py [--gpus 1] [--steps 128] [--warmup 8]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "batch-1 decode tok/s + achieved HBM GB/s, Qwen3.5-4B-shaped int8 layers"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def stack_bytes_per_token(cfg, st, kinds, seq_len: int) -> int:
+    """Algorithmic HBM bytes of one token at attention length seq_len: every weight
+    byte (codes, scales, biases) once, GDN and conv state read + write, conv
+    weights, KV rows [0, seq_len) read plus one row appended per full layer,
+    the lm_head, the embedding row, norm weights and the residual stream."""
+    b = st.weight_bytes
+    H = cfg.hidden
+    for li, kind in enumerate(kinds):
+        b += 2 * H * 2 * 2                                   # input_ln + post_ln, residual in/out
+        if kind == "gdn":
+            b += 2 * cfg.num_v_heads_lin * cfg.k_head_dim_lin * cfg.v_head_dim_lin * 4
+            b += 2 * cfg.qkv_total_lin * cfg.conv_kernel_size * 4
+            b += cfg.qkv_total_lin * cfg.conv_kernel_size * 2
+        else:
+            b += seq_len * cfg.kv_dim * 2 * 2                    # K and V rows read
+            b += cfg.kv_dim * 2 * 2                              # append
+    b += H * 2 * 2                                           # final norm + embedding row
+    return b
+
+
+def gate_up_bytes(cfg) -> int:
+    """Bytes one gate/up launch must move: both matrices (codes + bf16 scales and
+    biases), the fp32 residual and norm weight in, the fp32 product out."""
+    w = 2 * cfg.intermediate * cfg.hidden * (1 + 4 / 64)
+    return int(w + cfg.hidden * (4 + 2) + cfg.intermediate * 4)
+
+
+def cpu_baseline(cfg, w, sample_note):
+    import numpy as np
+
+    import oracle as O
+    from synth import gdn_state
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    kinds = w["kinds"]
+    gi = kinds.index("gdn")
+    fi = kinds.index("full")
+    x = w["embed"][w["start_token"]]
+    inv = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
+    t0 = time.perf_counter()
+    O.forward_linear_attention(cfg, w["layers"][gi], w["states"][gi], x)
+    t_gdn = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.forward_full_attention(cfg, w["layers"][fi], w["kvs"][fi], inv, x, w["ctx"])
+    t_full = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    logits = O.lm_head_logits(cfg, w["final_norm"], w["lm_head"], O.act_to_f64(x, "bf16"))
+    O.greedy(logits)
+    t_lm = time.perf_counter() - t0
+    n_gdn, n_full = kinds.count("gdn"), kinds.count("full")
+    t_tok = n_gdn * t_gdn + n_full * t_full + t_lm
+    return {"value": 1.0 / t_tok, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample_note.format(gdn=t_gdn, full=t_full, lm=t_lm, ng=n_gdn, nf=n_full),
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--ctx", type=int, default=8192)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dominant-rounds", type=int, default=4)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the decode path here is single-device "
+              f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from synth import workloads
+    from hybrid_decode_amd import build as hb
+    if hb.is_stale():
+        hb.build()
+    from hybrid_decode_amd import binding as B
+    from hybrid_decode_amd import runtime as rt
+
+    torch.cuda.set_device(0)
+    rt.kernels(0)
+    K, W = args.steps, args.warmup
+    t0 = time.time()
+    gen = synth.Gen(0)
+    log(f"generating the {args.layers}-layer stack (ctx {args.ctx})")
+    w = workloads.stack_4b(gen, num_layers=args.layers, ctx=args.ctx, extra=W + K + 64,
+                           progress=lambda i: log(f"  layer {i} generated") if i % 8 == 7 else None)
+    cfg, kinds = w["cfg"], w["kinds"]
+    log(f"generated in {time.time() - t0:.1f}s; uploading")
+    st = rt.DecodeStack(cfg, kinds, w["layers"], w["states"], w["kvs"], w["embed"],
+                        w["final_norm"], w["lm_head"], start_pos=args.ctx,
+                        start_token=w["start_token"], history_len=W + K + 8)
+    torch.cuda.synchronize()
+    log(f"resident weights {st.weight_bytes / 1e9:.3f} GB")
+
+    # one decode token captured once, replayed every step
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st.step(write_logits=False)
+    log("graph captured")
+    for _ in range(W):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / K
+    tok_s = K / (ms / 1e3)
+    L_mid = args.ctx + W + K // 2 + 1
+    bpt = stack_bytes_per_token(cfg, st, kinds, L_mid)
+    hist = st.history.cpu().numpy()[:W + K]
+    assert np.all(hist >= 0) and np.all(hist < cfg.vocab), "decode produced invalid tokens"
+    log(f"{K} tokens in {ms:.2f} ms: {ms_per_step * 1e3:.1f} us/token, {tok_s:.1f} tok/s, "
+        f"{bpt * tok_s / 1e9:.0f} GB/s")
+
+    # per-layer device time for one eager token (launches queued behind a spin so
+    # the host never starves the device)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(kinds) + 2)]
+    torch.cuda._sleep(200_000_000)
+    s = rt.stream_ptr()
+    x = st.x_embed.data_ptr()
+    evs[0].record()
+    for li, kind in enumerate(kinds):
+        if kind == "gdn":
+            x = B.q35_forward_linear_attention(st.k, st.c, st.layers[li].struct, st.states[li].struct,
+                                               st.gdn_scratch.struct, x, st.x_main.data_ptr(), s)
+        else:
+            x = B.q35_forward_full_attention_devpos(st.k, st.c, st.layers[li].struct,
+                                                    st.full_scratch.struct, st.kvs[li].struct,
+                                                    st.inv_freq.data_ptr(), st.positions.data_ptr(), x, s)
+        evs[li + 1].record()
+    B.q35_lm_head_argmax(st.k, st.c, st.final_norm.data_ptr(), st.lm_head.struct, x, None,
+                         st.lm_ws.data_ptr(), st.lm_ws.numel(), st.tokens.data_ptr(),
+                         st.positions.data_ptr(), None, 0, 0, st.embed.data_ptr(),
+                         st.x_embed.data_ptr(), s)
+    evs[-1].record()
+    torch.cuda.synchronize()
+    lay = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(len(kinds))]
+    gdn_us = float(np.mean([t for t, k in zip(lay, kinds) if k == "gdn"]))
+    full_us = float(np.mean([t for t, k in zip(lay, kinds) if k == "full"]))
+    lm_us = evs[-2].elapsed_time(evs[-1]) * 1e3
+    log(f"eager token: GDN layer {gdn_us:.1f} us, full layer {full_us:.1f} us, lm_head {lm_us:.1f} us")
+
+    # dominant kernel: the post-norm + gate/up SwiGLU GEMV, every layer's weights in
+    # turn (distinct addresses: nothing is served from the 256 MB last-level cache)
+    x_resid = torch.randn(cfg.hidden, dtype=torch.float32, device="cuda")
+    mlp = torch.empty(cfg.intermediate, dtype=torch.float32, device="cuda")
+    layers = st.layers
+    R = args.dominant_rounds
+    torch.cuda._sleep(100_000_000)
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for _ in range(R):
+        for L in layers:
+            B.q35_gate_up_swiglu(st.k, st.c, L.t["post_ln"].data_ptr(), L.q["gate_proj"].struct,
+                                 L.q["up_proj"].struct, x_resid.data_ptr(), mlp.data_ptr(), s)
+    d1.record()
+    torch.cuda.synchronize()
+    dom_us = d0.elapsed_time(d1) * 1e3 / (R * len(layers))
+    dom_bytes = gate_up_bytes(cfg)
+    dom_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
+    log(f"gate/up GEMV: {dom_us:.2f} us/launch, {dom_gbs:.0f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"Qwen3.5-4B-shaped {args.layers}-layer hybrid stack "
+                         f"({kinds.count('gdn')} GDN + {kinds.count('full')} gated full attention), "
+                         f"int8 g64 weights, bf16 activations and KV cache, int8 lm_head over "
+                         f"{cfg.vocab}, greedy decode from cache position {args.ctx}"),
+            "layers": args.layers, "ctx_start": args.ctx, "hidden": cfg.hidden,
+            "intermediate": cfg.intermediate, "vocab": cfg.vocab, "batch": 1,
+            "storage": "u8 codes + bf16 scale/bias per 64, bf16 activations/KV, fp32 GDN state",
+            "launch": "one HIP graph per token",
+        },
+        "bytes_per_token": bpt,
+        "hbm_gbs": round(bpt * tok_s / 1e9, 1),
+        "hbm_frac": round(bpt * tok_s / 1e9 / PEAK_HBM_GBS, 4),
+        "gdn_layer_us": round(gdn_us, 2),
+        "full_layer_us": round(full_us, 2),
+        "lm_head_us": round(lm_us, 2),
+        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<2560,true> (post-norm gate/up SwiGLU)",
+                     "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_launch": dom_bytes, "us_per_launch": round(dom_us, 3)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        note = ("float64 oracle as it stands (dequantises each matrix per call): one GDN layer "
+                "{gdn:.2f}s, one full-attention layer at ctx 8192 {full:.2f}s, the lm_head + argmax "
+                "{lm:.2f}s, each run once; tok/s = 1/({ng} GDN + {nf} full + lm_head)")
+        result["cpu_baseline"] = cpu_baseline(cfg, w, note)
+        log(f"oracle: {result['cpu_baseline']['value']:.4f} tok/s")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

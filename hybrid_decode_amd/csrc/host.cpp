@@ -1,0 +1,769 @@
+// C-ABI of q35decode: validation, launch geometry and kernel sequencing for the
+// single-token Qwen3.5 layer forwards.  No device memory is allocated here;
+// every call enqueues on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/q35decode.h"
+#include "q35_internal.h"
+
+using namespace q35;
+
+struct Qwen35Kernels {
+    int device;
+    int num_cu;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+q35_status fail(q35_status code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+q35_status ok() {
+    g_err.clear();
+    return Q35_OK;
+}
+
+#define Q35_TRY(expr)                                  \
+    do {                                               \
+        q35_status st__ = (expr);                      \
+        if (st__ != Q35_OK) return st__;               \
+    } while (0)
+
+#define Q35_HIP(expr, what)                                                               \
+    do {                                                                                  \
+        hipError_t e__ = (expr);                                                          \
+        if (e__ != hipSuccess) return fail(Q35_ERR_HIP, "%s: %s", what, hipGetErrorString(e__)); \
+    } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
+uint32_t q_total(const Qwen35ForwardConfig& c) { return 2 * c.num_heads * c.head_dim; }
+uint32_t q_only(const Qwen35ForwardConfig& c) { return c.num_heads * c.head_dim; }
+uint32_t kv_dim(const Qwen35ForwardConfig& c) { return c.num_kv_heads * c.head_dim; }
+uint32_t z_dim(const Qwen35ForwardConfig& c) { return c.num_v_heads_lin * c.v_head_dim_lin; }
+uint32_t qkv_total(const Qwen35ForwardConfig& c) {
+    return 2 * c.num_k_heads_lin * c.k_head_dim_lin + z_dim(c);
+}
+
+q35_status check_rows(const char* what, uint32_t rows, uint32_t k) {
+    const int r = gemv_rows_per_matrix_group(k);
+    if (rows == 0 || rows % (uint32_t)r != 0)
+        return fail(Q35_ERR_UNSUPPORTED, "%s: %u rows is not a multiple of %d (rows per wave group at K=%u)",
+                    what, rows, r, k);
+    return Q35_OK;
+}
+
+q35_status check_weight(const char* what, const Q35QuantWeight& w, uint32_t n, uint32_t k) {
+    if (!w.codes || !w.scales || !w.biases) return fail(Q35_ERR_INVALID_ARG, "%s: NULL pointer", what);
+    if (w.n != n || w.k != k)
+        return fail(Q35_ERR_INVALID_ARG, "%s: shape [%u, %u], expected [%u, %u]", what, w.n, w.k, n, k);
+    if (!aligned16(w.codes)) return fail(Q35_ERR_INVALID_ARG, "%s: codes not 16-byte aligned", what);
+    return Q35_OK;
+}
+
+q35_status need(const void* p, const char* what, bool vec = true) {
+    if (!p) return fail(Q35_ERR_INVALID_ARG, "%s is NULL", what);
+    if (vec && !aligned16(p)) return fail(Q35_ERR_INVALID_ARG, "%s not 16-byte aligned", what);
+    return Q35_OK;
+}
+
+q35_status opt(const void* p, const char* what) {
+    if (p && !aligned16(p)) return fail(Q35_ERR_INVALID_ARG, "%s not 16-byte aligned", what);
+    return Q35_OK;
+}
+
+// Attention split-K geometry: positions per block for a cache length n, and
+// the number of per-chunk partial slots a workspace must hold for a capacity.
+constexpr uint32_t kAttnTargetBlocks = 256;
+constexpr uint32_t kAttnMaxChunk = 2048;
+
+uint32_t attn_chunk(const Qwen35ForwardConfig& c, uint32_t n) {
+    const uint32_t rpi = attn_rows_per_iter(c.head_dim);
+    uint64_t want = ((uint64_t)n * c.num_kv_heads + kAttnTargetBlocks - 1) / kAttnTargetBlocks;
+    uint64_t t = ((want + rpi - 1) / rpi) * rpi;
+    if (t < rpi) t = rpi;
+    if (t > kAttnMaxChunk) t = kAttnMaxChunk;
+    return (uint32_t)t;
+}
+
+uint32_t attn_max_chunks(const Qwen35ForwardConfig& c, uint32_t capacity) {
+    uint32_t a = kAttnTargetBlocks / c.num_kv_heads + 2;
+    uint32_t b = (capacity + kAttnMaxChunk - 1) / kAttnMaxChunk + 1;
+    return a > b ? a : b;
+}
+
+struct AttnWs {
+    size_t acc_off, ml_off, cnt_off, total;
+};
+
+AttnWs attn_ws_layout(const Qwen35ForwardConfig& c, uint32_t capacity) {
+    const uint32_t G = c.num_heads / c.num_kv_heads;
+    const size_t mc = attn_max_chunks(c, capacity);
+    AttnWs w;
+    w.acc_off = 0;
+    w.ml_off = (mc * c.num_kv_heads * G * c.head_dim * sizeof(float) + 255) & ~size_t(255);
+    w.cnt_off = w.ml_off + ((mc * c.num_kv_heads * 2 * G * sizeof(float) + 255) & ~size_t(255));
+    w.total = w.cnt_off + 256;
+    return w;
+}
+
+struct LmWs {
+    size_t val_off, idx_off, cnt_off, total;
+    uint32_t blocks;
+};
+
+LmWs lm_ws_layout(const Qwen35ForwardConfig& c) {
+    LmWs w;
+    const uint32_t r = (uint32_t)gemv_rows_per_matrix_group(c.hidden);
+    w.blocks = gemv_pick_blocks(c.vocab / r);
+    w.val_off = 0;
+    w.idx_off = ((size_t)w.blocks * 4 + 255) & ~size_t(255);
+    w.cnt_off = w.idx_off + (((size_t)w.blocks * 4 + 255) & ~size_t(255));
+    w.total = w.cnt_off + 256;
+    return w;
+}
+
+// A GEMV launch under construction: segments over one shared x.
+struct GemvBuild {
+    GemvArgs a;
+    uint32_t k;
+    bool paired;
+    uint32_t r;  // rows of one matrix per row group
+
+    GemvBuild(uint32_t k_, bool paired_, bool act_f32) : k(k_), paired(paired_) {
+        std::memset(&a, 0, sizeof(a));
+        a.act_f32 = act_f32 ? 1 : 0;
+        r = (uint32_t)gemv_rows_per_matrix_group(k);
+    }
+    GemvSeg& add(const Q35QuantWeight& w, int32_t epi, const Q35QuantWeight* w2 = nullptr) {
+        GemvSeg& s = a.seg[a.nseg++];
+        s.codes[0] = w.codes;
+        s.scales[0] = w.scales;
+        s.biases[0] = w.biases;
+        if (w2) {
+            s.codes[1] = w2->codes;
+            s.scales[1] = w2->scales;
+            s.biases[1] = w2->biases;
+        }
+        s.rg_begin = a.total_rg;
+        a.total_rg += w.n / r;
+        s.rg_end = a.total_rg;
+        s.epi = epi;
+        return s;
+    }
+    q35_status launch(hipStream_t stream, const char* what, uint32_t blocks = 0) {
+        if (!blocks) blocks = gemv_pick_blocks(a.total_rg);
+        Q35_HIP(gemv_launch(k, paired, a, blocks, stream), what);
+        return Q35_OK;
+    }
+};
+
+// gate/up (paired, SwiGLU epilogue) and down (+ residual) shared by both layers.
+q35_status launch_mlp(const Qwen35ForwardConfig& c, const Q35QuantWeight& gate_proj,
+                      const Q35QuantWeight& up_proj, const Q35QuantWeight& down_proj,
+                      const uint16_t* post_ln, float* x_resid, float* x_norm2, float* mlp_act,
+                      float* gate_act, float* up_act, void* x_out, void* x_out2,
+                      hipStream_t stream) {
+    const bool f32 = c.act_dtype == Q35_ACT_F32;
+    {
+        GemvBuild b(c.hidden, true, f32);
+        b.a.pro.kind = kProRmsF32;
+        b.a.pro.x = x_resid;
+        b.a.pro.w = post_ln;
+        b.a.pro.eps = c.rms_eps;
+        b.a.pro.tap = x_norm2;
+        GemvSeg& s = b.add(gate_proj, kEpiSwiGLU, &up_proj);
+        s.out = mlp_act;
+        s.tap0 = gate_act;
+        s.tap1 = up_act;
+        Q35_TRY(b.launch(stream, "gate/up GEMV"));
+    }
+    {
+        GemvBuild b(c.intermediate, false, f32);
+        b.a.pro.kind = kProLoadF32;
+        b.a.pro.x = mlp_act;
+        GemvSeg& s = b.add(down_proj, kEpiResidToAct);
+        s.aux0 = x_resid;
+        s.out_act = x_out;
+        s.out_act2 = x_out2;
+        Q35_TRY(b.launch(stream, "down GEMV"));
+    }
+    return Q35_OK;
+}
+
+q35_status check_kernels(const Qwen35Kernels* k) {
+    if (!k) return fail(Q35_ERR_INVALID_ARG, "kernels handle is NULL (call q35_kernels_resolve)");
+    return Q35_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* q35_last_error(void) { return g_err.c_str(); }
+
+q35_status q35_config_qwen3_5_4b(Qwen35ForwardConfig* cfg) {
+    if (!cfg) return fail(Q35_ERR_INVALID_ARG, "cfg is NULL");
+    Qwen35ForwardConfig c;
+    c.hidden = 2560;
+    c.intermediate = 9216;
+    c.num_layers = 32;
+    c.vocab = 248320;
+    c.group_size = 64;
+    c.rms_eps = 1e-6f;
+    c.num_heads = 16;
+    c.num_kv_heads = 4;
+    c.head_dim = 256;
+    c.rope_theta = 10000000.0f;
+    c.rotary_dim = 64;
+    c.num_k_heads_lin = 16;
+    c.num_v_heads_lin = 32;
+    c.k_head_dim_lin = 128;
+    c.v_head_dim_lin = 128;
+    c.conv_kernel_size = 4;
+    c.act_dtype = Q35_ACT_BF16;
+    *cfg = c;
+    return ok();
+}
+
+q35_status q35_config_validate(const Qwen35ForwardConfig* cfg) {
+    if (!cfg) return fail(Q35_ERR_INVALID_ARG, "cfg is NULL");
+    const Qwen35ForwardConfig& c = *cfg;
+    if (c.group_size != 64) return fail(Q35_ERR_UNSUPPORTED, "group_size %u (only 64)", c.group_size);
+    if (c.act_dtype != Q35_ACT_BF16 && c.act_dtype != Q35_ACT_F32)
+        return fail(Q35_ERR_INVALID_ARG, "act_dtype %u", c.act_dtype);
+    if (!(c.rms_eps > 0.0f) || !std::isfinite(c.rms_eps))
+        return fail(Q35_ERR_INVALID_ARG, "rms_eps must be positive");
+    if (c.num_heads == 0 || c.num_kv_heads == 0 || c.num_heads % c.num_kv_heads)
+        return fail(Q35_ERR_INVALID_ARG, "num_heads %u not a multiple of num_kv_heads %u", c.num_heads,
+                    c.num_kv_heads);
+    if (!attn_dims_supported(c.head_dim, c.num_heads / c.num_kv_heads))
+        return fail(Q35_ERR_UNSUPPORTED, "head_dim %u with %u q heads per kv head", c.head_dim,
+                    c.num_heads / c.num_kv_heads);
+    if (c.rotary_dim == 0 || c.rotary_dim % 2 || c.rotary_dim > c.head_dim)
+        return fail(Q35_ERR_INVALID_ARG, "rotary_dim %u (even, <= head_dim)", c.rotary_dim);
+    if (c.num_k_heads_lin == 0 || c.num_v_heads_lin % c.num_k_heads_lin)
+        return fail(Q35_ERR_INVALID_ARG, "num_v_heads_lin %u not a multiple of num_k_heads_lin %u",
+                    c.num_v_heads_lin, c.num_k_heads_lin);
+    if (!gdn_dims_supported(c.k_head_dim_lin, c.v_head_dim_lin))
+        return fail(Q35_ERR_UNSUPPORTED, "k/v head dims %u/%u (equal, 32/64/128)", c.k_head_dim_lin,
+                    c.v_head_dim_lin);
+    if (c.conv_kernel_size != 4)
+        return fail(Q35_ERR_UNSUPPORTED, "conv_kernel_size %u (only 4)", c.conv_kernel_size);
+    const uint32_t widths[4] = {c.hidden, c.intermediate, q_only(c), z_dim(c)};
+    const char* names[4] = {"hidden", "intermediate", "q_only", "z_dim_lin"};
+    for (int i = 0; i < 4; ++i) {
+        if (widths[i] == 0 || widths[i] % 64)
+            return fail(Q35_ERR_INVALID_ARG, "%s %u not a multiple of 64", names[i], widths[i]);
+        if (!gemv_width_supported(widths[i]))
+            return fail(Q35_ERR_UNSUPPORTED, "%s %u is not a compiled GEMV width", names[i], widths[i]);
+    }
+    if (c.hidden > 8192) return fail(Q35_ERR_UNSUPPORTED, "hidden %u > 8192", c.hidden);
+    // output rows of every GEMV must tile the per-wave row groups
+    Q35_TRY(check_rows("q_proj", q_total(c), c.hidden));
+    Q35_TRY(check_rows("k_proj/v_proj", kv_dim(c), c.hidden));
+    Q35_TRY(check_rows("in_proj_qkv", qkv_total(c), c.hidden));
+    Q35_TRY(check_rows("in_proj_z", z_dim(c), c.hidden));
+    Q35_TRY(check_rows("in_proj_a/b", c.num_v_heads_lin, c.hidden));
+    Q35_TRY(check_rows("gate/up", c.intermediate, c.hidden));
+    Q35_TRY(check_rows("o_proj", c.hidden, q_only(c)));
+    Q35_TRY(check_rows("out_proj", c.hidden, z_dim(c)));
+    Q35_TRY(check_rows("down_proj", c.hidden, c.intermediate));
+    if (c.vocab) Q35_TRY(check_rows("lm_head", c.vocab, c.hidden));
+    return ok();
+}
+
+q35_status q35_rope_inv_freq(const Qwen35ForwardConfig* cfg, float* host_out) {
+    if (!cfg || !host_out) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    const uint32_t r = cfg->rotary_dim;
+    if (r == 0 || r % 2) return fail(Q35_ERR_INVALID_ARG, "rotary_dim %u", r);
+    for (uint32_t i = 0; i < r / 2; ++i)
+        host_out[i] = (float)std::pow((double)cfg->rope_theta, -2.0 * (double)i / (double)r);
+    return ok();
+}
+
+q35_status q35_kernels_resolve(int device, Qwen35Kernels** out) {
+    if (!out) return fail(Q35_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n == 0) return fail(Q35_ERR_NO_DEVICE, "no HIP device");
+    if (device < 0 || device >= n) return fail(Q35_ERR_NO_DEVICE, "device %d of %d", device, n);
+    hipDeviceProp_t prop;
+    Q35_HIP(hipGetDeviceProperties(&prop, device), "hipGetDeviceProperties");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(Q35_ERR_NO_DEVICE, "device %d is %s, this library is built for gfx950", device,
+                    prop.gcnArchName);
+    int prev = 0;
+    Q35_HIP(hipGetDevice(&prev), "hipGetDevice");
+    Q35_HIP(hipSetDevice(device), "hipSetDevice");
+    q35_status st = Q35_OK;
+    auto probe = [&](const void* fn, const char* name) {
+        if (st != Q35_OK) return;
+        hipFuncAttributes attr;
+        hipError_t e = hipFuncGetAttributes(&attr, fn);
+        if (e != hipSuccess) st = fail(Q35_ERR_HIP, "kernel %s does not load: %s", name, hipGetErrorString(e));
+    };
+    const uint32_t widths[] = {128, 256, 512, 1024, 2048, 2560, 3072, 4096, 5120, 6144, 8192, 9216, 12288};
+    for (uint32_t w : widths) {
+        probe(gemv_kernel_ptr(w, false), "gemv");
+        if (w <= 8192) probe(gemv_kernel_ptr(w, true), "gemv (paired)");
+    }
+    for (uint32_t dk : {32u, 64u, 128u}) probe(gdn_kernel_ptr(dk), "gated_delta_rule");
+    for (uint32_t d : {64u, 128u, 256u})
+        for (uint32_t g : {1u, 2u, 4u, 8u}) probe(attn_kernel_ptr(d, g), "attention");
+    probe(embed_kernel_ptr(), "embed");
+    (void)hipSetDevice(prev);
+    if (st != Q35_OK) return st;
+    Qwen35Kernels* k = new Qwen35Kernels;
+    k->device = device;
+    k->num_cu = prop.multiProcessorCount;
+    *out = k;
+    return ok();
+}
+
+void q35_kernels_release(Qwen35Kernels* k) { delete k; }
+
+q35_status q35_kv_dtype_from_str(const char* name, uint32_t* dtype) {
+    if (!name || !dtype) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    static const char* names[] = {"bf16", "turbo8", "turbo4", "turbo3", "turbo2",
+                                  "bf16k_turbo4v", "bf16k_turbo3v", "bf16k_turbo2v"};
+    for (uint32_t i = 0; i < 8; ++i)
+        if (std::strcmp(name, names[i]) == 0) {
+            *dtype = i;
+            return ok();
+        }
+    return fail(Q35_ERR_INVALID_ARG,
+                "kv dtype \"%s\" unknown (bf16 | turbo8 | turbo4 | turbo3 | turbo2 | bf16k_turbo4v/3v/2v)",
+                name);
+}
+
+q35_status q35_kv_cache_bytes(const Qwen35ForwardConfig* cfg, uint32_t dtype, uint32_t max_seq,
+                              size_t* k_bytes, size_t* v_bytes, size_t* k_scale_bytes,
+                              size_t* v_scale_bytes) {
+    if (!cfg || !k_bytes || !v_bytes || !k_scale_bytes || !v_scale_bytes)
+        return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    const size_t kvd = kv_dim(*cfg);
+    if (dtype > Q35_KV_BF16K_TURBO2V) return fail(Q35_ERR_INVALID_ARG, "kv dtype %u", dtype);
+    if (dtype != Q35_KV_BF16 && kvd % 16)
+        return fail(Q35_ERR_INVALID_ARG, "turbo KV formats need kv_dim divisible by 16 (kv_dim %zu)", kvd);
+    const size_t n = (size_t)max_seq * kvd;
+    const size_t se = n / 16;  // one scale per 16 elements
+    size_t kb = 0, vb = 0, ks = 0, vs = 0;
+    switch (dtype) {
+        case Q35_KV_BF16: kb = vb = n * 2; break;
+        case Q35_KV_TURBO8: kb = vb = n; ks = vs = se * 2; break;
+        case Q35_KV_TURBO4: kb = vb = n / 2; ks = vs = se; break;
+        case Q35_KV_TURBO3: kb = vb = n * 3 / 8; ks = vs = se; break;
+        case Q35_KV_TURBO2: kb = vb = n / 4; ks = vs = se; break;
+        case Q35_KV_BF16K_TURBO4V: kb = n * 2; vb = n / 2; vs = se; break;
+        case Q35_KV_BF16K_TURBO3V: kb = n * 2; vb = n * 3 / 8; vs = se; break;
+        case Q35_KV_BF16K_TURBO2V: kb = n * 2; vb = n / 4; vs = se; break;
+    }
+    *k_bytes = kb;
+    *v_bytes = vb;
+    *k_scale_bytes = ks;
+    *v_scale_bytes = vs;
+    return ok();
+}
+
+q35_status q35_full_attention_workspace_bytes(const Qwen35ForwardConfig* cfg, uint32_t capacity,
+                                              size_t* bytes) {
+    if (!cfg || !bytes) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    Q35_TRY(q35_config_validate(cfg));
+    *bytes = attn_ws_layout(*cfg, capacity).total;
+    return ok();
+}
+
+static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                                    const FullAttentionLayer* layer,
+                                    const FullAttentionScratch* s, const LayerKvCache* kv,
+                                    const float* inv_freq, const int32_t* positions,
+                                    const void* x_in, int64_t cache_pos, uint32_t seq_len_attn,
+                                    hipStream_t stream, void** out) {
+    Q35_TRY(check_kernels(kernels));
+    if (!cfg || !layer || !s || !kv || !out) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    Q35_TRY(q35_config_validate(cfg));
+    const Qwen35ForwardConfig& c = *cfg;
+    if (kv->dtype != Q35_KV_BF16)
+        return fail(Q35_ERR_UNSUPPORTED, "KV dtype %u: only bf16 caches are implemented", kv->dtype);
+    if (kv->k_scales || kv->v_scales) return fail(Q35_ERR_INVALID_ARG, "bf16 cache with scale buffers");
+    Q35_TRY(need(kv->k, "kv.k"));
+    Q35_TRY(need(kv->v, "kv.v"));
+    if (kv->capacity == 0) return fail(Q35_ERR_OUT_OF_RANGE, "cache capacity is 0");
+    if (cache_pos >= 0) {
+        if ((uint64_t)cache_pos >= kv->capacity)
+            return fail(Q35_ERR_OUT_OF_RANGE, "cache_pos %lld >= capacity %u", (long long)cache_pos, kv->capacity);
+        if (seq_len_attn != (uint64_t)cache_pos + 1)
+            return fail(Q35_ERR_OUT_OF_RANGE, "seq_len_attn %u != cache_pos + 1 (%lld)", seq_len_attn,
+                        (long long)cache_pos + 1);
+    }
+    Q35_TRY(need(inv_freq, "inv_freq", false));
+    Q35_TRY(need(positions, "positions", false));
+    Q35_TRY(need(x_in, "x_in"));
+    Q35_TRY(need(layer->input_ln, "input_ln"));
+    Q35_TRY(need(layer->q_norm, "q_norm"));
+    Q35_TRY(need(layer->k_norm, "k_norm"));
+    Q35_TRY(need(layer->post_ln, "post_ln"));
+    Q35_TRY(check_weight("q_proj", layer->q_proj, q_total(c), c.hidden));
+    Q35_TRY(check_weight("k_proj", layer->k_proj, kv_dim(c), c.hidden));
+    Q35_TRY(check_weight("v_proj", layer->v_proj, kv_dim(c), c.hidden));
+    Q35_TRY(check_weight("o_proj", layer->o_proj, c.hidden, q_only(c)));
+    Q35_TRY(check_weight("gate_proj", layer->gate_proj, c.intermediate, c.hidden));
+    Q35_TRY(check_weight("up_proj", layer->up_proj, c.intermediate, c.hidden));
+    Q35_TRY(check_weight("down_proj", layer->down_proj, c.hidden, c.intermediate));
+    Q35_TRY(need(s->q_full, "scratch.q_full"));
+    Q35_TRY(need(s->k, "scratch.k"));
+    Q35_TRY(need(s->v, "scratch.v"));
+    Q35_TRY(need(s->gated_attn, "scratch.gated_attn"));
+    Q35_TRY(need(s->x_resid, "scratch.x_resid"));
+    Q35_TRY(need(s->mlp_act, "scratch.mlp_act"));
+    Q35_TRY(need(s->x_out, "scratch.x_out"));
+    Q35_TRY(need(s->workspace, "scratch.workspace"));
+    Q35_TRY(opt(s->x_norm, "scratch.x_norm"));
+    Q35_TRY(opt(s->x_norm2, "scratch.x_norm2"));
+    const AttnWs ws = attn_ws_layout(c, kv->capacity);
+    if (s->workspace_bytes < ws.total)
+        return fail(Q35_ERR_INVALID_ARG, "workspace %zu bytes < %zu required", s->workspace_bytes, ws.total);
+    if (x_in == s->x_out) return fail(Q35_ERR_INVALID_ARG, "x_in aliases scratch.x_out");
+
+    const bool f32 = c.act_dtype == Q35_ACT_F32;
+    // 1. input RMSNorm + q/k/v projections
+    {
+        GemvBuild b(c.hidden, false, f32);
+        b.a.pro.kind = kProRmsAct;
+        b.a.pro.x_f32 = f32;
+        b.a.pro.x = x_in;
+        b.a.pro.w = layer->input_ln;
+        b.a.pro.eps = c.rms_eps;
+        b.a.pro.tap = s->x_norm;
+        b.add(layer->q_proj, kEpiStore).out = s->q_full;
+        b.add(layer->k_proj, kEpiStore).out = s->k;
+        b.add(layer->v_proj, kEpiStore).out = s->v;
+        Q35_TRY(b.launch(stream, "q/k/v GEMV"));
+    }
+    // 2. split, q/k norm, RoPE, KV append, split-K attention, sigmoid gate
+    {
+        AttnArgs a;
+        std::memset(&a, 0, sizeof(a));
+        const uint32_t G = c.num_heads / c.num_kv_heads;
+        uint8_t* wsb = static_cast<uint8_t*>(s->workspace);
+        a.q_full = s->q_full;
+        a.k = s->k;
+        a.v = s->v;
+        a.q_norm = layer->q_norm;
+        a.k_norm = layer->k_norm;
+        a.inv_freq = inv_freq;
+        a.positions = positions;
+        a.kc = static_cast<uint16_t*>(kv->k);
+        a.vc = static_cast<uint16_t*>(kv->v);
+        a.gated_attn = s->gated_attn;
+        a.attn_out = s->attn_out;
+        a.q_norm_out = s->q_norm_out;
+        a.k_norm_out = s->k_norm_out;
+        a.part_acc = reinterpret_cast<float*>(wsb + ws.acc_off);
+        a.part_ml = reinterpret_cast<float*>(wsb + ws.ml_off);
+        a.counters = reinterpret_cast<uint32_t*>(wsb + ws.cnt_off);
+        a.capacity = kv->capacity;
+        a.hq = c.num_heads;
+        a.hkv = c.num_kv_heads;
+        a.rotary = c.rotary_dim;
+        a.max_chunks = attn_max_chunks(c, kv->capacity);
+        a.eps = c.rms_eps;
+        a.scale = 1.0f / std::sqrt((float)c.head_dim);
+        uint32_t grid;
+        if (cache_pos >= 0) {
+            a.host_pos = (int32_t)cache_pos;
+            a.chunk = attn_chunk(c, seq_len_attn);
+            grid = (seq_len_attn + a.chunk - 1) / a.chunk;
+        } else {
+            a.host_pos = -1;
+            a.chunk = attn_chunk(c, kv->capacity);
+            grid = (kv->capacity + a.chunk - 1) / a.chunk;
+        }
+        if (grid > a.max_chunks) return fail(Q35_ERR_INVALID_ARG, "internal: %u chunks > %u", grid, a.max_chunks);
+        Q35_HIP(attn_launch(c.head_dim, G, a, grid, stream), "attention");
+        (void)G;
+    }
+    // 3. o projection + residual
+    {
+        GemvBuild b(q_only(c), false, f32);
+        b.a.pro.kind = kProLoadF32;
+        b.a.pro.x = s->gated_attn;
+        GemvSeg& sg = b.add(layer->o_proj, kEpiResidActIn);
+        sg.out = s->x_resid;
+        sg.aux0 = x_in;
+        sg.tap0 = s->o;
+        Q35_TRY(b.launch(stream, "o_proj GEMV"));
+    }
+    // 4-5. post-attention norm, SwiGLU MLP, residual
+    Q35_TRY(launch_mlp(c, layer->gate_proj, layer->up_proj, layer->down_proj, layer->post_ln,
+                       s->x_resid, s->x_norm2, s->mlp_act, s->gate_act, s->up_act, s->x_out,
+                       nullptr, stream));
+    *out = s->x_out;
+    return ok();
+}
+
+q35_status q35_forward_full_attention(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                                      const FullAttentionLayer* layer,
+                                      const FullAttentionScratch* scratch, const LayerKvCache* kv,
+                                      const float* inv_freq, const int32_t* positions,
+                                      const void* x_in, uint32_t cache_pos, uint32_t seq_len_attn,
+                                      hipStream_t stream, void** out) {
+    return forward_full_impl(kernels, cfg, layer, scratch, kv, inv_freq, positions, x_in,
+                             (int64_t)cache_pos, seq_len_attn, stream, out);
+}
+
+q35_status q35_forward_full_attention_devpos(const Qwen35Kernels* kernels,
+                                             const Qwen35ForwardConfig* cfg,
+                                             const FullAttentionLayer* layer,
+                                             const FullAttentionScratch* scratch,
+                                             const LayerKvCache* kv, const float* inv_freq,
+                                             const int32_t* positions, const void* x_in,
+                                             hipStream_t stream, void** out) {
+    return forward_full_impl(kernels, cfg, layer, scratch, kv, inv_freq, positions, x_in, -1, 0,
+                             stream, out);
+}
+
+q35_status q35_forward_linear_attention(const Qwen35Kernels* kernels,
+                                        const Qwen35ForwardConfig* cfg,
+                                        const LinearAttentionLayer* layer,
+                                        const LinearAttentionState* state,
+                                        const LinearAttentionScratch* s, const void* x_in,
+                                        void* x_buf, hipStream_t stream, q35_dump_fn dump,
+                                        void* dump_ctx, void** out) {
+    Q35_TRY(check_kernels(kernels));
+    if (!cfg || !layer || !state || !s || !out) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    Q35_TRY(q35_config_validate(cfg));
+    const Qwen35ForwardConfig& c = *cfg;
+    const uint32_t Hv = c.num_v_heads_lin;
+    Q35_TRY(need(x_in, "x_in"));
+    Q35_TRY(need(x_buf, "x_buf"));
+    Q35_TRY(need(state->conv1d_state, "state.conv1d_state"));
+    Q35_TRY(need(state->gdn_state, "state.gdn_state"));
+    Q35_TRY(need(layer->input_ln, "input_ln"));
+    Q35_TRY(need(layer->post_ln, "post_ln"));
+    Q35_TRY(need(layer->norm_weight, "norm_weight"));
+    Q35_TRY(need(layer->a_log, "a_log", false));
+    Q35_TRY(need(layer->dt_bias, "dt_bias", false));
+    if (!layer->conv1d_weight || !aligned8(layer->conv1d_weight))
+        return fail(Q35_ERR_INVALID_ARG, "conv1d_weight NULL or not 8-byte aligned");
+    Q35_TRY(check_weight("in_proj_a", layer->in_proj_a, Hv, c.hidden));
+    Q35_TRY(check_weight("in_proj_b", layer->in_proj_b, Hv, c.hidden));
+    Q35_TRY(check_weight("in_proj_qkv", layer->in_proj_qkv, qkv_total(c), c.hidden));
+    Q35_TRY(check_weight("in_proj_z", layer->in_proj_z, z_dim(c), c.hidden));
+    Q35_TRY(check_weight("out_proj", layer->out_proj, c.hidden, z_dim(c)));
+    Q35_TRY(check_weight("gate_proj", layer->gate_proj, c.intermediate, c.hidden));
+    Q35_TRY(check_weight("up_proj", layer->up_proj, c.intermediate, c.hidden));
+    Q35_TRY(check_weight("down_proj", layer->down_proj, c.hidden, c.intermediate));
+    Q35_TRY(need(s->qkv_conv, "scratch.qkv_conv"));
+    Q35_TRY(need(s->z, "scratch.z"));
+    Q35_TRY(need(s->gate, "scratch.gate", false));
+    Q35_TRY(need(s->beta, "scratch.beta", false));
+    Q35_TRY(need(s->y, "scratch.y"));
+    Q35_TRY(need(s->x_resid, "scratch.x_resid"));
+    Q35_TRY(need(s->mlp_act, "scratch.mlp_act"));
+    Q35_TRY(opt(s->x_norm, "scratch.x_norm"));
+    Q35_TRY(opt(s->y_norm, "scratch.y_norm"));
+    Q35_TRY(opt(s->x_norm2, "scratch.x_norm2"));
+
+    const bool f32 = c.act_dtype == Q35_ACT_F32;
+    // 1. input RMSNorm + in_proj qkv (conv epilogue) / z / a (gate) / b (beta)
+    {
+        GemvBuild b(c.hidden, false, f32);
+        b.a.pro.kind = kProRmsAct;
+        b.a.pro.x_f32 = f32;
+        b.a.pro.x = x_in;
+        b.a.pro.w = layer->input_ln;
+        b.a.pro.eps = c.rms_eps;
+        b.a.pro.tap = s->x_norm;
+        GemvSeg& sq = b.add(layer->in_proj_qkv, kEpiConv);
+        sq.out = s->qkv_conv;
+        sq.state = state->conv1d_state;
+        sq.aux0 = layer->conv1d_weight;
+        sq.tap0 = s->qkv;
+        b.add(layer->in_proj_z, kEpiStore).out = s->z;
+        GemvSeg& sa = b.add(layer->in_proj_a, kEpiGate);
+        sa.out = s->gate;
+        sa.aux0 = layer->dt_bias;
+        sa.aux1 = layer->a_log;
+        sa.tap0 = s->dt_raw;
+        GemvSeg& sb = b.add(layer->in_proj_b, kEpiBeta);
+        sb.out = s->beta;
+        sb.tap0 = s->b_raw;
+        Q35_TRY(b.launch(stream, "in_proj GEMV"));
+    }
+    // 2. L2 norm of q/k + gated delta rule
+    {
+        GdnArgs g;
+        std::memset(&g, 0, sizeof(g));
+        g.state = state->gdn_state;
+        g.qkv_conv = s->qkv_conv;
+        g.gate = s->gate;
+        g.beta = s->beta;
+        g.y = s->y;
+        g.qkv_smooth = s->qkv_smooth;
+        g.hk = c.num_k_heads_lin;
+        g.hv = Hv;
+        g.l2_eps = 1e-6f;
+        g.out_scale = 1.0f / std::sqrt((float)c.k_head_dim_lin);
+        Q35_HIP(gdn_launch(c.k_head_dim_lin, c.v_head_dim_lin, g, stream), "gated delta rule");
+    }
+    // 3. gated RMSNorm + out projection + residual
+    {
+        GemvBuild b(z_dim(c), false, f32);
+        b.a.pro.kind = kProGatedNorm;
+        b.a.pro.x = s->y;
+        b.a.pro.w = layer->norm_weight;
+        b.a.pro.z = s->z;
+        b.a.pro.head_dim = c.v_head_dim_lin;
+        b.a.pro.eps = c.rms_eps;
+        b.a.pro.tap = s->y_norm;
+        GemvSeg& so = b.add(layer->out_proj, kEpiResidActIn);
+        so.out = s->x_resid;
+        so.aux0 = x_in;
+        so.tap0 = s->out;
+        Q35_TRY(b.launch(stream, "out_proj GEMV"));
+    }
+    // 4-5. MLP; output residual stream straight into x_buf
+    Q35_TRY(launch_mlp(c, layer->gate_proj, layer->up_proj, layer->down_proj, layer->post_ln,
+                       s->x_resid, s->x_norm2, s->mlp_act, s->gate_act, s->up_act, x_buf,
+                       s->x_final, stream));
+    if (dump) {
+        Q35_HIP(hipStreamSynchronize(stream), "hipStreamSynchronize");
+        const uint32_t qt = qkv_total(c), zd = z_dim(c);
+        if (s->x_norm) dump(dump_ctx, "gdn_x_norm", s->x_norm, c.hidden);
+        if (s->qkv) dump(dump_ctx, "gdn_qkv_pre", s->qkv, qt);
+        if (s->qkv_smooth) dump(dump_ctx, "gdn_qkv_smooth", s->qkv_smooth, qt);
+        dump(dump_ctx, "gdn_y", s->y, zd);
+        if (s->y_norm) dump(dump_ctx, "gdn_y_norm", s->y_norm, zd);
+        if (s->out) dump(dump_ctx, "gdn_out", s->out, c.hidden);
+        dump(dump_ctx, "gdn_x_resid", s->x_resid, c.hidden);
+        dump(dump_ctx, "gdn_x_final", s->x_final ? s->x_final : x_buf, c.hidden);
+    }
+    *out = x_buf;
+    return ok();
+}
+
+q35_status q35_embed_lookup(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                            const uint16_t* table, const int32_t* tokens, void* x_out,
+                            hipStream_t stream) {
+    Q35_TRY(check_kernels(kernels));
+    if (!cfg || !table || !tokens || !x_out) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    if (cfg->vocab == 0 || cfg->hidden == 0) return fail(Q35_ERR_INVALID_ARG, "vocab/hidden is 0");
+    Q35_HIP(embed_launch(table, tokens, cfg->vocab, cfg->hidden, x_out, cfg->act_dtype == Q35_ACT_F32,
+                         stream), "embed");
+    return ok();
+}
+
+q35_status q35_lm_head_workspace_bytes(const Qwen35ForwardConfig* cfg, size_t* bytes) {
+    if (!cfg || !bytes) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    Q35_TRY(q35_config_validate(cfg));
+    if (cfg->vocab == 0) return fail(Q35_ERR_INVALID_ARG, "vocab is 0");
+    *bytes = lm_ws_layout(*cfg).total;
+    return ok();
+}
+
+q35_status q35_lm_head_argmax(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                              const uint16_t* final_norm, const Q35QuantWeight* lm_head,
+                              const void* x, float* logits, void* workspace,
+                              size_t workspace_bytes, int32_t* tokens, int32_t* positions,
+                              int32_t* history, uint32_t history_len, int32_t history_base,
+                              const uint16_t* embed_table, void* x_next, hipStream_t stream) {
+    Q35_TRY(check_kernels(kernels));
+    if (!cfg || !lm_head) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    Q35_TRY(q35_config_validate(cfg));
+    const Qwen35ForwardConfig& c = *cfg;
+    if (c.vocab == 0) return fail(Q35_ERR_INVALID_ARG, "vocab is 0");
+    Q35_TRY(check_weight("lm_head", *lm_head, c.vocab, c.hidden));
+    Q35_TRY(need(final_norm, "final_norm"));
+    Q35_TRY(need(x, "x"));
+    Q35_TRY(need(tokens, "tokens", false));
+    Q35_TRY(need(workspace, "workspace"));
+    if ((embed_table == nullptr) != (x_next == nullptr))
+        return fail(Q35_ERR_INVALID_ARG, "embed_table and x_next go together");
+    if (x_next && x_next == x) return fail(Q35_ERR_INVALID_ARG, "x_next aliases x");
+    const LmWs ws = lm_ws_layout(c);
+    if (workspace_bytes < ws.total)
+        return fail(Q35_ERR_INVALID_ARG, "workspace %zu bytes < %zu required", workspace_bytes, ws.total);
+    const bool f32 = c.act_dtype == Q35_ACT_F32;
+    GemvBuild b(c.hidden, false, f32);
+    b.a.pro.kind = kProRmsAct;
+    b.a.pro.x_f32 = f32;
+    b.a.pro.x = x;
+    b.a.pro.w = final_norm;
+    b.a.pro.eps = c.rms_eps;
+    b.add(*lm_head, kEpiArgmax).out = logits;
+    uint8_t* wsb = static_cast<uint8_t*>(workspace);
+    b.a.am.part_val = reinterpret_cast<float*>(wsb + ws.val_off);
+    b.a.am.part_idx = reinterpret_cast<int32_t*>(wsb + ws.idx_off);
+    b.a.am.counter = reinterpret_cast<uint32_t*>(wsb + ws.cnt_off);
+    b.a.am.tokens = tokens;
+    b.a.am.positions = positions;
+    b.a.am.history = history;
+    b.a.am.history_len = history ? history_len : 0;
+    b.a.am.history_base = history_base;
+    b.a.am.embed = embed_table;
+    b.a.am.x_next = x_next;
+    b.a.am.hidden = c.hidden;
+    b.a.am.vocab = c.vocab;
+    Q35_TRY(b.launch(stream, "lm_head GEMV", ws.blocks));
+    return ok();
+}
+
+q35_status q35_gate_up_swiglu(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                              const uint16_t* post_ln, const Q35QuantWeight* gate_proj,
+                              const Q35QuantWeight* up_proj, const float* x_resid,
+                              float* mlp_act, hipStream_t stream) {
+    Q35_TRY(check_kernels(kernels));
+    if (!cfg || !gate_proj || !up_proj) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    Q35_TRY(q35_config_validate(cfg));
+    const Qwen35ForwardConfig& c = *cfg;
+    Q35_TRY(check_weight("gate_proj", *gate_proj, c.intermediate, c.hidden));
+    Q35_TRY(check_weight("up_proj", *up_proj, c.intermediate, c.hidden));
+    Q35_TRY(need(post_ln, "post_ln"));
+    Q35_TRY(need(x_resid, "x_resid"));
+    Q35_TRY(need(mlp_act, "mlp_act"));
+    GemvBuild b(c.hidden, true, c.act_dtype == Q35_ACT_F32);
+    b.a.pro.kind = kProRmsF32;
+    b.a.pro.x = x_resid;
+    b.a.pro.w = post_ln;
+    b.a.pro.eps = c.rms_eps;
+    b.add(*gate_proj, kEpiSwiGLU, up_proj).out = mlp_act;
+    Q35_TRY(b.launch(stream, "gate/up GEMV"));
+    return ok();
+}
+
+q35_status q35_gemv(const Qwen35Kernels* kernels, const Q35QuantWeight* w, const float* x,
+                    float* y, hipStream_t stream) {
+    Q35_TRY(check_kernels(kernels));
+    if (!w) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    if (!gemv_width_supported(w->k)) return fail(Q35_ERR_UNSUPPORTED, "K = %u is not a compiled width", w->k);
+    Q35_TRY(check_weight("w", *w, w->n, w->k));
+    Q35_TRY(check_rows("w", w->n, w->k));
+    Q35_TRY(need(x, "x"));
+    Q35_TRY(need(y, "y", false));
+    GemvBuild b(w->k, false, true);
+    b.a.pro.kind = kProLoadF32;
+    b.a.pro.x = x;
+    b.add(*w, kEpiStore).out = y;
+    Q35_TRY(b.launch(stream, "GEMV"));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// Device helpers shared by the q35decode kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define Q35_DEV __device__ __forceinline__
+
+namespace q35 {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ dtypes
+
+Q35_DEV float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+Q35_DEV float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+Q35_DEV float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
+
+// Round-to-nearest-even fp32 -> bf16 bits; NaN -> canonical quiet NaN.
+Q35_DEV uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Read element i of an activation vector (bf16 bits or fp32).
+Q35_DEV float load_act(const void* p, uint32_t i, bool is_f32) {
+    return is_f32 ? static_cast<const float*>(p)[i]
+                  : bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+
+Q35_DEV void store_act(void* p, uint32_t i, float v, bool is_f32) {
+    if (is_f32)
+        static_cast<float*>(p)[i] = v;
+    else
+        static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(f32_to_bf16(v));
+}
+
+// ------------------------------------------------------------------ activations
+
+Q35_DEV float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+Q35_DEV float siluf_(float x) { return x / (1.0f + expf(-x)); }
+Q35_DEV float softplusf_(float x) { return x > 20.0f ? x : log1pf(expf(x)); }
+
+// ------------------------------------------------------------------ cross-lane sums
+
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
+Q35_DEV float dpp(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK,
+                                           BANK_MASK, false));
+}
+
+// Sum over aligned groups of W lanes (W in {2,4,8,16,32,64}).  The result is
+// valid in the LAST lane of each group (other lanes hold partial sums).
+template <int W>
+Q35_DEV float group_sum_last(float v) {
+    static_assert(W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "W");
+    v += dpp<0xB1>(v);                         // quad_perm [1,0,3,2]
+    if constexpr (W >= 4) v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]: all quad lanes hold the quad sum
+    if constexpr (W >= 8) v += dpp<0x124>(v);  // row_ror:4: odd quads hold their 8-lane sum
+    if constexpr (W >= 16) v += dpp<0x128>(v); // row_ror:8: every lane holds its 16-lane row sum
+    if constexpr (W >= 32) v += dpp<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    if constexpr (W >= 64) v += dpp<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+// Full wave sum, returned wave-uniform in every lane.
+Q35_DEV float wave_sum(float v) {
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0x124>(v);
+    v += dpp<0x128>(v);  // every lane: its row (16 lanes) sum
+    float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 15));
+    float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+    float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 47));
+    float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+    return (a + b) + (c + d);
+}
+
+Q35_DEV float wave_max(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// Block-wide sum for blockDim.x == NT (multiple of 64); every thread gets the
+// total.  `red` must hold NT/64 floats of shared memory.
+template <int NT>
+Q35_DEV float block_sum(float v, float* red) {
+    constexpr int NW = NT / kWave;
+    float w = wave_sum(v);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    __syncthreads();  // protect `red` from a previous use
+    if (lane == 0) red[wid] = w;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) t += red[i];
+    return t;
+}
+
+Q35_DEV float uniform_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+Q35_DEV uint32_t lane_id() { return threadIdx.x & 63u; }
+
+}  // namespace q35

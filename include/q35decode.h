@@ -1,0 +1,420 @@
+/*
+ * q35decode: single-token (batch-1) decode of Qwen3.5 hybrid decoder layers on
+ * AMD Instinct MI355X (gfx950), as a C ABI.
+ *
+ * The calls mirror the problem statement of the `qwen3_5` forward module
+ * documented on four pages: the rustdoc index "Module qwen3_5" and the source
+ * pages `mod.rs`, `full_attention.rs` and `linear_attention.rs`.  Two layer
+ * forwards, `forward_full_attention` and `forward_linear_attention`, each run one
+ * decoder layer for one token over a `Qwen35ForwardConfig`, with the layer's
+ * weights, state, KV cache and scratch all owned by the caller.
+ *
+ * Conventions for every call below:
+ *  - Pointers named in structs are DEVICE pointers unless the comment says
+ *    "host".  The library never frees or retains them past the call.
+ *  - The library allocates no device memory.  Calls that take a hipStream_t
+ *    only enqueue work on that stream and return; nothing is synchronised
+ *    unless stated.  Scratch, state and cache buffers must not be shared by
+ *    calls that may run concurrently.
+ *  - Every call returns a q35_status, and q35_last_error() then holds a message
+ *    (thread-local).  Argument errors are found before anything is enqueued;
+ *    Q35_ERR_HIP means a launch failed part way.
+ *  - Dtypes: "bf16" buffers hold bfloat16 bit patterns (uint16); "act" buffers
+ *    hold the activation dtype of the config (bf16 or fp32); everything else is
+ *    fp32 unless stated.
+ */
+#ifndef Q35DECODE_H
+#define Q35DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status */
+
+typedef int32_t q35_status;
+#define Q35_OK 0
+#define Q35_ERR_INVALID_ARG 1   /* bad config, size, alignment or NULL pointer       */
+#define Q35_ERR_UNSUPPORTED 2   /* a valid request this build does not implement     */
+#define Q35_ERR_OUT_OF_RANGE 3  /* cache position / sequence length out of bounds    */
+#define Q35_ERR_HIP 4           /* a HIP runtime call or launch failed               */
+#define Q35_ERR_NO_DEVICE 5     /* no device, or the device is not gfx950            */
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* q35_last_error(void);
+
+/* ------------------------------------------------------------------ config */
+
+#define Q35_ACT_BF16 0u
+#define Q35_ACT_F32 1u
+
+/*
+ * Qwen35ForwardConfig (mod.rs page, the config struct): the sixteen dimension
+ * fields of the pages, in the same order, plus `act_dtype`, the dtype of the
+ * residual stream (Q35_ACT_BF16 or Q35_ACT_F32).
+ */
+typedef struct Qwen35ForwardConfig {
+    uint32_t hidden;
+    uint32_t intermediate;
+    uint32_t num_layers;
+    uint32_t vocab;
+    uint32_t group_size;
+    float rms_eps;
+    uint32_t num_heads;
+    uint32_t num_kv_heads;
+    uint32_t head_dim;
+    float rope_theta;
+    uint32_t rotary_dim;
+    uint32_t num_k_heads_lin;
+    uint32_t num_v_heads_lin;
+    uint32_t k_head_dim_lin;
+    uint32_t v_head_dim_lin;
+    uint32_t conv_kernel_size;
+    uint32_t act_dtype;
+} Qwen35ForwardConfig;
+
+/* Fills *cfg with the Qwen3.5-4B dimensions (mod.rs page, the preset
+ * constructor) and act_dtype = Q35_ACT_BF16.  Host pointer. */
+q35_status q35_config_qwen3_5_4b(Qwen35ForwardConfig* cfg);
+
+/*
+ * Checks that this build supports *cfg (host pointer): group_size 64;
+ * hidden, intermediate, q_only, kv_dim and z_dim_lin multiples of 64 and
+ * among the GEMV widths compiled in; num_heads % num_kv_heads == 0 with a
+ * ratio in {1,2,4,8}; num_v_heads_lin % num_k_heads_lin == 0; head_dim in
+ * {64,128,256}; rotary_dim even and <= head_dim; k_head_dim_lin ==
+ * v_head_dim_lin in {32,64,128}; conv_kernel_size 4; act_dtype bf16 or f32.
+ * Q35_ERR_INVALID_ARG or Q35_ERR_UNSUPPORTED otherwise.
+ */
+q35_status q35_config_validate(const Qwen35ForwardConfig* cfg);
+
+/* inv_freq[i] = fp32(rope_theta^(-2i/rotary_dim)) for i < rotary_dim/2, computed
+ * in double.  This is the caller-built buffer `rope_apply` consumes
+ * (full_attention.rs page, the RoPE launches).  host_out: host, rotary_dim/2 floats. */
+q35_status q35_rope_inv_freq(const Qwen35ForwardConfig* cfg, float* host_out);
+
+/* ------------------------------------------------------------------ kernels */
+
+/*
+ * Qwen35Kernels (mod.rs page, the kernel table and its resolve function):
+ * checks once, at start-up, that `device` is a gfx950 GPU and that every
+ * kernel of this library loads on it, so nothing is looked up in the hot path.
+ * Errors: Q35_ERR_NO_DEVICE (no such device, or not gfx950), Q35_ERR_HIP.
+ * The handle is immutable and may be shared by threads; release it with
+ * q35_kernels_release.
+ */
+typedef struct Qwen35Kernels Qwen35Kernels;
+q35_status q35_kernels_resolve(int device, Qwen35Kernels** out);
+void q35_kernels_release(Qwen35Kernels* k);
+
+/* ------------------------------------------------------------------ weights */
+
+/*
+ * One 8-bit affine quantised matrix (the pages' QuantWeights, an MLX-8bit
+ * checkpoint with group_size 64): W[n][k] = scale[n][k/64] * code[n][k] +
+ * bias[n][k/64].  codes: uint8 [n, k] row-major; scales, biases: bf16 [n, k/64]
+ * row-major.  Device pointers, 16-byte aligned, read only.
+ */
+typedef struct Q35QuantWeight {
+    const uint8_t* codes;
+    const uint16_t* scales;
+    const uint16_t* biases;
+    uint32_t n;
+    uint32_t k;
+} Q35QuantWeight;
+
+/* ------------------------------------------------------------------ KV cache */
+
+#define Q35_KV_BF16 0u
+#define Q35_KV_TURBO8 1u
+#define Q35_KV_TURBO4 2u
+#define Q35_KV_TURBO3 3u
+#define Q35_KV_TURBO2 4u
+#define Q35_KV_BF16K_TURBO4V 5u
+#define Q35_KV_BF16K_TURBO3V 6u
+#define Q35_KV_BF16K_TURBO2V 7u
+
+/* Parses a KV storage-format name as the pages' MetalKvDtype FromStr does
+ * ("bf16", "turbo8", "turbo4", "turbo3", "turbo2", "bf16k_turbo4v",
+ * "bf16k_turbo3v", "bf16k_turbo2v").  Unknown names: Q35_ERR_INVALID_ARG.
+ * Only Q35_KV_BF16 is implemented by the forwards. */
+q35_status q35_kv_dtype_from_str(const char* name, uint32_t* dtype);
+
+/*
+ * Byte sizes of one layer's cache for `max_seq` tokens, per the page's
+ * LayerKvCache::alloc: K data, V data, K scales, V scales (0 where absent).
+ * A turbo format with kv_dim % 16 != 0 is Q35_ERR_INVALID_ARG (the page
+ * asserts).  Host output pointers.
+ */
+q35_status q35_kv_cache_bytes(const Qwen35ForwardConfig* cfg, uint32_t dtype, uint32_t max_seq,
+                              size_t* k_bytes, size_t* v_bytes, size_t* k_scale_bytes,
+                              size_t* v_scale_bytes);
+
+/*
+ * LayerKvCache (mod.rs page): k and v are bf16 [capacity, num_kv_heads, head_dim],
+ * token-major, so row `cache_pos` is one contiguous kv_dim vector.  capacity
+ * is in tokens and IS bounds-checked here.  k_scales / v_scales are unused for
+ * bf16 and must be NULL.
+ */
+typedef struct LayerKvCache {
+    void* k;
+    void* v;
+    uint32_t capacity;
+    uint32_t dtype;
+    void* k_scales;
+    void* v_scales;
+} LayerKvCache;
+
+/* ------------------------------------------------------------------ full-attention layer */
+
+/* FullAttentionLayer (mod.rs page).  Norm weights are bf16 [hidden] (input_ln,
+ * post_ln) and bf16 [head_dim] (q_norm, k_norm).  q_proj is [2*num_heads*head_dim,
+ * hidden] with each head's rows ordered [Q_h | gate_h]; k_proj and v_proj
+ * [kv_dim, hidden]; o_proj [hidden, q_only]; gate_proj and up_proj
+ * [intermediate, hidden]; down_proj [hidden, intermediate]. */
+typedef struct FullAttentionLayer {
+    const uint16_t* input_ln;
+    const uint16_t* q_norm;
+    const uint16_t* k_norm;
+    const uint16_t* post_ln;
+    Q35QuantWeight q_proj;
+    Q35QuantWeight k_proj;
+    Q35QuantWeight v_proj;
+    Q35QuantWeight o_proj;
+    Q35QuantWeight gate_proj;
+    Q35QuantWeight up_proj;
+    Q35QuantWeight down_proj;
+} FullAttentionLayer;
+
+/*
+ * FullAttentionScratch (mod.rs page).  The fused kernels materialise fewer
+ * buffers than the page's sixteen.  Required (fp32 unless noted):
+ *   q_full [q_total], k [kv_dim], v [kv_dim], gated_attn [q_only],
+ *   x_resid [hidden], mlp_act [intermediate] (= silu(gate) * up),
+ *   x_out [hidden] (act dtype),
+ *   workspace (bytes from q35_full_attention_workspace_bytes; the caller
+ *   zero-fills it once after allocation; every call leaves its counters at
+ *   zero again).
+ * Optional taps, written when non-NULL (fp32): x_norm [hidden],
+ *   q_norm_out [q_only] (post-RoPE q), k_norm_out [kv_dim] (post-RoPE k),
+ *   attn_out [q_only], o [hidden], x_norm2 [hidden], gate_act [intermediate],
+ *   up_act [intermediate].
+ */
+typedef struct FullAttentionScratch {
+    float* q_full;
+    float* k;
+    float* v;
+    float* gated_attn;
+    float* x_resid;
+    float* mlp_act;
+    void* x_out;
+    void* workspace;
+    size_t workspace_bytes;
+    float* x_norm;
+    float* q_norm_out;
+    float* k_norm_out;
+    float* attn_out;
+    float* o;
+    float* x_norm2;
+    float* gate_act;
+    float* up_act;
+} FullAttentionScratch;
+
+/* Workspace bytes one full-attention layer needs for caches of `capacity` tokens. */
+q35_status q35_full_attention_workspace_bytes(const Qwen35ForwardConfig* cfg, uint32_t capacity,
+                                              size_t* bytes);
+
+/*
+ * forward_full_attention (full_attention.rs page): one token through one gated
+ * full-attention layer.  x_in (act [hidden]) is the residual stream; the
+ * layer's output residual stream is written to scratch->x_out and *out is set
+ * to that pointer.  Steps: input RMSNorm; q/k/v projections; q/gate split;
+ * per-head RMSNorm of q and k; partial RoPE at positions[0]; append of k (after
+ * RoPE) and v as bf16 at row cache_pos; GQA softmax attention over rows
+ * [0, seq_len_attn); sigmoid output gate; o projection plus residual;
+ * post-attention RMSNorm; SwiGLU MLP plus residual.
+ *   inv_freq: fp32 [rotary_dim/2] (see q35_rope_inv_freq);
+ *   positions: int32 [1], must hold cache_pos (RoPE reads it on the device);
+ *   cache_pos < kv->capacity and seq_len_attn == cache_pos + 1, else
+ *   Q35_ERR_OUT_OF_RANGE; kv->dtype != Q35_KV_BF16: Q35_ERR_UNSUPPORTED.
+ * x_in must not alias any scratch buffer.
+ */
+q35_status q35_forward_full_attention(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                                      const FullAttentionLayer* layer,
+                                      const FullAttentionScratch* scratch, const LayerKvCache* kv,
+                                      const float* inv_freq, const int32_t* positions,
+                                      const void* x_in, uint32_t cache_pos, uint32_t seq_len_attn,
+                                      hipStream_t stream, void** out);
+
+/*
+ * Same as q35_forward_full_attention, but the cache position is read on the
+ * device from positions[0] (seq_len_attn = positions[0] + 1), so one captured
+ * HIP graph replays every decode step.  A device position outside
+ * [0, capacity) skips the append and the attention (the output is then
+ * meaningless but no memory outside the buffers is touched).
+ */
+q35_status q35_forward_full_attention_devpos(const Qwen35Kernels* kernels,
+                                             const Qwen35ForwardConfig* cfg,
+                                             const FullAttentionLayer* layer,
+                                             const FullAttentionScratch* scratch,
+                                             const LayerKvCache* kv, const float* inv_freq,
+                                             const int32_t* positions, const void* x_in,
+                                             hipStream_t stream, void** out);
+
+/* ------------------------------------------------------------------ GDN layer */
+
+/* LinearAttentionLayer (mod.rs page): input_ln, post_ln bf16 [hidden]; a_log fp32
+ * [num_v_heads_lin]; dt_bias bf16 [num_v_heads_lin]; conv1d_weight bf16
+ * [qkv_total_lin, conv_kernel_size]; in_proj_a and in_proj_b [num_v_heads_lin,
+ * hidden]; in_proj_qkv [qkv_total_lin, hidden] with rows [Q | K | V]; in_proj_z
+ * [z_dim_lin, hidden]; norm_weight bf16 [v_head_dim_lin]; out_proj [hidden,
+ * z_dim_lin]; gate_proj, up_proj, down_proj as in the full-attention layer. */
+typedef struct LinearAttentionLayer {
+    const uint16_t* input_ln;
+    const float* a_log;
+    const uint16_t* dt_bias;
+    const uint16_t* conv1d_weight;
+    Q35QuantWeight in_proj_a;
+    Q35QuantWeight in_proj_b;
+    Q35QuantWeight in_proj_qkv;
+    Q35QuantWeight in_proj_z;
+    const uint16_t* norm_weight;
+    Q35QuantWeight out_proj;
+    const uint16_t* post_ln;
+    Q35QuantWeight gate_proj;
+    Q35QuantWeight up_proj;
+    Q35QuantWeight down_proj;
+} LinearAttentionLayer;
+
+/* LinearAttentionState (mod.rs page): conv1d_state fp32 [qkv_total_lin,
+ * conv_kernel_size] (the last conv_kernel_size raw inputs per channel, newest
+ * last) and gdn_state fp32 [num_v_heads_lin, k_head_dim_lin, v_head_dim_lin].
+ * Carried across tokens and updated in place; the caller allocates and zeroes it. */
+typedef struct LinearAttentionState {
+    float* conv1d_state;
+    float* gdn_state;
+} LinearAttentionState;
+
+/*
+ * LinearAttentionScratch (mod.rs page).  Required (fp32):
+ *   qkv_conv [qkv_total_lin] (conv + SiLU output, before the Q/K L2 norm),
+ *   z [z_dim_lin], gate [num_v_heads_lin], beta [num_v_heads_lin],
+ *   y [z_dim_lin], x_resid [hidden], mlp_act [intermediate].
+ * Optional taps, written when non-NULL (fp32 unless noted): x_norm [hidden],
+ *   dt_raw, b_raw [num_v_heads_lin], qkv [qkv_total_lin] (before the conv),
+ *   qkv_smooth [qkv_total_lin] (after conv, SiLU and the Q/K L2 norm),
+ *   y_norm [z_dim_lin], out [hidden], x_norm2 [hidden], gate_act,
+ *   up_act [intermediate], x_final [hidden] (act dtype).
+ */
+typedef struct LinearAttentionScratch {
+    float* qkv_conv;
+    float* z;
+    float* gate;
+    float* beta;
+    float* y;
+    float* x_resid;
+    float* mlp_act;
+    float* x_norm;
+    float* dt_raw;
+    float* b_raw;
+    float* qkv;
+    float* qkv_smooth;
+    float* y_norm;
+    float* out;
+    float* x_norm2;
+    float* gate_act;
+    float* up_act;
+    void* x_final;
+} LinearAttentionScratch;
+
+/* Debug hook (the page's intra_dump): called on the host, after a stream
+ * synchronise, once per named intermediate with a device pointer and an element
+ * count.  Names: gdn_x_norm, gdn_qkv_pre, gdn_qkv_smooth, gdn_y, gdn_y_norm,
+ * gdn_out, gdn_x_resid, gdn_x_final; fp32 buffers except gdn_x_final (act). */
+typedef void (*q35_dump_fn)(void* ctx, const char* name, const void* device_ptr, uint32_t count);
+
+/*
+ * forward_linear_attention (linear_attention.rs page): one token through one
+ * GDN layer.  Steps: input RMSNorm; in_proj a/b/qkv/z projections; causal
+ * depthwise conv update with SiLU; decay gate exp(-exp(A_log) *
+ * softplus(a + dt_bias)) and beta = sigmoid(b); per-head L2 norm of Q and K;
+ * the gated delta-rule recurrence (query scale 1/sqrt(k_head_dim_lin) on the
+ * output); per-head RMSNorm times silu(z); out projection plus residual;
+ * post-attention RMSNorm; SwiGLU MLP plus residual.  The output residual
+ * stream (act [hidden]) is written to x_buf and *out is set to x_buf.
+ * x_buf may alias x_in (every read of x_in precedes the write of x_buf).
+ * When dump != NULL the stream is synchronised and dump is called for the
+ * taps that are non-NULL in scratch.
+ */
+q35_status q35_forward_linear_attention(const Qwen35Kernels* kernels,
+                                        const Qwen35ForwardConfig* cfg,
+                                        const LinearAttentionLayer* layer,
+                                        const LinearAttentionState* state,
+                                        const LinearAttentionScratch* scratch, const void* x_in,
+                                        void* x_buf, hipStream_t stream, q35_dump_fn dump,
+                                        void* dump_ctx, void** out);
+
+/* ------------------------------------------------------------------ stack tail */
+
+/*
+ * Embedding lookup for the caller's layer loop: x_out (act [hidden]) =
+ * table[tokens[0]] where table is bf16 [vocab, hidden].  tokens: int32 [1].
+ * A token outside [0, vocab) writes zeros.
+ */
+q35_status q35_embed_lookup(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                            const uint16_t* table, const int32_t* tokens, void* x_out,
+                            hipStream_t stream);
+
+/* Workspace bytes q35_lm_head_argmax needs (zero-filled once by the caller). */
+q35_status q35_lm_head_workspace_bytes(const Qwen35ForwardConfig* cfg, size_t* bytes);
+
+/*
+ * Caller-owned tail of a decode step: h = RMSNorm(x; final_norm) (x act
+ * [hidden], final_norm bf16 [hidden]); logits = lm_head h (lm_head
+ * [vocab, hidden]); tokens[0] = argmax (lowest index on ties).  Optional
+ * (may be NULL): logits fp32 [vocab]; history int32 [history_len], which
+ * receives the token at index positions[0] - history_base when that lies in
+ * range; positions int32 [1], incremented by one after the token is chosen;
+ * embed_table bf16 [vocab, hidden] with x_next act [hidden], which then
+ * receives the chosen token's embedding (the next step's input).
+ */
+q35_status q35_lm_head_argmax(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                              const uint16_t* final_norm, const Q35QuantWeight* lm_head,
+                              const void* x, float* logits, void* workspace,
+                              size_t workspace_bytes, int32_t* tokens, int32_t* positions,
+                              int32_t* history, uint32_t history_len, int32_t history_base,
+                              const uint16_t* embed_table, void* x_next, hipStream_t stream);
+
+/* ------------------------------------------------------------------ kernel-level export */
+
+/*
+ * The first half of the MLP shared by both layer forwards, as one launch:
+ * xn2 = RMSNorm(x_resid; post_ln), then gate_proj and up_proj over the same
+ * xn2 (the pages' `gemv_gate_up_with`), and mlp_act = silu(gate) * up (the
+ * product the pages' `gemv_silu_gate_resid` consumes).  x_resid fp32 [hidden],
+ * post_ln bf16 [hidden], gate_proj / up_proj [intermediate, hidden], mlp_act
+ * fp32 [intermediate].  This is the largest kernel of a layer; it is exported
+ * so that it can be timed on its own.
+ */
+q35_status q35_gate_up_swiglu(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                              const uint16_t* post_ln, const Q35QuantWeight* gate_proj,
+                              const Q35QuantWeight* up_proj, const float* x_resid,
+                              float* mlp_act, hipStream_t stream);
+
+/*
+ * Plain GEMV with the library's quantised-weight kernel: y (fp32 [w->n]) =
+ * W x (x fp32 [w->k]).  With x a one-hot vector e_j, y is column j of the
+ * dequantised matrix, bit for bit.
+ */
+q35_status q35_gemv(const Qwen35Kernels* kernels, const Q35QuantWeight* w, const float* x,
+                    float* y, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q35DECODE_H */

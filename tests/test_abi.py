@@ -1,0 +1,192 @@
+"""The C-ABI library loads, exports what include/q35decode.h declares, and its
+host-side logic (config validation, sizes, error paths) behaves.  No compute
+call is made: every call here fails validation before any HIP work."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from hybrid_decode_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q35decode.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+FAKE_KERNELS = 0x1000  # a non-NULL handle: only the argument checks run before it would be used
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from hybrid_decode_amd import build
+    if build.is_stale():
+        build.build(verbose=False)
+    return B.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(q35_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    decl = declared_functions()
+    assert decl == sorted(B.EXPORTS)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_preset_matches_pages(lib):
+    gold = json.load(open(os.path.join(GOLDEN, "qwen35_4b_preset.json")))
+    c = B.q35_config_qwen3_5_4b()
+    for k, v in gold.items():
+        if k in ("source", "derived"):
+            continue
+        assert getattr(c, k) == pytest.approx(v), k
+    assert c.act_dtype == B.Q35_ACT_BF16
+    B.q35_config_validate(c)
+
+
+def test_struct_sizes_match_header_layout(lib):
+    # 17 4-byte fields; the quantised-weight struct is 3 pointers + 2 u32
+    assert ctypes.sizeof(B.Qwen35ForwardConfig) == 17 * 4
+    assert ctypes.sizeof(B.Q35QuantWeight) == 32
+    assert ctypes.sizeof(B.LayerKvCache) == 40
+
+
+def test_tiny_config_validates(lib):
+    from hybrid_decode_amd.runtime import cfg_struct
+    B.q35_config_validate(cfg_struct(synth.tiny("f32")))
+    B.q35_config_validate(cfg_struct(synth.tiny("bf16")))
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("group_size", 32, B.Q35_ERR_UNSUPPORTED),
+    ("num_kv_heads", 3, B.Q35_ERR_INVALID_ARG),
+    ("head_dim", 96, B.Q35_ERR_UNSUPPORTED),
+    ("rotary_dim", 63, B.Q35_ERR_INVALID_ARG),
+    ("rotary_dim", 512, B.Q35_ERR_INVALID_ARG),
+    ("num_v_heads_lin", 24, B.Q35_ERR_INVALID_ARG),
+    ("v_head_dim_lin", 64, B.Q35_ERR_UNSUPPORTED),
+    ("conv_kernel_size", 3, B.Q35_ERR_UNSUPPORTED),
+    ("act_dtype", 7, B.Q35_ERR_INVALID_ARG),
+    ("hidden", 2500, B.Q35_ERR_INVALID_ARG),
+    ("intermediate", 9280, B.Q35_ERR_UNSUPPORTED),
+    ("rms_eps", 0.0, B.Q35_ERR_INVALID_ARG),
+])
+def test_config_validation_errors(lib, field, value, status):
+    c = B.q35_config_qwen3_5_4b()
+    setattr(c, field, value)
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_config_validate(c)
+    assert e.value.status == status
+    assert B.q35_last_error()
+
+
+def test_kv_dtype_names(lib):
+    gold = json.load(open(os.path.join(GOLDEN, "kv_cache_formats.json")))
+    for i, name in enumerate(gold["names"]):
+        assert B.q35_kv_dtype_from_str(name) == i
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_kv_dtype_from_str("fp8")
+    assert e.value.status == B.Q35_ERR_INVALID_ARG
+    assert "fp8" in str(e.value)
+
+
+def test_kv_cache_bytes_follow_the_alloc_table(lib):
+    c = B.q35_config_qwen3_5_4b()
+    n = 100 * 1024  # max_seq 100, kv_dim 1024
+    expect = {  # (k, v, k_scales, v_scales) per the page's LayerKvCache::alloc table
+        "bf16": (2 * n, 2 * n, 0, 0), "turbo8": (n, n, n // 8, n // 8),
+        "turbo4": (n // 2, n // 2, n // 16, n // 16), "turbo3": (n * 3 // 8, n * 3 // 8, n // 16, n // 16),
+        "turbo2": (n // 4, n // 4, n // 16, n // 16), "bf16k_turbo4v": (2 * n, n // 2, 0, n // 16),
+        "bf16k_turbo3v": (2 * n, n * 3 // 8, 0, n // 16), "bf16k_turbo2v": (2 * n, n // 4, 0, n // 16),
+    }
+    for name, sizes in expect.items():
+        assert B.q35_kv_cache_bytes(c, B.q35_kv_dtype_from_str(name), 100) == sizes, name
+    c.num_kv_heads, c.head_dim = 1, 8  # kv_dim 8: not a multiple of 16
+    with pytest.raises(B.Q35Error):
+        B.q35_kv_cache_bytes(c, 1, 4)
+    assert B.q35_kv_cache_bytes(c, 0, 4) == (64, 64, 0, 0)
+
+
+def test_workspace_sizes_grow_with_capacity(lib):
+    c = B.q35_config_qwen3_5_4b()
+    a = B.q35_full_attention_workspace_bytes(c, 4096)
+    b = B.q35_full_attention_workspace_bytes(c, 1 << 20)
+    assert 0 < a <= b
+    assert B.q35_lm_head_workspace_bytes(c) > 0
+
+
+def test_rope_inv_freq_matches_oracle(lib):
+    c = B.q35_config_qwen3_5_4b()
+    assert np.array_equal(B.q35_rope_inv_freq(c), O.rope_inv_freq(1e7, 64))
+
+
+def test_resolve_without_gpu_reports_no_device(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_kernels_resolve(0)
+    assert e.value.status == B.Q35_ERR_NO_DEVICE
+
+
+def _full_args(cap=16):
+    c = B.q35_config_qwen3_5_4b()
+    layer = B.FullAttentionLayer()
+    scratch = B.FullAttentionScratch()
+    kv = B.LayerKvCache(0x10000, 0x20000, cap, 0, None, None)
+    return c, layer, scratch, kv
+
+
+def test_forward_errors_before_any_launch(lib):
+    c, layer, scratch, kv = _full_args()
+    # NULL kernel handle
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_forward_full_attention(None, c, layer, scratch, kv, 0x100, 0x100, 0x100, 3, 4, None)
+    assert e.value.status == B.Q35_ERR_INVALID_ARG
+    # cache position beyond capacity, and a sequence length that is not cache_pos + 1
+    for pos, L in ((16, 17), (3, 5), (3, 3)):
+        with pytest.raises(B.Q35Error) as e:
+            B.q35_forward_full_attention(FAKE_KERNELS, c, layer, scratch, kv, 0x100, 0x100, 0x100,
+                                         pos, L, None)
+        assert e.value.status == B.Q35_ERR_OUT_OF_RANGE, (pos, L)
+    # a turbo cache is parsed but not implemented
+    kv.dtype = B.q35_kv_dtype_from_str("turbo8")
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_forward_full_attention(FAKE_KERNELS, c, layer, scratch, kv, 0x100, 0x100, 0x100, 3, 4, None)
+    assert e.value.status == B.Q35_ERR_UNSUPPORTED
+    # valid position but NULL weights
+    kv.dtype = 0
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_forward_full_attention(FAKE_KERNELS, c, layer, scratch, kv, 0x100, 0x100, 0x100, 3, 4, None)
+    assert e.value.status == B.Q35_ERR_INVALID_ARG
+
+
+def test_linear_attention_errors_before_any_launch(lib):
+    c = B.q35_config_qwen3_5_4b()
+    layer, state, scratch = B.LinearAttentionLayer(), B.LinearAttentionState(), B.LinearAttentionScratch()
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_forward_linear_attention(FAKE_KERNELS, c, layer, state, scratch, 0x100, 0x100, None)
+    assert e.value.status == B.Q35_ERR_INVALID_ARG
+    # misaligned activation pointer
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_forward_linear_attention(FAKE_KERNELS, c, layer, state, scratch, 0x104, 0x100, None)
+    assert "aligned" in str(e.value)
+
+
+def test_gemv_shape_errors(lib):
+    w = B.Q35QuantWeight(0x1000, 0x2000, 0x3000, 3, 2560)  # 3 rows: not a multiple of 2 at K=2560
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_gemv(FAKE_KERNELS, w, 0x100, 0x100, None)
+    assert e.value.status == B.Q35_ERR_UNSUPPORTED
+    w = B.Q35QuantWeight(0x1000, 0x2000, 0x3000, 4, 2496)
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_gemv(FAKE_KERNELS, w, 0x100, 0x100, None)
+    assert e.value.status == B.Q35_ERR_UNSUPPORTED
