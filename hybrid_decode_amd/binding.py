@@ -148,7 +148,7 @@ def lib():
                                         vp, sz, vp, vp, vp, u32, i32, vp, vp, vp]),
             "q35_gate_up_swiglu": (st, [vp, P(Qwen35ForwardConfig), vp, P(Q35QuantWeight),
                                         P(Q35QuantWeight), vp, vp, vp]),
-            "q35_gemv": (st, [vp, P(Q35QuantWeight), vp, vp, vp]),
+            "q35_gemv": (st, [vp, P(Q35QuantWeight), vp, vp, u32, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -266,5 +266,5 @@ def q35_gate_up_swiglu(kernels, cfg, post_ln, gate_proj, up_proj, x_resid, mlp_a
                                     C.byref(up_proj), x_resid, mlp_act, stream))
 
 
-def q35_gemv(kernels, w, x, y, stream) -> None:
-    _check(lib().q35_gemv(kernels, C.byref(w), x, y, stream))
+def q35_gemv(kernels, w, x, y, act_dtype, stream) -> None:
+    _check(lib().q35_gemv(kernels, C.byref(w), x, y, act_dtype, stream))

@@ -1,21 +1,28 @@
 // Gated GQA decode attention over a bf16 KV cache (gfx950), one token.
 //
-// Fuses the middle of the pages' full-attention forward (full_attention.rs
+// Covers the middle of the pages' full-attention forward (full_attention.rs
 // page: the q/gate split, the per-head q/k RMSNorm, partial RoPE, the KV
-// append and `attention_decode`, then the `sigmoid_gate` launch):
-//     q_h  = RoPE(RMSNorm(q_full[h, :D]; q_norm))        h in the kv group
+// append, `attention_decode`, then the `sigmoid_gate` launch):
+//     q_h  = RoPE(RMSNorm(q_full[h, :D]; q_norm))        h in kv group g
 //     k    = RoPE(RMSNorm(k_g; k_norm)),  v = v_g         appended as bf16 at row pos
 //     s_t  = q_h . K[t, g] / sqrt(D),  p = softmax(s),  a_h = sum_t p_t V[t, g]
 //     out  = a_h * sigmoid(q_full[h, D:])
-// Grid: (chunk of positions, kv head g).  One block reads each K/V row of its
-// chunk once for all G = Hq/Hkv query heads of the group (the GQA reuse), and
-// writes a partial (max, sum, unnormalised output) per head.  The last block
-// of each kv head to finish (an atomic ticket) merges the partials with the
-// usual log-sum-exp rescaling and applies the sigmoid gate, then resets the
-// ticket to zero so the next call (or graph replay) starts clean.
 //
-// Layouts: K/V caches bf16 [capacity, Hkv, D] (token-major); a lane holds 8
-// consecutive dims (one 16-byte load), D/8 lanes cover one row.
+// Two launches, no inter-block synchronisation inside either (an agent-scope
+// fence per block costs an L2 write-back per XCD on this part):
+//   attn_partial_kernel  grid (chunk of positions, kv head g), 256 threads.
+//       The first batch of K/V row loads is issued before anything else (it
+//       does not depend on this token), then the block builds the G query
+//       heads of its group and the new key in LDS; the block whose chunk holds
+//       `pos` also stores the new K/V row.  A row of the cache is D/8 lanes
+//       (16 bytes each); the block's row slots each run an online softmax over
+//       their rows (base-2 exponent), then merge in LDS and the block writes
+//       one (max, sum, unnormalised output) triple per query head.  Each K/V
+//       row is read once for all G heads of its group (the GQA reuse).
+//   attn_merge_kernel    grid (q head, D/64), 256 threads: log-sum-exp merge
+//       of the chunk partials, the division by the total, the sigmoid gate.
+//
+// Layouts: K/V caches bf16 [capacity, Hkv, D] (token-major).
 #include "q35_device.h"
 #include "q35_internal.h"
 
@@ -23,12 +30,14 @@ namespace q35 {
 namespace {
 
 constexpr int kNT = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 4;                    // rows per row slot per batch
+constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
 struct AGeo {
-    static constexpr int LPR = D / 8;        // lanes per cache row
-    static constexpr int RPI = kNT / LPR;    // rows per block iteration
+    static constexpr int LPR = D / 8;         // lanes per cache row
+    static constexpr int RPI = kNT / LPR;     // row slots per block
+    static constexpr int B = RPI * kUnroll;   // rows per batch
 };
 
 Q35_DEV void unpack8(const uint4& u, float v[8]) {
@@ -42,10 +51,14 @@ Q35_DEV void unpack8(const uint4& u, float v[8]) {
     v[7] = bf16_hi(u.w);
 }
 
+Q35_DEV int32_t attn_pos(const AttnArgs& a) {
+    return a.host_pos >= 0 ? a.host_pos : a.positions[0];
+}
+
 template <int D, int G>
-__global__ __launch_bounds__(kNT) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     using Geo = AGeo<D>;
-    constexpr int LPR = Geo::LPR, RPI = Geo::RPI;
+    constexpr int LPR = Geo::LPR, RPI = Geo::RPI, B = Geo::B;
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     const int j = t % LPR;   // dim slice [8j, 8j+8)
     const int rs = t / LPR;  // row slot
@@ -53,15 +66,13 @@ __global__ __launch_bounds__(kNT) void attn_kernel(AttnArgs a) {
     const uint32_t c = blockIdx.x;
     const uint32_t T = a.chunk;
 
-    extern __shared__ float smem[];
-    float* qs = smem;                       // [G+1][D]: q heads, then k
-    float* vn = qs + (G + 1) * D;           // [D] new v (bf16-rounded)
-    float* rsq = vn + D;                    // [G+1] rms factors
-    float* ml = rsq + (G + 1);              // [G][2] max, sum
-    float* sc = ml + 2 * G + 2;             // union: [G][T] scores, or [RPI][G][D] partial outputs
-    __shared__ int last_flag;
+    __shared__ float qs[(G + 1) * D];  // q heads of the group, then the new k
+    __shared__ float vn[D];            // new v, bf16-rounded
+    __shared__ float rsq[G + 1];
+    __shared__ float mls[RPI][2 * G];  // per-slot (max, sum)
+    __shared__ float red[RPI * D];     // per-slot outputs of one head
 
-    const int32_t pos = a.host_pos >= 0 ? a.host_pos : a.positions[0];
+    const int32_t pos = attn_pos(a);
     if (pos < 0 || (uint32_t)pos >= a.capacity) return;
     const uint32_t L = (uint32_t)pos + 1;
     const uint32_t nch = (L + T - 1) / T;
@@ -70,6 +81,24 @@ __global__ __launch_bounds__(kNT) void attn_kernel(AttnArgs a) {
     const uint32_t t1 = min(t0 + T, L);
     const bool has_new = (uint32_t)pos >= t0 && (uint32_t)pos < t1;
     const int32_t rope_pos = a.positions[0];
+
+    // ---------------- first batch of K/V loads, in flight during the prologue
+    const uint32_t row_bytes = a.hkv * D * 2u;
+    const uint32_t span = (t1 - t0) * row_bytes;
+    const auto rk = rsrc(a.kc + ((size_t)t0 * a.hkv + g) * D, span);
+    const auto rv = rsrc(a.vc + ((size_t)t0 * a.hkv + g) * D, span);
+    uint4 kr[kUnroll], vr[kUnroll];
+    auto load_batch = [&](uint32_t tb) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t tt = tb + u * RPI + rs;
+            const bool live = tt < t1 && tt != (uint32_t)pos;
+            const uint32_t off = live ? (tt - t0) * row_bytes + 16u * j : span;  // past the end: zero
+            kr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kAuxStream));
+            vr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, kAuxStream));
+        }
+    };
+    load_batch(t0);
 
     // ---------------- prologue: q heads of this group and the new k, v
     for (int e = t; e < (G + 1) * D; e += kNT) {
@@ -115,34 +144,33 @@ __global__ __launch_bounds__(kNT) void attn_kernel(AttnArgs a) {
             const uint32_t kb = f32_to_bf16(qs[G * D + d]);
             krow[d] = (uint16_t)kb;
             vrow[d] = (uint16_t)f32_to_bf16(a.v[g * D + d]);
-            qs[G * D + d] = bf16_to_f32(kb);  // the row this block attends to is the stored one
+            qs[G * D + d] = bf16_to_f32(kb);  // attend to the row as stored
         }
         __syncthreads();
     }
 
-    // ---------------- pass 1: scores for rows [t0, t1)
+    // ---------------- batches of B rows: scores, online softmax, p V
     float qr[G][8];
 #pragma unroll
     for (int i = 0; i < G; ++i)
 #pragma unroll
         for (int e = 0; e < 8; ++e) qr[i][e] = qs[i * D + 8 * j + e];
+    const float sscale = a.scale * kLog2e;  // scores in the base-2 exponent domain
 
-    const size_t row_stride = (size_t)a.hkv * D;
-    const uint16_t* kbase = a.kc + (size_t)g * D + 8 * j;
-    const uint16_t* vbase = a.vc + (size_t)g * D + 8 * j;
+    float m[G], l[G], acc[G][8];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        m[i] = -INFINITY;
+        l[i] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+    }
 
-    for (uint32_t tb = t0 + rs; tb < t1; tb += RPI * kUnroll) {
-        uint4 kr[kUnroll];
+    for (uint32_t tb = t0;;) {
+        float s[kUnroll][G];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t tt = tb + u * RPI;
-            kr[u] = make_uint4(0u, 0u, 0u, 0u);
-            if (tt < t1 && tt != (uint32_t)pos)
-                kr[u] = *reinterpret_cast<const uint4*>(kbase + (size_t)tt * row_stride);
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t tt = tb + u * RPI;
+            const uint32_t tt = tb + u * RPI + rs;
             float kv[8];
             if (tt == (uint32_t)pos) {
 #pragma unroll
@@ -152,55 +180,30 @@ __global__ __launch_bounds__(kNT) void attn_kernel(AttnArgs a) {
             }
 #pragma unroll
             for (int i = 0; i < G; ++i) {
-                float s = 0.f;
+                float d = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) s = fmaf(qr[i][e], kv[e], s);
-                s = group_sum_last<LPR>(s);
-                if (j == LPR - 1 && tt < t1) sc[i * T + (tt - t0)] = s * a.scale;
+                for (int e = 0; e < 8; ++e) d = fmaf(qr[i][e], kv[e], d);
+                d = group_sum_all<LPR>(d);
+                s[u][i] = tt < t1 ? d * sscale : -INFINITY;
             }
         }
-    }
-    __syncthreads();
-
-    // ---------------- softmax over the chunk, per head
-    const uint32_t n = t1 - t0;
-    for (int i = wid; i < G; i += kNT / 64) {
-        float m = -INFINITY;
-        for (uint32_t e = lane; e < n; e += 64) m = fmaxf(m, sc[i * T + e]);
-        m = wave_max(m);
-        float l = 0.f;
-        for (uint32_t e = lane; e < n; e += 64) {
-            const float p = expf(sc[i * T + e] - m);
-            sc[i * T + e] = p;
-            l += p;
-        }
-        l = wave_sum(l);
-        if (lane == 0) {
-            ml[2 * i] = m;
-            ml[2 * i + 1] = l;
-        }
-    }
-    __syncthreads();
-
-    // ---------------- pass 2: unnormalised p V
-    float acc[G][8];
 #pragma unroll
-    for (int i = 0; i < G; ++i)
+        for (int i = 0; i < G; ++i) {
+            float mx = m[i];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
-    for (uint32_t tb = t0 + rs; tb < t1; tb += RPI * kUnroll) {
-        uint4 vr[kUnroll];
+            for (int u = 0; u < kUnroll; ++u) mx = fmaxf(mx, s[u][i]);
+            const float mref = mx == -INFINITY ? 0.f : mx;  // slot with no rows yet
+            const float corr = exp2f(m[i] - mref);
+            m[i] = mx;
+            l[i] *= corr;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t tt = tb + u * RPI;
-            vr[u] = make_uint4(0u, 0u, 0u, 0u);
-            if (tt < t1 && tt != (uint32_t)pos)
-                vr[u] = *reinterpret_cast<const uint4*>(vbase + (size_t)tt * row_stride);
+            for (int e = 0; e < 8; ++e) acc[i][e] *= corr;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) s[u][i] = exp2f(s[u][i] - mref);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t tt = tb + u * RPI;
-            if (tt >= t1) break;
+            const uint32_t tt = tb + u * RPI + rs;
             float vv[8];
             if (tt == (uint32_t)pos) {
 #pragma unroll
@@ -210,84 +213,107 @@ __global__ __launch_bounds__(kNT) void attn_kernel(AttnArgs a) {
             }
 #pragma unroll
             for (int i = 0; i < G; ++i) {
-                const float p = sc[i * T + (tt - t0)];
+                l[i] += s[u][i];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(p, vv[e], acc[i][e]);
+                for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(s[u][i], vv[e], acc[i][e]);
             }
         }
+        tb += B;
+        if (tb >= t1) break;
+        load_batch(tb);
     }
-    __syncthreads();  // everyone is done with the probabilities: reuse sc
+
+    // ---------------- merge the row slots, write this chunk's partials
+    if (j == 0)
 #pragma unroll
-    for (int i = 0; i < G; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sc[(rs * G + i) * D + 8 * j + e] = acc[i][e];
-    __syncthreads();
-
-    float* pacc = a.part_acc + ((size_t)g * a.max_chunks + c) * G * D;
-    for (int e = t; e < G * D; e += kNT) {
-        float s = 0.f;
-#pragma unroll 4
-        for (int r = 0; r < RPI; ++r) s += sc[r * G * D + e];
-        pacc[e] = s;
-    }
-    if (t < 2 * G) a.part_ml[((size_t)g * a.max_chunks + c) * 2 * G + t] = ml[t];
-
-    // ---------------- last block of this kv head merges the partials
-    __threadfence();
-    __syncthreads();
-    if (t == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(a.counters + g, 1u, __ATOMIC_ACQ_REL,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        last_flag = (prev == nch - 1);
-    }
-    __syncthreads();
-    if (!last_flag) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-
-    // per (chunk, head) weights exp(m_c - M) in sc[c*G + i]; M and the total in ml
-    const float* pml = a.part_ml + (size_t)g * a.max_chunks * 2 * G;
-    for (int i = wid; i < G; i += kNT / 64) {
-        float m = -INFINITY;
-        for (uint32_t cc = lane; cc < nch; cc += 64) m = fmaxf(m, pml[cc * 2 * G + 2 * i]);
-        m = wave_max(m);
-        float l = 0.f;
-        for (uint32_t cc = lane; cc < nch; cc += 64) {
-            const float w = expf(pml[cc * 2 * G + 2 * i] - m);
-            sc[cc * G + i] = w;
-            l = fmaf(w, pml[cc * 2 * G + 2 * i + 1], l);
+        for (int i = 0; i < G; ++i) {
+            mls[rs][2 * i] = m[i];
+            mls[rs][2 * i + 1] = l[i];
         }
-        l = wave_sum(l);
-        if (lane == 0) rsq[i] = 1.0f / l;
-    }
     __syncthreads();
-    const float* pa = a.part_acc + (size_t)g * a.max_chunks * G * D;
-    for (int e = t; e < G * D; e += kNT) {
-        const int i = e / D, d = e % D;
-        float o = 0.f;
-        for (uint32_t cc = 0; cc < nch; ++cc) o = fmaf(sc[cc * G + i], pa[(size_t)cc * G * D + e], o);
-        o *= rsq[i];
-        const uint32_t h = g * G + i;
+    float* pacc = a.part_acc + ((size_t)g * a.max_chunks + c) * G * D;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        float M = -INFINITY;
+        for (int r = 0; r < RPI; ++r) M = fmaxf(M, mls[r][2 * i]);  // slot 0 always has a row
+        const float w = exp2f(m[i] - M);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[rs * D + 8 * j + e] = acc[i][e] * w;
+        __syncthreads();
+        for (int d = t; d < D; d += kNT) {
+            float o = 0.f;
+#pragma unroll 8
+            for (int r = 0; r < RPI; ++r) o += red[r * D + d];
+            pacc[i * D + d] = o;
+        }
+        if (t == 0) {
+            float tot = 0.f;
+            for (int r = 0; r < RPI; ++r) tot = fmaf(exp2f(mls[r][2 * i] - M), mls[r][2 * i + 1], tot);
+            float* pml = a.part_ml + ((size_t)g * a.max_chunks + c) * 2 * G;
+            pml[2 * i] = M;
+            pml[2 * i + 1] = tot;
+        }
+        __syncthreads();
+    }
+}
+
+// grid (Hq, D/64); thread t: dim d0 + (t & 63), chunk lane t >> 6.
+template <int D, int G>
+__global__ __launch_bounds__(kNT) void attn_merge_kernel(AttnArgs a) {
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const uint32_t h = blockIdx.x, g = h / G, i = h % G;
+    const uint32_t d = blockIdx.y * 64 + lane;
+    extern __shared__ float wsh[];  // [max_chunks] chunk weights
+    __shared__ float red[kNT];
+    __shared__ float stat[kNT / 64];
+
+    const int32_t pos = attn_pos(a);
+    if (pos < 0 || (uint32_t)pos >= a.capacity) return;
+    const uint32_t nch = ((uint32_t)pos + a.chunk) / a.chunk;
+    const float* pml = a.part_ml + (size_t)g * a.max_chunks * 2 * G + 2 * i;
+
+    float mx = -INFINITY;
+    for (uint32_t cc = t; cc < nch; cc += kNT) mx = fmaxf(mx, pml[cc * 2 * G]);
+    mx = wave_max(mx);
+    if (lane == 0) red[wid] = mx;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float tot = 0.f;
+    for (uint32_t cc = t; cc < nch; cc += kNT) {
+        const float w = exp2f(pml[cc * 2 * G] - M);
+        wsh[cc] = w;
+        tot = fmaf(w, pml[cc * 2 * G + 1], tot);
+    }
+    tot = block_sum<kNT>(tot, stat);  // its barriers also publish wsh
+
+    const float* pa = a.part_acc + ((size_t)g * a.max_chunks * G + i) * D + d;
+    float o = 0.f;
+#pragma unroll 8
+    for (uint32_t cc = wid; cc < nch; cc += kNT / 64) o = fmaf(wsh[cc], pa[(size_t)cc * G * D], o);
+    red[t] = o;
+    __syncthreads();
+    if (wid == 0) {
+        o = (red[lane] + red[lane + 64]) + (red[lane + 128] + red[lane + 192]);
+        o /= tot;
         if (a.attn_out) a.attn_out[h * D + d] = o;
         const float gate = a.q_full[(size_t)h * 2 * D + D + d];
         a.gated_attn[h * D + d] = o * sigmoidf_(gate);
     }
-    if (t == 0) __hip_atomic_store(a.counters + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int G>
 hipError_t launch_t(const AttnArgs& a, uint32_t grid_chunks, hipStream_t stream) {
-    constexpr int RPI = AGeo<D>::RPI;
-    size_t uni = (size_t)G * a.chunk;
-    if ((size_t)RPI * G * D > uni) uni = (size_t)RPI * G * D;
-    if ((size_t)a.max_chunks * G > uni) uni = (size_t)a.max_chunks * G;
-    const size_t lds = ((G + 1) * D + D + (G + 1) + 2 * G + 2 + uni) * sizeof(float);
-    hipLaunchKernelGGL((attn_kernel<D, G>), dim3(grid_chunks, a.hkv), dim3(kNT), lds, stream, a);
+    hipLaunchKernelGGL((attn_partial_kernel<D, G>), dim3(grid_chunks, a.hkv), dim3(kNT), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_merge_kernel<D, G>), dim3(a.hq, D / 64), dim3(kNT),
+                       (size_t)a.max_chunks * sizeof(float), stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-uint32_t attn_rows_per_iter(uint32_t head_dim) { return kNT / (head_dim / 8); }
+uint32_t attn_rows_per_iter(uint32_t head_dim) { return (kNT / (head_dim / 8)) * kUnroll; }
 
 #define Q35_ATTN_SHAPES(X) \
     X(64, 1) X(64, 2) X(64, 4) X(64, 8) X(128, 1) X(128, 2) X(128, 4) X(128, 8) \
@@ -311,7 +337,15 @@ hipError_t attn_launch(uint32_t head_dim, uint32_t group, const AttnArgs& a, uin
 
 const void* attn_kernel_ptr(uint32_t head_dim, uint32_t group) {
 #define X(DD, GG) \
-    if (head_dim == DD && group == GG) return (const void*)&attn_kernel<DD, GG>;
+    if (head_dim == DD && group == GG) return (const void*)&attn_partial_kernel<DD, GG>;
+    Q35_ATTN_SHAPES(X)
+#undef X
+    return nullptr;
+}
+
+const void* attn_combine_kernel_ptr(uint32_t head_dim, uint32_t group) {
+#define X(DD, GG) \
+    if (head_dim == DD && group == GG) return (const void*)&attn_merge_kernel<DD, GG>;
     Q35_ATTN_SHAPES(X)
 #undef X
     return nullptr;

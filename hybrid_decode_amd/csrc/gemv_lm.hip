@@ -1,0 +1,39 @@
+// GEMV instantiations: kOpLmHead.
+#include "gemv_core.h"
+
+namespace q35 {
+
+hipError_t gemv_launch_lm(int op, uint32_t k, bool half, bool xreg, const GemvArgs& a,
+                          uint32_t blocks, hipStream_t stream) {
+    (void)xreg;
+    if (op == kOpLmHead) {
+#define X(KK)                                                                                   \
+        if (k == KK) {                                                                          \
+            if (xreg) return half ? gemv::launch_t<KK, kOpLmHead, true, true>(a, blocks, stream)     \
+                                  : gemv::launch_t<KK, kOpLmHead, false, true>(a, blocks, stream);   \
+            return half ? gemv::launch_t<KK, kOpLmHead, true, false>(a, blocks, stream)              \
+                        : gemv::launch_t<KK, kOpLmHead, false, false>(a, blocks, stream);            \
+        }
+        Q35_W_HIDDEN(X)
+#undef X
+    }
+    return hipErrorInvalidValue;
+}
+
+const void* gemv_ptr_lm(int op, uint32_t k, bool half, bool xreg) {
+    (void)xreg;
+    if (op == kOpLmHead) {
+#define X(KK)                                                                                   \
+        if (k == KK) {                                                                          \
+            if (xreg) return half ? gemv::kernel_ptr_t<KK, kOpLmHead, true, true>()                  \
+                                  : gemv::kernel_ptr_t<KK, kOpLmHead, false, true>();                \
+            return half ? gemv::kernel_ptr_t<KK, kOpLmHead, true, false>()                           \
+                        : gemv::kernel_ptr_t<KK, kOpLmHead, false, false>();                         \
+        }
+        Q35_W_HIDDEN(X)
+#undef X
+    }
+    return nullptr;
+}
+
+}  // namespace q35

@@ -61,8 +61,8 @@ uint32_t qkv_total(const Qwen35ForwardConfig& c) {
     return 2 * c.num_k_heads_lin * c.k_head_dim_lin + z_dim(c);
 }
 
-q35_status check_rows(const char* what, uint32_t rows, uint32_t k) {
-    const int r = gemv_rows_per_matrix_group(k);
+q35_status check_rows(const char* what, uint32_t rows, uint32_t k, bool paired = false) {
+    const int r = gemv_rows_per_matrix_group(k, paired);
     if (rows == 0 || rows % (uint32_t)r != 0)
         return fail(Q35_ERR_UNSUPPORTED, "%s: %u rows is not a multiple of %d (rows per wave group at K=%u)",
                     what, rows, r, k);
@@ -90,7 +90,7 @@ q35_status opt(const void* p, const char* what) {
 
 // Attention split-K geometry: positions per block for a cache length n, and
 // the number of per-chunk partial slots a workspace must hold for a capacity.
-constexpr uint32_t kAttnTargetBlocks = 256;
+constexpr uint32_t kAttnTargetBlocks = 512;
 constexpr uint32_t kAttnMaxChunk = 2048;
 
 uint32_t attn_chunk(const Qwen35ForwardConfig& c, uint32_t n) {
@@ -109,7 +109,7 @@ uint32_t attn_max_chunks(const Qwen35ForwardConfig& c, uint32_t capacity) {
 }
 
 struct AttnWs {
-    size_t acc_off, ml_off, cnt_off, total;
+    size_t acc_off, ml_off, total;
 };
 
 AttnWs attn_ws_layout(const Qwen35ForwardConfig& c, uint32_t capacity) {
@@ -118,38 +118,37 @@ AttnWs attn_ws_layout(const Qwen35ForwardConfig& c, uint32_t capacity) {
     AttnWs w;
     w.acc_off = 0;
     w.ml_off = (mc * c.num_kv_heads * G * c.head_dim * sizeof(float) + 255) & ~size_t(255);
-    w.cnt_off = w.ml_off + ((mc * c.num_kv_heads * 2 * G * sizeof(float) + 255) & ~size_t(255));
-    w.total = w.cnt_off + 256;
+    w.total = w.ml_off + ((mc * c.num_kv_heads * 2 * G * sizeof(float) + 255) & ~size_t(255));
     return w;
 }
 
 struct LmWs {
-    size_t val_off, idx_off, cnt_off, total;
+    size_t val_off, idx_off, total;
     uint32_t blocks;
 };
 
 LmWs lm_ws_layout(const Qwen35ForwardConfig& c) {
     LmWs w;
-    const uint32_t r = (uint32_t)gemv_rows_per_matrix_group(c.hidden);
+    const uint32_t r = (uint32_t)gemv_rows_per_matrix_group(c.hidden, false);
     w.blocks = gemv_pick_blocks(c.vocab / r);
     w.val_off = 0;
     w.idx_off = ((size_t)w.blocks * 4 + 255) & ~size_t(255);
-    w.cnt_off = w.idx_off + (((size_t)w.blocks * 4 + 255) & ~size_t(255));
-    w.total = w.cnt_off + 256;
+    w.total = w.idx_off + (((size_t)w.blocks * 4 + 255) & ~size_t(255));
     return w;
 }
 
 // A GEMV launch under construction: segments over one shared x.
 struct GemvBuild {
     GemvArgs a;
+    int op;
     uint32_t k;
     bool paired;
     uint32_t r;  // rows of one matrix per row group
 
-    GemvBuild(uint32_t k_, bool paired_, bool act_f32) : k(k_), paired(paired_) {
+    GemvBuild(int op_, uint32_t k_, bool act_f32) : op(op_), k(k_), paired(op_ == kOpGateUp) {
         std::memset(&a, 0, sizeof(a));
         a.act_f32 = act_f32 ? 1 : 0;
-        r = (uint32_t)gemv_rows_per_matrix_group(k);
+        r = (uint32_t)gemv_rows_per_matrix_group(k, paired);
     }
     GemvSeg& add(const Q35QuantWeight& w, int32_t epi, const Q35QuantWeight* w2 = nullptr) {
         GemvSeg& s = a.seg[a.nseg++];
@@ -162,6 +161,7 @@ struct GemvBuild {
             s.biases[1] = w2->biases;
         }
         s.rg_begin = a.total_rg;
+        s.rows = w.n;
         a.total_rg += w.n / r;
         s.rg_end = a.total_rg;
         s.epi = epi;
@@ -169,7 +169,7 @@ struct GemvBuild {
     }
     q35_status launch(hipStream_t stream, const char* what, uint32_t blocks = 0) {
         if (!blocks) blocks = gemv_pick_blocks(a.total_rg);
-        Q35_HIP(gemv_launch(k, paired, a, blocks, stream), what);
+        Q35_HIP(gemv_launch(op, k, a.act_f32 == 0, a, blocks, stream), what);
         return Q35_OK;
     }
 };
@@ -182,7 +182,7 @@ q35_status launch_mlp(const Qwen35ForwardConfig& c, const Q35QuantWeight& gate_p
                       hipStream_t stream) {
     const bool f32 = c.act_dtype == Q35_ACT_F32;
     {
-        GemvBuild b(c.hidden, true, f32);
+        GemvBuild b(kOpGateUp, c.hidden, f32);
         b.a.pro.kind = kProRmsF32;
         b.a.pro.x = x_resid;
         b.a.pro.w = post_ln;
@@ -195,7 +195,7 @@ q35_status launch_mlp(const Qwen35ForwardConfig& c, const Q35QuantWeight& gate_p
         Q35_TRY(b.launch(stream, "gate/up GEMV"));
     }
     {
-        GemvBuild b(c.intermediate, false, f32);
+        GemvBuild b(kOpDown, c.intermediate, f32);
         b.a.pro.kind = kProLoadF32;
         b.a.pro.x = mlp_act;
         GemvSeg& s = b.add(down_proj, kEpiResidToAct);
@@ -267,21 +267,21 @@ q35_status q35_config_validate(const Qwen35ForwardConfig* cfg) {
     if (c.conv_kernel_size != 4)
         return fail(Q35_ERR_UNSUPPORTED, "conv_kernel_size %u (only 4)", c.conv_kernel_size);
     const uint32_t widths[4] = {c.hidden, c.intermediate, q_only(c), z_dim(c)};
+    const int roles[4] = {kWidthHidden, kWidthInter, kWidthProj, kWidthProj};
     const char* names[4] = {"hidden", "intermediate", "q_only", "z_dim_lin"};
     for (int i = 0; i < 4; ++i) {
         if (widths[i] == 0 || widths[i] % 64)
             return fail(Q35_ERR_INVALID_ARG, "%s %u not a multiple of 64", names[i], widths[i]);
-        if (!gemv_width_supported(widths[i]))
+        if (!gemv_width_supported(roles[i], widths[i]))
             return fail(Q35_ERR_UNSUPPORTED, "%s %u is not a compiled GEMV width", names[i], widths[i]);
     }
-    if (c.hidden > 8192) return fail(Q35_ERR_UNSUPPORTED, "hidden %u > 8192", c.hidden);
     // output rows of every GEMV must tile the per-wave row groups
     Q35_TRY(check_rows("q_proj", q_total(c), c.hidden));
     Q35_TRY(check_rows("k_proj/v_proj", kv_dim(c), c.hidden));
     Q35_TRY(check_rows("in_proj_qkv", qkv_total(c), c.hidden));
     Q35_TRY(check_rows("in_proj_z", z_dim(c), c.hidden));
     Q35_TRY(check_rows("in_proj_a/b", c.num_v_heads_lin, c.hidden));
-    Q35_TRY(check_rows("gate/up", c.intermediate, c.hidden));
+    Q35_TRY(check_rows("gate/up", c.intermediate, c.hidden, true));
     Q35_TRY(check_rows("o_proj", c.hidden, q_only(c)));
     Q35_TRY(check_rows("out_proj", c.hidden, z_dim(c)));
     Q35_TRY(check_rows("down_proj", c.hidden, c.intermediate));
@@ -319,15 +319,34 @@ q35_status q35_kernels_resolve(int device, Qwen35Kernels** out) {
         hipError_t e = hipFuncGetAttributes(&attr, fn);
         if (e != hipSuccess) st = fail(Q35_ERR_HIP, "kernel %s does not load: %s", name, hipGetErrorString(e));
     };
-    const uint32_t widths[] = {128, 256, 512, 1024, 2048, 2560, 3072, 4096, 5120, 6144, 8192, 9216, 12288};
-    for (uint32_t w : widths) {
-        probe(gemv_kernel_ptr(w, false), "gemv");
-        if (w <= 8192) probe(gemv_kernel_ptr(w, true), "gemv (paired)");
+    const int ops_hidden[] = {kOpInGdn, kOpInFull, kOpGateUp, kOpLmHead};
+    for (bool half : {false, true}) {
+#define X(KK)                                                                        \
+        probe(gemv_kernel_ptr(kOpPlain, KK, half, false), "gemv");                  \
+        probe(gemv_kernel_ptr(kOpPlain, KK, half, true), "gemv (streaming)");
+        Q35_W_ALL(X)
+#undef X
+#define X(KK)                                                                           \
+        for (int op : ops_hidden) probe(gemv_kernel_ptr(op, KK, half, false), "gemv");  \
+        probe(gemv_kernel_ptr(kOpLmHead, KK, half, true), "lm_head");
+        Q35_W_HIDDEN(X)
+#undef X
+#define X(KK)                                                          \
+        probe(gemv_kernel_ptr(kOpOutGated, KK, half, false), "out_proj"); \
+        probe(gemv_kernel_ptr(kOpOProj, KK, half, false), "o_proj");
+        Q35_W_PROJ(X)
+#undef X
+#define X(KK) probe(gemv_kernel_ptr(kOpDown, KK, half, false), "down");
+        Q35_W_INTER(X)
+#undef X
     }
     for (uint32_t dk : {32u, 64u, 128u}) probe(gdn_kernel_ptr(dk), "gated_delta_rule");
     for (uint32_t d : {64u, 128u, 256u})
         for (uint32_t g : {1u, 2u, 4u, 8u}) probe(attn_kernel_ptr(d, g), "attention");
     probe(embed_kernel_ptr(), "embed");
+    probe(lm_finish_kernel_ptr(), "lm_head argmax");
+    for (uint32_t d : {64u, 128u, 256u})
+        for (uint32_t g : {1u, 2u, 4u, 8u}) probe(attn_combine_kernel_ptr(d, g), "attention merge");
     (void)hipSetDevice(prev);
     if (st != Q35_OK) return st;
     Qwen35Kernels* k = new Qwen35Kernels;
@@ -445,7 +464,7 @@ static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35Fo
     const bool f32 = c.act_dtype == Q35_ACT_F32;
     // 1. input RMSNorm + q/k/v projections
     {
-        GemvBuild b(c.hidden, false, f32);
+        GemvBuild b(kOpInFull, c.hidden, f32);
         b.a.pro.kind = kProRmsAct;
         b.a.pro.x_f32 = f32;
         b.a.pro.x = x_in;
@@ -478,7 +497,6 @@ static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35Fo
         a.k_norm_out = s->k_norm_out;
         a.part_acc = reinterpret_cast<float*>(wsb + ws.acc_off);
         a.part_ml = reinterpret_cast<float*>(wsb + ws.ml_off);
-        a.counters = reinterpret_cast<uint32_t*>(wsb + ws.cnt_off);
         a.capacity = kv->capacity;
         a.hq = c.num_heads;
         a.hkv = c.num_kv_heads;
@@ -502,7 +520,7 @@ static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35Fo
     }
     // 3. o projection + residual
     {
-        GemvBuild b(q_only(c), false, f32);
+        GemvBuild b(kOpOProj, q_only(c), f32);
         b.a.pro.kind = kProLoadF32;
         b.a.pro.x = s->gated_attn;
         GemvSeg& sg = b.add(layer->o_proj, kEpiResidActIn);
@@ -585,7 +603,7 @@ q35_status q35_forward_linear_attention(const Qwen35Kernels* kernels,
     const bool f32 = c.act_dtype == Q35_ACT_F32;
     // 1. input RMSNorm + in_proj qkv (conv epilogue) / z / a (gate) / b (beta)
     {
-        GemvBuild b(c.hidden, false, f32);
+        GemvBuild b(kOpInGdn, c.hidden, f32);
         b.a.pro.kind = kProRmsAct;
         b.a.pro.x_f32 = f32;
         b.a.pro.x = x_in;
@@ -626,7 +644,7 @@ q35_status q35_forward_linear_attention(const Qwen35Kernels* kernels,
     }
     // 3. gated RMSNorm + out projection + residual
     {
-        GemvBuild b(z_dim(c), false, f32);
+        GemvBuild b(kOpOutGated, z_dim(c), f32);
         b.a.pro.kind = kProGatedNorm;
         b.a.pro.x = s->y;
         b.a.pro.w = layer->norm_weight;
@@ -702,7 +720,7 @@ q35_status q35_lm_head_argmax(const Qwen35Kernels* kernels, const Qwen35ForwardC
     if (workspace_bytes < ws.total)
         return fail(Q35_ERR_INVALID_ARG, "workspace %zu bytes < %zu required", workspace_bytes, ws.total);
     const bool f32 = c.act_dtype == Q35_ACT_F32;
-    GemvBuild b(c.hidden, false, f32);
+    GemvBuild b(kOpLmHead, c.hidden, f32);
     b.a.pro.kind = kProRmsAct;
     b.a.pro.x_f32 = f32;
     b.a.pro.x = x;
@@ -712,17 +730,23 @@ q35_status q35_lm_head_argmax(const Qwen35Kernels* kernels, const Qwen35ForwardC
     uint8_t* wsb = static_cast<uint8_t*>(workspace);
     b.a.am.part_val = reinterpret_cast<float*>(wsb + ws.val_off);
     b.a.am.part_idx = reinterpret_cast<int32_t*>(wsb + ws.idx_off);
-    b.a.am.counter = reinterpret_cast<uint32_t*>(wsb + ws.cnt_off);
-    b.a.am.tokens = tokens;
-    b.a.am.positions = positions;
-    b.a.am.history = history;
-    b.a.am.history_len = history ? history_len : 0;
-    b.a.am.history_base = history_base;
-    b.a.am.embed = embed_table;
-    b.a.am.x_next = x_next;
-    b.a.am.hidden = c.hidden;
-    b.a.am.vocab = c.vocab;
     Q35_TRY(b.launch(stream, "lm_head GEMV", ws.blocks));
+    LmFinishArgs f;
+    std::memset(&f, 0, sizeof(f));
+    f.part_val = b.a.am.part_val;
+    f.part_idx = b.a.am.part_idx;
+    f.nparts = ws.blocks;
+    f.vocab = c.vocab;
+    f.tokens = tokens;
+    f.positions = positions;
+    f.history = history;
+    f.history_len = history ? history_len : 0;
+    f.history_base = history_base;
+    f.embed = embed_table;
+    f.x_next = x_next;
+    f.hidden = c.hidden;
+    f.act_f32 = f32 ? 1 : 0;
+    Q35_HIP(lm_finish_launch(f, stream), "lm_head argmax");
     return ok();
 }
 
@@ -739,7 +763,7 @@ q35_status q35_gate_up_swiglu(const Qwen35Kernels* kernels, const Qwen35ForwardC
     Q35_TRY(need(post_ln, "post_ln"));
     Q35_TRY(need(x_resid, "x_resid"));
     Q35_TRY(need(mlp_act, "mlp_act"));
-    GemvBuild b(c.hidden, true, c.act_dtype == Q35_ACT_F32);
+    GemvBuild b(kOpGateUp, c.hidden, c.act_dtype == Q35_ACT_F32);
     b.a.pro.kind = kProRmsF32;
     b.a.pro.x = x_resid;
     b.a.pro.w = post_ln;
@@ -750,15 +774,18 @@ q35_status q35_gate_up_swiglu(const Qwen35Kernels* kernels, const Qwen35ForwardC
 }
 
 q35_status q35_gemv(const Qwen35Kernels* kernels, const Q35QuantWeight* w, const float* x,
-                    float* y, hipStream_t stream) {
+                    float* y, uint32_t act_dtype, hipStream_t stream) {
     Q35_TRY(check_kernels(kernels));
     if (!w) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
-    if (!gemv_width_supported(w->k)) return fail(Q35_ERR_UNSUPPORTED, "K = %u is not a compiled width", w->k);
+    if (!gemv_width_supported(kWidthAny, w->k))
+        return fail(Q35_ERR_UNSUPPORTED, "K = %u is not a compiled width", w->k);
     Q35_TRY(check_weight("w", *w, w->n, w->k));
     Q35_TRY(check_rows("w", w->n, w->k));
     Q35_TRY(need(x, "x"));
     Q35_TRY(need(y, "y", false));
-    GemvBuild b(w->k, false, true);
+    if (act_dtype != Q35_ACT_BF16 && act_dtype != Q35_ACT_F32)
+        return fail(Q35_ERR_INVALID_ARG, "act_dtype %u", act_dtype);
+    GemvBuild b(kOpPlain, w->k, act_dtype == Q35_ACT_F32);
     b.a.pro.kind = kProLoadF32;
     b.a.pro.x = x;
     b.add(*w, kEpiStore).out = y;

@@ -52,6 +52,32 @@ Q35_DEV float dpp(float v) {
                                            BANK_MASK, false));
 }
 
+// Sum over aligned groups of W lanes (W in {2,...,64}), returned in EVERY lane
+// of the group (butterfly: each step pairs lanes whose partial sums cover
+// disjoint halves, so all lanes end with the same value).
+template <int W>
+Q35_DEV float group_sum_all(float v) {
+    static_assert(W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "W");
+    v += dpp<0xB1>(v);                          // quad_perm [1,0,3,2]
+    if constexpr (W >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+    if constexpr (W >= 8) v += dpp<0x141>(v);   // row_half_mirror: quad 0 <-> quad 1
+    if constexpr (W >= 16) v += dpp<0x140>(v);  // row_mirror: half-row 0 <-> half-row 1
+    if constexpr (W >= 32)                      // ds_swizzle bitmask mode, lane ^ 16
+        v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+    if constexpr (W >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+// ------------------------------------------------------------------ buffer loads
+
+constexpr int kBufWord3 = 0x00020000;  // raw buffer resource, gfx9 family
+constexpr int kAuxStream = 2;          // non-temporal: data streamed once per call
+
+// Raw buffer resource over [p, p + bytes): loads past the end return zero.
+Q35_DEV __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kBufWord3);
+}
+
 // Sum over aligned groups of W lanes (W in {2,4,8,16,32,64}).  The result is
 // valid in the LAST lane of each group (other lanes hold partial sums).
 template <int W>

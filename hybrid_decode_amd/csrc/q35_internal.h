@@ -34,6 +34,7 @@ struct GemvSeg {
     const uint16_t* scales[2];
     const uint16_t* biases[2];
     uint32_t rg_begin, rg_end;  // row-group range of this segment in the launch
+    uint32_t rows;              // rows of each matrix of the segment
     int32_t epi;
     float* out;
     void* out_act;
@@ -57,18 +58,8 @@ struct GemvPro {
 };
 
 struct GemvArgmax {
-    float* part_val;
-    int32_t* part_idx;
-    uint32_t* counter;  // nullptr: no argmax in this launch
-    int32_t* tokens;
-    int32_t* positions;
-    int32_t* history;
-    uint32_t history_len;
-    int32_t history_base;
-    const uint16_t* embed;
-    void* x_next;
-    uint32_t hidden;
-    uint32_t vocab;
+    float* part_val;    // [blocks] per-block maximum
+    int32_t* part_idx;  // [blocks] its row
 };
 
 struct GemvArgs {
@@ -80,13 +71,37 @@ struct GemvArgs {
     GemvArgmax am;
 };
 
-bool gemv_width_supported(uint32_t k);
-int gemv_rows_per_group(uint32_t k, bool paired);   // rows per row group
-int gemv_rows_per_matrix_group(uint32_t k);         // rows of one matrix per row group
+// Operations: each GEMV launch is one of these, fixing its prologue and the
+// epilogue of every segment.
+enum : int32_t {
+    kOpPlain = 0,     // x loaded as is; y stored                         (segments: 1)
+    kOpInGdn = 1,     // RMSNorm(x_in); qkv->conv, z->store, a->gate, b->beta (4)
+    kOpInFull = 2,    // RMSNorm(x_in); q, k, v stored                    (3)
+    kOpOutGated = 3,  // gated per-head RMSNorm; out + residual           (1)
+    kOpOProj = 4,     // x loaded; o + residual                           (1)
+    kOpGateUp = 5,    // RMSNorm(x_resid); paired gate/up -> silu(g) * u  (1)
+    kOpDown = 6,      // x loaded; down + residual -> activation dtype    (1)
+    kOpLmHead = 7,    // RMSNorm(x); logits + argmax                      (1)
+};
+
+// GEMV widths compiled in, by role.
+#define Q35_W_HIDDEN(X) X(256) X(1024) X(2048) X(2560) X(3072) X(4096) X(5120) X(6144) X(8192)
+#define Q35_W_PROJ(X) X(128) X(256) X(512) X(1024) X(2048) X(4096) X(6144) X(8192)
+#define Q35_W_INTER(X) \
+    X(512) X(1024) X(2048) X(3072) X(4096) X(5120) X(6144) X(8192) X(9216) X(12288)
+#define Q35_W_ALL(X)                                                                              \
+    X(128) X(256) X(512) X(1024) X(2048) X(2560) X(3072) X(4096) X(5120) X(6144) X(8192) X(9216) \
+    X(12288)
+enum : int { kWidthHidden = 0, kWidthProj = 1, kWidthInter = 2, kWidthAny = 3 };
+
+bool gemv_width_supported(int role, uint32_t k);
+int gemv_rows_per_matrix_group(uint32_t k, bool paired);  // rows of each matrix per row group
+uint32_t gemv_row_groups_per_wave(uint32_t total_rg);
 uint32_t gemv_pick_blocks(uint32_t total_rg);
-hipError_t gemv_launch(uint32_t k, bool paired, const GemvArgs& a, uint32_t blocks,
+// half: the f16-product variant used for bf16 activations (else exact fp32 products)
+hipError_t gemv_launch(int op, uint32_t k, bool half, const GemvArgs& a, uint32_t blocks,
                        hipStream_t stream);
-const void* gemv_kernel_ptr(uint32_t k, bool paired);
+const void* gemv_kernel_ptr(int op, uint32_t k, bool half, bool xreg);
 
 // ------------------------------------------------------------------ GDN recurrence
 
@@ -123,7 +138,6 @@ struct AttnArgs {
     float* k_norm_out;       // optional tap (post-RoPE)
     float* part_acc;         // workspace: [Hkv][max_chunks][G][D]
     float* part_ml;          // workspace: [Hkv][max_chunks][G][2]
-    uint32_t* counters;      // workspace: [Hkv]
     uint32_t capacity;
     uint32_t hq, hkv, rotary;
     uint32_t chunk;          // positions per block
@@ -134,14 +148,36 @@ struct AttnArgs {
 };
 bool attn_dims_supported(uint32_t head_dim, uint32_t group);
 uint32_t attn_rows_per_iter(uint32_t head_dim);
+// Two launches: per-chunk partials, then the log-sum-exp merge with the sigmoid gate.
 hipError_t attn_launch(uint32_t head_dim, uint32_t group, const AttnArgs& a, uint32_t grid_chunks,
                        hipStream_t stream);
 const void* attn_kernel_ptr(uint32_t head_dim, uint32_t group);
+const void* attn_combine_kernel_ptr(uint32_t head_dim, uint32_t group);
 
 // ------------------------------------------------------------------ misc
 
 hipError_t embed_launch(const uint16_t* table, const int32_t* tokens, uint32_t vocab,
                         uint32_t hidden, void* x_out, bool act_f32, hipStream_t stream);
 const void* embed_kernel_ptr();
+
+// Greedy token from the lm_head's per-block partials, then the caller's
+// bookkeeping: history entry, position increment, next embedding.
+struct LmFinishArgs {
+    const float* part_val;
+    const int32_t* part_idx;
+    uint32_t nparts;
+    uint32_t vocab;
+    int32_t* tokens;
+    int32_t* positions;
+    int32_t* history;
+    uint32_t history_len;
+    int32_t history_base;
+    const uint16_t* embed;
+    void* x_next;
+    uint32_t hidden;
+    int32_t act_f32;
+};
+hipError_t lm_finish_launch(const LmFinishArgs& a, hipStream_t stream);
+const void* lm_finish_kernel_ptr();
 
 }  // namespace q35

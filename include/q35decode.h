@@ -407,11 +407,14 @@ q35_status q35_gate_up_swiglu(const Qwen35Kernels* kernels, const Qwen35ForwardC
 
 /*
  * Plain GEMV with the library's quantised-weight kernel: y (fp32 [w->n]) =
- * W x (x fp32 [w->k]).  With x a one-hot vector e_j, y is column j of the
- * dequantised matrix, bit for bit.
+ * W x (x fp32 [w->k]).  act_dtype picks the arithmetic the layer forwards use
+ * for that activation dtype: Q35_ACT_F32, fp32 products; Q35_ACT_BF16, x
+ * rounded to f16 after a power-of-two scaling of the whole vector and exact
+ * f16 x u8 products summed in fp32.  With x a one-hot vector e_j, y is column
+ * j of the dequantised matrix, bit for bit, in both.
  */
 q35_status q35_gemv(const Qwen35Kernels* kernels, const Q35QuantWeight* w, const float* x,
-                    float* y, hipStream_t stream);
+                    float* y, uint32_t act_dtype, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -7,6 +7,9 @@ import oracle as O
 TOL_BF16 = 2e-2    # bf16 activations
 TOL_F32 = 1e-3     # fp32 activations (tiny config) and the fp32 GDN state after 64 steps
 TOL_GEMV = 2e-5    # one fp32 GEMV against float64
+# one GEMV whose x is rounded to f16 (11 significant bits) before exact products:
+# the error is that rounding, ~2^-12 relative per element, averaged over the dot
+TOL_GEMV_F16 = 1e-3
 
 
 def rel(gpu, ref) -> float:

@@ -184,9 +184,9 @@ def test_linear_attention_errors_before_any_launch(lib):
 def test_gemv_shape_errors(lib):
     w = B.Q35QuantWeight(0x1000, 0x2000, 0x3000, 3, 2560)  # 3 rows: not a multiple of 2 at K=2560
     with pytest.raises(B.Q35Error) as e:
-        B.q35_gemv(FAKE_KERNELS, w, 0x100, 0x100, None)
+        B.q35_gemv(FAKE_KERNELS, w, 0x100, 0x100, B.Q35_ACT_F32, None)
     assert e.value.status == B.Q35_ERR_UNSUPPORTED
     w = B.Q35QuantWeight(0x1000, 0x2000, 0x3000, 4, 2496)
     with pytest.raises(B.Q35Error) as e:
-        B.q35_gemv(FAKE_KERNELS, w, 0x100, 0x100, None)
+        B.q35_gemv(FAKE_KERNELS, w, 0x100, 0x100, B.Q35_ACT_F32, None)
     assert e.value.status == B.Q35_ERR_UNSUPPORTED

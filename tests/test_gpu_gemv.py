@@ -5,7 +5,7 @@ import torch
 
 import oracle as O
 import synth
-from gpu_common import TOL_GEMV, rel, say
+from gpu_common import TOL_GEMV, TOL_GEMV_F16, rel, say
 
 pytestmark = pytest.mark.gpu
 
@@ -21,34 +21,40 @@ def rt():
 SHAPES = [(128, 16), (256, 16), (512, 8), (2560, 8), (4096, 4), (9216, 4)]
 
 
+@pytest.mark.parametrize("act", ["f32", "bf16"])
 @pytest.mark.parametrize("K,rows", SHAPES)
-def test_one_hot_gemv_returns_dequantised_columns_bit_exact(rt, gen, K, rows):
+def test_one_hot_gemv_returns_dequantised_columns_bit_exact(rt, gen, K, rows, act):
     from hybrid_decode_amd import binding as B
     w = gen.quant(f"gpu.onehot.{K}", rows, K)
     dense = O.dequant(w)
     W = rt.QuantWeightDev(w)
     for j in sorted({0, 1, 15, 16, 63, 64, 65, K // 2, K - 1}):
-        say(f"one-hot GEMV K={K} rows={rows} column={j}")
+        say(f"one-hot GEMV ({act}) K={K} rows={rows} column={j}")
         x = torch.zeros(K, dtype=torch.float32, device="cuda")
         x[j] = 1.0
         y = torch.empty(rows, dtype=torch.float32, device="cuda")
-        B.q35_gemv(rt.kernels(), W.struct, x.data_ptr(), y.data_ptr(), rt.stream_ptr())
+        B.q35_gemv(rt.kernels(), W.struct, x.data_ptr(), y.data_ptr(),
+                   B.Q35_ACT_F32 if act == "f32" else B.Q35_ACT_BF16, rt.stream_ptr())
         torch.cuda.synchronize()
         assert np.array_equal(y.cpu().numpy(), dense[:, j]), (K, j)
 
 
+@pytest.mark.parametrize("act,tol", [("f32", TOL_GEMV), ("bf16", TOL_GEMV_F16)])
 @pytest.mark.parametrize("K,rows", [(2560, 1024), (4096, 320), (9216, 256), (512, 130), (128, 200)])
-def test_random_gemv_matches_oracle(rt, gen, K, rows):
+def test_random_gemv_matches_oracle(rt, gen, K, rows, act, tol):
     from hybrid_decode_amd import binding as B
-    say(f"random GEMV K={K} rows={rows}")
+    say(f"random GEMV ({act}) K={K} rows={rows}")
     w = gen.quant(f"gpu.gemv.{K}.{rows}", rows, K)
     x = gen.normal_f32(f"gpu.gemv.x.{K}", (K,))
     W = rt.QuantWeightDev(w)
     y = torch.empty(rows, dtype=torch.float32, device="cuda")
-    B.q35_gemv(rt.kernels(), W.struct, rt.to_dev(x).data_ptr(), y.data_ptr(), rt.stream_ptr())
+    B.q35_gemv(rt.kernels(), W.struct, rt.to_dev(x).data_ptr(), y.data_ptr(),
+               B.Q35_ACT_F32 if act == "f32" else B.Q35_ACT_BF16, rt.stream_ptr())
     torch.cuda.synchronize()
     ref = O.as_qm(w) @ x.astype(np.float64)
-    assert rel(y.cpu().numpy(), ref) < TOL_GEMV
+    r = rel(y.cpu().numpy(), ref)
+    say(f"  rel {r:.2e}")
+    assert r < tol
 
 
 def test_lm_head_full_vocab_argmax_and_embedding(rt, gen):
@@ -83,7 +89,9 @@ def test_lm_head_full_vocab_argmax_and_embedding(rt, gen):
     for r0 in range(0, cfg.vocab, 16384):
         blk = {k: v[r0:r0 + 16384] for k, v in lm.items()}
         ref[r0:r0 + 16384] = O.dequant(blk).astype(np.float64) @ h
-    assert rel(g, ref) < TOL_GEMV
+    r = rel(g, ref)
+    say(f"lm_head logits rel {r:.2e}")
+    assert r < TOL_GEMV_F16
     tok = int(tokens.cpu()[0])
     assert tok == int(np.argmax(g))                       # argmax of its own logits, exactly
     top2 = np.sort(ref)[-2:]

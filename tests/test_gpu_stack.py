@@ -8,7 +8,7 @@ import torch
 import oracle as O
 import synth
 from synth import workloads
-from gpu_common import TOL_BF16, TOL_F32, rel, say
+from gpu_common import TOL_BF16, TOL_F32, TOL_GEMV_F16, rel, say
 
 pytestmark = pytest.mark.gpu
 
@@ -126,7 +126,9 @@ def test_stack_4b_sampled_layers_logits_and_token(rt, stack8):
     rows = np.unique(np.concatenate([rows, [tok, int(np.argmax(g))]]))
     h = O.rms_norm(O.act_to_f64(outs[-1], "bf16"), w["final_norm"], cfg.rms_eps)
     ref = O.dequant({k: v[rows] for k, v in w["lm_head"].items()}).astype(np.float64) @ h
-    assert rel(g[rows], ref) < 2e-5
+    r = rel(g[rows], ref)
+    say(f"sampled logits rel {r:.2e}")
+    assert r < TOL_GEMV_F16
     assert tok == int(np.argmax(g))
     assert int(st.positions.cpu()[0]) == pos + 1
     _restore(st, snap)
