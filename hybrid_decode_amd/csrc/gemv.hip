@@ -19,21 +19,27 @@ const void* gemv_ptr_mlp(int, uint32_t, bool, bool);
 const void* gemv_ptr_lm(int, uint32_t, bool, bool);
 
 int gemv_rows_per_matrix_group(uint32_t k, bool paired) {
-    const int kc = (int)k / 16;
-    return paired ? 32 / gcd_i(32, kc) : 64 / gcd_i(64, kc);
+    (void)paired;  // a paired row group holds the same rows of both matrices
+    return 64 / gcd_i(64, (int)k / 16);
 }
 
-// Row groups per wave: one while the whole launch fits in the resident waves
-// (all of its weights requested at once), more for long streams (the lm_head).
+// Launch shape.  A launch that fits in the chip's resident waves gets about
+// three waves per four row groups: every wave has its first row group in
+// flight from the start and a third of them stream a second one, which
+// measured faster on MI355X than one row group per wave (more blocks, each
+// rebuilding x) or several (longer per-wave chains).  Long streams (the
+// lm_head) use all resident waves with many row groups each.
+constexpr uint32_t kResidentWaves = 256u * 32u;
+
 uint32_t gemv_row_groups_per_wave(uint32_t total_rg) {
-    const uint32_t resident = 256u * 32u;
-    return total_rg <= resident ? 1u : (total_rg + resident - 1) / resident;
+    return total_rg <= kResidentWaves ? 1u : (total_rg + kResidentWaves - 1) / kResidentWaves;
 }
 
 uint32_t gemv_pick_blocks(uint32_t total_rg) {
     const uint32_t rgw = gemv_row_groups_per_wave(total_rg);
-    const uint32_t waves = (total_rg + rgw - 1) / rgw;
-    const uint32_t blocks = (waves + 3) / 4;
+    const uint32_t waves = rgw == 1u ? (3u * total_rg + 3u) / 4u : (total_rg + rgw - 1) / rgw;
+    const uint32_t wpb = kGemvThreads / 64;
+    const uint32_t blocks = (waves + wpb - 1) / wpb;
     return blocks ? blocks : 1;
 }
 

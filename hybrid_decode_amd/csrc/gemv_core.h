@@ -16,12 +16,14 @@
 // A row group is 64/LR rows; LR = gcd(64, K/16) lanes of a wave share one row
 // and each lane streams K/(16 LR) 16-byte chunks of it, so every lane works on
 // exactly one row and every wave-wide load covers LR*16 contiguous bytes per
-// row.  For the paired gate+up segment LR = gcd(32, K/16) and the row slots of
-// a wave alternate gate row / up row of the same index, so the SwiGLU product
-// is formed in the epilogue.  Loads go through buffer resources: one SGPR
-// descriptor per matrix, a lane-constant 32-bit offset, and the row group's
-// offset as the scalar offset, so a load is one instruction with no per-load
-// address arithmetic; code loads are marked non-temporal (streamed once).
+// row.  For the paired gate+up segment a wave loads the row group of each
+// matrix (same rows, same lanes) and forms both dot products from one read of
+// x, so the SwiGLU product is formed in the epilogue of the lane holding both
+// sums.  Loads go through buffer resources: one SGPR descriptor per matrix
+// (wave-uniform, so no load needs a per-lane descriptor loop), a lane-constant
+// 32-bit offset, and the row group's offset as the scalar offset, so a load is
+// one instruction with no per-load address arithmetic; code loads are marked
+// non-temporal (streamed once).
 //
 // Ordering.  A wave first issues the loads of its share of x (and the norm
 // weights), then the loads of its first row group of weights, then builds x in
@@ -32,16 +34,20 @@
 //
 // Arithmetic.  Two variants, chosen by the activation dtype of the layer:
 //  * fp32 (HALF = false): codes -> fp32 (v_cvt_f32_ubyteN), fp32 FMAs.
-//  * HALF: x is held as f16 after a power-of-two scaling of the whole vector
-//    (11 significant bits: finer than the bf16 the activations are stored in,
-//    and the scaling keeps it clear of f16 overflow).  One v_perm_b32 turns two
-//    code bytes into the exact f16 pair (1024 + q0, 1024 + q1) and one
-//    v_dot2_f32_f16 multiplies it into an fp32 sum, so sum (1024+q) x =
-//    sum q x + 1024 sum x; the 1024 sum x term is folded into the bias:
-//    y = s * dot' + (b - 1024 s) * sum x.  Products of f16 inputs are exact in
-//    fp32 and accumulation is fp32, so the only extra rounding is that of x.
-// x (and its 16-element chunk sums, needed by the bias term) lives in LDS,
-// laid out so that the lanes of a wave read consecutive 16-byte words.
+//  * HALF: x is held as f16 after a power-of-two scaling of each 16-element
+//    chunk (11 significant bits: finer than the bf16 the activations are
+//    stored in, and the scaling keeps it clear of f16 overflow).  One
+//    v_perm_b32 turns two code bytes into the exact f16 pair (1024 + q0,
+//    1024 + q1) and one v_dot2_f32_f16 multiplies it into an fp32 sum, so
+//    sum (1024+q) x = sum q x + 1024 sum x; the 1024 sum x term is folded into
+//    the bias: chunk term = s * dot' + (b - 1024 s) * sum x.  Products of f16
+//    inputs are exact in fp32 and accumulation is fp32, so the only extra
+//    rounding is that of x.
+// x (with per-chunk factors and sums, needed by the bias term) lives in LDS,
+// laid out so that the lanes of a wave read consecutive 16-byte words.  Every
+// block builds it in one pass with a single barrier: the RMS factor of the
+// norm prologues multiplies each row's dot product instead of x, so no step
+// waits for a block-wide reduction before the image is written.
 #pragma once
 
 #include "q35_device.h"
@@ -50,7 +56,7 @@
 namespace q35 {
 namespace gemv {
 
-constexpr int kNT = 256;  // threads per block (4 waves)
+constexpr int kRedSlots = 64;  // LDS floats for block reductions (two per wave, 16 waves max)
 
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
@@ -105,11 +111,10 @@ struct Op<kOpLmHead> {
 template <int K, bool PAIRED>
 struct Geo {
     static constexpr int KC = K / 16;                                  // 16-byte chunks per row
-    static constexpr int LR = PAIRED ? gcd_c(32, KC) : gcd_c(64, KC);  // lanes per row
+    static constexpr int LR = gcd_c(64, KC);                           // lanes per row
     static constexpr int SLOTS = 64 / LR;                              // rows per row group
-    static constexpr int R = PAIRED ? SLOTS / 2 : SLOTS;               // rows of each matrix per row group
+    static constexpr int R = SLOTS;                                    // rows of each matrix per row group
     static constexpr int NC = KC / LR;                                 // chunks per lane
-    static constexpr int MC = (KC + kNT - 1) / kNT;                    // prologue chunks per thread
     static_assert(K % 64 == 0, "K must be a multiple of the group size");
     static_assert(LR >= 8, "rows must span at least 8 lanes");
 };
@@ -201,26 +206,40 @@ Q35_DEV void with_seg(const GemvArgs& a, uint32_t g, F&& f) {
     }
 }
 
+// A field of the segment with (wave-uniform) index si, picked with scalar
+// selects rather than branches.
+template <int NSEG, class F>
+Q35_DEV auto pick(int si, F&& f) {
+    auto v = f(0);
+#pragma unroll
+    for (int i = 1; i < NSEG; ++i)
+        if (si == i) v = f(i);
+    return v;
+}
+
 // ---------------------------------------------------------------- prologue
 
 // The prologue's global loads for one thread: x (and z) chunks and norm-weight
 // chunks, raw, issued before the weights.
-template <int K, int PRO>
+template <int K, int NT>
+constexpr int pro_chunks() { return (K / 16 + NT - 1) / NT; }  // prologue chunks per thread
+
+template <int K, int PRO, int NT>
 struct ProRegs {
-    static constexpr int MC = Geo<K, false>::MC;
+    static constexpr int MC = pro_chunks<K, NT>();
     uint4 x[MC][4];  // 16 fp32 (4 uint4) or 16 bf16 (2 uint4)
     uint4 z[MC][4];  // gated norm: 16 fp32 of z
     uint4 w[MC][2];  // 16 bf16 norm weights
 };
 
-template <int K, int PRO, bool HALF>
-Q35_DEV void prologue_issue(const GemvPro& p, ProRegs<K, PRO>& r) {
-    constexpr int KC = K / 16, MC = Geo<K, false>::MC;
+template <int K, int PRO, bool HALF, int NT>
+Q35_DEV void prologue_issue(const GemvPro& p, ProRegs<K, PRO, NT>& r) {
+    constexpr int KC = K / 16, MC = pro_chunks<K, NT>();
     constexpr bool X_BF16 = (PRO == kProRmsAct) && HALF;  // the residual stream is bf16 for HALF
     const int t = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < MC; ++m) {
-        const int cc = t + kNT * m;
+        const int cc = t + NT * m;
         if (cc < KC) {
             if constexpr (X_BF16) {
                 const uint4* px = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + 16u * cc);
@@ -270,80 +289,106 @@ Q35_DEV void unpack_bf16x16(const uint4* u, float v[16]) {
     }
 }
 
-// Stage a 16-element chunk of fp32 values in LDS slots {cc, KC+cc, 2KC+cc, 3KC+cc}.
-template <int K>
-Q35_DEV void stage_chunk(float4* xq, int cc, const float v[16]) {
-    constexpr int KC = K / 16;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        xq[j * KC + cc] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+// Power of two s with max|x| * s in [2^13, 2^14): f16 keeps 11 significant bits
+// for the large entries and nothing can overflow.  Built from the exponent
+// field: amax in [2^(E-127), 2^(E-126)) gives s = 2^(140-E); E is clamped so s
+// stays a normal float (a chunk below 2^-114 keeps its tiny values as they
+// are), and zero, inf and NaN chunks get s = 1.
+Q35_DEV float half_scale(float amax) {
+    const uint32_t E = (__float_as_uint(amax) >> 23) & 0xFFu;
+    if (E == 0u || E == 0xFFu) return 1.0f;
+    const uint32_t Ec = E < 13u ? 13u : E;
+    return __uint_as_float((267u - Ec) << 23);
 }
 
-template <int K>
-Q35_DEV void unstage_chunk(const float4* xq, int cc, float v[16]) {
-    constexpr int KC = K / 16;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float4 t = xq[j * KC + cc];
-        v[4 * j] = t.x;
-        v[4 * j + 1] = t.y;
-        v[4 * j + 2] = t.z;
-        v[4 * j + 3] = t.w;
-    }
-}
+// silu(z) with the hardware exp and reciprocal (about 1 ulp each): cheap
+// enough for a prologue that every block runs over all of x.
+Q35_DEV float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
-// LDS image of x.  fp32: xq float4 [4][KC]; HALF: xq viewed as uint4 [2][KC] of f16
-// pairs.  xs[KC]: per-chunk sums of the values actually multiplied.
+constexpr uint32_t kF16OnePair = 0x3C003C00u;  // (1.0, 1.0) in f16
+
+// LDS image of x, built once per block in one pass.
+//   HALF: xh  uint4 [2][KC]  f16 pairs of x_k * s_c, s_c a power of two per 16-element
+//                            chunk (so no block-wide maximum is needed);
+//         xab float2 [KC]    A_c = f_c / s_c and B_c = A_c * (sum of the chunk's f16 values),
+//                            so a row's chunk term is sc * A_c * dot' + (b - 1024 sc) * B_c.
+//   fp32: xq  float4 [4][KC] x_k * f_c;  xab[cc].y = the chunk sum.
+// f_c is the per-head RMS factor of the gated norm (constant over a chunk), else
+// 1.  The RMS prologues leave the global 1/rms factor out of x: it multiplies
+// every row's dot product instead, so x does not wait for that reduction.
 template <int K, bool HALF>
-Q35_DEV void write_chunk(float4* xq, float* xs, int cc, const float v[16], float scale) {
+Q35_DEV void write_chunk(uint4* ximg, float2* xab, int cc, const float v[16], float f) {
     constexpr int KC = K / 16;
     if constexpr (HALF) {
-        uint4* xh = reinterpret_cast<uint4*>(xq);
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+        const float sc = half_scale(amax);
         uint32_t p[8];
-        float s = 0.f;
+        float sum = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            p[j] = pack_f16x2(v[2 * j] * scale, v[2 * j + 1] * scale);
-            s += f16_lo(p[j]) + f16_hi(p[j]);
+            p[j] = pack_f16x2(v[2 * j] * sc, v[2 * j + 1] * sc);
+            sum = fdot2(p[j], kF16OnePair, sum);  // sum of the f16 values as multiplied
         }
-        xh[cc] = make_uint4(p[0], p[1], p[2], p[3]);
-        xh[KC + cc] = make_uint4(p[4], p[5], p[6], p[7]);
-        xs[cc] = s;
+        ximg[cc] = make_uint4(p[0], p[1], p[2], p[3]);
+        ximg[KC + cc] = make_uint4(p[4], p[5], p[6], p[7]);
+        const float A = f / sc;
+        xab[cc] = make_float2(A, A * sum);
     } else {
-        float s = 0.f;
+        float4* xq = reinterpret_cast<float4*>(ximg);
+        float sum = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) s += v[j];
-        stage_chunk<K>(xq, cc, v);
-        xs[cc] = s;
+        for (int j = 0; j < 4; ++j) {
+            const float4 q = make_float4(v[4 * j] * f, v[4 * j + 1] * f, v[4 * j + 2] * f, v[4 * j + 3] * f);
+            sum += (q.x + q.y) + (q.z + q.w);
+            xq[j * KC + cc] = q;
+        }
+        xab[cc] = make_float2(f, sum);
     }
 }
 
-// Power of two s with max|x| * s in [2^13, 2^14): f16 keeps 11 significant bits
-// for the large entries and nothing can overflow.  1 for an all-zero vector.
-Q35_DEV float half_scale(float amax) {
-    if (!(amax > 0.0f) || !isfinite(amax)) return 1.0f;
-    int e;
-    frexpf(amax, &e);  // amax in [2^(e-1), 2^e)
-    return ldexpf(1.0f, 14 - e);
+// The value of x_k * f_c (times `post`) as held in the image (for the RMS tap).
+template <int K, bool HALF>
+Q35_DEV void read_chunk(const uint4* ximg, const float2* xab, int cc, float v[16]) {
+    constexpr int KC = K / 16;
+    if constexpr (HALF) {
+        const uint4 lo = ximg[cc], hi = ximg[KC + cc];
+        const float A = xab[cc].x;
+        const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            v[2 * j] = f16_lo(d[j]) * A;
+            v[2 * j + 1] = f16_hi(d[j]) * A;
+        }
+    } else {
+        const float4* xq = reinterpret_cast<const float4*>(ximg);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 q = xq[j * KC + cc];
+            v[4 * j] = q.x;
+            v[4 * j + 1] = q.y;
+            v[4 * j + 2] = q.z;
+            v[4 * j + 3] = q.w;
+        }
+    }
 }
 
-// Builds x in LDS from the registers prologue_issue filled; returns the factor
-// x was multiplied by (HALF only).  Pass 1 forms the values chunk by chunk and
-// stages them in LDS as fp32 (gathering the block-wide statistics it needs);
-// pass 2 turns each thread's own staged chunk into the final image in place:
-// the image of chunk cc only covers LDS slots of chunk cc.
-template <int K, int PRO, bool HALF>
-Q35_DEV float prologue_finish(const GemvPro& p, const ProRegs<K, PRO>& r, float4* xq, float* xs,
-                              float* red) {
-    constexpr int KC = K / 16, MC = Geo<K, false>::MC;
+// Builds the image from the registers prologue_issue filled; returns the factor
+// every row's dot product is multiplied by (1/rms for the RMS prologues, else 1).
+template <int K, int PRO, bool HALF, int NT>
+Q35_DEV float prologue_build(const GemvPro& p, const ProRegs<K, PRO, NT>& r, uint4* ximg,
+                             float2* xab, float* red) {
+    constexpr int KC = K / 16, MC = pro_chunks<K, NT>(), NW = NT / 64;
     constexpr bool X_BF16 = (PRO == kProRmsAct) && HALF;
+    constexpr bool RMS = (PRO == kProRmsAct || PRO == kProRmsF32);
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     const bool tap = (p.tap != nullptr) && blockIdx.x == 0;
-    float amax = 0.f, ss = 0.f;
+    float ss = 0.f;
 
 #pragma unroll
     for (int m = 0; m < MC; ++m) {
-        const int cc = t + kNT * m;
+        const int cc = t + NT * m;
         float v[16];
         for (int j = 0; j < 16; ++j) v[j] = 0.f;
         if (cc < KC) {
@@ -353,8 +398,8 @@ Q35_DEV float prologue_finish(const GemvPro& p, const ProRegs<K, PRO>& r, float4
                 unpack_f32x16(r.x[m], v);
             }
         }
-        if constexpr (PRO == kProRmsAct || PRO == kProRmsF32) {
-            // x * w staged; sum of squares of x and max |x * w| reduced together
+        float f = 1.0f;
+        if constexpr (RMS) {
             if (cc < KC) {
                 float wv[16];
                 unpack_bf16x16(r.w[m], wv);
@@ -362,140 +407,120 @@ Q35_DEV float prologue_finish(const GemvPro& p, const ProRegs<K, PRO>& r, float4
                 for (int j = 0; j < 16; ++j) {
                     ss = fmaf(v[j], v[j], ss);
                     v[j] *= wv[j];
-                    amax = fmaxf(amax, fabsf(v[j]));
                 }
-                stage_chunk<K>(xq, cc, v);
             }
         } else if constexpr (PRO == kProGatedNorm) {
-            // RMSNorm over each head of p.head_dim, times the norm weight, times silu(z)
-            const int per_head = (int)p.head_dim / 16;  // chunks per head: 2, 4 or 8
+            // RMSNorm over each head of p.head_dim (2, 4 or 8 chunks held by
+            // consecutive threads), times the norm weight, times silu(z)
+            const int per_head = (int)p.head_dim / 16;
             float hs = 0.f;
             if (cc < KC) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) hs = fmaf(v[j], v[j], hs);
             }
             for (int o = 1; o < per_head; o <<= 1) hs += __shfl_xor(hs, o);
+            f = 1.0f / sqrtf(hs / (float)p.head_dim + p.eps);
             if (cc < KC) {
-                const float rs = 1.0f / sqrtf(hs / (float)p.head_dim + p.eps);
                 float wv[16], zv[16];
                 unpack_bf16x16(r.w[m], wv);
                 unpack_f32x16(r.z[m], zv);
 #pragma unroll
-                for (int j = 0; j < 16; ++j) v[j] = v[j] * rs * wv[j];
+                for (int j = 0; j < 16; ++j) v[j] *= wv[j];
                 if (tap) {
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) p.tap[16 * cc + j] = v[j];
+                    for (int j = 0; j < 16; ++j) p.tap[16 * cc + j] = v[j] * f;
                 }
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    v[j] *= siluf_(zv[j]);
-                    amax = fmaxf(amax, fabsf(v[j]));
-                }
-                stage_chunk<K>(xq, cc, v);
-            }
-        } else {  // kProLoadF32
-            if (cc < KC) {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
-                stage_chunk<K>(xq, cc, v);
+                for (int j = 0; j < 16; ++j) v[j] *= silu_fast(zv[j]);
             }
         }
+        if (cc < KC) write_chunk<K, HALF>(ximg, xab, cc, v, f);
     }
 
     float post = 1.0f;
-    constexpr bool RMS = (PRO == kProRmsAct || PRO == kProRmsF32);
-    if constexpr (RMS || HALF) {
-        // one block reduction: sum of squares (RMS) and max magnitude (HALF scaling)
-        const float s_w = RMS ? wave_sum(ss) : 0.f;
-        const float m_w = HALF ? wave_max(amax) : 0.f;
-        if (lane == 0) {
-            red[wid] = s_w;
-            red[4 + wid] = m_w;
-        }
-        __syncthreads();
-        float ss_t = 0.f, am_t = 0.f;
-#pragma unroll
-        for (int i = 0; i < kNT / 64; ++i) {
-            ss_t += red[i];
-            am_t = fmaxf(am_t, red[4 + i]);
-        }
-        if constexpr (RMS) post = 1.0f / sqrtf(ss_t / (float)K + p.eps);
-        amax = am_t * post;
+    if constexpr (RMS) {
+        const float s_w = wave_sum(ss);
+        if (lane == 0) red[wid] = s_w;
     }
-    float scale = 1.0f;
-    if constexpr (HALF) scale = half_scale(amax);
-    if constexpr (!RMS && !HALF) return scale;  // the staged fp32 chunks are already the image
-
+    __syncthreads();
+    if constexpr (RMS) {
+        float ss_t = 0.f;
 #pragma unroll
-    for (int m = 0; m < MC; ++m) {
-        const int cc = t + kNT * m;
-        if (cc < KC) {
-            float v[16];
-            unstage_chunk<K>(xq, cc, v);
+        for (int i = 0; i < NW; ++i) ss_t += red[i];
+        post = 1.0f / sqrtf(ss_t / (float)K + p.eps);
+        if (tap) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) v[j] *= post;
-            if (RMS && tap) {
+            for (int m = 0; m < MC; ++m) {
+                const int cc = t + NT * m;
+                if (cc < KC) {
+                    float v[16];
+                    read_chunk<K, HALF>(ximg, xab, cc, v);
 #pragma unroll
-                for (int j = 0; j < 16; ++j) p.tap[16 * cc + j] = v[j];
+                    for (int j = 0; j < 16; ++j) p.tap[16 * cc + j] = v[j] * post;
+                }
             }
-            write_chunk<K, HALF>(xq, xs, cc, v, scale);
         }
     }
-    return scale;
-}
-
-// The !RMS && !HALF path stages fp32 values without chunk sums; fill them.
-template <int K>
-Q35_DEV void chunk_sums_f32(const float4* xq, float* xs) {
-    constexpr int KC = K / 16;
-    for (int cc = threadIdx.x; cc < KC; cc += kNT) {
-        float v[16];
-        unstage_chunk<K>(xq, cc, v);
-        float s = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) s += v[j];
-        xs[cc] = s;
-    }
+    return post;
 }
 
 // ---------------------------------------------------------------- epilogues
 
+// Operands an epilogue reads from memory (GemvSeg::pre16/8/4/2, element n),
+// loaded with the row group's weights: a load issued in the epilogue would
+// wait, in order, for the next row group's weight loads issued before it.
+// Every segment of an operation issues the same loads (a NULL operand gets an
+// empty buffer range and reads zero), so the compiler's count of outstanding
+// loads is the same on every path and its waits stay exact.
+struct EpiPre {
+    uint4 q16;    // conv state of channel n (4 fp32)
+    uint2 q8;     // conv weights of channel n (4 bf16)
+    uint32_t q4;  // fp32: residual, A_log
+    uint32_t q2;  // bf16: residual, dt_bias
+};
+
+template <int OP, bool HALF>
+constexpr int pre_mask() {  // which of the 16/8/4/2-byte operands the op's epilogues read
+    return OP == kOpInGdn ? (16 | 8 | 4 | 2)
+         : (OP == kOpOutGated || OP == kOpOProj) ? (HALF ? 2 : 4)
+         : OP == kOpDown ? 4
+         : 0;
+}
+
 template <int OP, int SI>
 Q35_DEV void epilogue(const GemvArgs& a, const GemvSeg& s, uint32_t n, float v, float v2,
-                      float& best_v, int& best_i) {
+                      const EpiPre& e, float& best_v, int& best_i) {
     if constexpr (OP == kOpPlain || OP == kOpInFull || (OP == kOpInGdn && SI == 1)) {
         s.out[n] = v;
     } else if constexpr (OP == kOpInGdn && SI == 0) {
         // causal depthwise conv update of channel n (window: state[1..3] + new input), SiLU
         if (s.tap0) s.tap0[n] = v;
-        float4* st = reinterpret_cast<float4*>(s.state) + n;
-        const float4 o = *st;
-        const uint2 w = reinterpret_cast<const uint2*>(s.aux0)[n];
+        const float4 o = make_float4(__uint_as_float(e.q16.x), __uint_as_float(e.q16.y),
+                                     __uint_as_float(e.q16.z), __uint_as_float(e.q16.w));
+        const uint2 w = e.q8;
         float u = bf16_lo(w.x) * o.y;
         u = fmaf(bf16_hi(w.x), o.z, u);
         u = fmaf(bf16_lo(w.y), o.w, u);
         u = fmaf(bf16_hi(w.y), v, u);
-        *st = make_float4(o.y, o.z, o.w, v);
+        reinterpret_cast<float4*>(s.state)[n] = make_float4(o.y, o.z, o.w, v);
         s.out[n] = siluf_(u);
     } else if constexpr (OP == kOpInGdn && SI == 2) {
         // decay gate exp(-exp(A_log) * softplus(a + dt_bias))
         if (s.tap0) s.tap0[n] = v;
-        const float dtb = bf16_to_f32(static_cast<const uint16_t*>(s.aux0)[n]);
-        const float al = static_cast<const float*>(s.aux1)[n];
-        s.out[n] = expf(-expf(al) * softplusf_(v + dtb));
+        s.out[n] = expf(-expf(__uint_as_float(e.q4)) * softplusf_(v + bf16_to_f32(e.q2)));
     } else if constexpr (OP == kOpInGdn && SI == 3) {
         if (s.tap0) s.tap0[n] = v;
         s.out[n] = sigmoidf_(v);
     } else if constexpr (OP == kOpOutGated || OP == kOpOProj) {
         // residual from the layer input (activation dtype)
         if (s.tap0) s.tap0[n] = v;
-        s.out[n] = load_act(s.aux0, n, a.act_f32) + v;
+        s.out[n] = (a.act_f32 ? __uint_as_float(e.q4) : bf16_to_f32(e.q2)) + v;
     } else if constexpr (OP == kOpGateUp) {
         if (s.tap0) s.tap0[n] = v;
         if (s.tap1) s.tap1[n] = v2;
         s.out[n] = siluf_(v) * v2;
     } else if constexpr (OP == kOpDown) {
-        const float r = static_cast<const float*>(s.aux0)[n] + v;
+        const float r = __uint_as_float(e.q4) + v;
         store_act(s.out_act, n, r, a.act_f32);
         if (s.out_act2) store_act(s.out_act2, n, r, a.act_f32);
     } else if constexpr (OP == kOpLmHead) {
@@ -515,8 +540,9 @@ Q35_DEV bool better(float v, int i, float bv, int bi) {
 
 // Per-block partial argmax (lowest index on ties), stored plainly; a follow-up
 // kernel reduces the partials, so no block needs a device-wide fence.
+template <int NT>
 Q35_DEV void argmax_partial(const GemvArgs& a, float best_v, int best_i, float* red) {
-    int* redi = reinterpret_cast<int*>(red + 8);
+    int* redi = reinterpret_cast<int*>(red + kRedSlots / 2);
     for (int o = 32; o > 0; o >>= 1) {
         const float ov = __shfl_xor(best_v, o);
         const int oi = __shfl_xor(best_i, o);
@@ -535,7 +561,7 @@ Q35_DEV void argmax_partial(const GemvArgs& a, float best_v, int best_i, float* 
     if (threadIdx.x == 0) {
         float bv = red[0];
         int bi = redi[0];
-        for (int w = 1; w < kNT / 64; ++w)
+        for (int w = 1; w < NT / 64; ++w)
             if (better(red[w], redi[w], bv, bi)) {
                 bv = red[w];
                 bi = redi[w];
@@ -547,66 +573,87 @@ Q35_DEV void argmax_partial(const GemvArgs& a, float best_v, int best_i, float* 
 
 // ---------------------------------------------------------------- the kernel
 
-template <int K, int OP, bool HALF, bool XREG>
-__global__ __launch_bounds__(kNT) void gemv_kernel(GemvArgs a) {
+template <int K, int OP, bool HALF, bool XREG, int NT>
+__global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a) {
     using T = Op<OP>;
     constexpr bool PAIRED = T::PAIRED;
     using G = Geo<K, PAIRED>;
     constexpr int KC = G::KC, LR = G::LR, R = G::R, NC = G::NC;
     constexpr int KG = K / 64;  // scale groups per row
 
-    extern __shared__ float4 smem4[];
-    float4* xq = smem4;
-    float* xs = reinterpret_cast<float*>(smem4 + 4 * KC);
-    float* red = xs + KC;
-    const uint4* xh = reinterpret_cast<const uint4*>(smem4);
+    extern __shared__ uint4 smem4[];
+    uint4* ximg = smem4;                                         // x image (f16: 2*KC, fp32: 4*KC)
+    float2* xab = reinterpret_cast<float2*>(smem4 + (HALF ? 2 : 4) * KC);  // per-chunk (A, B)
+    float* red = reinterpret_cast<float*>(xab + KC);
+    const float4* xq = reinterpret_cast<const float4*>(smem4);
 
     const int lane = threadIdx.x & 63;
-    const int slot = lane / LR, li = lane % LR;
-    const int m = PAIRED ? (slot & 1) : 0;  // paired: odd slots are up rows
-    const uint32_t rloc = PAIRED ? (uint32_t)(slot >> 1) : (uint32_t)slot;
-    const uint32_t nw = gridDim.x * (kNT / 64);
+    const int li = lane % LR;
+    const uint32_t rloc = (uint32_t)(lane / LR);  // row of the row group
+    const uint32_t nw = gridDim.x * (NT / 64);
     const uint32_t total = a.total_rg;
 
-    u32x4_t w[NC];
-    uint32_t sv[NC], bv[NC];
+    constexpr int NC2 = PAIRED ? NC : 1;
+    u32x4_t w[NC], w2[NC2];  // paired: w2 holds the second matrix's rows of the same index
+    uint32_t sv[NC], bv[NC], sv2[NC2], bv2[NC2];
+    static_assert(!PAIRED || T::NSEG == 1, "a paired launch has one segment");
+    EpiPre pre;
+    constexpr int PM = pre_mask<OP, HALF>();
+    // Branch-free in the segment: the same loads are issued whatever the row group.
     auto load_rg = [&](uint32_t g) {
-        with_seg<T::NSEG>(a, g, [&](const GemvSeg& s, auto) {
-            const uint32_t row0 = (g - s.rg_begin) * R;
-            const uint32_t cbytes = s.rows * (uint32_t)K, sbytes = s.rows * (uint32_t)KG * 2u;
-            const uint32_t coff = row0 * (uint32_t)K, soff = row0 * (uint32_t)KG * 2u;
-            auto issue = [&](const void* c, const void* sc, const void* bi) {
-                const auto rc = rsrc(c, cbytes), rs = rsrc(sc, sbytes), rb = rsrc(bi, sbytes);
+        const int si = find_seg<T::NSEG>(a, g);
+        const uint32_t rows = pick<T::NSEG>(si, [&](int i) { return a.seg[i].rows; });
+        const uint32_t row0 = (g - pick<T::NSEG>(si, [&](int i) { return a.seg[i].rg_begin; })) * R;
+        const uint32_t n = row0 + rloc;
+        // epilogue operands first: they have landed once the weights have
+        auto pre_rsrc = [&](const void* p, uint32_t elt) { return rsrc(p, p ? rows * elt : 0u); };
+        if constexpr (PM & 16)
+            pre.q16 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                pre_rsrc(pick<T::NSEG>(si, [&](int i) { return a.seg[i].pre16; }), 16u), n * 16u, 0, 0));
+        if constexpr (PM & 8)
+            pre.q8 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                pre_rsrc(pick<T::NSEG>(si, [&](int i) { return a.seg[i].pre8; }), 8u), n * 8u, 0, 0));
+        if constexpr (PM & 4)
+            pre.q4 = __builtin_amdgcn_raw_buffer_load_b32(
+                pre_rsrc(pick<T::NSEG>(si, [&](int i) { return a.seg[i].pre4; }), 4u), n * 4u, 0, 0);
+        if constexpr (PM & 2)
+            pre.q2 = __builtin_amdgcn_raw_buffer_load_b16(
+                pre_rsrc(pick<T::NSEG>(si, [&](int i) { return a.seg[i].pre2; }), 2u), n * 2u, 0, 0);
+        const uint32_t cbytes = rows * (uint32_t)K, sbytes = rows * (uint32_t)KG * 2u;
+        const uint32_t coff = row0 * (uint32_t)K, soff = row0 * (uint32_t)KG * 2u;
+        auto issue = [&](const void* c, const void* sc, const void* bi, u32x4_t* wd, uint32_t* sd,
+                         uint32_t* bd) {
+            const auto rc = rsrc(c, cbytes), rs = rsrc(sc, sbytes), rb = rsrc(bi, sbytes);
 #pragma unroll
-                for (int i = 0; i < NC; ++i) {
-                    const uint32_t cc = (uint32_t)li + LR * i;
-                    w[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, rloc * K + 16u * cc, coff, kAuxStream);
-                    sv[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, (rloc * KG + (cc >> 2)) * 2u, soff, 0);
-                    bv[i] = __builtin_amdgcn_raw_buffer_load_b16(rb, (rloc * KG + (cc >> 2)) * 2u, soff, 0);
-                }
-            };
-            if (!PAIRED || m == 0)
-                issue(s.codes[0], s.scales[0], s.biases[0]);
-            else
-                issue(s.codes[1], s.scales[1], s.biases[1]);
-        });
+            for (int i = 0; i < NC; ++i) {
+                const uint32_t cc = (uint32_t)li + LR * i;
+                wd[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, rloc * K + 16u * cc, coff, kAuxStream);
+                sd[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, (rloc * KG + (cc >> 2)) * 2u, soff, 0);
+                bd[i] = __builtin_amdgcn_raw_buffer_load_b16(rb, (rloc * KG + (cc >> 2)) * 2u, soff, 0);
+            }
+        };
+        issue(pick<T::NSEG>(si, [&](int i) { return a.seg[i].codes[0]; }),
+              pick<T::NSEG>(si, [&](int i) { return a.seg[i].scales[0]; }),
+              pick<T::NSEG>(si, [&](int i) { return a.seg[i].biases[0]; }), w, sv, bv);
+        if constexpr (PAIRED)
+            issue(a.seg[0].codes[1], a.seg[0].scales[1], a.seg[0].biases[1], w2, sv2, bv2);
     };
 
     // x loads first, then the first row group's weights (vector loads complete in order)
-    ProRegs<K, T::PRO> pr;
-    prologue_issue<K, T::PRO, HALF>(a.pro, pr);
+    ProRegs<K, T::PRO, NT> pr;
+    prologue_issue<K, T::PRO, HALF, NT>(a.pro, pr);
     asm volatile("" ::: "memory");
-    uint32_t rg = blockIdx.x * (kNT / 64) + (threadIdx.x >> 6);
-    if (rg < total) load_rg(rg);
+    // wave-uniform by construction; readfirstlane lets the compiler keep the row
+    // group (and so every buffer load's scalar offset) in SGPRs
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint32_t rg = blockIdx.x * (NT / 64) + wave;
+    // Unconditional (a spare wave re-reads the last row group and discards it):
+    // the compiler then knows exactly how many loads follow x and waits for x
+    // alone instead of for every outstanding load.
+    load_rg(rg < total ? rg : total - 1);
     asm volatile("" ::: "memory");
 
-    const float scale = prologue_finish<K, T::PRO, HALF>(a.pro, pr, xq, xs, red);
-    if constexpr (T::PRO != kProRmsAct && T::PRO != kProRmsF32 && !HALF) {
-        __syncthreads();
-        chunk_sums_f32<K>(xq, xs);   // fp32 x was staged as-is: add its chunk sums
-    }
-    const float inv_scale = 1.0f / scale;
-    __syncthreads();
+    const float post = prologue_build<K, T::PRO, HALF, NT>(a.pro, pr, ximg, xab, red);
 
     float best_v = -INFINITY;
     int best_i = 0x7FFFFFFF;
@@ -617,51 +664,58 @@ __global__ __launch_bounds__(kNT) void gemv_kernel(GemvArgs a) {
         // long streams (XREG) keep the hoisted copy in registers.
         int xo = 0;
         if constexpr (!XREG) asm volatile("" : "+v"(xo));
-        float acc = 0.f;
+        float acc = 0.f, acc2 = 0.f;
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             const int cc = li + LR * i + xo;
-            const float xsum = xs[cc];
-            const float sc = bf16_to_f32(sv[i]), bi = bf16_to_f32(bv[i]);
-            const uint4 wi = make_uint4(w[i].x, w[i].y, w[i].z, w[i].w);
-            float p;
-            if constexpr (HALF) {
-                p = fmaf(sc, dot16h(wi, xh[cc], xh[KC + cc]), fmaf(-1024.0f, sc, bi) * xsum);
-            } else {
-                p = fmaf(sc, dot16(wi, xq[cc], xq[KC + cc], xq[2 * KC + cc], xq[3 * KC + cc]), bi * xsum);
-            }
-            acc += p;
+            const float2 ab = xab[cc];
+            auto term = [&](const u32x4_t& wv, uint32_t sb, uint32_t bb) {
+                const float sc = bf16_to_f32(sb), bi = bf16_to_f32(bb);
+                const uint4 wi = make_uint4(wv.x, wv.y, wv.z, wv.w);
+                if constexpr (HALF)
+                    return fmaf(sc * ab.x, dot16h(wi, ximg[cc], ximg[KC + cc]), fmaf(-1024.0f, sc, bi) * ab.y);
+                else
+                    return fmaf(sc, dot16(wi, xq[cc], xq[KC + cc], xq[2 * KC + cc], xq[3 * KC + cc]), bi * ab.y);
+            };
+            acc += term(w[i], sv[i], bv[i]);
+            if constexpr (PAIRED) acc2 += term(w2[i % NC2], sv2[i % NC2], bv2[i % NC2]);
         }
         // row sums land in the last lane of each group of LR lanes
-        const float v = group_sum_last<LR>(acc) * inv_scale;
-        with_seg<T::NSEG>(a, rg, [&](const GemvSeg& s, auto si) {
-            constexpr int SI = decltype(si)::value;
-            const uint32_t n = (rg - s.rg_begin) * R + rloc;
-            if constexpr (PAIRED) {
-                const float gate = __shfl_up(v, LR, 64);  // the gate row sum sits LR lanes below
-                if (li == LR - 1 && m == 1) epilogue<OP, SI>(a, s, n, gate, v, best_v, best_i);
-            } else {
-                if (li == LR - 1) epilogue<OP, SI>(a, s, n, v, 0.f, best_v, best_i);
-            }
-        });
+        const float v = group_sum_last<LR>(acc) * post;
+        const float v2 = PAIRED ? group_sum_last<LR>(acc2) * post : 0.f;
+        // Next row group's loads go out before this one's epilogue stores: on
+        // this ISA the vector memory counter also counts stores, so a store
+        // issued first would make the next wait include its write latency.
+        const uint32_t cur = rg;
+        const EpiPre cpre = pre;
         rg += nw;
         if (rg < total) load_rg(rg);
+        with_seg<T::NSEG>(a, cur, [&](const GemvSeg& s, auto si) {
+            constexpr int SI = decltype(si)::value;
+            const uint32_t n = (cur - s.rg_begin) * R + rloc;
+            if (li == LR - 1) epilogue<OP, SI>(a, s, n, v, v2, cpre, best_v, best_i);
+        });
     }
 
-    if constexpr (OP == kOpLmHead) argmax_partial(a, best_v, best_i, red);
+    if constexpr (OP == kOpLmHead) argmax_partial<NT>(a, best_v, best_i, red);
+}
+
+template <int K, bool HALF>
+constexpr size_t lds_bytes() {  // x image + per-chunk (A, B) + reduction slots
+    return (size_t)(K / 16) * ((HALF ? 2 : 4) * 16 + 8) + kRedSlots * sizeof(float);
 }
 
 template <int K, int OP, bool HALF, bool XREG>
 hipError_t launch_t(const GemvArgs& a, uint32_t blocks, hipStream_t stream) {
-    constexpr int KC = K / 16;
-    const size_t lds = (size_t)KC * (4 * sizeof(float4) + sizeof(float)) + 16 * sizeof(float);
-    hipLaunchKernelGGL((gemv_kernel<K, OP, HALF, XREG>), dim3(blocks), dim3(kNT), lds, stream, a);
+    constexpr int NT = kGemvThreads;
+    const size_t lds = lds_bytes<K, HALF>();
+    hipLaunchKernelGGL((gemv_kernel<K, OP, HALF, XREG, NT>), dim3(blocks), dim3(NT), lds, stream, a);
     return hipGetLastError();
 }
 
 template <int K, int OP, bool HALF, bool XREG>
 const void* kernel_ptr_t() {
-    return (const void*)&gemv_kernel<K, OP, HALF, XREG>;
+    return (const void*)&gemv_kernel<K, OP, HALF, XREG, kGemvThreads>;
 }
 
 }  // namespace gemv

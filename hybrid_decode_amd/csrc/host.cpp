@@ -199,7 +199,7 @@ q35_status launch_mlp(const Qwen35ForwardConfig& c, const Q35QuantWeight& gate_p
         b.a.pro.kind = kProLoadF32;
         b.a.pro.x = mlp_act;
         GemvSeg& s = b.add(down_proj, kEpiResidToAct);
-        s.aux0 = x_resid;
+        s.pre4 = x_resid;
         s.out_act = x_out;
         s.out_act2 = x_out2;
         Q35_TRY(b.launch(stream, "down GEMV"));
@@ -525,7 +525,7 @@ static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35Fo
         b.a.pro.x = s->gated_attn;
         GemvSeg& sg = b.add(layer->o_proj, kEpiResidActIn);
         sg.out = s->x_resid;
-        sg.aux0 = x_in;
+        (f32 ? sg.pre4 : sg.pre2) = x_in;
         sg.tap0 = s->o;
         Q35_TRY(b.launch(stream, "o_proj GEMV"));
     }
@@ -613,13 +613,14 @@ q35_status q35_forward_linear_attention(const Qwen35Kernels* kernels,
         GemvSeg& sq = b.add(layer->in_proj_qkv, kEpiConv);
         sq.out = s->qkv_conv;
         sq.state = state->conv1d_state;
-        sq.aux0 = layer->conv1d_weight;
+        sq.pre16 = state->conv1d_state;
+        sq.pre8 = layer->conv1d_weight;
         sq.tap0 = s->qkv;
         b.add(layer->in_proj_z, kEpiStore).out = s->z;
         GemvSeg& sa = b.add(layer->in_proj_a, kEpiGate);
         sa.out = s->gate;
-        sa.aux0 = layer->dt_bias;
-        sa.aux1 = layer->a_log;
+        sa.pre2 = layer->dt_bias;
+        sa.pre4 = layer->a_log;
         sa.tap0 = s->dt_raw;
         GemvSeg& sb = b.add(layer->in_proj_b, kEpiBeta);
         sb.out = s->beta;
@@ -654,7 +655,7 @@ q35_status q35_forward_linear_attention(const Qwen35Kernels* kernels,
         b.a.pro.tap = s->y_norm;
         GemvSeg& so = b.add(layer->out_proj, kEpiResidActIn);
         so.out = s->x_resid;
-        so.aux0 = x_in;
+        (f32 ? so.pre4 : so.pre2) = x_in;
         so.tap0 = s->out;
         Q35_TRY(b.launch(stream, "out_proj GEMV"));
     }

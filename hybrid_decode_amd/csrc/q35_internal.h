@@ -10,6 +10,7 @@ namespace q35 {
 // ------------------------------------------------------------------ GEMV family
 
 constexpr int kMaxSegs = 4;
+constexpr int kGemvThreads = 256;  // threads per GEMV block
 
 enum : int32_t {
     kProRmsAct = 0,     // x = RMSNorm(x_act; w)          (x in the activation dtype)
@@ -20,10 +21,10 @@ enum : int32_t {
 
 enum : int32_t {
     kEpiStore = 0,       // out[n] = y
-    kEpiResidActIn = 1,  // out[n] = act(aux0)[n] + y            (tap0 = y)
-    kEpiResidToAct = 2,  // out_act[n] = act(f32(aux0)[n] + y)   (out_act2 copy)
-    kEpiConv = 3,        // causal conv update + SiLU on channel n (state, aux0 = weights, tap0 = y)
-    kEpiGate = 4,        // out[n] = exp(-exp(A_log[n]) softplus(y + dt_bias[n]))   (tap0 = y)
+    kEpiResidActIn = 1,  // out[n] = act(pre2|pre4)[n] + y       (tap0 = y)
+    kEpiResidToAct = 2,  // out_act[n] = act(f32(pre4)[n] + y)   (out_act2 copy)
+    kEpiConv = 3,        // causal conv update + SiLU on channel n (state = pre16, weights = pre8, tap0 = y)
+    kEpiGate = 4,        // out[n] = exp(-exp(A_log = pre4[n]) softplus(y + dt_bias = pre2[n]))   (tap0 = y)
     kEpiBeta = 5,        // out[n] = sigmoid(y)                  (tap0 = y)
     kEpiSwiGLU = 6,      // paired: out[n] = silu(y_a) * y_b     (tap0 = y_a, tap1 = y_b)
     kEpiArgmax = 7,      // logits (optional out) + running argmax
@@ -41,9 +42,13 @@ struct GemvSeg {
     void* out_act2;
     float* tap0;
     float* tap1;
-    const void* aux0;
-    const void* aux1;
     float* state;
+    // Per-row epilogue operands, fetched with the row group's weights: element
+    // n of each (16, 8, 4 and 2-byte elements); NULL where the epilogue has none.
+    const void* pre16;
+    const void* pre8;
+    const void* pre4;
+    const void* pre2;
 };
 
 struct GemvPro {
