@@ -9,6 +9,7 @@ from one replayed HIP graph.  Prints one JSON line (rank 0).
     python bench.py [--gpus 1] [--steps 128] [--warmup 8]
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -52,6 +53,65 @@ def gate_up_bytes(cfg) -> int:
     return int(w + cfg.hidden * (4 + 2) + cfg.intermediate * 4)
 
 
+# HBM traffic of the dominant kernel from rocprofv3 PMC runs (FETCH_SIZE and
+# WRITE_SIZE, calibrated on a device copy of known size), valid only for the
+# kernel source it was measured on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemv_traffic.json")
+KERNEL_SOURCES = ["hybrid_decode_amd/csrc/gemv_core.h", "hybrid_decode_amd/csrc/gemv_mlp.hip",
+                  "hybrid_decode_amd/csrc/gemv.hip", "hybrid_decode_amd/csrc/q35_device.h",
+                  "hybrid_decode_amd/csrc/q35_internal.h"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """Bytes per launch from the committed PMC summary, or None when it is absent
+    or was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def copy_bandwidth(torch, nbytes=1 << 29, reps=10):
+    """Device-to-device copy rate (read + write bytes per second) for reference."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    return 2 * nbytes / s / 1e9, nbytes
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, w, sample_note):
     import numpy as np
 
@@ -81,7 +141,7 @@ def cpu_baseline(cfg, w, sample_note):
     t_tok = n_gdn * t_gdn + n_full * t_full + t_lm
     return {"value": 1.0 / t_tok, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
             "sample": sample_note.format(gdn=t_gdn, full=t_full, lm=t_lm, ng=n_gdn, nf=n_full),
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
 
 
 def main():
@@ -105,7 +165,7 @@ def main():
     import synth
     from synth import workloads
     from hybrid_decode_amd import build as hb
-    if hb.is_stale():
+    if not hb.is_built():
         hb.build()
     from hybrid_decode_amd import binding as B
     from hybrid_decode_amd import runtime as rt
@@ -197,6 +257,9 @@ def main():
     dom_bytes = gate_up_bytes(cfg)
     dom_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
     log(f"gate/up GEMV: {dom_us:.2f} us/launch, {dom_gbs:.0f} GB/s")
+    copy_gbs, copy_bytes = copy_bandwidth(torch)
+    log(f"device copy of {copy_bytes >> 20} MiB: {copy_gbs:.0f} GB/s (read + write)")
+    traffic = measured_traffic()
 
     result = {
         "metric": METRIC,
@@ -209,7 +272,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32",  # fp32 accumulation; x as f16 (HALF GEMV) or fp32, codes u8
         "data": "synthetic",
         "config": {
             "workload": (f"Qwen3.5-4B-shaped {args.layers}-layer hybrid stack "
@@ -227,9 +290,10 @@ def main():
         "gdn_layer_us": round(gdn_us, 2),
         "full_layer_us": round(full_us, 2),
         "lm_head_us": round(lm_us, 2),
+        "copy_gbs": round(copy_gbs, 1),
         "roofline": {"bound": "hbm", "kernel": "gemv_kernel<2560,true> (post-norm gate/up SwiGLU)",
                      "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": dom_bytes, "us_per_launch": round(dom_us, 3)},
     }
     if not args.no_cpu_baseline:

@@ -67,6 +67,12 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+def is_built() -> bool:
+    """Whether the library exists (callers load what is built; they build only
+    when nothing is)."""
+    return os.path.exists(LIB)
+
+
 def is_stale() -> bool:
     if not os.path.exists(LIB):
         return True

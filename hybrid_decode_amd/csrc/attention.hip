@@ -19,7 +19,7 @@
 //       their rows (base-2 exponent), then merge in LDS and the block writes
 //       one (max, sum, unnormalised output) triple per query head.  Each K/V
 //       row is read once for all G heads of its group (the GQA reuse).
-//   attn_merge_kernel    grid (q head, D/64), 256 threads: log-sum-exp merge
+//   attn_merge_kernel    grid (q head, D/32), 256 threads: log-sum-exp merge
 //       of the chunk partials, the division by the total, the sigmoid gate.
 //
 // Layouts: K/V caches bf16 [capacity, Hkv, D] (token-major).
@@ -57,6 +57,7 @@ Q35_DEV int32_t attn_pos(const AttnArgs& a) {
 
 template <int D, int G>
 __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
+    static_assert(D <= kNT && D % 32 == 0, "one new-v element per thread; merge blocks of 32 dims");
     using Geo = AGeo<D>;
     constexpr int LPR = Geo::LPR, RPI = Geo::RPI, B = Geo::B;
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
@@ -69,6 +70,7 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     __shared__ float qs[(G + 1) * D];  // q heads of the group, then the new k
     __shared__ float vn[D];            // new v, bf16-rounded
     __shared__ float rsq[G + 1];
+    __shared__ float2 rot[D / 2];      // (cos, sin) of pos * inv_freq[d], d < rotary / 2
     __shared__ float mls[RPI][2 * G];  // per-slot (max, sum)
     __shared__ float red[RPI * D];     // per-slot outputs of one head
 
@@ -85,27 +87,49 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     // ---------------- first batch of K/V loads, in flight during the prologue
     const uint32_t row_bytes = a.hkv * D * 2u;
     const uint32_t span = (t1 - t0) * row_bytes;
+
+    // ---------------- the prologue's own loads go out first (vector loads
+    // complete in order, so the prologue then waits for them alone)
+    constexpr int PQ = ((G + 1) * D + kNT - 1) / kNT;  // q/k elements per thread
+    float qv[PQ], nv[PQ];
+#pragma unroll
+    for (int r = 0; r < PQ; ++r) {
+        const int e = min(t + kNT * r, (G + 1) * D - 1);  // clamped: no branch around the loads
+        const int i = e / D, d = e % D;
+        qv[r] = (i < G) ? a.q_full[(size_t)(g * G + i) * 2 * D + d] : a.k[g * D + d];
+        nv[r] = bf16_to_f32((i < G) ? a.q_norm[d] : a.k_norm[d]);
+    }
+    const float vnew = a.v[g * D + min(t, D - 1)];
+    const float invf = a.inv_freq[min(t, (int)a.rotary / 2 - 1)];
+    asm volatile("" ::: "memory");
+
     const auto rk = rsrc(a.kc + ((size_t)t0 * a.hkv + g) * D, span);
     const auto rv = rsrc(a.vc + ((size_t)t0 * a.hkv + g) * D, span);
-    uint4 kr[kUnroll], vr[kUnroll];
-    auto load_batch = [&](uint32_t tb) {
+    // two batches in flight: the next batch's rows load while this one computes
+    uint4 kr[2][kUnroll], vr[2][kUnroll];
+    auto load_batch = [&](uint4 (&kd)[kUnroll], uint4 (&vd)[kUnroll], uint32_t tb) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const uint32_t tt = tb + u * RPI + rs;
             const bool live = tt < t1 && tt != (uint32_t)pos;
             const uint32_t off = live ? (tt - t0) * row_bytes + 16u * j : span;  // past the end: zero
-            kr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kAuxStream));
-            vr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, kAuxStream));
+            kd[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kAuxStream));
+            vd[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, kAuxStream));
         }
     };
-    load_batch(t0);
+    load_batch(kr[0], vr[0], t0);
+    load_batch(kr[1], vr[1], t0 + B);  // loads past the chunk return zero and are never used
 
     // ---------------- prologue: q heads of this group and the new k, v
-    for (int e = t; e < (G + 1) * D; e += kNT) {
-        const int i = e / D, d = e % D;
-        qs[e] = (i < G) ? a.q_full[(size_t)(g * G + i) * 2 * D + d] : a.k[g * D + d];
+#pragma unroll
+    for (int r = 0; r < PQ; ++r)
+        if (t + kNT * r < (G + 1) * D) qs[t + kNT * r] = qv[r];
+    if (t < D) vn[t] = bf16_to_f32(f32_to_bf16(vnew));
+    if (t < (int)a.rotary / 2) {
+        float sn, cs;
+        sincosf((float)rope_pos * invf, &sn, &cs);
+        rot[t] = make_float2(cs, sn);
     }
-    for (int d = t; d < D; d += kNT) vn[d] = bf16_to_f32(f32_to_bf16(a.v[g * D + d]));
     __syncthreads();
     for (int i = wid; i < G + 1; i += kNT / 64) {
         float ss = 0.f;
@@ -114,19 +138,17 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
         if (lane == 0) rsq[i] = 1.0f / sqrtf(ss / (float)D + a.eps);
     }
     __syncthreads();
-    for (int e = t; e < (G + 1) * D; e += kNT) {
-        const int i = e / D, d = e % D;
-        const uint16_t* w = (i < G) ? a.q_norm : a.k_norm;
-        qs[e] = qs[e] * rsq[i] * bf16_to_f32(w[d]);
+#pragma unroll
+    for (int r = 0; r < PQ; ++r) {
+        const int e = t + kNT * r;
+        if (e < (G + 1) * D) qs[e] = qs[e] * rsq[e / D] * nv[r];
     }
     __syncthreads();
     {
         const int half = (int)a.rotary / 2;
         for (int e = t; e < (G + 1) * half; e += kNT) {
             const int i = e / half, d = e % half;
-            const float ang = (float)rope_pos * a.inv_freq[d];
-            float sn, cs;
-            sincosf(ang, &sn, &cs);
+            const float cs = rot[d].x, sn = rot[d].y;
             const float x1 = qs[i * D + d], x2 = qs[i * D + d + half];
             qs[i * D + d] = x1 * cs - x2 * sn;
             qs[i * D + d + half] = x2 * cs + x1 * sn;
@@ -143,7 +165,7 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
         for (int d = t; d < D; d += kNT) {
             const uint32_t kb = f32_to_bf16(qs[G * D + d]);
             krow[d] = (uint16_t)kb;
-            vrow[d] = (uint16_t)f32_to_bf16(a.v[g * D + d]);
+            vrow[d] = (uint16_t)f32_to_bf16(vn[d]);  // vn is already bf16-exact
             qs[G * D + d] = bf16_to_f32(kb);  // attend to the row as stored
         }
         __syncthreads();
@@ -166,7 +188,7 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
         for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
     }
 
-    for (uint32_t tb = t0;;) {
+    auto batch = [&](const uint4 (&kd)[kUnroll], const uint4 (&vd)[kUnroll], uint32_t tb) {
         float s[kUnroll][G];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -176,7 +198,7 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) kv[e] = qs[G * D + 8 * j + e];
             } else {
-                unpack8(kr[u], kv);
+                unpack8(kd[u], kv);
             }
 #pragma unroll
             for (int i = 0; i < G; ++i) {
@@ -209,7 +231,7 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) vv[e] = vn[8 * j + e];
             } else {
-                unpack8(vr[u], vv);
+                unpack8(vd[u], vv);
             }
 #pragma unroll
             for (int i = 0; i < G; ++i) {
@@ -218,9 +240,17 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
                 for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(s[u][i], vv[e], acc[i][e]);
             }
         }
-        tb += B;
-        if (tb >= t1) break;
-        load_batch(tb);
+    };
+    // Reloads are unconditional (rows past the chunk read zero and move no
+    // data), so the count of loads in flight is the same on every path and
+    // each wait is for the batch about to be used alone.
+    for (uint32_t tb = t0;; tb += 2 * B) {
+        batch(kr[0], vr[0], tb);
+        if (tb + B >= t1) break;
+        load_batch(kr[0], vr[0], tb + 2 * B);
+        batch(kr[1], vr[1], tb + B);
+        if (tb + 2 * B >= t1) break;
+        load_batch(kr[1], vr[1], tb + 3 * B);
     }
 
     // ---------------- merge the row slots, write this chunk's partials
@@ -257,12 +287,19 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     }
 }
 
-// grid (Hq, D/64); thread t: dim d0 + (t & 63), chunk lane t >> 6.
+// grid (Hq, D/32); thread t: dim d0 + t % 32, chunk lane t / 32.  Each thread
+// issues its first kPrefetch partial loads before the weights are known, so the
+// partials and the (max, sum) pairs arrive together.
+constexpr int kMergeDims = 32;
+constexpr int kMergeLanes = kNT / kMergeDims;
+constexpr int kPrefetch = 16;
+
 template <int D, int G>
 __global__ __launch_bounds__(kNT) void attn_merge_kernel(AttnArgs a) {
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int dl = t % kMergeDims, cl = t / kMergeDims;
     const uint32_t h = blockIdx.x, g = h / G, i = h % G;
-    const uint32_t d = blockIdx.y * 64 + lane;
+    const uint32_t d = blockIdx.y * kMergeDims + dl;
     extern __shared__ float wsh[];  // [max_chunks] chunk weights
     __shared__ float red[kNT];
     __shared__ float stat[kNT / 64];
@@ -270,6 +307,16 @@ __global__ __launch_bounds__(kNT) void attn_merge_kernel(AttnArgs a) {
     const int32_t pos = attn_pos(a);
     if (pos < 0 || (uint32_t)pos >= a.capacity) return;
     const uint32_t nch = ((uint32_t)pos + a.chunk) / a.chunk;
+
+    // partials of head h, dim d: part_acc[g][cc][i][d], chunk stride G*D floats
+    const uint32_t cstride = (uint32_t)(G * D) * 4u;
+    const auto racc = rsrc(a.part_acc + ((size_t)g * a.max_chunks * G + i) * D, nch * cstride);
+    float pa[kPrefetch];
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+        const uint32_t cc = (uint32_t)(cl + kMergeLanes * k);
+        pa[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(racc, cc * cstride + d * 4u, 0, 0));
+    }
     const float* pml = a.part_ml + (size_t)g * a.max_chunks * 2 * G + 2 * i;
 
     float mx = -INFINITY;
@@ -277,23 +324,31 @@ __global__ __launch_bounds__(kNT) void attn_merge_kernel(AttnArgs a) {
     mx = wave_max(mx);
     if (lane == 0) red[wid] = mx;
     __syncthreads();
-    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float M = red[0];
+#pragma unroll
+    for (int w = 1; w < kNT / 64; ++w) M = fmaxf(M, red[w]);
     float tot = 0.f;
     for (uint32_t cc = t; cc < nch; cc += kNT) {
         const float w = exp2f(pml[cc * 2 * G] - M);
         wsh[cc] = w;
         tot = fmaf(w, pml[cc * 2 * G + 1], tot);
     }
-    tot = block_sum<kNT>(tot, stat);  // its barriers also publish wsh
+    tot = block_sum<kNT>(tot, stat);  // its barriers also publish wsh (and free red)
 
-    const float* pa = a.part_acc + ((size_t)g * a.max_chunks * G + i) * D + d;
     float o = 0.f;
-#pragma unroll 8
-    for (uint32_t cc = wid; cc < nch; cc += kNT / 64) o = fmaf(wsh[cc], pa[(size_t)cc * G * D], o);
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+        const uint32_t cc = (uint32_t)(cl + kMergeLanes * k);
+        if (cc < nch) o = fmaf(wsh[cc], pa[k], o);
+    }
+    for (uint32_t cc = cl + kMergeLanes * kPrefetch; cc < nch; cc += kMergeLanes)
+        o = fmaf(wsh[cc], __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(racc, cc * cstride + d * 4u, 0, 0)), o);
     red[t] = o;
     __syncthreads();
-    if (wid == 0) {
-        o = (red[lane] + red[lane + 64]) + (red[lane + 128] + red[lane + 192]);
+    if (cl == 0) {
+        o = 0.f;
+#pragma unroll
+        for (int c2 = 0; c2 < kMergeLanes; ++c2) o += red[c2 * kMergeDims + dl];
         o /= tot;
         if (a.attn_out) a.attn_out[h * D + d] = o;
         const float gate = a.q_full[(size_t)h * 2 * D + D + d];
@@ -306,7 +361,7 @@ hipError_t launch_t(const AttnArgs& a, uint32_t grid_chunks, hipStream_t stream)
     hipLaunchKernelGGL((attn_partial_kernel<D, G>), dim3(grid_chunks, a.hkv), dim3(kNT), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_merge_kernel<D, G>), dim3(a.hq, D / 64), dim3(kNT),
+    hipLaunchKernelGGL((attn_merge_kernel<D, G>), dim3(a.hq, D / kMergeDims), dim3(kNT),
                        (size_t)a.max_chunks * sizeof(float), stream, a);
     return hipGetLastError();
 }

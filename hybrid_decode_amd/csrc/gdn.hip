@@ -9,7 +9,7 @@
 //     S     <- S + k delta^T
 //     y      = S^T q / sqrt(dk)
 // Columns of S are independent, so the grid splits each head into tiles of
-// 32 columns.  With a = S_old^T k and b = S_old^T q the step is
+// 16 columns.  With a = S_old^T k and b = S_old^T q the step is
 //     delta = beta (v - g a),   y = (g b + (k.q) delta) / sqrt(dk),
 //     S'    = g S_old + k delta^T,
 // so one pass over the state computes both dot products, and one more writes
@@ -22,50 +22,80 @@
 namespace q35 {
 namespace {
 
-constexpr int kNT = 256;
-constexpr int kCT = 32;  // state columns per block
+constexpr int kCT = 16;  // state columns per block
 
+// Threads: 2*DK.  Thread t holds state rows {2r, 2r+1} (r = t / 4) for the 4
+// columns 4c..4c+3 (c = t % 4) of the block's tile: two float4 per thread.
 template <int DK>
-__global__ __launch_bounds__(kNT) void gdn_kernel(GdnArgs a) {
+__global__ __launch_bounds__(2 * DK) void gdn_kernel(GdnArgs a) {
     constexpr int DV = DK;
-    constexpr int RJ = DK / 32;  // state rows per thread
-    __shared__ float qs[DK], ks[DK], vs[kCT], dl[kCT];
-    __shared__ float red[3][kNT / 64];
-    __shared__ float part[kNT / 64][8][8];
+    constexpr int NT = 2 * DK, NW = (NT + 63) / 64;
+    constexpr int NPR = NT / 16;  // 16-lane DPP rows; each sums 4 row pairs (8 state rows)
+    static_assert(NT >= 64 && kCT == 16, "at least one wave; a DPP row covers the 16 columns");
+    __shared__ float dl[kCT];
+    __shared__ float red[3][NW];
+    __shared__ float part[NPR][2][kCT];  // per DPP row: a and b partials of the tile's columns
 
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-    const int cq = t & 7, rgp = t >> 3;
+    const int cq = t & 3, r = t >> 2;
     const uint32_t h = blockIdx.y;
     const uint32_t col0 = blockIdx.x * kCT;
     const uint32_t rep = a.hv / a.hk;
     const uint32_t i = h / rep;
+    const uint32_t row0 = 2 * r;
 
-    // 1. state tile -> registers (issued first: the longest-latency loads)
-    float4 S[RJ];
+    // 1. every load is issued up front: the state tile, this thread's two q and
+    //    k entries (raw; the L2 norms become two scalar factors), v, gate, beta
     float* sbase = a.state + (size_t)h * DK * DV + col0 + 4 * cq;
-#pragma unroll
-    for (int j = 0; j < RJ; ++j) S[j] = *reinterpret_cast<const float4*>(sbase + (size_t)(rgp + 32 * j) * DV);
-
-    // 2. q, k of k-head i; v slice of v-head h; gate, beta
-    float qv = 0.f, kv = 0.f;
-    if (t < DK) {
-        qv = a.qkv_conv[i * DK + t];
-        kv = a.qkv_conv[a.hk * DK + i * DK + t];
-    }
-    if (t < kCT) vs[t] = a.qkv_conv[2 * a.hk * DK + h * DV + col0 + t];
+    const float4 S0 = *reinterpret_cast<const float4*>(sbase + (size_t)row0 * DV);
+    const float4 S1 = *reinterpret_cast<const float4*>(sbase + (size_t)(row0 + 1) * DV);
+    const float2 qr = *reinterpret_cast<const float2*>(a.qkv_conv + i * DK + row0);
+    const float2 kr = *reinterpret_cast<const float2*>(a.qkv_conv + a.hk * DK + i * DK + row0);
+    const float vv = a.qkv_conv[2 * a.hk * DK + h * DV + col0 + min(t, kCT - 1)];
     const float g = a.gate[h];
     const float beta = a.beta[h];
 
-    float r0 = wave_sum(qv * qv), r1 = wave_sum(kv * kv), r2 = wave_sum(kv * qv);
+    // 2. partial a = S^T k, b = S^T q (raw q, k) and the norms' sums, reduced
+    //    over the rows of each 16-lane DPP row (lanes of equal column quad)
+    float pa[4], pb[4];
+    pa[0] = fmaf(S0.x, kr.x, S1.x * kr.y);
+    pa[1] = fmaf(S0.y, kr.x, S1.y * kr.y);
+    pa[2] = fmaf(S0.z, kr.x, S1.z * kr.y);
+    pa[3] = fmaf(S0.w, kr.x, S1.w * kr.y);
+    pb[0] = fmaf(S0.x, qr.x, S1.x * qr.y);
+    pb[1] = fmaf(S0.y, qr.x, S1.y * qr.y);
+    pb[2] = fmaf(S0.z, qr.x, S1.z * qr.y);
+    pb[3] = fmaf(S0.w, qr.x, S1.w * qr.y);
+    // rotating a 16-lane row by 4 and then 8 keeps lane & 3 (the column quad):
+    // every lane ends with the sum over the row's 4 row pairs for its columns
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        pa[c] += dpp<0x124>(pa[c]);  // row_ror:4
+        pb[c] += dpp<0x124>(pb[c]);
+        pa[c] += dpp<0x128>(pa[c]);  // row_ror:8
+        pb[c] += dpp<0x128>(pb[c]);
+    }
+    const bool own = cq == 0;  // one thread per row pair feeds the norms
+    float r0 = wave_sum(own ? fmaf(qr.x, qr.x, qr.y * qr.y) : 0.f);
+    float r1 = wave_sum(own ? fmaf(kr.x, kr.x, kr.y * kr.y) : 0.f);
+    float r2 = wave_sum(own ? fmaf(kr.x, qr.x, kr.y * qr.y) : 0.f);
     if (lane == 0) {
         red[0][wid] = r0;
         red[1][wid] = r1;
         red[2][wid] = r2;
     }
+    if ((lane & 15) < 4) {  // lanes 0..3 of each DPP row: column quads 0..3
+        const int pr = t >> 4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            part[pr][0][4 * cq + c] = pa[c];
+            part[pr][1][4 * cq + c] = pb[c];
+        }
+    }
     __syncthreads();
     float qq = 0.f, kk = 0.f, kq = 0.f;
 #pragma unroll
-    for (int w = 0; w < kNT / 64; ++w) {
+    for (int w = 0; w < NW; ++w) {
         qq += red[0][w];
         kk += red[1][w];
         kq += red[2][w];
@@ -73,78 +103,44 @@ __global__ __launch_bounds__(kNT) void gdn_kernel(GdnArgs a) {
     const float rq = 1.0f / sqrtf(qq + a.l2_eps);
     const float rk = 1.0f / sqrtf(kk + a.l2_eps);
     kq *= rq * rk;
-    if (t < DK) {
-        qs[t] = qv * rq;
-        ks[t] = kv * rk;
-    }
-    if (a.qkv_smooth) {
-        if (blockIdx.x == 0 && (h % rep) == 0 && t < DK) {
-            a.qkv_smooth[i * DK + t] = qv * rq;
-            a.qkv_smooth[a.hk * DK + i * DK + t] = kv * rk;
-        }
-        if (t < kCT) a.qkv_smooth[2 * a.hk * DK + h * DV + col0 + t] = vs[t];
-    }
-    __syncthreads();
 
-    // 3. a = S^T k, b = S^T q over this thread's rows, for its 4 columns
-    float pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < RJ; ++j) {
-        const float kr = ks[rgp + 32 * j], qr = qs[rgp + 32 * j];
-        pa[0] = fmaf(S[j].x, kr, pa[0]);
-        pa[1] = fmaf(S[j].y, kr, pa[1]);
-        pa[2] = fmaf(S[j].z, kr, pa[2]);
-        pa[3] = fmaf(S[j].w, kr, pa[3]);
-        pb[0] = fmaf(S[j].x, qr, pb[0]);
-        pb[1] = fmaf(S[j].y, qr, pb[1]);
-        pb[2] = fmaf(S[j].z, qr, pb[2]);
-        pb[3] = fmaf(S[j].w, qr, pb[3]);
-    }
-    // sum over the 8 row groups of this wave that share cq (lane bits 3..5)
-#pragma unroll
-    for (int o = 8; o < 64; o <<= 1) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            pa[c] += __shfl_xor(pa[c], o);
-            pb[c] += __shfl_xor(pb[c], o);
-        }
-    }
-    if (lane < 8) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            part[wid][lane][c] = pa[c];
-            part[wid][lane][4 + c] = pb[c];
-        }
-    }
-    __syncthreads();
-
-    // 4. per column: delta and y
+    // 3. per column: delta and y
     if (t < kCT) {
-        const int q4 = t >> 2, c = t & 3;
         float av = 0.f, bv = 0.f;
 #pragma unroll
-        for (int w = 0; w < kNT / 64; ++w) {
-            av += part[w][q4][c];
-            bv += part[w][q4][4 + c];
+        for (int w = 0; w < NPR; ++w) {
+            av += part[w][0][t];
+            bv += part[w][1][t];
         }
-        const float d = beta * (vs[t] - g * av);
+        const float d = beta * (vv - g * av * rk);
         dl[t] = d;
-        a.y[h * DV + col0 + t] = (g * bv + kq * d) * a.out_scale;
+        a.y[h * DV + col0 + t] = (g * bv * rq + kq * d) * a.out_scale;
+    }
+    if (a.qkv_smooth) {
+        if (blockIdx.x == 0 && (h % rep) == 0 && own) {
+            a.qkv_smooth[i * DK + row0] = qr.x * rq;
+            a.qkv_smooth[i * DK + row0 + 1] = qr.y * rq;
+            a.qkv_smooth[a.hk * DK + i * DK + row0] = kr.x * rk;
+            a.qkv_smooth[a.hk * DK + i * DK + row0 + 1] = kr.y * rk;
+        }
+        if (t < kCT) a.qkv_smooth[2 * a.hk * DK + h * DV + col0 + t] = vv;
     }
     __syncthreads();
 
-    // 5. S' = g S + k delta^T
+    // 4. S' = g S + k delta^T (k normalised)
     const float d0 = dl[4 * cq], d1 = dl[4 * cq + 1], d2 = dl[4 * cq + 2], d3 = dl[4 * cq + 3];
-#pragma unroll
-    for (int j = 0; j < RJ; ++j) {
-        const float kr = ks[rgp + 32 * j];
-        float4 o;
-        o.x = fmaf(kr, d0, g * S[j].x);
-        o.y = fmaf(kr, d1, g * S[j].y);
-        o.z = fmaf(kr, d2, g * S[j].z);
-        o.w = fmaf(kr, d3, g * S[j].w);
-        *reinterpret_cast<float4*>(sbase + (size_t)(rgp + 32 * j) * DV) = o;
-    }
+    const float k0 = kr.x * rk, k1 = kr.y * rk;
+    float4 o0, o1;
+    o0.x = fmaf(k0, d0, g * S0.x);
+    o0.y = fmaf(k0, d1, g * S0.y);
+    o0.z = fmaf(k0, d2, g * S0.z);
+    o0.w = fmaf(k0, d3, g * S0.w);
+    o1.x = fmaf(k1, d0, g * S1.x);
+    o1.y = fmaf(k1, d1, g * S1.y);
+    o1.z = fmaf(k1, d2, g * S1.z);
+    o1.w = fmaf(k1, d3, g * S1.w);
+    *reinterpret_cast<float4*>(sbase + (size_t)row0 * DV) = o0;
+    *reinterpret_cast<float4*>(sbase + (size_t)(row0 + 1) * DV) = o1;
 }
 
 }  // namespace
@@ -156,9 +152,9 @@ bool gdn_dims_supported(uint32_t dk, uint32_t dv) {
 hipError_t gdn_launch(uint32_t dk, uint32_t dv, const GdnArgs& a, hipStream_t stream) {
     dim3 grid(dv / kCT, a.hv);
     switch (dk) {
-        case 32: hipLaunchKernelGGL(gdn_kernel<32>, grid, dim3(kNT), 0, stream, a); break;
-        case 64: hipLaunchKernelGGL(gdn_kernel<64>, grid, dim3(kNT), 0, stream, a); break;
-        case 128: hipLaunchKernelGGL(gdn_kernel<128>, grid, dim3(kNT), 0, stream, a); break;
+        case 32: hipLaunchKernelGGL(gdn_kernel<32>, grid, dim3(64), 0, stream, a); break;
+        case 64: hipLaunchKernelGGL(gdn_kernel<64>, grid, dim3(128), 0, stream, a); break;
+        case 128: hipLaunchKernelGGL(gdn_kernel<128>, grid, dim3(256), 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

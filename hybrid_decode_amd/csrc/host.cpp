@@ -717,6 +717,8 @@ q35_status q35_lm_head_argmax(const Qwen35Kernels* kernels, const Qwen35ForwardC
     if ((embed_table == nullptr) != (x_next == nullptr))
         return fail(Q35_ERR_INVALID_ARG, "embed_table and x_next go together");
     if (x_next && x_next == x) return fail(Q35_ERR_INVALID_ARG, "x_next aliases x");
+    Q35_TRY(opt(embed_table, "embed_table"));
+    Q35_TRY(opt(x_next, "x_next"));
     const LmWs ws = lm_ws_layout(c);
     if (workspace_bytes < ws.total)
         return fail(Q35_ERR_INVALID_ARG, "workspace %zu bytes < %zu required", workspace_bytes, ws.total);

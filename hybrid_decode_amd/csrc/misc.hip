@@ -20,19 +20,33 @@ Q35_DEV bool better_tok(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
 
-__global__ __launch_bounds__(256) void lm_finish_kernel(LmFinishArgs a) {
-    __shared__ float sv[4];
-    __shared__ int si[4];
+constexpr int kFinishThreads = 256;
+constexpr int kFinishPer = 16;  // partials each thread loads before comparing
+
+__global__ __launch_bounds__(kFinishThreads) void lm_finish_kernel(LmFinishArgs a) {
+    __shared__ float sv[kFinishThreads / 64];
+    __shared__ int si[kFinishThreads / 64];
     __shared__ int tok_sh;
+    const int t = threadIdx.x;
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
-    for (uint32_t b = threadIdx.x; b < a.nparts; b += blockDim.x) {
-        const float v = a.part_val[b];
-        const int i = a.part_idx[b];
-        if (better_tok(v, i, bv, bi)) {
-            bv = v;
-            bi = i;
+    // all loads of a round are issued before any comparison
+    for (uint32_t base = 0; base < a.nparts; base += kFinishThreads * kFinishPer) {
+        float v[kFinishPer];
+        int ix[kFinishPer];
+#pragma unroll
+        for (int r = 0; r < kFinishPer; ++r) {
+            const uint32_t b = base + t + kFinishThreads * r;
+            const bool in = b < a.nparts;
+            v[r] = in ? a.part_val[b] : -INFINITY;
+            ix[r] = in ? a.part_idx[b] : 0x7FFFFFFF;
         }
+#pragma unroll
+        for (int r = 0; r < kFinishPer; ++r)
+            if (better_tok(v[r], ix[r], bv, bi)) {
+                bv = v[r];
+                bi = ix[r];
+            }
     }
     for (int o = 32; o > 0; o >>= 1) {
         const float ov = __shfl_xor(bv, o);
@@ -42,14 +56,14 @@ __global__ __launch_bounds__(256) void lm_finish_kernel(LmFinishArgs a) {
             bi = oi;
         }
     }
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = t & 63, wid = t >> 6;
     if (lane == 0) {
         sv[wid] = bv;
         si[wid] = bi;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int w = 1; w < 4; ++w)
+    if (t == 0) {
+        for (int w = 1; w < kFinishThreads / 64; ++w)
             if (better_tok(sv[w], si[w], sv[0], si[0])) {
                 sv[0] = sv[w];
                 si[0] = si[w];
@@ -66,16 +80,29 @@ __global__ __launch_bounds__(256) void lm_finish_kernel(LmFinishArgs a) {
     }
     __syncthreads();
     if (a.embed) {
-        const uint16_t* row = a.embed + (size_t)tok_sh * a.hidden;
-        for (uint32_t k = threadIdx.x; k < a.hidden; k += blockDim.x)
-            store_act(a.x_next, k, bf16_to_f32(row[k]), a.act_f32 != 0);
+        // the next token's embedding row, 8 elements (16 bytes) per thread and step
+        const uint4* row = reinterpret_cast<const uint4*>(a.embed + (size_t)tok_sh * a.hidden);
+        const bool f32 = a.act_f32 != 0;
+        for (uint32_t c = t; c < a.hidden / 8; c += kFinishThreads) {
+            const uint4 u = row[c];
+            if (f32) {
+                float4* o = reinterpret_cast<float4*>(a.x_next) + 2 * c;
+                o[0] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+                o[1] = make_float4(bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w));
+            } else {
+                reinterpret_cast<uint4*>(a.x_next)[c] = u;
+            }
+        }
     }
 }
 
 }  // namespace
 
 hipError_t lm_finish_launch(const LmFinishArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(lm_finish_kernel, dim3(1), dim3(256), 0, stream, a);
+    if (a.embed && (a.hidden % 8 != 0 || (reinterpret_cast<uintptr_t>(a.embed) & 15) ||
+                    (reinterpret_cast<uintptr_t>(a.x_next) & 15)))
+        return hipErrorInvalidValue;  // the row copy moves 16-byte words
+    hipLaunchKernelGGL(lm_finish_kernel, dim3(1), dim3(kFinishThreads), 0, stream, a);
     return hipGetLastError();
 }
 

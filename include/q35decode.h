@@ -196,9 +196,8 @@ typedef struct FullAttentionLayer {
  *   q_full [q_total], k [kv_dim], v [kv_dim], gated_attn [q_only],
  *   x_resid [hidden], mlp_act [intermediate] (= silu(gate) * up),
  *   x_out [hidden] (act dtype),
- *   workspace (bytes from q35_full_attention_workspace_bytes; the caller
- *   zero-fills it once after allocation; every call leaves its counters at
- *   zero again).
+ *   workspace (bytes from q35_full_attention_workspace_bytes: per-chunk
+ *   attention partials, rewritten by every call; no initialisation needed).
  * Optional taps, written when non-NULL (fp32): x_norm [hidden],
  *   q_norm_out [q_only] (post-RoPE q), k_norm_out [kv_dim] (post-RoPE k),
  *   attn_out [q_only], o [hidden], x_norm2 [hidden], gate_act [intermediate],
@@ -369,7 +368,7 @@ q35_status q35_embed_lookup(const Qwen35Kernels* kernels, const Qwen35ForwardCon
                             const uint16_t* table, const int32_t* tokens, void* x_out,
                             hipStream_t stream);
 
-/* Workspace bytes q35_lm_head_argmax needs (zero-filled once by the caller). */
+/* Workspace bytes q35_lm_head_argmax needs (scratch: no initialisation needed). */
 q35_status q35_lm_head_workspace_bytes(const Qwen35ForwardConfig* cfg, size_t* bytes);
 
 /*
@@ -379,8 +378,10 @@ q35_status q35_lm_head_workspace_bytes(const Qwen35ForwardConfig* cfg, size_t* b
  * (may be NULL): logits fp32 [vocab]; history int32 [history_len], which
  * receives the token at index positions[0] - history_base when that lies in
  * range; positions int32 [1], incremented by one after the token is chosen;
- * embed_table bf16 [vocab, hidden] with x_next act [hidden], which then
- * receives the chosen token's embedding (the next step's input).
+ * embed_table bf16 [vocab, hidden] with x_next act [hidden] (both 16-byte
+ * aligned), which then receives the chosen token's embedding (the next step's
+ * input).  Two launches: the GEMV leaves one (max, row) pair per block in the
+ * workspace and a one-block kernel reduces them, so no block waits on another.
  */
 q35_status q35_lm_head_argmax(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
                               const uint16_t* final_norm, const Q35QuantWeight* lm_head,

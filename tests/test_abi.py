@@ -23,7 +23,7 @@ FAKE_KERNELS = 0x1000  # a non-NULL handle: only the argument checks run before 
 @pytest.fixture(scope="module")
 def lib():
     from hybrid_decode_amd import build
-    if build.is_stale():
+    if not build.is_built():
         build.build(verbose=False)
     return B.lib()
 
