@@ -136,8 +136,10 @@ def test_full_layer_tiny_fp32_every_step_tap_and_append(rt, gen):
         assert np.array_equal(after["v"][t], O.f64_to_bf16(vv.astype(np.float64)))
 
 
-def test_gdn_layer_4b_bf16_64_steps_and_state(rt, gen):
-    w = workloads.gdn_layer_4b(gen, steps=64)
+def test_gdn_layer_4b_bf16_256_steps_and_state(rt, gen):
+    """Config 2: 256 sequential steps; every output within the bf16 tolerance, the
+    fp32 GDN and conv states within 1e-3 after 64 steps (and reported at 256)."""
+    w = workloads.gdn_layer_4b(gen, steps=256)
     cfg, layer, st = w["cfg"], w["layer"], w["state"]
     L, S = rt.GdnLayerDev(layer), rt.GdnStateDev(st)
     scr = rt.GdnScratchDev(cfg)
@@ -145,7 +147,7 @@ def test_gdn_layer_4b_bf16_64_steps_and_state(rt, gen):
     ost = st
     worst = 0.0
     for t, x in enumerate(w["xs"]):
-        if t % 16 == 0:
+        if t % 32 == 0:
             say(f"4B GDN step {t}")
         rt.forward_linear_attention(cfg, L, S, scr, rt.to_dev(x), x_buf)
         ox, ost, _ = O.forward_linear_attention(cfg, layer, ost, x)
@@ -153,16 +155,23 @@ def test_gdn_layer_4b_bf16_64_steps_and_state(rt, gen):
         r = rel(rt.act_to_f32(x_buf, cfg), ox)
         worst = max(worst, r)
         assert r < TOL_BF16, (t, r)
+        if t == 63:
+            gst = S.to_host()
+            r_state = rel(gst["gdn_state"], ost["gdn_state"])
+            r_conv = rel(gst["conv1d_state"], ost["conv1d_state"])
+            say(f"4B GDN after 64 steps: state rel {r_state:.2e}, conv rel {r_conv:.2e}")
+            assert r_state < TOL_F32
+            assert r_conv < TOL_F32
     gst = S.to_host()
-    r_state = rel(gst["gdn_state"], ost["gdn_state"])
-    r_conv = rel(gst["conv1d_state"], ost["conv1d_state"])
-    say(f"4B GDN: worst output rel {worst:.2e}, state rel after 64 steps {r_state:.2e}, conv {r_conv:.2e}")
-    assert r_state < TOL_F32
-    assert r_conv < TOL_F32
+    say(f"4B GDN: worst output rel {worst:.2e}; after 256 steps state rel "
+        f"{rel(gst['gdn_state'], ost['gdn_state']):.2e}")
 
 
-def test_full_layer_4b_bf16_prefilled_cache(rt, gen):
-    w = workloads.full_layer_4b(gen, steps=4)
+def test_full_layer_4b_bf16_64_steps_from_4096(rt, gen):
+    """Config 3: 64 steps at cache_pos 4096..4159 over a prefilled bf16 cache;
+    every output within the bf16 tolerance, KV placement exact."""
+    steps = 64
+    w = workloads.full_layer_4b(gen, steps=steps)
     cfg, layer, kv = w["cfg"], w["layer"], w["kv"]
     start = w["start"]
     cap = kv["k"].shape[0]
@@ -174,29 +183,35 @@ def test_full_layer_4b_bf16_prefilled_cache(rt, gen):
     inv_h = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
     okv = {"k": kv["k"].copy(), "v": kv["v"].copy()}
     outs = []
+    worst = 0.0
     for i, x in enumerate(w["xs"]):
         t = start + i
-        say(f"4B full attention at cache_pos {t}")
+        if i % 16 == 0:
+            say(f"4B full attention at cache_pos {t}")
         pos = torch.tensor([t], dtype=torch.int32, device="cuda")
         rt.forward_full_attention(cfg, Ld, scr, KVd, inv, pos, rt.to_dev(x), t)
         ox, okv, _ = O.forward_full_attention(cfg, layer, okv, inv_h, x, t)
         torch.cuda.synchronize()
         g = rt.act_to_f32(scr.t["x_out"], cfg)
         outs.append(g.copy())
-        assert rel(g, ox) < TOL_BF16, t
+        r = rel(g, ox)
+        worst = max(worst, r)
+        assert r < TOL_BF16, (t, r)
+    say(f"4B full attention: worst output rel {worst:.2e}")
     after = KVd.to_host()
     for side in ("k", "v"):
         assert np.array_equal(after[side][:start], kv[side][:start])          # prefill untouched
-        assert np.all(after[side][start + 4:] == NAN_BF16)                    # beyond: untouched
-        assert rel(O.bf16_to_f64(after[side][start:start + 4]),
-                   O.bf16_to_f64(okv[side][start:start + 4])) < TOL_BF16
+        assert np.all(after[side][start + steps:] == NAN_BF16)                # beyond: untouched
+        assert rel(O.bf16_to_f64(after[side][start:start + steps]),
+                   O.bf16_to_f64(okv[side][start:start + steps])) < TOL_BF16
 
     # device-side position (the graph-replay entry point) gives the same layer
     KV2 = rt.KvCacheDev(kv)
     scr2 = rt.FullScratchDev(cfg, cap)
     pos = torch.tensor([start], dtype=torch.int32, device="cuda")
     for i, x in enumerate(w["xs"]):
-        say(f"4B full attention, device position {start + i}")
+        if i % 16 == 0:
+            say(f"4B full attention, device position {start + i}")
         rt.forward_full_attention(cfg, Ld, scr2, KV2, inv, pos, rt.to_dev(x), None)
         torch.cuda.synchronize()
         assert rel(rt.act_to_f32(scr2.t["x_out"], cfg), outs[i]) < 1e-5

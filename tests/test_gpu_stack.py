@@ -1,6 +1,8 @@
 """GPU parity of the layer loop: the tiny two-layer hybrid at every step, and the
-4B-shaped stack (real lm_head, KV at 8192) on sampled layers, the logits and the
-greedy token, plus HIP-graph replay against eager execution."""
+32-layer 4B-shaped stack (real lm_head) at KV context 8192 and 65536 in the
+benchmark's launch configuration, on sampled layers (each fed the GPU's own
+input to that layer), sampled logits and the greedy token, plus HIP-graph replay
+against eager execution."""
 import numpy as np
 import pytest
 import torch
@@ -41,18 +43,21 @@ def test_tiny_stack_16_tokens(rt, gen):
     assert rel(S0.to_host()["gdn_state"], states[0]["gdn_state"]) < TOL_F32
 
 
-@pytest.fixture(scope="module")
-def stack8(rt):
-    """The 4B stack at 8 layers (two full-attention layers, ctx 8192): the same shapes,
-    launches and lm_head as the 32-layer benchmark stack, fewer layers."""
-    say("generating the 8-layer 4B stack")
+def _make_stack(rt, ctx):
+    say(f"generating the 32-layer 4B stack at ctx {ctx}")
     g = synth.Gen(0)
-    w = workloads.stack_4b(g, num_layers=8, ctx=8192, extra=64)
+    w = workloads.stack_4b(g, num_layers=32, ctx=ctx, extra=64)
     st = rt.DecodeStack(w["cfg"], w["kinds"], w["layers"], w["states"], w["kvs"], w["embed"],
                         w["final_norm"], w["lm_head"], start_pos=w["ctx"],
                         start_token=w["start_token"], history_len=64)
     torch.cuda.synchronize()
     return w, st
+
+
+@pytest.fixture(scope="module")
+def stack8k(rt):
+    """Config 4: 32 layers (8 full attention), KV at 8192 tokens, lm_head 248320."""
+    return _make_stack(rt, 8192)
 
 
 def _snapshot(st):
@@ -77,20 +82,21 @@ def _restore(st, snap):
     st.history.fill_(-1)
 
 
-def test_stack_4b_sampled_layers_logits_and_token(rt, stack8):
+def _check_one_token(rt, w, st, sample_layers):
+    """Runs one token layer by layer through the C-ABI (the same calls one graph
+    replay makes), checks the sampled layers against the oracle fed with the
+    GPU's input to that layer, then the lm_head on sampled rows and the token."""
     from hybrid_decode_amd import binding as B
-    w, st = stack8
     cfg, kinds = w["cfg"], w["kinds"]
     snap = _snapshot(st)
-    # embedding of the start token, bit-exact
     assert np.array_equal(rt.act_to_host(st.x_embed, cfg), w["embed"][w["start_token"]])
-    # run the layers one by one, keeping every layer's input and output
     s = rt.stream_ptr()
     x = st.x_embed.data_ptr()
-    ins, outs = [], []
+    ins, outs = {}, {}
+    last = st.x_embed
     for li, kind in enumerate(kinds):
-        say(f"4B stack layer {li} ({kind})")
-        ins.append(rt.act_to_host(st.x_embed if li == 0 else last, cfg).copy())
+        if li in sample_layers:
+            ins[li] = rt.act_to_host(last, cfg).copy()
         if kind == "gdn":
             B.q35_forward_linear_attention(st.k, st.c, st.layers[li].struct, st.states[li].struct,
                                            st.gdn_scratch.struct, x, st.x_main.data_ptr(), s)
@@ -101,18 +107,22 @@ def test_stack_4b_sampled_layers_logits_and_token(rt, stack8):
                                                 st.inv_freq.data_ptr(), st.positions.data_ptr(), x, s)
             last = st.full_scratch.t["x_out"]
         x = last.data_ptr()
-        torch.cuda.synchronize()
-        outs.append(rt.act_to_host(last, cfg).copy())
+        if li in sample_layers:
+            torch.cuda.synchronize()
+            outs[li] = rt.act_to_host(last, cfg).copy()
+    torch.cuda.synchronize()
+    x_last = rt.act_to_host(last, cfg).copy()
     inv_h = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
     pos = w["ctx"]
-    for li in (0, 1, 3, 7):   # GDN (first), GDN, full attention, full attention (last)
-        say(f"oracle check of layer {li}")
+    for li in sample_layers:
+        say(f"oracle check of layer {li} ({kinds[li]})")
         if kinds[li] == "gdn":
             ox, _, _ = O.forward_linear_attention(cfg, w["layers"][li], w["states"][li], ins[li])
         else:
             ox, _, _ = O.forward_full_attention(cfg, w["layers"][li], w["kvs"][li], inv_h, ins[li], pos)
-        assert rel(O.act_to_f64(outs[li], "bf16"), ox) < TOL_BF16, li
-    # lm_head + greedy token on the last layer's output
+        r = rel(O.act_to_f64(outs[li], "bf16"), ox)
+        say(f"  layer {li}: rel {r:.2e}")
+        assert r < TOL_BF16, li
     say("lm_head on the stack output")
     B.q35_lm_head_argmax(st.k, st.c, st.final_norm.data_ptr(), st.lm_head.struct, x,
                          st.logits.data_ptr(), st.lm_ws.data_ptr(), st.lm_ws.numel(),
@@ -124,18 +134,26 @@ def test_stack_4b_sampled_layers_logits_and_token(rt, stack8):
     rows = np.random.default_rng(0).choice(cfg.vocab, 4096, replace=False)
     tok = int(st.tokens.cpu()[0])
     rows = np.unique(np.concatenate([rows, [tok, int(np.argmax(g))]]))
-    h = O.rms_norm(O.act_to_f64(outs[-1], "bf16"), w["final_norm"], cfg.rms_eps)
+    h = O.rms_norm(O.act_to_f64(x_last, "bf16"), w["final_norm"], cfg.rms_eps)
     ref = O.dequant({k: v[rows] for k, v in w["lm_head"].items()}).astype(np.float64) @ h
     r = rel(g[rows], ref)
     say(f"sampled logits rel {r:.2e}")
     assert r < TOL_GEMV_F16
     assert tok == int(np.argmax(g))
     assert int(st.positions.cpu()[0]) == pos + 1
+    assert int(st.history.cpu()[0]) == tok
+    assert np.array_equal(rt.act_to_host(st.x_embed, cfg), w["embed"][tok])
     _restore(st, snap)
 
 
-def test_stack_4b_graph_replay_matches_eager(rt, stack8):
-    w, st = stack8
+def test_stack_4b_ctx8192_sampled_layers_logits_and_token(rt, stack8k):
+    w, st = stack8k
+    # first GDN, a middle GDN, first / middle / last full attention, last GDN before it
+    _check_one_token(rt, w, st, sample_layers=(0, 3, 13, 15, 30, 31))
+
+
+def test_stack_4b_ctx8192_graph_replay_matches_eager(rt, stack8k):
+    w, st = stack8k
     snap = _snapshot(st)
     steps = 6
     say("eager decode of 6 tokens")
@@ -145,6 +163,7 @@ def test_stack_4b_graph_replay_matches_eager(rt, stack8):
     eager_hist = st.history.cpu().numpy()[:steps].copy()
     eager_logits = st.logits.cpu().numpy().copy()
     eager_state = st.states[0].gdn_state.cpu().numpy().copy()
+    eager_k = st.kvs[3].k.cpu().numpy().copy()
     assert np.all(eager_hist >= 0)
     _restore(st, snap)
     say("capturing one decode step into a HIP graph")
@@ -167,4 +186,16 @@ def test_stack_4b_graph_replay_matches_eager(rt, stack8):
     assert np.array_equal(st.history.cpu().numpy()[:steps], eager_hist)
     assert np.array_equal(st.logits.cpu().numpy(), eager_logits)
     assert np.array_equal(st.states[0].gdn_state.cpu().numpy(), eager_state)
+    assert np.array_equal(st.kvs[3].k.cpu().numpy(), eager_k)
     _restore(st, snap)
+
+
+def test_stack_4b_ctx65536_sampled_layers_logits_and_token(rt):
+    """Config 5: the same stack with every KV cache filled to 65536 positions
+    (2.15 GB of bf16 KV), which stresses split-K attention at its longest."""
+    w, st = _make_stack(rt, 65536)
+    try:
+        _check_one_token(rt, w, st, sample_layers=(0, 3, 31))
+    finally:
+        del st
+        torch.cuda.empty_cache()
