@@ -35,7 +35,13 @@ EXPORTS = [
     "q35_full_attention_workspace_bytes", "q35_forward_full_attention",
     "q35_forward_full_attention_devpos", "q35_forward_linear_attention", "q35_embed_lookup",
     "q35_lm_head_workspace_bytes", "q35_lm_head_argmax", "q35_gate_up_swiglu", "q35_gemv",
+    "q35_decode_workspace_bytes", "q35_decode_plan_create", "q35_decode_plan_release",
+    "q35_decode_step", "q35_decode_check", "q35_decode_layer_input", "q35_decode_stage_layout",
+    "q35_decode_stage_times",
 ]
+
+Q35_LAYER_LINEAR = 0
+Q35_LAYER_FULL = 1
 
 
 class Q35Error(RuntimeError):
@@ -106,6 +112,20 @@ class LinearAttentionScratch(C.Structure):
                 ("gate_act", C.c_void_p), ("up_act", C.c_void_p), ("x_final", C.c_void_p)]
 
 
+class Q35StackLayer(C.Structure):
+    _fields_ = [("kind", C.c_uint32), ("linear", C.POINTER(LinearAttentionLayer)),
+                ("state", C.POINTER(LinearAttentionState)), ("full", C.POINTER(FullAttentionLayer)),
+                ("kv", C.POINTER(LayerKvCache))]
+
+
+class Q35DecodeStackDesc(C.Structure):
+    _fields_ = [("n_layers", C.c_uint32), ("layers", C.POINTER(Q35StackLayer)),
+                ("inv_freq", C.c_void_p), ("positions", C.c_void_p),
+                ("lm_head", C.POINTER(Q35QuantWeight)), ("final_norm", C.c_void_p),
+                ("embed", C.c_void_p), ("tokens", C.c_void_p), ("logits", C.c_void_p),
+                ("history", C.c_void_p), ("history_len", C.c_uint32), ("history_base", C.c_int32)]
+
+
 DUMP_FN = C.CFUNCTYPE(None, C.c_void_p, C.c_char_p, C.c_void_p, C.c_uint32)
 
 # --------------------------------------------------------------------------- library
@@ -149,6 +169,16 @@ def lib():
             "q35_gate_up_swiglu": (st, [vp, P(Qwen35ForwardConfig), vp, P(Q35QuantWeight),
                                         P(Q35QuantWeight), vp, vp, vp]),
             "q35_gemv": (st, [vp, P(Q35QuantWeight), vp, vp, u32, vp]),
+            "q35_decode_workspace_bytes": (st, [vp, P(Qwen35ForwardConfig), P(Q35DecodeStackDesc),
+                                                P(sz)]),
+            "q35_decode_plan_create": (st, [vp, P(Qwen35ForwardConfig), P(Q35DecodeStackDesc), vp,
+                                            sz, P(vp)]),
+            "q35_decode_plan_release": (None, [vp]),
+            "q35_decode_step": (st, [vp, vp]),
+            "q35_decode_check": (st, [vp, P(u32)]),
+            "q35_decode_layer_input": (st, [vp, u32, P(vp)]),
+            "q35_decode_stage_layout": (st, [vp, P(u32), P(u32)]),
+            "q35_decode_stage_times": (st, [vp, P(C.c_uint64), u32, P(C.c_uint64)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -268,3 +298,52 @@ def q35_gate_up_swiglu(kernels, cfg, post_ln, gate_proj, up_proj, x_resid, mlp_a
 
 def q35_gemv(kernels, w, x, y, act_dtype, stream) -> None:
     _check(lib().q35_gemv(kernels, C.byref(w), x, y, act_dtype, stream))
+
+
+def q35_decode_workspace_bytes(kernels, cfg, desc) -> int:
+    b = C.c_size_t()
+    _check(lib().q35_decode_workspace_bytes(kernels, C.byref(cfg), C.byref(desc), C.byref(b)))
+    return b.value
+
+
+def q35_decode_plan_create(kernels, cfg, desc, workspace, workspace_bytes) -> int:
+    h = C.c_void_p()
+    _check(lib().q35_decode_plan_create(kernels, C.byref(cfg), C.byref(desc), workspace,
+                                        workspace_bytes, C.byref(h)))
+    return h.value
+
+
+def q35_decode_plan_release(plan) -> None:
+    lib().q35_decode_plan_release(plan)
+
+
+def q35_decode_step(plan, stream) -> None:
+    _check(lib().q35_decode_step(plan, stream))
+
+
+def q35_decode_check(plan) -> int:
+    e = C.c_uint32()
+    _check(lib().q35_decode_check(plan, C.byref(e)))
+    return e.value
+
+
+def q35_decode_layer_input(plan, layer: int) -> int:
+    x = C.c_void_p()
+    _check(lib().q35_decode_layer_input(plan, layer, C.byref(x)))
+    return x.value
+
+
+def q35_decode_stage_layout(plan, n_layers: int):
+    n = C.c_uint32()
+    first = (C.c_uint32 * (n_layers + 1))()
+    _check(lib().q35_decode_stage_layout(plan, C.byref(n), first))
+    return n.value, list(first)
+
+
+def q35_decode_stage_times(plan, n: int):
+    import numpy as np
+    ticks = np.zeros(n, np.uint64)
+    hz = C.c_uint64()
+    _check(lib().q35_decode_stage_times(plan, ticks.ctypes.data_as(C.POINTER(C.c_uint64)), n,
+                                        C.byref(hz)))
+    return ticks, hz.value

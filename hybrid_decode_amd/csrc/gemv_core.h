@@ -232,11 +232,51 @@ struct ProRegs {
     uint4 w[MC][2];  // 16 bf16 norm weights
 };
 
-template <int K, int PRO, bool HALF, int NT>
+#ifndef Q35_PERSIST_X_AUX
+#define Q35_PERSIST_X_AUX kAuxCoherent
+#endif
+constexpr int kAuxXPersist = Q35_PERSIST_X_AUX;
+
+template <int K, int PRO, bool HALF, int NT, bool COH = false>
 Q35_DEV void prologue_issue(const GemvPro& p, ProRegs<K, PRO, NT>& r) {
     constexpr int KC = K / 16, MC = pro_chunks<K, NT>();
     constexpr bool X_BF16 = (PRO == kProRmsAct) && HALF;  // the residual stream is bf16 for HALF
-    const int t = threadIdx.x;
+    const int t = tid_x();
+    if constexpr (COH) {
+        // x (and z) were written by other blocks of the same launch: device-coherent
+        // buffer loads over a wave-uniform resource, per-lane offsets
+        const auto rx = rsrc(p.x, K * (X_BF16 ? 2u : 4u));
+        const auto rz = rsrc(p.z, PRO == kProGatedNorm ? K * 4u : 0u);
+        const auto rw = rsrc(p.w, (PRO == kProGatedNorm ? p.head_dim : K) * 2u);
+#pragma unroll
+        for (int m = 0; m < MC; ++m) {
+            const int cc = t + NT * m;
+            if (cc < KC) {
+                if constexpr (X_BF16) {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        r.x[m][j] = ld_b128<kAuxXPersist>(rx, 32u * cc + 16u * j);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        r.x[m][j] = ld_b128<kAuxXPersist>(rx, 64u * cc + 16u * j);
+                }
+                if constexpr (PRO == kProRmsAct || PRO == kProRmsF32) {
+                    r.w[m][0] = ld_b128<0>(rw, 32u * cc);
+                    r.w[m][1] = ld_b128<0>(rw, 32u * cc + 16u);
+                }
+                if constexpr (PRO == kProGatedNorm) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        r.z[m][j] = ld_b128<kAuxXPersist>(rz, 64u * cc + 16u * j);
+                    const uint32_t wo = ((16u * cc) % p.head_dim) * 2u;
+                    r.w[m][0] = ld_b128<0>(rw, wo);
+                    r.w[m][1] = ld_b128<0>(rw, wo + 16u);
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int m = 0; m < MC; ++m) {
         const int cc = t + NT * m;
@@ -382,7 +422,7 @@ Q35_DEV float prologue_build(const GemvPro& p, const ProRegs<K, PRO, NT>& r, uin
     constexpr int KC = K / 16, MC = pro_chunks<K, NT>(), NW = NT / 64;
     constexpr bool X_BF16 = (PRO == kProRmsAct) && HALF;
     constexpr bool RMS = (PRO == kProRmsAct || PRO == kProRmsF32);
-    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int t = tid_x(), lane = t & 63, wid = t >> 6;
     const bool tap = (p.tap != nullptr) && blockIdx.x == 0;
     float ss = 0.f;
 
@@ -487,11 +527,11 @@ constexpr int pre_mask() {  // which of the 16/8/4/2-byte operands the op's epil
          : 0;
 }
 
-template <int OP, int SI>
+template <int OP, int SI, bool COH>
 Q35_DEV void epilogue(const GemvArgs& a, const GemvSeg& s, uint32_t n, float v, float v2,
                       const EpiPre& e, float& best_v, int& best_i) {
     if constexpr (OP == kOpPlain || OP == kOpInFull || (OP == kOpInGdn && SI == 1)) {
-        s.out[n] = v;
+        st_f32<COH>(s.out, n, v);
     } else if constexpr (OP == kOpInGdn && SI == 0) {
         // causal depthwise conv update of channel n (window: state[1..3] + new input), SiLU
         if (s.tap0) s.tap0[n] = v;
@@ -502,27 +542,28 @@ Q35_DEV void epilogue(const GemvArgs& a, const GemvSeg& s, uint32_t n, float v, 
         u = fmaf(bf16_hi(w.x), o.z, u);
         u = fmaf(bf16_lo(w.y), o.w, u);
         u = fmaf(bf16_hi(w.y), v, u);
+        // the conv state row is read and written by this lane only
         reinterpret_cast<float4*>(s.state)[n] = make_float4(o.y, o.z, o.w, v);
-        s.out[n] = siluf_(u);
+        st_f32<COH>(s.out, n, siluf_(u));
     } else if constexpr (OP == kOpInGdn && SI == 2) {
         // decay gate exp(-exp(A_log) * softplus(a + dt_bias))
         if (s.tap0) s.tap0[n] = v;
-        s.out[n] = expf(-expf(__uint_as_float(e.q4)) * softplusf_(v + bf16_to_f32(e.q2)));
+        st_f32<COH>(s.out, n, expf(-expf(__uint_as_float(e.q4)) * softplusf_(v + bf16_to_f32(e.q2))));
     } else if constexpr (OP == kOpInGdn && SI == 3) {
         if (s.tap0) s.tap0[n] = v;
-        s.out[n] = sigmoidf_(v);
+        st_f32<COH>(s.out, n, sigmoidf_(v));
     } else if constexpr (OP == kOpOutGated || OP == kOpOProj) {
         // residual from the layer input (activation dtype)
         if (s.tap0) s.tap0[n] = v;
-        s.out[n] = (a.act_f32 ? __uint_as_float(e.q4) : bf16_to_f32(e.q2)) + v;
+        st_f32<COH>(s.out, n, (a.act_f32 ? __uint_as_float(e.q4) : bf16_to_f32(e.q2)) + v);
     } else if constexpr (OP == kOpGateUp) {
         if (s.tap0) s.tap0[n] = v;
         if (s.tap1) s.tap1[n] = v2;
-        s.out[n] = siluf_(v) * v2;
+        st_f32<COH>(s.out, n, siluf_(v) * v2);
     } else if constexpr (OP == kOpDown) {
         const float r = __uint_as_float(e.q4) + v;
-        store_act(s.out_act, n, r, a.act_f32);
-        if (s.out_act2) store_act(s.out_act2, n, r, a.act_f32);
+        st_act_t<COH>(s.out_act, n, r, a.act_f32);
+        if (s.out_act2) st_act_t<COH>(s.out_act2, n, r, a.act_f32);
     } else if constexpr (OP == kOpLmHead) {
         if (s.out) s.out[n] = v;
         if (v > best_v || (v == best_v && (int)n < best_i)) {
@@ -540,7 +581,7 @@ Q35_DEV bool better(float v, int i, float bv, int bi) {
 
 // Per-block partial argmax (lowest index on ties), stored plainly; a follow-up
 // kernel reduces the partials, so no block needs a device-wide fence.
-template <int NT>
+template <int NT, bool COH>
 Q35_DEV void argmax_partial(const GemvArgs& a, float best_v, int best_i, float* red) {
     int* redi = reinterpret_cast<int*>(red + kRedSlots / 2);
     for (int o = 32; o > 0; o >>= 1) {
@@ -551,14 +592,14 @@ Q35_DEV void argmax_partial(const GemvArgs& a, float best_v, int best_i, float* 
             best_i = oi;
         }
     }
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = tid_x() & 63, wid = tid_x() >> 6;
     __syncthreads();
     if (lane == 0) {
         red[wid] = best_v;
         redi[wid] = best_i;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (tid_x() == 0) {
         float bv = red[0];
         int bi = redi[0];
         for (int w = 1; w < NT / 64; ++w)
@@ -566,15 +607,22 @@ Q35_DEV void argmax_partial(const GemvArgs& a, float best_v, int best_i, float* 
                 bv = red[w];
                 bi = redi[w];
             }
-        a.am.part_val[blockIdx.x] = bv;
-        a.am.part_idx[blockIdx.x] = bi;
+        st_f32<COH>(a.am.part_val, blockIdx.x, bv);
+        st_i32<COH>(a.am.part_idx, blockIdx.x, bi);
     }
 }
 
 // ---------------------------------------------------------------- the kernel
 
-template <int K, int OP, bool HALF, bool XREG, int NT>
-__global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a) {
+// The body shared by the standalone kernels and the stages of the persistent
+// decode kernel.  rg: this wave's first row group; nw: the stride between its
+// row groups.  COH (persistent stages): x, the epilogue operands and the
+// outputs are exchanged with other blocks of the same launch, so they use
+// device-coherent loads and stores; the wave's first row group of weights is
+// issued before wait() (which returns once the stage's inputs are published),
+// and a wave with no row group issues no loads.
+template <int K, int OP, bool HALF, bool XREG, int NT, bool COH, class Wait>
+Q35_DEV void gemv_body(const GemvArgs& a, uint32_t rg, uint32_t nw, Wait&& wait) {
     using T = Op<OP>;
     constexpr bool PAIRED = T::PAIRED;
     using G = Geo<K, PAIRED>;
@@ -587,11 +635,11 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a) {
     float* red = reinterpret_cast<float*>(xab + KC);
     const float4* xq = reinterpret_cast<const float4*>(smem4);
 
-    const int lane = threadIdx.x & 63;
+    const int lane = tid_x() & 63;
     const int li = lane % LR;
     const uint32_t rloc = (uint32_t)(lane / LR);  // row of the row group
-    const uint32_t nw = gridDim.x * (NT / 64);
     const uint32_t total = a.total_rg;
+    constexpr int PRE_AUX = COH ? kAuxCoherent : 0;
 
     constexpr int NC2 = PAIRED ? NC : 1;
     u32x4_t w[NC], w2[NC2];  // paired: w2 holds the second matrix's rows of the same index
@@ -609,16 +657,16 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a) {
         auto pre_rsrc = [&](const void* p, uint32_t elt) { return rsrc(p, p ? rows * elt : 0u); };
         if constexpr (PM & 16)
             pre.q16 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                pre_rsrc(pick<T::NSEG>(si, [&](int i) { return a.seg[i].pre16; }), 16u), n * 16u, 0, 0));
+                pre_rsrc(pick<T::NSEG>(si, [&](int i) { return a.seg[i].pre16; }), 16u), n * 16u, 0, PRE_AUX));
         if constexpr (PM & 8)
             pre.q8 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                pre_rsrc(pick<T::NSEG>(si, [&](int i) { return a.seg[i].pre8; }), 8u), n * 8u, 0, 0));
+                pre_rsrc(pick<T::NSEG>(si, [&](int i) { return a.seg[i].pre8; }), 8u), n * 8u, 0, PRE_AUX));
         if constexpr (PM & 4)
             pre.q4 = __builtin_amdgcn_raw_buffer_load_b32(
-                pre_rsrc(pick<T::NSEG>(si, [&](int i) { return a.seg[i].pre4; }), 4u), n * 4u, 0, 0);
+                pre_rsrc(pick<T::NSEG>(si, [&](int i) { return a.seg[i].pre4; }), 4u), n * 4u, 0, PRE_AUX);
         if constexpr (PM & 2)
             pre.q2 = __builtin_amdgcn_raw_buffer_load_b16(
-                pre_rsrc(pick<T::NSEG>(si, [&](int i) { return a.seg[i].pre2; }), 2u), n * 2u, 0, 0);
+                pre_rsrc(pick<T::NSEG>(si, [&](int i) { return a.seg[i].pre2; }), 2u), n * 2u, 0, PRE_AUX);
         const uint32_t cbytes = rows * (uint32_t)K, sbytes = rows * (uint32_t)KG * 2u;
         const uint32_t coff = row0 * (uint32_t)K, soff = row0 * (uint32_t)KG * 2u;
         auto issue = [&](const void* c, const void* sc, const void* bi, u32x4_t* wd, uint32_t* sd,
@@ -639,18 +687,29 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a) {
             issue(a.seg[0].codes[1], a.seg[0].scales[1], a.seg[0].biases[1], w2, sv2, bv2);
     };
 
-    // x loads first, then the first row group's weights (vector loads complete in order)
     ProRegs<K, T::PRO, NT> pr;
-    prologue_issue<K, T::PRO, HALF, NT>(a.pro, pr);
-    asm volatile("" ::: "memory");
-    // wave-uniform by construction; readfirstlane lets the compiler keep the row
-    // group (and so every buffer load's scalar offset) in SGPRs
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    uint32_t rg = blockIdx.x * (NT / 64) + wave;
-    // Unconditional (a spare wave re-reads the last row group and discards it):
-    // the compiler then knows exactly how many loads follow x and waits for x
-    // alone instead of for every outstanding load.
-    load_rg(rg < total ? rg : total - 1);
+    if constexpr (COH) {
+        // weights first (they do not depend on this launch), then the wait for
+        // the stage's inputs, then x
+#ifdef Q35_PERSIST_PRE_WAVES
+        const bool early = (tid_x() >> 6) < Q35_PERSIST_PRE_WAVES;
+#else
+        const bool early = true;
+#endif
+        if (early && rg < total) load_rg(rg);
+        asm volatile("" ::: "memory");
+        wait();
+        if (!early && rg < total) load_rg(rg);
+        prologue_issue<K, T::PRO, HALF, NT, true>(a.pro, pr);
+    } else {
+        // x loads first, then the first row group's weights (vector loads complete in order)
+        prologue_issue<K, T::PRO, HALF, NT>(a.pro, pr);
+        asm volatile("" ::: "memory");
+        // Unconditional (a spare wave re-reads the last row group and discards it):
+        // the compiler then knows exactly how many loads follow x and waits for x
+        // alone instead of for every outstanding load.
+        load_rg(rg < total ? rg : total - 1);
+    }
     asm volatile("" ::: "memory");
 
     const float post = prologue_build<K, T::PRO, HALF, NT>(a.pro, pr, ximg, xab, red);
@@ -693,11 +752,20 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a) {
         with_seg<T::NSEG>(a, cur, [&](const GemvSeg& s, auto si) {
             constexpr int SI = decltype(si)::value;
             const uint32_t n = (cur - s.rg_begin) * R + rloc;
-            if (li == LR - 1) epilogue<OP, SI>(a, s, n, v, v2, cpre, best_v, best_i);
+            if (li == LR - 1) epilogue<OP, SI, COH>(a, s, n, v, v2, cpre, best_v, best_i);
         });
     }
 
-    if constexpr (OP == kOpLmHead) argmax_partial<NT>(a, best_v, best_i, red);
+    if constexpr (OP == kOpLmHead) argmax_partial<NT, COH>(a, best_v, best_i, red);
+}
+
+template <int K, int OP, bool HALF, bool XREG, int NT>
+__global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a) {
+    // wave-uniform by construction; readfirstlane lets the compiler keep the row
+    // group (and so every buffer load's scalar offset) in SGPRs
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid_x() >> 6);
+    gemv_body<K, OP, HALF, XREG, NT, false>(a, blockIdx.x * (NT / 64) + wave, gridDim.x * (NT / 64),
+                                            [] {});
 }
 
 template <int K, bool HALF>

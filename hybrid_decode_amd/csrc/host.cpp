@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/q35decode.h"
 #include "q35_internal.h"
@@ -204,6 +205,54 @@ q35_status launch_mlp(const Qwen35ForwardConfig& c, const Q35QuantWeight& gate_p
         s.out_act2 = x_out2;
         Q35_TRY(b.launch(stream, "down GEMV"));
     }
+    return Q35_OK;
+}
+
+q35_status check_full_layer(const Qwen35ForwardConfig& c, const FullAttentionLayer& l) {
+    Q35_TRY(need(l.input_ln, "input_ln"));
+    Q35_TRY(need(l.q_norm, "q_norm"));
+    Q35_TRY(need(l.k_norm, "k_norm"));
+    Q35_TRY(need(l.post_ln, "post_ln"));
+    Q35_TRY(check_weight("q_proj", l.q_proj, q_total(c), c.hidden));
+    Q35_TRY(check_weight("k_proj", l.k_proj, kv_dim(c), c.hidden));
+    Q35_TRY(check_weight("v_proj", l.v_proj, kv_dim(c), c.hidden));
+    Q35_TRY(check_weight("o_proj", l.o_proj, c.hidden, q_only(c)));
+    Q35_TRY(check_weight("gate_proj", l.gate_proj, c.intermediate, c.hidden));
+    Q35_TRY(check_weight("up_proj", l.up_proj, c.intermediate, c.hidden));
+    Q35_TRY(check_weight("down_proj", l.down_proj, c.hidden, c.intermediate));
+    return Q35_OK;
+}
+
+q35_status check_kv(const LayerKvCache& kv) {
+    if (kv.dtype != Q35_KV_BF16)
+        return fail(Q35_ERR_UNSUPPORTED, "KV dtype %u: only bf16 caches are implemented", kv.dtype);
+    if (kv.k_scales || kv.v_scales) return fail(Q35_ERR_INVALID_ARG, "bf16 cache with scale buffers");
+    Q35_TRY(need(kv.k, "kv.k"));
+    Q35_TRY(need(kv.v, "kv.v"));
+    if (kv.capacity == 0) return fail(Q35_ERR_OUT_OF_RANGE, "cache capacity is 0");
+    return Q35_OK;
+}
+
+q35_status check_linear_layer(const Qwen35ForwardConfig& c, const LinearAttentionLayer& l,
+                              const LinearAttentionState& st) {
+    const uint32_t Hv = c.num_v_heads_lin;
+    Q35_TRY(need(st.conv1d_state, "state.conv1d_state"));
+    Q35_TRY(need(st.gdn_state, "state.gdn_state"));
+    Q35_TRY(need(l.input_ln, "input_ln"));
+    Q35_TRY(need(l.post_ln, "post_ln"));
+    Q35_TRY(need(l.norm_weight, "norm_weight"));
+    Q35_TRY(need(l.a_log, "a_log", false));
+    Q35_TRY(need(l.dt_bias, "dt_bias", false));
+    if (!l.conv1d_weight || !aligned8(l.conv1d_weight))
+        return fail(Q35_ERR_INVALID_ARG, "conv1d_weight NULL or not 8-byte aligned");
+    Q35_TRY(check_weight("in_proj_a", l.in_proj_a, Hv, c.hidden));
+    Q35_TRY(check_weight("in_proj_b", l.in_proj_b, Hv, c.hidden));
+    Q35_TRY(check_weight("in_proj_qkv", l.in_proj_qkv, qkv_total(c), c.hidden));
+    Q35_TRY(check_weight("in_proj_z", l.in_proj_z, z_dim(c), c.hidden));
+    Q35_TRY(check_weight("out_proj", l.out_proj, c.hidden, z_dim(c)));
+    Q35_TRY(check_weight("gate_proj", l.gate_proj, c.intermediate, c.hidden));
+    Q35_TRY(check_weight("up_proj", l.up_proj, c.intermediate, c.hidden));
+    Q35_TRY(check_weight("down_proj", l.down_proj, c.hidden, c.intermediate));
     return Q35_OK;
 }
 
@@ -419,12 +468,7 @@ static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35Fo
     if (!cfg || !layer || !s || !kv || !out) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
     Q35_TRY(q35_config_validate(cfg));
     const Qwen35ForwardConfig& c = *cfg;
-    if (kv->dtype != Q35_KV_BF16)
-        return fail(Q35_ERR_UNSUPPORTED, "KV dtype %u: only bf16 caches are implemented", kv->dtype);
-    if (kv->k_scales || kv->v_scales) return fail(Q35_ERR_INVALID_ARG, "bf16 cache with scale buffers");
-    Q35_TRY(need(kv->k, "kv.k"));
-    Q35_TRY(need(kv->v, "kv.v"));
-    if (kv->capacity == 0) return fail(Q35_ERR_OUT_OF_RANGE, "cache capacity is 0");
+    Q35_TRY(check_kv(*kv));
     if (cache_pos >= 0) {
         if ((uint64_t)cache_pos >= kv->capacity)
             return fail(Q35_ERR_OUT_OF_RANGE, "cache_pos %lld >= capacity %u", (long long)cache_pos, kv->capacity);
@@ -435,17 +479,7 @@ static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35Fo
     Q35_TRY(need(inv_freq, "inv_freq", false));
     Q35_TRY(need(positions, "positions", false));
     Q35_TRY(need(x_in, "x_in"));
-    Q35_TRY(need(layer->input_ln, "input_ln"));
-    Q35_TRY(need(layer->q_norm, "q_norm"));
-    Q35_TRY(need(layer->k_norm, "k_norm"));
-    Q35_TRY(need(layer->post_ln, "post_ln"));
-    Q35_TRY(check_weight("q_proj", layer->q_proj, q_total(c), c.hidden));
-    Q35_TRY(check_weight("k_proj", layer->k_proj, kv_dim(c), c.hidden));
-    Q35_TRY(check_weight("v_proj", layer->v_proj, kv_dim(c), c.hidden));
-    Q35_TRY(check_weight("o_proj", layer->o_proj, c.hidden, q_only(c)));
-    Q35_TRY(check_weight("gate_proj", layer->gate_proj, c.intermediate, c.hidden));
-    Q35_TRY(check_weight("up_proj", layer->up_proj, c.intermediate, c.hidden));
-    Q35_TRY(check_weight("down_proj", layer->down_proj, c.hidden, c.intermediate));
+    Q35_TRY(check_full_layer(c, *layer));
     Q35_TRY(need(s->q_full, "scratch.q_full"));
     Q35_TRY(need(s->k, "scratch.k"));
     Q35_TRY(need(s->v, "scratch.v"));
@@ -572,23 +606,7 @@ q35_status q35_forward_linear_attention(const Qwen35Kernels* kernels,
     const uint32_t Hv = c.num_v_heads_lin;
     Q35_TRY(need(x_in, "x_in"));
     Q35_TRY(need(x_buf, "x_buf"));
-    Q35_TRY(need(state->conv1d_state, "state.conv1d_state"));
-    Q35_TRY(need(state->gdn_state, "state.gdn_state"));
-    Q35_TRY(need(layer->input_ln, "input_ln"));
-    Q35_TRY(need(layer->post_ln, "post_ln"));
-    Q35_TRY(need(layer->norm_weight, "norm_weight"));
-    Q35_TRY(need(layer->a_log, "a_log", false));
-    Q35_TRY(need(layer->dt_bias, "dt_bias", false));
-    if (!layer->conv1d_weight || !aligned8(layer->conv1d_weight))
-        return fail(Q35_ERR_INVALID_ARG, "conv1d_weight NULL or not 8-byte aligned");
-    Q35_TRY(check_weight("in_proj_a", layer->in_proj_a, Hv, c.hidden));
-    Q35_TRY(check_weight("in_proj_b", layer->in_proj_b, Hv, c.hidden));
-    Q35_TRY(check_weight("in_proj_qkv", layer->in_proj_qkv, qkv_total(c), c.hidden));
-    Q35_TRY(check_weight("in_proj_z", layer->in_proj_z, z_dim(c), c.hidden));
-    Q35_TRY(check_weight("out_proj", layer->out_proj, c.hidden, z_dim(c)));
-    Q35_TRY(check_weight("gate_proj", layer->gate_proj, c.intermediate, c.hidden));
-    Q35_TRY(check_weight("up_proj", layer->up_proj, c.intermediate, c.hidden));
-    Q35_TRY(check_weight("down_proj", layer->down_proj, c.hidden, c.intermediate));
+    Q35_TRY(check_linear_layer(c, *layer, *state));
     Q35_TRY(need(s->qkv_conv, "scratch.qkv_conv"));
     Q35_TRY(need(s->z, "scratch.z"));
     Q35_TRY(need(s->gate, "scratch.gate", false));
@@ -793,6 +811,418 @@ q35_status q35_gemv(const Qwen35Kernels* kernels, const Q35QuantWeight* w, const
     b.a.pro.x = x;
     b.add(*w, kEpiStore).out = y;
     Q35_TRY(b.launch(stream, "GEMV"));
+    return ok();
+}
+
+// ------------------------------------------------------------------ persistent decode
+
+}  // extern "C"
+
+struct Q35DecodePlan {
+    int device;
+    int shape;
+    uint32_t blocks;
+    PersistArgs args;
+    uint32_t n_layers;
+    std::vector<uint32_t> first_stage;  // [n_layers + 1]
+    std::vector<void*> x_in;            // [n_layers + 1]
+    uint64_t clock_hz;
+};
+
+namespace {
+
+// Bump allocation of the plan's workspace sections (256-byte aligned, so no two
+// buffers share a cache line); base == nullptr only counts.
+struct Bump {
+    uint8_t* base;
+    size_t off = 0;
+    void* take(size_t bytes) {
+        void* p = base ? base + off : nullptr;
+        off += (bytes + 255) & ~size_t(255);
+        return p;
+    }
+    float* f32(size_t n) { return static_cast<float*>(take(n * sizeof(float))); }
+};
+
+constexpr uint32_t kStagesGdn = 5, kStagesFull = 6, kStagesTail = 2;
+constexpr double kWaitLimitSeconds = 0.2;  // a wait longer than this is an error
+
+// Validates the stack, lays out the workspace and (when ws != nullptr) fills
+// the stage table and the plan's host view.
+q35_status plan_build(const Qwen35Kernels* k, const Qwen35ForwardConfig* cfg,
+                      const Q35DecodeStackDesc* d, uint8_t* ws, size_t* total,
+                      std::vector<PStage>* stages, Q35DecodePlan* plan) {
+    Q35_TRY(check_kernels(k));
+    if (!cfg || !d) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    Q35_TRY(q35_config_validate(cfg));
+    const Qwen35ForwardConfig& c = *cfg;
+    const bool f32 = c.act_dtype == Q35_ACT_F32;
+    const uint32_t G = c.num_heads / c.num_kv_heads;
+    const int shape = persist_shape_id(c.hidden, c.intermediate, q_only(c), z_dim(c), c.k_head_dim_lin,
+                                       c.head_dim, G, !f32);
+    if (!shape)
+        return fail(Q35_ERR_UNSUPPORTED, "the persistent kernel is not built for these dimensions "
+                                         "(use the per-layer calls)");
+    if (d->n_layers == 0 || !d->layers) return fail(Q35_ERR_INVALID_ARG, "empty stack");
+    const uint32_t blocks = (uint32_t)k->num_cu;
+    if (blocks < c.num_kv_heads || blocks > 1024)
+        return fail(Q35_ERR_UNSUPPORTED, "%u compute units", blocks);
+    const uint32_t cpb = blocks / c.num_kv_heads;  // attention chunks per kv head
+    if (c.num_v_heads_lin * (c.v_head_dim_lin / 16) > blocks)
+        return fail(Q35_ERR_UNSUPPORTED, "more recurrence tiles than blocks");
+    Q35_TRY(need(d->positions, "positions", false));
+    const bool tail = d->lm_head != nullptr;
+    bool any_full = false;
+    for (uint32_t l = 0; l < d->n_layers; ++l) {
+        const Q35StackLayer& L = d->layers[l];
+        if (L.kind == Q35_LAYER_LINEAR) {
+            if (!L.linear || !L.state) return fail(Q35_ERR_INVALID_ARG, "layer %u: NULL weights/state", l);
+            Q35_TRY(check_linear_layer(c, *L.linear, *L.state));
+        } else if (L.kind == Q35_LAYER_FULL) {
+            if (!L.full || !L.kv) return fail(Q35_ERR_INVALID_ARG, "layer %u: NULL weights/cache", l);
+            Q35_TRY(check_full_layer(c, *L.full));
+            Q35_TRY(check_kv(*L.kv));
+            any_full = true;
+        } else {
+            return fail(Q35_ERR_INVALID_ARG, "layer %u: kind %u", l, L.kind);
+        }
+    }
+    if (any_full) Q35_TRY(need(d->inv_freq, "inv_freq", false));
+    if (tail) {
+        if (c.vocab == 0) return fail(Q35_ERR_INVALID_ARG, "vocab is 0");
+        Q35_TRY(check_weight("lm_head", *d->lm_head, c.vocab, c.hidden));
+        Q35_TRY(need(d->final_norm, "final_norm"));
+        Q35_TRY(need(d->tokens, "tokens", false));
+        if (!d->embed || !aligned16(d->embed) || c.hidden % 8 != 0)
+            return fail(Q35_ERR_INVALID_ARG, "embed NULL or not 16-byte aligned, or hidden %% 8 != 0");
+        Q35_TRY(opt(d->logits, "logits"));
+    }
+
+    const uint32_t nst = [&] {
+        uint32_t n = tail ? kStagesTail : 0;
+        for (uint32_t l = 0; l < d->n_layers; ++l)
+            n += d->layers[l].kind == Q35_LAYER_LINEAR ? kStagesGdn : kStagesFull;
+        return n;
+    }();
+    const size_t act = f32 ? 4 : 2;
+    Bump b{ws};
+    uint32_t* ctl = static_cast<uint32_t*>(b.take(256));
+    uint32_t* flags = static_cast<uint32_t*>(b.take(4u * blocks));
+    uint64_t* stamps = static_cast<uint64_t*>(b.take(8u * nst));
+    PStage* table = static_cast<PStage*>(b.take(sizeof(PStage) * nst));
+    std::vector<void*> X(d->n_layers + 1);
+    for (auto& x : X) x = b.take(act * c.hidden);
+    std::vector<PStage> st;
+    std::vector<uint32_t> first;
+    auto gemv_stage = [&](int kind, const GemvBuild& gb) {
+        PStage ps;
+        std::memset(&ps, 0, sizeof(ps));
+        ps.kind = kind;
+        ps.g = gb.a;
+        st.push_back(ps);
+    };
+    auto mlp = [&](const Q35QuantWeight& gp, const Q35QuantWeight& up, const Q35QuantWeight& dp,
+                   const uint16_t* post_ln, float* x_resid, void* x_out) {
+        float* h = b.f32(c.intermediate);
+        GemvBuild g1(kOpGateUp, c.hidden, f32);
+        g1.a.pro.kind = kProRmsF32;
+        g1.a.pro.x = x_resid;
+        g1.a.pro.w = post_ln;
+        g1.a.pro.eps = c.rms_eps;
+        g1.add(gp, kEpiSwiGLU, &up).out = h;
+        gemv_stage(kStGateUp, g1);
+        GemvBuild g2(kOpDown, c.intermediate, f32);
+        g2.a.pro.kind = kProLoadF32;
+        g2.a.pro.x = h;
+        GemvSeg& sd = g2.add(dp, kEpiResidToAct);
+        sd.pre4 = x_resid;
+        sd.out_act = x_out;
+        gemv_stage(kStDown, g2);
+    };
+    for (uint32_t l = 0; l < d->n_layers; ++l) {
+        const Q35StackLayer& L = d->layers[l];
+        first.push_back((uint32_t)st.size());
+        float* x_resid = b.f32(c.hidden);
+        if (L.kind == Q35_LAYER_LINEAR) {
+            const LinearAttentionLayer& w = *L.linear;
+            const uint32_t qt = qkv_total(c), zd = z_dim(c), Hv = c.num_v_heads_lin;
+            float* qkv = b.f32(qt);
+            float* z = b.f32(zd);
+            float* gate = b.f32(Hv);
+            float* beta = b.f32(Hv);
+            float* y = b.f32(zd);
+            GemvBuild g(kOpInGdn, c.hidden, f32);
+            g.a.pro.kind = kProRmsAct;
+            g.a.pro.x_f32 = f32;
+            g.a.pro.x = X[l];
+            g.a.pro.w = w.input_ln;
+            g.a.pro.eps = c.rms_eps;
+            GemvSeg& sq = g.add(w.in_proj_qkv, kEpiConv);
+            sq.out = qkv;
+            sq.state = L.state->conv1d_state;
+            sq.pre16 = L.state->conv1d_state;
+            sq.pre8 = w.conv1d_weight;
+            g.add(w.in_proj_z, kEpiStore).out = z;
+            GemvSeg& sa = g.add(w.in_proj_a, kEpiGate);
+            sa.out = gate;
+            sa.pre2 = w.dt_bias;
+            sa.pre4 = w.a_log;
+            g.add(w.in_proj_b, kEpiBeta).out = beta;
+            gemv_stage(kStInGdn, g);
+            PStage ps;
+            std::memset(&ps, 0, sizeof(ps));
+            ps.kind = kStGdn;
+            ps.d.state = L.state->gdn_state;
+            ps.d.qkv_conv = qkv;
+            ps.d.gate = gate;
+            ps.d.beta = beta;
+            ps.d.y = y;
+            ps.d.hk = c.num_k_heads_lin;
+            ps.d.hv = Hv;
+            ps.d.l2_eps = 1e-6f;
+            ps.d.out_scale = 1.0f / std::sqrt((float)c.k_head_dim_lin);
+            st.push_back(ps);
+            GemvBuild go(kOpOutGated, zd, f32);
+            go.a.pro.kind = kProGatedNorm;
+            go.a.pro.x = y;
+            go.a.pro.w = w.norm_weight;
+            go.a.pro.z = z;
+            go.a.pro.head_dim = c.v_head_dim_lin;
+            go.a.pro.eps = c.rms_eps;
+            GemvSeg& so = go.add(w.out_proj, kEpiResidActIn);
+            so.out = x_resid;
+            (f32 ? so.pre4 : so.pre2) = X[l];
+            gemv_stage(kStOutGated, go);
+            mlp(w.gate_proj, w.up_proj, w.down_proj, w.post_ln, x_resid, X[l + 1]);
+        } else {
+            const FullAttentionLayer& w = *L.full;
+            float* qf = b.f32(q_total(c));
+            float* kk = b.f32(kv_dim(c));
+            float* vv = b.f32(kv_dim(c));
+            float* ga = b.f32(q_only(c));
+            float* pacc = b.f32((size_t)c.num_kv_heads * cpb * G * c.head_dim);
+            float* pml = b.f32((size_t)c.num_kv_heads * cpb * 2 * G);
+            GemvBuild g(kOpInFull, c.hidden, f32);
+            g.a.pro.kind = kProRmsAct;
+            g.a.pro.x_f32 = f32;
+            g.a.pro.x = X[l];
+            g.a.pro.w = w.input_ln;
+            g.a.pro.eps = c.rms_eps;
+            g.add(w.q_proj, kEpiStore).out = qf;
+            g.add(w.k_proj, kEpiStore).out = kk;
+            g.add(w.v_proj, kEpiStore).out = vv;
+            gemv_stage(kStInFull, g);
+            PStage ps;
+            std::memset(&ps, 0, sizeof(ps));
+            ps.kind = kStAttn;
+            AttnArgs& a = ps.at;
+            a.q_full = qf;
+            a.k = kk;
+            a.v = vv;
+            a.q_norm = w.q_norm;
+            a.k_norm = w.k_norm;
+            a.inv_freq = d->inv_freq;
+            a.positions = d->positions;
+            a.kc = static_cast<uint16_t*>(L.kv->k);
+            a.vc = static_cast<uint16_t*>(L.kv->v);
+            a.gated_attn = ga;
+            a.part_acc = pacc;
+            a.part_ml = pml;
+            a.capacity = L.kv->capacity;
+            a.hq = c.num_heads;
+            a.hkv = c.num_kv_heads;
+            a.rotary = c.rotary_dim;
+            a.max_chunks = cpb;
+            a.host_pos = -1;
+            a.eps = c.rms_eps;
+            a.scale = 1.0f / std::sqrt((float)c.head_dim);
+            st.push_back(ps);
+            ps.kind = kStAttnMerge;
+            st.push_back(ps);
+            GemvBuild go(kOpOProj, q_only(c), f32);
+            go.a.pro.kind = kProLoadF32;
+            go.a.pro.x = ga;
+            GemvSeg& so = go.add(w.o_proj, kEpiResidActIn);
+            so.out = x_resid;
+            (f32 ? so.pre4 : so.pre2) = X[l];
+            gemv_stage(kStOProj, go);
+            mlp(w.gate_proj, w.up_proj, w.down_proj, w.post_ln, x_resid, X[l + 1]);
+        }
+    }
+    first.push_back((uint32_t)st.size());
+    if (tail) {
+        float* pval = b.f32(blocks);
+        int32_t* pidx = reinterpret_cast<int32_t*>(b.f32(blocks));
+        GemvBuild g(kOpLmHead, c.hidden, f32);
+        g.a.pro.kind = kProRmsAct;
+        g.a.pro.x_f32 = f32;
+        g.a.pro.x = X[d->n_layers];
+        g.a.pro.w = d->final_norm;
+        g.a.pro.eps = c.rms_eps;
+        g.add(*d->lm_head, kEpiArgmax).out = d->logits;
+        g.a.am.part_val = pval;
+        g.a.am.part_idx = pidx;
+        gemv_stage(kStLmHead, g);
+        PStage ps;
+        std::memset(&ps, 0, sizeof(ps));
+        ps.kind = kStFinish;
+        LmFinishArgs& f = ps.f;
+        f.part_val = pval;
+        f.part_idx = pidx;
+        f.nparts = blocks;
+        f.vocab = c.vocab;
+        f.tokens = d->tokens;
+        f.positions = d->positions;
+        f.history = d->history;
+        f.history_len = d->history ? d->history_len : 0;
+        f.history_base = d->history_base;
+        f.embed = d->embed;
+        f.x_next = X[0];
+        f.hidden = c.hidden;
+        f.act_f32 = f32 ? 1 : 0;
+        st.push_back(ps);
+    }
+    if (st.size() != nst) return fail(Q35_ERR_INVALID_ARG, "internal: %zu stages != %u", st.size(), nst);
+    *total = b.off;
+    if (stages) *stages = std::move(st);
+    if (plan) {
+        plan->shape = shape;
+        plan->blocks = blocks;
+        plan->args.stages = table;
+        plan->args.nstages = nst;
+        plan->args.flags = flags;
+        plan->args.ctl = ctl;
+        plan->args.stamps = stamps;
+        plan->n_layers = d->n_layers;
+        plan->first_stage = first;
+        plan->x_in = X;
+    }
+    return Q35_OK;
+}
+
+// Runs f with the plan's device current, restoring the caller's.
+template <class F>
+q35_status on_device(int dev, F&& f) {
+    int prev = 0;
+    Q35_HIP(hipGetDevice(&prev), "hipGetDevice");
+    if (prev != dev) Q35_HIP(hipSetDevice(dev), "hipSetDevice");
+    const q35_status st = f();
+    if (prev != dev) (void)hipSetDevice(prev);
+    return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+q35_status q35_decode_workspace_bytes(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                                      const Q35DecodeStackDesc* stack, size_t* bytes) {
+    if (!bytes) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    size_t total = 0;
+    Q35_TRY(plan_build(kernels, cfg, stack, nullptr, &total, nullptr, nullptr));
+    *bytes = total;
+    return ok();
+}
+
+q35_status q35_decode_plan_create(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                                  const Q35DecodeStackDesc* stack, void* workspace,
+                                  size_t workspace_bytes, Q35DecodePlan** out) {
+    if (!out) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    *out = nullptr;
+    size_t total = 0;
+    Q35_TRY(plan_build(kernels, cfg, stack, nullptr, &total, nullptr, nullptr));
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(Q35_ERR_INVALID_ARG, "workspace NULL or not 256-byte aligned");
+    if (workspace_bytes < total)
+        return fail(Q35_ERR_INVALID_ARG, "workspace %zu bytes < %zu required", workspace_bytes, total);
+    Q35DecodePlan* plan = new Q35DecodePlan();
+    plan->device = kernels->device;
+    std::vector<PStage> stages;
+    q35_status st = plan_build(kernels, cfg, stack, static_cast<uint8_t*>(workspace), &total, &stages, plan);
+    if (st == Q35_OK) {
+        st = on_device(plan->device, [&]() -> q35_status {
+            int coop = 0, khz = 0;
+            Q35_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, plan->device),
+                    "hipDeviceGetAttribute");
+            if (!coop) return fail(Q35_ERR_UNSUPPORTED, "device %d cannot launch cooperatively", plan->device);
+            Q35_HIP(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, plan->device),
+                    "hipDeviceGetAttribute");
+            if (khz <= 0) return fail(Q35_ERR_UNSUPPORTED, "no device wall clock");
+            plan->clock_hz = (uint64_t)khz * 1000u;
+            plan->args.spin_ticks = (uint64_t)(kWaitLimitSeconds * (double)plan->clock_hz);
+            int per_cu = 0;
+            Q35_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                        &per_cu, persist_kernel_ptr(plan->shape), kPersistThreads,
+                        persist_lds_bytes(plan->shape)),
+                    "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+            if (per_cu < 1) return fail(Q35_ERR_UNSUPPORTED, "the persistent kernel does not fit on a CU");
+            Q35_HIP(hipMemcpy(const_cast<PStage*>(plan->args.stages), stages.data(),
+                              stages.size() * sizeof(PStage), hipMemcpyHostToDevice),
+                    "stage table upload");
+            Q35_HIP(hipMemset(plan->args.ctl, 0, 256), "sync word clear");
+            Q35_HIP(hipMemset(plan->args.flags, 0, 4u * plan->blocks), "sync word clear");
+            Q35_HIP(hipMemset(plan->args.stamps, 0, 8u * plan->args.nstages), "stamp clear");
+            if (stack->lm_head) {
+                Q35_HIP(embed_launch(stack->embed, stack->tokens, cfg->vocab, cfg->hidden, plan->x_in[0],
+                                     cfg->act_dtype == Q35_ACT_F32, nullptr),
+                        "first embedding");
+            }
+            Q35_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize");
+            return Q35_OK;
+        });
+    }
+    if (st != Q35_OK) {
+        delete plan;
+        return st;
+    }
+    *out = plan;
+    return ok();
+}
+
+void q35_decode_plan_release(Q35DecodePlan* plan) { delete plan; }
+
+q35_status q35_decode_step(const Q35DecodePlan* plan, hipStream_t stream) {
+    if (!plan) return fail(Q35_ERR_INVALID_ARG, "NULL plan");
+    Q35_HIP(persist_launch(plan->shape, plan->args, plan->blocks, stream), "persistent decode launch");
+    return ok();
+}
+
+q35_status q35_decode_check(const Q35DecodePlan* plan, uint32_t* error_word) {
+    if (!plan || !error_word) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    Q35_TRY(on_device(plan->device, [&]() -> q35_status {
+        Q35_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize");
+        Q35_HIP(hipMemcpy(error_word, plan->args.ctl + 1, 4, hipMemcpyDeviceToHost), "error word read");
+        return Q35_OK;
+    }));
+    return ok();
+}
+
+q35_status q35_decode_layer_input(const Q35DecodePlan* plan, uint32_t layer, void** x) {
+    if (!plan || !x) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    if (layer > plan->n_layers) return fail(Q35_ERR_OUT_OF_RANGE, "layer %u > %u", layer, plan->n_layers);
+    *x = plan->x_in[layer];
+    return ok();
+}
+
+q35_status q35_decode_stage_layout(const Q35DecodePlan* plan, uint32_t* n_stages,
+                                   uint32_t* layer_first_stage) {
+    if (!plan) return fail(Q35_ERR_INVALID_ARG, "NULL plan");
+    if (n_stages) *n_stages = plan->args.nstages;
+    if (layer_first_stage)
+        std::memcpy(layer_first_stage, plan->first_stage.data(), plan->first_stage.size() * sizeof(uint32_t));
+    return ok();
+}
+
+q35_status q35_decode_stage_times(const Q35DecodePlan* plan, uint64_t* ticks, uint32_t n,
+                                  uint64_t* ticks_per_second) {
+    if (!plan || !ticks) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    if (n > plan->args.nstages) return fail(Q35_ERR_OUT_OF_RANGE, "%u > %u stages", n, plan->args.nstages);
+    Q35_TRY(on_device(plan->device, [&]() -> q35_status {
+        Q35_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize");
+        Q35_HIP(hipMemcpy(ticks, plan->args.stamps, 8u * n, hipMemcpyDeviceToHost), "stamp read");
+        return Q35_OK;
+    }));
+    if (ticks_per_second) *ticks_per_second = plan->clock_hz;
     return ok();
 }
 

@@ -73,9 +73,58 @@ Q35_DEV float group_sum_all(float v) {
 constexpr int kBufWord3 = 0x00020000;  // raw buffer resource, gfx9 family
 constexpr int kAuxStream = 2;          // non-temporal: data streamed once per call
 
+// Device-coherent access (the sc1 cache-policy bit): what agent-scope atomic
+// loads and stores use.  Data one block writes and another block of the same
+// launch reads later goes through these, so no stage needs an L2 write-back
+// or invalidate.
+constexpr int kAuxCoherent = 16;
+
 // Raw buffer resource over [p, p + bytes): loads past the end return zero.
 Q35_DEV __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kBufWord3);
+}
+
+template <int AUX>
+Q35_DEV uint4 ld_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+}
+
+// Stores of values another block reads in the same launch (COH), else plain.
+template <bool COH>
+Q35_DEV void st_f32(float* p, uint32_t i, float v) {
+    if constexpr (COH)
+        __hip_atomic_store(p + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        p[i] = v;
+}
+
+template <bool COH>
+Q35_DEV void st_i32(int32_t* p, uint32_t i, int32_t v) {
+    if constexpr (COH)
+        __hip_atomic_store(p + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        p[i] = v;
+}
+
+template <bool COH>
+Q35_DEV void st_act_t(void* p, uint32_t i, float v, bool is_f32) {
+    if (is_f32) {
+        st_f32<COH>(static_cast<float*>(p), i, v);
+    } else {
+        const uint16_t b = static_cast<uint16_t>(f32_to_bf16(v));
+        if constexpr (COH)
+            __hip_atomic_store(static_cast<uint16_t*>(p) + i, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            static_cast<uint16_t*>(p)[i] = b;
+    }
+}
+
+// Loads of values another block wrote earlier in the same launch.
+Q35_DEV float ld_coh_f32(const float* p, uint32_t i) {
+    return __hip_atomic_load(const_cast<float*>(p) + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+Q35_DEV int32_t ld_coh_i32(const int32_t* p, uint32_t i) {
+    return __hip_atomic_load(const_cast<int32_t*>(p) + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Sum over aligned groups of W lanes (W in {2,4,8,16,32,64}).  The result is
@@ -138,5 +187,15 @@ Q35_DEV float uniform_f(float v) {
 }
 
 Q35_DEV uint32_t lane_id() { return threadIdx.x & 63u; }
+
+// threadIdx.x through an opaque copy.  In a kernel that runs many stages in a
+// loop, the compiler would otherwise compute every stage's thread-derived
+// values once, before the loop, and hold them all in registers for the whole
+// launch; the opaque copy makes each use site compute its own.
+Q35_DEV int tid_x() {
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
 
 }  // namespace q35

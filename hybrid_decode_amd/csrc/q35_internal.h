@@ -185,4 +185,50 @@ struct LmFinishArgs {
 hipError_t lm_finish_launch(const LmFinishArgs& a, hipStream_t stream);
 const void* lm_finish_kernel_ptr();
 
+// ------------------------------------------------------------------ persistent decode
+
+// One cooperative launch runs a table of stages (a token through the stack).
+constexpr int kPersistThreads = 1024;  // threads per block; one block per CU
+
+enum : int32_t {
+    kStInGdn = 1,   // GEMV kOpInGdn
+    kStGdn,         // gated delta rule
+    kStOutGated,    // GEMV kOpOutGated
+    kStInFull,      // GEMV kOpInFull
+    kStAttn,        // attention partials (q/k norm, RoPE, KV append)
+    kStAttnMerge,   // log-sum-exp merge + sigmoid gate
+    kStOProj,       // GEMV kOpOProj
+    kStGateUp,      // GEMV kOpGateUp
+    kStDown,        // GEMV kOpDown
+    kStLmHead,      // GEMV kOpLmHead (per-block argmax partials)
+    kStFinish,      // block 0: greedy token, bookkeeping, next embedding
+};
+
+struct PStage {
+    int32_t kind;
+    int32_t pad;
+    union {
+        GemvArgs g;
+        GdnArgs d;
+        AttnArgs at;  // max_chunks = chunks per kv head (blocks / Hkv)
+        LmFinishArgs f;
+    };
+};
+
+struct PersistArgs {
+    const PStage* stages;  // device, [nstages]
+    uint32_t nstages;
+    uint32_t* flags;       // [blocks] stages completed (wrapping)
+    uint32_t* ctl;         // [0] epoch (launches completed), [1] error (a wait expired)
+    uint64_t* stamps;      // optional [nstages]: block 0's time at each stage's start
+    uint64_t spin_ticks;   // wall-clock ticks before a wait gives up
+};
+
+// 1: Qwen3.5-4B shapes with bf16 activations; 2: the tiny fp32 shapes; 0: none.
+int persist_shape_id(uint32_t hidden, uint32_t inter, uint32_t q_only, uint32_t z_dim, uint32_t dk,
+                     uint32_t head_dim, uint32_t group, bool half);
+size_t persist_lds_bytes(int shape);
+const void* persist_kernel_ptr(int shape);
+hipError_t persist_launch(int shape, const PersistArgs& a, uint32_t blocks, hipStream_t stream);
+
 }  // namespace q35

@@ -221,6 +221,77 @@ def inv_freq_dev(cfg, device="cuda") -> torch.Tensor:
     return torch.from_numpy(B.q35_rope_inv_freq(cfg_struct(cfg))).to(device)
 
 
+# --------------------------------------------------------------------------- persistent decode
+
+class DecodePlan:
+    """A stack's layers (and optionally its tail) run by the persistent decode
+    kernel: ``step()`` is one cooperative launch per token."""
+
+    def __init__(self, cfg, kinds, layers, states, kvs, inv_freq, positions, tail=None,
+                 device: int = 0):
+        import ctypes as C
+        self.cfg, self.kinds, self.device = cfg, list(kinds), device
+        self.c = cfg_struct(cfg)
+        self.k = kernels(device)
+        n = len(kinds)
+        arr = (B.Q35StackLayer * n)()
+        for i, kind in enumerate(kinds):
+            if kind == "gdn":
+                arr[i].kind = B.Q35_LAYER_LINEAR
+                arr[i].linear = C.pointer(layers[i].struct)
+                arr[i].state = C.pointer(states[i].struct)
+            else:
+                arr[i].kind = B.Q35_LAYER_FULL
+                arr[i].full = C.pointer(layers[i].struct)
+                arr[i].kv = C.pointer(kvs[i].struct)
+        d = B.Q35DecodeStackDesc()
+        d.n_layers = n
+        d.layers = arr
+        d.inv_freq = ptr(inv_freq)
+        d.positions = ptr(positions)
+        self.tail = tail
+        if tail is not None:
+            d.lm_head = C.pointer(tail["lm_head"].struct)
+            d.final_norm = ptr(tail["final_norm"])
+            d.embed = ptr(tail["embed"])
+            d.tokens = ptr(tail["tokens"])
+            d.logits = ptr(tail.get("logits"))
+            d.history = ptr(tail.get("history"))
+            d.history_len = tail.get("history_len", 0)
+            d.history_base = tail.get("history_base", 0)
+        self._keep = (arr, d, layers, states, kvs, inv_freq, positions)
+        nbytes = B.q35_decode_workspace_bytes(self.k, self.c, d)
+        self.ws = torch.zeros(nbytes + 256, dtype=torch.uint8, device=f"cuda:{device}")
+        off = (-self.ws.data_ptr()) % 256
+        self.ws_off = off
+        self.plan = B.q35_decode_plan_create(self.k, self.c, d, self.ws.data_ptr() + off, nbytes)
+        self.n_stages, self.first_stage = B.q35_decode_stage_layout(self.plan, n)
+
+    def step(self, stream=None) -> None:
+        B.q35_decode_step(self.plan, stream_ptr(stream))
+
+    def check(self) -> int:
+        """Error word of the plan (0: every inter-block wait completed)."""
+        return B.q35_decode_check(self.plan)
+
+    def layer_input(self, layer: int) -> torch.Tensor:
+        """View of layer `layer`'s input residual stream (layer == n: the last output)."""
+        p = B.q35_decode_layer_input(self.plan, layer)
+        o = p - self.ws.data_ptr()
+        nb = self.cfg.hidden * (4 if self.cfg.act_dtype == "f32" else 2)
+        return self.ws[o:o + nb].view(act_dtype(self.cfg))
+
+    def stage_times_us(self):
+        ticks, hz = B.q35_decode_stage_times(self.plan, self.n_stages)
+        return ticks, hz
+
+    def __del__(self):
+        try:
+            B.q35_decode_plan_release(self.plan)
+        except Exception:
+            pass
+
+
 # --------------------------------------------------------------------------- decode stack
 
 class DecodeStack:
@@ -233,7 +304,8 @@ class DecodeStack:
     """
 
     def __init__(self, cfg, kinds, layers, states, kvs, embed, final_norm, lm_head, start_pos: int,
-                 start_token: int, history_len: int = 0, device: int = 0, taps: bool = False):
+                 start_token: int, history_len: int = 0, device: int = 0, taps: bool = False,
+                 persistent: bool = False):
         dev = f"cuda:{device}"
         self.cfg, self.kinds, self.device = cfg, list(kinds), device
         self.c = cfg_struct(cfg)
@@ -262,12 +334,23 @@ class DecodeStack:
         self.k = kernels(device)
         B.q35_embed_lookup(self.k, self.c, ptr(self.embed), ptr(self.tokens), ptr(self.x_embed),
                            stream_ptr())
+        self.plan = None
+        if persistent:
+            tail = {"lm_head": self.lm_head, "final_norm": self.final_norm, "embed": self.embed,
+                    "tokens": self.tokens, "logits": self.logits,
+                    "history": self.history if history_len else None,
+                    "history_len": history_len, "history_base": self.history_base}
+            self.plan = DecodePlan(cfg, self.kinds, self.layers, self.states, self.kvs,
+                                   self.inv_freq, self.positions, tail, device)
 
     @property
     def weight_bytes(self) -> int:
         return sum(l.weight_bytes for l in self.layers) + self.lm_head.nbytes
 
     def step(self, stream=None, write_logits: bool = True) -> None:
+        if self.plan is not None:  # one persistent launch (logits always written when held)
+            self.plan.step(stream)
+            return
         s = stream_ptr(stream)
         x = ptr(self.x_embed)
         for li, kind in enumerate(self.kinds):

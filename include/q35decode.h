@@ -390,6 +390,111 @@ q35_status q35_lm_head_argmax(const Qwen35Kernels* kernels, const Qwen35ForwardC
                               int32_t* history, uint32_t history_len, int32_t history_base,
                               const uint16_t* embed_table, void* x_next, hipStream_t stream);
 
+/* ------------------------------------------------------------------ persistent decode */
+
+/*
+ * The same per-token computation as calling q35_forward_linear_attention /
+ * q35_forward_full_attention layer by layer and then q35_lm_head_argmax
+ * (linear_attention.rs and full_attention.rs pages: every step of both
+ * forwards, in the pages' order), run as ONE cooperative launch per token: a
+ * persistent kernel with one block per compute unit executes a table of
+ * stages (5 per GDN layer, 6 per full-attention layer, 2 for the tail) and
+ * synchronises the blocks between stages itself.  Each stage's weight loads
+ * are issued before the wait for its inputs, so HBM keeps streaming across
+ * stage and layer boundaries.  Results equal the layer-by-layer path up to
+ * fp32 summation order (split-K attention chunks follow the block count).
+ *
+ * Supported shapes: the Qwen3.5-4B layer dimensions with bf16 activations
+ * (hidden 2560, intermediate 9216, 16 q heads / 4 kv heads of 256, 16 k / 32 v
+ * heads of 128) and the small fp32 test dimensions (hidden 256, intermediate
+ * 512, 4 q / 2 kv heads of 64, 2 k / 4 v heads of 32); others return
+ * Q35_ERR_UNSUPPORTED (use the per-layer calls).
+ */
+#define Q35_LAYER_LINEAR 0u
+#define Q35_LAYER_FULL 1u
+
+typedef struct Q35StackLayer {
+    uint32_t kind;                       /* Q35_LAYER_LINEAR or Q35_LAYER_FULL */
+    const LinearAttentionLayer* linear;  /* kind == LINEAR: weights */
+    const LinearAttentionState* state;   /* kind == LINEAR: conv and GDN state (updated) */
+    const FullAttentionLayer* full;      /* kind == FULL: weights */
+    const LayerKvCache* kv;              /* kind == FULL: bf16 cache (row positions[0] written) */
+} Q35StackLayer;
+
+/* Host-side description of a stack; every pointer member other than `layers`
+ * is a device pointer owned by the caller and must outlive the plan. */
+typedef struct Q35DecodeStackDesc {
+    uint32_t n_layers;
+    const Q35StackLayer* layers;   /* host array [n_layers], read at plan creation */
+    const float* inv_freq;         /* fp32 [rotary_dim/2] (q35_rope_inv_freq); any full layer */
+    int32_t* positions;            /* int32 [1]: this token's cache position (the tail adds 1) */
+    /* Stack tail (final RMSNorm, lm_head, greedy token, next embedding).  With
+     * lm_head == NULL the plan is layers only and the caller writes each token's
+     * input into q35_decode_layer_input(plan, 0) before the step. */
+    const Q35QuantWeight* lm_head; /* [vocab, hidden] (host struct, device arrays) */
+    const uint16_t* final_norm;    /* bf16 [hidden] */
+    const uint16_t* embed;         /* bf16 [vocab, hidden], 16-byte aligned */
+    int32_t* tokens;               /* int32 [1]: current token; receives the next one */
+    float* logits;                 /* optional fp32 [vocab] */
+    int32_t* history;              /* optional int32 [history_len]: token at positions[0]-history_base */
+    uint32_t history_len;
+    int32_t history_base;
+} Q35DecodeStackDesc;
+
+typedef struct Q35DecodePlan Q35DecodePlan;
+
+/* Device workspace q35_decode_plan_create needs for this stack (per-layer
+ * activation buffers, attention partials, the stage table, sync words). */
+q35_status q35_decode_workspace_bytes(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                                      const Q35DecodeStackDesc* stack, size_t* bytes);
+
+/*
+ * Validates the stack (as the per-layer calls do), writes the stage table into
+ * the caller's device workspace (256-byte aligned; synchronous copy), clears its
+ * sync words, and,
+ * with a tail, writes the embedding of tokens[0] into the first layer's input.
+ * The workspace must not be used by anything else while the plan lives.  *out
+ * is a host object freed with q35_decode_plan_release.  Errors:
+ * Q35_ERR_UNSUPPORTED (shape, or a device that cannot launch the grid
+ * cooperatively), Q35_ERR_INVALID_ARG (as the per-layer calls; workspace too
+ * small), Q35_ERR_HIP.
+ */
+q35_status q35_decode_plan_create(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                                  const Q35DecodeStackDesc* stack, void* workspace,
+                                  size_t workspace_bytes, Q35DecodePlan** out);
+void q35_decode_plan_release(Q35DecodePlan* plan);
+
+/*
+ * One token: every layer at cache position positions[0] (read on the device,
+ * so one captured graph replays every token), then the tail.  Enqueued on
+ * `stream`; capturable.  Steps of one plan must not overlap (one stream).
+ */
+q35_status q35_decode_step(const Q35DecodePlan* plan, hipStream_t stream);
+
+/*
+ * Synchronises the device and reads the plan's error word: 0 when every
+ * inter-block wait so far completed; 1 when one gave up after its time limit
+ * (the results of that step are invalid; create a new plan).
+ */
+q35_status q35_decode_check(const Q35DecodePlan* plan, uint32_t* error_word);
+
+/* Device pointer of layer `layer`'s input residual stream (act [hidden]);
+ * layer == n_layers gives the last layer's output (the tail's input). */
+q35_status q35_decode_layer_input(const Q35DecodePlan* plan, uint32_t layer, void** x);
+
+/* Number of stages, and the first stage of each layer (host array [n_layers + 1]:
+ * the last entry is the tail's first stage). */
+q35_status q35_decode_stage_layout(const Q35DecodePlan* plan, uint32_t* n_stages,
+                                   uint32_t* layer_first_stage);
+
+/*
+ * Synchronises and copies, for the last step, block 0's wall-clock time at the
+ * start of each stage (after its wait; stage 0 does not wait) into host ticks
+ * [n], n <= n_stages, plus the clock rate in Hz.
+ */
+q35_status q35_decode_stage_times(const Q35DecodePlan* plan, uint64_t* ticks, uint32_t n,
+                                  uint64_t* ticks_per_second);
+
 /* ------------------------------------------------------------------ kernel-level export */
 
 /*

@@ -1,8 +1,9 @@
 """GPU parity of the layer loop: the tiny two-layer hybrid at every step, and the
-32-layer 4B-shaped stack (real lm_head) at KV context 8192 and 65536 in the
-benchmark's launch configuration, on sampled layers (each fed the GPU's own
-input to that layer), sampled logits and the greedy token, plus HIP-graph replay
-against eager execution."""
+32-layer 4B-shaped stack (real lm_head) at KV context 8192 and 65536, both
+layer by layer and through the persistent decode kernel (the benchmark's launch
+configuration), on sampled layers (each fed the GPU's own input to that layer),
+sampled logits and the greedy token, plus HIP-graph replay against eager
+execution and the two paths against each other."""
 import numpy as np
 import pytest
 import torch
@@ -43,15 +44,19 @@ def test_tiny_stack_16_tokens(rt, gen):
     assert rel(S0.to_host()["gdn_state"], states[0]["gdn_state"]) < TOL_F32
 
 
-def _make_stack(rt, ctx):
+def _stack_from(rt, w, persistent=False):
+    st = rt.DecodeStack(w["cfg"], w["kinds"], w["layers"], w["states"], w["kvs"], w["embed"],
+                        w["final_norm"], w["lm_head"], start_pos=w["ctx"],
+                        start_token=w["start_token"], history_len=64, persistent=persistent)
+    torch.cuda.synchronize()
+    return st
+
+
+def _make_stack(rt, ctx, persistent=False):
     say(f"generating the 32-layer 4B stack at ctx {ctx}")
     g = synth.Gen(0)
     w = workloads.stack_4b(g, num_layers=32, ctx=ctx, extra=64)
-    st = rt.DecodeStack(w["cfg"], w["kinds"], w["layers"], w["states"], w["kvs"], w["embed"],
-                        w["final_norm"], w["lm_head"], start_pos=w["ctx"],
-                        start_token=w["start_token"], history_len=64)
-    torch.cuda.synchronize()
-    return w, st
+    return w, _stack_from(rt, w, persistent)
 
 
 @pytest.fixture(scope="module")
@@ -63,11 +68,14 @@ def stack8k(rt):
 def _snapshot(st):
     return ([None if s is None else (s.conv1d_state.clone(), s.gdn_state.clone()) for s in st.states],
             [None if kv is None else (kv.k.clone(), kv.v.clone()) for kv in st.kvs],
-            st.positions.clone(), st.tokens.clone(), st.x_embed.clone())
+            st.positions.clone(), st.tokens.clone(), st.x_embed.clone(),
+            None if st.plan is None else st.plan.layer_input(0).clone())
 
 
 def _restore(st, snap):
-    ss, kk, p, t, x = snap
+    ss, kk, p, t, x, x0 = snap
+    if x0 is not None:
+        st.plan.layer_input(0).copy_(x0)
     for s, v in zip(st.states, ss):
         if s is not None:
             s.conv1d_state.copy_(v[0])
@@ -196,6 +204,152 @@ def test_stack_4b_ctx65536_sampled_layers_logits_and_token(rt):
     w, st = _make_stack(rt, 65536)
     try:
         _check_one_token(rt, w, st, sample_layers=(0, 3, 31))
+    finally:
+        del st
+        torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------- persistent kernel
+
+
+@pytest.fixture(scope="module")
+def persist8k(rt, stack8k):
+    """The same workload run by the persistent decode kernel (the benchmark's path)."""
+    w, _ = stack8k
+    say("persistent plan over the 8192-context stack")
+    return _stack_from(rt, w, persistent=True)
+
+
+def _check_persistent_token(rt, w, st, sample_layers):
+    """One persistent step; every layer's input and output stay in the plan's
+    buffers, so each sampled layer is checked against the oracle fed with the
+    GPU's own input to it, then sampled logits, the token and the bookkeeping."""
+    cfg, kinds = w["cfg"], w["kinds"]
+    plan = st.plan
+    snap = _snapshot(st)
+    x0 = rt.act_to_host(plan.layer_input(0), cfg).copy()
+    assert np.array_equal(x0, w["embed"][w["start_token"]])
+    say("one persistent decode step")
+    st.step()
+    torch.cuda.synchronize()
+    assert plan.check() == 0
+    inv_h = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
+    pos = w["ctx"]
+    for li in sample_layers:
+        xin = x0 if li == 0 else rt.act_to_host(plan.layer_input(li), cfg).copy()
+        xout = rt.act_to_host(plan.layer_input(li + 1), cfg).copy()
+        say(f"oracle check of layer {li} ({kinds[li]})")
+        if kinds[li] == "gdn":
+            ox, _, _ = O.forward_linear_attention(cfg, w["layers"][li], w["states"][li], xin)
+        else:
+            ox, _, _ = O.forward_full_attention(cfg, w["layers"][li], w["kvs"][li], inv_h, xin, pos)
+        r = rel(O.act_to_f64(xout, "bf16"), ox)
+        say(f"  layer {li}: rel {r:.2e}")
+        assert r < TOL_BF16, li
+    x_last = rt.act_to_host(plan.layer_input(len(kinds)), cfg).copy()
+    g = st.logits.cpu().numpy()
+    tok = int(st.tokens.cpu()[0])
+    rows = np.random.default_rng(1).choice(cfg.vocab, 4096, replace=False)
+    rows = np.unique(np.concatenate([rows, [tok, int(np.argmax(g))]]))
+    h = O.rms_norm(O.act_to_f64(x_last, "bf16"), w["final_norm"], cfg.rms_eps)
+    ref = O.dequant({k: v[rows] for k, v in w["lm_head"].items()}).astype(np.float64) @ h
+    r = rel(g[rows], ref)
+    say(f"sampled logits rel {r:.2e}")
+    assert r < TOL_GEMV_F16
+    assert tok == int(np.argmax(g))
+    assert int(st.positions.cpu()[0]) == pos + 1
+    assert int(st.history.cpu()[0]) == tok
+    assert np.array_equal(rt.act_to_host(plan.layer_input(0), cfg), w["embed"][tok])
+    _restore(st, snap)
+
+
+def test_persistent_stack_4b_ctx8192_sampled_layers_logits_and_token(rt, stack8k, persist8k):
+    w, _ = stack8k
+    _check_persistent_token(rt, w, persist8k, sample_layers=(0, 3, 13, 15, 30, 31))
+
+
+def test_persistent_stack_matches_layer_by_layer(rt, stack8k, persist8k):
+    """One token through both paths from the same state, every layer compared.
+    GDN layers use the same row arithmetic, so they agree bit for bit until the
+    first full-attention layer, whose split-K chunking differs; from there the
+    paths differ by fp32 summation order carried through bf16 residuals (the
+    greedy tokens may then legitimately differ), within the bf16 tolerance."""
+    from hybrid_decode_amd import binding as B
+    w, st = stack8k
+    ps = persist8k
+    cfg, kinds = w["cfg"], w["kinds"]
+    sa, sb = _snapshot(st), _snapshot(ps)
+    s = rt.stream_ptr()
+    x = st.x_embed.data_ptr()
+    outs = []
+    for li, kind in enumerate(kinds):
+        if kind == "gdn":
+            B.q35_forward_linear_attention(st.k, st.c, st.layers[li].struct, st.states[li].struct,
+                                           st.gdn_scratch.struct, x, st.x_main.data_ptr(), s)
+            last = st.x_main
+        else:
+            B.q35_forward_full_attention_devpos(st.k, st.c, st.layers[li].struct,
+                                                st.full_scratch.struct, st.kvs[li].struct,
+                                                st.inv_freq.data_ptr(), st.positions.data_ptr(), x, s)
+            last = st.full_scratch.t["x_out"]
+        x = last.data_ptr()
+        torch.cuda.synchronize()
+        outs.append(rt.act_to_f32(last, cfg).copy())
+    say("persistent step")
+    ps.step()
+    torch.cuda.synchronize()
+    assert ps.plan.check() == 0
+    first_full = kinds.index("full")
+    worst = 0.0
+    for li in range(len(kinds)):
+        r = rel(rt.act_to_f32(ps.plan.layer_input(li + 1), cfg), outs[li])
+        worst = max(worst, r)
+        if li < first_full:
+            assert r == 0.0, li
+        assert r < TOL_BF16, (li, r)
+    say(f"first full layer rel {rel(rt.act_to_f32(ps.plan.layer_input(first_full + 1), cfg), outs[first_full]):.2e}; "
+        f"worst layer rel {worst:.2e}")
+    assert rel(rt.act_to_f32(ps.plan.layer_input(first_full + 1), cfg), outs[first_full]) < 1e-3
+    _restore(st, sa)
+    _restore(ps, sb)
+
+
+def test_persistent_graph_replay_matches_eager(rt, persist8k):
+    st = persist8k
+    snap = _snapshot(st)
+    steps = 4
+    say("eager persistent decode of 4 tokens")
+    for _ in range(steps):
+        st.step()
+    torch.cuda.synchronize()
+    eager_hist = st.history.cpu().numpy()[:steps].copy()
+    eager_logits = st.logits.cpu().numpy().copy()
+    eager_state = st.states[0].gdn_state.cpu().numpy().copy()
+    eager_k = st.kvs[3].k.cpu().numpy().copy()
+    _restore(st, snap)
+    say("capturing one persistent step into a HIP graph")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st.step()
+    torch.cuda.synchronize()
+    _restore(st, snap)
+    for i in range(steps):
+        say(f"persistent graph replay {i}")
+        graph.replay()
+        torch.cuda.synchronize()
+    assert st.plan.check() == 0
+    assert np.array_equal(st.history.cpu().numpy()[:steps], eager_hist)
+    assert np.array_equal(st.logits.cpu().numpy(), eager_logits)
+    assert np.array_equal(st.states[0].gdn_state.cpu().numpy(), eager_state)
+    assert np.array_equal(st.kvs[3].k.cpu().numpy(), eager_k)
+    _restore(st, snap)
+
+
+def test_persistent_stack_4b_ctx65536_sampled_layers_logits_and_token(rt):
+    """Config 5 through the persistent kernel (2.15 GB of bf16 KV)."""
+    w, st = _make_stack(rt, 65536, persistent=True)
+    try:
+        _check_persistent_token(rt, w, st, sample_layers=(0, 3, 31))
     finally:
         del st
         torch.cuda.empty_cache()
