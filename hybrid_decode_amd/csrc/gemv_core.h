@@ -621,6 +621,22 @@ Q35_DEV void argmax_partial(const GemvArgs& a, float best_v, int best_i, float* 
 // device-coherent loads and stores; the wave's first row group of weights is
 // issued before wait() (which returns once the stage's inputs are published),
 // and a wave with no row group issues no loads.
+// The registers of one row group in flight: codes, scales and biases of each
+// matrix, and the epilogue operands.
+template <int NC, int NC2>
+struct RgBuf {
+    u32x4_t w[NC], w2[NC2];  // paired: w2 holds the second matrix's rows of the same index
+    uint32_t sv[NC], bv[NC], sv2[NC2], bv2[NC2];
+    EpiPre pre;
+};
+
+// The body shared by the standalone kernels and the stages of the persistent
+// decode kernel.  rg: this wave's first row group; nw: the stride between its
+// row groups.  COH (persistent stages): x, the epilogue operands and the outputs are exchanged with other
+// blocks of the same launch, so they use device-coherent loads and stores;
+// the wave's first row group of weights is issued before wait() (which
+// returns once the stage's inputs are published), and a wave with no row
+// group issues no loads.
 template <int K, int OP, bool HALF, bool XREG, int NT, bool COH, class Wait>
 Q35_DEV void gemv_body(const GemvArgs& a, uint32_t rg, uint32_t nw, Wait&& wait) {
     using T = Op<OP>;
@@ -642,30 +658,33 @@ Q35_DEV void gemv_body(const GemvArgs& a, uint32_t rg, uint32_t nw, Wait&& wait)
     constexpr int PRE_AUX = COH ? kAuxCoherent : 0;
 
     constexpr int NC2 = PAIRED ? NC : 1;
-    u32x4_t w[NC], w2[NC2];  // paired: w2 holds the second matrix's rows of the same index
-    uint32_t sv[NC], bv[NC], sv2[NC2], bv2[NC2];
+    using Buf = RgBuf<NC, NC2>;
     static_assert(!PAIRED || T::NSEG == 1, "a paired launch has one segment");
-    EpiPre pre;
     constexpr int PM = pre_mask<OP, HALF>();
-    // Branch-free in the segment: the same loads are issued whatever the row group.
-    auto load_rg = [&](uint32_t g) {
+    // Branch-free in the segment: the same loads are issued whatever the row
+    // group.  A row group past the end (live == false) gets empty buffer
+    // ranges: its loads return zero without touching memory, so they can be
+    // issued unconditionally and the compiler's count of loads in flight stays
+    // exact on every path.
+    auto load_rg = [&](uint32_t g, bool live, Buf& b) {
+        if (!live) g = total - 1;
         const int si = find_seg<T::NSEG>(a, g);
-        const uint32_t rows = pick<T::NSEG>(si, [&](int i) { return a.seg[i].rows; });
+        const uint32_t rows = live ? pick<T::NSEG>(si, [&](int i) { return a.seg[i].rows; }) : 0u;
         const uint32_t row0 = (g - pick<T::NSEG>(si, [&](int i) { return a.seg[i].rg_begin; })) * R;
         const uint32_t n = row0 + rloc;
         // epilogue operands first: they have landed once the weights have
         auto pre_rsrc = [&](const void* p, uint32_t elt) { return rsrc(p, p ? rows * elt : 0u); };
         if constexpr (PM & 16)
-            pre.q16 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+            b.pre.q16 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                 pre_rsrc(pick<T::NSEG>(si, [&](int i) { return a.seg[i].pre16; }), 16u), n * 16u, 0, PRE_AUX));
         if constexpr (PM & 8)
-            pre.q8 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+            b.pre.q8 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
                 pre_rsrc(pick<T::NSEG>(si, [&](int i) { return a.seg[i].pre8; }), 8u), n * 8u, 0, PRE_AUX));
         if constexpr (PM & 4)
-            pre.q4 = __builtin_amdgcn_raw_buffer_load_b32(
+            b.pre.q4 = __builtin_amdgcn_raw_buffer_load_b32(
                 pre_rsrc(pick<T::NSEG>(si, [&](int i) { return a.seg[i].pre4; }), 4u), n * 4u, 0, PRE_AUX);
         if constexpr (PM & 2)
-            pre.q2 = __builtin_amdgcn_raw_buffer_load_b16(
+            b.pre.q2 = __builtin_amdgcn_raw_buffer_load_b16(
                 pre_rsrc(pick<T::NSEG>(si, [&](int i) { return a.seg[i].pre2; }), 2u), n * 2u, 0, PRE_AUX);
         const uint32_t cbytes = rows * (uint32_t)K, sbytes = rows * (uint32_t)KG * 2u;
         const uint32_t coff = row0 * (uint32_t)K, soff = row0 * (uint32_t)KG * 2u;
@@ -682,11 +701,12 @@ Q35_DEV void gemv_body(const GemvArgs& a, uint32_t rg, uint32_t nw, Wait&& wait)
         };
         issue(pick<T::NSEG>(si, [&](int i) { return a.seg[i].codes[0]; }),
               pick<T::NSEG>(si, [&](int i) { return a.seg[i].scales[0]; }),
-              pick<T::NSEG>(si, [&](int i) { return a.seg[i].biases[0]; }), w, sv, bv);
+              pick<T::NSEG>(si, [&](int i) { return a.seg[i].biases[0]; }), b.w, b.sv, b.bv);
         if constexpr (PAIRED)
-            issue(a.seg[0].codes[1], a.seg[0].scales[1], a.seg[0].biases[1], w2, sv2, bv2);
+            issue(a.seg[0].codes[1], a.seg[0].scales[1], a.seg[0].biases[1], b.w2, b.sv2, b.bv2);
     };
 
+    Buf b0;
     ProRegs<K, T::PRO, NT> pr;
     if constexpr (COH) {
         // weights first (they do not depend on this launch), then the wait for
@@ -696,19 +716,16 @@ Q35_DEV void gemv_body(const GemvArgs& a, uint32_t rg, uint32_t nw, Wait&& wait)
 #else
         const bool early = true;
 #endif
-        if (early && rg < total) load_rg(rg);
+        if (early && rg < total) load_rg(rg, true, b0);
         asm volatile("" ::: "memory");
         wait();
-        if (!early && rg < total) load_rg(rg);
+        if (!early && rg < total) load_rg(rg, true, b0);
         prologue_issue<K, T::PRO, HALF, NT, true>(a.pro, pr);
     } else {
-        // x loads first, then the first row group's weights (vector loads complete in order)
+        // x loads first, then the first row groups' weights (vector loads complete in order)
         prologue_issue<K, T::PRO, HALF, NT>(a.pro, pr);
         asm volatile("" ::: "memory");
-        // Unconditional (a spare wave re-reads the last row group and discards it):
-        // the compiler then knows exactly how many loads follow x and waits for x
-        // alone instead of for every outstanding load.
-        load_rg(rg < total ? rg : total - 1);
+        load_rg(rg, rg < total, b0);
     }
     asm volatile("" ::: "memory");
 
@@ -717,7 +734,11 @@ Q35_DEV void gemv_body(const GemvArgs& a, uint32_t rg, uint32_t nw, Wait&& wait)
     float best_v = -INFINITY;
     int best_i = 0x7FFFFFFF;
 
-    while (rg < total) {
+    // One row group: dot products from buffer b, then (before this row group's
+    // epilogue stores: on this ISA the vector memory counter also counts stores,
+    // so a store issued first would make the next wait include its write
+    // latency) the request for the wave's next row group into b.
+    auto step = [&](Buf& b) {
         // Short streams keep x in LDS (an opaque zero offset stops the compiler
         // from hoisting every chunk of x into registers, which costs occupancy);
         // long streams (XREG) keep the hoisted copy in registers.
@@ -736,25 +757,24 @@ Q35_DEV void gemv_body(const GemvArgs& a, uint32_t rg, uint32_t nw, Wait&& wait)
                 else
                     return fmaf(sc, dot16(wi, xq[cc], xq[KC + cc], xq[2 * KC + cc], xq[3 * KC + cc]), bi * ab.y);
             };
-            acc += term(w[i], sv[i], bv[i]);
-            if constexpr (PAIRED) acc2 += term(w2[i % NC2], sv2[i % NC2], bv2[i % NC2]);
+            acc += term(b.w[i], b.sv[i], b.bv[i]);
+            if constexpr (PAIRED) acc2 += term(b.w2[i % NC2], b.sv2[i % NC2], b.bv2[i % NC2]);
         }
         // row sums land in the last lane of each group of LR lanes
         const float v = group_sum_last<LR>(acc) * post;
         const float v2 = PAIRED ? group_sum_last<LR>(acc2) * post : 0.f;
-        // Next row group's loads go out before this one's epilogue stores: on
-        // this ISA the vector memory counter also counts stores, so a store
-        // issued first would make the next wait include its write latency.
         const uint32_t cur = rg;
-        const EpiPre cpre = pre;
+        const EpiPre cpre = b.pre;
         rg += nw;
-        if (rg < total) load_rg(rg);
+        if (rg < total) load_rg(rg, true, b);
         with_seg<T::NSEG>(a, cur, [&](const GemvSeg& s, auto si) {
             constexpr int SI = decltype(si)::value;
             const uint32_t n = (cur - s.rg_begin) * R + rloc;
             if (li == LR - 1) epilogue<OP, SI, COH>(a, s, n, v, v2, cpre, best_v, best_i);
         });
-    }
+    };
+
+    while (rg < total) step(b0);
 
     if constexpr (OP == kOpLmHead) argmax_partial<NT, COH>(a, best_v, best_i, red);
 }
@@ -775,7 +795,7 @@ constexpr size_t lds_bytes() {  // x image + per-chunk (A, B) + reduction slots
 
 template <int K, int OP, bool HALF, bool XREG>
 hipError_t launch_t(const GemvArgs& a, uint32_t blocks, hipStream_t stream) {
-    constexpr int NT = kGemvThreads;
+    constexpr int NT = gemv_threads(OP);
     const size_t lds = lds_bytes<K, HALF>();
     hipLaunchKernelGGL((gemv_kernel<K, OP, HALF, XREG, NT>), dim3(blocks), dim3(NT), lds, stream, a);
     return hipGetLastError();
@@ -783,7 +803,7 @@ hipError_t launch_t(const GemvArgs& a, uint32_t blocks, hipStream_t stream) {
 
 template <int K, int OP, bool HALF, bool XREG>
 const void* kernel_ptr_t() {
-    return (const void*)&gemv_kernel<K, OP, HALF, XREG, kGemvThreads>;
+    return (const void*)&gemv_kernel<K, OP, HALF, XREG, gemv_threads(OP)>;
 }
 
 }  // namespace gemv

@@ -131,7 +131,7 @@ struct LmWs {
 LmWs lm_ws_layout(const Qwen35ForwardConfig& c) {
     LmWs w;
     const uint32_t r = (uint32_t)gemv_rows_per_matrix_group(c.hidden, false);
-    w.blocks = gemv_pick_blocks(c.vocab / r);
+    w.blocks = gemv_pick_blocks(c.vocab / r, kOpLmHead, 0);  // streaming shape: no CU count needed
     w.val_off = 0;
     w.idx_off = ((size_t)w.blocks * 4 + 255) & ~size_t(255);
     w.total = w.idx_off + (((size_t)w.blocks * 4 + 255) & ~size_t(255));
@@ -168,15 +168,15 @@ struct GemvBuild {
         s.epi = epi;
         return s;
     }
-    q35_status launch(hipStream_t stream, const char* what, uint32_t blocks = 0) {
-        if (!blocks) blocks = gemv_pick_blocks(a.total_rg);
+    q35_status launch(uint32_t num_cu, hipStream_t stream, const char* what, uint32_t blocks = 0) {
+        if (!blocks) blocks = gemv_pick_blocks(a.total_rg, op, num_cu);
         Q35_HIP(gemv_launch(op, k, a.act_f32 == 0, a, blocks, stream), what);
         return Q35_OK;
     }
 };
 
 // gate/up (paired, SwiGLU epilogue) and down (+ residual) shared by both layers.
-q35_status launch_mlp(const Qwen35ForwardConfig& c, const Q35QuantWeight& gate_proj,
+q35_status launch_mlp(uint32_t num_cu, const Qwen35ForwardConfig& c, const Q35QuantWeight& gate_proj,
                       const Q35QuantWeight& up_proj, const Q35QuantWeight& down_proj,
                       const uint16_t* post_ln, float* x_resid, float* x_norm2, float* mlp_act,
                       float* gate_act, float* up_act, void* x_out, void* x_out2,
@@ -193,7 +193,7 @@ q35_status launch_mlp(const Qwen35ForwardConfig& c, const Q35QuantWeight& gate_p
         s.out = mlp_act;
         s.tap0 = gate_act;
         s.tap1 = up_act;
-        Q35_TRY(b.launch(stream, "gate/up GEMV"));
+        Q35_TRY(b.launch(num_cu, stream, "gate/up GEMV"));
     }
     {
         GemvBuild b(kOpDown, c.intermediate, f32);
@@ -203,7 +203,7 @@ q35_status launch_mlp(const Qwen35ForwardConfig& c, const Q35QuantWeight& gate_p
         s.pre4 = x_resid;
         s.out_act = x_out;
         s.out_act2 = x_out2;
-        Q35_TRY(b.launch(stream, "down GEMV"));
+        Q35_TRY(b.launch(num_cu, stream, "down GEMV"));
     }
     return Q35_OK;
 }
@@ -508,7 +508,7 @@ static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35Fo
         b.add(layer->q_proj, kEpiStore).out = s->q_full;
         b.add(layer->k_proj, kEpiStore).out = s->k;
         b.add(layer->v_proj, kEpiStore).out = s->v;
-        Q35_TRY(b.launch(stream, "q/k/v GEMV"));
+        Q35_TRY(b.launch((uint32_t)kernels->num_cu, stream, "q/k/v GEMV"));
     }
     // 2. split, q/k norm, RoPE, KV append, split-K attention, sigmoid gate
     {
@@ -561,10 +561,10 @@ static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35Fo
         sg.out = s->x_resid;
         (f32 ? sg.pre4 : sg.pre2) = x_in;
         sg.tap0 = s->o;
-        Q35_TRY(b.launch(stream, "o_proj GEMV"));
+        Q35_TRY(b.launch((uint32_t)kernels->num_cu, stream, "o_proj GEMV"));
     }
     // 4-5. post-attention norm, SwiGLU MLP, residual
-    Q35_TRY(launch_mlp(c, layer->gate_proj, layer->up_proj, layer->down_proj, layer->post_ln,
+    Q35_TRY(launch_mlp((uint32_t)kernels->num_cu, c, layer->gate_proj, layer->up_proj, layer->down_proj, layer->post_ln,
                        s->x_resid, s->x_norm2, s->mlp_act, s->gate_act, s->up_act, s->x_out,
                        nullptr, stream));
     *out = s->x_out;
@@ -643,7 +643,7 @@ q35_status q35_forward_linear_attention(const Qwen35Kernels* kernels,
         GemvSeg& sb = b.add(layer->in_proj_b, kEpiBeta);
         sb.out = s->beta;
         sb.tap0 = s->b_raw;
-        Q35_TRY(b.launch(stream, "in_proj GEMV"));
+        Q35_TRY(b.launch((uint32_t)kernels->num_cu, stream, "in_proj GEMV"));
     }
     // 2. L2 norm of q/k + gated delta rule
     {
@@ -675,10 +675,10 @@ q35_status q35_forward_linear_attention(const Qwen35Kernels* kernels,
         so.out = s->x_resid;
         (f32 ? so.pre4 : so.pre2) = x_in;
         so.tap0 = s->out;
-        Q35_TRY(b.launch(stream, "out_proj GEMV"));
+        Q35_TRY(b.launch((uint32_t)kernels->num_cu, stream, "out_proj GEMV"));
     }
     // 4-5. MLP; output residual stream straight into x_buf
-    Q35_TRY(launch_mlp(c, layer->gate_proj, layer->up_proj, layer->down_proj, layer->post_ln,
+    Q35_TRY(launch_mlp((uint32_t)kernels->num_cu, c, layer->gate_proj, layer->up_proj, layer->down_proj, layer->post_ln,
                        s->x_resid, s->x_norm2, s->mlp_act, s->gate_act, s->up_act, x_buf,
                        s->x_final, stream));
     if (dump) {
@@ -751,7 +751,7 @@ q35_status q35_lm_head_argmax(const Qwen35Kernels* kernels, const Qwen35ForwardC
     uint8_t* wsb = static_cast<uint8_t*>(workspace);
     b.a.am.part_val = reinterpret_cast<float*>(wsb + ws.val_off);
     b.a.am.part_idx = reinterpret_cast<int32_t*>(wsb + ws.idx_off);
-    Q35_TRY(b.launch(stream, "lm_head GEMV", ws.blocks));
+    Q35_TRY(b.launch((uint32_t)kernels->num_cu, stream, "lm_head GEMV", ws.blocks));
     LmFinishArgs f;
     std::memset(&f, 0, sizeof(f));
     f.part_val = b.a.am.part_val;
@@ -790,7 +790,7 @@ q35_status q35_gate_up_swiglu(const Qwen35Kernels* kernels, const Qwen35ForwardC
     b.a.pro.w = post_ln;
     b.a.pro.eps = c.rms_eps;
     b.add(*gate_proj, kEpiSwiGLU, up_proj).out = mlp_act;
-    Q35_TRY(b.launch(stream, "gate/up GEMV"));
+    Q35_TRY(b.launch((uint32_t)kernels->num_cu, stream, "gate/up GEMV"));
     return ok();
 }
 
@@ -810,7 +810,7 @@ q35_status q35_gemv(const Qwen35Kernels* kernels, const Q35QuantWeight* w, const
     b.a.pro.kind = kProLoadF32;
     b.a.pro.x = x;
     b.add(*w, kEpiStore).out = y;
-    Q35_TRY(b.launch(stream, "GEMV"));
+    Q35_TRY(b.launch((uint32_t)kernels->num_cu, stream, "GEMV"));
     return ok();
 }
 

@@ -10,7 +10,8 @@ namespace q35 {
 // ------------------------------------------------------------------ GEMV family
 
 constexpr int kMaxSegs = 4;
-constexpr int kGemvThreads = 256;  // threads per GEMV block
+constexpr int kGemvThreads = 256;       // threads per block of the streaming GEMVs (plain, lm_head)
+constexpr int kGemvLayerThreads = 640;  // threads per block of the per-layer GEMVs (one block per CU)
 
 enum : int32_t {
     kProRmsAct = 0,     // x = RMSNorm(x_act; w)          (x in the activation dtype)
@@ -99,10 +100,14 @@ enum : int32_t {
     X(12288)
 enum : int { kWidthHidden = 0, kWidthProj = 1, kWidthInter = 2, kWidthAny = 3 };
 
+constexpr int gemv_threads(int op) {
+    return (op == kOpPlain || op == kOpLmHead) ? kGemvThreads : kGemvLayerThreads;
+}
+
 bool gemv_width_supported(int role, uint32_t k);
 int gemv_rows_per_matrix_group(uint32_t k, bool paired);  // rows of each matrix per row group
 uint32_t gemv_row_groups_per_wave(uint32_t total_rg);
-uint32_t gemv_pick_blocks(uint32_t total_rg);
+uint32_t gemv_pick_blocks(uint32_t total_rg, int op, uint32_t num_cu);
 // half: the f16-product variant used for bf16 activations (else exact fp32 products)
 hipError_t gemv_launch(int op, uint32_t k, bool half, const GemvArgs& a, uint32_t blocks,
                        hipStream_t stream);
