@@ -23,17 +23,19 @@ int gemv_rows_per_matrix_group(uint32_t k, bool paired) {
     return 64 / gcd_i(64, (int)k / 16);
 }
 
-// Launch shape.  Streaming launches (plain, lm_head) that fit in the chip's
-// resident waves get about three waves per four row groups of 256-thread
-// blocks: every wave has its first row group in flight from the start and a
-// third of them stream a second one; long streams (the lm_head) use all
-// resident waves with many row groups each.  The per-layer GEMVs (a few to
-// 50 MB) run one 640-thread block per compute unit, each wave taking about two
-// row groups in turn: measured on MI355X against 864 blocks of 256 threads for
-// the 50 MB gate/up launch, 11.2 against 12.1 us per launch; every CU gets the
-// same share of the matrix and builds x once, and none waits behind a second
-// round of blocks.  (Two row groups in flight per wave need too many
-// registers for the paired gate/up; 16 waves per CU measured slower.)
+// Launch shape.  The streaming GEMVs (plain, lm_head) and the GDN
+// in-projection get about three waves per four row groups of 256-thread blocks
+// when they fit in the chip's resident waves: every wave has its first row
+// group in flight from the start and a third of them stream a second one;
+// long streams (the lm_head) use all resident waves with many row groups
+// each.  The other per-layer GEMVs run one 640-thread block per compute unit,
+// each wave taking about two row groups in turn.  Measured on MI355X inside
+// the 32-layer stack (us per launch, 256-thread shape -> per-CU shape):
+// gate/up 11.55 -> 10.5-10.8, out_proj 5.39 -> 4.66, o_proj 4.67 -> 4.43,
+// down and q/k/v unchanged, GDN in-projection 9.43 -> 10.43 (6176 row groups:
+// some waves run three in turn), so it keeps the 256-thread shape.  Row groups
+// stay contiguous within a block: interleaving them over the CUs balances the
+// rounds but measured slower for every GEMV (DRAM page and TLB locality).
 constexpr uint32_t kResidentWaves = 256u * 32u;
 
 uint32_t gemv_row_groups_per_wave(uint32_t total_rg) {

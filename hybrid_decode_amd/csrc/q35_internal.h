@@ -10,8 +10,8 @@ namespace q35 {
 // ------------------------------------------------------------------ GEMV family
 
 constexpr int kMaxSegs = 4;
-constexpr int kGemvThreads = 256;       // threads per block of the streaming GEMVs (plain, lm_head)
-constexpr int kGemvLayerThreads = 640;  // threads per block of the per-layer GEMVs (one block per CU)
+constexpr int kGemvThreads = 256;       // threads per block: streaming GEMVs, GDN in-projection
+constexpr int kGemvLayerThreads = 640;  // threads per block of the other per-layer GEMVs (one per CU)
 
 enum : int32_t {
     kProRmsAct = 0,     // x = RMSNorm(x_act; w)          (x in the activation dtype)
@@ -101,7 +101,7 @@ enum : int32_t {
 enum : int { kWidthHidden = 0, kWidthProj = 1, kWidthInter = 2, kWidthAny = 3 };
 
 constexpr int gemv_threads(int op) {
-    return (op == kOpPlain || op == kOpLmHead) ? kGemvThreads : kGemvLayerThreads;
+    return (op == kOpPlain || op == kOpLmHead || op == kOpInGdn) ? kGemvThreads : kGemvLayerThreads;
 }
 
 bool gemv_width_supported(int role, uint32_t k);
