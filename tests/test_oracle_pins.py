@@ -514,3 +514,105 @@ def test_generator_is_reproducible_and_independent_of_threads(gen):
     assert np.array_equal(x, y[:10])
     z = gen.normal_f32("pin.stats", (200_000,))
     assert abs(z.mean()) < 0.01 and abs(z.std() - 1) < 0.01
+
+
+# --------------------------------------------------------------------------- Turbo8 KV cache
+
+from oracle import turbo8 as T8  # noqa: E402
+
+
+@pytest.mark.parametrize("D", [16, 64, 256])
+def test_wht_matches_scipy_hadamard_and_is_an_involution(D):
+    import scipy.linalg
+    x = np.random.default_rng(D).standard_normal((3, D))
+    ref = x @ scipy.linalg.hadamard(D).T / math.sqrt(D)
+    assert np.allclose(T8.wht(x), ref, rtol=0, atol=1e-12)
+    assert np.allclose(T8.wht(T8.wht(x)), x, rtol=0, atol=1e-12)
+    e0 = np.zeros(D)
+    e0[0] = 1.0
+    assert np.allclose(T8.wht(e0), np.full(D, 1 / math.sqrt(D)), rtol=0, atol=1e-15)
+
+
+def test_e4m3_decode_matches_torch_float8_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = T8.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.nanmax(got) == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+
+
+def test_e4m3_encode_matches_torch_round_to_nearest_even():
+    rng = np.random.default_rng(7)
+    grid = T8.e4m3_decode(np.arange(0x7F, dtype=np.uint8))       # non-negative finite values
+    mids = (grid[:-1] + grid[1:]) / 2                                # exact ties (representable in fp32)
+    x = np.concatenate([rng.uniform(-448, 448, 4000), rng.uniform(-0.02, 0.02, 2000),
+                        mids, -mids, grid, -grid, [0.0, 2.0 ** -10, 3 * 2.0 ** -10]]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(T8.e4m3_encode(x), ref)
+
+
+def test_e4m3_encode_ties_and_saturation_closed_forms():
+    enc = T8.e4m3_encode
+    assert enc(np.float32(1.0 + 1 / 16)) == 0x38      # tie between 1.0 and 1.125 -> even mantissa
+    assert enc(np.float32(1.0 + 3 / 16)) == 0x3A      # tie between 1.125 and 1.25 -> 1.25
+    assert enc(np.float32(2.0 ** -10)) == 0x00        # half the smallest subnormal -> 0
+    assert enc(np.float32(3 * 2.0 ** -10)) == 0x02    # 1.5 steps -> 2 steps
+    assert enc(np.float32(500.0)) == 0x7E and enc(np.float32(-1e30)) == 0xFE
+    assert enc(np.float32(np.inf)) == 0x7E
+
+
+def test_turbo8_group_round_trip_and_error_bound():
+    rng = np.random.default_rng(11)
+    # a group on the grid: scale a power of two, largest magnitude 448 * scale
+    s = 2.0 ** -7
+    vals = T8.e4m3_decode(rng.integers(0, 0x7F, 16, dtype=np.uint8)) * s
+    vals[3] = 448.0 * s
+    codes, sc = T8.turbo8_quantize(vals[None])
+    assert O.bf16_to_f64(sc)[0, 0] == s
+    assert np.array_equal(T8.turbo8_dequantize(codes, sc)[0], vals)
+    # random groups: half an E4M3 step, relative to the value (normals) or to the scale (subnormals)
+    x = (rng.standard_normal((64, 256)) * np.exp(rng.uniform(-6, 6, (64, 1)))).astype(np.float32)
+    codes, sc = T8.turbo8_quantize(x)
+    xh = T8.turbo8_dequantize(codes, sc)
+    s_el = np.repeat(O.bf16_to_f64(sc), 16, axis=-1)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4 * 1.01, s_el * 2.0 ** -10)
+    assert np.all(np.abs(xh - x) <= bound)
+    # a zero group: scale 0, codes 0
+    z = np.zeros((1, 16), np.float32)
+    c0, s0 = T8.turbo8_quantize(z)
+    assert not c0.any() and not s0.any()
+
+
+def test_turbo8_attention_equals_sdpa_on_unrotated_dequantised_cache():
+    rng = np.random.default_rng(5)
+    Hq, Hkv, D, L = 8, 2, 64, 37
+    kc = rng.integers(0, 0x7F, (L + 3, Hkv, D), dtype=np.uint8) | (rng.integers(0, 2, (L + 3, Hkv, D), dtype=np.uint8) << 7)
+    vc = rng.integers(0, 0x7F, (L + 3, Hkv, D), dtype=np.uint8) | (rng.integers(0, 2, (L + 3, Hkv, D), dtype=np.uint8) << 7)
+    ks = O.f64_to_bf16(rng.uniform(1e-3, 4e-3, (L + 3, Hkv, D // 16)))
+    vs = O.f64_to_bf16(rng.uniform(1e-3, 4e-3, (L + 3, Hkv, D // 16)))
+    q = rng.standard_normal((Hq, D)) * 4
+    got = T8.attention_decode_turbo8(q, kc, ks, vc, vs, L)
+    K = torch.from_numpy(T8.wht(T8.turbo8_dequantize(kc[:L], ks[:L]))).permute(1, 0, 2)
+    V = torch.from_numpy(T8.wht(T8.turbo8_dequantize(vc[:L], vs[:L]))).permute(1, 0, 2)
+    K = K.repeat_interleave(Hq // Hkv, dim=0)
+    V = V.repeat_interleave(Hq // Hkv, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, None, :], K, V, scale=1 / math.sqrt(D))[:, 0, :].numpy()
+    assert np.allclose(got, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_turbo8_append_places_one_row_within_the_quantisation_bound():
+    rng = np.random.default_rng(9)
+    cap, Hkv, D = 6, 2, 64
+    kv = {"k": np.zeros((cap, Hkv, D), np.uint8), "v": np.zeros((cap, Hkv, D), np.uint8),
+          "k_scales": np.zeros((cap, Hkv, D // 16), np.uint16),
+          "v_scales": np.zeros((cap, Hkv, D // 16), np.uint16)}
+    k, v = rng.standard_normal((Hkv, D)), rng.standard_normal((Hkv, D))
+    out = T8.turbo8_append(kv, 4, k, v)
+    for name in kv:
+        changed = np.nonzero(np.any((out[name] != kv[name]).reshape(cap, -1), axis=1))[0].tolist()
+        assert changed == [4], name
+    back = T8.wht(T8.turbo8_dequantize(out["k"][4], out["k_scales"][4]))
+    assert np.linalg.norm(back - k) / np.linalg.norm(k) < 2.0 ** -4
