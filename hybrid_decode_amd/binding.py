@@ -27,6 +27,7 @@ Q35_ACT_F32 = 1
 KV_DTYPES = ["bf16", "turbo8", "turbo4", "turbo3", "turbo2", "bf16k_turbo4v", "bf16k_turbo3v",
              "bf16k_turbo2v"]
 Q35_KV_BF16 = 0
+Q35_KV_TURBO8 = 1
 
 # Every symbol include/q35decode.h declares.
 EXPORTS = [
@@ -37,7 +38,7 @@ EXPORTS = [
     "q35_lm_head_workspace_bytes", "q35_lm_head_argmax", "q35_gate_up_swiglu", "q35_gemv",
     "q35_decode_workspace_bytes", "q35_decode_plan_create", "q35_decode_plan_release",
     "q35_decode_step", "q35_decode_check", "q35_decode_layer_input", "q35_decode_stage_layout",
-    "q35_decode_stage_times",
+    "q35_decode_stage_times", "q35_turbo8_quantize", "q35_fp8_e4m3_table",
 ]
 
 Q35_LAYER_LINEAR = 0
@@ -179,6 +180,8 @@ def lib():
             "q35_decode_layer_input": (st, [vp, u32, P(vp)]),
             "q35_decode_stage_layout": (st, [vp, P(u32), P(u32)]),
             "q35_decode_stage_times": (st, [vp, P(C.c_uint64), u32, P(C.c_uint64)]),
+            "q35_turbo8_quantize": (st, [vp, vp, u32, vp, vp, vp]),
+            "q35_fp8_e4m3_table": (st, [vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -347,3 +350,11 @@ def q35_decode_stage_times(plan, n: int):
     _check(lib().q35_decode_stage_times(plan, ticks.ctypes.data_as(C.POINTER(C.c_uint64)), n,
                                         C.byref(hz)))
     return ticks, hz.value
+
+
+def q35_turbo8_quantize(kernels, x, n: int, codes, scales, stream) -> None:
+    _check(lib().q35_turbo8_quantize(kernels, x, n, codes, scales, stream))
+
+
+def q35_fp8_e4m3_table(kernels, out, stream) -> None:
+    _check(lib().q35_fp8_e4m3_table(kernels, out, stream))

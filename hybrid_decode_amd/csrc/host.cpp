@@ -223,10 +223,17 @@ q35_status check_full_layer(const Qwen35ForwardConfig& c, const FullAttentionLay
     return Q35_OK;
 }
 
-q35_status check_kv(const LayerKvCache& kv) {
-    if (kv.dtype != Q35_KV_BF16)
-        return fail(Q35_ERR_UNSUPPORTED, "KV dtype %u: only bf16 caches are implemented", kv.dtype);
-    if (kv.k_scales || kv.v_scales) return fail(Q35_ERR_INVALID_ARG, "bf16 cache with scale buffers");
+// bf16 everywhere; Turbo8 (E4M3 codes + bf16 scales per 16) in the per-layer forward.
+q35_status check_kv(const LayerKvCache& kv, bool allow_turbo8) {
+    if (kv.dtype == Q35_KV_TURBO8 && allow_turbo8) {
+        Q35_TRY(need(kv.k_scales, "kv.k_scales"));
+        Q35_TRY(need(kv.v_scales, "kv.v_scales"));
+    } else if (kv.dtype == Q35_KV_BF16) {
+        if (kv.k_scales || kv.v_scales) return fail(Q35_ERR_INVALID_ARG, "bf16 cache with scale buffers");
+    } else {
+        return fail(Q35_ERR_UNSUPPORTED, "KV dtype %u is not implemented on this path (%s)", kv.dtype,
+                    allow_turbo8 ? "bf16 | turbo8" : "bf16");
+    }
     Q35_TRY(need(kv.k, "kv.k"));
     Q35_TRY(need(kv.v, "kv.v"));
     if (kv.capacity == 0) return fail(Q35_ERR_OUT_OF_RANGE, "cache capacity is 0");
@@ -391,7 +398,8 @@ q35_status q35_kernels_resolve(int device, Qwen35Kernels** out) {
     }
     for (uint32_t dk : {32u, 64u, 128u}) probe(gdn_kernel_ptr(dk), "gated_delta_rule");
     for (uint32_t d : {64u, 128u, 256u})
-        for (uint32_t g : {1u, 2u, 4u, 8u}) probe(attn_kernel_ptr(d, g), "attention");
+        for (uint32_t g : {1u, 2u, 4u, 8u})
+            for (bool t8 : {false, true}) probe(attn_kernel_ptr(d, g, t8), "attention");
     probe(embed_kernel_ptr(), "embed");
     probe(lm_finish_kernel_ptr(), "lm_head argmax");
     for (uint32_t d : {64u, 128u, 256u})
@@ -468,7 +476,7 @@ static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35Fo
     if (!cfg || !layer || !s || !kv || !out) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
     Q35_TRY(q35_config_validate(cfg));
     const Qwen35ForwardConfig& c = *cfg;
-    Q35_TRY(check_kv(*kv));
+    Q35_TRY(check_kv(*kv, true));
     if (cache_pos >= 0) {
         if ((uint64_t)cache_pos >= kv->capacity)
             return fail(Q35_ERR_OUT_OF_RANGE, "cache_pos %lld >= capacity %u", (long long)cache_pos, kv->capacity);
@@ -525,6 +533,8 @@ static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35Fo
         a.positions = positions;
         a.kc = static_cast<uint16_t*>(kv->k);
         a.vc = static_cast<uint16_t*>(kv->v);
+        a.ks = static_cast<uint16_t*>(kv->k_scales);
+        a.vs = static_cast<uint16_t*>(kv->v_scales);
         a.gated_attn = s->gated_attn;
         a.attn_out = s->attn_out;
         a.q_norm_out = s->q_norm_out;
@@ -549,7 +559,7 @@ static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35Fo
             grid = (kv->capacity + a.chunk - 1) / a.chunk;
         }
         if (grid > a.max_chunks) return fail(Q35_ERR_INVALID_ARG, "internal: %u chunks > %u", grid, a.max_chunks);
-        Q35_HIP(attn_launch(c.head_dim, G, a, grid, stream), "attention");
+        Q35_HIP(attn_launch(c.head_dim, G, a, grid, kv->dtype == Q35_KV_TURBO8, stream), "attention");
         (void)G;
     }
     // 3. o projection + residual
@@ -794,6 +804,26 @@ q35_status q35_gate_up_swiglu(const Qwen35Kernels* kernels, const Qwen35ForwardC
     return ok();
 }
 
+q35_status q35_turbo8_quantize(const Qwen35Kernels* kernels, const float* x, uint32_t n,
+                               uint8_t* codes, uint16_t* scales, hipStream_t stream) {
+    Q35_TRY(check_kernels(kernels));
+    if (n % 16) return fail(Q35_ERR_INVALID_ARG, "n = %u is not a multiple of 16", n);
+    if (n == 0) return ok();
+    Q35_TRY(need(x, "x"));
+    Q35_TRY(need(codes, "codes"));
+    Q35_TRY(need(scales, "scales", false));
+    if (reinterpret_cast<uintptr_t>(scales) & 1u) return fail(Q35_ERR_INVALID_ARG, "scales not 2-byte aligned");
+    Q35_HIP(turbo8_quantize_launch(x, n, codes, scales, stream), "turbo8 quantise");
+    return ok();
+}
+
+q35_status q35_fp8_e4m3_table(const Qwen35Kernels* kernels, float* out, hipStream_t stream) {
+    Q35_TRY(check_kernels(kernels));
+    Q35_TRY(need(out, "out"));
+    Q35_HIP(e4m3_table_launch(out, stream), "e4m3 table");
+    return ok();
+}
+
 q35_status q35_gemv(const Qwen35Kernels* kernels, const Q35QuantWeight* w, const float* x,
                     float* y, uint32_t act_dtype, hipStream_t stream) {
     Q35_TRY(check_kernels(kernels));
@@ -881,7 +911,7 @@ q35_status plan_build(const Qwen35Kernels* k, const Qwen35ForwardConfig* cfg,
         } else if (L.kind == Q35_LAYER_FULL) {
             if (!L.full || !L.kv) return fail(Q35_ERR_INVALID_ARG, "layer %u: NULL weights/cache", l);
             Q35_TRY(check_full_layer(c, *L.full));
-            Q35_TRY(check_kv(*L.kv));
+            Q35_TRY(check_kv(*L.kv, false));
             any_full = true;
         } else {
             return fail(Q35_ERR_INVALID_ARG, "layer %u: kind %u", l, L.kind);

@@ -37,6 +37,59 @@ Q35_DEV void store_act(void* p, uint32_t i, float v, bool is_f32) {
         static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(f32_to_bf16(v));
 }
 
+// ------------------------------------------------------------------ FP8 E4M3 (OCP "fn")
+
+// fp32 -> E4M3 code: round to nearest-even, saturating to +-448 (the largest
+// finite magnitude; infinities and NaN saturate too).  Below the smallest
+// normal 2^-6 the step is 2^-9; a subnormal that rounds up to 8 steps lands on
+// the smallest normal, whose code follows on.  Normals round the fp32 mantissa
+// to three bits; a carry moves into the exponent field.
+Q35_DEV uint32_t e4m3_encode(float y) {
+    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+    const float a = fabsf(y);
+    uint32_t code;
+    if (!(a < 448.0f)) {
+        code = 0x7Eu;
+    } else if (a < 0.015625f) {
+        code = (uint32_t)rintf(a * 512.0f);
+    } else {
+        const uint32_t ab = __float_as_uint(a);
+        const uint32_t e = (ab >> 23) - 120u;  // exponent field: unbiased + 7
+        const uint32_t m = ab & 0x7FFFFFu;
+        const uint32_t r = (m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20;
+        code = (e << 3) + r;
+    }
+    return code | sign;
+}
+
+typedef float q35_float2_t __attribute__((ext_vector_type(2)));
+
+// Two E4M3 codes (bytes 0-1 of w, or 2-3 when HI) -> two fp32 values, exactly.
+template <bool HI>
+Q35_DEV q35_float2_t e4m3x2_to_f32(uint32_t w) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+
+// Turbo8 group of 16 rotated values: scale = bf16(amax / 448), codes = E4M3 of
+// x / scale (a zero group keeps scale 0 and codes 0).  codes[w] holds elements
+// 4w..4w+3, element i in byte i % 4.  Returns the scale's bf16 bits.
+Q35_DEV uint32_t turbo8_quantize16(const float v[16], uint32_t codes[4]) {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const uint32_t sb = f32_to_bf16(amax / 448.0f);
+    const float s = bf16_to_f32(sb);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            if (s != 0.0f) c |= e4m3_encode(v[4 * w + b] / s) << (8 * b);
+        codes[w] = c;
+    }
+    return sb;
+}
+
 // ------------------------------------------------------------------ activations
 
 Q35_DEV float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }

@@ -148,6 +148,8 @@ struct AttnArgs {
     float* k_norm_out;       // optional tap (post-RoPE)
     float* part_acc;         // workspace: [Hkv][max_chunks][G][D]
     float* part_ml;          // workspace: [Hkv][max_chunks][G][2]
+    uint16_t* ks;            // Turbo8 only: bf16 group scales [cap, Hkv, D/16] (kc/vc then hold E4M3 codes)
+    uint16_t* vs;
     uint32_t capacity;
     uint32_t hq, hkv, rotary;
     uint32_t chunk;          // positions per block
@@ -160,8 +162,12 @@ bool attn_dims_supported(uint32_t head_dim, uint32_t group);
 uint32_t attn_rows_per_iter(uint32_t head_dim);
 // Two launches: per-chunk partials, then the log-sum-exp merge with the sigmoid gate.
 hipError_t attn_launch(uint32_t head_dim, uint32_t group, const AttnArgs& a, uint32_t grid_chunks,
-                       hipStream_t stream);
-const void* attn_kernel_ptr(uint32_t head_dim, uint32_t group);
+                       bool turbo8, hipStream_t stream);
+const void* attn_kernel_ptr(uint32_t head_dim, uint32_t group, bool turbo8);
+// Turbo8 group quantiser and E4M3 decoder of the attention kernels, over plain buffers.
+hipError_t turbo8_quantize_launch(const float* x, uint32_t n, uint8_t* codes, uint16_t* scales,
+                                  hipStream_t stream);
+hipError_t e4m3_table_launch(float* out256, hipStream_t stream);
 const void* attn_combine_kernel_ptr(uint32_t head_dim, uint32_t group);
 
 // ------------------------------------------------------------------ misc

@@ -131,13 +131,29 @@ class GdnStateDev:
 
 
 class KvCacheDev:
+    """One layer's KV cache in device memory.  bf16: {"k", "v"} uint16 bits
+    [cap, Hkv, D]; Turbo8 (when "k_scales" is present): "k", "v" uint8 E4M3
+    codes [cap, Hkv, D] and "k_scales", "v_scales" bf16 bits [cap, Hkv, D/16]."""
+
     def __init__(self, kv: dict, device="cuda"):
+        self.turbo8 = "k_scales" in kv
         self.k = to_dev(kv["k"], device)
         self.v = to_dev(kv["v"], device)
         self.capacity = int(kv["k"].shape[0])
-        self.struct = B.LayerKvCache(ptr(self.k), ptr(self.v), self.capacity, B.Q35_KV_BF16, None, None)
+        if self.turbo8:
+            self.k_scales = to_dev(kv["k_scales"], device)
+            self.v_scales = to_dev(kv["v_scales"], device)
+            self.struct = B.LayerKvCache(ptr(self.k), ptr(self.v), self.capacity, B.Q35_KV_TURBO8,
+                                         ptr(self.k_scales), ptr(self.v_scales))
+        else:
+            self.struct = B.LayerKvCache(ptr(self.k), ptr(self.v), self.capacity, B.Q35_KV_BF16,
+                                         None, None)
 
     def to_host(self) -> dict:
+        if self.turbo8:
+            return {"k": self.k.cpu().numpy(), "v": self.v.cpu().numpy(),
+                    "k_scales": self.k_scales.cpu().numpy().view(np.uint16),
+                    "v_scales": self.v_scales.cpu().numpy().view(np.uint16)}
         return {"k": self.k.cpu().numpy().view(np.uint16), "v": self.v.cpu().numpy().view(np.uint16)}
 
 

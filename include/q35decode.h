@@ -141,7 +141,8 @@ typedef struct Q35QuantWeight {
 /* Parses a KV storage-format name as the pages' MetalKvDtype FromStr does
  * ("bf16", "turbo8", "turbo4", "turbo3", "turbo2", "bf16k_turbo4v",
  * "bf16k_turbo3v", "bf16k_turbo2v").  Unknown names: Q35_ERR_INVALID_ARG.
- * Only Q35_KV_BF16 is implemented by the forwards. */
+ * The per-layer full-attention forward implements Q35_KV_BF16 and
+ * Q35_KV_TURBO8; the persistent decode path implements Q35_KV_BF16. */
 q35_status q35_kv_dtype_from_str(const char* name, uint32_t* dtype);
 
 /*
@@ -155,10 +156,18 @@ q35_status q35_kv_cache_bytes(const Qwen35ForwardConfig* cfg, uint32_t dtype, ui
                               size_t* v_scale_bytes);
 
 /*
- * LayerKvCache (mod.rs page): k and v are bf16 [capacity, num_kv_heads, head_dim],
- * token-major, so row `cache_pos` is one contiguous kv_dim vector.  capacity
- * is in tokens and IS bounds-checked here.  k_scales / v_scales are unused for
- * bf16 and must be NULL.
+ * LayerKvCache (mod.rs page): token-major, so row `cache_pos` is one
+ * contiguous kv_dim vector; capacity is in tokens and IS bounds-checked here.
+ *   Q35_KV_BF16:   k, v bf16 [capacity, num_kv_heads, head_dim]; k_scales and
+ *                  v_scales NULL.
+ *   Q35_KV_TURBO8 (mod.rs: MetalKvDtype::Turbo8, the Turbo branch of
+ *                  full_attention.rs): k, v are FP8 E4M3 (OCP) codes, uint8
+ *                  [capacity, num_kv_heads, head_dim], of the head vectors
+ *                  after the orthonormal Walsh-Hadamard transform; k_scales,
+ *                  v_scales bf16 [capacity, num_kv_heads, head_dim / 16], one per
+ *                  16 consecutive elements: value = e4m3(code) * scale.  The
+ *                  append stores scale = bf16(amax / 448) and codes = E4M3 of
+ *                  x / scale, rounded to nearest-even, saturating.
  */
 typedef struct LayerKvCache {
     void* k;
@@ -239,7 +248,10 @@ q35_status q35_full_attention_workspace_bytes(const Qwen35ForwardConfig* cfg, ui
  *   inv_freq: fp32 [rotary_dim/2] (see q35_rope_inv_freq);
  *   positions: int32 [1], must hold cache_pos (RoPE reads it on the device);
  *   cache_pos < kv->capacity and seq_len_attn == cache_pos + 1, else
- *   Q35_ERR_OUT_OF_RANGE; kv->dtype != Q35_KV_BF16: Q35_ERR_UNSUPPORTED.
+ *   Q35_ERR_OUT_OF_RANGE; kv->dtype other than Q35_KV_BF16 or Q35_KV_TURBO8:
+ *   Q35_ERR_UNSUPPORTED.  With Turbo8 the query heads, the new key and value are
+ *   rotated before the quantising append and the attention output is rotated
+ *   back (exact attention over all rows; the pages' sparse-V gate is not applied).
  * x_in must not alias any scratch buffer.
  */
 q35_status q35_forward_full_attention(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
@@ -455,8 +467,8 @@ q35_status q35_decode_workspace_bytes(const Qwen35Kernels* kernels, const Qwen35
  * with a tail, writes the embedding of tokens[0] into the first layer's input.
  * The workspace must not be used by anything else while the plan lives.  *out
  * is a host object freed with q35_decode_plan_release.  Errors:
- * Q35_ERR_UNSUPPORTED (shape, or a device that cannot launch the grid
- * cooperatively), Q35_ERR_INVALID_ARG (as the per-layer calls; workspace too
+ * Q35_ERR_UNSUPPORTED (shape, a KV cache other than bf16, or a device that
+ * cannot launch the grid cooperatively), Q35_ERR_INVALID_ARG (as the per-layer calls; workspace too
  * small), Q35_ERR_HIP.
  */
 q35_status q35_decode_plan_create(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
@@ -510,6 +522,25 @@ q35_status q35_gate_up_swiglu(const Qwen35Kernels* kernels, const Qwen35ForwardC
                               const uint16_t* post_ln, const Q35QuantWeight* gate_proj,
                               const Q35QuantWeight* up_proj, const float* x_resid,
                               float* mlp_act, hipStream_t stream);
+
+/*
+ * The Turbo8 group quantiser of the full-attention append, over a plain device
+ * vector: for each group of 16 consecutive fp32 values of x [n] (n a multiple
+ * of 16), scales[g] = bf16(amax / 448) and codes[16g..16g+15] = E4M3 of
+ * x / scale (round to nearest-even, saturating; a zero group gets scale 0 and
+ * codes 0).  All device pointers, caller-owned: x fp32 [n] and codes uint8 [n]
+ * 16-byte aligned, scales bf16 [n / 16] 2-byte aligned.  n not a multiple of
+ * 16, a NULL or misaligned pointer: Q35_ERR_INVALID_ARG; n == 0 launches
+ * nothing.  Asynchronous on `stream`.
+ */
+q35_status q35_turbo8_quantize(const Qwen35Kernels* kernels, const float* x, uint32_t n,
+                               uint8_t* codes, uint16_t* scales, hipStream_t stream);
+
+/* The E4M3 decoder of the Turbo8 attention over every code: out fp32 [256]
+ * (device, caller-owned, 16-byte aligned), out[c] = value of code c; 0x7F and
+ * 0xFF decode to NaN.  NULL or misaligned out: Q35_ERR_INVALID_ARG.
+ * Asynchronous on `stream`. */
+q35_status q35_fp8_e4m3_table(const Qwen35Kernels* kernels, float* out, hipStream_t stream);
 
 /*
  * Plain GEMV with the library's quantised-weight kernel: y (fp32 [w->n]) =

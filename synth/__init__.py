@@ -267,3 +267,24 @@ def kv_cache(g: Gen, cfg: Config, prefix: str, capacity: int, filled: int) -> di
         k[:filled] = g.normal_bf16(prefix + ".k_prefill", (filled,) + shape[1:])
         v[:filled] = g.normal_bf16(prefix + ".v_prefill", (filled,) + shape[1:])
     return {"k": k, "v": v, "capacity": capacity}
+
+
+def kv_cache_turbo8(g: Gen, cfg: Config, prefix: str, capacity: int, filled: int) -> dict:
+    """Turbo8 caches: E4M3 codes uint8 [capacity, Hkv, D] and bf16 group scales
+    [capacity, Hkv, D/16].  Rows [0, filled) hold codes drawn uniformly from the
+    finite codes (0x00-0x7E and 0x80-0xFE, either sign) and scales bf16(U(1e-3,
+    1e-2)), so stored values span the whole E4M3 range, up to about 4.5; the
+    other rows are zero."""
+    Hkv, D = cfg.num_kv_heads, cfg.head_dim
+    shape = (capacity, Hkv, D)
+    out = {"k": np.zeros(shape, np.uint8), "v": np.zeros(shape, np.uint8),
+           "k_scales": np.zeros((capacity, Hkv, D // 16), np.uint16),
+           "v_scales": np.zeros((capacity, Hkv, D // 16), np.uint16), "capacity": capacity}
+    if filled:
+        for side in ("k", "v"):
+            u = g.uniform_f32(f"{prefix}.{side}_t8codes", (filled, Hkv, D), 0.0, 254.0)
+            c = np.minimum(np.floor(u), 253.0).astype(np.int64)   # 254 finite codes
+            out[side][:filled] = np.where(c < 127, c, c + 1).astype(np.uint8)
+            out[side + "_scales"][:filled] = g.uniform_bf16(f"{prefix}.{side}_t8scales",
+                                                            (filled, Hkv, D // 16), 1e-3, 1e-2)
+    return out

@@ -6,13 +6,17 @@
                       N(0, 0.1), conv state N(0, 1), 256 single-token steps;
 * ``full_layer_4b``   one full-attention layer at the 4B dims, bf16 KV cache with
                       rows [0, 4096) prefilled N(0, 1), 64 steps from position 4096;
+* ``full_layer_4b_turbo8``  the same layer over a Turbo8 cache whose rows
+                      [0, 4096) hold uniformly drawn finite E4M3 codes and bf16
+                      scales U(1e-3, 1e-2);
 * ``stack_4b``        the 4B-shaped stack (every 4th layer full attention), int8
                       lm_head over the 248 320-token vocabulary, bf16 embedding table
                       N(0, 1), zero GDN states, KV rows [0, ctx) prefilled N(0, 1).
 """
 from __future__ import annotations
 
-from . import Gen, gdn_layer, full_layer, gdn_state, kv_cache, layer_kinds, qwen3_5_4b, tiny
+from . import (Gen, gdn_layer, full_layer, gdn_state, kv_cache, kv_cache_turbo8, layer_kinds,
+               qwen3_5_4b, tiny)
 
 
 def tiny_stack(gen: Gen, steps: int = 16, capacity: int = 16):
@@ -38,6 +42,14 @@ def full_layer_4b(gen: Gen, steps: int = 64, prefill: int = 4096):
     layer = full_layer(gen, cfg, "c3.L")
     kv = kv_cache(gen, cfg, "c3.L", prefill + steps, prefill)
     xs = [gen.act(f"c3.x{t}", (cfg.hidden,), cfg.act_dtype) for t in range(steps)]
+    return {"cfg": cfg, "layer": layer, "kv": kv, "xs": xs, "start": prefill}
+
+
+def full_layer_4b_turbo8(gen: Gen, steps: int = 12, prefill: int = 4096):
+    cfg = qwen3_5_4b("bf16")
+    layer = full_layer(gen, cfg, "c3t8.L")
+    kv = kv_cache_turbo8(gen, cfg, "c3t8.L", prefill + steps, prefill)
+    xs = [gen.act(f"c3t8.x{t}", (cfg.hidden,), cfg.act_dtype) for t in range(steps)]
     return {"cfg": cfg, "layer": layer, "kv": kv, "xs": xs, "start": prefill}
 
 

@@ -157,11 +157,22 @@ def test_forward_errors_before_any_launch(lib):
             B.q35_forward_full_attention(FAKE_KERNELS, c, layer, scratch, kv, 0x100, 0x100, 0x100,
                                          pos, L, None)
         assert e.value.status == B.Q35_ERR_OUT_OF_RANGE, (pos, L)
-    # a turbo cache is parsed but not implemented
+    # Turbo8 needs both scale arrays; the other turbo formats are parsed but not implemented
     kv.dtype = B.q35_kv_dtype_from_str("turbo8")
     with pytest.raises(B.Q35Error) as e:
         B.q35_forward_full_attention(FAKE_KERNELS, c, layer, scratch, kv, 0x100, 0x100, 0x100, 3, 4, None)
-    assert e.value.status == B.Q35_ERR_UNSUPPORTED
+    assert e.value.status == B.Q35_ERR_INVALID_ARG and "k_scales" in str(e.value)
+    kv.k_scales = 0x100
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_forward_full_attention(FAKE_KERNELS, c, layer, scratch, kv, 0x100, 0x100, 0x100, 3, 4, None)
+    assert e.value.status == B.Q35_ERR_INVALID_ARG and "v_scales" in str(e.value)
+    kv.k_scales = None
+    for name in ("turbo4", "turbo3", "turbo2", "bf16k_turbo4v"):
+        kv.dtype = B.q35_kv_dtype_from_str(name)
+        with pytest.raises(B.Q35Error) as e:
+            B.q35_forward_full_attention(FAKE_KERNELS, c, layer, scratch, kv, 0x100, 0x100, 0x100, 3, 4,
+                                         None)
+        assert e.value.status == B.Q35_ERR_UNSUPPORTED, name
     # valid position but NULL weights
     kv.dtype = 0
     with pytest.raises(B.Q35Error) as e:
