@@ -6,7 +6,7 @@ attention over a bf16 KV cache at ~8192 tokens), final RMSNorm, int8 lm_head ove
 248 320 tokens, greedy argmax and the next token's embedding, all on the device
 from one replayed HIP graph.  Prints one JSON line (rank 0).
 
-    python bench.py [--gpus 1] [--steps 128] [--warmup 8]
+    python bench.py [--gpus 1] [--steps 128] [--warmup 8] [--ctx 8192] [--kv bf16|turbo8]
 """
 import argparse
 import hashlib
@@ -26,11 +26,12 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def stack_bytes_per_token(cfg, st, kinds, seq_len: int) -> int:
+def stack_bytes_per_token(cfg, st, kinds, seq_len: int, kv_bytes: float = 2.0) -> int:
     """Algorithmic HBM bytes of one token at attention length seq_len: every weight
     byte (codes, scales, biases) once, GDN and conv state read + write, conv
-    weights, KV rows [0, seq_len) read plus one row appended per full layer,
-    the lm_head, the embedding row, norm weights and the residual stream."""
+    weights, KV rows [0, seq_len) read plus one row appended per full layer
+    (kv_bytes per element: 2 for bf16, 1 + 2/16 for Turbo8), the lm_head, the
+    embedding row, norm weights and the residual stream."""
     b = st.weight_bytes
     H = cfg.hidden
     for li, kind in enumerate(kinds):
@@ -40,8 +41,8 @@ def stack_bytes_per_token(cfg, st, kinds, seq_len: int) -> int:
             b += 2 * cfg.qkv_total_lin * cfg.conv_kernel_size * 4
             b += cfg.qkv_total_lin * cfg.conv_kernel_size * 2
         else:
-            b += seq_len * cfg.kv_dim * 2 * 2                    # K and V rows read
-            b += cfg.kv_dim * 2 * 2                              # append
+            b += int(seq_len * cfg.kv_dim * 2 * kv_bytes)        # K and V rows read
+            b += int(cfg.kv_dim * 2 * kv_bytes)                  # append
     b += H * 2 * 2                                           # final norm + embedding row
     return b
 
@@ -112,7 +113,7 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(cfg, w, sample_note):
+def cpu_baseline(cfg, w, sample_note, kv="bf16"):
     import numpy as np
 
     import oracle as O
@@ -131,7 +132,12 @@ def cpu_baseline(cfg, w, sample_note):
     O.forward_linear_attention(cfg, w["layers"][gi], w["states"][gi], x)
     t_gdn = time.perf_counter() - t0
     t0 = time.perf_counter()
-    O.forward_full_attention(cfg, w["layers"][fi], w["kvs"][fi], inv, x, w["ctx"])
+    if kv == "turbo8":
+        from oracle import turbo8 as T8
+        kvd = {k: v for k, v in w["kvs"][fi].items() if k != "capacity"}
+        T8.forward_full_attention_turbo8(cfg, w["layers"][fi], kvd, inv, x, w["ctx"])
+    else:
+        O.forward_full_attention(cfg, w["layers"][fi], w["kvs"][fi], inv, x, w["ctx"])
     t_full = time.perf_counter() - t0
     t0 = time.perf_counter()
     logits = O.lm_head_logits(cfg, w["final_norm"], w["lm_head"], O.act_to_f64(x, "bf16"))
@@ -153,6 +159,8 @@ def main():
     ap.add_argument("--ctx", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dominant-rounds", type=int, default=4)
+    ap.add_argument("--kv", choices=["bf16", "turbo8"], default="bf16",
+                    help="KV cache format of the full-attention layers")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the decode path here is single-device "
@@ -177,7 +185,9 @@ def main():
     gen = synth.Gen(0)
     log(f"generating the {args.layers}-layer stack (ctx {args.ctx})")
     w = workloads.stack_4b(gen, num_layers=args.layers, ctx=args.ctx, extra=W + K + 64,
-                           progress=lambda i: log(f"  layer {i} generated") if i % 8 == 7 else None)
+                           progress=lambda i: log(f"  layer {i} generated") if i % 8 == 7 else None,
+                           kv=args.kv)
+    kv_bytes = 2.0 if args.kv == "bf16" else 1.0 + 2.0 / 16
     cfg, kinds = w["cfg"], w["kinds"]
     log(f"generated in {time.time() - t0:.1f}s; uploading")
     st = rt.DecodeStack(cfg, kinds, w["layers"], w["states"], w["kvs"], w["embed"],
@@ -204,7 +214,7 @@ def main():
     ms_per_step = ms / K
     tok_s = K / (ms / 1e3)
     L_mid = args.ctx + W + K // 2 + 1
-    bpt = stack_bytes_per_token(cfg, st, kinds, L_mid)
+    bpt = stack_bytes_per_token(cfg, st, kinds, L_mid, kv_bytes)
     hist = st.history.cpu().numpy()[:W + K]
     assert np.all(hist >= 0) and np.all(hist < cfg.vocab), "decode produced invalid tokens"
     log(f"{K} tokens in {ms:.2f} ms: {ms_per_step * 1e3:.1f} us/token, {tok_s:.1f} tok/s, "
@@ -261,6 +271,7 @@ def main():
     log(f"device copy of {copy_bytes >> 20} MiB: {copy_gbs:.0f} GB/s (read + write)")
     traffic = measured_traffic()
 
+    kv_desc = "bf16" if args.kv == "bf16" else "Turbo8 (WHT-rotated E4M3 + bf16 scale per 16)"
     result = {
         "metric": METRIC,
         "value": round(tok_s, 2),
@@ -277,11 +288,12 @@ def main():
         "config": {
             "workload": (f"Qwen3.5-4B-shaped {args.layers}-layer hybrid stack "
                          f"({kinds.count('gdn')} GDN + {kinds.count('full')} gated full attention), "
-                         f"int8 g64 weights, bf16 activations and KV cache, int8 lm_head over "
-                         f"{cfg.vocab}, greedy decode from cache position {args.ctx}"),
+                         f"int8 g64 weights, bf16 activations, {kv_desc} KV cache, int8 lm_head "
+                         f"over {cfg.vocab}, greedy decode from cache position {args.ctx}"),
             "layers": args.layers, "ctx_start": args.ctx, "hidden": cfg.hidden,
             "intermediate": cfg.intermediate, "vocab": cfg.vocab, "batch": 1,
-            "storage": "u8 codes + bf16 scale/bias per 64, bf16 activations/KV, fp32 GDN state",
+            "kv": args.kv,
+            "storage": f"u8 codes + bf16 scale/bias per 64, bf16 activations, {kv_desc} KV, fp32 GDN state",
             "launch": "one HIP graph per token",
         },
         "bytes_per_token": bpt,
@@ -299,9 +311,10 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         note = ("float64 oracle as it stands (dequantises each matrix per call): one GDN layer "
-                "{gdn:.2f}s, one full-attention layer at ctx 8192 {full:.2f}s, the lm_head + argmax "
-                "{lm:.2f}s, each run once; tok/s = 1/({ng} GDN + {nf} full + lm_head)")
-        result["cpu_baseline"] = cpu_baseline(cfg, w, note)
+                "{gdn:.2f}s, one full-attention layer at ctx " + str(args.ctx) + " ({kv}) {full:.2f}s, "
+                "the lm_head + argmax {lm:.2f}s, each run once; tok/s = 1/({ng} GDN + {nf} full + "
+                "lm_head)").replace("{kv}", args.kv)
+        result["cpu_baseline"] = cpu_baseline(cfg, w, note, args.kv)
         log(f"oracle: {result['cpu_baseline']['value']:.4f} tok/s")
     print(json.dumps(result), flush=True)
 

@@ -57,6 +57,130 @@ Q35_DEV int32_t attn_pos(const AttnArgs& a) {
     return a.host_pos >= 0 ? a.host_pos : a.positions[0];
 }
 
+// Row reductions.  A cache row spans LPR lanes; lane j of a row holds G
+// partial dot products, one per query head of the group.  Lane j keeps them in
+// its own order: slot p holds head p ^ hl(j), hl(j) = head_of_lane<G>(j).
+// The first log2(G) exchange steps each halve what a lane carries: it keeps
+// the lower half of its slots and adds the partner's upper half, which holds
+// the same heads (the partner differs in the one bit of hl that the step
+// retires).  Lane j ends with head hl(j) alone in slot 0 after about
+// G + log2(LPR) exchanges instead of G * log2(LPR), with no selects.
+//   bit 0, 1: quad permutations; bit 2: rotate a 16-lane row by 4 (a cache
+//   row fills whole 16-lane rows when LPR >= 16), else a swizzle of lane ^ 4;
+//   bit 3: rotate by 8; bit 4: swizzle of lane ^ 16.  A rotation pairs each
+//   lane with one whose bit differs and whose lower bits agree, and two of
+//   them cover the four quads of a row.
+template <int B, int LPR>
+Q35_DEV float row_partner(float v) {
+    if constexpr (B == 0) return dpp<0xB1>(v);        // quad_perm [1,0,3,2]
+    else if constexpr (B == 1) return dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    else if constexpr (B == 2 && LPR >= 16) return dpp<0x124>(v);  // row_ror:4
+    else if constexpr (B == 2)
+        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x101F));
+    else if constexpr (B == 3) return dpp<0x128>(v);  // row_ror:8
+    else return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+
+constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
+
+// Lane bit b (b < log2 G) carries head bit log2(G) - 1 - b.
+template <int G>
+Q35_DEV int head_of_lane(int j) {
+    int h = 0;
+#pragma unroll
+    for (int b = 0; b < ilog2c(G); ++b) h |= ((j >> b) & 1) << (ilog2c(G) - 1 - b);
+    return h;
+}
+
+template <int G, int LPR>
+Q35_DEV float row_reduce(float (&x)[G]) {
+    constexpr int LG = ilog2c(G), LL = ilog2c(LPR);
+    static_assert(LG <= LL && LL <= 5, "rows of G to 32 lanes");
+#pragma unroll
+    for (int i = 0; i < G / 2; ++i) x[i] += row_partner<0, LPR>(x[i + G / 2]);
+    if constexpr (G >= 4)
+#pragma unroll
+        for (int i = 0; i < G / 4; ++i) x[i] += row_partner<1, LPR>(x[i + G / 4]);
+    if constexpr (G >= 8) x[0] += row_partner<2, LPR>(x[1]);
+    float v = x[0];
+    if constexpr (LG <= 0 && LL > 0) v += row_partner<0, LPR>(v);
+    if constexpr (LG <= 1 && LL > 1) v += row_partner<1, LPR>(v);
+    if constexpr (LG <= 2 && LL > 2) v += row_partner<2, LPR>(v);
+    if constexpr (LL > 3) v += row_partner<3, LPR>(v);
+    if constexpr (LL > 4) v += row_partner<4, LPR>(v);
+    return v;
+}
+
+// For slot p: the value of the lane (in this lane's group of G lanes) whose
+// own head is this lane's head in slot p, i.e. lane q ^ rev(p).  Slot 0 is the
+// lane itself.
+template <int G>
+Q35_DEV float slot_bcast(float v, int p) {
+    if constexpr (G == 1) {
+        (void)p;
+        return v;
+    } else {
+        int r = 0;  // p with its log2(G) bits reversed
+#pragma unroll
+        for (int b = 0; b < ilog2c(G); ++b) r |= ((p >> b) & 1) << (ilog2c(G) - 1 - b);
+        if constexpr (G <= 4) {
+            switch (r) {  // quad_perm: lane q reads lane q ^ r
+                case 0: return v;
+                case 1: return dpp<0xB1>(v);   // [1,0,3,2]
+                case 2: return dpp<0x4E>(v);   // [2,3,0,1]
+                default: return dpp<0x1B>(v);  // [3,2,1,0]
+            }
+        } else {
+            return __shfl_xor(v, r);
+        }
+    }
+}
+
+// Value of lane (lane ^ LB) of the wave.
+template <int LB>
+Q35_DEV float lane_xor(float v) {
+    if constexpr (LB == 1) return dpp<0xB1>(v);       // quad_perm [1,0,3,2]
+    else if constexpr (LB == 2) return dpp<0x4E>(v);  // quad_perm [2,3,0,1]
+    else if constexpr (LB < 32)                       // swizzle, bitmask mode: xor LB
+        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x1F | (LB << 10)));
+    else return __shfl_xor(v, 32);
+}
+
+// Orthonormal Walsh-Hadamard transform of one D-vector held by a wave, lane l
+// holding elements [E l, E l + E), E = D / 64: butterflies of doubling width h
+// ((x_i, x_i+h) -> (x_i + x_i+h, x_i - x_i+h)), inside the lane while h < E,
+// then between lanes l and l ^ (h / E); 1/sqrt(D) applied in the last stage.
+template <int D>
+Q35_DEV void wht_regs(float (&x)[D / 64], int lane) {
+    constexpr int E = D / 64;
+    constexpr float f = D == 64 ? 0.125f : D == 256 ? 0.0625f : 0.08838834764831845f;
+#pragma unroll
+    for (int h = 1; h < E; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < E; ++i)
+            if ((i & h) == 0) {
+                const float u = x[i], w = x[i + h];
+                x[i] = u + w;
+                x[i + h] = u - w;
+            }
+    auto stage = [&](auto lbc) {
+        constexpr int LB = decltype(lbc)::value;
+        const bool hi = (lane & LB) != 0;
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            const float p = lane_xor<LB>(x[i]);
+            const float y = hi ? p - x[i] : x[i] + p;
+            x[i] = LB == 32 ? y * f : y;
+        }
+    };
+    stage(std::integral_constant<int, 1>{});
+    stage(std::integral_constant<int, 2>{});
+    stage(std::integral_constant<int, 4>{});
+    stage(std::integral_constant<int, 8>{});
+    stage(std::integral_constant<int, 16>{});
+    stage(std::integral_constant<int, 32>{});
+}
+
 // T8: Turbo8 cache (E4M3 codes [capacity, Hkv, D] with bf16 scales per 16
 // [capacity, Hkv, D/16], in the orthonormal Walsh-Hadamard basis of a head).
 // The prologue also rotates the G query heads and the new k and v, the block
@@ -81,9 +205,8 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     __shared__ float rsq[G + 1];
     __shared__ float2 rot[D / 2];      // (cos, sin) of pos * inv_freq[d], d < rotary / 2
     __shared__ float mls[RPI][2 * G];  // per-slot (max, sum)
-    __shared__ float red[RPI * D];     // per-slot outputs of one head
+    __shared__ float red[(G < 4 ? G : 4) * RPI * D];  // per-slot outputs of up to 4 heads
     __shared__ float ov[T8 ? G * D : 1];  // Turbo8: merged accumulators, rotated back in place
-    constexpr float kInvSqrtD = D == 64 ? 0.125f : D == 256 ? 0.0625f : 0.08838834764831845f;
 
     const int32_t pos = attn_pos(a);
     if (pos < 0 || (uint32_t)pos >= a.capacity) return;
@@ -124,7 +247,9 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     const size_t srow0 = ((size_t)t0 * a.hkv + g) * (D / 16);
     const auto rks = rsrc(a.ks + (T8 ? srow0 : 0), sspan);
     const auto rvs = rsrc(a.vs + (T8 ? srow0 : 0), sspan);
-    // two batches in flight: the next batch's rows load while this one computes
+    // two batches in flight: the next batch's rows load while this one
+    // computes (three, or smaller batches at higher occupancy, measured no
+    // faster)
     using KT = std::conditional_t<T8, uint2, uint4>;  // 8 elements of one row per lane
     KT kr[2][kUnroll], vr[2][kUnroll];
     uint32_t ksr[2][kUnroll], vsr[2][kUnroll];  // Turbo8: the lane's group scale (bf16 bits)
@@ -193,20 +318,17 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
             for (int d = t; d < D; d += kNT) a.k_norm_out[g * D + d] = qs[G * D + d];
         __syncthreads();  // the taps read qs before the rotation rewrites it
         // orthonormal Walsh-Hadamard transform of the G query heads, the new k and
-        // the new v: butterflies of doubling width, 1/sqrt(D) in the last stage
-        auto vec = [&](int vi) { return vi <= G ? qs + vi * D : vn; };
-        for (int h = 1; h < D; h <<= 1) {
-            const float f = 2 * h == D ? kInvSqrtD : 1.0f;
-            for (int e = t; e < (G + 2) * (D / 2); e += kNT) {
-                const int vi = e / (D / 2), p = e % (D / 2);
-                const int i = (p / h) * 2 * h + p % h;
-                float* x = vec(vi);
-                const float u = x[i], w = x[i + h];
-                x[i] = (u + w) * f;
-                x[i + h] = (u - w) * f;
-            }
-            __syncthreads();
+        // the new v, one vector per wave
+        for (int vi = wid; vi < G + 2; vi += kNT / 64) {
+            float* xv = vi <= G ? qs + vi * D : vn;
+            float x[D / 64];
+#pragma unroll
+            for (int i = 0; i < D / 64; ++i) x[i] = xv[lane * (D / 64) + i];
+            wht_regs<D>(x, lane);
+#pragma unroll
+            for (int i = 0; i < D / 64; ++i) xv[lane * (D / 64) + i] = x[i];
         }
+        __syncthreads();
         if (has_new) {
             // quantising append: one thread per group of 16 of the rotated k or v;
             // the block then attends to the dequantised row, as stored
@@ -248,93 +370,150 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     }
 
     // ---------------- batches of B rows: scores, online softmax, p V
-    float qr[G][8];
+    // Rows at `pos` are left out here (their loads read zero and their scores
+    // are masked) and attended after the loop from LDS, as stored.
+    // Lane slots: slot p is head p ^ hl (see row_reduce); after the reduction
+    // the lane holds head hl's score, and m, l are that head's running max and
+    // sum for the lane's row slot.
+    const int hl = head_of_lane<G>(j);
+    // bf16 keys: q as a bf16 pair (hi + lo, 16 significant bits) for the
+    // two-element bf16 dot instruction, so the keys need no unpacking
+    using Q2 = std::conditional_t<T8, float, uint32_t>;
+    constexpr int QN = T8 ? 8 : 4;
+    Q2 qh[G][QN], ql[G][T8 ? 1 : 4];
+#pragma unroll
+    for (int p = 0; p < G; ++p) {
+        const float* qp = qs + (p ^ hl) * D + 8 * j;
+        if constexpr (T8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qh[p][e] = qp[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x0 = qp[2 * e], x1 = qp[2 * e + 1];
+                const uint32_t h0 = f32_to_bf16(x0), h1 = f32_to_bf16(x1);
+                const uint32_t l0 = f32_to_bf16(x0 - bf16_to_f32(h0)), l1 = f32_to_bf16(x1 - bf16_to_f32(h1));
+                qh[p][e] = h0 | (h1 << 16);
+                ql[p][e] = l0 | (l1 << 16);
+            }
+        }
+    }
+    const float sscale = a.scale * kLog2e;  // scores in the base-2 exponent domain
+
+    float m = -INFINITY, l = 0.f, acc[G][8];
 #pragma unroll
     for (int i = 0; i < G; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qr[i][e] = qs[i * D + 8 * j + e];
-    const float sscale = a.scale * kLog2e;  // scores in the base-2 exponent domain
-
-    float m[G], l[G], acc[G][8];
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-        m[i] = -INFINITY;
-        l[i] = 0.f;
-#pragma unroll
         for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
-    }
 
-    // 8 elements of a row: bf16 pairs, or Turbo8 codes times the group scale
-    auto unpack = [&](const KT& w, uint32_t sbits, float v[8]) {
+    // 8 elements of a row: bf16 pairs, or Turbo8 codes (the group scale is
+    // applied to the partial dot products and to the weights instead)
+    auto unpack = [&](const KT& w, float v[8]) {
         if constexpr (T8) {
-            const float sc = bf16_to_f32(sbits & 0xFFFFu);
             const q35_float2_t p0 = e4m3x2_to_f32<false>(w.x), p1 = e4m3x2_to_f32<true>(w.x);
             const q35_float2_t p2 = e4m3x2_to_f32<false>(w.y), p3 = e4m3x2_to_f32<true>(w.y);
-            v[0] = p0.x * sc;
-            v[1] = p0.y * sc;
-            v[2] = p1.x * sc;
-            v[3] = p1.y * sc;
-            v[4] = p2.x * sc;
-            v[5] = p2.y * sc;
-            v[6] = p3.x * sc;
-            v[7] = p3.y * sc;
+            v[0] = p0.x;
+            v[1] = p0.y;
+            v[2] = p1.x;
+            v[3] = p1.y;
+            v[4] = p2.x;
+            v[5] = p2.y;
+            v[6] = p3.x;
+            v[7] = p3.y;
         } else {
-            (void)sbits;
             unpack8(w, v);
+        }
+    };
+    // one row's score for head hl from the lane's 8 key elements
+    auto score = [&](const KT& w, float kscale) {
+        float d[G];
+        if constexpr (T8) {
+            float kv[8];
+            unpack(w, kv);
+#pragma unroll
+            for (int p = 0; p < G; ++p) {
+                float x = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x = fmaf(qh[p][e], kv[e], x);
+                d[p] = x * kscale;
+            }
+        } else {
+            (void)kscale;
+            const uint32_t kw[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int p = 0; p < G; ++p) {
+                float x = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x = bf16_dot2(qh[p][e], kw[e], x);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x = bf16_dot2(ql[p][e], kw[e], x);
+                d[p] = x;
+            }
+        }
+        return row_reduce<G, LPR>(d) * sscale;
+    };
+    // the appended row (fp32 values in LDS)
+    auto score_f32 = [&](const float kv[8]) {
+        float d[G];
+#pragma unroll
+        for (int p = 0; p < G; ++p) {
+            const float* qp = qs + (p ^ hl) * D + 8 * j;
+            float x = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x = fmaf(qp[e], kv[e], x);
+            d[p] = x;
+        }
+        return row_reduce<G, LPR>(d) * sscale;
+    };
+    // Online-softmax rescale towards the new max mx of head hl.  It runs only
+    // when some lane's max grows by more than 8 (base 2; weights stay below
+    // 2^8, the result is the same up to rounding), and then in every lane of
+    // the wave: lanes of one head sum the same values in different orders, so
+    // their maxima can differ in the last bit, and a per-lane decision could
+    // leave two of them 2^8 apart.
+    auto rescale_to = [&](float mx) {
+        if (__builtin_amdgcn_ballot_w64(mx > m + 8.0f) != 0) {
+            const float mn = fmaxf(m, mx);
+            const float corr = mn == -INFINITY ? 1.0f : exp2f(m - mn);
+            m = mn;
+            l *= corr;
+#pragma unroll
+            for (int p = 0; p < G; ++p) {
+                const float cp = slot_bcast<G>(corr, p);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[p][e] *= cp;
+            }
+        }
+    };
+    auto accumulate = [&](float pw, const float vv[8], float vscale) {
+        l += pw;
+#pragma unroll
+        for (int p = 0; p < G; ++p) {
+            float pp = slot_bcast<G>(pw, p);
+            if constexpr (T8) pp *= vscale;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[p][e] = fmaf(pp, vv[e], acc[p][e]);
         }
     };
     auto batch = [&](const KT (&kd)[kUnroll], const KT (&vd)[kUnroll], const uint32_t (&ksd)[kUnroll],
                      const uint32_t (&vsd)[kUnroll], uint32_t tb) {
-        float s[kUnroll][G];
+        float s[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const uint32_t tt = tb + u * RPI + rs;
-            float kv[8];
-            if (tt == (uint32_t)pos) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) kv[e] = qs[G * D + 8 * j + e];
-            } else {
-                unpack(kd[u], ksd[u], kv);
-            }
-#pragma unroll
-            for (int i = 0; i < G; ++i) {
-                float d = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) d = fmaf(qr[i][e], kv[e], d);
-                d = group_sum_all<LPR>(d);
-                s[u][i] = tt < t1 ? d * sscale : -INFINITY;
-            }
+            const float r = score(kd[u], T8 ? bf16_to_f32(ksd[u] & 0xFFFFu) : 1.0f);
+            s[u] = (tt < t1 && tt != (uint32_t)pos) ? r : -INFINITY;
         }
+        float mx = m;
 #pragma unroll
-        for (int i = 0; i < G; ++i) {
-            float mx = m[i];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) mx = fmaxf(mx, s[u][i]);
-            const float mref = mx == -INFINITY ? 0.f : mx;  // slot with no rows yet
-            const float corr = exp2f(m[i] - mref);
-            m[i] = mx;
-            l[i] *= corr;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[i][e] *= corr;
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) s[u][i] = exp2f(s[u][i] - mref);
-        }
+        for (int u = 0; u < kUnroll; ++u) mx = fmaxf(mx, s[u]);
+        rescale_to(mx);
+        const float mref = m == -INFINITY ? 0.f : m;  // slot with no rows yet
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t tt = tb + u * RPI + rs;
             float vv[8];
-            if (tt == (uint32_t)pos) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vv[e] = vn[8 * j + e];
-            } else {
-                unpack(vd[u], vsd[u], vv);
-            }
-#pragma unroll
-            for (int i = 0; i < G; ++i) {
-                l[i] += s[u][i];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(s[u][i], vv[e], acc[i][e]);
-            }
+            unpack(vd[u], vv);
+            accumulate(exp2f(s[u] - mref), vv, T8 ? bf16_to_f32(vsd[u] & 0xFFFFu) : 1.0f);
         }
     };
     // Reloads are unconditional (rows past the chunk read zero and move no
@@ -348,58 +527,78 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
         if (tb + 2 * B >= t1) break;
         load_batch(kr[1], vr[1], ksr[1], vsr[1], tb + 3 * B);
     }
+    if (has_new) {
+        // the appended row, as stored (dequantised for Turbo8), in row slot 0
+        float kv[8], vv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kv[e] = qs[G * D + 8 * j + e];
+            vv[e] = vn[8 * j + e];
+        }
+        const float r = score_f32(kv);
+        const float sn = rs == 0 ? r : -INFINITY;
+        rescale_to(fmaxf(m, sn));
+        const float mref = m == -INFINITY ? 0.f : m;
+        accumulate(exp2f(sn - mref), vv, 1.0f);
+    }
 
     // ---------------- merge the row slots, write this chunk's partials
-    if (j == 0)
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            mls[rs][2 * i] = m[i];
-            mls[rs][2 * i + 1] = l[i];
-        }
+    if (j < G) {  // one lane per head in each row slot
+        mls[rs][2 * hl] = m;
+        mls[rs][2 * hl + 1] = l;
+    }
     __syncthreads();
     float* pacc = a.part_acc + ((size_t)g * a.max_chunks + c) * G * D;
+    float* pml = a.part_ml + ((size_t)g * a.max_chunks + c) * 2 * G;
+    if (t < G) {
+        float M = -INFINITY, tot = 0.f;
+        for (int r = 0; r < RPI; ++r) M = fmaxf(M, mls[r][2 * t]);  // slot 0 always has a row
+        for (int r = 0; r < RPI; ++r) tot = fmaf(exp2f(mls[r][2 * t] - M), mls[r][2 * t + 1], tot);
+        pml[2 * t] = M;
+        pml[2 * t + 1] = tot;
+    }
+    // heads in rounds of HM: each slot writes its weighted accumulators, then
+    // every thread sums the slots for HM * D / 256 outputs
+    constexpr int HM = G < 4 ? G : 4;
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-        float M = -INFINITY;
-        for (int r = 0; r < RPI; ++r) M = fmaxf(M, mls[r][2 * i]);  // slot 0 always has a row
-        const float w = exp2f(m[i] - M);
+    for (int h0 = 0; h0 < G; h0 += HM) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) red[rs * D + 8 * j + e] = acc[i][e] * w;
+        for (int p = 0; p < G; ++p) {
+            const int h = p ^ hl;
+            if (h >= h0 && h < h0 + HM) {
+                float M = -INFINITY;
+                for (int r = 0; r < RPI; ++r) M = fmaxf(M, mls[r][2 * h]);
+                const float w = exp2f(mls[rs][2 * h] - M);
+                float* dst = red + ((h - h0) * RPI + rs) * D + 8 * j;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dst[e] = acc[p][e] * w;
+            }
+        }
         __syncthreads();
-        for (int d = t; d < D; d += kNT) {
+        for (int e = t; e < HM * D; e += kNT) {
+            const int hh = e / D, d = e % D;
             float o = 0.f;
 #pragma unroll 8
-            for (int r = 0; r < RPI; ++r) o += red[r * D + d];
+            for (int r = 0; r < RPI; ++r) o += red[(hh * RPI + r) * D + d];
             if constexpr (T8)
-                ov[i * D + d] = o;
+                ov[(h0 + hh) * D + d] = o;
             else
-                pacc[i * D + d] = o;
-        }
-        if (t == 0) {
-            float tot = 0.f;
-            for (int r = 0; r < RPI; ++r) tot = fmaf(exp2f(mls[r][2 * i] - M), mls[r][2 * i + 1], tot);
-            float* pml = a.part_ml + ((size_t)g * a.max_chunks + c) * 2 * G;
-            pml[2 * i] = M;
-            pml[2 * i + 1] = tot;
+                pacc[(h0 + hh) * D + d] = o;
         }
         __syncthreads();
     }
     if constexpr (T8) {
         // each head's merged accumulator back to the original basis (the
-        // orthonormal transform is its own inverse; the merge is linear)
-        for (int h = 1; h < D; h <<= 1) {
-            const float f = 2 * h == D ? kInvSqrtD : 1.0f;
-            for (int e = t; e < G * (D / 2); e += kNT) {
-                const int vi = e / (D / 2), p = e % (D / 2);
-                const int i = (p / h) * 2 * h + p % h;
-                float* x = ov + vi * D;
-                const float u = x[i], w = x[i + h];
-                x[i] = (u + w) * f;
-                x[i + h] = (u - w) * f;
-            }
-            __syncthreads();
+        // orthonormal transform is its own inverse; the merge is linear), one
+        // head per wave
+        for (int vi = wid; vi < G; vi += kNT / 64) {
+            float x[D / 64];
+#pragma unroll
+            for (int i = 0; i < D / 64; ++i) x[i] = ov[vi * D + lane * (D / 64) + i];
+            wht_regs<D>(x, lane);
+#pragma unroll
+            for (int i = 0; i < D / 64; ++i) pacc[vi * D + lane * (D / 64) + i] = x[i];
         }
-        for (int e = t; e < G * D; e += kNT) pacc[e] = ov[e];
     }
 }
 

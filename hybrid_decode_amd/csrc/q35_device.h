@@ -37,6 +37,14 @@ Q35_DEV void store_act(void* p, uint32_t i, float v, bool is_f32) {
         static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(f32_to_bf16(v));
 }
 
+typedef __bf16 q35_bf16x2_t __attribute__((ext_vector_type(2)));
+
+// a.lo * b.lo + a.hi * b.hi + c over two bf16 pairs (exact products, fp32 sum).
+Q35_DEV float bf16_dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(q35_bf16x2_t, a),
+                                           __builtin_bit_cast(q35_bf16x2_t, b), c, false);
+}
+
 // ------------------------------------------------------------------ FP8 E4M3 (OCP "fn")
 
 // fp32 -> E4M3 code: round to nearest-even, saturating to +-448 (the largest

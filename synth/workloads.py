@@ -11,7 +11,8 @@
                       scales U(1e-3, 1e-2);
 * ``stack_4b``        the 4B-shaped stack (every 4th layer full attention), int8
                       lm_head over the 248 320-token vocabulary, bf16 embedding table
-                      N(0, 1), zero GDN states, KV rows [0, ctx) prefilled N(0, 1).
+                      N(0, 1), zero GDN states, KV rows [0, ctx) prefilled N(0, 1)
+                      (bf16) or with uniformly drawn codes and scales (Turbo8).
 """
 from __future__ import annotations
 
@@ -53,8 +54,11 @@ def full_layer_4b_turbo8(gen: Gen, steps: int = 12, prefill: int = 4096):
     return {"cfg": cfg, "layer": layer, "kv": kv, "xs": xs, "start": prefill}
 
 
-def stack_4b(gen: Gen, num_layers: int = 32, ctx: int = 8192, extra: int = 256, progress=None):
-    """The 4B-shaped stack.  ``capacity = ctx + extra`` tokens per KV cache."""
+def stack_4b(gen: Gen, num_layers: int = 32, ctx: int = 8192, extra: int = 256, progress=None,
+             kv: str = "bf16"):
+    """The 4B-shaped stack.  ``capacity = ctx + extra`` tokens per KV cache; ``kv``
+    "bf16" (rows N(0, 1)) or "turbo8" (rows of uniformly drawn finite E4M3 codes
+    and bf16 scales U(1e-3, 1e-2))."""
     cfg = qwen3_5_4b("bf16")
     kinds = layer_kinds(num_layers)
     layers, states, kvs = [], [], []
@@ -66,7 +70,8 @@ def stack_4b(gen: Gen, num_layers: int = 32, ctx: int = 8192, extra: int = 256, 
         else:
             layers.append(full_layer(gen, cfg, f"c4.L{i}"))
             states.append(None)
-            kvs.append(kv_cache(gen, cfg, f"c4.L{i}", ctx + extra, ctx))
+            make = kv_cache_turbo8 if kv == "turbo8" else kv_cache
+            kvs.append(make(gen, cfg, f"c4.L{i}", ctx + extra, ctx))
         if progress:
             progress(i)
     embed = gen.normal_bf16("c4.embed", (cfg.vocab, cfg.hidden))
