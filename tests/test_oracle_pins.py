@@ -616,3 +616,105 @@ def test_turbo8_append_places_one_row_within_the_quantisation_bound():
         assert changed == [4], name
     back = T8.wht(T8.turbo8_dequantize(out["k"][4], out["k_scales"][4]))
     assert np.linalg.norm(back - k) / np.linalg.norm(k) < 2.0 ** -4
+
+
+# --------------------------------------------------------------------------- Turbo4V KV cache (bf16 K)
+
+from oracle import turbo4v as T4  # noqa: E402
+
+
+def test_lloyd_max_codebook_meets_lloyds_conditions_by_quadrature():
+    from scipy import integrate, stats
+    c = T4.lloyd_max_normal()
+    assert c.shape == (16,) and np.all(np.diff(c) > 0)
+    assert np.array_equal(c, -c[::-1])
+    t = [-np.inf, *((c[:-1] + c[1:]) / 2), np.inf]
+    for i in range(16):
+        mass = stats.norm.cdf(t[i + 1]) - stats.norm.cdf(t[i]) if t[i] < 0 else \
+            stats.norm.sf(t[i]) - stats.norm.sf(t[i + 1])
+        first = integrate.quad(lambda x: x * stats.norm.pdf(x), t[i], t[i + 1], epsabs=1e-14)[0]
+        assert abs(first / mass - c[i]) < 1e-9, i      # each level is the mean of its cell
+
+
+def test_lloyd_max_codebook_agrees_with_kmeans_on_gaussian_samples():
+    rng = np.random.default_rng(123)
+    x = np.sort(rng.standard_normal(1 << 20))
+    lv = np.quantile(x, (np.arange(16) + 0.5) / 16)
+    for _ in range(200):                               # 1-D k-means on the samples
+        t = (lv[:-1] + lv[1:]) / 2
+        cell = np.searchsorted(t, x)
+        lv = np.array([x[cell == i].mean() for i in range(16)])
+    assert np.max(np.abs(lv - T4.lloyd_max_normal())) < 0.02
+    # and the distortion is the smallest among nearby codebooks (a minimum)
+    def mse(levels):
+        t = (levels[:-1] + levels[1:]) / 2
+        return np.mean((x - levels[np.searchsorted(t, x)]) ** 2)
+    base = mse(T4.lloyd_max_normal())
+    for k in range(8):
+        bumped = T4.lloyd_max_normal().copy()
+        bumped[k] += 0.05
+        bumped[15 - k] -= 0.05
+        assert mse(bumped) > base
+
+
+def test_turbo4_packing_low_nibble_first():
+    idx = np.arange(16) % 16
+    packed = (idx[0::2] | (idx[1::2] << 4)).astype(np.uint8)
+    assert np.array_equal(T4.turbo4_unpack(packed), idx)
+    assert packed[0] == 0x10 and packed[7] == 0xFE
+
+
+def test_turbo4_indices_are_nearest_levels_and_the_norm_is_kept():
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((200, 64)) * np.exp(rng.uniform(-4, 4, (200, 1)))).astype(np.float32)
+    packed, sc = T4.turbo4_quantize(x)
+    idx = T4.turbo4_unpack(packed).reshape(200, 4, 16)
+    g = x.reshape(200, 4, 16).astype(np.float64)
+    lv = T4.codebook_f32().astype(np.float64)
+    rms = np.sqrt(np.mean(g ** 2, axis=-1, keepdims=True))
+    brute = np.argmin(np.abs((g / rms)[..., None] - lv), axis=-1)
+    assert np.mean(brute == idx) > 0.999             # ties and fp32-vs-fp64 edges aside
+    assert np.all(np.abs(brute - idx) <= 1)
+    # the scale is the norm ratio itself, up to its E4M3 rounding (half a step:
+    # 2^-4 relative for normals, 2^-10 absolute below 2^-6), so the norm is kept
+    # to that same error
+    s = np.linalg.norm(g, axis=-1) / np.linalg.norm(lv[idx], axis=-1)
+    err = np.maximum(s * 2.0 ** -4, 2.0 ** -10) * 1.001
+    assert np.all(np.abs(T8.e4m3_decode(sc) - s) <= err)
+    xh = T4.turbo4_dequantize(packed, sc).reshape(200, 4, 16)
+    ratio = np.linalg.norm(xh, axis=-1) / np.linalg.norm(g, axis=-1)
+    assert np.all(np.abs(ratio - 1) <= err / s)
+    z = np.zeros((1, 16), np.float32)
+    p0, s0 = T4.turbo4_quantize(z)
+    assert not p0.any() and not s0.any()
+
+
+def test_turbo4v_attention_equals_sdpa_on_dequantised_values():
+    rng = np.random.default_rng(6)
+    Hq, Hkv, D, L = 8, 2, 64, 29
+    kc = O.f64_to_bf16(rng.standard_normal((L + 2, Hkv, D)))
+    vc = rng.integers(0, 256, (L + 2, Hkv, D // 2), dtype=np.uint8)
+    vs = T8.e4m3_encode(rng.uniform(0.05, 2.0, (L + 2, Hkv, D // 16)).astype(np.float32))
+    q = rng.standard_normal((Hq, D)) * 3
+    got = T4.attention_decode_bf16k_turbo4v(q, kc, vc, vs, L)
+    K = torch.from_numpy(O.bf16_to_f64(kc[:L])).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+    V = torch.from_numpy(T8.wht(T4.turbo4_dequantize(vc[:L], vs[:L]))).permute(1, 0, 2)
+    V = V.repeat_interleave(Hq // Hkv, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, None, :], K, V, scale=1 / math.sqrt(D))[:, 0, :].numpy()
+    assert np.allclose(got, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_bf16k_turbo4v_append_places_one_row():
+    rng = np.random.default_rng(8)
+    cap, Hkv, D = 5, 2, 64
+    kv = {"k": np.zeros((cap, Hkv, D), np.uint16), "v": np.zeros((cap, Hkv, D // 2), np.uint8),
+          "v_scales": np.zeros((cap, Hkv, D // 16), np.uint8)}
+    k, v = rng.standard_normal((Hkv, D)), rng.standard_normal((Hkv, D))
+    out = T4.bf16k_turbo4v_append(kv, 3, k, v)
+    for name in kv:
+        changed = np.nonzero(np.any((out[name] != kv[name]).reshape(cap, -1), axis=1))[0].tolist()
+        assert changed == [3], name
+    assert np.array_equal(out["k"][3], O.f64_to_bf16(k))
+    back = T8.wht(T4.turbo4_dequantize(out["v"][3], out["v_scales"][3]))
+    assert np.linalg.norm(back - v) / np.linalg.norm(v) < 0.2   # 4-bit Gaussian codebook: about 0.1
