@@ -6,7 +6,7 @@ attention over a bf16 KV cache at ~8192 tokens), final RMSNorm, int8 lm_head ove
 248 320 tokens, greedy argmax and the next token's embedding, all on the device
 from one replayed HIP graph.  Prints one JSON line (rank 0).
 
-    python bench.py [--gpus 1] [--steps 128] [--warmup 8] [--ctx 8192] [--kv bf16|turbo8]
+    python bench.py [--gpus 1] [--steps 128] [--warmup 8] [--ctx 8192] [--kv bf16|turbo8|bf16k_turbo4v]
 """
 import argparse
 import hashlib
@@ -132,10 +132,13 @@ def cpu_baseline(cfg, w, sample_note, kv="bf16"):
     O.forward_linear_attention(cfg, w["layers"][gi], w["states"][gi], x)
     t_gdn = time.perf_counter() - t0
     t0 = time.perf_counter()
+    kvd = {k: v for k, v in w["kvs"][fi].items() if k != "capacity"}
     if kv == "turbo8":
         from oracle import turbo8 as T8
-        kvd = {k: v for k, v in w["kvs"][fi].items() if k != "capacity"}
         T8.forward_full_attention_turbo8(cfg, w["layers"][fi], kvd, inv, x, w["ctx"])
+    elif kv == "bf16k_turbo4v":
+        from oracle import turbo4v as T4
+        T4.forward_full_attention_bf16k_turbo4v(cfg, w["layers"][fi], kvd, inv, x, w["ctx"])
     else:
         O.forward_full_attention(cfg, w["layers"][fi], w["kvs"][fi], inv, x, w["ctx"])
     t_full = time.perf_counter() - t0
@@ -159,7 +162,7 @@ def main():
     ap.add_argument("--ctx", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dominant-rounds", type=int, default=4)
-    ap.add_argument("--kv", choices=["bf16", "turbo8"], default="bf16",
+    ap.add_argument("--kv", choices=["bf16", "turbo8", "bf16k_turbo4v"], default="bf16",
                     help="KV cache format of the full-attention layers")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -187,7 +190,8 @@ def main():
     w = workloads.stack_4b(gen, num_layers=args.layers, ctx=args.ctx, extra=W + K + 64,
                            progress=lambda i: log(f"  layer {i} generated") if i % 8 == 7 else None,
                            kv=args.kv)
-    kv_bytes = 2.0 if args.kv == "bf16" else 1.0 + 2.0 / 16
+    # bytes per K and V element, averaged over the two
+    kv_bytes = {"bf16": 2.0, "turbo8": 1.0 + 2.0 / 16, "bf16k_turbo4v": (2.0 + 0.5 + 1.0 / 16) / 2}[args.kv]
     cfg, kinds = w["cfg"], w["kinds"]
     log(f"generated in {time.time() - t0:.1f}s; uploading")
     st = rt.DecodeStack(cfg, kinds, w["layers"], w["states"], w["kvs"], w["embed"],
@@ -271,7 +275,8 @@ def main():
     log(f"device copy of {copy_bytes >> 20} MiB: {copy_gbs:.0f} GB/s (read + write)")
     traffic = measured_traffic()
 
-    kv_desc = "bf16" if args.kv == "bf16" else "Turbo8 (WHT-rotated E4M3 + bf16 scale per 16)"
+    kv_desc = {"bf16": "bf16", "turbo8": "Turbo8 (WHT-rotated E4M3 + bf16 scale per 16)",
+               "bf16k_turbo4v": "bf16 K + Turbo4 V (WHT-rotated 4-bit Lloyd-Max + E4M3 scale per 16)"}[args.kv]
     result = {
         "metric": METRIC,
         "value": round(tok_s, 2),

@@ -25,6 +25,7 @@
 // Layouts: K/V caches bf16 [capacity, Hkv, D] (token-major).
 #include <type_traits>
 
+#include "q35decode.h"
 #include "q35_device.h"
 #include "q35_internal.h"
 
@@ -188,9 +189,15 @@ Q35_DEV void wht_regs(float (&x)[D / 64], int lane) {
 // dequantised in the loop, and the block's unnormalised per-head accumulators
 // are rotated back before they are written (the transform is linear and its
 // own inverse, so the merge is unchanged).
-template <int D, int G, bool T8>
+template <int D, int G, int F>
 __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     static_assert(D <= kNT && D % 32 == 0, "one new-v element per thread; merge blocks of 32 dims");
+    // row formats: F = Q35_KV_BF16, Q35_KV_TURBO8 (K and V rotated, E4M3 with a
+    // bf16 scale per 16) or Q35_KV_BF16K_TURBO4V (K bf16 unrotated, V rotated
+    // 4-bit codebook indices with an E4M3 scale per 16)
+    constexpr bool T8 = F == Q35_KV_TURBO8;
+    constexpr bool V4 = F == Q35_KV_BF16K_TURBO4V;
+    constexpr bool ROTV = T8 || V4;
     using Geo = AGeo<D>;
     constexpr int LPR = Geo::LPR, RPI = Geo::RPI, B = Geo::B;
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
@@ -206,7 +213,8 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     __shared__ float2 rot[D / 2];      // (cos, sin) of pos * inv_freq[d], d < rotary / 2
     __shared__ float mls[RPI][2 * G];  // per-slot (max, sum)
     __shared__ float red[(G < 4 ? G : 4) * RPI * D];  // per-slot outputs of up to 4 heads
-    __shared__ float ov[T8 ? G * D : 1];  // Turbo8: merged accumulators, rotated back in place
+    __shared__ float ov[ROTV ? G * D : 1];  // rotated V: merged accumulators, rotated back
+    __shared__ float lut[V4 ? 16 : 1];      // Turbo4: the codebook levels
 
     const int32_t pos = attn_pos(a);
     if (pos < 0 || (uint32_t)pos >= a.capacity) return;
@@ -219,10 +227,12 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     const int32_t rope_pos = a.positions[0];
 
     // ---------------- first batch of K/V loads, in flight during the prologue
-    const uint32_t row_bytes = a.hkv * D * (T8 ? 1u : 2u);      // one token's row of K (or V) data
-    const uint32_t span = (t1 - t0) * row_bytes;
-    const uint32_t srow_bytes = a.hkv * (D / 16) * 2u;          // Turbo8: one token's scales
-    const uint32_t sspan = T8 ? (t1 - t0) * srow_bytes : 0u;
+    // bytes of one token's row: K data, V data, K scales, V scales
+    const uint32_t krow_bytes = a.hkv * D * (T8 ? 1u : 2u);
+    const uint32_t vrow_bytes = a.hkv * D * (T8 ? 2u : V4 ? 1u : 4u) / 2u;
+    const uint32_t ksrow_bytes = T8 ? a.hkv * (D / 16) * 2u : 0u;
+    const uint32_t vsrow_bytes = a.hkv * (D / 16) * (T8 ? 2u : V4 ? 1u : 0u);
+    const uint32_t nrows = t1 - t0;
 
     // ---------------- the prologue's own loads go out first (vector loads
     // complete in order, so the prologue then waits for them alone)
@@ -240,36 +250,43 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     asm volatile("" ::: "memory");
 
     const size_t row0 = ((size_t)t0 * a.hkv + g) * D;  // element offset of the chunk's first row
-    const auto rk = rsrc(T8 ? (const void*)(reinterpret_cast<const uint8_t*>(a.kc) + row0)
-                            : (const void*)(a.kc + row0), span);
-    const auto rv = rsrc(T8 ? (const void*)(reinterpret_cast<const uint8_t*>(a.vc) + row0)
-                            : (const void*)(a.vc + row0), span);
     const size_t srow0 = ((size_t)t0 * a.hkv + g) * (D / 16);
-    const auto rks = rsrc(a.ks + (T8 ? srow0 : 0), sspan);
-    const auto rvs = rsrc(a.vs + (T8 ? srow0 : 0), sspan);
+    const auto rk = rsrc(reinterpret_cast<const uint8_t*>(a.kc) + row0 * (T8 ? 1 : 2), nrows * krow_bytes);
+    const auto rv = rsrc(reinterpret_cast<const uint8_t*>(a.vc) + row0 * (T8 ? 2 : V4 ? 1 : 4) / 2,
+                         nrows * vrow_bytes);
+    const auto rks = rsrc(reinterpret_cast<const uint8_t*>(a.ks) + srow0 * 2, nrows * ksrow_bytes);
+    const auto rvs = rsrc(reinterpret_cast<const uint8_t*>(a.vs) + srow0 * (T8 ? 2 : 1), nrows * vsrow_bytes);
     // two batches in flight: the next batch's rows load while this one
     // computes (three, or smaller batches at higher occupancy, measured no
-    // faster)
-    using KT = std::conditional_t<T8, uint2, uint4>;  // 8 elements of one row per lane
-    KT kr[2][kUnroll], vr[2][kUnroll];
-    uint32_t ksr[2][kUnroll], vsr[2][kUnroll];  // Turbo8: the lane's group scale (bf16 bits)
-    auto load_batch = [&](KT (&kd)[kUnroll], KT (&vd)[kUnroll], uint32_t (&ksd)[kUnroll],
+    // faster).  A lane holds 8 elements of a row.
+    using KT = std::conditional_t<T8, uint2, uint4>;
+    using VT = std::conditional_t<T8, uint2, std::conditional_t<V4, uint32_t, uint4>>;
+    KT kr[2][kUnroll];
+    VT vr[2][kUnroll];
+    uint32_t ksr[2][kUnroll], vsr[2][kUnroll];  // the lane's group scale, raw bits
+    auto load_batch = [&](KT (&kd)[kUnroll], VT (&vd)[kUnroll], uint32_t (&ksd)[kUnroll],
                           uint32_t (&vsd)[kUnroll], uint32_t tb) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const uint32_t tt = tb + u * RPI + rs;
             const bool live = tt < t1 && tt != (uint32_t)pos;
+            const uint32_t r = live ? tt - t0 : nrows;  // past the end: loads return zero
             if constexpr (T8) {
-                const uint32_t off = live ? (tt - t0) * row_bytes + 8u * j : span;  // past the end: zero
-                const uint32_t soff = live ? (tt - t0) * srow_bytes + 2u * (j / 2) : sspan;
-                kd[u] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, kAuxStream));
-                vd[u] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, kAuxStream));
-                ksd[u] = __builtin_amdgcn_raw_buffer_load_b16(rks, soff, 0, kAuxStream);
-                vsd[u] = __builtin_amdgcn_raw_buffer_load_b16(rvs, soff, 0, kAuxStream);
+                kd[u] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, r * krow_bytes + 8u * j, 0, kAuxStream));
+                ksd[u] = __builtin_amdgcn_raw_buffer_load_b16(rks, r * ksrow_bytes + 2u * (j / 2), 0, kAuxStream);
             } else {
-                const uint32_t off = live ? (tt - t0) * row_bytes + 16u * j : span;  // past the end: zero
-                kd[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kAuxStream));
-                vd[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, kAuxStream));
+                kd[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, r * krow_bytes + 16u * j, 0, kAuxStream));
+                ksd[u] = 0;
+            }
+            if constexpr (T8) {
+                vd[u] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, r * vrow_bytes + 8u * j, 0, kAuxStream));
+                vsd[u] = __builtin_amdgcn_raw_buffer_load_b16(rvs, r * vsrow_bytes + 2u * (j / 2), 0, kAuxStream);
+            } else if constexpr (V4) {
+                vd[u] = __builtin_amdgcn_raw_buffer_load_b32(rv, r * vrow_bytes + 4u * j, 0, kAuxStream);
+                vsd[u] = __builtin_amdgcn_raw_buffer_load_b8(rvs, r * vsrow_bytes + (j / 2), 0, kAuxStream);
+            } else {
+                vd[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, r * vrow_bytes + 16u * j, 0, kAuxStream));
+                vsd[u] = 0;
             }
         }
     };
@@ -280,7 +297,9 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < PQ; ++r)
         if (t + kNT * r < (G + 1) * D) qs[t + kNT * r] = qv[r];
-    if (t < D) vn[t] = T8 ? vnew : bf16_to_f32(f32_to_bf16(vnew));
+    if (t < D) vn[t] = ROTV ? vnew : bf16_to_f32(f32_to_bf16(vnew));
+    if constexpr (V4)
+        if (t < 16) lut[t] = a.t4_levels[t];
     if (t < (int)a.rotary / 2) {
         float sn, cs;
         sincosf((float)rope_pos * invf, &sn, &cs);
@@ -359,12 +378,38 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
         if (a.k_norm_out)
             for (int d = t; d < D; d += kNT) a.k_norm_out[g * D + d] = qs[G * D + d];
         uint16_t* krow = a.kc + ((size_t)pos * a.hkv + g) * D;
-        uint16_t* vrow = a.vc + ((size_t)pos * a.hkv + g) * D;
         for (int d = t; d < D; d += kNT) {
             const uint32_t kb = f32_to_bf16(qs[G * D + d]);
             krow[d] = (uint16_t)kb;
-            vrow[d] = (uint16_t)f32_to_bf16(vn[d]);  // vn is already bf16-exact
+            if constexpr (!V4)  // vn is already bf16-exact
+                a.vc[((size_t)pos * a.hkv + g) * D + d] = (uint16_t)f32_to_bf16(vn[d]);
             qs[G * D + d] = bf16_to_f32(kb);  // attend to the row as stored
+        }
+        if constexpr (V4) {
+            // the new v: rotated by wave 0, then quantised in groups of 16 (one
+            // thread each); the block attends to the dequantised row, as stored
+            if (wid == 0) {
+                float x[D / 64];
+#pragma unroll
+                for (int i = 0; i < D / 64; ++i) x[i] = vn[lane * (D / 64) + i];
+                wht_regs<D>(x, lane);
+#pragma unroll
+                for (int i = 0; i < D / 64; ++i) vn[lane * (D / 64) + i] = x[i];
+            }
+            __syncthreads();
+            if (t < D / 16) {
+                float v16[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) v16[e] = vn[16 * t + e];
+                uint32_t idx[2];
+                const uint32_t sc = turbo4_quantize16(v16, a.t4_levels, idx);
+                const size_t gi = ((size_t)pos * a.hkv + g) * (D / 16) + t;
+                reinterpret_cast<uint2*>(a.vc)[gi] = make_uint2(idx[0], idx[1]);
+                reinterpret_cast<uint8_t*>(a.vs)[gi] = (uint8_t)sc;
+                const float s = e4m3x2_to_f32<false>(sc).x;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) vn[16 * t + e] = s * lut[(idx[e / 8] >> (4 * (e % 8))) & 0xFu];
+            }
         }
         __syncthreads();
     }
@@ -406,30 +451,42 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
 
-    // 8 elements of a row: bf16 pairs, or Turbo8 codes (the group scale is
-    // applied to the partial dot products and to the weights instead)
-    auto unpack = [&](const KT& w, float v[8]) {
+    // 8 elements of a row: bf16 pairs, Turbo8 codes or Turbo4 levels (the
+    // group scale is applied to the partial dot products and to the weights
+    // instead)
+    auto unpack_e4m3x8 = [](const uint2& w, float v[8]) {
+        const q35_float2_t p0 = e4m3x2_to_f32<false>(w.x), p1 = e4m3x2_to_f32<true>(w.x);
+        const q35_float2_t p2 = e4m3x2_to_f32<false>(w.y), p3 = e4m3x2_to_f32<true>(w.y);
+        v[0] = p0.x;
+        v[1] = p0.y;
+        v[2] = p1.x;
+        v[3] = p1.y;
+        v[4] = p2.x;
+        v[5] = p2.y;
+        v[6] = p3.x;
+        v[7] = p3.y;
+    };
+    auto unpack_v = [&](const VT& w, float v[8]) {
         if constexpr (T8) {
-            const q35_float2_t p0 = e4m3x2_to_f32<false>(w.x), p1 = e4m3x2_to_f32<true>(w.x);
-            const q35_float2_t p2 = e4m3x2_to_f32<false>(w.y), p3 = e4m3x2_to_f32<true>(w.y);
-            v[0] = p0.x;
-            v[1] = p0.y;
-            v[2] = p1.x;
-            v[3] = p1.y;
-            v[4] = p2.x;
-            v[5] = p2.y;
-            v[6] = p3.x;
-            v[7] = p3.y;
+            unpack_e4m3x8(w, v);
+        } else if constexpr (V4) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = lut[(w >> (4 * e)) & 0xFu];
         } else {
             unpack8(w, v);
         }
+    };
+    auto vscale_of = [](uint32_t bits) {
+        if constexpr (T8) return bf16_to_f32(bits & 0xFFFFu);
+        else if constexpr (V4) return e4m3x2_to_f32<false>(bits & 0xFFu).x;
+        else return 1.0f;
     };
     // one row's score for head hl from the lane's 8 key elements
     auto score = [&](const KT& w, float kscale) {
         float d[G];
         if constexpr (T8) {
             float kv[8];
-            unpack(w, kv);
+            unpack_e4m3x8(w, kv);
 #pragma unroll
             for (int p = 0; p < G; ++p) {
                 float x = 0.f;
@@ -490,12 +547,12 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
         for (int p = 0; p < G; ++p) {
             float pp = slot_bcast<G>(pw, p);
-            if constexpr (T8) pp *= vscale;
+            if constexpr (ROTV) pp *= vscale;
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[p][e] = fmaf(pp, vv[e], acc[p][e]);
         }
     };
-    auto batch = [&](const KT (&kd)[kUnroll], const KT (&vd)[kUnroll], const uint32_t (&ksd)[kUnroll],
+    auto batch = [&](const KT (&kd)[kUnroll], const VT (&vd)[kUnroll], const uint32_t (&ksd)[kUnroll],
                      const uint32_t (&vsd)[kUnroll], uint32_t tb) {
         float s[kUnroll];
 #pragma unroll
@@ -512,8 +569,8 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             float vv[8];
-            unpack(vd[u], vv);
-            accumulate(exp2f(s[u] - mref), vv, T8 ? bf16_to_f32(vsd[u] & 0xFFFFu) : 1.0f);
+            unpack_v(vd[u], vv);
+            accumulate(exp2f(s[u] - mref), vv, vscale_of(vsd[u]));
         }
     };
     // Reloads are unconditional (rows past the chunk read zero and move no
@@ -580,14 +637,14 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
             float o = 0.f;
 #pragma unroll 8
             for (int r = 0; r < RPI; ++r) o += red[(hh * RPI + r) * D + d];
-            if constexpr (T8)
+            if constexpr (ROTV)
                 ov[(h0 + hh) * D + d] = o;
             else
                 pacc[(h0 + hh) * D + d] = o;
         }
         __syncthreads();
     }
-    if constexpr (T8) {
+    if constexpr (ROTV) {
         // each head's merged accumulator back to the original basis (the
         // orthonormal transform is its own inverse; the merge is linear), one
         // head per wave
@@ -672,11 +729,16 @@ __global__ __launch_bounds__(kNT) void attn_merge_kernel(AttnArgs a) {
 }
 
 template <int D, int G>
-hipError_t launch_t(const AttnArgs& a, uint32_t grid_chunks, bool t8, hipStream_t stream) {
-    if (t8)
-        hipLaunchKernelGGL((attn_partial_kernel<D, G, true>), dim3(grid_chunks, a.hkv), dim3(kNT), 0, stream, a);
+hipError_t launch_t(const AttnArgs& a, uint32_t grid_chunks, uint32_t fmt, hipStream_t stream) {
+    if (fmt == Q35_KV_TURBO8)
+        hipLaunchKernelGGL((attn_partial_kernel<D, G, Q35_KV_TURBO8>), dim3(grid_chunks, a.hkv), dim3(kNT), 0, stream, a);
+    else if (fmt == Q35_KV_BF16K_TURBO4V)
+        hipLaunchKernelGGL((attn_partial_kernel<D, G, Q35_KV_BF16K_TURBO4V>), dim3(grid_chunks, a.hkv), dim3(kNT), 0,
+                           stream, a);
+    else if (fmt == Q35_KV_BF16)
+        hipLaunchKernelGGL((attn_partial_kernel<D, G, Q35_KV_BF16>), dim3(grid_chunks, a.hkv), dim3(kNT), 0, stream, a);
     else
-        hipLaunchKernelGGL((attn_partial_kernel<D, G, false>), dim3(grid_chunks, a.hkv), dim3(kNT), 0, stream, a);
+        return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_merge_kernel<D, G>), dim3(a.hq, D / kMergeDims), dim3(kNT),
@@ -696,6 +758,20 @@ __global__ __launch_bounds__(256) void turbo8_quantize_kernel(const float* x, ui
     uint32_t cw[4];
     scales[gi] = (uint16_t)turbo8_quantize16(v, cw);
     *reinterpret_cast<uint4*>(codes + 16u * gi) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+}
+
+// Turbo4 group quantiser over a plain vector (kernel-level export): one thread
+// per group of 16.
+__global__ __launch_bounds__(256) void turbo4_quantize_kernel(const float* x, uint32_t groups, Turbo4Levels lv,
+                                                              uint8_t* packed, uint8_t* scales) {
+    const uint32_t gi = blockIdx.x * 256u + threadIdx.x;
+    if (gi >= groups) return;
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = x[16u * gi + e];
+    uint32_t idx[2];
+    scales[gi] = (uint8_t)turbo4_quantize16(v, lv.v, idx);
+    reinterpret_cast<uint2*>(packed)[gi] = make_uint2(idx[0], idx[1]);
 }
 
 // Every E4M3 code through the decoder the attention loop uses (kernel-level export).
@@ -725,19 +801,21 @@ bool attn_dims_supported(uint32_t head_dim, uint32_t group) {
 }
 
 hipError_t attn_launch(uint32_t head_dim, uint32_t group, const AttnArgs& a, uint32_t grid_chunks,
-                       bool turbo8, hipStream_t stream) {
+                       uint32_t kv_dtype, hipStream_t stream) {
 #define X(DD, GG) \
-    if (head_dim == DD && group == GG) return launch_t<DD, GG>(a, grid_chunks, turbo8, stream);
+    if (head_dim == DD && group == GG) return launch_t<DD, GG>(a, grid_chunks, kv_dtype, stream);
     Q35_ATTN_SHAPES(X)
 #undef X
     return hipErrorInvalidValue;
 }
 
-const void* attn_kernel_ptr(uint32_t head_dim, uint32_t group, bool turbo8) {
-#define X(DD, GG)                                                                             \
-    if (head_dim == DD && group == GG)                                                        \
-        return turbo8 ? (const void*)&attn_partial_kernel<DD, GG, true>                       \
-                      : (const void*)&attn_partial_kernel<DD, GG, false>;
+const void* attn_kernel_ptr(uint32_t head_dim, uint32_t group, uint32_t kv_dtype) {
+#define X(DD, GG)                                                                              \
+    if (head_dim == DD && group == GG)                                                         \
+        return kv_dtype == Q35_KV_TURBO8          ? (const void*)&attn_partial_kernel<DD, GG, Q35_KV_TURBO8> \
+               : kv_dtype == Q35_KV_BF16K_TURBO4V ? (const void*)&attn_partial_kernel<DD, GG, Q35_KV_BF16K_TURBO4V> \
+               : kv_dtype == Q35_KV_BF16          ? (const void*)&attn_partial_kernel<DD, GG, Q35_KV_BF16> \
+                                                  : nullptr;
     Q35_ATTN_SHAPES(X)
 #undef X
     return nullptr;
@@ -757,6 +835,15 @@ hipError_t turbo8_quantize_launch(const float* x, uint32_t n, uint8_t* codes, ui
     if (groups == 0) return hipSuccess;
     hipLaunchKernelGGL(turbo8_quantize_kernel, dim3((groups + 255) / 256), dim3(256), 0, stream, x,
                        groups, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t turbo4_quantize_launch(const float* x, uint32_t n, const Turbo4Levels& levels, uint8_t* packed,
+                                  uint8_t* scales, hipStream_t stream) {
+    const uint32_t groups = n / 16;
+    if (groups == 0) return hipSuccess;
+    hipLaunchKernelGGL(turbo4_quantize_kernel, dim3((groups + 255) / 256), dim3(256), 0, stream, x, groups, levels,
+                       packed, scales);
     return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 // every call enqueues on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -18,6 +19,7 @@ using namespace q35;
 struct Qwen35Kernels {
     int device;
     int num_cu;
+    q35::Turbo4Levels t4;  // the Turbo4 codebook (computed at resolve)
 };
 
 namespace {
@@ -223,16 +225,56 @@ q35_status check_full_layer(const Qwen35ForwardConfig& c, const FullAttentionLay
     return Q35_OK;
 }
 
-// bf16 everywhere; Turbo8 (E4M3 codes + bf16 scales per 16) in the per-layer forward.
-q35_status check_kv(const LayerKvCache& kv, bool allow_turbo8) {
-    if (kv.dtype == Q35_KV_TURBO8 && allow_turbo8) {
+// The Turbo4 codebook (mod.rs: the Turbo4 variant's Lloyd-Max indices; the
+// level values are not given there): the 16-level Lloyd-Max quantiser of the
+// standard normal distribution.  Lloyd's iteration in double precision --
+// thresholds halfway between adjacent levels, each level moved to the mean of
+// N(0, 1) over its cell -- until no level moves, then made exactly symmetric
+// and rounded to float.
+double normal_cell_mean(double lo, double hi) {
+    const double r2 = std::sqrt(2.0), r2pi = std::sqrt(2.0 * 3.14159265358979323846);
+    auto pdf = [&](double x) { return std::isinf(x) ? 0.0 : std::exp(-0.5 * x * x) / r2pi; };
+    double mass;  // from the tail on the far side of 0, so small cells keep their digits
+    if (lo >= 0.0)
+        mass = 0.5 * (std::erfc(lo / r2) - std::erfc(hi / r2));
+    else if (hi <= 0.0)
+        mass = 0.5 * (std::erfc(-hi / r2) - std::erfc(-lo / r2));
+    else
+        mass = 1.0 - 0.5 * std::erfc(-lo / r2) - 0.5 * std::erfc(hi / r2);
+    return (pdf(lo) - pdf(hi)) / mass;
+}
+
+void lloyd_max_normal16(float out[16]) {
+    double c[16];
+    for (int i = 0; i < 16; ++i) c[i] = -2.5 + 5.0 * i / 15.0;
+    for (int it = 0; it < 20000; ++it) {
+        double nc[16], moved = 0.0;
+        for (int i = 0; i < 16; ++i) {
+            const double lo = i == 0 ? -INFINITY : 0.5 * (c[i - 1] + c[i]);
+            const double hi = i == 15 ? INFINITY : 0.5 * (c[i] + c[i + 1]);
+            nc[i] = normal_cell_mean(lo, hi);
+            moved = std::max(moved, std::fabs(nc[i] - c[i]));
+        }
+        std::memcpy(c, nc, sizeof(c));
+        if (moved < 1e-15) break;
+    }
+    for (int i = 0; i < 16; ++i) out[i] = (float)((c[i] - c[15 - i]) / 2.0);
+}
+
+// bf16 everywhere; Turbo8 (E4M3 codes + bf16 scales per 16) and Bf16K + Turbo4V
+// (bf16 K, 4-bit V indices + E4M3 scales per 16) in the per-layer forward.
+q35_status check_kv(const LayerKvCache& kv, bool allow_quantised) {
+    if (kv.dtype == Q35_KV_TURBO8 && allow_quantised) {
         Q35_TRY(need(kv.k_scales, "kv.k_scales"));
+        Q35_TRY(need(kv.v_scales, "kv.v_scales"));
+    } else if (kv.dtype == Q35_KV_BF16K_TURBO4V && allow_quantised) {
+        if (kv.k_scales) return fail(Q35_ERR_INVALID_ARG, "bf16k_turbo4v cache with a K scale buffer");
         Q35_TRY(need(kv.v_scales, "kv.v_scales"));
     } else if (kv.dtype == Q35_KV_BF16) {
         if (kv.k_scales || kv.v_scales) return fail(Q35_ERR_INVALID_ARG, "bf16 cache with scale buffers");
     } else {
         return fail(Q35_ERR_UNSUPPORTED, "KV dtype %u is not implemented on this path (%s)", kv.dtype,
-                    allow_turbo8 ? "bf16 | turbo8" : "bf16");
+                    allow_quantised ? "bf16 | turbo8 | bf16k_turbo4v" : "bf16");
     }
     Q35_TRY(need(kv.k, "kv.k"));
     Q35_TRY(need(kv.v, "kv.v"));
@@ -399,7 +441,8 @@ q35_status q35_kernels_resolve(int device, Qwen35Kernels** out) {
     for (uint32_t dk : {32u, 64u, 128u}) probe(gdn_kernel_ptr(dk), "gated_delta_rule");
     for (uint32_t d : {64u, 128u, 256u})
         for (uint32_t g : {1u, 2u, 4u, 8u})
-            for (bool t8 : {false, true}) probe(attn_kernel_ptr(d, g, t8), "attention");
+            for (uint32_t f : {Q35_KV_BF16, Q35_KV_TURBO8, Q35_KV_BF16K_TURBO4V})
+                probe(attn_kernel_ptr(d, g, f), "attention");
     probe(embed_kernel_ptr(), "embed");
     probe(lm_finish_kernel_ptr(), "lm_head argmax");
     for (uint32_t d : {64u, 128u, 256u})
@@ -409,6 +452,7 @@ q35_status q35_kernels_resolve(int device, Qwen35Kernels** out) {
     Qwen35Kernels* k = new Qwen35Kernels;
     k->device = device;
     k->num_cu = prop.multiProcessorCount;
+    lloyd_max_normal16(k->t4.v);
     *out = k;
     return ok();
 }
@@ -548,6 +592,7 @@ static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35Fo
         a.max_chunks = attn_max_chunks(c, kv->capacity);
         a.eps = c.rms_eps;
         a.scale = 1.0f / std::sqrt((float)c.head_dim);
+        std::memcpy(a.t4_levels, kernels->t4.v, sizeof(a.t4_levels));
         uint32_t grid;
         if (cache_pos >= 0) {
             a.host_pos = (int32_t)cache_pos;
@@ -559,7 +604,7 @@ static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35Fo
             grid = (kv->capacity + a.chunk - 1) / a.chunk;
         }
         if (grid > a.max_chunks) return fail(Q35_ERR_INVALID_ARG, "internal: %u chunks > %u", grid, a.max_chunks);
-        Q35_HIP(attn_launch(c.head_dim, G, a, grid, kv->dtype == Q35_KV_TURBO8, stream), "attention");
+        Q35_HIP(attn_launch(c.head_dim, G, a, grid, kv->dtype, stream), "attention");
         (void)G;
     }
     // 3. o projection + residual
@@ -814,6 +859,26 @@ q35_status q35_turbo8_quantize(const Qwen35Kernels* kernels, const float* x, uin
     Q35_TRY(need(scales, "scales", false));
     if (reinterpret_cast<uintptr_t>(scales) & 1u) return fail(Q35_ERR_INVALID_ARG, "scales not 2-byte aligned");
     Q35_HIP(turbo8_quantize_launch(x, n, codes, scales, stream), "turbo8 quantise");
+    return ok();
+}
+
+q35_status q35_turbo4_codebook(const Qwen35Kernels* kernels, float* levels) {
+    Q35_TRY(check_kernels(kernels));
+    if (!levels) return fail(Q35_ERR_INVALID_ARG, "levels is NULL");
+    std::memcpy(levels, kernels->t4.v, 16 * sizeof(float));
+    return ok();
+}
+
+q35_status q35_turbo4_quantize(const Qwen35Kernels* kernels, const float* x, uint32_t n, uint8_t* packed,
+                               uint8_t* scales, hipStream_t stream) {
+    Q35_TRY(check_kernels(kernels));
+    if (n % 16) return fail(Q35_ERR_INVALID_ARG, "n = %u is not a multiple of 16", n);
+    if (n == 0) return ok();
+    Q35_TRY(need(x, "x"));
+    Q35_TRY(need(packed, "packed", false));
+    if (reinterpret_cast<uintptr_t>(packed) & 7u) return fail(Q35_ERR_INVALID_ARG, "packed not 8-byte aligned");
+    Q35_TRY(need(scales, "scales", false));
+    Q35_HIP(turbo4_quantize_launch(x, n, kernels->t4, packed, scales, stream), "turbo4 quantise");
     return ok();
 }
 

@@ -98,6 +98,38 @@ Q35_DEV uint32_t turbo8_quantize16(const float v[16], uint32_t codes[4]) {
     return sb;
 }
 
+// Turbo4 group of 16 rotated values over a 16-level codebook (ascending):
+// each index is the number of thresholds (fp32 midpoints of adjacent levels)
+// below x / sigma, sigma = sqrt(sum(x^2) / 16) with the sum in double and
+// sigma in fp32 (the nearest level, ties to the lower); packed two per byte,
+// low nibble first, into idx[0] (elements 0-7) and idx[1] (8-15).  Returns
+// the E4M3 code of the scale ||x|| / ||levels[idx]|| (double, rounded to
+// fp32, then E4M3), which keeps the group's norm up to that rounding.  A zero
+// group: scale 0 and indices 0.
+Q35_DEV uint32_t turbo4_quantize16(const float v[16], const float* levels, uint32_t idx[2]) {
+    double ss = 0.0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ss += (double)v[e] * (double)v[e];
+    idx[0] = idx[1] = 0u;
+    if (ss == 0.0) return 0u;
+    const float sigma = sqrtf((float)ss / 16.0f);
+    float th[15];
+#pragma unroll
+    for (int k = 0; k < 15; ++k) th[k] = (levels[k] + levels[k + 1]) * 0.5f;
+    double cn = 0.0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const float y = v[e] / sigma;
+        uint32_t n = 0;
+#pragma unroll
+        for (int k = 0; k < 15; ++k) n += y > th[k] ? 1u : 0u;
+        idx[e / 8] |= n << (4 * (e % 8));
+        const double l = levels[n];
+        cn += l * l;
+    }
+    return e4m3_encode((float)(sqrt(ss) / sqrt(cn)));
+}
+
 // ------------------------------------------------------------------ activations
 
 Q35_DEV float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }

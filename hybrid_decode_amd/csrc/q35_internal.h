@@ -148,8 +148,9 @@ struct AttnArgs {
     float* k_norm_out;       // optional tap (post-RoPE)
     float* part_acc;         // workspace: [Hkv][max_chunks][G][D]
     float* part_ml;          // workspace: [Hkv][max_chunks][G][2]
-    uint16_t* ks;            // Turbo8 only: bf16 group scales [cap, Hkv, D/16] (kc/vc then hold E4M3 codes)
-    uint16_t* vs;
+    uint16_t* ks;            // Turbo8: bf16 K group scales [cap, Hkv, D/16] (kc then holds E4M3 codes)
+    uint16_t* vs;            // Turbo8: bf16 V group scales; Bf16K+Turbo4V: E4M3 bytes [cap, Hkv, D/16]
+                             // (vc then holds packed 4-bit indices [cap, Hkv, D/2])
     uint32_t capacity;
     uint32_t hq, hkv, rotary;
     uint32_t chunk;          // positions per block
@@ -157,17 +158,24 @@ struct AttnArgs {
     int32_t host_pos;        // >= 0: cache position from the host; < 0: read positions[0]
     float eps;
     float scale;
+    float t4_levels[16];     // Bf16K+Turbo4V: the codebook levels
 };
 bool attn_dims_supported(uint32_t head_dim, uint32_t group);
 uint32_t attn_rows_per_iter(uint32_t head_dim);
 // Two launches: per-chunk partials, then the log-sum-exp merge with the sigmoid gate.
+// kv_dtype: Q35_KV_BF16, Q35_KV_TURBO8 or Q35_KV_BF16K_TURBO4V
 hipError_t attn_launch(uint32_t head_dim, uint32_t group, const AttnArgs& a, uint32_t grid_chunks,
-                       bool turbo8, hipStream_t stream);
-const void* attn_kernel_ptr(uint32_t head_dim, uint32_t group, bool turbo8);
+                       uint32_t kv_dtype, hipStream_t stream);
+const void* attn_kernel_ptr(uint32_t head_dim, uint32_t group, uint32_t kv_dtype);
 // Turbo8 group quantiser and E4M3 decoder of the attention kernels, over plain buffers.
 hipError_t turbo8_quantize_launch(const float* x, uint32_t n, uint8_t* codes, uint16_t* scales,
                                   hipStream_t stream);
 hipError_t e4m3_table_launch(float* out256, hipStream_t stream);
+struct Turbo4Levels {
+    float v[16];
+};
+hipError_t turbo4_quantize_launch(const float* x, uint32_t n, const Turbo4Levels& levels, uint8_t* packed,
+                                  uint8_t* scales, hipStream_t stream);
 const void* attn_combine_kernel_ptr(uint32_t head_dim, uint32_t group);
 
 // ------------------------------------------------------------------ misc

@@ -131,29 +131,37 @@ class GdnStateDev:
 
 
 class KvCacheDev:
-    """One layer's KV cache in device memory.  bf16: {"k", "v"} uint16 bits
-    [cap, Hkv, D]; Turbo8 (when "k_scales" is present): "k", "v" uint8 E4M3
-    codes [cap, Hkv, D] and "k_scales", "v_scales" bf16 bits [cap, Hkv, D/16]."""
+    """One layer's KV cache in device memory, its format read from the arrays:
+    bf16: {"k", "v"} uint16 bits [cap, Hkv, D]; Turbo8 ("k_scales" present):
+    "k", "v" uint8 E4M3 codes [cap, Hkv, D], "k_scales", "v_scales" bf16 bits
+    [cap, Hkv, D/16]; Bf16K + Turbo4V ("v_scales" only): "k" bf16 bits
+    [cap, Hkv, D], "v" packed 4-bit indices uint8 [cap, Hkv, D/2], "v_scales"
+    E4M3 bytes [cap, Hkv, D/16]."""
 
     def __init__(self, kv: dict, device="cuda"):
-        self.turbo8 = "k_scales" in kv
+        if "k_scales" in kv:
+            self.dtype = B.Q35_KV_TURBO8
+        elif "v_scales" in kv:
+            self.dtype = B.Q35_KV_BF16K_TURBO4V
+        else:
+            self.dtype = B.Q35_KV_BF16
+        self.turbo8 = self.dtype == B.Q35_KV_TURBO8
         self.k = to_dev(kv["k"], device)
         self.v = to_dev(kv["v"], device)
         self.capacity = int(kv["k"].shape[0])
-        if self.turbo8:
-            self.k_scales = to_dev(kv["k_scales"], device)
-            self.v_scales = to_dev(kv["v_scales"], device)
-            self.struct = B.LayerKvCache(ptr(self.k), ptr(self.v), self.capacity, B.Q35_KV_TURBO8,
-                                         ptr(self.k_scales), ptr(self.v_scales))
-        else:
-            self.struct = B.LayerKvCache(ptr(self.k), ptr(self.v), self.capacity, B.Q35_KV_BF16,
-                                         None, None)
+        self.k_scales = to_dev(kv["k_scales"], device) if "k_scales" in kv else None
+        self.v_scales = to_dev(kv["v_scales"], device) if "v_scales" in kv else None
+        self.struct = B.LayerKvCache(ptr(self.k), ptr(self.v), self.capacity, self.dtype,
+                                     ptr(self.k_scales), ptr(self.v_scales))
 
     def to_host(self) -> dict:
-        if self.turbo8:
+        if self.dtype == B.Q35_KV_TURBO8:
             return {"k": self.k.cpu().numpy(), "v": self.v.cpu().numpy(),
                     "k_scales": self.k_scales.cpu().numpy().view(np.uint16),
                     "v_scales": self.v_scales.cpu().numpy().view(np.uint16)}
+        if self.dtype == B.Q35_KV_BF16K_TURBO4V:
+            return {"k": self.k.cpu().numpy().view(np.uint16), "v": self.v.cpu().numpy(),
+                    "v_scales": self.v_scales.cpu().numpy()}
         return {"k": self.k.cpu().numpy().view(np.uint16), "v": self.v.cpu().numpy().view(np.uint16)}
 
 

@@ -269,6 +269,24 @@ def kv_cache(g: Gen, cfg: Config, prefix: str, capacity: int, filled: int) -> di
     return {"k": k, "v": v, "capacity": capacity}
 
 
+def kv_cache_bf16k_turbo4v(g: Gen, cfg: Config, prefix: str, capacity: int, filled: int) -> dict:
+    """Bf16K + Turbo4V caches: k bf16 [capacity, Hkv, D] with rows [0, filled)
+    N(0, 1); v packed 4-bit indices uint8 [capacity, Hkv, D/2], every byte drawn
+    uniformly, and E4M3 scale bytes [capacity, Hkv, D/16] drawn uniformly from
+    the codes 0x28-0x3F (0.25 to 1.875); the other rows are zero."""
+    Hkv, D = cfg.num_kv_heads, cfg.head_dim
+    out = {"k": np.zeros((capacity, Hkv, D), np.uint16),
+           "v": np.zeros((capacity, Hkv, D // 2), np.uint8),
+           "v_scales": np.zeros((capacity, Hkv, D // 16), np.uint8), "capacity": capacity}
+    if filled:
+        out["k"][:filled] = g.normal_bf16(prefix + ".k_prefill", (filled, Hkv, D))
+        u = g.uniform_f32(prefix + ".v_t4codes", (filled, Hkv, D // 2), 0.0, 256.0)
+        out["v"][:filled] = np.minimum(np.floor(u), 255.0).astype(np.uint8)
+        u = g.uniform_f32(prefix + ".v_t4scales", (filled, Hkv, D // 16), 0.0, 24.0)
+        out["v_scales"][:filled] = (0x28 + np.minimum(np.floor(u), 23.0)).astype(np.uint8)
+    return out
+
+
 def kv_cache_turbo8(g: Gen, cfg: Config, prefix: str, capacity: int, filled: int) -> dict:
     """Turbo8 caches: E4M3 codes uint8 [capacity, Hkv, D] and bf16 group scales
     [capacity, Hkv, D/16].  Rows [0, filled) hold codes drawn uniformly from the

@@ -9,6 +9,9 @@
 * ``full_layer_4b_turbo8``  the same layer over a Turbo8 cache whose rows
                       [0, 4096) hold uniformly drawn finite E4M3 codes and bf16
                       scales U(1e-3, 1e-2);
+* ``full_layer_4b_bf16k_turbo4v``  the same layer over a Bf16K + Turbo4V cache
+                      (bf16 keys N(0, 1), uniformly drawn value indices and
+                      E4M3 scales);
 * ``stack_4b``        the 4B-shaped stack (every 4th layer full attention), int8
                       lm_head over the 248 320-token vocabulary, bf16 embedding table
                       N(0, 1), zero GDN states, KV rows [0, ctx) prefilled N(0, 1)
@@ -16,8 +19,8 @@
 """
 from __future__ import annotations
 
-from . import (Gen, gdn_layer, full_layer, gdn_state, kv_cache, kv_cache_turbo8, layer_kinds,
-               qwen3_5_4b, tiny)
+from . import (Gen, gdn_layer, full_layer, gdn_state, kv_cache, kv_cache_bf16k_turbo4v,
+               kv_cache_turbo8, layer_kinds, qwen3_5_4b, tiny)
 
 
 def tiny_stack(gen: Gen, steps: int = 16, capacity: int = 16):
@@ -54,11 +57,20 @@ def full_layer_4b_turbo8(gen: Gen, steps: int = 12, prefill: int = 4096):
     return {"cfg": cfg, "layer": layer, "kv": kv, "xs": xs, "start": prefill}
 
 
+def full_layer_4b_bf16k_turbo4v(gen: Gen, steps: int = 12, prefill: int = 4096):
+    cfg = qwen3_5_4b("bf16")
+    layer = full_layer(gen, cfg, "c3t4.L")
+    kv = kv_cache_bf16k_turbo4v(gen, cfg, "c3t4.L", prefill + steps, prefill)
+    xs = [gen.act(f"c3t4.x{t}", (cfg.hidden,), cfg.act_dtype) for t in range(steps)]
+    return {"cfg": cfg, "layer": layer, "kv": kv, "xs": xs, "start": prefill}
+
+
 def stack_4b(gen: Gen, num_layers: int = 32, ctx: int = 8192, extra: int = 256, progress=None,
              kv: str = "bf16"):
     """The 4B-shaped stack.  ``capacity = ctx + extra`` tokens per KV cache; ``kv``
-    "bf16" (rows N(0, 1)) or "turbo8" (rows of uniformly drawn finite E4M3 codes
-    and bf16 scales U(1e-3, 1e-2))."""
+    "bf16" (rows N(0, 1)), "turbo8" (rows of uniformly drawn finite E4M3 codes
+    and bf16 scales U(1e-3, 1e-2)) or "bf16k_turbo4v" (bf16 keys N(0, 1), uniformly
+    drawn 4-bit value indices and E4M3 scales)."""
     cfg = qwen3_5_4b("bf16")
     kinds = layer_kinds(num_layers)
     layers, states, kvs = [], [], []
@@ -70,7 +82,8 @@ def stack_4b(gen: Gen, num_layers: int = 32, ctx: int = 8192, extra: int = 256, 
         else:
             layers.append(full_layer(gen, cfg, f"c4.L{i}"))
             states.append(None)
-            make = kv_cache_turbo8 if kv == "turbo8" else kv_cache
+            make = {"bf16": kv_cache, "turbo8": kv_cache_turbo8,
+                    "bf16k_turbo4v": kv_cache_bf16k_turbo4v}[kv]
             kvs.append(make(gen, cfg, f"c4.L{i}", ctx + extra, ctx))
         if progress:
             progress(i)

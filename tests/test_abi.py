@@ -167,7 +167,17 @@ def test_forward_errors_before_any_launch(lib):
         B.q35_forward_full_attention(FAKE_KERNELS, c, layer, scratch, kv, 0x100, 0x100, 0x100, 3, 4, None)
     assert e.value.status == B.Q35_ERR_INVALID_ARG and "v_scales" in str(e.value)
     kv.k_scales = None
-    for name in ("turbo4", "turbo3", "turbo2", "bf16k_turbo4v"):
+    # Bf16K + Turbo4V needs the V scales and no K scales
+    kv.dtype = B.q35_kv_dtype_from_str("bf16k_turbo4v")
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_forward_full_attention(FAKE_KERNELS, c, layer, scratch, kv, 0x100, 0x100, 0x100, 3, 4, None)
+    assert e.value.status == B.Q35_ERR_INVALID_ARG and "v_scales" in str(e.value)
+    kv.k_scales, kv.v_scales = 0x100, 0x100
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_forward_full_attention(FAKE_KERNELS, c, layer, scratch, kv, 0x100, 0x100, 0x100, 3, 4, None)
+    assert e.value.status == B.Q35_ERR_INVALID_ARG and "K scale" in str(e.value)
+    kv.k_scales, kv.v_scales = None, None
+    for name in ("turbo4", "turbo3", "turbo2", "bf16k_turbo3v", "bf16k_turbo2v"):
         kv.dtype = B.q35_kv_dtype_from_str(name)
         with pytest.raises(B.Q35Error) as e:
             B.q35_forward_full_attention(FAKE_KERNELS, c, layer, scratch, kv, 0x100, 0x100, 0x100, 3, 4,
