@@ -137,7 +137,7 @@ def cpu_baseline(cfg, w, sample_note, kv="bf16"):
         from oracle import turbo8 as T8
         T8.forward_full_attention_turbo8(cfg, w["layers"][fi], kvd, inv, x, w["ctx"])
     elif kv == "bf16k_turbo4v":
-        from oracle import turbo4v as T4
+        from oracle import turbo_lm as T4
         T4.forward_full_attention_bf16k_turbo4v(cfg, w["layers"][fi], kvd, inv, x, w["ctx"])
     else:
         O.forward_full_attention(cfg, w["layers"][fi], w["kvs"][fi], inv, x, w["ctx"])

@@ -11,4 +11,4 @@ print no worked example): "parity unpinned" beyond composition.
 from .qwen35 import *  # noqa: F401,F403
 from . import qwen35  # noqa: F401
 from . import turbo8  # noqa: F401
-from . import turbo4v  # noqa: F401
+from . import turbo_lm  # noqa: F401

@@ -24,7 +24,7 @@ import pytest
 import torch
 
 import oracle as O
-from oracle import turbo4v as T4
+from oracle import turbo_lm as T4
 from oracle import turbo8 as T8
 import synth
 from synth import workloads

@@ -620,41 +620,55 @@ def test_turbo8_append_places_one_row_within_the_quantisation_bound():
 
 # --------------------------------------------------------------------------- Turbo4V KV cache (bf16 K)
 
-from oracle import turbo4v as T4  # noqa: E402
+from oracle import turbo_lm as T4  # noqa: E402
 
 
-def test_lloyd_max_codebook_meets_lloyds_conditions_by_quadrature():
+@pytest.mark.parametrize("n", [4, 8, 16])
+def test_lloyd_max_codebook_meets_lloyds_conditions_by_quadrature(n):
     from scipy import integrate, stats
-    c = T4.lloyd_max_normal()
-    assert c.shape == (16,) and np.all(np.diff(c) > 0)
+    c = T4.lloyd_max_normal(n)
+    assert c.shape == (n,) and np.all(np.diff(c) > 0)
     assert np.array_equal(c, -c[::-1])
     t = [-np.inf, *((c[:-1] + c[1:]) / 2), np.inf]
-    for i in range(16):
+    for i in range(n):
         mass = stats.norm.cdf(t[i + 1]) - stats.norm.cdf(t[i]) if t[i] < 0 else \
             stats.norm.sf(t[i]) - stats.norm.sf(t[i + 1])
         first = integrate.quad(lambda x: x * stats.norm.pdf(x), t[i], t[i + 1], epsabs=1e-14)[0]
         assert abs(first / mass - c[i]) < 1e-9, i      # each level is the mean of its cell
 
 
-def test_lloyd_max_codebook_agrees_with_kmeans_on_gaussian_samples():
+@pytest.mark.parametrize("n", [4, 8, 16])
+def test_lloyd_max_codebook_agrees_with_kmeans_on_gaussian_samples(n):
     rng = np.random.default_rng(123)
     x = np.sort(rng.standard_normal(1 << 20))
-    lv = np.quantile(x, (np.arange(16) + 0.5) / 16)
+    lv = np.quantile(x, (np.arange(n) + 0.5) / n)
     for _ in range(200):                               # 1-D k-means on the samples
         t = (lv[:-1] + lv[1:]) / 2
         cell = np.searchsorted(t, x)
-        lv = np.array([x[cell == i].mean() for i in range(16)])
-    assert np.max(np.abs(lv - T4.lloyd_max_normal())) < 0.02
+        lv = np.array([x[cell == i].mean() for i in range(n)])
+    assert np.max(np.abs(lv - T4.lloyd_max_normal(n))) < 0.02
     # and the distortion is the smallest among nearby codebooks (a minimum)
     def mse(levels):
         t = (levels[:-1] + levels[1:]) / 2
         return np.mean((x - levels[np.searchsorted(t, x)]) ** 2)
-    base = mse(T4.lloyd_max_normal())
-    for k in range(8):
-        bumped = T4.lloyd_max_normal().copy()
+    base = mse(T4.lloyd_max_normal(n))
+    for k in range(n // 2):
+        bumped = T4.lloyd_max_normal(n).copy()
         bumped[k] += 0.05
-        bumped[15 - k] -= 0.05
+        bumped[n - 1 - k] -= 0.05
         assert mse(bumped) > base
+
+
+def test_packing_is_a_little_endian_bit_stream():
+    assert T4.pack_indices(np.arange(8), 3).tolist() == [0x88, 0xC6, 0xFA]
+    assert T4.pack_indices(np.array([0, 1, 2, 3]), 2).tolist() == [0xE4]
+    assert T4.pack_indices(np.array([1, 14]), 4).tolist() == [0xE1]
+    rng = np.random.default_rng(4)
+    for bits in (2, 3, 4):
+        idx = rng.integers(0, 1 << bits, (3, 5, 32))
+        packed = T4.pack_indices(idx, bits)
+        assert packed.shape == (3, 5, 32 * bits // 8)
+        assert np.array_equal(T4.unpack_indices(packed, bits), idx)
 
 
 def test_turbo4_packing_low_nibble_first():
@@ -687,6 +701,48 @@ def test_turbo4_indices_are_nearest_levels_and_the_norm_is_kept():
     z = np.zeros((1, 16), np.float32)
     p0, s0 = T4.turbo4_quantize(z)
     assert not p0.any() and not s0.any()
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_low_bit_indices_are_nearest_levels_and_the_norm_is_kept(bits):
+    rng = np.random.default_rng(22 + bits)
+    x = (rng.standard_normal((100, 32)) * np.exp(rng.uniform(-3, 3, (100, 1)))).astype(np.float32)
+    packed, sc = T4.quantize(x, bits)
+    assert packed.shape == (100, 32 * bits // 8) and sc.shape == (100, 2)
+    idx = T4.unpack_indices(packed, bits).reshape(100, 2, 16)
+    g = x.reshape(100, 2, 16).astype(np.float64)
+    lv = T4.codebook_f32(bits).astype(np.float64)
+    rms = np.sqrt(np.mean(g ** 2, axis=-1, keepdims=True))
+    brute = np.argmin(np.abs((g / rms)[..., None] - lv), axis=-1)
+    assert np.mean(brute == idx) > 0.999 and np.all(np.abs(brute - idx) <= 1)
+    s = np.linalg.norm(g, axis=-1) / np.linalg.norm(lv[idx], axis=-1)
+    err = np.maximum(s * 2.0 ** -4, 2.0 ** -10) * 1.001
+    assert np.all(np.abs(T8.e4m3_decode(sc) - s) <= err)
+
+
+@pytest.mark.parametrize("fmt", ["turbo4", "turbo3", "turbo2", "bf16k_turbo3v", "bf16k_turbo2v"])
+def test_lloyd_max_format_attention_equals_sdpa(fmt):
+    kq, bits = T4.FORMATS[fmt]
+    rng = np.random.default_rng(31)
+    Hq, Hkv, D, L = 8, 2, 64, 23
+    nb = D * bits // 8
+    kv = {"v": rng.integers(0, 256, (L + 2, Hkv, nb), dtype=np.uint8),
+          "v_scales": T8.e4m3_encode(rng.uniform(0.05, 2.0, (L + 2, Hkv, D // 16)).astype(np.float32))}
+    if kq:
+        kv["k"] = rng.integers(0, 256, (L + 2, Hkv, nb), dtype=np.uint8)
+        kv["k_scales"] = T8.e4m3_encode(rng.uniform(0.05, 2.0, (L + 2, Hkv, D // 16)).astype(np.float32))
+        K = T8.wht(T4.dequantize(kv["k"][:L], kv["k_scales"][:L], bits))
+    else:
+        kv["k"] = O.f64_to_bf16(rng.standard_normal((L + 2, Hkv, D)))
+        K = O.bf16_to_f64(kv["k"][:L])
+    q = rng.standard_normal((Hq, D)) * 3
+    got = T4.attention_decode(fmt, q, kv, L)
+    V = T8.wht(T4.dequantize(kv["v"][:L], kv["v_scales"][:L], bits))
+    Kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+    Vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, None, :], Kt, Vt, scale=1 / math.sqrt(D))[:, 0, :].numpy()
+    assert np.allclose(got, ref, rtol=1e-10, atol=1e-12)
 
 
 def test_turbo4v_attention_equals_sdpa_on_dequantised_values():
