@@ -6,7 +6,7 @@ attention over a bf16 KV cache at ~8192 tokens), final RMSNorm, int8 lm_head ove
 248 320 tokens, greedy argmax and the next token's embedding, all on the device
 from one replayed HIP graph.  Prints one JSON line (rank 0).
 
-    python bench.py [--gpus 1] [--steps 128] [--warmup 8] [--ctx 8192] [--kv bf16|turbo8|bf16k_turbo4v]
+    python bench.py [--gpus 1] [--steps 128] [--warmup 8] [--ctx 8192] [--kv FORMAT]
 """
 import argparse
 import hashlib
@@ -136,9 +136,10 @@ def cpu_baseline(cfg, w, sample_note, kv="bf16"):
     if kv == "turbo8":
         from oracle import turbo8 as T8
         T8.forward_full_attention_turbo8(cfg, w["layers"][fi], kvd, inv, x, w["ctx"])
-    elif kv == "bf16k_turbo4v":
-        from oracle import turbo_lm as T4
-        T4.forward_full_attention_bf16k_turbo4v(cfg, w["layers"][fi], kvd, inv, x, w["ctx"])
+    elif kv != "bf16":
+        from oracle import turbo_lm as TL
+        kvd.pop("kv_dtype", None)
+        TL.forward_full_attention(kv, cfg, w["layers"][fi], kvd, inv, x, w["ctx"])
     else:
         O.forward_full_attention(cfg, w["layers"][fi], w["kvs"][fi], inv, x, w["ctx"])
     t_full = time.perf_counter() - t0
@@ -162,7 +163,8 @@ def main():
     ap.add_argument("--ctx", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dominant-rounds", type=int, default=4)
-    ap.add_argument("--kv", choices=["bf16", "turbo8", "bf16k_turbo4v"], default="bf16",
+    ap.add_argument("--kv", choices=["bf16", "turbo8", "turbo4", "turbo3", "turbo2", "bf16k_turbo4v",
+                                     "bf16k_turbo3v", "bf16k_turbo2v"], default="bf16",
                     help="KV cache format of the full-attention layers")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -191,7 +193,13 @@ def main():
                            progress=lambda i: log(f"  layer {i} generated") if i % 8 == 7 else None,
                            kv=args.kv)
     # bytes per K and V element, averaged over the two
-    kv_bytes = {"bf16": 2.0, "turbo8": 1.0 + 2.0 / 16, "bf16k_turbo4v": (2.0 + 0.5 + 1.0 / 16) / 2}[args.kv]
+    lm_bits = {"turbo4": 4, "turbo3": 3, "turbo2": 2, "bf16k_turbo4v": 4, "bf16k_turbo3v": 3,
+               "bf16k_turbo2v": 2}
+    if args.kv in lm_bits:
+        side = lm_bits[args.kv] / 8 + 1.0 / 16
+        kv_bytes = (side + (2.0 if args.kv.startswith("bf16k") else side)) / 2
+    else:
+        kv_bytes = {"bf16": 2.0, "turbo8": 1.0 + 2.0 / 16}[args.kv]
     cfg, kinds = w["cfg"], w["kinds"]
     log(f"generated in {time.time() - t0:.1f}s; uploading")
     st = rt.DecodeStack(cfg, kinds, w["layers"], w["states"], w["kvs"], w["embed"],
@@ -275,8 +283,11 @@ def main():
     log(f"device copy of {copy_bytes >> 20} MiB: {copy_gbs:.0f} GB/s (read + write)")
     traffic = measured_traffic()
 
-    kv_desc = {"bf16": "bf16", "turbo8": "Turbo8 (WHT-rotated E4M3 + bf16 scale per 16)",
-               "bf16k_turbo4v": "bf16 K + Turbo4 V (WHT-rotated 4-bit Lloyd-Max + E4M3 scale per 16)"}[args.kv]
+    kv_desc = {"bf16": "bf16", "turbo8": "Turbo8 (WHT-rotated E4M3 + bf16 scale per 16)"}.get(args.kv)
+    if kv_desc is None:
+        b = lm_bits[args.kv]
+        lm = f"Turbo{b} (WHT-rotated {b}-bit Lloyd-Max + E4M3 scale per 16)"
+        kv_desc = f"bf16 K + {lm} V" if args.kv.startswith("bf16k") else f"{lm} K and V"
     result = {
         "metric": METRIC,
         "value": round(tok_s, 2),

@@ -28,7 +28,12 @@ KV_DTYPES = ["bf16", "turbo8", "turbo4", "turbo3", "turbo2", "bf16k_turbo4v", "b
              "bf16k_turbo2v"]
 Q35_KV_BF16 = 0
 Q35_KV_TURBO8 = 1
+Q35_KV_TURBO4 = 2
+Q35_KV_TURBO3 = 3
+Q35_KV_TURBO2 = 4
 Q35_KV_BF16K_TURBO4V = 5
+Q35_KV_BF16K_TURBO3V = 6
+Q35_KV_BF16K_TURBO2V = 7
 
 # Every symbol include/q35decode.h declares.
 EXPORTS = [
@@ -40,7 +45,7 @@ EXPORTS = [
     "q35_decode_workspace_bytes", "q35_decode_plan_create", "q35_decode_plan_release",
     "q35_decode_step", "q35_decode_check", "q35_decode_layer_input", "q35_decode_stage_layout",
     "q35_decode_stage_times", "q35_turbo8_quantize", "q35_fp8_e4m3_table",
-    "q35_turbo4_codebook", "q35_turbo4_quantize",
+    "q35_turbo_codebook", "q35_turbo_quantize",
 ]
 
 Q35_LAYER_LINEAR = 0
@@ -184,8 +189,8 @@ def lib():
             "q35_decode_stage_times": (st, [vp, P(C.c_uint64), u32, P(C.c_uint64)]),
             "q35_turbo8_quantize": (st, [vp, vp, u32, vp, vp, vp]),
             "q35_fp8_e4m3_table": (st, [vp, vp, vp]),
-            "q35_turbo4_codebook": (st, [vp, P(C.c_float)]),
-            "q35_turbo4_quantize": (st, [vp, vp, u32, vp, vp, vp]),
+            "q35_turbo_codebook": (st, [vp, u32, P(C.c_float)]),
+            "q35_turbo_quantize": (st, [vp, u32, vp, u32, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -364,13 +369,13 @@ def q35_fp8_e4m3_table(kernels, out, stream) -> None:
     _check(lib().q35_fp8_e4m3_table(kernels, out, stream))
 
 
-def q35_turbo4_codebook(kernels):
-    """The library's Turbo4 codebook (16 floats, ascending) as a NumPy array."""
+def q35_turbo_codebook(kernels, bits: int):
+    """The library's b-bit Lloyd-Max codebook (2^bits floats, ascending) as a NumPy array."""
     import numpy as np
     out = (C.c_float * 16)()
-    _check(lib().q35_turbo4_codebook(kernels, out))
-    return np.array(out[:], dtype=np.float32)
+    _check(lib().q35_turbo_codebook(kernels, bits, out))
+    return np.array(out[:1 << bits], dtype=np.float32)
 
 
-def q35_turbo4_quantize(kernels, x, n: int, packed, scales, stream) -> None:
-    _check(lib().q35_turbo4_quantize(kernels, x, n, packed, scales, stream))
+def q35_turbo_quantize(kernels, bits: int, x, n: int, packed, scales, stream) -> None:
+    _check(lib().q35_turbo_quantize(kernels, bits, x, n, packed, scales, stream))

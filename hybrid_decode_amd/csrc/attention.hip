@@ -182,6 +182,44 @@ Q35_DEV void wht_regs(float (&x)[D / 64], int lane) {
     stage(std::integral_constant<int, 32>{});
 }
 
+// Lloyd-Max row formats: index bits of a format (0: not one), and whether K
+// is stored in it too.
+constexpr int lm_bits(int f) {
+    return (f == Q35_KV_TURBO4 || f == Q35_KV_BF16K_TURBO4V)   ? 4
+           : (f == Q35_KV_TURBO3 || f == Q35_KV_BF16K_TURBO3V) ? 3
+           : (f == Q35_KV_TURBO2 || f == Q35_KV_BF16K_TURBO2V) ? 2
+                                                               : 0;
+}
+constexpr bool lm_k(int f) { return f == Q35_KV_TURBO4 || f == Q35_KV_TURBO3 || f == Q35_KV_TURBO2; }
+
+// Quantises one group of 16 rotated values into the cache (2 * BITS bytes of
+// indices at group index gi, one E4M3 scale byte) and writes the dequantised
+// values, as stored, to out[16].
+template <int BITS>
+Q35_DEV void lm_append_group(const float v[16], const float* levels, const float* lut, uint8_t* data,
+                             uint8_t* scales, size_t gi, float* out) {
+    uint32_t idx[2];
+    const uint32_t sc = lm_quantize16<BITS>(v, levels, idx);
+    if constexpr (BITS == 4) {
+        reinterpret_cast<uint2*>(data)[gi] = make_uint2(idx[0], idx[1]);
+    } else if constexpr (BITS == 2) {
+        reinterpret_cast<uint32_t*>(data)[gi] = idx[0];
+    } else {  // 6 bytes, 2-byte aligned
+        uint16_t* d16 = reinterpret_cast<uint16_t*>(data + gi * 6);
+        d16[0] = (uint16_t)idx[0];
+        d16[1] = (uint16_t)(idx[0] >> 16);
+        d16[2] = (uint16_t)idx[1];
+    }
+    scales[gi] = (uint8_t)sc;
+    const float s = e4m3x2_to_f32<false>(sc).x;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int b0 = BITS * e;  // bit offset in the group's stream (idx[0]: bits 0-31)
+        const uint64_t w = ((uint64_t)idx[1] << 32) | idx[0];
+        out[e] = s * lut[(uint32_t)(w >> b0) & ((1u << BITS) - 1u)];
+    }
+}
+
 // T8: Turbo8 cache (E4M3 codes [capacity, Hkv, D] with bf16 scales per 16
 // [capacity, Hkv, D/16], in the orthonormal Walsh-Hadamard basis of a head).
 // The prologue also rotates the G query heads and the new k and v, the block
@@ -192,12 +230,16 @@ Q35_DEV void wht_regs(float (&x)[D / 64], int lane) {
 template <int D, int G, int F>
 __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     static_assert(D <= kNT && D % 32 == 0, "one new-v element per thread; merge blocks of 32 dims");
-    // row formats: F = Q35_KV_BF16, Q35_KV_TURBO8 (K and V rotated, E4M3 with a
-    // bf16 scale per 16) or Q35_KV_BF16K_TURBO4V (K bf16 unrotated, V rotated
-    // 4-bit codebook indices with an E4M3 scale per 16)
+    // row formats (F = a Q35_KV_* value): bf16; Turbo8 (K and V rotated, E4M3
+    // with a bf16 scale per 16); the Lloyd-Max formats (LMB-bit codebook
+    // indices with an E4M3 scale per 16, rotated): K and V for Turbo4/3/2, V
+    // only (K bf16, not rotated) for Bf16K + Turbo4V/3V/2V
     constexpr bool T8 = F == Q35_KV_TURBO8;
-    constexpr bool V4 = F == Q35_KV_BF16K_TURBO4V;
-    constexpr bool ROTV = T8 || V4;
+    constexpr int LMB = lm_bits(F);
+    constexpr bool LMK = lm_k(F);      // K in a Lloyd-Max format
+    constexpr bool LMV = LMB > 0;      // V in a Lloyd-Max format
+    constexpr bool ROTQK = T8 || LMK;  // query and key rotated
+    constexpr bool ROTV = T8 || LMV;
     using Geo = AGeo<D>;
     constexpr int LPR = Geo::LPR, RPI = Geo::RPI, B = Geo::B;
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
@@ -214,7 +256,7 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     __shared__ float mls[RPI][2 * G];  // per-slot (max, sum)
     __shared__ float red[(G < 4 ? G : 4) * RPI * D];  // per-slot outputs of up to 4 heads
     __shared__ float ov[ROTV ? G * D : 1];  // rotated V: merged accumulators, rotated back
-    __shared__ float lut[V4 ? 16 : 1];      // Turbo4: the codebook levels
+    __shared__ float lut[LMV ? 16 : 1];     // Lloyd-Max formats: the codebook levels
 
     const int32_t pos = attn_pos(a);
     if (pos < 0 || (uint32_t)pos >= a.capacity) return;
@@ -228,10 +270,14 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
 
     // ---------------- first batch of K/V loads, in flight during the prologue
     // bytes of one token's row: K data, V data, K scales, V scales
-    const uint32_t krow_bytes = a.hkv * D * (T8 ? 1u : 2u);
-    const uint32_t vrow_bytes = a.hkv * D * (T8 ? 2u : V4 ? 1u : 4u) / 2u;
-    const uint32_t ksrow_bytes = T8 ? a.hkv * (D / 16) * 2u : 0u;
-    const uint32_t vsrow_bytes = a.hkv * (D / 16) * (T8 ? 2u : V4 ? 1u : 0u);
+    // bits per element of K and V data, bytes per group scale of K and V
+    constexpr uint32_t KBITS = T8 ? 8u : LMK ? (uint32_t)LMB : 16u;
+    constexpr uint32_t VBITS = T8 ? 8u : LMV ? (uint32_t)LMB : 16u;
+    constexpr uint32_t KSB = T8 ? 2u : LMK ? 1u : 0u, VSB = T8 ? 2u : LMV ? 1u : 0u;
+    const uint32_t krow_bytes = a.hkv * D * KBITS / 8u;
+    const uint32_t vrow_bytes = a.hkv * D * VBITS / 8u;
+    const uint32_t ksrow_bytes = a.hkv * (D / 16) * KSB;
+    const uint32_t vsrow_bytes = a.hkv * (D / 16) * VSB;
     const uint32_t nrows = t1 - t0;
 
     // ---------------- the prologue's own loads go out first (vector loads
@@ -251,16 +297,28 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
 
     const size_t row0 = ((size_t)t0 * a.hkv + g) * D;  // element offset of the chunk's first row
     const size_t srow0 = ((size_t)t0 * a.hkv + g) * (D / 16);
-    const auto rk = rsrc(reinterpret_cast<const uint8_t*>(a.kc) + row0 * (T8 ? 1 : 2), nrows * krow_bytes);
-    const auto rv = rsrc(reinterpret_cast<const uint8_t*>(a.vc) + row0 * (T8 ? 2 : V4 ? 1 : 4) / 2,
-                         nrows * vrow_bytes);
-    const auto rks = rsrc(reinterpret_cast<const uint8_t*>(a.ks) + srow0 * 2, nrows * ksrow_bytes);
-    const auto rvs = rsrc(reinterpret_cast<const uint8_t*>(a.vs) + srow0 * (T8 ? 2 : 1), nrows * vsrow_bytes);
+    const auto rk = rsrc(reinterpret_cast<const uint8_t*>(a.kc) + row0 * KBITS / 8, nrows * krow_bytes);
+    const auto rv = rsrc(reinterpret_cast<const uint8_t*>(a.vc) + row0 * VBITS / 8, nrows * vrow_bytes);
+    const auto rks = rsrc(reinterpret_cast<const uint8_t*>(a.ks) + srow0 * KSB, nrows * ksrow_bytes);
+    const auto rvs = rsrc(reinterpret_cast<const uint8_t*>(a.vs) + srow0 * VSB, nrows * vsrow_bytes);
     // two batches in flight: the next batch's rows load while this one
     // computes (three, or smaller batches at higher occupancy, measured no
     // faster).  A lane holds 8 elements of a row.
-    using KT = std::conditional_t<T8, uint2, uint4>;
-    using VT = std::conditional_t<T8, uint2, std::conditional_t<V4, uint32_t, uint4>>;
+    using KT = std::conditional_t<T8, uint2, std::conditional_t<LMK, uint32_t, uint4>>;
+    using VT = std::conditional_t<T8, uint2, std::conditional_t<LMV, uint32_t, uint4>>;
+    // a lane's 8 Lloyd-Max indices: LMB bytes at byte LMB * j of the row (3
+    // bytes for 3-bit indices: two aligned words and a byte shift)
+    auto load_lm = [&](__amdgpu_buffer_rsrc_t rr, uint32_t off) -> uint32_t {
+        if constexpr (LMB == 4) {
+            return __builtin_amdgcn_raw_buffer_load_b32(rr, off, 0, kAuxStream);
+        } else if constexpr (LMB == 2) {
+            return __builtin_amdgcn_raw_buffer_load_b16(rr, off, 0, kAuxStream);
+        } else {
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(rr, off & ~3u, 0, kAuxStream);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(rr, (off & ~3u) + 4u, 0, kAuxStream);
+            return __builtin_amdgcn_alignbyte(hi, lo, off & 3u) & 0xFFFFFFu;
+        }
+    };
     KT kr[2][kUnroll];
     VT vr[2][kUnroll];
     uint32_t ksr[2][kUnroll], vsr[2][kUnroll];  // the lane's group scale, raw bits
@@ -274,6 +332,9 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
             if constexpr (T8) {
                 kd[u] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, r * krow_bytes + 8u * j, 0, kAuxStream));
                 ksd[u] = __builtin_amdgcn_raw_buffer_load_b16(rks, r * ksrow_bytes + 2u * (j / 2), 0, kAuxStream);
+            } else if constexpr (LMK) {
+                kd[u] = load_lm(rk, r * krow_bytes + (uint32_t)LMB * j);
+                ksd[u] = __builtin_amdgcn_raw_buffer_load_b8(rks, r * ksrow_bytes + (j / 2), 0, kAuxStream);
             } else {
                 kd[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, r * krow_bytes + 16u * j, 0, kAuxStream));
                 ksd[u] = 0;
@@ -281,8 +342,8 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
             if constexpr (T8) {
                 vd[u] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, r * vrow_bytes + 8u * j, 0, kAuxStream));
                 vsd[u] = __builtin_amdgcn_raw_buffer_load_b16(rvs, r * vsrow_bytes + 2u * (j / 2), 0, kAuxStream);
-            } else if constexpr (V4) {
-                vd[u] = __builtin_amdgcn_raw_buffer_load_b32(rv, r * vrow_bytes + 4u * j, 0, kAuxStream);
+            } else if constexpr (LMV) {
+                vd[u] = load_lm(rv, r * vrow_bytes + (uint32_t)LMB * j);
                 vsd[u] = __builtin_amdgcn_raw_buffer_load_b8(rvs, r * vsrow_bytes + (j / 2), 0, kAuxStream);
             } else {
                 vd[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, r * vrow_bytes + 16u * j, 0, kAuxStream));
@@ -298,8 +359,8 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     for (int r = 0; r < PQ; ++r)
         if (t + kNT * r < (G + 1) * D) qs[t + kNT * r] = qv[r];
     if (t < D) vn[t] = ROTV ? vnew : bf16_to_f32(f32_to_bf16(vnew));
-    if constexpr (V4)
-        if (t < 16) lut[t] = a.t4_levels[t];
+    if constexpr (LMV)
+        if (t < 16) lut[t] = a.lm_levels[t];
     if (t < (int)a.rotary / 2) {
         float sn, cs;
         sincosf((float)rope_pos * invf, &sn, &cs);
@@ -332,7 +393,7 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     __syncthreads();
     if (a.q_norm_out && c == 0)
         for (int e = t; e < G * D; e += kNT) a.q_norm_out[(size_t)g * G * D + e] = qs[e];
-    if constexpr (T8) {
+    if constexpr (ROTQK) {
         if (has_new && a.k_norm_out)
             for (int d = t; d < D; d += kNT) a.k_norm_out[g * D + d] = qs[G * D + d];
         __syncthreads();  // the taps read qs before the rotation rewrites it
@@ -357,19 +418,25 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
                 float v16[16];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) v16[e] = src[e];
-                uint32_t cw[4];
-                const uint32_t sb = turbo8_quantize16(v16, cw);
-                uint8_t* dst = reinterpret_cast<uint8_t*>(side ? a.vc : a.kc) + ((size_t)pos * a.hkv + g) * D + 16 * grp;
-                *reinterpret_cast<uint4*>(dst) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-                (side ? a.vs : a.ks)[((size_t)pos * a.hkv + g) * (D / 16) + grp] = (uint16_t)sb;
-                const float sc = bf16_to_f32(sb);
+                const size_t gi = ((size_t)pos * a.hkv + g) * (D / 16) + grp;  // group index in the cache
+                if constexpr (T8) {
+                    uint32_t cw[4];
+                    const uint32_t sb = turbo8_quantize16(v16, cw);
+                    uint8_t* dst = reinterpret_cast<uint8_t*>(side ? a.vc : a.kc) + gi * 16;
+                    *reinterpret_cast<uint4*>(dst) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+                    (side ? a.vs : a.ks)[gi] = (uint16_t)sb;
+                    const float sc = bf16_to_f32(sb);
 #pragma unroll
-                for (int w4 = 0; w4 < 4; ++w4) {
-                    const q35_float2_t lo = e4m3x2_to_f32<false>(cw[w4]), hi = e4m3x2_to_f32<true>(cw[w4]);
-                    src[4 * w4] = lo.x * sc;
-                    src[4 * w4 + 1] = lo.y * sc;
-                    src[4 * w4 + 2] = hi.x * sc;
-                    src[4 * w4 + 3] = hi.y * sc;
+                    for (int w4 = 0; w4 < 4; ++w4) {
+                        const q35_float2_t lo = e4m3x2_to_f32<false>(cw[w4]), hi = e4m3x2_to_f32<true>(cw[w4]);
+                        src[4 * w4] = lo.x * sc;
+                        src[4 * w4 + 1] = lo.y * sc;
+                        src[4 * w4 + 2] = hi.x * sc;
+                        src[4 * w4 + 3] = hi.y * sc;
+                    }
+                } else {
+                    lm_append_group<LMB>(v16, a.lm_levels, lut, reinterpret_cast<uint8_t*>(side ? a.vc : a.kc),
+                                         reinterpret_cast<uint8_t*>(side ? a.vs : a.ks), gi, src);
                 }
             }
             __syncthreads();
@@ -381,11 +448,11 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
         for (int d = t; d < D; d += kNT) {
             const uint32_t kb = f32_to_bf16(qs[G * D + d]);
             krow[d] = (uint16_t)kb;
-            if constexpr (!V4)  // vn is already bf16-exact
+            if constexpr (!LMV)  // vn is already bf16-exact
                 a.vc[((size_t)pos * a.hkv + g) * D + d] = (uint16_t)f32_to_bf16(vn[d]);
             qs[G * D + d] = bf16_to_f32(kb);  // attend to the row as stored
         }
-        if constexpr (V4) {
+        if constexpr (LMV) {
             // the new v: rotated by wave 0, then quantised in groups of 16 (one
             // thread each); the block attends to the dequantised row, as stored
             if (wid == 0) {
@@ -401,14 +468,9 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
                 float v16[16];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) v16[e] = vn[16 * t + e];
-                uint32_t idx[2];
-                const uint32_t sc = turbo4_quantize16(v16, a.t4_levels, idx);
-                const size_t gi = ((size_t)pos * a.hkv + g) * (D / 16) + t;
-                reinterpret_cast<uint2*>(a.vc)[gi] = make_uint2(idx[0], idx[1]);
-                reinterpret_cast<uint8_t*>(a.vs)[gi] = (uint8_t)sc;
-                const float s = e4m3x2_to_f32<false>(sc).x;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) vn[16 * t + e] = s * lut[(idx[e / 8] >> (4 * (e % 8))) & 0xFu];
+                lm_append_group<LMB>(v16, a.lm_levels, lut, reinterpret_cast<uint8_t*>(a.vc),
+                                     reinterpret_cast<uint8_t*>(a.vs), ((size_t)pos * a.hkv + g) * (D / 16) + t,
+                                     vn + 16 * t);
             }
         }
         __syncthreads();
@@ -423,13 +485,13 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     const int hl = head_of_lane<G>(j);
     // bf16 keys: q as a bf16 pair (hi + lo, 16 significant bits) for the
     // two-element bf16 dot instruction, so the keys need no unpacking
-    using Q2 = std::conditional_t<T8, float, uint32_t>;
-    constexpr int QN = T8 ? 8 : 4;
-    Q2 qh[G][QN], ql[G][T8 ? 1 : 4];
+    using Q2 = std::conditional_t<ROTQK, float, uint32_t>;
+    constexpr int QN = ROTQK ? 8 : 4;
+    Q2 qh[G][QN], ql[G][ROTQK ? 1 : 4];
 #pragma unroll
     for (int p = 0; p < G; ++p) {
         const float* qp = qs + (p ^ hl) * D + 8 * j;
-        if constexpr (T8) {
+        if constexpr (ROTQK) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) qh[p][e] = qp[e];
         } else {
@@ -469,24 +531,28 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     auto unpack_v = [&](const VT& w, float v[8]) {
         if constexpr (T8) {
             unpack_e4m3x8(w, v);
-        } else if constexpr (V4) {
+        } else if constexpr (LMV) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = lut[(w >> (4 * e)) & 0xFu];
+            for (int e = 0; e < 8; ++e) v[e] = lut[(w >> (LMB * e)) & ((1u << LMB) - 1u)];
         } else {
             unpack8(w, v);
         }
     };
     auto vscale_of = [](uint32_t bits) {
         if constexpr (T8) return bf16_to_f32(bits & 0xFFFFu);
-        else if constexpr (V4) return e4m3x2_to_f32<false>(bits & 0xFFu).x;
+        else if constexpr (LMV) return e4m3x2_to_f32<false>(bits & 0xFFu).x;
         else return 1.0f;
     };
     // one row's score for head hl from the lane's 8 key elements
     auto score = [&](const KT& w, float kscale) {
         float d[G];
-        if constexpr (T8) {
+        if constexpr (ROTQK) {
             float kv[8];
-            unpack_e4m3x8(w, kv);
+            if constexpr (T8)
+                unpack_e4m3x8(w, kv);
+            else
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kv[e] = lut[(w >> (LMB * e)) & ((1u << LMB) - 1u)];
 #pragma unroll
             for (int p = 0; p < G; ++p) {
                 float x = 0.f;
@@ -558,7 +624,9 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const uint32_t tt = tb + u * RPI + rs;
-            const float r = score(kd[u], T8 ? bf16_to_f32(ksd[u] & 0xFFFFu) : 1.0f);
+            const float r = score(kd[u], T8    ? bf16_to_f32(ksd[u] & 0xFFFFu)
+                                         : LMK ? e4m3x2_to_f32<false>(ksd[u] & 0xFFu).x
+                                               : 1.0f);
             s[u] = (tt < t1 && tt != (uint32_t)pos) ? r : -INFINITY;
         }
         float mx = m;
@@ -728,17 +796,26 @@ __global__ __launch_bounds__(kNT) void attn_merge_kernel(AttnArgs a) {
     }
 }
 
+template <int D, int G, int F>
+void launch_partial(const AttnArgs& a, uint32_t grid_chunks, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_partial_kernel<D, G, F>), dim3(grid_chunks, a.hkv), dim3(kNT), 0, stream, a);
+}
+
+#define Q35_KV_FORMATS(X)                                                                          \
+    X(Q35_KV_BF16) X(Q35_KV_TURBO8) X(Q35_KV_TURBO4) X(Q35_KV_TURBO3) X(Q35_KV_TURBO2)             \
+    X(Q35_KV_BF16K_TURBO4V) X(Q35_KV_BF16K_TURBO3V) X(Q35_KV_BF16K_TURBO2V)
+
 template <int D, int G>
 hipError_t launch_t(const AttnArgs& a, uint32_t grid_chunks, uint32_t fmt, hipStream_t stream) {
-    if (fmt == Q35_KV_TURBO8)
-        hipLaunchKernelGGL((attn_partial_kernel<D, G, Q35_KV_TURBO8>), dim3(grid_chunks, a.hkv), dim3(kNT), 0, stream, a);
-    else if (fmt == Q35_KV_BF16K_TURBO4V)
-        hipLaunchKernelGGL((attn_partial_kernel<D, G, Q35_KV_BF16K_TURBO4V>), dim3(grid_chunks, a.hkv), dim3(kNT), 0,
-                           stream, a);
-    else if (fmt == Q35_KV_BF16)
-        hipLaunchKernelGGL((attn_partial_kernel<D, G, Q35_KV_BF16>), dim3(grid_chunks, a.hkv), dim3(kNT), 0, stream, a);
-    else
-        return hipErrorInvalidValue;
+    bool known = false;
+#define X(FF)                                                   \
+    if (fmt == FF) {                                            \
+        launch_partial<D, G, FF>(a, grid_chunks, stream);       \
+        known = true;                                           \
+    }
+    Q35_KV_FORMATS(X)
+#undef X
+    if (!known) return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_merge_kernel<D, G>), dim3(a.hq, D / kMergeDims), dim3(kNT),
@@ -760,18 +837,21 @@ __global__ __launch_bounds__(256) void turbo8_quantize_kernel(const float* x, ui
     *reinterpret_cast<uint4*>(codes + 16u * gi) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
 }
 
-// Turbo4 group quantiser over a plain vector (kernel-level export): one thread
-// per group of 16.
-__global__ __launch_bounds__(256) void turbo4_quantize_kernel(const float* x, uint32_t groups, Turbo4Levels lv,
-                                                              uint8_t* packed, uint8_t* scales) {
+// Lloyd-Max group quantiser over a plain vector (kernel-level export): one
+// thread per group of 16; the levels go to LDS for the dequantised copy the
+// append path also writes (not kept here).
+template <int BITS>
+__global__ __launch_bounds__(256) void lm_quantize_kernel(const float* x, uint32_t groups, LmLevels lv,
+                                                          uint8_t* packed, uint8_t* scales) {
+    __shared__ float lut[16];
+    if (threadIdx.x < 16) lut[threadIdx.x] = lv.v[threadIdx.x];
+    __syncthreads();
     const uint32_t gi = blockIdx.x * 256u + threadIdx.x;
     if (gi >= groups) return;
-    float v[16];
+    float v[16], out[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) v[e] = x[16u * gi + e];
-    uint32_t idx[2];
-    scales[gi] = (uint8_t)turbo4_quantize16(v, lv.v, idx);
-    reinterpret_cast<uint2*>(packed)[gi] = make_uint2(idx[0], idx[1]);
+    lm_append_group<BITS>(v, lv.v, lut, packed, scales, gi, out);
 }
 
 // Every E4M3 code through the decoder the attention loop uses (kernel-level export).
@@ -809,13 +889,18 @@ hipError_t attn_launch(uint32_t head_dim, uint32_t group, const AttnArgs& a, uin
     return hipErrorInvalidValue;
 }
 
+template <int D, int G>
+const void* partial_ptr(uint32_t fmt) {
+#define X(FF) \
+    if (fmt == FF) return (const void*)&attn_partial_kernel<D, G, FF>;
+    Q35_KV_FORMATS(X)
+#undef X
+    return nullptr;
+}
+
 const void* attn_kernel_ptr(uint32_t head_dim, uint32_t group, uint32_t kv_dtype) {
-#define X(DD, GG)                                                                              \
-    if (head_dim == DD && group == GG)                                                         \
-        return kv_dtype == Q35_KV_TURBO8          ? (const void*)&attn_partial_kernel<DD, GG, Q35_KV_TURBO8> \
-               : kv_dtype == Q35_KV_BF16K_TURBO4V ? (const void*)&attn_partial_kernel<DD, GG, Q35_KV_BF16K_TURBO4V> \
-               : kv_dtype == Q35_KV_BF16          ? (const void*)&attn_partial_kernel<DD, GG, Q35_KV_BF16> \
-                                                  : nullptr;
+#define X(DD, GG) \
+    if (head_dim == DD && group == GG) return partial_ptr<DD, GG>(kv_dtype);
     Q35_ATTN_SHAPES(X)
 #undef X
     return nullptr;
@@ -838,12 +923,19 @@ hipError_t turbo8_quantize_launch(const float* x, uint32_t n, uint8_t* codes, ui
     return hipGetLastError();
 }
 
-hipError_t turbo4_quantize_launch(const float* x, uint32_t n, const Turbo4Levels& levels, uint8_t* packed,
-                                  uint8_t* scales, hipStream_t stream) {
+hipError_t lm_quantize_launch(uint32_t bits, const float* x, uint32_t n, const LmLevels& levels, uint8_t* packed,
+                              uint8_t* scales, hipStream_t stream) {
     const uint32_t groups = n / 16;
     if (groups == 0) return hipSuccess;
-    hipLaunchKernelGGL(turbo4_quantize_kernel, dim3((groups + 255) / 256), dim3(256), 0, stream, x, groups, levels,
-                       packed, scales);
+    const dim3 grid((groups + 255) / 256), block(256);
+    if (bits == 4)
+        hipLaunchKernelGGL(lm_quantize_kernel<4>, grid, block, 0, stream, x, groups, levels, packed, scales);
+    else if (bits == 3)
+        hipLaunchKernelGGL(lm_quantize_kernel<3>, grid, block, 0, stream, x, groups, levels, packed, scales);
+    else if (bits == 2)
+        hipLaunchKernelGGL(lm_quantize_kernel<2>, grid, block, 0, stream, x, groups, levels, packed, scales);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

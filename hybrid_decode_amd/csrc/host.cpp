@@ -19,7 +19,7 @@ using namespace q35;
 struct Qwen35Kernels {
     int device;
     int num_cu;
-    q35::Turbo4Levels t4;  // the Turbo4 codebook (computed at resolve)
+    q35::LmLevels lm[5];  // Lloyd-Max codebooks of 2, 3 and 4 bits (computed at resolve)
 };
 
 namespace {
@@ -225,9 +225,9 @@ q35_status check_full_layer(const Qwen35ForwardConfig& c, const FullAttentionLay
     return Q35_OK;
 }
 
-// The Turbo4 codebook (mod.rs: the Turbo4 variant's Lloyd-Max indices; the
-// level values are not given there): the 16-level Lloyd-Max quantiser of the
-// standard normal distribution.  Lloyd's iteration in double precision --
+// The Lloyd-Max codebooks (mod.rs: the Turbo4/3/2 variants' Lloyd-Max indices;
+// the level values are not given there): the n-level Lloyd-Max quantiser of
+// the standard normal distribution.  Lloyd's iteration in double precision --
 // thresholds halfway between adjacent levels, each level moved to the mean of
 // N(0, 1) over its cell -- until no level moves, then made exactly symmetric
 // and rounded to float.
@@ -244,37 +244,55 @@ double normal_cell_mean(double lo, double hi) {
     return (pdf(lo) - pdf(hi)) / mass;
 }
 
-void lloyd_max_normal16(float out[16]) {
-    double c[16];
-    for (int i = 0; i < 16; ++i) c[i] = -2.5 + 5.0 * i / 15.0;
+void lloyd_max_normal(int n, float* out) {  // n <= 16 levels; out[n..16) = 0
+    double c[16] = {};
+    for (int i = 0; i < n; ++i) c[i] = -2.5 + 5.0 * i / (n - 1);
     for (int it = 0; it < 20000; ++it) {
-        double nc[16], moved = 0.0;
-        for (int i = 0; i < 16; ++i) {
+        double nc[16] = {}, moved = 0.0;
+        for (int i = 0; i < n; ++i) {
             const double lo = i == 0 ? -INFINITY : 0.5 * (c[i - 1] + c[i]);
-            const double hi = i == 15 ? INFINITY : 0.5 * (c[i] + c[i + 1]);
+            const double hi = i == n - 1 ? INFINITY : 0.5 * (c[i] + c[i + 1]);
             nc[i] = normal_cell_mean(lo, hi);
             moved = std::max(moved, std::fabs(nc[i] - c[i]));
         }
         std::memcpy(c, nc, sizeof(c));
         if (moved < 1e-15) break;
     }
-    for (int i = 0; i < 16; ++i) out[i] = (float)((c[i] - c[15 - i]) / 2.0);
+    for (int i = 0; i < 16; ++i) out[i] = i < n ? (float)((c[i] - c[n - 1 - i]) / 2.0) : 0.0f;
 }
 
-// bf16 everywhere; Turbo8 (E4M3 codes + bf16 scales per 16) and Bf16K + Turbo4V
-// (bf16 K, 4-bit V indices + E4M3 scales per 16) in the per-layer forward.
+// Index bits of a Lloyd-Max KV format (0 for the others) and whether its K is
+// quantised as well.
+int kv_lm_bits(uint32_t dt) {
+    switch (dt) {
+        case Q35_KV_TURBO4: case Q35_KV_BF16K_TURBO4V: return 4;
+        case Q35_KV_TURBO3: case Q35_KV_BF16K_TURBO3V: return 3;
+        case Q35_KV_TURBO2: case Q35_KV_BF16K_TURBO2V: return 2;
+        default: return 0;
+    }
+}
+bool kv_lm_k(uint32_t dt) { return dt == Q35_KV_TURBO4 || dt == Q35_KV_TURBO3 || dt == Q35_KV_TURBO2; }
+
+// bf16 everywhere; in the per-layer forward also Turbo8 (E4M3 codes + bf16
+// scales per 16) and the Lloyd-Max formats (packed indices + E4M3 scale bytes
+// per 16; K too for the symmetric ones, K bf16 for Bf16K + TurboNV).
 q35_status check_kv(const LayerKvCache& kv, bool allow_quantised) {
-    if (kv.dtype == Q35_KV_TURBO8 && allow_quantised) {
-        Q35_TRY(need(kv.k_scales, "kv.k_scales"));
-        Q35_TRY(need(kv.v_scales, "kv.v_scales"));
-    } else if (kv.dtype == Q35_KV_BF16K_TURBO4V && allow_quantised) {
-        if (kv.k_scales) return fail(Q35_ERR_INVALID_ARG, "bf16k_turbo4v cache with a K scale buffer");
-        Q35_TRY(need(kv.v_scales, "kv.v_scales"));
-    } else if (kv.dtype == Q35_KV_BF16) {
+    if (kv.dtype == Q35_KV_BF16) {
         if (kv.k_scales || kv.v_scales) return fail(Q35_ERR_INVALID_ARG, "bf16 cache with scale buffers");
+    } else if (allow_quantised && kv.dtype <= Q35_KV_BF16K_TURBO2V) {
+        const bool k_quant = kv.dtype == Q35_KV_TURBO8 || kv_lm_k(kv.dtype);
+        if (k_quant) {
+            Q35_TRY(need(kv.k_scales, "kv.k_scales", false));
+        } else if (kv.k_scales) {
+            return fail(Q35_ERR_INVALID_ARG, "KV dtype %u keeps K in bf16: no K scale buffer", kv.dtype);
+        }
+        Q35_TRY(need(kv.v_scales, "kv.v_scales", false));
+        if (kv.dtype == Q35_KV_TURBO8 &&
+            ((reinterpret_cast<uintptr_t>(kv.k_scales) | reinterpret_cast<uintptr_t>(kv.v_scales)) & 1u))
+            return fail(Q35_ERR_INVALID_ARG, "turbo8 scales not 2-byte aligned");
     } else {
         return fail(Q35_ERR_UNSUPPORTED, "KV dtype %u is not implemented on this path (%s)", kv.dtype,
-                    allow_quantised ? "bf16 | turbo8 | bf16k_turbo4v" : "bf16");
+                    allow_quantised ? "bf16 | turbo8 | turbo4/3/2 | bf16k_turbo4v/3v/2v" : "bf16");
     }
     Q35_TRY(need(kv.k, "kv.k"));
     Q35_TRY(need(kv.v, "kv.v"));
@@ -452,7 +470,7 @@ q35_status q35_kernels_resolve(int device, Qwen35Kernels** out) {
     Qwen35Kernels* k = new Qwen35Kernels;
     k->device = device;
     k->num_cu = prop.multiProcessorCount;
-    lloyd_max_normal16(k->t4.v);
+    for (int bits = 2; bits <= 4; ++bits) lloyd_max_normal(1 << bits, k->lm[bits].v);
     *out = k;
     return ok();
 }
@@ -592,7 +610,7 @@ static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35Fo
         a.max_chunks = attn_max_chunks(c, kv->capacity);
         a.eps = c.rms_eps;
         a.scale = 1.0f / std::sqrt((float)c.head_dim);
-        std::memcpy(a.t4_levels, kernels->t4.v, sizeof(a.t4_levels));
+        if (kv_lm_bits(kv->dtype)) std::memcpy(a.lm_levels, kernels->lm[kv_lm_bits(kv->dtype)].v, sizeof(a.lm_levels));
         uint32_t grid;
         if (cache_pos >= 0) {
             a.host_pos = (int32_t)cache_pos;
@@ -862,23 +880,27 @@ q35_status q35_turbo8_quantize(const Qwen35Kernels* kernels, const float* x, uin
     return ok();
 }
 
-q35_status q35_turbo4_codebook(const Qwen35Kernels* kernels, float* levels) {
+q35_status q35_turbo_codebook(const Qwen35Kernels* kernels, uint32_t bits, float* levels) {
     Q35_TRY(check_kernels(kernels));
+    if (bits < 2 || bits > 4) return fail(Q35_ERR_INVALID_ARG, "bits = %u (2, 3 or 4)", bits);
     if (!levels) return fail(Q35_ERR_INVALID_ARG, "levels is NULL");
-    std::memcpy(levels, kernels->t4.v, 16 * sizeof(float));
+    std::memcpy(levels, kernels->lm[bits].v, (1u << bits) * sizeof(float));
     return ok();
 }
 
-q35_status q35_turbo4_quantize(const Qwen35Kernels* kernels, const float* x, uint32_t n, uint8_t* packed,
-                               uint8_t* scales, hipStream_t stream) {
+q35_status q35_turbo_quantize(const Qwen35Kernels* kernels, uint32_t bits, const float* x, uint32_t n,
+                              uint8_t* packed, uint8_t* scales, hipStream_t stream) {
     Q35_TRY(check_kernels(kernels));
+    if (bits < 2 || bits > 4) return fail(Q35_ERR_INVALID_ARG, "bits = %u (2, 3 or 4)", bits);
     if (n % 16) return fail(Q35_ERR_INVALID_ARG, "n = %u is not a multiple of 16", n);
     if (n == 0) return ok();
     Q35_TRY(need(x, "x"));
     Q35_TRY(need(packed, "packed", false));
-    if (reinterpret_cast<uintptr_t>(packed) & 7u) return fail(Q35_ERR_INVALID_ARG, "packed not 8-byte aligned");
+    const uintptr_t align = bits == 4 ? 8u : bits == 2 ? 4u : 2u;  // one group's indices
+    if (reinterpret_cast<uintptr_t>(packed) & (align - 1))
+        return fail(Q35_ERR_INVALID_ARG, "packed not %u-byte aligned", (unsigned)align);
     Q35_TRY(need(scales, "scales", false));
-    Q35_HIP(turbo4_quantize_launch(x, n, kernels->t4, packed, scales, stream), "turbo4 quantise");
+    Q35_HIP(lm_quantize_launch(bits, x, n, kernels->lm[bits], packed, scales, stream), "turbo quantise");
     return ok();
 }
 

@@ -98,35 +98,41 @@ Q35_DEV uint32_t turbo8_quantize16(const float v[16], uint32_t codes[4]) {
     return sb;
 }
 
-// Turbo4 group of 16 rotated values over a 16-level codebook (ascending):
-// each index is the number of thresholds (fp32 midpoints of adjacent levels)
-// below x / sigma, sigma = sqrt(sum(x^2) / 16) with the sum in double and
-// sigma in fp32 (the nearest level, ties to the lower); packed two per byte,
-// low nibble first, into idx[0] (elements 0-7) and idx[1] (8-15).  Returns
-// the E4M3 code of the scale ||x|| / ||levels[idx]|| (double, rounded to
-// fp32, then E4M3), which keeps the group's norm up to that rounding.  A zero
-// group: scale 0 and indices 0.
-Q35_DEV uint32_t turbo4_quantize16(const float v[16], const float* levels, uint32_t idx[2]) {
+// Lloyd-Max group of 16 rotated values over a 2^BITS-level codebook
+// (ascending): each index is the number of thresholds (fp32 midpoints of
+// adjacent levels) below x / sigma, sigma = sqrt(sum(x^2) / 16) with the sum in
+// double and sigma in fp32 (the nearest level, ties to the lower); packed as a
+// little-endian bit stream, element e at bits [BITS e, BITS e + BITS) of
+// idx[0] (bits 0-31) : idx[1] (bits 32-63).  Returns the E4M3 code of the
+// scale ||x|| / ||levels[idx]|| (double, rounded to fp32, then E4M3), which
+// keeps the group's norm up to that rounding.  A zero group: scale 0 and
+// indices 0.
+template <int BITS>
+Q35_DEV uint32_t lm_quantize16(const float v[16], const float* levels, uint32_t idx[2]) {
+    constexpr int NL = 1 << BITS;
     double ss = 0.0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) ss += (double)v[e] * (double)v[e];
     idx[0] = idx[1] = 0u;
     if (ss == 0.0) return 0u;
     const float sigma = sqrtf((float)ss / 16.0f);
-    float th[15];
+    float th[NL - 1];
 #pragma unroll
-    for (int k = 0; k < 15; ++k) th[k] = (levels[k] + levels[k + 1]) * 0.5f;
+    for (int k = 0; k < NL - 1; ++k) th[k] = (levels[k] + levels[k + 1]) * 0.5f;
     double cn = 0.0;
+    uint64_t w = 0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         const float y = v[e] / sigma;
         uint32_t n = 0;
 #pragma unroll
-        for (int k = 0; k < 15; ++k) n += y > th[k] ? 1u : 0u;
-        idx[e / 8] |= n << (4 * (e % 8));
+        for (int k = 0; k < NL - 1; ++k) n += y > th[k] ? 1u : 0u;
+        w |= (uint64_t)n << (BITS * e);
         const double l = levels[n];
         cn += l * l;
     }
+    idx[0] = (uint32_t)w;
+    idx[1] = (uint32_t)(w >> 32);
     return e4m3_encode((float)(sqrt(ss) / sqrt(cn)));
 }
 

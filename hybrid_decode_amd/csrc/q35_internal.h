@@ -149,8 +149,8 @@ struct AttnArgs {
     float* part_acc;         // workspace: [Hkv][max_chunks][G][D]
     float* part_ml;          // workspace: [Hkv][max_chunks][G][2]
     uint16_t* ks;            // Turbo8: bf16 K group scales [cap, Hkv, D/16] (kc then holds E4M3 codes)
-    uint16_t* vs;            // Turbo8: bf16 V group scales; Bf16K+Turbo4V: E4M3 bytes [cap, Hkv, D/16]
-                             // (vc then holds packed 4-bit indices [cap, Hkv, D/2])
+    uint16_t* vs;            // Turbo8: bf16 V group scales; Lloyd-Max formats: E4M3 bytes [cap, Hkv, D/16]
+                             // (kc/vc of a Lloyd-Max side hold packed indices [cap, Hkv, D*bits/8])
     uint32_t capacity;
     uint32_t hq, hkv, rotary;
     uint32_t chunk;          // positions per block
@@ -158,7 +158,7 @@ struct AttnArgs {
     int32_t host_pos;        // >= 0: cache position from the host; < 0: read positions[0]
     float eps;
     float scale;
-    float t4_levels[16];     // Bf16K+Turbo4V: the codebook levels
+    float lm_levels[16];     // Lloyd-Max formats: the codebook levels of the format's width
 };
 bool attn_dims_supported(uint32_t head_dim, uint32_t group);
 uint32_t attn_rows_per_iter(uint32_t head_dim);
@@ -171,11 +171,11 @@ const void* attn_kernel_ptr(uint32_t head_dim, uint32_t group, uint32_t kv_dtype
 hipError_t turbo8_quantize_launch(const float* x, uint32_t n, uint8_t* codes, uint16_t* scales,
                                   hipStream_t stream);
 hipError_t e4m3_table_launch(float* out256, hipStream_t stream);
-struct Turbo4Levels {
+struct LmLevels {
     float v[16];
 };
-hipError_t turbo4_quantize_launch(const float* x, uint32_t n, const Turbo4Levels& levels, uint8_t* packed,
-                                  uint8_t* scales, hipStream_t stream);
+hipError_t lm_quantize_launch(uint32_t bits, const float* x, uint32_t n, const LmLevels& levels, uint8_t* packed,
+                              uint8_t* scales, hipStream_t stream);
 const void* attn_combine_kernel_ptr(uint32_t head_dim, uint32_t group);
 
 // ------------------------------------------------------------------ misc

@@ -134,12 +134,15 @@ class KvCacheDev:
     """One layer's KV cache in device memory, its format read from the arrays:
     bf16: {"k", "v"} uint16 bits [cap, Hkv, D]; Turbo8 ("k_scales" present):
     "k", "v" uint8 E4M3 codes [cap, Hkv, D], "k_scales", "v_scales" bf16 bits
-    [cap, Hkv, D/16]; Bf16K + Turbo4V ("v_scales" only): "k" bf16 bits
-    [cap, Hkv, D], "v" packed 4-bit indices uint8 [cap, Hkv, D/2], "v_scales"
-    E4M3 bytes [cap, Hkv, D/16]."""
+    [cap, Hkv, D/16]; a Lloyd-Max format (named by "kv_dtype"; "v_scales" only
+    means Bf16K + Turbo4V): packed indices uint8 [cap, Hkv, D*bits/8] and E4M3
+    scale bytes [cap, Hkv, D/16] for each quantised side, "k" bf16 bits
+    [cap, Hkv, D] for the asymmetric ones."""
 
     def __init__(self, kv: dict, device="cuda"):
-        if "k_scales" in kv:
+        if "kv_dtype" in kv:
+            self.dtype = B.KV_DTYPES.index(kv["kv_dtype"])
+        elif "k_scales" in kv:
             self.dtype = B.Q35_KV_TURBO8
         elif "v_scales" in kv:
             self.dtype = B.Q35_KV_BF16K_TURBO4V
@@ -155,14 +158,16 @@ class KvCacheDev:
                                      ptr(self.k_scales), ptr(self.v_scales))
 
     def to_host(self) -> dict:
-        if self.dtype == B.Q35_KV_TURBO8:
-            return {"k": self.k.cpu().numpy(), "v": self.v.cpu().numpy(),
-                    "k_scales": self.k_scales.cpu().numpy().view(np.uint16),
-                    "v_scales": self.v_scales.cpu().numpy().view(np.uint16)}
-        if self.dtype == B.Q35_KV_BF16K_TURBO4V:
-            return {"k": self.k.cpu().numpy().view(np.uint16), "v": self.v.cpu().numpy(),
-                    "v_scales": self.v_scales.cpu().numpy()}
-        return {"k": self.k.cpu().numpy().view(np.uint16), "v": self.v.cpu().numpy().view(np.uint16)}
+        """The arrays as NumPy, in the dtypes the generators use."""
+        def host(t):
+            a = t.cpu().numpy()
+            return a.view(np.uint16) if a.dtype == np.int16 else a
+        out = {"k": host(self.k), "v": host(self.v)}
+        if self.k_scales is not None:
+            out["k_scales"] = host(self.k_scales)
+        if self.v_scales is not None:
+            out["v_scales"] = host(self.v_scales)
+        return out
 
 
 def _f32(n, device):

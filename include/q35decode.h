@@ -141,8 +141,8 @@ typedef struct Q35QuantWeight {
 /* Parses a KV storage-format name as the pages' MetalKvDtype FromStr does
  * ("bf16", "turbo8", "turbo4", "turbo3", "turbo2", "bf16k_turbo4v",
  * "bf16k_turbo3v", "bf16k_turbo2v").  Unknown names: Q35_ERR_INVALID_ARG.
- * The per-layer full-attention forward implements Q35_KV_BF16, Q35_KV_TURBO8
- * and Q35_KV_BF16K_TURBO4V; the persistent decode path implements Q35_KV_BF16. */
+ * The per-layer full-attention forward implements every format; the persistent
+ * decode path implements Q35_KV_BF16. */
 q35_status q35_kv_dtype_from_str(const char* name, uint32_t* dtype);
 
 /*
@@ -168,17 +168,19 @@ q35_status q35_kv_cache_bytes(const Qwen35ForwardConfig* cfg, uint32_t dtype, ui
  *                  16 consecutive elements: value = e4m3(code) * scale.  The
  *                  append stores scale = bf16(amax / 448) and codes = E4M3 of
  *                  x / scale, rounded to nearest-even, saturating.
- *   Q35_KV_BF16K_TURBO4V (mod.rs: MetalKvDtype::Bf16KTurbo4V; the asymmetric
- *                  branch of full_attention.rs): k bf16 [capacity, num_kv_heads,
- *                  head_dim], not rotated; v packed 4-bit indices, uint8
- *                  [capacity, num_kv_heads, head_dim / 2] (element 2i in the low
- *                  nibble of byte i), into the 16-level codebook of
- *                  q35_turbo4_codebook, of the head vectors after the orthonormal
- *                  Walsh-Hadamard transform; v_scales one FP8 E4M3 byte per 16
+ *   Lloyd-Max formats (mod.rs: MetalKvDtype::Turbo4/3/2 and Bf16KTurbo4V/3V/2V;
+ *                  the Turbo branches of full_attention.rs), b = 4, 3 or 2 bits:
+ *                  a quantised side holds b-bit indices into the 2^b-level
+ *                  codebook of q35_turbo_codebook, uint8 [capacity, num_kv_heads,
+ *                  head_dim * b / 8], a little-endian bit stream (element e at
+ *                  bits [b e, b e + b)), of the head vectors after the orthonormal
+ *                  Walsh-Hadamard transform, with one FP8 E4M3 scale byte per 16
  *                  elements [capacity, num_kv_heads, head_dim / 16]:
- *                  value = e4m3(scale) * level[index]; k_scales NULL.  The append
- *                  picks each index as the nearest level to x / rms(group) and
- *                  stores the scale ||x|| / ||level[idx]|| (the group's norm).
+ *                  value = e4m3(scale) * level[index].  Q35_KV_TURBO4/3/2 quantise
+ *                  K (k_scales) and V (v_scales); Q35_KV_BF16K_TURBO4V/3V/2V keep
+ *                  k as bf16 [capacity, num_kv_heads, head_dim], not rotated, with
+ *                  k_scales NULL.  The append picks each index as the nearest level
+ *                  to x / rms(group) and stores the scale ||x|| / ||level[idx]||.
  */
 typedef struct LayerKvCache {
     void* k;
@@ -259,12 +261,11 @@ q35_status q35_full_attention_workspace_bytes(const Qwen35ForwardConfig* cfg, ui
  *   inv_freq: fp32 [rotary_dim/2] (see q35_rope_inv_freq);
  *   positions: int32 [1], must hold cache_pos (RoPE reads it on the device);
  *   cache_pos < kv->capacity and seq_len_attn == cache_pos + 1, else
- *   Q35_ERR_OUT_OF_RANGE; kv->dtype other than Q35_KV_BF16, Q35_KV_TURBO8 or
- *   Q35_KV_BF16K_TURBO4V: Q35_ERR_UNSUPPORTED.  With Turbo8 the query heads, the
- *   new key and value are rotated before the quantising append and the
- *   attention output is rotated back; with Bf16K + Turbo4V only the value is
- *   rotated (and the output rotated back).  Attention is exact over all rows
- *   (the pages' sparse-V gate is not applied).
+ *   Q35_ERR_OUT_OF_RANGE; an unknown kv->dtype: Q35_ERR_UNSUPPORTED.  With
+ *   Turbo8 and Turbo4/3/2 the query heads, the new key and value are rotated
+ *   before the quantising append and the attention output is rotated back; with
+ *   Bf16K + TurboNV only the value is rotated (and the output rotated back).
+ *   Attention is exact over all rows (the pages' sparse-V gate is not applied).
  * x_in must not alias any scratch buffer.
  */
 q35_status q35_forward_full_attention(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
@@ -549,26 +550,28 @@ q35_status q35_gate_up_swiglu(const Qwen35Kernels* kernels, const Qwen35ForwardC
 q35_status q35_turbo8_quantize(const Qwen35Kernels* kernels, const float* x, uint32_t n,
                                uint8_t* codes, uint16_t* scales, hipStream_t stream);
 
-/* The Turbo4 codebook this library uses (mod.rs: the Turbo4 variant's
- * Lloyd-Max indices): the 16-level Lloyd-Max quantiser of the standard normal
- * distribution, ascending, computed once by q35_kernels_resolve.  levels: host
- * float [16], caller-owned.  NULL argument: Q35_ERR_INVALID_ARG. */
-q35_status q35_turbo4_codebook(const Qwen35Kernels* kernels, float* levels);
+/* The Lloyd-Max codebook of the b-bit formats (mod.rs: the Turbo4/3/2
+ * variants' Lloyd-Max indices): the 2^b-level Lloyd-Max quantiser of the
+ * standard normal distribution, ascending, computed once by
+ * q35_kernels_resolve.  bits 2, 3 or 4; levels: host float [2^bits],
+ * caller-owned.  Other bits or NULL: Q35_ERR_INVALID_ARG. */
+q35_status q35_turbo_codebook(const Qwen35Kernels* kernels, uint32_t bits, float* levels);
 
 /*
- * The Turbo4 group quantiser of the Bf16K + Turbo4V append, over a plain
- * device vector: for each group of 16 fp32 values of x [n] (n a multiple of 16),
+ * The group quantiser of the Lloyd-Max formats' append, over a plain device
+ * vector: for each group of 16 fp32 values of x [n] (n a multiple of 16),
  * sigma = sqrt(sum(x^2) / 16) (sum in double, sigma in fp32), each index the
  * number of thresholds (fp32 midpoints of adjacent levels) below x / sigma, and
  * the scale the E4M3 code of ||x|| / ||level[idx]|| (double, rounded to fp32,
  * then round-to-nearest-even, saturating); a zero group gets scale 0 and
- * indices 0.  packed uint8 [n / 2] (8-byte aligned, low nibble first), scales
- * uint8 [n / 16]; x 16-byte aligned; device pointers, caller-owned.  n not a
- * multiple of 16, a NULL or misaligned pointer: Q35_ERR_INVALID_ARG; n == 0
- * launches nothing.  Asynchronous on `stream`.
+ * indices 0.  packed uint8 [n * bits / 8] (little-endian bit stream; aligned
+ * to one group's 2 * bits bytes), scales uint8 [n / 16]; x 16-byte aligned;
+ * device pointers, caller-owned.  bits other than 2, 3, 4, n not a multiple of
+ * 16, a NULL or misaligned pointer: Q35_ERR_INVALID_ARG; n == 0 launches
+ * nothing.  Asynchronous on `stream`.
  */
-q35_status q35_turbo4_quantize(const Qwen35Kernels* kernels, const float* x, uint32_t n, uint8_t* packed,
-                               uint8_t* scales, hipStream_t stream);
+q35_status q35_turbo_quantize(const Qwen35Kernels* kernels, uint32_t bits, const float* x, uint32_t n,
+                              uint8_t* packed, uint8_t* scales, hipStream_t stream);
 
 /* The E4M3 decoder of the Turbo8 attention over every code: out fp32 [256]
  * (device, caller-owned, 16-byte aligned), out[c] = value of code c; 0x7F and

@@ -269,22 +269,43 @@ def kv_cache(g: Gen, cfg: Config, prefix: str, capacity: int, filled: int) -> di
     return {"k": k, "v": v, "capacity": capacity}
 
 
-def kv_cache_bf16k_turbo4v(g: Gen, cfg: Config, prefix: str, capacity: int, filled: int) -> dict:
-    """Bf16K + Turbo4V caches: k bf16 [capacity, Hkv, D] with rows [0, filled)
-    N(0, 1); v packed 4-bit indices uint8 [capacity, Hkv, D/2], every byte drawn
-    uniformly, and E4M3 scale bytes [capacity, Hkv, D/16] drawn uniformly from
-    the codes 0x28-0x3F (0.25 to 1.875); the other rows are zero."""
+LM_FORMATS = {"turbo4": (True, 4), "turbo3": (True, 3), "turbo2": (True, 2),
+              "bf16k_turbo4v": (False, 4), "bf16k_turbo3v": (False, 3), "bf16k_turbo2v": (False, 2)}
+
+
+def kv_cache_lm(g: Gen, cfg: Config, prefix: str, capacity: int, filled: int, fmt: str) -> dict:
+    """Lloyd-Max format caches (``fmt`` a key of LM_FORMATS).  A quantised side:
+    packed indices uint8 [capacity, Hkv, D*bits/8] with every byte drawn
+    uniformly and E4M3 scale bytes [capacity, Hkv, D/16] drawn uniformly from the
+    codes 0x28-0x3F (0.25 to 1.875); a bf16 K: [capacity, Hkv, D] N(0, 1).
+    Rows [0, filled) are drawn, the others zero."""
+    kq, bits = LM_FORMATS[fmt]
     Hkv, D = cfg.num_kv_heads, cfg.head_dim
-    out = {"k": np.zeros((capacity, Hkv, D), np.uint16),
-           "v": np.zeros((capacity, Hkv, D // 2), np.uint8),
-           "v_scales": np.zeros((capacity, Hkv, D // 16), np.uint8), "capacity": capacity}
+    nb = D * bits // 8
+    out = {"v": np.zeros((capacity, Hkv, nb), np.uint8),
+           "v_scales": np.zeros((capacity, Hkv, D // 16), np.uint8), "capacity": capacity,
+           "kv_dtype": fmt}
+    sides = ["v"]
+    if kq:
+        out["k"] = np.zeros((capacity, Hkv, nb), np.uint8)
+        out["k_scales"] = np.zeros((capacity, Hkv, D // 16), np.uint8)
+        sides.append("k")
+    else:
+        out["k"] = np.zeros((capacity, Hkv, D), np.uint16)
+        if filled:
+            out["k"][:filled] = g.normal_bf16(prefix + ".k_prefill", (filled, Hkv, D))
     if filled:
-        out["k"][:filled] = g.normal_bf16(prefix + ".k_prefill", (filled, Hkv, D))
-        u = g.uniform_f32(prefix + ".v_t4codes", (filled, Hkv, D // 2), 0.0, 256.0)
-        out["v"][:filled] = np.minimum(np.floor(u), 255.0).astype(np.uint8)
-        u = g.uniform_f32(prefix + ".v_t4scales", (filled, Hkv, D // 16), 0.0, 24.0)
-        out["v_scales"][:filled] = (0x28 + np.minimum(np.floor(u), 23.0)).astype(np.uint8)
+        for side in sides:
+            u = g.uniform_f32(f"{prefix}.{side}_lm{bits}codes", (filled, Hkv, nb), 0.0, 256.0)
+            out[side][:filled] = np.minimum(np.floor(u), 255.0).astype(np.uint8)
+            u = g.uniform_f32(f"{prefix}.{side}_lm{bits}scales", (filled, Hkv, D // 16), 0.0, 24.0)
+            out[side + "_scales"][:filled] = (0x28 + np.minimum(np.floor(u), 23.0)).astype(np.uint8)
     return out
+
+
+def kv_cache_bf16k_turbo4v(g: Gen, cfg: Config, prefix: str, capacity: int, filled: int) -> dict:
+    """Bf16K + Turbo4V caches (``kv_cache_lm`` with that format)."""
+    return kv_cache_lm(g, cfg, prefix, capacity, filled, "bf16k_turbo4v")
 
 
 def kv_cache_turbo8(g: Gen, cfg: Config, prefix: str, capacity: int, filled: int) -> dict:

@@ -9,9 +9,9 @@
 * ``full_layer_4b_turbo8``  the same layer over a Turbo8 cache whose rows
                       [0, 4096) hold uniformly drawn finite E4M3 codes and bf16
                       scales U(1e-3, 1e-2);
-* ``full_layer_4b_bf16k_turbo4v``  the same layer over a Bf16K + Turbo4V cache
-                      (bf16 keys N(0, 1), uniformly drawn value indices and
-                      E4M3 scales);
+* ``full_layer_4b_lm``  the same layer over a Lloyd-Max format cache (uniformly
+                      drawn indices and E4M3 scales; bf16 keys N(0, 1) for the
+                      asymmetric formats);
 * ``stack_4b``        the 4B-shaped stack (every 4th layer full attention), int8
                       lm_head over the 248 320-token vocabulary, bf16 embedding table
                       N(0, 1), zero GDN states, KV rows [0, ctx) prefilled N(0, 1)
@@ -19,7 +19,7 @@
 """
 from __future__ import annotations
 
-from . import (Gen, gdn_layer, full_layer, gdn_state, kv_cache, kv_cache_bf16k_turbo4v,
+from . import (LM_FORMATS, Gen, gdn_layer, full_layer, gdn_state, kv_cache, kv_cache_lm,
                kv_cache_turbo8, layer_kinds, qwen3_5_4b, tiny)
 
 
@@ -57,11 +57,12 @@ def full_layer_4b_turbo8(gen: Gen, steps: int = 12, prefill: int = 4096):
     return {"cfg": cfg, "layer": layer, "kv": kv, "xs": xs, "start": prefill}
 
 
-def full_layer_4b_bf16k_turbo4v(gen: Gen, steps: int = 12, prefill: int = 4096):
+def full_layer_4b_lm(gen: Gen, fmt: str, steps: int = 12, prefill: int = 4096):
+    """The 4B full-attention layer over a Lloyd-Max format cache (``kv_cache_lm``)."""
     cfg = qwen3_5_4b("bf16")
-    layer = full_layer(gen, cfg, "c3t4.L")
-    kv = kv_cache_bf16k_turbo4v(gen, cfg, "c3t4.L", prefill + steps, prefill)
-    xs = [gen.act(f"c3t4.x{t}", (cfg.hidden,), cfg.act_dtype) for t in range(steps)]
+    layer = full_layer(gen, cfg, f"c3{fmt}.L")
+    kv = kv_cache_lm(gen, cfg, f"c3{fmt}.L", prefill + steps, prefill, fmt)
+    xs = [gen.act(f"c3{fmt}.x{t}", (cfg.hidden,), cfg.act_dtype) for t in range(steps)]
     return {"cfg": cfg, "layer": layer, "kv": kv, "xs": xs, "start": prefill}
 
 
@@ -69,8 +70,7 @@ def stack_4b(gen: Gen, num_layers: int = 32, ctx: int = 8192, extra: int = 256, 
              kv: str = "bf16"):
     """The 4B-shaped stack.  ``capacity = ctx + extra`` tokens per KV cache; ``kv``
     "bf16" (rows N(0, 1)), "turbo8" (rows of uniformly drawn finite E4M3 codes
-    and bf16 scales U(1e-3, 1e-2)) or "bf16k_turbo4v" (bf16 keys N(0, 1), uniformly
-    drawn 4-bit value indices and E4M3 scales)."""
+    and bf16 scales U(1e-3, 1e-2)) or a Lloyd-Max format (``kv_cache_lm``)."""
     cfg = qwen3_5_4b("bf16")
     kinds = layer_kinds(num_layers)
     layers, states, kvs = [], [], []
@@ -82,9 +82,11 @@ def stack_4b(gen: Gen, num_layers: int = 32, ctx: int = 8192, extra: int = 256, 
         else:
             layers.append(full_layer(gen, cfg, f"c4.L{i}"))
             states.append(None)
-            make = {"bf16": kv_cache, "turbo8": kv_cache_turbo8,
-                    "bf16k_turbo4v": kv_cache_bf16k_turbo4v}[kv]
-            kvs.append(make(gen, cfg, f"c4.L{i}", ctx + extra, ctx))
+            if kv in LM_FORMATS:
+                kvs.append(kv_cache_lm(gen, cfg, f"c4.L{i}", ctx + extra, ctx, kv))
+            else:
+                make = {"bf16": kv_cache, "turbo8": kv_cache_turbo8}[kv]
+                kvs.append(make(gen, cfg, f"c4.L{i}", ctx + extra, ctx))
         if progress:
             progress(i)
     embed = gen.normal_bf16("c4.embed", (cfg.vocab, cfg.hidden))

@@ -177,12 +177,20 @@ def test_forward_errors_before_any_launch(lib):
         B.q35_forward_full_attention(FAKE_KERNELS, c, layer, scratch, kv, 0x100, 0x100, 0x100, 3, 4, None)
     assert e.value.status == B.Q35_ERR_INVALID_ARG and "K scale" in str(e.value)
     kv.k_scales, kv.v_scales = None, None
-    for name in ("turbo4", "turbo3", "turbo2", "bf16k_turbo3v", "bf16k_turbo2v"):
+    # the symmetric Lloyd-Max formats need both scale arrays, the asymmetric ones V's only
+    for name, needs_k in (("turbo4", True), ("turbo3", True), ("turbo2", True),
+                          ("bf16k_turbo3v", False), ("bf16k_turbo2v", False)):
         kv.dtype = B.q35_kv_dtype_from_str(name)
         with pytest.raises(B.Q35Error) as e:
             B.q35_forward_full_attention(FAKE_KERNELS, c, layer, scratch, kv, 0x100, 0x100, 0x100, 3, 4,
                                          None)
-        assert e.value.status == B.Q35_ERR_UNSUPPORTED, name
+        assert e.value.status == B.Q35_ERR_INVALID_ARG, name
+        assert ("k_scales" if needs_k else "v_scales") in str(e.value), name
+    # an unknown format number
+    kv.dtype = 8
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_forward_full_attention(FAKE_KERNELS, c, layer, scratch, kv, 0x100, 0x100, 0x100, 3, 4, None)
+    assert e.value.status == B.Q35_ERR_UNSUPPORTED
     # valid position but NULL weights
     kv.dtype = 0
     with pytest.raises(B.Q35Error) as e:

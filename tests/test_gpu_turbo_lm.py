@@ -1,16 +1,19 @@
-"""GPU parity of the Bf16K + Turbo4V KV cache (bf16 keys; values as 4-bit
-Lloyd-Max indices with an E4M3 norm-keeping scale per 16, in the
-Walsh-Hadamard basis of a head) against the oracle.
+"""GPU parity of the Lloyd-Max KV formats against the oracle: the symmetric
+Turbo4/3/2 formats (K and V as b-bit indices into a Lloyd-Max codebook with an
+E4M3 norm-keeping scale per 16, in the Walsh-Hadamard basis of a head) and the
+asymmetric Bf16K + Turbo4V/3V/2V formats (K in bf16).
 
-* the library's codebook equals the oracle's, bit for bit (each computed on
-  its own side from the definition);
-* the group quantiser of the append: indices and scales bit-exact on identical
-  fp32 inputs, zero groups, saturating and subnormal scales included;
-* tiny layer (fp32 activations, 512 prefilled rows, several chunks): every
-  step's taps and output at rel 1e-3, the stored row placed exactly, its key the
-  bf16 of the kernel's own key and its value the oracle's quantisation of the
-  kernel's own value; attention re-derived from the stored cache;
-* 4B layer (bf16 activations, 4096 prefilled rows, 12 steps): outputs at 2e-2.
+* the library's codebooks (2, 3 and 4 bits) equal the oracle's, bit for bit
+  (each computed on its own side from the definition);
+* the group quantiser of the append: packed indices and scales bit-exact on
+  identical fp32 inputs, zero groups, saturating and subnormal scales included;
+* tiny layer for each format (fp32 activations, 512 prefilled rows, several
+  chunks): every step's taps and output at rel 1e-3, the stored row placed
+  exactly, each stored side the oracle's quantisation of the kernel's own k or
+  v (a bf16 K the bf16 of the kernel's own k); attention re-derived from the
+  stored cache and the kernel's own query;
+* 4B layer for each format (bf16 activations, 4096 prefilled rows, 12 steps):
+  outputs at 2e-2.
 
 An index is decided on a rotated value that the GPU computes in fp32 and the
 oracle in fp64: the two can straddle a threshold, so stored rows are compared
@@ -24,13 +27,15 @@ import pytest
 import torch
 
 import oracle as O
-from oracle import turbo_lm as T4
+from oracle import turbo_lm as TL
 from oracle import turbo8 as T8
 import synth
 from synth import workloads
 from gpu_common import TOL_BF16, TOL_F32, rel, say
 
 pytestmark = pytest.mark.gpu
+
+FORMATS = ["turbo4", "turbo3", "turbo2", "bf16k_turbo4v", "bf16k_turbo3v", "bf16k_turbo2v"]
 
 
 @pytest.fixture(scope="module")
@@ -40,12 +45,13 @@ def rt():
     return runtime
 
 
-def test_codebook_matches_oracle_bit_exact(rt):
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_codebook_matches_oracle_bit_exact(rt, bits):
     from hybrid_decode_amd import binding as B
-    say("Turbo4 codebook")
-    lib = B.q35_turbo4_codebook(rt.kernels())
-    ref = T4.codebook_f32()
-    assert lib.dtype == np.float32 and ref.dtype == np.float32
+    say(f"{bits}-bit codebook")
+    lib = B.q35_turbo_codebook(rt.kernels(), bits)
+    ref = TL.codebook_f32(bits)
+    assert lib.dtype == np.float32 and ref.dtype == np.float32 and lib.shape == ref.shape
     assert np.array_equal(lib.view(np.uint32), ref.view(np.uint32))
 
 
@@ -66,19 +72,21 @@ def _quantiser_inputs(gen) -> np.ndarray:
     return np.concatenate(groups).astype(np.float32)
 
 
-def test_turbo4_quantiser_bit_exact(rt, gen):
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantiser_bit_exact(rt, gen, bits):
     from hybrid_decode_amd import binding as B
     x = _quantiser_inputs(gen)
     G = x.shape[0]
-    say(f"Turbo4 quantiser over {G} groups")
+    nb = 2 * bits  # bytes of one group's indices
+    say(f"{bits}-bit quantiser over {G} groups")
     xd = rt.to_dev(x.ravel())
-    packed = torch.full((G * 8,), 0xAB, dtype=torch.uint8, device="cuda")
+    packed = torch.full((G * nb,), 0xAB, dtype=torch.uint8, device="cuda")
     scales = torch.full((G,), 0xCD, dtype=torch.uint8, device="cuda")
-    B.q35_turbo4_quantize(rt.kernels(), xd.data_ptr(), G * 16, packed.data_ptr(), scales.data_ptr(),
-                          rt.stream_ptr())
+    B.q35_turbo_quantize(rt.kernels(), bits, xd.data_ptr(), G * 16, packed.data_ptr(), scales.data_ptr(),
+                         rt.stream_ptr())
     torch.cuda.synchronize()
-    rp, rs = T4.turbo4_quantize(x.astype(np.float64))
-    gp = packed.cpu().numpy().reshape(G, 8)
+    rp, rs = TL.quantize(x.astype(np.float64), bits)
+    gp = packed.cpu().numpy().reshape(G, nb)
     gs = scales.cpu().numpy()
     rs = rs.reshape(G)
     bad = np.nonzero(np.any(gp != rp, axis=1) | (gs != rs))[0]
@@ -86,16 +94,18 @@ def test_turbo4_quantiser_bit_exact(rt, gen):
                             int(rs[i])) for i in bad[:3]]
 
 
-def test_turbo4_quantiser_rejects_bad_arguments(rt):
+def test_quantiser_rejects_bad_arguments(rt):
     from hybrid_decode_amd import binding as B
     x = torch.zeros(32, dtype=torch.float32, device="cuda")
     p = torch.zeros(32, dtype=torch.uint8, device="cuda")
     s = torch.zeros(4, dtype=torch.uint8, device="cuda")
     with pytest.raises(B.Q35Error):
-        B.q35_turbo4_quantize(rt.kernels(), x.data_ptr(), 24, p.data_ptr(), s.data_ptr(), None)
+        B.q35_turbo_quantize(rt.kernels(), 4, x.data_ptr(), 24, p.data_ptr(), s.data_ptr(), None)
     with pytest.raises(B.Q35Error):
-        B.q35_turbo4_quantize(rt.kernels(), x.data_ptr(), 32, p.data_ptr() + 4, s.data_ptr(), None)
-    B.q35_turbo4_quantize(rt.kernels(), x.data_ptr(), 0, p.data_ptr(), s.data_ptr(), None)
+        B.q35_turbo_quantize(rt.kernels(), 4, x.data_ptr(), 32, p.data_ptr() + 4, s.data_ptr(), None)
+    with pytest.raises(B.Q35Error):
+        B.q35_turbo_quantize(rt.kernels(), 5, x.data_ptr(), 32, p.data_ptr(), s.data_ptr(), None)
+    B.q35_turbo_quantize(rt.kernels(), 3, x.data_ptr(), 0, p.data_ptr(), s.data_ptr(), None)
 
 
 FULL_TAPS_PRE = {"x_norm": "x_norm", "q_full": "q_full", "k": "k", "v": "v",
@@ -105,39 +115,62 @@ FULL_TAPS_POST = {"attn_out": "attn_out", "gated_attn": "gated_attn", "o": "o",
                   "up_act": "up_act"}
 
 
-def _check_row(after, before, t, scr, cfg, okv):
-    """Row t is the only row that changed; its key is the bf16 of the kernel's
-    k tap; its value is the oracle's quantisation of the kernel's v tap
-    (rotated in fp64) up to rare one-step index flips; and it is close to the
-    row the oracle forward appended.  Returns whether the row equals that one."""
+def _check_side(after, t, data, scales, x, bits, okv):
+    """A quantised side of row t: the oracle's quantisation of the kernel's own
+    input (rotated in fp64) up to rare one-step index flips; close to the row
+    the oracle forward appended.  Returns whether it equals that row."""
+    rp, rsc = TL.quantize(T8.wht(x), bits)
+    gi = TL.unpack_indices(after[data][t], bits)
+    ri = TL.unpack_indices(rp, bits)
+    assert np.all(np.abs(gi - ri) <= 1), (data, t)
+    assert np.mean(gi == ri) >= 0.99, (data, t)
+    assert np.all(np.abs(after[scales][t].astype(int) - rsc.astype(int)) <= 1), (data, t)
+    g = TL.dequantize(after[data][t], after[scales][t], bits)
+    r = TL.dequantize(okv[data][t], okv[scales][t], bits)
+    assert rel(g, r) < 5e-2, (data, t)
+    return bool(np.array_equal(after[data][t], okv[data][t]) and
+                np.array_equal(after[scales][t], okv[scales][t]))
+
+
+def _check_row(fmt, after, before, t, scr, cfg, okv):
+    """Row t is the only row that changed, and each side is as the oracle
+    stores the kernel's own k and v.  Returns whether the row equals the oracle
+    forward's."""
+    kq, bits = TL.FORMATS[fmt]
     Hkv, D = cfg.num_kv_heads, cfg.head_dim
-    for side in ("k", "v", "v_scales"):
+    for side in after:
         changed = np.nonzero(np.any((after[side] != before[side]).reshape(after[side].shape[0], -1),
                                     axis=1))[0].tolist()
         assert changed == [t], (side, t, changed)
     kt = scr.t["k_norm_out"].cpu().numpy().astype(np.float64).reshape(Hkv, D)
-    assert np.array_equal(after["k"][t], O.f64_to_bf16(kt))
     vt = scr.t["v"].cpu().numpy().astype(np.float64).reshape(Hkv, D)
-    rp, rsc = T4.turbo4_quantize(T8.wht(vt))
-    gi, ri = T4.turbo4_unpack(after["v"][t]), T4.turbo4_unpack(rp)
-    assert np.all(np.abs(gi - ri) <= 1), t
-    assert np.mean(gi == ri) >= 0.99, t
-    assert np.all(np.abs(after["v_scales"][t].astype(int) - rsc.astype(int)) <= 1), t
-    g = T4.turbo4_dequantize(after["v"][t], after["v_scales"][t])
-    r = T4.turbo4_dequantize(okv["v"][t], okv["v_scales"][t])
-    assert rel(g, r) < 5e-2, t
-    return bool(np.array_equal(after["v"][t], okv["v"][t]) and
-                np.array_equal(after["v_scales"][t], okv["v_scales"][t]) and
-                np.array_equal(after["k"][t], okv["k"][t]))
+    same = _check_side(after, t, "v", "v_scales", vt, bits, okv)
+    if kq:
+        same &= _check_side(after, t, "k", "k_scales", kt, bits, okv)
+    else:
+        assert np.array_equal(after["k"][t], O.f64_to_bf16(kt))
+        same &= bool(np.array_equal(after["k"][t], okv["k"][t]))
+    return same
 
 
-def test_full_layer_tiny_bf16k_turbo4v_taps_append_and_attention(rt, gen):
+def _poison(kv, fmt, start):
+    """Unwritten rows read as NaN: bf16 keys NaN, quantised sides a NaN scale."""
+    kq, _ = TL.FORMATS[fmt]
+    if kq:
+        kv["k_scales"][start:] = 0x7F
+    else:
+        kv["k"][start:] = 0x7FC0
+    kv["v_scales"][start:] = 0x7F
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_full_layer_tiny_taps_append_and_attention(rt, gen, fmt):
     cfg = synth.tiny("f32")
-    layer = synth.full_layer(gen, cfg, "gpu.t4f")
+    layer = synth.full_layer(gen, cfg, f"gpu.lm.{fmt}")
     start, steps = 512, 16
     cap = start + steps + 8
-    kv = synth.kv_cache_bf16k_turbo4v(gen, cfg, "gpu.t4f", cap, start)
-    kv["k"][start:] = 0x7FC0   # poison: a read of an unwritten key row gives NaN
+    kv = synth.kv_cache_lm(gen, cfg, f"gpu.lm.{fmt}", cap, start, fmt)
+    _poison(kv, fmt, start)
     Ld, KVd = rt.FullLayerDev(layer), rt.KvCacheDev(kv)
     scr = rt.FullScratchDev(cfg, cap, taps=True)
     inv = rt.inv_freq_dev(cfg)
@@ -145,33 +178,34 @@ def test_full_layer_tiny_bf16k_turbo4v_taps_append_and_attention(rt, gen):
     okv = {k: np.array(v, copy=True) for k, v in kv.items() if isinstance(v, np.ndarray)}
     for i in range(steps):
         t = start + i
-        say(f"tiny Bf16K+Turbo4V full attention at cache_pos {t}")
-        x = gen.act(f"gpu.t4f.x{i}", (cfg.hidden,), "f32")
+        say(f"tiny {fmt} full attention at cache_pos {t}")
+        x = gen.act(f"gpu.lm.{fmt}.x{i}", (cfg.hidden,), "f32")
         pos = torch.tensor([t], dtype=torch.int32, device="cuda")
         before = KVd.to_host()
         rt.forward_full_attention(cfg, Ld, scr, KVd, inv, pos, rt.to_dev(x), t)
         torch.cuda.synchronize()
-        ox, nkv, taps = T4.forward_full_attention_bf16k_turbo4v(cfg, layer, okv, inv_h, x, t)
+        ox, nkv, taps = TL.forward_full_attention(fmt, cfg, layer, okv, inv_h, x, t)
         for k, ok in FULL_TAPS_PRE.items():
             assert rel(scr.t[k].cpu().numpy(), taps[ok]) < TOL_F32, (t, k)
         after = KVd.to_host()
-        same = _check_row(after, before, t, scr, cfg, nkv)
+        same = _check_row(fmt, after, before, t, scr, cfg, nkv)
         tol = TOL_F32 if same else TOL_BF16
         assert rel(rt.act_to_f32(scr.t["x_out"], cfg), ox) < tol, (t, same)
         for k, ok in FULL_TAPS_POST.items():
             assert rel(scr.t[k].cpu().numpy(), taps[ok]) < tol, (t, k, same)
         qk = scr.t["q_norm_out"].cpu().numpy().astype(np.float64).reshape(cfg.num_heads, cfg.head_dim)
-        ref = T4.attention_decode_bf16k_turbo4v(qk, after["k"], after["v"], after["v_scales"], t + 1)
+        ref = TL.attention_decode(fmt, qk, after, t + 1)
         assert rel(scr.t["attn_out"].cpu().numpy(), ref) < TOL_F32, t
         okv = {k: np.array(v, copy=True) for k, v in after.items()}   # teacher forcing
-    say("tiny Bf16K+Turbo4V: all steps within tolerance")
+    say(f"tiny {fmt}: all steps within tolerance")
 
 
-def test_full_layer_4b_bf16k_turbo4v_from_4096(rt, gen):
-    w = workloads.full_layer_4b_bf16k_turbo4v(gen, steps=12)
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_full_layer_4b_from_4096(rt, gen, fmt):
+    w = workloads.full_layer_4b_lm(gen, fmt, steps=12)
     cfg, layer, kv, start = w["cfg"], w["layer"], w["kv"], w["start"]
     cap = kv["k"].shape[0]
-    kv["k"][start:] = 0x7FC0
+    _poison(kv, fmt, start)
     Ld, KVd = rt.FullLayerDev(layer), rt.KvCacheDev(kv)
     scr = rt.FullScratchDev(cfg, cap, taps=True)
     inv = rt.inv_freq_dev(cfg)
@@ -181,34 +215,33 @@ def test_full_layer_4b_bf16k_turbo4v_from_4096(rt, gen):
     for i, x in enumerate(w["xs"]):
         t = start + i
         if i % 8 == 0:
-            say(f"4B Bf16K+Turbo4V full attention at cache_pos {t}")
+            say(f"4B {fmt} full attention at cache_pos {t}")
         pos = torch.tensor([t], dtype=torch.int32, device="cuda")
         before = KVd.to_host()
         rt.forward_full_attention(cfg, Ld, scr, KVd, inv, pos, rt.to_dev(x), t)
         torch.cuda.synchronize()
-        ox, nkv, _ = T4.forward_full_attention_bf16k_turbo4v(cfg, layer, okv, inv_h, x, t)
+        ox, nkv, _ = TL.forward_full_attention(fmt, cfg, layer, okv, inv_h, x, t)
         after = KVd.to_host()
-        _check_row(after, before, t, scr, cfg, nkv)
+        _check_row(fmt, after, before, t, scr, cfg, nkv)
         r = rel(rt.act_to_f32(scr.t["x_out"], cfg), ox)
         worst = max(worst, r)
         assert r < TOL_BF16, (t, r)
         if i == 0:
             qk = scr.t["q_norm_out"].cpu().numpy().astype(np.float64).reshape(cfg.num_heads,
                                                                                cfg.head_dim)
-            ref = T4.attention_decode_bf16k_turbo4v(qk, after["k"], after["v"], after["v_scales"],
-                                                    t + 1)
-            ra = rel(scr.t["attn_out"].cpu().numpy(), ref)
-            say(f"4B Bf16K+Turbo4V attention vs oracle on the stored cache: rel {ra:.2e}")
+            ra = rel(scr.t["attn_out"].cpu().numpy(), TL.attention_decode(fmt, qk, after, t + 1))
+            say(f"4B {fmt} attention vs oracle on the stored cache: rel {ra:.2e}")
             assert ra < TOL_F32
         okv = {k: np.array(v, copy=True) for k, v in after.items()}
-    say(f"4B Bf16K+Turbo4V full attention: worst output rel {worst:.2e}")
+    say(f"4B {fmt} full attention: worst output rel {worst:.2e}")
 
 
-def test_persistent_plan_rejects_bf16k_turbo4v_cache(rt, gen):
+@pytest.mark.parametrize("fmt", ["turbo3", "bf16k_turbo4v"])
+def test_persistent_plan_rejects_lloyd_max_caches(rt, gen, fmt):
     from hybrid_decode_amd import binding as B
     w = workloads.tiny_stack(gen, steps=1, capacity=16)
     kvs = list(w["kvs"])
-    kvs[1] = synth.kv_cache_bf16k_turbo4v(gen, w["cfg"], "gpu.t4plan", 16, 0)
+    kvs[1] = synth.kv_cache_lm(gen, w["cfg"], f"gpu.lmplan.{fmt}", 16, 0, fmt)
     states = [rt.GdnStateDev(s) if s is not None else None for s in w["states"]]
     layers = [rt.GdnLayerDev(l) if k == "gdn" else rt.FullLayerDev(l)
               for k, l in zip(w["kinds"], w["layers"])]
