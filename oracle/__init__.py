@@ -12,3 +12,4 @@ from .qwen35 import *  # noqa: F401,F403
 from . import qwen35  # noqa: F401
 from . import turbo8  # noqa: F401
 from . import turbo_lm  # noqa: F401
+from . import prefill  # noqa: F401
