@@ -45,7 +45,8 @@ EXPORTS = [
     "q35_decode_workspace_bytes", "q35_decode_plan_create", "q35_decode_plan_release",
     "q35_decode_step", "q35_decode_check", "q35_decode_layer_input", "q35_decode_stage_layout",
     "q35_decode_stage_times", "q35_turbo8_quantize", "q35_fp8_e4m3_table",
-    "q35_turbo_codebook", "q35_turbo_quantize",
+    "q35_turbo_codebook", "q35_turbo_quantize", "q35_prefill_workspace_bytes",
+    "q35_prefill_linear_attention", "q35_prefill_full_attention", "q35_prefill_gemm",
 ]
 
 Q35_LAYER_LINEAR = 0
@@ -191,6 +192,12 @@ def lib():
             "q35_fp8_e4m3_table": (st, [vp, vp, vp]),
             "q35_turbo_codebook": (st, [vp, u32, P(C.c_float)]),
             "q35_turbo_quantize": (st, [vp, u32, vp, u32, vp, vp, vp]),
+            "q35_prefill_workspace_bytes": (st, [P(Qwen35ForwardConfig), u32, P(sz)]),
+            "q35_prefill_linear_attention": (st, [vp, P(Qwen35ForwardConfig), P(LinearAttentionLayer),
+                                                  P(LinearAttentionState), vp, u32, vp, vp, sz, vp]),
+            "q35_prefill_full_attention": (st, [vp, P(Qwen35ForwardConfig), P(FullAttentionLayer),
+                                                P(LayerKvCache), vp, vp, u32, u32, vp, vp, sz, vp]),
+            "q35_prefill_gemm": (st, [vp, P(Q35QuantWeight), vp, u32, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -379,3 +386,28 @@ def q35_turbo_codebook(kernels, bits: int):
 
 def q35_turbo_quantize(kernels, bits: int, x, n: int, packed, scales, stream) -> None:
     _check(lib().q35_turbo_quantize(kernels, bits, x, n, packed, scales, stream))
+
+
+def q35_prefill_workspace_bytes(cfg, max_tokens: int) -> int:
+    b = C.c_size_t()
+    _check(lib().q35_prefill_workspace_bytes(C.byref(cfg), max_tokens, C.byref(b)))
+    return b.value
+
+
+def q35_prefill_linear_attention(kernels, cfg, layer, state, x_in, n_tokens: int, x_out, workspace,
+                                 workspace_bytes: int, stream) -> None:
+    _check(lib().q35_prefill_linear_attention(kernels, C.byref(cfg), C.byref(layer), C.byref(state),
+                                              x_in, n_tokens, x_out, workspace, workspace_bytes,
+                                              stream))
+
+
+def q35_prefill_full_attention(kernels, cfg, layer, kv, inv_freq, x_in, n_tokens: int,
+                               cache_pos: int, x_out, workspace, workspace_bytes: int,
+                               stream) -> None:
+    _check(lib().q35_prefill_full_attention(kernels, C.byref(cfg), C.byref(layer), C.byref(kv),
+                                            inv_freq, x_in, n_tokens, cache_pos, x_out, workspace,
+                                            workspace_bytes, stream))
+
+
+def q35_prefill_gemm(kernels, w, x_f16, m: int, y, stream) -> None:
+    _check(lib().q35_prefill_gemm(kernels, C.byref(w), x_f16, m, y, stream))

@@ -461,6 +461,7 @@ q35_status q35_kernels_resolve(int device, Qwen35Kernels** out) {
         for (uint32_t g : {1u, 2u, 4u, 8u})
             for (uint32_t f : {Q35_KV_BF16, Q35_KV_TURBO8, Q35_KV_BF16K_TURBO4V})
                 probe(attn_kernel_ptr(d, g, f), "attention");
+    for (int i = 0; pf_kernel_ptr(i); ++i) probe(pf_kernel_ptr(i), "prefill");
     probe(embed_kernel_ptr(), "embed");
     probe(lm_finish_kernel_ptr(), "lm_head argmax");
     for (uint32_t d : {64u, 128u, 256u})
@@ -928,6 +929,294 @@ q35_status q35_gemv(const Qwen35Kernels* kernels, const Q35QuantWeight* w, const
     b.a.pro.x = x;
     b.add(*w, kEpiStore).out = y;
     Q35_TRY(b.launch((uint32_t)kernels->num_cu, stream, "GEMV"));
+    return ok();
+}
+
+// ------------------------------------------------------------------ prefill
+
+}  // extern "C"
+
+namespace {
+
+// Prefill workspace: the buffers of one layer kind for T tokens, each
+// 256-byte aligned; the two kinds share one region.
+struct PfWs {
+    size_t xh, qkv, z, fa, fb, qkvs, lg, beta, wc, uc, pc, lc, y, yz, r, h;  // GDN
+    size_t qf, kf, vf, qb, ga;                                               // full (xh, r, h shared)
+    uint32_t nch;
+    size_t bytes;
+};
+
+PfWs pf_ws_layout(const Qwen35ForwardConfig& c, uint32_t T) {
+    PfWs w{};
+    auto take = [](size_t& off, size_t n) {
+        const size_t o = off;
+        off += (n + 255) & ~(size_t)255;
+        return o;
+    };
+    const size_t t = T, H = c.hidden, I = c.intermediate, C = qkv_total(c), Z = z_dim(c);
+    const size_t hv = c.num_v_heads_lin, dk = c.k_head_dim_lin, dv = c.v_head_dim_lin;
+    w.nch = (T + 63) / 64;
+    size_t o = 0;
+    w.xh = take(o, t * H * 2);
+    w.r = take(o, t * H * 4);
+    w.h = take(o, t * I * 2);
+    const size_t shared = o;
+    w.qkv = take(o, t * C * 4);
+    w.z = take(o, t * Z * 4);
+    w.fa = take(o, t * hv * 4);
+    w.fb = take(o, t * hv * 4);
+    w.qkvs = take(o, t * C * 4);
+    w.lg = take(o, t * hv * 4);
+    w.beta = take(o, t * hv * 4);
+    w.wc = take(o, hv * w.nch * 64 * dk * 4);
+    w.uc = take(o, hv * w.nch * 64 * dv * 4);
+    w.pc = take(o, hv * w.nch * 64 * 64 * 4);
+    w.lc = take(o, hv * w.nch * 64 * 4);
+    w.y = take(o, t * Z * 4);
+    w.yz = take(o, t * Z * 2);
+    const size_t gdn = o;
+    o = shared;
+    w.qf = take(o, t * q_total(c) * 4);
+    w.kf = take(o, t * kv_dim(c) * 4);
+    w.vf = take(o, t * kv_dim(c) * 4);
+    w.qb = take(o, t * q_only(c) * 2);
+    w.ga = take(o, t * q_only(c) * 2);
+    w.bytes = gdn > o ? gdn : o;
+    return w;
+}
+
+template <class T>
+T* at_off(void* base, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+q35_status pf_gemm(const char* what, int mode, const uint16_t* x, uint32_t M, const Q35QuantWeight& w0,
+                   const Q35QuantWeight* w1, void* out, uint32_t ldo, const void* resid, bool resid_f32,
+                   bool out_f32, hipStream_t stream) {
+    PfGemmArgs g{};
+    g.x = x;
+    g.w0 = w0.codes;
+    g.s0 = w0.scales;
+    g.b0 = w0.biases;
+    if (w1) {
+        g.w1 = w1->codes;
+        g.s1 = w1->scales;
+        g.b1 = w1->biases;
+    }
+    g.out = out;
+    g.resid = resid;
+    g.M = M;
+    g.N = w0.n;
+    g.K = w0.k;
+    g.ldo = ldo;
+    g.resid_f32 = resid_f32 ? 1 : 0;
+    g.out_f32 = out_f32 ? 1 : 0;
+    Q35_HIP(pf_gemm_launch(mode, g, stream), what);
+    return Q35_OK;
+}
+
+q35_status pf_check_ws(const Qwen35ForwardConfig& c, uint32_t T, const void* ws, size_t bytes,
+                       PfWs* out) {
+    *out = pf_ws_layout(c, T);
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u))
+        return fail(Q35_ERR_INVALID_ARG, "workspace NULL or not 256-byte aligned");
+    if (bytes < out->bytes)
+        return fail(Q35_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed for %u tokens", bytes,
+                    out->bytes, T);
+    return Q35_OK;
+}
+
+// the MLP half shared by both kinds: xn2 = RMSNorm(r), gate/up SwiGLU, down + r -> x_out
+template <class L>
+q35_status pf_mlp(const Qwen35ForwardConfig& c, const L& l, const PfWs& w, void* ws, uint32_t T,
+                  void* x_out, hipStream_t stream) {
+    uint16_t* xh = at_off<uint16_t>(ws, w.xh);
+    float* r = at_off<float>(ws, w.r);
+    uint16_t* h = at_off<uint16_t>(ws, w.h);
+    Q35_HIP(pf_rmsnorm_launch(r, true, l.post_ln, xh, T, c.hidden, c.rms_eps, stream), "prefill post norm");
+    Q35_TRY(pf_gemm("prefill gate/up", kPfSwiglu, xh, T, l.gate_proj, &l.up_proj, h, c.intermediate, nullptr,
+                    false, false, stream));
+    Q35_TRY(pf_gemm("prefill down", kPfResid, h, T, l.down_proj, nullptr, x_out, c.hidden, r, true,
+                    c.act_dtype == Q35_ACT_F32, stream));
+    return Q35_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+q35_status q35_prefill_workspace_bytes(const Qwen35ForwardConfig* cfg, uint32_t max_tokens,
+                                       size_t* bytes) {
+    Q35_TRY(q35_config_validate(cfg));
+    if (!bytes) return fail(Q35_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = pf_ws_layout(*cfg, max_tokens).bytes;
+    return ok();
+}
+
+q35_status q35_prefill_linear_attention(const Qwen35Kernels* kernels,
+                                        const Qwen35ForwardConfig* cfg,
+                                        const LinearAttentionLayer* layer,
+                                        const LinearAttentionState* state, const void* x_in,
+                                        uint32_t n_tokens, void* x_out, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+    Q35_TRY(check_kernels(kernels));
+    Q35_TRY(q35_config_validate(cfg));
+    if (!layer || !state) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    const Qwen35ForwardConfig& c = *cfg;
+    Q35_TRY(check_linear_layer(c, *layer, *state));
+    Q35_TRY(need(x_in, "x_in", false));
+    Q35_TRY(need(x_out, "x_out", false));
+    const uint32_t dk = c.k_head_dim_lin, dv = c.v_head_dim_lin, hv = c.num_v_heads_lin;
+    if (!pf_gdn_dims_supported(dk, dv))
+        return fail(Q35_ERR_UNSUPPORTED, "prefill GDN head dims %u x %u (32, 64 or 128, equal)", dk, dv);
+    PfWs w;
+    Q35_TRY(pf_check_ws(c, n_tokens, workspace, workspace_bytes, &w));
+    if (n_tokens == 0) return ok();
+    const uint32_t T = n_tokens, C = qkv_total(c), Z = z_dim(c);
+    const bool f32 = c.act_dtype == Q35_ACT_F32;
+    void* ws = workspace;
+    const LinearAttentionLayer& l = *layer;
+    uint16_t* xh = at_off<uint16_t>(ws, w.xh);
+    float* qkv = at_off<float>(ws, w.qkv);
+    float* z = at_off<float>(ws, w.z);
+    float* fa = at_off<float>(ws, w.fa);
+    float* fb = at_off<float>(ws, w.fb);
+
+    Q35_HIP(pf_rmsnorm_launch(x_in, f32, l.input_ln, xh, T, c.hidden, c.rms_eps, stream), "prefill input norm");
+    Q35_TRY(pf_gemm("prefill in_proj_a", kPfF32, xh, T, l.in_proj_a, nullptr, fa, hv, nullptr, false, true, stream));
+    Q35_TRY(pf_gemm("prefill in_proj_b", kPfF32, xh, T, l.in_proj_b, nullptr, fb, hv, nullptr, false, true, stream));
+    Q35_TRY(pf_gemm("prefill in_proj_qkv", kPfF32, xh, T, l.in_proj_qkv, nullptr, qkv, C, nullptr, false, true,
+                    stream));
+    Q35_TRY(pf_gemm("prefill in_proj_z", kPfF32, xh, T, l.in_proj_z, nullptr, z, Z, nullptr, false, true, stream));
+
+    PfConvArgs cv{};
+    cv.qkv = qkv;
+    cv.conv_state = state->conv1d_state;
+    cv.conv_w = l.conv1d_weight;
+    cv.a_raw = fa;
+    cv.b_raw = fb;
+    cv.a_log = l.a_log;
+    cv.dt_bias = l.dt_bias;
+    cv.qkvs = at_off<float>(ws, w.qkvs);
+    cv.lg = at_off<float>(ws, w.lg);
+    cv.beta = at_off<float>(ws, w.beta);
+    cv.T = T;
+    cv.C = C;
+    cv.nqk = 2 * c.num_k_heads_lin * dk;
+    cv.dk = dk;
+    cv.hv = hv;
+    PfGdnArgs g{};
+    g.qkvs = cv.qkvs;
+    g.lg = cv.lg;
+    g.beta = cv.beta;
+    g.Wc = at_off<float>(ws, w.wc);
+    g.Uc = at_off<float>(ws, w.uc);
+    g.Pc = at_off<float>(ws, w.pc);
+    g.Lc = at_off<float>(ws, w.lc);
+    g.y = at_off<float>(ws, w.y);
+    g.state = state->gdn_state;
+    g.T = T;
+    g.C = C;
+    g.hk = c.num_k_heads_lin;
+    g.hv = hv;
+    g.dk = dk;
+    g.dv = dv;
+    g.nch = w.nch;
+    g.out_scale = 1.0f / std::sqrt((float)dk);
+    Q35_HIP(pf_gdn_launch(cv, g, state->conv1d_state, stream), "prefill gated delta rule");
+    uint16_t* yz = at_off<uint16_t>(ws, w.yz);
+    Q35_HIP(pf_gdn_out_launch(g.y, z, l.norm_weight, yz, T, hv, dv, c.rms_eps, stream), "prefill gated norm");
+    Q35_TRY(pf_gemm("prefill out_proj", kPfResid, yz, T, l.out_proj, nullptr, at_off<float>(ws, w.r), c.hidden,
+                    x_in, f32, true, stream));
+    Q35_TRY(pf_mlp(c, l, w, ws, T, x_out, stream));
+    return ok();
+}
+
+q35_status q35_prefill_full_attention(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                                      const FullAttentionLayer* layer, const LayerKvCache* kv,
+                                      const float* inv_freq, const void* x_in, uint32_t n_tokens,
+                                      uint32_t cache_pos, void* x_out, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+    Q35_TRY(check_kernels(kernels));
+    Q35_TRY(q35_config_validate(cfg));
+    if (!layer || !kv) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    const Qwen35ForwardConfig& c = *cfg;
+    Q35_TRY(check_full_layer(c, *layer));
+    Q35_TRY(check_kv(*kv, false));
+    Q35_TRY(need(inv_freq, "inv_freq", false));
+    Q35_TRY(need(x_in, "x_in", false));
+    Q35_TRY(need(x_out, "x_out", false));
+    const uint32_t G = c.num_heads / c.num_kv_heads;
+    if (!pf_attn_dims_supported(c.head_dim, G))
+        return fail(Q35_ERR_UNSUPPORTED, "prefill attention head_dim %u, group %u", c.head_dim, G);
+    if ((uint64_t)cache_pos + n_tokens > kv->capacity)
+        return fail(Q35_ERR_OUT_OF_RANGE, "cache_pos %u + %u tokens > capacity %u", cache_pos, n_tokens,
+                    kv->capacity);
+    PfWs w;
+    Q35_TRY(pf_check_ws(c, n_tokens, workspace, workspace_bytes, &w));
+    if (n_tokens == 0) return ok();
+    const uint32_t T = n_tokens;
+    const bool f32 = c.act_dtype == Q35_ACT_F32;
+    void* ws = workspace;
+    const FullAttentionLayer& l = *layer;
+    uint16_t* xh = at_off<uint16_t>(ws, w.xh);
+    float* qf = at_off<float>(ws, w.qf);
+    float* kf = at_off<float>(ws, w.kf);
+    float* vf = at_off<float>(ws, w.vf);
+    Q35_HIP(pf_rmsnorm_launch(x_in, f32, l.input_ln, xh, T, c.hidden, c.rms_eps, stream), "prefill input norm");
+    Q35_TRY(pf_gemm("prefill q_proj", kPfF32, xh, T, l.q_proj, nullptr, qf, q_total(c), nullptr, false, true,
+                    stream));
+    Q35_TRY(pf_gemm("prefill k_proj", kPfF32, xh, T, l.k_proj, nullptr, kf, kv_dim(c), nullptr, false, true,
+                    stream));
+    Q35_TRY(pf_gemm("prefill v_proj", kPfF32, xh, T, l.v_proj, nullptr, vf, kv_dim(c), nullptr, false, true,
+                    stream));
+    PfRopeArgs rp{};
+    rp.q_full = qf;
+    rp.k = kf;
+    rp.v = vf;
+    rp.q_norm = l.q_norm;
+    rp.k_norm = l.k_norm;
+    rp.inv_freq = inv_freq;
+    rp.qb = at_off<uint16_t>(ws, w.qb);
+    rp.kc = static_cast<uint16_t*>(kv->k);
+    rp.vc = static_cast<uint16_t*>(kv->v);
+    rp.T = T;
+    rp.cache_pos = cache_pos;
+    rp.hq = c.num_heads;
+    rp.hkv = c.num_kv_heads;
+    rp.D = c.head_dim;
+    rp.rotary = c.rotary_dim;
+    rp.eps = c.rms_eps;
+    PfAttnArgs at{};
+    at.qb = rp.qb;
+    at.q_full = qf;
+    at.kc = rp.kc;
+    at.vc = rp.vc;
+    at.ga = at_off<uint16_t>(ws, w.ga);
+    at.T = T;
+    at.cache_pos = cache_pos;
+    at.hq = c.num_heads;
+    at.hkv = c.num_kv_heads;
+    at.scale_log2 = 1.4426950408889634f / std::sqrt((float)c.head_dim);
+    Q35_HIP(pf_attn_launch(rp, at, stream), "prefill attention");
+    Q35_TRY(pf_gemm("prefill o_proj", kPfResid, at.ga, T, l.o_proj, nullptr, at_off<float>(ws, w.r), c.hidden,
+                    x_in, f32, true, stream));
+    Q35_TRY(pf_mlp(c, l, w, ws, T, x_out, stream));
+    return ok();
+}
+
+q35_status q35_prefill_gemm(const Qwen35Kernels* kernels, const Q35QuantWeight* w, const uint16_t* x_f16,
+                            uint32_t m, float* y, hipStream_t stream) {
+    Q35_TRY(check_kernels(kernels));
+    if (!w) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    Q35_TRY(check_weight("w", *w, w->n, w->k));
+    if (w->n == 0 || w->k == 0 || w->k % 64 != 0)
+        return fail(Q35_ERR_INVALID_ARG, "w: shape [%u, %u] (k a nonzero multiple of 64)", w->n, w->k);
+    Q35_TRY(need(x_f16, "x_f16"));
+    Q35_TRY(need(y, "y", false));
+    if (m == 0) return ok();
+    Q35_TRY(pf_gemm("prefill GEMM", kPfF32, x_f16, m, *w, nullptr, y, w->n, nullptr, false, true, stream));
     return ok();
 }
 

@@ -1,0 +1,849 @@
+// Multi-token prefill of the two Qwen3.5 layer kinds (gfx950).
+//
+// The pages' forward module runs one token (rustdoc index "Module qwen3_5",
+// first paragraph; the prompt pass is left to the caller).  A prefill of T
+// tokens is defined as T decode steps in order, token t at cache position
+// cache_pos + t; here the T tokens go through each step together:
+//
+//  * every projection is one GEMM over the T rows (MFMA 32x32x16 f16: the
+//    8-bit codes are dequantised to f16 on their way into LDS, the inputs are
+//    the f16 rows the norm kernels write);
+//  * the causal conv1d, the gates and the per-head L2 norm run per token, the
+//    conv state then advances by T inputs at once;
+//  * the gated delta rule runs in chunks of 64 tokens: a chunk's corrections
+//    solve a unit lower-triangular system built from its own keys (no state
+//    needed, all chunks in parallel), and one pass per head then carries the
+//    state across the chunks (linear_attention.rs page, the recurrence
+//    kernel's update order);
+//  * the causal attention is a flash-style pass over K/V tiles of the bf16
+//    cache (MFMA 32x32x16 f16) with the online softmax, output gate fused.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "q35decode.h"
+#include "q35_device.h"
+#include "q35_internal.h"
+
+namespace q35 {
+namespace pf {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+Q35_DEV float silu(float x) { return x / (1.0f + expf(-x)); }
+
+Q35_DEV uint32_t pack_h2(float a, float b) {
+    half2v h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+Q35_DEV uint16_t to_h(float a) { return __builtin_bit_cast(uint16_t, (_Float16)a); }
+
+// two bf16 (low half first) -> two f16, through fp32 (exact for normal bf16 values
+// of magnitude up to 65504; smaller than 2^-14 they keep f16's subnormal step)
+Q35_DEV uint32_t bf2_to_h2(uint32_t w) { return pack_h2(bf16_lo(w), bf16_hi(w)); }
+
+// ====================================================================== GEMM
+//
+// out[m, n] = sum_k x[m, k] * W[n, k], W[n, k] = s[n, k/64] * code[n, k] + b[n, k/64]
+// (weights dequantised in fp32, rounded once to f16).  Block tile 128 (rows of
+// x) x 128 (rows of W) x 64 (one quantisation group); four waves, each 64 x 64
+// as 2 x 2 MFMA tiles.  SwiGLU mode: the 128 W rows are 64 gate rows and the
+// same 64 up rows; a wave holds a gate tile and its up tile, so the epilogue
+// is elementwise in registers.
+
+constexpr int kBM = 128, kBN = 128, kBK = 64, kRow = kBK + 8;  // LDS row: 144 bytes
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void gemm_kernel(PfGemmArgs a) {
+    __shared__ __align__(16) _Float16 xs[2][kBM * kRow];
+    __shared__ __align__(16) _Float16 ws[2][kBN * kRow];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int wm = wid >> 1, wn = wid & 1;
+    const uint32_t m0 = blockIdx.y * kBM;
+    const uint32_t n0 = blockIdx.x * (MODE == kPfSwiglu ? kBN / 2 : kBN);
+    const uint32_t nk = a.K / kBK, ng = a.K / 64;
+
+    // global -> register staging of one k tile
+    uint4 xr[4];
+    uint4 wr[2];
+    float sc[2], bi[2];
+    auto load = [&](uint32_t kt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
+            const uint32_t m = m0 + row;
+            xr[i] = m < a.M ? *reinterpret_cast<const uint4*>(a.x + (size_t)m * a.K + kt * kBK + col)
+                            : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = tid + 256 * i, row = c >> 2, col = (c & 3) * 16;
+            const uint8_t* w = a.w0;
+            const uint16_t* s = a.s0;
+            const uint16_t* b = a.b0;
+            uint32_t n = n0 + row;
+            if (MODE == kPfSwiglu && i == 1) {  // rows 64..127: the up rows of n0..n0+63
+                w = a.w1;
+                s = a.s1;
+                b = a.b1;
+                n = n0 + row - kBN / 2;
+            }
+            if (n < a.N) {
+                wr[i] = *reinterpret_cast<const uint4*>(w + (size_t)n * a.K + kt * kBK + col);
+                sc[i] = bf16_to_f32(s[(size_t)n * ng + kt]);
+                bi[i] = bf16_to_f32(b[(size_t)n * ng + kt]);
+            } else {
+                wr[i] = make_uint4(0, 0, 0, 0);
+                sc[i] = 0.f;
+                bi[i] = 0.f;
+            }
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
+            *reinterpret_cast<uint4*>(&xs[buf][row * kRow + col]) = xr[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = tid + 256 * i, row = c >> 2, col = (c & 3) * 16;
+            const uint32_t wv[4] = {wr[i].x, wr[i].y, wr[i].z, wr[i].w};
+            uint32_t h[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t v = wv[q];
+                h[2 * q] = pack_h2(fmaf(sc[i], (float)(v & 0xFFu), bi[i]),
+                                   fmaf(sc[i], (float)((v >> 8) & 0xFFu), bi[i]));
+                h[2 * q + 1] = pack_h2(fmaf(sc[i], (float)((v >> 16) & 0xFFu), bi[i]),
+                                       fmaf(sc[i], (float)(v >> 24), bi[i]));
+            }
+            uint4* dst = reinterpret_cast<uint4*>(&ws[buf][row * kRow + col]);
+            dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
+            dst[1] = make_uint4(h[4], h[5], h[6], h[7]);
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // LDS rows this wave reads: x rows 64 wm + 32 mi + lane%32; W rows per mode
+    int wrow[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        wrow[j] = (MODE == kPfSwiglu ? j * 64 + 32 * wn : 64 * wn + 32 * j) + (lane & 31);
+    const int koff = 8 * (lane >> 5);
+
+    load(0);
+    stash(0);
+    __syncthreads();
+    for (uint32_t kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) load(kt + 1);
+#pragma unroll
+        for (int ks = 0; ks < kBK / 16; ++ks) {
+            half8 av[2], bv[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                av[i] = *reinterpret_cast<const half8*>(
+                    &xs[cur][(64 * wm + 32 * i + (lane & 31)) * kRow + ks * 16 + koff]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bv[j] = *reinterpret_cast<const half8*>(&ws[cur][wrow[j] * kRow + ks * 16 + koff]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < nk) stash(cur ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: acc[i][j][r] is (row 8 (r/4) + 4 (lane/32) + r%4, column lane%32) of its tile
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint32_t m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (m >= a.M) continue;
+            if constexpr (MODE == kPfSwiglu) {
+                const uint32_t n = n0 + 32 * wn + (lane & 31);
+                if (n < a.N)
+                    static_cast<uint16_t*>(a.out)[(size_t)m * a.ldo + n] =
+                        to_h(silu(acc[i][0][r]) * acc[i][1][r]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const uint32_t n = n0 + 64 * wn + 32 * j + (lane & 31);
+                    if (n >= a.N) continue;
+                    const size_t o = (size_t)m * a.ldo + n;
+                    if constexpr (MODE == kPfF32) {
+                        static_cast<float*>(a.out)[o] = acc[i][j][r];
+                    } else {
+                        const float v = acc[i][j][r] + load_act(a.resid, o, a.resid_f32);
+                        store_act(a.out, o, v, a.out_f32);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ====================================================================== row norms
+
+// out[t, :] = f16(x[t, :] * w / sqrt(mean(x[t, :]^2) + eps)); one block per row.
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const void* x, uint32_t x_f32,
+                                                           const uint16_t* w, uint16_t* out,
+                                                           uint32_t H, float eps) {
+    __shared__ float red[4];
+    const size_t base = (size_t)blockIdx.x * H;
+    float ss = 0.f;
+    for (uint32_t i = threadIdx.x; i < H; i += 256) {
+        const float v = load_act(x, base + i, x_f32);
+        ss = fmaf(v, v, ss);
+    }
+    ss = block_sum<256>(ss, red);
+    const float rs = 1.0f / sqrtf(ss / (float)H + eps);
+    for (uint32_t i = threadIdx.x; i < H; i += 256)
+        out[base + i] = to_h(load_act(x, base + i, x_f32) * rs * bf16_to_f32(w[i]));
+}
+
+// ====================================================================== GDN: conv, gates
+
+// One block per token: causal depthwise conv over the last K raw inputs (the
+// conv state supplies those before the first token), SiLU, the L2 norm of each
+// Q and K head, and the token's decay (as log g) and beta.
+__global__ __launch_bounds__(256) void gdn_conv_kernel(PfConvArgs a) {
+    extern __shared__ float sq[];  // [nqk]
+    const uint32_t t = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const size_t row = (size_t)t * a.C;
+    for (uint32_t c = tid; c < a.C; c += 256) {
+        float u = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int tau = (int)t - 3 + j;
+            const float in = tau >= 0 ? a.qkv[(size_t)tau * a.C + c] : a.conv_state[c * 4 + 4 + tau];
+            u = fmaf(bf16_to_f32(a.conv_w[c * 4 + j]), in, u);
+        }
+        const float s = silu(u);
+        if (c < a.nqk)
+            sq[c] = s;
+        else
+            a.qkvs[row + c] = s;
+    }
+    if (tid < (int)a.hv) {
+        const float av = a.a_raw[(size_t)t * a.hv + tid] + bf16_to_f32(a.dt_bias[tid]);
+        const float sp = av > 20.0f ? av : log1pf(expf(av));
+        a.lg[(size_t)t * a.hv + tid] = -expf(a.a_log[tid]) * sp;
+        a.beta[(size_t)t * a.hv + tid] = 1.0f / (1.0f + expf(-a.b_raw[(size_t)t * a.hv + tid]));
+    }
+    __syncthreads();
+    const uint32_t nh = a.nqk / a.dk;
+    for (uint32_t h = wid; h < nh; h += 4) {
+        float ss = 0.f;
+        for (uint32_t i = lane; i < a.dk; i += 64) ss = fmaf(sq[h * a.dk + i], sq[h * a.dk + i], ss);
+        ss = wave_sum(ss);
+        const float inv = 1.0f / sqrtf(ss + 1e-6f);
+        for (uint32_t i = lane; i < a.dk; i += 64) a.qkvs[row + h * a.dk + i] = sq[h * a.dk + i] * inv;
+    }
+}
+
+// The conv state after T tokens: the last four raw inputs per channel (older
+// state entries where T < 4).
+__global__ __launch_bounds__(256) void gdn_conv_state_kernel(const float* qkv, float* state,
+                                                             uint32_t T, uint32_t C) {
+    const uint32_t c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= C) return;
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int tau = (int)T - 4 + j;
+        v[j] = tau >= 0 ? qkv[(size_t)tau * C + c] : state[c * 4 + 4 + tau];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) state[c * 4 + j] = v[j];
+}
+
+// ====================================================================== GDN: chunks
+//
+// Within a chunk of 64 tokens (L_r = running sum of log g from the chunk
+// start), the recurrence S_r = g_r S_{r-1} + k_r d_r^T with
+// d_r = beta_r (v_r - g_r S_{r-1}^T k_r) gives, for the corrections D = [d_r],
+//   (I + A) D = beta V - beta e^L (K S0),  A[r][s] = beta_r e^(L_r - L_s) k_r.k_s  (s < r)
+// so D = U - W S0 with U = (I + A)^-1 beta V and W = (I + A)^-1 beta e^L K,
+// both free of the state.  The outputs and the state at the chunk end are
+//   y_r = e^(L_r) S0^T q_r + sum_{s <= r} e^(L_r - L_s) (q_r.k_s) d_s
+//   S_end = e^(L_end) S0 + sum_s e^(L_end - L_s) k_s d_s^T.
+// gdn_chunk_kernel builds U, W, P[r][s] = e^(L_r - L_s) q_r.k_s (s <= r) and L
+// for every (head, chunk); gdn_scan_kernel carries the state.
+
+constexpr int kC = 64;
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void gdn_chunk_kernel(PfGdnArgs a) {
+    static_assert(DK + DV <= 256 && DK % 4 == 0, "chunk kernel: one thread per column of [V | K]");
+    constexpr int KR = DK + 4;
+    __shared__ __align__(16) float ks[kC * KR];
+    __shared__ __align__(16) float qs[kC * KR];
+    __shared__ __align__(16) float am[kC * 68];   // A, row-major
+    __shared__ __align__(16) float at[kC * 68];   // A, transposed
+    __shared__ float xsol[(kC - 16) * (DK + DV)];  // solved rows of the first three blocks
+    __shared__ float L[kC], bt[kC];
+    const int tid = threadIdx.x;
+    const uint32_t ch = blockIdx.x, j = blockIdx.y, nch = gridDim.x;
+    const uint32_t i = j / (a.hv / a.hk);
+    const uint32_t t0 = ch * kC;
+    const int n = (int)min((uint32_t)kC, a.T - t0);
+    const uint32_t qoff = i * DK, koff = a.hk * DK + i * DK, voff = 2 * a.hk * DK + j * DV;
+
+    for (int c = tid; c < kC * DK / 4; c += 256) {
+        const int r = c / (DK / 4), d = (c % (DK / 4)) * 4;
+        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
+        if (r < n) {
+            const float* src = a.qkvs + (size_t)(t0 + r) * a.C;
+            kv = *reinterpret_cast<const float4*>(src + koff + d);
+            qv = *reinterpret_cast<const float4*>(src + qoff + d);
+        }
+        *reinterpret_cast<float4*>(&ks[r * KR + d]) = kv;
+        *reinterpret_cast<float4*>(&qs[r * KR + d]) = qv;
+    }
+    if (tid < 64) {
+        float lg = tid < n ? a.lg[(size_t)(t0 + tid) * a.hv + j] : 0.f;
+        bt[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * a.hv + j] : 0.f;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {  // inclusive scan over the wave
+            const float u = __shfl_up(lg, o);
+            if (tid >= o) lg += u;
+        }
+        L[tid] = lg;
+    }
+    __syncthreads();
+
+    // Gram blocks: thread (rb, sb) -> rows 4 rb.., columns 4 sb..
+    {
+        const int rb = tid >> 4, sb = tid & 15;
+        float kk[4][4] = {}, qk[4][4] = {};
+        for (int d = 0; d < DK; d += 4) {
+            float4 kr[4], qr[4], kc[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                kr[u] = *reinterpret_cast<const float4*>(&ks[(4 * rb + u) * KR + d]);
+                qr[u] = *reinterpret_cast<const float4*>(&qs[(4 * rb + u) * KR + d]);
+                kc[u] = *reinterpret_cast<const float4*>(&ks[(4 * sb + u) * KR + d]);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    kk[u][v] = fmaf(kr[u].x, kc[v].x, fmaf(kr[u].y, kc[v].y,
+                               fmaf(kr[u].z, kc[v].z, fmaf(kr[u].w, kc[v].w, kk[u][v]))));
+                    qk[u][v] = fmaf(qr[u].x, kc[v].x, fmaf(qr[u].y, kc[v].y,
+                               fmaf(qr[u].z, kc[v].z, fmaf(qr[u].w, kc[v].w, qk[u][v]))));
+                }
+        }
+        float* P = a.Pc + ((size_t)j * nch + ch) * kC * kC;
+        float av[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = 4 * rb + u;
+            float pv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int s = 4 * sb + v;
+                const float e = s <= r ? expf(L[r] - L[s]) : 0.f;
+                av[u][v] = s < r ? bt[r] * e * kk[u][v] : 0.f;
+                pv[v] = e * qk[u][v];
+            }
+            *reinterpret_cast<float4*>(&am[r * 68 + 4 * sb]) =
+                make_float4(av[u][0], av[u][1], av[u][2], av[u][3]);
+            *reinterpret_cast<float4*>(&P[r * kC + 4 * sb]) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            *reinterpret_cast<float4*>(&at[(4 * sb + v) * 68 + 4 * rb]) =
+                make_float4(av[0][v], av[1][v], av[2][v], av[3][v]);
+    }
+    __syncthreads();
+
+    // forward substitution, one thread per column of the right-hand side
+    // [beta V | beta e^L K], in blocks of 16 rows: a block first takes the
+    // contributions of the rows solved before it (kept in LDS), then solves its
+    // own 16 x 16 triangle in registers
+    if (tid < DK + DV) {
+        const int c = tid;
+        const size_t blk = (size_t)j * nch + ch;
+        float* out = c < DV ? a.Uc + blk * kC * DV + c : a.Wc + blk * kC * DK + (c - DV);
+        const int ld = c < DV ? DV : DK;
+        for (int rb = 0; rb < kC; rb += 16) {
+            float x[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int r = rb + u;
+                x[u] = c < DV ? (r < n ? bt[r] * a.qkvs[(size_t)(t0 + r) * a.C + voff + c] : 0.f)
+                              : bt[r] * expf(L[r]) * ks[r * KR + (c - DV)];
+            }
+            for (int s = 0; s < rb; ++s) {
+                const float xv = xsol[s * (DK + DV) + c];
+                const float4* ar = reinterpret_cast<const float4*>(&at[s * 68 + rb]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 w = ar[q];
+                    x[4 * q] = fmaf(-w.x, xv, x[4 * q]);
+                    x[4 * q + 1] = fmaf(-w.y, xv, x[4 * q + 1]);
+                    x[4 * q + 2] = fmaf(-w.z, xv, x[4 * q + 2]);
+                    x[4 * q + 3] = fmaf(-w.w, xv, x[4 * q + 3]);
+                }
+            }
+#pragma unroll
+            for (int u = 1; u < 16; ++u)
+#pragma unroll
+                for (int v = 0; v < u; ++v) x[u] = fmaf(-am[(rb + u) * 68 + rb + v], x[v], x[u]);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                out[(size_t)(rb + u) * ld] = x[u];
+                if (rb + 16 < kC) xsol[(rb + u) * (DK + DV) + c] = x[u];
+            }
+        }
+    }
+    if (tid < kC) a.Lc[((size_t)j * nch + ch) * kC + tid] = L[tid];
+}
+
+// One block per (v-head, 16 state columns): the state slice S0 [DK, 16] stays in
+// LDS and is carried through the chunks in order.
+constexpr int kSL = 16;
+
+template <int DK>
+__global__ __launch_bounds__(256) void gdn_scan_kernel(PfGdnArgs a) {
+    constexpr int KR = DK + 4;
+    constexpr int PER = DK * kSL / 256;   // state entries per thread in the update
+    constexpr int TPR = kSL / PER;        // threads per state row
+    __shared__ __align__(16) float S[DK * kSL];
+    __shared__ __align__(16) float wl[kC * KR];
+    __shared__ __align__(16) float ql[kC * KR];
+    __shared__ __align__(16) float kl[kC * KR];
+    __shared__ __align__(16) float pl[kC * 68];
+    __shared__ __align__(16) float dl[kC * kSL];
+    __shared__ float L[kC], ef[kC];
+    const int tid = threadIdx.x;
+    const uint32_t j = blockIdx.x, c0 = blockIdx.y * kSL, nch = a.nch;
+    const uint32_t dv = a.dv, i = j / (a.hv / a.hk);
+    const uint32_t qoff = i * DK, koff = a.hk * DK + i * DK;
+    float* st = a.state + (size_t)j * DK * dv;
+
+    for (int e = tid; e < DK * kSL; e += 256) S[e] = st[(e / kSL) * dv + c0 + (e % kSL)];
+
+    const int r = tid >> 2, cq = (tid & 3) * 4;   // outputs (row r, columns cq..cq+3)
+    const int ud = tid / TPR, uc = (tid % TPR) * PER;  // state update: row ud, columns uc..
+
+    for (uint32_t ch = 0; ch < nch; ++ch) {
+        const uint32_t t0 = ch * kC;
+        const int n = (int)min((uint32_t)kC, a.T - t0);
+        const size_t blk = (size_t)j * nch + ch;
+        const float* W = a.Wc + blk * kC * DK;
+        const float* P = a.Pc + blk * kC * kC;
+        for (int c = tid; c < kC * DK / 4; c += 256) {
+            const int rr = c / (DK / 4), d = (c % (DK / 4)) * 4;
+            float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), kv = qv;
+            if (rr < n) {
+                const float* src = a.qkvs + (size_t)(t0 + rr) * a.C;
+                qv = *reinterpret_cast<const float4*>(src + qoff + d);
+                kv = *reinterpret_cast<const float4*>(src + koff + d);
+            }
+            *reinterpret_cast<float4*>(&wl[rr * KR + d]) = *reinterpret_cast<const float4*>(W + rr * DK + d);
+            *reinterpret_cast<float4*>(&ql[rr * KR + d]) = qv;
+            *reinterpret_cast<float4*>(&kl[rr * KR + d]) = kv;
+        }
+        for (int c = tid; c < kC * kC / 4; c += 256) {
+            const int rr = c / (kC / 4), s = (c % (kC / 4)) * 4;
+            *reinterpret_cast<float4*>(&pl[rr * 68 + s]) = *reinterpret_cast<const float4*>(P + rr * kC + s);
+        }
+        if (tid < kC) L[tid] = a.Lc[blk * kC + tid];
+        __syncthreads();
+        if (tid < kC) ef[tid] = expf(L[kC - 1] - L[tid]);
+
+        // D = U - W S0 and Q S0 for row r, columns cq..cq+3
+        float wsum[4] = {}, qsum[4] = {};
+        for (int d = 0; d < DK; d += 4) {
+            const float4 wv = *reinterpret_cast<const float4*>(&wl[r * KR + d]);
+            const float4 qv = *reinterpret_cast<const float4*>(&ql[r * KR + d]);
+            const float wa[4] = {wv.x, wv.y, wv.z, wv.w}, qa[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float4 sv = *reinterpret_cast<const float4*>(&S[(d + e) * kSL + cq]);
+                const float sa[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    wsum[v] = fmaf(wa[e], sa[v], wsum[v]);
+                    qsum[v] = fmaf(qa[e], sa[v], qsum[v]);
+                }
+            }
+        }
+        {
+            const float* U = a.Uc + blk * kC * dv + (size_t)r * dv + c0 + cq;
+            const float4 uv = *reinterpret_cast<const float4*>(U);
+            *reinterpret_cast<float4*>(&dl[r * kSL + cq]) =
+                make_float4(uv.x - wsum[0], uv.y - wsum[1], uv.z - wsum[2], uv.w - wsum[3]);
+        }
+        __syncthreads();
+
+        // y_r = e^(L_r) (Q S0)_r + sum_s P[r][s] d_s
+        {
+            const float g = expf(L[r]);
+            float yv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) yv[v] = g * qsum[v];
+            for (int s = 0; s <= r; ++s) {
+                const float p = pl[r * 68 + s];
+                const float4 dv4 = *reinterpret_cast<const float4*>(&dl[s * kSL + cq]);
+                yv[0] = fmaf(p, dv4.x, yv[0]);
+                yv[1] = fmaf(p, dv4.y, yv[1]);
+                yv[2] = fmaf(p, dv4.z, yv[2]);
+                yv[3] = fmaf(p, dv4.w, yv[3]);
+            }
+            if (r < n) {
+                float* y = a.y + (size_t)(t0 + r) * a.hv * dv + (size_t)j * dv + c0 + cq;
+                *reinterpret_cast<float4*>(y) = make_float4(yv[0] * a.out_scale, yv[1] * a.out_scale,
+                                                            yv[2] * a.out_scale, yv[3] * a.out_scale);
+            }
+        }
+
+        // S <- e^(L_end) S0 + sum_s e^(L_end - L_s) k_s d_s^T
+        {
+            const float ge = expf(L[kC - 1]);
+            float sv[PER];
+#pragma unroll
+            for (int v = 0; v < PER; ++v) sv[v] = ge * S[ud * kSL + uc + v];
+            for (int s = 0; s < kC; ++s) {
+                const float kf = kl[s * KR + ud] * ef[s];
+#pragma unroll
+                for (int v = 0; v < PER; ++v) sv[v] = fmaf(kf, dl[s * kSL + uc + v], sv[v]);
+            }
+            __syncthreads();  // every read of S0 above is done
+#pragma unroll
+            for (int v = 0; v < PER; ++v) S[ud * kSL + uc + v] = sv[v];
+        }
+        __syncthreads();
+    }
+    for (int e = tid; e < DK * kSL; e += 256) st[(e / kSL) * dv + c0 + (e % kSL)] = S[e];
+}
+
+// yz[t, j, :] = f16(RMSNorm(y[t, j, :]; w) * silu(z[t, j, :])); one block per token.
+__global__ __launch_bounds__(256) void gdn_out_kernel(const float* y, const float* z,
+                                                      const uint16_t* w, uint16_t* yz, uint32_t hv,
+                                                      uint32_t dv, float eps) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const size_t row = (size_t)blockIdx.x * hv * dv;
+    for (uint32_t j = wid; j < hv; j += 4) {
+        float ss = 0.f;
+        for (uint32_t d = lane; d < dv; d += 64) ss = fmaf(y[row + j * dv + d], y[row + j * dv + d], ss);
+        ss = wave_sum(ss);
+        const float rs = 1.0f / sqrtf(ss / (float)dv + eps);
+        for (uint32_t d = lane; d < dv; d += 64) {
+            const size_t o = row + j * dv + d;
+            yz[o] = to_h(y[o] * rs * bf16_to_f32(w[d]) * silu(z[o]));
+        }
+    }
+}
+
+// ====================================================================== attention
+
+// One block per token: q and k per-head RMSNorm, RoPE at cache_pos + t, q to an
+// f16 row for the attention, k and v appended to the bf16 cache.
+__global__ __launch_bounds__(256) void qk_rope_append_kernel(PfRopeArgs a) {
+    extern __shared__ float buf[];  // [(hq + hkv) * D] then rsq[hq + hkv], rot[2 * R/2]
+    const uint32_t t = blockIdx.x, D = a.D, nh = a.hq + a.hkv, half = a.rotary / 2;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    float* rsq = buf + nh * D;
+    float* rot = rsq + nh;
+    const uint32_t pos = a.cache_pos + t;
+    const float* qrow = a.q_full + (size_t)t * a.hq * 2 * D;
+    for (uint32_t e = tid; e < nh * D; e += 256) {
+        const uint32_t h = e / D, d = e % D;
+        buf[e] = h < a.hq ? qrow[h * 2 * D + d] : a.k[(size_t)t * a.hkv * D + (h - a.hq) * D + d];
+    }
+    if (tid < (int)half) {
+        float sn, cs;
+        sincosf((float)pos * a.inv_freq[tid], &sn, &cs);
+        rot[2 * tid] = cs;
+        rot[2 * tid + 1] = sn;
+    }
+    __syncthreads();
+    for (uint32_t h = wid; h < nh; h += 4) {
+        float ss = 0.f;
+        for (uint32_t d = lane; d < D; d += 64) ss = fmaf(buf[h * D + d], buf[h * D + d], ss);
+        ss = wave_sum(ss);
+        if (lane == 0) rsq[h] = 1.0f / sqrtf(ss / (float)D + a.eps);
+    }
+    __syncthreads();
+    for (uint32_t e = tid; e < nh * D; e += 256) {
+        const uint32_t h = e / D, d = e % D;
+        const uint16_t* nw = h < a.hq ? a.q_norm : a.k_norm;
+        float x = buf[e] * rsq[h] * bf16_to_f32(nw[d]);
+        if (d < a.rotary) {
+            const uint32_t pd = d < half ? d + half : d - half;
+            const float xp = buf[h * D + pd] * rsq[h] * bf16_to_f32(nw[pd]);
+            const float cs = rot[2 * (d % half)], sn = rot[2 * (d % half) + 1];
+            x = d < half ? x * cs - xp * sn : x * cs + xp * sn;
+        }
+        if (h < a.hq)
+            a.qb[((size_t)t * a.hq + h) * D + d] = to_h(x);
+        else
+            a.kc[((size_t)pos * a.hkv + (h - a.hq)) * D + d] = (uint16_t)f32_to_bf16(x);
+    }
+    for (uint32_t e = tid; e < a.hkv * D; e += 256)
+        a.vc[(size_t)pos * a.hkv * D + e] = (uint16_t)f32_to_bf16(a.v[(size_t)t * a.hkv * D + e]);
+}
+
+// Causal GQA attention over the bf16 cache for 32 tokens x G heads of one kv
+// head per block (one wave per q-head), key tiles of 32.  The tiles go to LDS
+// as f16 (a bf16 value of the cache's range is exact in f16), the query is an
+// f16 row and the probabilities are rounded to f16, so the products are f16 x
+// f16 on the matrix cores with fp32 sums.  S^T = K Q^T puts one query per lane:
+// the softmax statistics are per lane (plus the partner lane l ^ 32), and the
+// probabilities in registers are already the B operand of O^T += V^T P^T.
+// Output: f16(attention * sigmoid(gate)).
+template <int D, int G>
+__global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
+    constexpr int NT = 64 * G, KRW = D + 8, VRW = 32 + 4, DT = D / 32;
+    __shared__ __align__(16) uint16_t kt_s[32 * KRW];
+    __shared__ __align__(16) uint16_t vt_s[D * VRW];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, h2 = lane >> 5;
+    const uint32_t g = blockIdx.y, h = g * G + wid;
+    const uint32_t t0 = (gridDim.x - 1 - blockIdx.x) * 32;  // longest blocks first
+    const uint32_t tq = t0 + (lane & 31);
+    const uint32_t kend = a.cache_pos + min(t0 + 32, a.T);  // rows any query here may read
+    const size_t rs = (size_t)a.hkv * D;                     // cache row stride (elements)
+
+    half8 qv[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (tq < a.T)
+            w = *reinterpret_cast<const uint4*>(a.qb + ((size_t)tq * a.hq + h) * D + ks * 16 + 8 * h2);
+        qv[ks] = __builtin_bit_cast(half8, w);
+    }
+    f32x16 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+    float m = -INFINITY, l = 0.f;
+    const uint32_t nkt = (kend + 31) / 32;
+    for (uint32_t kt = 0; kt < nkt; ++kt) {
+        const uint32_t k0 = kt * 32;
+        for (int c = tid; c < 32 * D / 8; c += NT) {
+            const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+            uint4 w = make_uint4(0, 0, 0, 0);
+            if (k0 + row < kend) w = *reinterpret_cast<const uint4*>(a.kc + (k0 + row) * rs + g * D + col);
+            *reinterpret_cast<uint4*>(&kt_s[row * KRW + col]) =
+                make_uint4(bf2_to_h2(w.x), bf2_to_h2(w.y), bf2_to_h2(w.z), bf2_to_h2(w.w));
+        }
+        for (int c = tid; c < D; c += NT) {  // 8 key quads x D/8 column octets
+            const int b = c % (D / 8), q4 = c / (D / 8);
+            uint4 w[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t key = k0 + 4 * q4 + u;
+                w[u] = key < kend ? *reinterpret_cast<const uint4*>(a.vc + key * rs + g * D + 8 * b)
+                                  : make_uint4(0, 0, 0, 0);
+            }
+            const uint32_t* p0 = reinterpret_cast<const uint32_t*>(&w[0]);
+            const uint32_t* p1 = reinterpret_cast<const uint32_t*>(&w[1]);
+            const uint32_t* p2 = reinterpret_cast<const uint32_t*>(&w[2]);
+            const uint32_t* p3 = reinterpret_cast<const uint32_t*>(&w[3]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int sh = (e & 1) * 16;
+                const uint32_t v0 = (p0[e >> 1] >> sh) & 0xFFFFu, v1 = (p1[e >> 1] >> sh) & 0xFFFFu;
+                const uint32_t v2 = (p2[e >> 1] >> sh) & 0xFFFFu, v3 = (p3[e >> 1] >> sh) & 0xFFFFu;
+                *reinterpret_cast<uint2*>(&vt_s[(8 * b + e) * VRW + 4 * q4]) =
+                    make_uint2(bf2_to_h2(v0 | (v1 << 16)), bf2_to_h2(v2 | (v3 << 16)));
+            }
+        }
+        __syncthreads();
+
+        f32x16 s;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const half8 kv = *reinterpret_cast<const half8*>(&kt_s[(lane & 31) * KRW + ks * 16 + 8 * h2]);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kv, qv[ks], s, 0, 0, 0);
+        }
+        // s[r]: key k0 + 8 (r/4) + 4 h2 + r%4, query tq
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint32_t key = k0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            const bool ok = key <= a.cache_pos + tq && key < kend;
+            s[r] = ok ? s[r] * a.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, s[r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m, mx);
+        const float al = exp2f(m - mn);
+        m = mn;
+        float ps = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            s[r] = exp2f(s[r] - mn);
+            ps += s[r];
+        }
+        l = l * al + ps;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][r] *= al;
+        half8 pb[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pb[kk][e] = (_Float16)s[8 * kk + e];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const uint16_t* vrow = &vt_s[(32 * dt + (lane & 31)) * VRW + 4 * h2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 16 * kk);
+                const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 * kk + 8);
+                const half8 vv = __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv, pb[kk], o[dt], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+    l += __shfl_xor(l, 32);
+    if (tq >= a.T) return;
+    const float inv = 1.0f / l;
+    const float* gate = a.q_full + (size_t)tq * a.hq * 2 * D + (size_t)h * 2 * D + D;
+    uint16_t* out = a.ga + ((size_t)tq * a.hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int d = 32 * dt + 8 * r4 + 4 * h2;
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float gt = gate[d + u];
+                v[u] = o[dt][4 * r4 + u] * inv / (1.0f + expf(-gt));
+            }
+            *reinterpret_cast<uint2*>(out + d) = make_uint2(pack_h2(v[0], v[1]), pack_h2(v[2], v[3]));
+        }
+}
+
+}  // namespace pf
+
+// ====================================================================== launchers
+
+const void* pf_kernel_ptr(int i) {
+    static const void* const k[] = {
+        reinterpret_cast<const void*>(pf::gemm_kernel<kPfF32>),
+        reinterpret_cast<const void*>(pf::gemm_kernel<kPfResid>),
+        reinterpret_cast<const void*>(pf::gemm_kernel<kPfSwiglu>),
+        reinterpret_cast<const void*>(pf::rmsnorm_rows_kernel),
+        reinterpret_cast<const void*>(pf::gdn_conv_kernel),
+        reinterpret_cast<const void*>(pf::gdn_conv_state_kernel),
+        reinterpret_cast<const void*>(pf::gdn_chunk_kernel<32, 32>),
+        reinterpret_cast<const void*>(pf::gdn_chunk_kernel<64, 64>),
+        reinterpret_cast<const void*>(pf::gdn_chunk_kernel<128, 128>),
+        reinterpret_cast<const void*>(pf::gdn_scan_kernel<32>),
+        reinterpret_cast<const void*>(pf::gdn_scan_kernel<64>),
+        reinterpret_cast<const void*>(pf::gdn_scan_kernel<128>),
+        reinterpret_cast<const void*>(pf::gdn_out_kernel),
+        reinterpret_cast<const void*>(pf::qk_rope_append_kernel),
+        reinterpret_cast<const void*>(pf::flash_kernel<64, 2>),
+        reinterpret_cast<const void*>(pf::flash_kernel<256, 4>),
+    };
+    return i >= 0 && i < (int)(sizeof(k) / sizeof(k[0])) ? k[i] : nullptr;
+}
+
+hipError_t pf_gemm_launch(int mode, const PfGemmArgs& a, hipStream_t s) {
+    if (a.M == 0) return hipSuccess;
+    const uint32_t bn = mode == kPfSwiglu ? pf::kBN / 2 : pf::kBN;
+    dim3 grid((a.N + bn - 1) / bn, (a.M + pf::kBM - 1) / pf::kBM);
+    switch (mode) {
+        case kPfF32: pf::gemm_kernel<kPfF32><<<grid, 256, 0, s>>>(a); break;
+        case kPfResid: pf::gemm_kernel<kPfResid><<<grid, 256, 0, s>>>(a); break;
+        case kPfSwiglu: pf::gemm_kernel<kPfSwiglu><<<grid, 256, 0, s>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t pf_rmsnorm_launch(const void* x, bool x_f32, const uint16_t* w, uint16_t* out, uint32_t T,
+                             uint32_t H, float eps, hipStream_t s) {
+    pf::rmsnorm_rows_kernel<<<T, 256, 0, s>>>(x, x_f32, w, out, H, eps);
+    return hipGetLastError();
+}
+
+bool pf_gdn_dims_supported(uint32_t dk, uint32_t dv) {
+    return dk == dv && (dk == 32 || dk == 64 || dk == 128);
+}
+
+hipError_t pf_gdn_launch(const PfConvArgs& c, const PfGdnArgs& g, float* conv_state_out,
+                         hipStream_t s) {
+    pf::gdn_conv_kernel<<<c.T, 256, c.nqk * sizeof(float), s>>>(c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    pf::gdn_conv_state_kernel<<<(c.C + 255) / 256, 256, 0, s>>>(c.qkv, conv_state_out, c.T, c.C);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    dim3 gc(g.nch, g.hv), gs(g.hv, g.dv / pf::kSL);
+    switch (g.dk) {
+        case 32:
+            pf::gdn_chunk_kernel<32, 32><<<gc, 256, 0, s>>>(g);
+            pf::gdn_scan_kernel<32><<<gs, 256, 0, s>>>(g);
+            break;
+        case 64:
+            pf::gdn_chunk_kernel<64, 64><<<gc, 256, 0, s>>>(g);
+            pf::gdn_scan_kernel<64><<<gs, 256, 0, s>>>(g);
+            break;
+        case 128:
+            pf::gdn_chunk_kernel<128, 128><<<gc, 256, 0, s>>>(g);
+            pf::gdn_scan_kernel<128><<<gs, 256, 0, s>>>(g);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t pf_gdn_out_launch(const float* y, const float* z, const uint16_t* w, uint16_t* yz,
+                             uint32_t T, uint32_t hv, uint32_t dv, float eps, hipStream_t s) {
+    pf::gdn_out_kernel<<<T, 256, 0, s>>>(y, z, w, yz, hv, dv, eps);
+    return hipGetLastError();
+}
+
+bool pf_attn_dims_supported(uint32_t d, uint32_t g) {
+    return (d == 64 || d == 128 || d == 256) && (g == 1 || g == 2 || g == 4 || g == 8);
+}
+
+hipError_t pf_attn_launch(const PfRopeArgs& r, const PfAttnArgs& a, hipStream_t s) {
+    const size_t lds = ((size_t)(r.hq + r.hkv) * r.D + (r.hq + r.hkv) + r.rotary) * sizeof(float);
+    pf::qk_rope_append_kernel<<<r.T, 256, lds, s>>>(r);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const uint32_t G = a.hq / a.hkv;
+    dim3 grid((a.T + 31) / 32, a.hkv);
+#define Q35_PF_FLASH(DD, GG)                                                  \
+    if (r.D == DD && G == GG) {                                               \
+        pf::flash_kernel<DD, GG><<<grid, 64 * GG, 0, s>>>(a);                 \
+        return hipGetLastError();                                             \
+    }
+    Q35_PF_FLASH(64, 1) Q35_PF_FLASH(64, 2) Q35_PF_FLASH(64, 4) Q35_PF_FLASH(64, 8)
+    Q35_PF_FLASH(128, 1) Q35_PF_FLASH(128, 2) Q35_PF_FLASH(128, 4) Q35_PF_FLASH(128, 8)
+    Q35_PF_FLASH(256, 1) Q35_PF_FLASH(256, 2) Q35_PF_FLASH(256, 4) Q35_PF_FLASH(256, 8)
+#undef Q35_PF_FLASH
+    return hipErrorInvalidValue;
+}
+
+}  // namespace q35

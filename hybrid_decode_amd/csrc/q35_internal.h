@@ -250,4 +250,88 @@ size_t persist_lds_bytes(int shape);
 const void* persist_kernel_ptr(int shape);
 hipError_t persist_launch(int shape, const PersistArgs& a, uint32_t blocks, hipStream_t stream);
 
+// ------------------------------------------------------------------ prefill (T tokens per launch)
+
+enum { kPfF32 = 0, kPfResid = 1, kPfSwiglu = 2 };
+
+// out[m, n] = sum_k x[m, k] W[n, k]: x f16 [M, K]; W 8-bit codes [N, K] with bf16
+// scale/bias per 64.  kPfF32: fp32 out.  kPfResid: out = resid + product (resid and
+// out fp32 or bf16 per flag).  kPfSwiglu: W0 gate, W1 up, out f16 silu(gate) * up.
+struct PfGemmArgs {
+    const uint16_t* x;
+    const uint8_t* w0;
+    const uint16_t* s0;
+    const uint16_t* b0;
+    const uint8_t* w1;
+    const uint16_t* s1;
+    const uint16_t* b1;
+    void* out;
+    const void* resid;
+    uint32_t M, N, K, ldo;
+    uint32_t resid_f32, out_f32;
+};
+hipError_t pf_gemm_launch(int mode, const PfGemmArgs& a, hipStream_t s);
+// f16 rows of RMSNorm(x) for T rows of H (x fp32 or bf16)
+hipError_t pf_rmsnorm_launch(const void* x, bool x_f32, const uint16_t* w, uint16_t* out, uint32_t T,
+                             uint32_t H, float eps, hipStream_t s);
+
+struct PfConvArgs {
+    const float* qkv;          // [T, C] conv inputs
+    const float* conv_state;   // [C, 4] before the first token
+    const uint16_t* conv_w;    // bf16 [C, 4]
+    const float* a_raw;        // [T, hv]
+    const float* b_raw;        // [T, hv]
+    const float* a_log;        // [hv]
+    const uint16_t* dt_bias;   // bf16 [hv]
+    float* qkvs;               // [T, C] conv + SiLU, Q/K heads L2-normalised
+    float* lg;                 // [T, hv] log of the decay gate
+    float* beta;               // [T, hv]
+    uint32_t T, C, nqk, dk, hv;
+};
+struct PfGdnArgs {
+    const float* qkvs;
+    const float* lg;
+    const float* beta;
+    float* Wc;                 // [hv, nch, 64, dk]
+    float* Uc;                 // [hv, nch, 64, dv]
+    float* Pc;                 // [hv, nch, 64, 64]
+    float* Lc;                 // [hv, nch, 64]
+    float* y;                  // [T, hv * dv]
+    float* state;              // [hv, dk, dv], updated
+    uint32_t T, C, hk, hv, dk, dv, nch;
+    float out_scale;
+};
+bool pf_gdn_dims_supported(uint32_t dk, uint32_t dv);
+// conv, conv-state advance, chunk build and the state scan
+hipError_t pf_gdn_launch(const PfConvArgs& c, const PfGdnArgs& g, float* conv_state_out, hipStream_t s);
+hipError_t pf_gdn_out_launch(const float* y, const float* z, const uint16_t* w, uint16_t* yz, uint32_t T,
+                             uint32_t hv, uint32_t dv, float eps, hipStream_t s);
+
+struct PfRopeArgs {
+    const float* q_full;       // [T, hq * 2D]
+    const float* k;            // [T, hkv * D]
+    const float* v;            // [T, hkv * D]
+    const uint16_t* q_norm;
+    const uint16_t* k_norm;
+    const float* inv_freq;
+    uint16_t* qb;              // f16 [T, hq, D]
+    uint16_t* kc;              // bf16 cache [cap, hkv, D]
+    uint16_t* vc;
+    uint32_t T, cache_pos, hq, hkv, D, rotary;
+    float eps;
+};
+struct PfAttnArgs {
+    const uint16_t* qb;
+    const float* q_full;       // gate halves
+    const uint16_t* kc;
+    const uint16_t* vc;
+    uint16_t* ga;              // f16 [T, hq * D]
+    uint32_t T, cache_pos, hq, hkv;
+    float scale_log2;
+};
+bool pf_attn_dims_supported(uint32_t head_dim, uint32_t group);
+hipError_t pf_attn_launch(const PfRopeArgs& r, const PfAttnArgs& a, hipStream_t s);
+// the prefill kernels, i = 0, 1, ... until nullptr (for the load check at resolve)
+const void* pf_kernel_ptr(int i);
+
 }  // namespace q35

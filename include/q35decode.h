@@ -590,6 +590,68 @@ q35_status q35_fp8_e4m3_table(const Qwen35Kernels* kernels, float* out, hipStrea
 q35_status q35_gemv(const Qwen35Kernels* kernels, const Q35QuantWeight* w, const float* x,
                     float* y, uint32_t act_dtype, hipStream_t stream);
 
+/* ------------------------------------------------------------------ prefill */
+
+/*
+ * Multi-token prefill of one layer.  The pages define the decode step only
+ * (rustdoc index "Module qwen3_5": the module runs one token; the prompt pass
+ * is the caller's).  A prefill of n_tokens tokens computes what n_tokens decode
+ * calls would, in order: token t runs at cache position cache_pos + t (its RoPE
+ * position and its KV row) and attends to rows [0, cache_pos + t]; the conv
+ * and GDN states advance token by token.  The results agree with those calls
+ * up to rounding (the projections take f16 inputs and f16-rounded weights on
+ * the matrix cores, the recurrence runs in chunks of 64 tokens, the attention
+ * takes f16 queries and f16 probabilities).
+ *
+ * Workspace: device memory of at least q35_prefill_workspace_bytes(cfg,
+ * n_tokens) bytes, 256-byte aligned, caller-owned, rewritten by every call (no
+ * initialisation needed; shared by the two layer kinds, not by concurrent
+ * calls).
+ */
+q35_status q35_prefill_workspace_bytes(const Qwen35ForwardConfig* cfg, uint32_t max_tokens,
+                                       size_t* bytes);
+
+/*
+ * n_tokens tokens through one GDN layer (linear_attention.rs page, every step
+ * of forward_linear_attention per token).  x_in and x_out: act [n_tokens,
+ * hidden], x_out may equal x_in; state: as in q35_forward_linear_attention,
+ * updated in place to the state after the last token.  n_tokens == 0 enqueues
+ * nothing.  k_head_dim_lin != v_head_dim_lin or not 32, 64 or 128:
+ * Q35_ERR_UNSUPPORTED; a small workspace: Q35_ERR_INVALID_ARG.
+ */
+q35_status q35_prefill_linear_attention(const Qwen35Kernels* kernels,
+                                        const Qwen35ForwardConfig* cfg,
+                                        const LinearAttentionLayer* layer,
+                                        const LinearAttentionState* state, const void* x_in,
+                                        uint32_t n_tokens, void* x_out, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * n_tokens tokens through one gated full-attention layer (full_attention.rs
+ * page, every step of forward_full_attention per token), the KV rows
+ * [cache_pos, cache_pos + n_tokens) appended as bf16.  x_in and x_out: act
+ * [n_tokens, hidden], x_out may equal x_in; inv_freq as in
+ * q35_forward_full_attention.  cache_pos + n_tokens > kv->capacity:
+ * Q35_ERR_OUT_OF_RANGE; a cache dtype other than bf16, or a head_dim / group
+ * the attention kernels do not cover: Q35_ERR_UNSUPPORTED.  n_tokens == 0
+ * enqueues nothing.
+ */
+q35_status q35_prefill_full_attention(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                                      const FullAttentionLayer* layer, const LayerKvCache* kv,
+                                      const float* inv_freq, const void* x_in, uint32_t n_tokens,
+                                      uint32_t cache_pos, void* x_out, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The prefill's quantised-weight GEMM: y (fp32 [m, w->n]) = x W^T with x f16
+ * [m, w->k] (16-byte aligned rows), W[n, k] = scale * code + bias evaluated in
+ * fp32 and rounded to f16, products on the matrix cores with fp32 sums.
+ * Exported so that it can be tested and timed on its own.  m == 0 enqueues
+ * nothing.
+ */
+q35_status q35_prefill_gemm(const Qwen35Kernels* kernels, const Q35QuantWeight* w,
+                            const uint16_t* x_f16, uint32_t m, float* y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -219,3 +219,68 @@ def test_gemv_shape_errors(lib):
     with pytest.raises(B.Q35Error) as e:
         B.q35_gemv(FAKE_KERNELS, w, 0x100, 0x100, B.Q35_ACT_F32, None)
     assert e.value.status == B.Q35_ERR_UNSUPPORTED
+
+
+def _prefill_layers():
+    c = B.q35_config_qwen3_5_4b()
+    fake = 0x100000
+
+    def qw(n, k):
+        return B.Q35QuantWeight(fake, fake, fake, n, k)
+    H, I = c.hidden, c.intermediate
+    full = B.FullAttentionLayer(fake, fake, fake, fake, qw(2 * c.num_heads * c.head_dim, H),
+                                qw(c.num_kv_heads * c.head_dim, H), qw(c.num_kv_heads * c.head_dim, H),
+                                qw(H, c.num_heads * c.head_dim), qw(I, H), qw(I, H), qw(H, I))
+    z = c.num_v_heads_lin * c.v_head_dim_lin
+    qkv = 2 * c.num_k_heads_lin * c.k_head_dim_lin + z
+    lin = B.LinearAttentionLayer(fake, fake, fake, fake, qw(c.num_v_heads_lin, H), qw(c.num_v_heads_lin, H),
+                                 qw(qkv, H), qw(z, H), fake, qw(H, z), fake, qw(I, H), qw(I, H), qw(H, I))
+    return c, full, lin, fake
+
+
+def test_prefill_workspace_grows_with_tokens(lib):
+    c = B.q35_config_qwen3_5_4b()
+    sizes = [B.q35_prefill_workspace_bytes(c, t) for t in (0, 1, 64, 65, 4096)]
+    assert sizes[0] == 0 and all(a < b for a, b in zip(sizes, sizes[1:]))
+    assert sizes[-1] % 256 == 0
+
+
+def test_prefill_errors_before_any_launch(lib):
+    c, full, lin, fake = _prefill_layers()
+    st = B.LinearAttentionState(fake, fake)
+    kv = B.LayerKvCache(fake, fake, 128, 0, None, None)
+    ws_bytes = B.q35_prefill_workspace_bytes(c, 100)
+    # zero tokens: nothing to enqueue, so the fake pointers are never used
+    B.q35_prefill_linear_attention(FAKE_KERNELS, c, lin, st, fake, 0, fake, fake, ws_bytes, None)
+    B.q35_prefill_full_attention(FAKE_KERNELS, c, full, kv, fake, fake, 0, 5, fake, fake, ws_bytes, None)
+    # workspace smaller than the token count needs, or misaligned
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_prefill_linear_attention(FAKE_KERNELS, c, lin, st, fake, 101, fake, fake, ws_bytes, None)
+    assert e.value.status == B.Q35_ERR_INVALID_ARG and "workspace" in str(e.value)
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_prefill_linear_attention(FAKE_KERNELS, c, lin, st, fake, 10, fake, fake + 16, ws_bytes, None)
+    assert e.value.status == B.Q35_ERR_INVALID_ARG and "aligned" in str(e.value)
+    # rows past the cache
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_prefill_full_attention(FAKE_KERNELS, c, full, kv, fake, fake, 100, 29, fake, fake, ws_bytes, None)
+    assert e.value.status == B.Q35_ERR_OUT_OF_RANGE
+    # the prefill appends bf16 rows only
+    kv.dtype = B.q35_kv_dtype_from_str("turbo8")
+    kv.k_scales, kv.v_scales = fake, fake
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_prefill_full_attention(FAKE_KERNELS, c, full, kv, fake, fake, 10, 0, fake, fake, ws_bytes, None)
+    assert e.value.status == B.Q35_ERR_UNSUPPORTED
+    # a NULL weight
+    lin.in_proj_z.codes = None
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_prefill_linear_attention(FAKE_KERNELS, c, lin, st, fake, 10, fake, fake, ws_bytes, None)
+    assert e.value.status == B.Q35_ERR_INVALID_ARG and "in_proj_z" in str(e.value)
+
+
+def test_prefill_gemm_shape_errors(lib):
+    w = B.Q35QuantWeight(0x1000, 0x2000, 0x3000, 8, 96)  # k not a multiple of 64
+    with pytest.raises(B.Q35Error) as e:
+        B.q35_prefill_gemm(FAKE_KERNELS, w, 0x100, 4, 0x100, None)
+    assert e.value.status == B.Q35_ERR_INVALID_ARG
+    w = B.Q35QuantWeight(0x1000, 0x2000, 0x3000, 8, 128)
+    B.q35_prefill_gemm(FAKE_KERNELS, w, 0x100, 0, 0x100, None)  # m == 0: nothing enqueued
