@@ -7,6 +7,12 @@ attention over a bf16 KV cache at ~8192 tokens), final RMSNorm, int8 lm_head ove
 from one replayed HIP graph.  Prints one JSON line (rank 0).
 
     python bench.py [--gpus 1] [--steps 128] [--warmup 8] [--ctx 8192] [--kv FORMAT]
+                    [--prefill-tokens 4096]
+
+With bf16 caches the line also carries "prefill": a prompt of --prefill-tokens
+tokens through the same stack with the multi-token prefill calls (timed after
+the decode, it overwrites the first cache rows), and the rate of its
+dequantising GEMM against the f16 matrix-core peak.
 """
 import argparse
 import hashlib
@@ -154,6 +160,90 @@ def cpu_baseline(cfg, w, sample_note, kv="bf16"):
             "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
 
 
+PEAK_MFMA_F16_TFLOPS = 2500.0
+
+
+def prefill_stack(torch, B, rt, st, kinds, cfg, T, reps=3):
+    """T prompt tokens through every layer of the stack (the multi-token prefill
+    calls; full layers at cache positions [0, T)); returns ms per pass."""
+    import numpy as np
+    ws_bytes = B.q35_prefill_workspace_bytes(st.c, T)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    g = np.random.default_rng(7)
+    x0 = torch.from_numpy((g.standard_normal((T, cfg.hidden), dtype=np.float32)).astype(np.float32))
+    xa = x0.to("cuda").to(torch.bfloat16).view(torch.int16).contiguous()
+    xb = torch.empty_like(xa)
+    s = rt.stream_ptr()
+
+    def one_pass():
+        x, y = xa, xb
+        for li, kind in enumerate(kinds):
+            if kind == "gdn":
+                B.q35_prefill_linear_attention(st.k, st.c, st.layers[li].struct, st.states[li].struct,
+                                               x.data_ptr(), T, y.data_ptr(), ws.data_ptr(), ws_bytes, s)
+            else:
+                B.q35_prefill_full_attention(st.k, st.c, st.layers[li].struct, st.kvs[li].struct,
+                                             st.inv_freq.data_ptr(), x.data_ptr(), T, 0, y.data_ptr(),
+                                             ws.data_ptr(), ws_bytes, s)
+            x, y = y, x
+
+    one_pass()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        one_pass()
+    e1.record()
+    torch.cuda.synchronize()
+    del ws
+    return e0.elapsed_time(e1) / reps
+
+
+def prefill_gemm_rate(torch, B, rt, st, cfg, T, rounds=2):
+    """The prefill's dequantising GEMM at the gate_proj shape (T x intermediate x
+    hidden), every layer's weights in turn; returns (us per launch, flops per launch)."""
+    x = torch.zeros((T, cfg.hidden), dtype=torch.int16, device="cuda")
+    y = torch.empty((T, cfg.intermediate), dtype=torch.float32, device="cuda")
+    s = rt.stream_ptr()
+    B.q35_prefill_gemm(st.k, st.layers[0].q["gate_proj"].struct, x.data_ptr(), T, y.data_ptr(), s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(rounds):
+        for L in st.layers:
+            B.q35_prefill_gemm(st.k, L.q["gate_proj"].struct, x.data_ptr(), T, y.data_ptr(), s)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (rounds * len(st.layers))
+    return us, 2.0 * T * cfg.intermediate * cfg.hidden
+
+
+def prefill_cpu_baseline(cfg, w, n=8):
+    """The prefill oracle (the decode step looped over the tokens) on n tokens
+    through one GDN and one full-attention layer, composed over the stack."""
+    import numpy as np
+
+    import oracle as O
+    kinds = w["kinds"]
+    gi, fi = kinds.index("gdn"), kinds.index("full")
+    x = w["embed"][np.arange(n) + 1]
+    inv = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
+    kv = {"k": np.zeros((n, cfg.num_kv_heads, cfg.head_dim), np.uint16),
+          "v": np.zeros((n, cfg.num_kv_heads, cfg.head_dim), np.uint16)}
+    t0 = time.perf_counter()
+    O.prefill.prefill_linear_attention(cfg, w["layers"][gi], w["states"][gi], x)
+    t_gdn = (time.perf_counter() - t0) / n
+    t0 = time.perf_counter()
+    O.prefill.prefill_full_attention(cfg, w["layers"][fi], kv, inv, x, 0)
+    t_full = (time.perf_counter() - t0) / n
+    t_tok = kinds.count("gdn") * t_gdn + kinds.count("full") * t_full
+    return 1.0 / t_tok, (f"float64 prefill oracle as it stands (the decode step looped over the "
+                         f"tokens; each call dequantises its layer once) on {n} tokens through one GDN "
+                         f"layer ({t_gdn:.3f}s/token) and one full layer at cache positions 0..{n - 1} "
+                         f"({t_full:.3f}s/token), composed over {kinds.count('gdn')} + "
+                         f"{kinds.count('full')} layers")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +253,8 @@ def main():
     ap.add_argument("--ctx", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dominant-rounds", type=int, default=4)
+    ap.add_argument("--prefill-tokens", type=int, default=4096,
+                    help="also time a prompt of this many tokens through the stack (0: skip)")
     ap.add_argument("--kv", choices=["bf16", "turbo8", "turbo4", "turbo3", "turbo2", "bf16k_turbo4v",
                                      "bf16k_turbo3v", "bf16k_turbo2v"], default="bf16",
                     help="KV cache format of the full-attention layers")
@@ -283,6 +375,25 @@ def main():
     log(f"device copy of {copy_bytes >> 20} MiB: {copy_gbs:.0f} GB/s (read + write)")
     traffic = measured_traffic()
 
+    prefill = None
+    if args.prefill_tokens > 0 and args.kv == "bf16":
+        T = min(args.prefill_tokens, min(kv.capacity for kv in st.kvs if kv is not None))
+        pf_ms = prefill_stack(torch, B, rt, st, kinds, cfg, T)
+        g_us, g_flops = prefill_gemm_rate(torch, B, rt, st, cfg, T)
+        g_tf = g_flops / (g_us * 1e-6) / 1e12
+        log(f"prefill of {T} tokens through {len(kinds)} layers: {pf_ms:.2f} ms ({T / pf_ms * 1e3:.0f} tok/s); "
+            f"GEMM {T}x{cfg.intermediate}x{cfg.hidden}: {g_us:.1f} us, {g_tf:.0f} TFLOP/s")
+        prefill = {
+            "tokens": T, "ms": round(pf_ms, 3), "tok_s": round(T / pf_ms * 1e3, 1),
+            "workload": (f"{T}-token prompt (synthetic bf16 rows) through the {len(kinds)}-layer stack, "
+                         f"full layers at cache positions 0..{T - 1}"),
+            "roofline": {"bound": "mfma", "kernel": "pf::gemm_kernel<0> (dequantising f16 GEMM, "
+                                                    f"{T} x {cfg.intermediate} x {cfg.hidden})",
+                         "achieved": round(g_tf, 1), "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(g_tf / PEAK_MFMA_F16_TFLOPS, 4), "traffic": None,
+                         "flops_per_launch": g_flops, "us_per_launch": round(g_us, 2)},
+        }
+
     kv_desc = {"bf16": "bf16", "turbo8": "Turbo8 (WHT-rotated E4M3 + bf16 scale per 16)"}.get(args.kv)
     if kv_desc is None:
         b = lm_bits[args.kv]
@@ -332,6 +443,13 @@ def main():
                 "lm_head)").replace("{kv}", args.kv)
         result["cpu_baseline"] = cpu_baseline(cfg, w, note, args.kv)
         log(f"oracle: {result['cpu_baseline']['value']:.4f} tok/s")
+    if prefill is not None:
+        if not args.no_cpu_baseline:
+            v, note = prefill_cpu_baseline(cfg, w)
+            prefill["cpu_baseline"] = {"value": v, "unit": "tok/s", "kind": "oracle", "sample": note,
+                                       "cores": result["cpu_baseline"]["cores"]}
+            log(f"prefill oracle: {v:.4f} tok/s")
+        result["prefill"] = prefill
     print(json.dumps(result), flush=True)
 
 

@@ -66,17 +66,19 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(PfGemmArgs a) {
     const uint32_t n0 = blockIdx.x * (MODE == kPfSwiglu ? kBN / 2 : kBN);
     const uint32_t nk = a.K / kBK, ng = a.K / 64;
 
-    // global -> register staging of one k tile
-    uint4 xr[4];
-    uint4 wr[2];
-    float sc[2], bi[2];
-    auto load = [&](uint32_t kt) {
+    // global -> register staging of one k tile (two stages in flight)
+    struct Stage {
+        uint4 xr[4];
+        uint4 wr[2];
+        float sc[2], bi[2];
+    };
+    auto load = [&](Stage& g, uint32_t kt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
             const uint32_t m = m0 + row;
-            xr[i] = m < a.M ? *reinterpret_cast<const uint4*>(a.x + (size_t)m * a.K + kt * kBK + col)
-                            : make_uint4(0, 0, 0, 0);
+            g.xr[i] = m < a.M ? *reinterpret_cast<const uint4*>(a.x + (size_t)m * a.K + kt * kBK + col)
+                              : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -92,34 +94,33 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(PfGemmArgs a) {
                 n = n0 + row - kBN / 2;
             }
             if (n < a.N) {
-                wr[i] = *reinterpret_cast<const uint4*>(w + (size_t)n * a.K + kt * kBK + col);
-                sc[i] = bf16_to_f32(s[(size_t)n * ng + kt]);
-                bi[i] = bf16_to_f32(b[(size_t)n * ng + kt]);
+                g.wr[i] = *reinterpret_cast<const uint4*>(w + (size_t)n * a.K + kt * kBK + col);
+                g.sc[i] = bf16_to_f32(s[(size_t)n * ng + kt]);
+                g.bi[i] = bf16_to_f32(b[(size_t)n * ng + kt]);
             } else {
-                wr[i] = make_uint4(0, 0, 0, 0);
-                sc[i] = 0.f;
-                bi[i] = 0.f;
+                g.wr[i] = make_uint4(0, 0, 0, 0);
+                g.sc[i] = 0.f;
+                g.bi[i] = 0.f;
             }
         }
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](const Stage& g, int buf) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-            *reinterpret_cast<uint4*>(&xs[buf][row * kRow + col]) = xr[i];
+            *reinterpret_cast<uint4*>(&xs[buf][row * kRow + col]) = g.xr[i];
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int c = tid + 256 * i, row = c >> 2, col = (c & 3) * 16;
-            const uint32_t wv[4] = {wr[i].x, wr[i].y, wr[i].z, wr[i].w};
+            const uint32_t wv[4] = {g.wr[i].x, g.wr[i].y, g.wr[i].z, g.wr[i].w};
+            const float sc = g.sc[i], bi = g.bi[i];
             uint32_t h[8];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const uint32_t v = wv[q];
-                h[2 * q] = pack_h2(fmaf(sc[i], (float)(v & 0xFFu), bi[i]),
-                                   fmaf(sc[i], (float)((v >> 8) & 0xFFu), bi[i]));
-                h[2 * q + 1] = pack_h2(fmaf(sc[i], (float)((v >> 16) & 0xFFu), bi[i]),
-                                       fmaf(sc[i], (float)(v >> 24), bi[i]));
+                h[2 * q] = pack_h2(fmaf(sc, (float)(v & 0xFFu), bi), fmaf(sc, (float)((v >> 8) & 0xFFu), bi));
+                h[2 * q + 1] = pack_h2(fmaf(sc, (float)((v >> 16) & 0xFFu), bi), fmaf(sc, (float)(v >> 24), bi));
             }
             uint4* dst = reinterpret_cast<uint4*>(&ws[buf][row * kRow + col]);
             dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
@@ -142,12 +143,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(PfGemmArgs a) {
         wrow[j] = (MODE == kPfSwiglu ? j * 64 + 32 * wn : 64 * wn + 32 * j) + (lane & 31);
     const int koff = 8 * (lane >> 5);
 
-    load(0);
-    stash(0);
-    __syncthreads();
-    for (uint32_t kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) load(kt + 1);
+    auto compute = [&](int cur) {
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
             half8 av[2], bv[2];
@@ -164,7 +160,24 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(PfGemmArgs a) {
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < nk) stash(cur ^ 1);
+    };
+
+    // k tile kt sits in LDS buffer kt % 2 while tile kt + 1 waits in registers and
+    // tile kt + 2 is being fetched
+    Stage g0, g1;
+    load(g0, 0);
+    if (nk > 1) load(g1, 1);
+    stash(g0, 0);
+    __syncthreads();
+    for (uint32_t kt = 0; kt < nk; kt += 2) {
+        if (kt + 2 < nk) load(g0, kt + 2);
+        compute(0);
+        if (kt + 1 < nk) stash(g1, 1);
+        __syncthreads();
+        if (kt + 1 >= nk) break;
+        if (kt + 3 < nk) load(g1, kt + 3);
+        compute(1);
+        if (kt + 2 < nk) stash(g0, 0);
         __syncthreads();
     }
 
@@ -423,7 +436,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(PfGdnArgs a) {
 constexpr int kSL = 16;
 
 template <int DK>
-__global__ __launch_bounds__(256) void gdn_scan_kernel(PfGdnArgs a) {
+__global__ __launch_bounds__(256, 1) void gdn_scan_kernel(PfGdnArgs a) {
     constexpr int KR = DK + 4;
     constexpr int PER = DK * kSL / 256;   // state entries per thread in the update
     constexpr int TPR = kSL / PER;        // threads per state row
@@ -445,30 +458,59 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(PfGdnArgs a) {
     const int r = tid >> 2, cq = (tid & 3) * 4;   // outputs (row r, columns cq..cq+3)
     const int ud = tid / TPR, uc = (tid % TPR) * PER;  // state update: row ud, columns uc..
 
+    // chunk ch + 1's operands are fetched into registers while chunk ch computes
+    constexpr int NW4 = kC * DK / 4 / 256;
+    struct Regs {
+        float4 w[NW4], q[NW4], k[NW4], p[4], u;
+        float l;
+    } R;
+    // buffer loads (not plain loads, which the compiler may turn into a copy
+    // through scratch); a resource over the chunk's own token rows returns zero
+    // for the rows past the last token
+    auto gload = [&](Regs& g, uint32_t ch) {
+        const uint32_t t0 = ch * kC;
+        const uint32_t n = min((uint32_t)kC, a.T - t0);
+        const size_t blk = (size_t)j * nch + ch;
+        const auto rW = rsrc(a.Wc + blk * kC * DK, kC * DK * 4);
+        const auto rP = rsrc(a.Pc + blk * kC * kC, kC * kC * 4);
+        const auto rX = rsrc(a.qkvs + (size_t)t0 * a.C, n * a.C * 4);
+#pragma unroll
+        for (int i = 0; i < NW4; ++i) {
+            const uint32_t c = tid + 256 * i, rr = c / (DK / 4), d = (c % (DK / 4)) * 4;
+            g.w[i] = __builtin_bit_cast(float4, ld_b128<0>(rW, (rr * DK + d) * 4));
+            g.q[i] = __builtin_bit_cast(float4, ld_b128<0>(rX, (rr * a.C + qoff + d) * 4));
+            g.k[i] = __builtin_bit_cast(float4, ld_b128<0>(rX, (rr * a.C + koff + d) * 4));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t c = tid + 256 * i, rr = c / (kC / 4), s4 = (c % (kC / 4)) * 4;
+            g.p[i] = __builtin_bit_cast(float4, ld_b128<0>(rP, (rr * kC + s4) * 4));
+        }
+        const auto rU = rsrc(a.Uc + blk * kC * dv, kC * dv * 4);
+        g.u = __builtin_bit_cast(float4, ld_b128<0>(rU, ((uint32_t)r * dv + c0 + cq) * 4));
+        g.l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(a.Lc + blk * kC, kC * 4),
+                                                                            (uint32_t)(tid & 63) * 4, 0, 0));
+    };
+    gload(R, 0);
     for (uint32_t ch = 0; ch < nch; ++ch) {
         const uint32_t t0 = ch * kC;
         const int n = (int)min((uint32_t)kC, a.T - t0);
-        const size_t blk = (size_t)j * nch + ch;
-        const float* W = a.Wc + blk * kC * DK;
-        const float* P = a.Pc + blk * kC * kC;
-        for (int c = tid; c < kC * DK / 4; c += 256) {
-            const int rr = c / (DK / 4), d = (c % (DK / 4)) * 4;
-            float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), kv = qv;
-            if (rr < n) {
-                const float* src = a.qkvs + (size_t)(t0 + rr) * a.C;
-                qv = *reinterpret_cast<const float4*>(src + qoff + d);
-                kv = *reinterpret_cast<const float4*>(src + koff + d);
-            }
-            *reinterpret_cast<float4*>(&wl[rr * KR + d]) = *reinterpret_cast<const float4*>(W + rr * DK + d);
-            *reinterpret_cast<float4*>(&ql[rr * KR + d]) = qv;
-            *reinterpret_cast<float4*>(&kl[rr * KR + d]) = kv;
+#pragma unroll
+        for (int i = 0; i < NW4; ++i) {
+            const int c = tid + 256 * i, rr = c / (DK / 4), d = (c % (DK / 4)) * 4;
+            *reinterpret_cast<float4*>(&wl[rr * KR + d]) = R.w[i];
+            *reinterpret_cast<float4*>(&ql[rr * KR + d]) = R.q[i];
+            *reinterpret_cast<float4*>(&kl[rr * KR + d]) = R.k[i];
         }
-        for (int c = tid; c < kC * kC / 4; c += 256) {
-            const int rr = c / (kC / 4), s = (c % (kC / 4)) * 4;
-            *reinterpret_cast<float4*>(&pl[rr * 68 + s]) = *reinterpret_cast<const float4*>(P + rr * kC + s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + 256 * i, rr = c / (kC / 4), s4 = (c % (kC / 4)) * 4;
+            *reinterpret_cast<float4*>(&pl[rr * 68 + s4]) = R.p[i];
         }
-        if (tid < kC) L[tid] = a.Lc[blk * kC + tid];
+        if (tid < kC) L[tid] = R.l;
+        const float4 uv = R.u;
         __syncthreads();
+        if (ch + 1 < nch) gload(R, ch + 1);
         if (tid < kC) ef[tid] = expf(L[kC - 1] - L[tid]);
 
         // D = U - W S0 and Q S0 for row r, columns cq..cq+3
@@ -489,8 +531,6 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(PfGdnArgs a) {
             }
         }
         {
-            const float* U = a.Uc + blk * kC * dv + (size_t)r * dv + c0 + cq;
-            const float4 uv = *reinterpret_cast<const float4*>(U);
             *reinterpret_cast<float4*>(&dl[r * kSL + cq]) =
                 make_float4(uv.x - wsum[0], uv.y - wsum[1], uv.z - wsum[2], uv.w - wsum[3]);
         }
@@ -638,29 +678,45 @@ __global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
     float m = -INFINITY, l = 0.f;
-    const uint32_t nkt = (kend + 31) / 32;
-    for (uint32_t kt = 0; kt < nkt; ++kt) {
-        const uint32_t k0 = kt * 32;
-        for (int c = tid; c < 32 * D / 8; c += NT) {
-            const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-            uint4 w = make_uint4(0, 0, 0, 0);
-            if (k0 + row < kend) w = *reinterpret_cast<const uint4*>(a.kc + (k0 + row) * rs + g * D + col);
-            *reinterpret_cast<uint4*>(&kt_s[row * KRW + col]) =
-                make_uint4(bf2_to_h2(w.x), bf2_to_h2(w.y), bf2_to_h2(w.z), bf2_to_h2(w.w));
+    // tile kt + 1 is fetched into registers while tile kt is in LDS
+    constexpr int KL = (32 * D / 8 + NT - 1) / NT, VL = (D + NT - 1) / NT;
+    uint4 kr[KL], vr[VL][4];
+    auto gload = [&](uint32_t k0) {
+#pragma unroll
+        for (int i = 0; i < KL; ++i) {
+            const int c = tid + NT * i, row = c / (D / 8), col = (c % (D / 8)) * 8;
+            kr[i] = (c < 32 * D / 8 && k0 + row < kend)
+                        ? *reinterpret_cast<const uint4*>(a.kc + (k0 + row) * rs + g * D + col)
+                        : make_uint4(0, 0, 0, 0);
         }
-        for (int c = tid; c < D; c += NT) {  // 8 key quads x D/8 column octets
-            const int b = c % (D / 8), q4 = c / (D / 8);
-            uint4 w[4];
+#pragma unroll
+        for (int i = 0; i < VL; ++i) {  // 8 key quads x D/8 column octets
+            const int c = tid + NT * i, b = c % (D / 8), q4 = c / (D / 8);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const uint32_t key = k0 + 4 * q4 + u;
-                w[u] = key < kend ? *reinterpret_cast<const uint4*>(a.vc + key * rs + g * D + 8 * b)
-                                  : make_uint4(0, 0, 0, 0);
+                vr[i][u] = (c < D && key < kend)
+                               ? *reinterpret_cast<const uint4*>(a.vc + key * rs + g * D + 8 * b)
+                               : make_uint4(0, 0, 0, 0);
             }
-            const uint32_t* p0 = reinterpret_cast<const uint32_t*>(&w[0]);
-            const uint32_t* p1 = reinterpret_cast<const uint32_t*>(&w[1]);
-            const uint32_t* p2 = reinterpret_cast<const uint32_t*>(&w[2]);
-            const uint32_t* p3 = reinterpret_cast<const uint32_t*>(&w[3]);
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < KL; ++i) {
+            const int c = tid + NT * i, row = c / (D / 8), col = (c % (D / 8)) * 8;
+            if (c < 32 * D / 8)
+                *reinterpret_cast<uint4*>(&kt_s[row * KRW + col]) =
+                    make_uint4(bf2_to_h2(kr[i].x), bf2_to_h2(kr[i].y), bf2_to_h2(kr[i].z), bf2_to_h2(kr[i].w));
+        }
+#pragma unroll
+        for (int i = 0; i < VL; ++i) {
+            const int c = tid + NT * i, b = c % (D / 8), q4 = c / (D / 8);
+            if (c >= D) continue;
+            const uint32_t* p0 = reinterpret_cast<const uint32_t*>(&vr[i][0]);
+            const uint32_t* p1 = reinterpret_cast<const uint32_t*>(&vr[i][1]);
+            const uint32_t* p2 = reinterpret_cast<const uint32_t*>(&vr[i][2]);
+            const uint32_t* p3 = reinterpret_cast<const uint32_t*>(&vr[i][3]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int sh = (e & 1) * 16;
@@ -670,7 +726,14 @@ __global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
                     make_uint2(bf2_to_h2(v0 | (v1 << 16)), bf2_to_h2(v2 | (v3 << 16)));
             }
         }
+    };
+    const uint32_t nkt = (kend + 31) / 32;
+    gload(0);
+    for (uint32_t kt = 0; kt < nkt; ++kt) {
+        const uint32_t k0 = kt * 32;
+        lstore();
         __syncthreads();
+        if (kt + 1 < nkt) gload(k0 + 32);
 
         f32x16 s;
 #pragma unroll
@@ -690,20 +753,27 @@ __global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
             mx = fmaxf(mx, s[r]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m, mx);
-        const float al = exp2f(m - mn);
-        m = mn;
+        // the running maximum moves (and the accumulators are rescaled) only when
+        // some query's tile maximum exceeds it by more than 2^8: probabilities stay
+        // below 256, far inside f16 and fp32 range, and the rescale is skipped for
+        // most tiles; the decision is wave-uniform
+        if (__ballot(mx > m + 8.0f)) {
+            const float mn = fmaxf(m, mx);
+            const float al = __builtin_amdgcn_exp2f(m - mn);
+            m = mn;
+            l *= al;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] *= al;
+        }
         float ps = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            s[r] = exp2f(s[r] - mn);
+            s[r] = __builtin_amdgcn_exp2f(s[r] - m);
             ps += s[r];
         }
-        l = l * al + ps;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][r] *= al;
+        l += ps;
         half8 pb[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
