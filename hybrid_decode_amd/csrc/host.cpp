@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 #include <vector>
 
@@ -991,25 +992,31 @@ T* at_off(void* base, size_t off) {
     return reinterpret_cast<T*>(static_cast<char*>(base) + off);
 }
 
-q35_status pf_gemm(const char* what, int mode, const uint16_t* x, uint32_t M, const Q35QuantWeight& w0,
-                   const Q35QuantWeight* w1, void* out, uint32_t ldo, const void* resid, bool resid_f32,
-                   bool out_f32, hipStream_t stream) {
+// One prefill GEMM launch.  F32 mode: up to four matrices stacked by rows, each
+// writing its own fp32 output (row stride = its rows); RESID and SWIGLU: ws[0]
+// (and ws[1] = up_proj for SWIGLU) into out with row stride ldo.
+q35_status pf_gemm(const char* what, int mode, const uint16_t* x, uint32_t M,
+                   std::initializer_list<const Q35QuantWeight*> ws, std::initializer_list<void*> outs,
+                   uint32_t ldo, const void* resid, bool resid_f32, bool out_f32, hipStream_t stream) {
     PfGemmArgs g{};
     g.x = x;
-    g.w0 = w0.codes;
-    g.s0 = w0.scales;
-    g.b0 = w0.biases;
-    if (w1) {
-        g.w1 = w1->codes;
-        g.s1 = w1->scales;
-        g.b1 = w1->biases;
+    uint32_t i = 0, rows = 0;
+    for (const Q35QuantWeight* w : ws) {
+        g.w[i] = w->codes;
+        g.s[i] = w->scales;
+        g.b[i] = w->biases;
+        if (mode == kPfF32 || i == 0) rows += w->n;
+        g.seg_end[i] = rows;
+        g.ldo[i] = mode == kPfF32 ? w->n : ldo;
+        ++i;
     }
-    g.out = out;
+    for (uint32_t k = i; k < 4; ++k) g.seg_end[k] = rows;
+    uint32_t o = 0;
+    for (void* p : outs) g.out[o++] = p;
     g.resid = resid;
     g.M = M;
-    g.N = w0.n;
-    g.K = w0.k;
-    g.ldo = ldo;
+    g.N = rows;
+    g.K = (*ws.begin())->k;
     g.resid_f32 = resid_f32 ? 1 : 0;
     g.out_f32 = out_f32 ? 1 : 0;
     Q35_HIP(pf_gemm_launch(mode, g, stream), what);
@@ -1035,9 +1042,9 @@ q35_status pf_mlp(const Qwen35ForwardConfig& c, const L& l, const PfWs& w, void*
     float* r = at_off<float>(ws, w.r);
     uint16_t* h = at_off<uint16_t>(ws, w.h);
     Q35_HIP(pf_rmsnorm_launch(r, true, l.post_ln, xh, T, c.hidden, c.rms_eps, stream), "prefill post norm");
-    Q35_TRY(pf_gemm("prefill gate/up", kPfSwiglu, xh, T, l.gate_proj, &l.up_proj, h, c.intermediate, nullptr,
-                    false, false, stream));
-    Q35_TRY(pf_gemm("prefill down", kPfResid, h, T, l.down_proj, nullptr, x_out, c.hidden, r, true,
+    Q35_TRY(pf_gemm("prefill gate/up", kPfSwiglu, xh, T, {&l.gate_proj, &l.up_proj}, {h}, c.intermediate,
+                    nullptr, false, false, stream));
+    Q35_TRY(pf_gemm("prefill down", kPfResid, h, T, {&l.down_proj}, {x_out}, c.hidden, r, true,
                     c.act_dtype == Q35_ACT_F32, stream));
     return Q35_OK;
 }
@@ -1073,7 +1080,7 @@ q35_status q35_prefill_linear_attention(const Qwen35Kernels* kernels,
     PfWs w;
     Q35_TRY(pf_check_ws(c, n_tokens, workspace, workspace_bytes, &w));
     if (n_tokens == 0) return ok();
-    const uint32_t T = n_tokens, C = qkv_total(c), Z = z_dim(c);
+    const uint32_t T = n_tokens, C = qkv_total(c);
     const bool f32 = c.act_dtype == Q35_ACT_F32;
     void* ws = workspace;
     const LinearAttentionLayer& l = *layer;
@@ -1084,11 +1091,8 @@ q35_status q35_prefill_linear_attention(const Qwen35Kernels* kernels,
     float* fb = at_off<float>(ws, w.fb);
 
     Q35_HIP(pf_rmsnorm_launch(x_in, f32, l.input_ln, xh, T, c.hidden, c.rms_eps, stream), "prefill input norm");
-    Q35_TRY(pf_gemm("prefill in_proj_a", kPfF32, xh, T, l.in_proj_a, nullptr, fa, hv, nullptr, false, true, stream));
-    Q35_TRY(pf_gemm("prefill in_proj_b", kPfF32, xh, T, l.in_proj_b, nullptr, fb, hv, nullptr, false, true, stream));
-    Q35_TRY(pf_gemm("prefill in_proj_qkv", kPfF32, xh, T, l.in_proj_qkv, nullptr, qkv, C, nullptr, false, true,
-                    stream));
-    Q35_TRY(pf_gemm("prefill in_proj_z", kPfF32, xh, T, l.in_proj_z, nullptr, z, Z, nullptr, false, true, stream));
+    Q35_TRY(pf_gemm("prefill in_proj", kPfF32, xh, T, {&l.in_proj_qkv, &l.in_proj_z, &l.in_proj_a, &l.in_proj_b},
+                    {qkv, z, fa, fb}, 0, nullptr, false, true, stream));
 
     PfConvArgs cv{};
     cv.qkv = qkv;
@@ -1127,7 +1131,7 @@ q35_status q35_prefill_linear_attention(const Qwen35Kernels* kernels,
     Q35_HIP(pf_gdn_launch(cv, g, state->conv1d_state, stream), "prefill gated delta rule");
     uint16_t* yz = at_off<uint16_t>(ws, w.yz);
     Q35_HIP(pf_gdn_out_launch(g.y, z, l.norm_weight, yz, T, hv, dv, c.rms_eps, stream), "prefill gated norm");
-    Q35_TRY(pf_gemm("prefill out_proj", kPfResid, yz, T, l.out_proj, nullptr, at_off<float>(ws, w.r), c.hidden,
+    Q35_TRY(pf_gemm("prefill out_proj", kPfResid, yz, T, {&l.out_proj}, {at_off<float>(ws, w.r)}, c.hidden,
                     x_in, f32, true, stream));
     Q35_TRY(pf_mlp(c, l, w, ws, T, x_out, stream));
     return ok();
@@ -1165,12 +1169,8 @@ q35_status q35_prefill_full_attention(const Qwen35Kernels* kernels, const Qwen35
     float* kf = at_off<float>(ws, w.kf);
     float* vf = at_off<float>(ws, w.vf);
     Q35_HIP(pf_rmsnorm_launch(x_in, f32, l.input_ln, xh, T, c.hidden, c.rms_eps, stream), "prefill input norm");
-    Q35_TRY(pf_gemm("prefill q_proj", kPfF32, xh, T, l.q_proj, nullptr, qf, q_total(c), nullptr, false, true,
-                    stream));
-    Q35_TRY(pf_gemm("prefill k_proj", kPfF32, xh, T, l.k_proj, nullptr, kf, kv_dim(c), nullptr, false, true,
-                    stream));
-    Q35_TRY(pf_gemm("prefill v_proj", kPfF32, xh, T, l.v_proj, nullptr, vf, kv_dim(c), nullptr, false, true,
-                    stream));
+    Q35_TRY(pf_gemm("prefill q/k/v", kPfF32, xh, T, {&l.q_proj, &l.k_proj, &l.v_proj}, {qf, kf, vf}, 0, nullptr,
+                    false, true, stream));
     PfRopeArgs rp{};
     rp.q_full = qf;
     rp.k = kf;
@@ -1200,7 +1200,7 @@ q35_status q35_prefill_full_attention(const Qwen35Kernels* kernels, const Qwen35
     at.hkv = c.num_kv_heads;
     at.scale_log2 = 1.4426950408889634f / std::sqrt((float)c.head_dim);
     Q35_HIP(pf_attn_launch(rp, at, stream), "prefill attention");
-    Q35_TRY(pf_gemm("prefill o_proj", kPfResid, at.ga, T, l.o_proj, nullptr, at_off<float>(ws, w.r), c.hidden,
+    Q35_TRY(pf_gemm("prefill o_proj", kPfResid, at.ga, T, {&l.o_proj}, {at_off<float>(ws, w.r)}, c.hidden,
                     x_in, f32, true, stream));
     Q35_TRY(pf_mlp(c, l, w, ws, T, x_out, stream));
     return ok();
@@ -1216,7 +1216,7 @@ q35_status q35_prefill_gemm(const Qwen35Kernels* kernels, const Q35QuantWeight* 
     Q35_TRY(need(x_f16, "x_f16"));
     Q35_TRY(need(y, "y", false));
     if (m == 0) return ok();
-    Q35_TRY(pf_gemm("prefill GEMM", kPfF32, x_f16, m, *w, nullptr, y, w->n, nullptr, false, true, stream));
+    Q35_TRY(pf_gemm("prefill GEMM", kPfF32, x_f16, m, {w}, {y}, 0, nullptr, false, true, stream));
     return ok();
 }
 

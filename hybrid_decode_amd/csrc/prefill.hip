@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "q35decode.h"
 #include "q35_device.h"
 #include "q35_internal.h"
@@ -48,84 +50,102 @@ Q35_DEV uint32_t bf2_to_h2(uint32_t w) { return pack_h2(bf16_lo(w), bf16_hi(w));
 // ====================================================================== GEMM
 //
 // out[m, n] = sum_k x[m, k] * W[n, k], W[n, k] = s[n, k/64] * code[n, k] + b[n, k/64]
-// (weights dequantised in fp32, rounded once to f16).  Block tile 128 (rows of
-// x) x 128 (rows of W) x 64 (one quantisation group); four waves, each 64 x 64
-// as 2 x 2 MFMA tiles.  SwiGLU mode: the 128 W rows are 64 gate rows and the
+// (weights dequantised in fp32, rounded once to f16).  Block tile 256 (rows of
+// x) x 128 (rows of W) x 64 (one quantisation group); eight waves, each 64 x 64
+// as 2 x 2 MFMA tiles, so each dequantised weight serves 256 rows.  SwiGLU mode: the 128 W rows are 64 gate rows and the
 // same 64 up rows; a wave holds a gate tile and its up tile, so the epilogue
 // is elementwise in registers.
 
-constexpr int kBM = 128, kBN = 128, kBK = 64, kRow = kBK + 8;  // LDS row: 144 bytes
+constexpr int kBM = 256, kBN = 128, kBK = 64, kRow = kBK + 8;  // LDS row: 144 bytes
+constexpr int kGemmThreads = 512;
 
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(PfGemmArgs a) {
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(PfGemmArgs a) {
     __shared__ __align__(16) _Float16 xs[2][kBM * kRow];
     __shared__ __align__(16) _Float16 ws[2][kBN * kRow];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wm = wid >> 1, wn = wid & 1;
-    const uint32_t m0 = blockIdx.y * kBM;
-    const uint32_t n0 = blockIdx.x * (MODE == kPfSwiglu ? kBN / 2 : kBN);
+    // Tiles per XCD: consecutive blocks go to the 8 XCDs in turn, so block b runs
+    // on XCD b % 8.  When the row tiles divide evenly, XCD x takes the row tiles
+    // x, x + 8, ... and sweeps all column tiles of one row tile before the next:
+    // the blocks an XCD runs at once share their x tile in that XCD's L2.
+    const uint32_t bn = MODE == kPfSwiglu ? kBN / 2 : kBN;
+    const uint32_t n_nt = (a.N + bn - 1) / bn, n_mt = (a.M + kBM - 1) / kBM, b = blockIdx.x;
+    uint32_t mt, nt;
+    if (n_mt % 8 == 0) {
+        const uint32_t slot = b / 8;
+        mt = b % 8 + 8 * (slot / n_nt);
+        nt = slot % n_nt;
+    } else {
+        mt = b / n_nt;
+        nt = b % n_nt;
+    }
+    const uint32_t m0 = mt * kBM;
+    const uint32_t n0 = nt * bn;
     const uint32_t nk = a.K / kBK, ng = a.K / 64;
 
     // global -> register staging of one k tile (two stages in flight)
     struct Stage {
         uint4 xr[4];
-        uint4 wr[2];
-        float sc[2], bi[2];
+        uint4 wr;
+        uint32_t sc, bi;  // raw bf16 bits
     };
+    // This thread's W row (fixed for the whole k loop): rows 64..127 of a SwiGLU
+    // tile are the up rows of n0..n0+63; otherwise the row's segment picks the
+    // matrix.  A row past the last one reads row 0 of the first matrix (always
+    // present) and is masked to zero at the stash.
+    const uint8_t* wrow_p;
+    const uint16_t* srow_p;
+    const uint16_t* brow_p;
+    uint32_t wmsk;
+    {
+        const int row = tid >> 2, col = (tid & 3) * 16;
+        const uint32_t gn = n0 + row;
+        uint32_t q = 0, n = gn;
+        if constexpr (MODE == kPfSwiglu) {
+            q = row >= kBN / 2 ? 1 : 0;
+            n = n0 + (q ? row - kBN / 2 : row);
+        } else if constexpr (MODE == kPfF32) {
+            q = (gn >= a.seg_end[0]) + (gn >= a.seg_end[1]) + (gn >= a.seg_end[2]);
+            n = gn - (q == 0 ? 0 : q == 1 ? a.seg_end[0] : q == 2 ? a.seg_end[1] : a.seg_end[2]);
+        }
+        const bool live = (MODE == kPfSwiglu ? n : gn) < a.N;
+        if (!live) q = 0;
+        const size_t nn = live ? n : 0;
+        wrow_p = (q == 0 ? a.w[0] : q == 1 ? a.w[1] : q == 2 ? a.w[2] : a.w[3]) + nn * a.K + col;
+        srow_p = (q == 0 ? a.s[0] : q == 1 ? a.s[1] : q == 2 ? a.s[2] : a.s[3]) + nn * ng;
+        brow_p = (q == 0 ? a.b[0] : q == 1 ? a.b[1] : q == 2 ? a.b[2] : a.b[3]) + nn * ng;
+        wmsk = live ? 0xFFFFFFFFu : 0u;
+    }
     auto load = [&](Stage& g, uint32_t kt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
+            const int c = tid + kGemmThreads * i, row = c >> 3, col = (c & 7) * 8;
             const uint32_t m = m0 + row;
             g.xr[i] = m < a.M ? *reinterpret_cast<const uint4*>(a.x + (size_t)m * a.K + kt * kBK + col)
                               : make_uint4(0, 0, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + 256 * i, row = c >> 2, col = (c & 3) * 16;
-            const uint8_t* w = a.w0;
-            const uint16_t* s = a.s0;
-            const uint16_t* b = a.b0;
-            uint32_t n = n0 + row;
-            if (MODE == kPfSwiglu && i == 1) {  // rows 64..127: the up rows of n0..n0+63
-                w = a.w1;
-                s = a.s1;
-                b = a.b1;
-                n = n0 + row - kBN / 2;
-            }
-            if (n < a.N) {
-                g.wr[i] = *reinterpret_cast<const uint4*>(w + (size_t)n * a.K + kt * kBK + col);
-                g.sc[i] = bf16_to_f32(s[(size_t)n * ng + kt]);
-                g.bi[i] = bf16_to_f32(b[(size_t)n * ng + kt]);
-            } else {
-                g.wr[i] = make_uint4(0, 0, 0, 0);
-                g.sc[i] = 0.f;
-                g.bi[i] = 0.f;
-            }
+        g.wr = *reinterpret_cast<const uint4*>(wrow_p + kt * kBK);
+        g.sc = srow_p[kt];
+        g.bi = brow_p[kt];
+    };
+    // part q (0..3) of moving a staged tile into LDS: one x chunk, and four weights
+    // dequantised (fp32 fma, one f16 rounding); spread over the MFMA steps
+    auto stash_part = [&](const Stage& g, int buf, int q) {
+        {
+            const int c = tid + kGemmThreads * q, row = c >> 3, col = (c & 7) * 8;
+            *reinterpret_cast<uint4*>(&xs[buf][row * kRow + col]) = g.xr[q];
         }
+        const int row = tid >> 2, col = (tid & 3) * 16;
+        const uint32_t v = (q == 0 ? g.wr.x : q == 1 ? g.wr.y : q == 2 ? g.wr.z : g.wr.w) & wmsk;
+        const float sc = __uint_as_float((g.sc << 16) & wmsk), bi = __uint_as_float((g.bi << 16) & wmsk);
+        *reinterpret_cast<uint2*>(&ws[buf][row * kRow + col + 4 * q]) =
+            make_uint2(pack_h2(fmaf(sc, (float)(v & 0xFFu), bi), fmaf(sc, (float)((v >> 8) & 0xFFu), bi)),
+                       pack_h2(fmaf(sc, (float)((v >> 16) & 0xFFu), bi), fmaf(sc, (float)(v >> 24), bi)));
     };
     auto stash = [&](const Stage& g, int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-            *reinterpret_cast<uint4*>(&xs[buf][row * kRow + col]) = g.xr[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + 256 * i, row = c >> 2, col = (c & 3) * 16;
-            const uint32_t wv[4] = {g.wr[i].x, g.wr[i].y, g.wr[i].z, g.wr[i].w};
-            const float sc = g.sc[i], bi = g.bi[i];
-            uint32_t h[8];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t v = wv[q];
-                h[2 * q] = pack_h2(fmaf(sc, (float)(v & 0xFFu), bi), fmaf(sc, (float)((v >> 8) & 0xFFu), bi));
-                h[2 * q + 1] = pack_h2(fmaf(sc, (float)((v >> 16) & 0xFFu), bi), fmaf(sc, (float)(v >> 24), bi));
-            }
-            uint4* dst = reinterpret_cast<uint4*>(&ws[buf][row * kRow + col]);
-            dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
-            dst[1] = make_uint4(h[4], h[5], h[6], h[7]);
-        }
+        for (int q = 0; q < 4; ++q) stash_part(g, buf, q);
     };
 
     f32x16 acc[2][2];
@@ -143,7 +163,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(PfGemmArgs a) {
         wrow[j] = (MODE == kPfSwiglu ? j * 64 + 32 * wn : 64 * wn + 32 * j) + (lane & 31);
     const int koff = 8 * (lane >> 5);
 
-    auto compute = [&](int cur) {
+    // MFMAs on LDS buffer CUR; with do_stash, the stash of the stage that feeds the
+    // other buffer is interleaved, a quarter per k step
+    Stage g0, g1;
+    auto compute = [&](auto cur_c, bool do_stash) {
+        constexpr int cur = decltype(cur_c)::value;
+        const Stage& nxt = cur == 0 ? g1 : g0;
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
             half8 av[2], bv[2];
@@ -159,54 +184,64 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(PfGemmArgs a) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+            if (do_stash) stash_part(nxt, cur ^ 1, ks);
         }
     };
 
     // k tile kt sits in LDS buffer kt % 2 while tile kt + 1 waits in registers and
     // tile kt + 2 is being fetched
-    Stage g0, g1;
     load(g0, 0);
     if (nk > 1) load(g1, 1);
     stash(g0, 0);
     __syncthreads();
     for (uint32_t kt = 0; kt < nk; kt += 2) {
         if (kt + 2 < nk) load(g0, kt + 2);
-        compute(0);
-        if (kt + 1 < nk) stash(g1, 1);
+        compute(std::integral_constant<int, 0>{}, kt + 1 < nk);
         __syncthreads();
         if (kt + 1 >= nk) break;
         if (kt + 3 < nk) load(g1, kt + 3);
-        compute(1);
-        if (kt + 2 < nk) stash(g0, 0);
+        compute(std::integral_constant<int, 1>{}, kt + 2 < nk);
         __syncthreads();
     }
 
     // epilogue: acc[i][j][r] is (row 8 (r/4) + 4 (lane/32) + r%4, column lane%32) of its tile
+    if constexpr (MODE == kPfSwiglu) {
+        const uint32_t n = n0 + 32 * wn + (lane & 31);
+        if (n < a.N) {
+            uint16_t* out = static_cast<uint16_t*>(a.out[0]) + n;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const uint32_t m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (m >= a.M) continue;
-            if constexpr (MODE == kPfSwiglu) {
-                const uint32_t n = n0 + 32 * wn + (lane & 31);
-                if (n < a.N)
-                    static_cast<uint16_t*>(a.out)[(size_t)m * a.ldo + n] =
-                        to_h(silu(acc[i][0][r]) * acc[i][1][r]);
-            } else {
+                for (int r = 0; r < 16; ++r) {
+                    const uint32_t m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (m < a.M) out[(size_t)m * a.ldo[0]] = to_h(silu(acc[i][0][r]) * acc[i][1][r]);
+                }
+        }
+    } else {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const uint32_t n = n0 + 64 * wn + 32 * j + (lane & 31);
-                    if (n >= a.N) continue;
-                    const size_t o = (size_t)m * a.ldo + n;
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t n = n0 + 64 * wn + 32 * j + (lane & 31);
+            if (n >= a.N) continue;
+            uint32_t q = 0, n1 = n;
+            if constexpr (MODE == kPfF32) {
+                q = (n >= a.seg_end[0]) + (n >= a.seg_end[1]) + (n >= a.seg_end[2]);
+                n1 = n - (q == 0 ? 0 : q == 1 ? a.seg_end[0] : q == 2 ? a.seg_end[1] : a.seg_end[2]);
+            }
+            void* out = q == 0 ? a.out[0] : q == 1 ? a.out[1] : q == 2 ? a.out[2] : a.out[3];
+            const uint32_t ld = q == 0 ? a.ldo[0] : q == 1 ? a.ldo[1] : q == 2 ? a.ldo[2] : a.ldo[3];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const uint32_t m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (m >= a.M) continue;
+                    const size_t o = (size_t)m * ld + n1;
                     if constexpr (MODE == kPfF32) {
-                        static_cast<float*>(a.out)[o] = acc[i][j][r];
+                        static_cast<float*>(out)[o] = acc[i][j][r];
                     } else {
-                        const float v = acc[i][j][r] + load_act(a.resid, o, a.resid_f32);
-                        store_act(a.out, o, v, a.out_f32);
+                        store_act(out, o, acc[i][j][r] + load_act(a.resid, o, a.resid_f32), a.out_f32);
                     }
                 }
-            }
         }
     }
 }
@@ -841,11 +876,11 @@ const void* pf_kernel_ptr(int i) {
 hipError_t pf_gemm_launch(int mode, const PfGemmArgs& a, hipStream_t s) {
     if (a.M == 0) return hipSuccess;
     const uint32_t bn = mode == kPfSwiglu ? pf::kBN / 2 : pf::kBN;
-    dim3 grid((a.N + bn - 1) / bn, (a.M + pf::kBM - 1) / pf::kBM);
+    const dim3 grid(((a.N + bn - 1) / bn) * ((a.M + pf::kBM - 1) / pf::kBM));
     switch (mode) {
-        case kPfF32: pf::gemm_kernel<kPfF32><<<grid, 256, 0, s>>>(a); break;
-        case kPfResid: pf::gemm_kernel<kPfResid><<<grid, 256, 0, s>>>(a); break;
-        case kPfSwiglu: pf::gemm_kernel<kPfSwiglu><<<grid, 256, 0, s>>>(a); break;
+        case kPfF32: pf::gemm_kernel<kPfF32><<<grid, pf::kGemmThreads, 0, s>>>(a); break;
+        case kPfResid: pf::gemm_kernel<kPfResid><<<grid, pf::kGemmThreads, 0, s>>>(a); break;
+        case kPfSwiglu: pf::gemm_kernel<kPfSwiglu><<<grid, pf::kGemmThreads, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

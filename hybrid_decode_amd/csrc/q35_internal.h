@@ -254,20 +254,21 @@ hipError_t persist_launch(int shape, const PersistArgs& a, uint32_t blocks, hipS
 
 enum { kPfF32 = 0, kPfResid = 1, kPfSwiglu = 2 };
 
-// out[m, n] = sum_k x[m, k] W[n, k]: x f16 [M, K]; W 8-bit codes [N, K] with bf16
-// scale/bias per 64.  kPfF32: fp32 out.  kPfResid: out = resid + product (resid and
-// out fp32 or bf16 per flag).  kPfSwiglu: W0 gate, W1 up, out f16 silu(gate) * up.
+// out[m, n] = sum_k x[m, k] W[n, k]: x f16 [M, K]; W 8-bit codes with bf16 scale/bias
+// per 64.  kPfF32: W is up to four matrices stacked by rows (segment i holds rows
+// [seg_end[i-1], seg_end[i]) and writes fp32 out[i] with row stride ldo[i]).
+// kPfResid: one matrix, out[0] = resid + product (resid and out fp32 or bf16 per
+// flag).  kPfSwiglu: w[0] gate, w[1] up, out[0] f16 silu(gate) * up.
 struct PfGemmArgs {
     const uint16_t* x;
-    const uint8_t* w0;
-    const uint16_t* s0;
-    const uint16_t* b0;
-    const uint8_t* w1;
-    const uint16_t* s1;
-    const uint16_t* b1;
-    void* out;
+    const uint8_t* w[4];
+    const uint16_t* s[4];
+    const uint16_t* b[4];
+    void* out[4];
+    uint32_t ldo[4];
+    uint32_t seg_end[4];       // cumulative; unused entries equal N
     const void* resid;
-    uint32_t M, N, K, ldo;
+    uint32_t M, N, K;
     uint32_t resid_f32, out_f32;
 };
 hipError_t pf_gemm_launch(int mode, const PfGemmArgs& a, hipStream_t s);
