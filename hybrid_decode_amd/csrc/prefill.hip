@@ -466,42 +466,43 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(PfGdnArgs a) {
     if (tid < kC) a.Lc[((size_t)j * nch + ch) * kC + tid] = L[tid];
 }
 
-// One block per (v-head, 16 state columns): the state slice S0 [DK, 16] stays in
-// LDS and is carried through the chunks in order.
+// One block per (v-head, 16 state columns): the state slice S0 [DK, 16] is
+// carried through the chunks in order.  The products run on the fp32 matrix
+// cores (16x16x4: A row i = lane % 16, B column j = lane % 16, both with
+// k = lane / 16; D row 4 (lane / 16) + r, column lane % 16).  Within each
+// 16-wide k block, lane group g supplies k = 4 g + s to step s, so a lane reads
+// its four k values as one float4.  Every wave holds all of S0 as B operands;
+// S0 and D are kept transposed in LDS for those float4 reads.
 constexpr int kSL = 16;
 
 template <int DK>
 __global__ __launch_bounds__(256, 1) void gdn_scan_kernel(PfGdnArgs a) {
-    constexpr int KR = DK + 4;
-    constexpr int PER = DK * kSL / 256;   // state entries per thread in the update
-    constexpr int TPR = kSL / PER;        // threads per state row
-    __shared__ __align__(16) float S[DK * kSL];
-    __shared__ __align__(16) float wl[kC * KR];
-    __shared__ __align__(16) float ql[kC * KR];
-    __shared__ __align__(16) float kl[kC * KR];
-    __shared__ __align__(16) float pl[kC * 68];
-    __shared__ __align__(16) float dl[kC * kSL];
-    __shared__ float L[kC], ef[kC];
-    const int tid = threadIdx.x;
+    constexpr int KR = DK + 4, TR = kC + 4, NB = DK / 16;
+    __shared__ __align__(16) float wl[kC * KR];   // W rows
+    __shared__ __align__(16) float ql[kC * KR];   // Q rows
+    __shared__ __align__(16) float kl[kC * KR];   // K rows
+    __shared__ __align__(16) float pl[kC * TR];   // P rows
+    __shared__ __align__(16) float dlt[kSL * TR]; // D transposed [column][token]
+    __shared__ __align__(16) float st[kSL * KR];  // S transposed [column][d]
+    __shared__ __align__(16) float L[kC], ef[kC], el[kC];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;      // MFMA row/column, k group
     const uint32_t j = blockIdx.x, c0 = blockIdx.y * kSL, nch = a.nch;
     const uint32_t dv = a.dv, i = j / (a.hv / a.hk);
     const uint32_t qoff = i * DK, koff = a.hk * DK + i * DK;
-    float* st = a.state + (size_t)j * DK * dv;
+    float* gst = a.state + (size_t)j * DK * dv;
 
-    for (int e = tid; e < DK * kSL; e += 256) S[e] = st[(e / kSL) * dv + c0 + (e % kSL)];
-
-    const int r = tid >> 2, cq = (tid & 3) * 4;   // outputs (row r, columns cq..cq+3)
-    const int ud = tid / TPR, uc = (tid % TPR) * PER;  // state update: row ud, columns uc..
+    for (int e = tid; e < DK * kSL; e += 256) st[(e % kSL) * KR + e / kSL] = gst[(e / kSL) * dv + c0 + (e % kSL)];
 
     // chunk ch + 1's operands are fetched into registers while chunk ch computes
+    // (buffer loads: a resource over the chunk's own token rows returns zero past
+    // the last token)
     constexpr int NW4 = kC * DK / 4 / 256;
     struct Regs {
-        float4 w[NW4], q[NW4], k[NW4], p[4], u;
+        float4 w[NW4], q[NW4], k[NW4], p[4];
+        float u[4];
         float l;
     } R;
-    // buffer loads (not plain loads, which the compiler may turn into a copy
-    // through scratch); a resource over the chunk's own token rows returns zero
-    // for the rows past the last token
     auto gload = [&](Regs& g, uint32_t ch) {
         const uint32_t t0 = ch * kC;
         const uint32_t n = min((uint32_t)kC, a.T - t0);
@@ -510,106 +511,134 @@ __global__ __launch_bounds__(256, 1) void gdn_scan_kernel(PfGdnArgs a) {
         const auto rP = rsrc(a.Pc + blk * kC * kC, kC * kC * 4);
         const auto rX = rsrc(a.qkvs + (size_t)t0 * a.C, n * a.C * 4);
 #pragma unroll
-        for (int i = 0; i < NW4; ++i) {
-            const uint32_t c = tid + 256 * i, rr = c / (DK / 4), d = (c % (DK / 4)) * 4;
-            g.w[i] = __builtin_bit_cast(float4, ld_b128<0>(rW, (rr * DK + d) * 4));
-            g.q[i] = __builtin_bit_cast(float4, ld_b128<0>(rX, (rr * a.C + qoff + d) * 4));
-            g.k[i] = __builtin_bit_cast(float4, ld_b128<0>(rX, (rr * a.C + koff + d) * 4));
+        for (int e = 0; e < NW4; ++e) {
+            const uint32_t c = tid + 256 * e, rr = c / (DK / 4), d = (c % (DK / 4)) * 4;
+            g.w[e] = __builtin_bit_cast(float4, ld_b128<0>(rW, (rr * DK + d) * 4));
+            g.q[e] = __builtin_bit_cast(float4, ld_b128<0>(rX, (rr * a.C + qoff + d) * 4));
+            g.k[e] = __builtin_bit_cast(float4, ld_b128<0>(rX, (rr * a.C + koff + d) * 4));
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t c = tid + 256 * i, rr = c / (kC / 4), s4 = (c % (kC / 4)) * 4;
-            g.p[i] = __builtin_bit_cast(float4, ld_b128<0>(rP, (rr * kC + s4) * 4));
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t c = tid + 256 * e, rr = c / (kC / 4), s4 = (c % (kC / 4)) * 4;
+            g.p[e] = __builtin_bit_cast(float4, ld_b128<0>(rP, (rr * kC + s4) * 4));
         }
         const auto rU = rsrc(a.Uc + blk * kC * dv, kC * dv * 4);
-        g.u = __builtin_bit_cast(float4, ld_b128<0>(rU, ((uint32_t)r * dv + c0 + cq) * 4));
+#pragma unroll
+        for (int r = 0; r < 4; ++r)  // U at (token 16 wid + 4 lg + r, column c0 + li)
+            g.u[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   rU, ((16 * wid + 4 * lg + r) * dv + c0 + li) * 4, 0, 0));
         g.l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(a.Lc + blk * kC, kC * 4),
-                                                                            (uint32_t)(tid & 63) * 4, 0, 0));
+                                                                            (uint32_t)lane * 4, 0, 0));
     };
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    auto mfma = [](float x, float y, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, c, 0, 0, 0); };
+    auto f4z = []() { f4 z = {0.f, 0.f, 0.f, 0.f}; return z; };
+
     gload(R, 0);
+    __syncthreads();  // st filled
     for (uint32_t ch = 0; ch < nch; ++ch) {
         const uint32_t t0 = ch * kC;
         const int n = (int)min((uint32_t)kC, a.T - t0);
 #pragma unroll
-        for (int i = 0; i < NW4; ++i) {
-            const int c = tid + 256 * i, rr = c / (DK / 4), d = (c % (DK / 4)) * 4;
-            *reinterpret_cast<float4*>(&wl[rr * KR + d]) = R.w[i];
-            *reinterpret_cast<float4*>(&ql[rr * KR + d]) = R.q[i];
-            *reinterpret_cast<float4*>(&kl[rr * KR + d]) = R.k[i];
+        for (int e = 0; e < NW4; ++e) {
+            const int c = tid + 256 * e, rr = c / (DK / 4), d = (c % (DK / 4)) * 4;
+            *reinterpret_cast<float4*>(&wl[rr * KR + d]) = R.w[e];
+            *reinterpret_cast<float4*>(&ql[rr * KR + d]) = R.q[e];
+            *reinterpret_cast<float4*>(&kl[rr * KR + d]) = R.k[e];
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + 256 * i, rr = c / (kC / 4), s4 = (c % (kC / 4)) * 4;
-            *reinterpret_cast<float4*>(&pl[rr * 68 + s4]) = R.p[i];
+        for (int e = 0; e < 4; ++e) {
+            const int c = tid + 256 * e, rr = c / (kC / 4), s4 = (c % (kC / 4)) * 4;
+            *reinterpret_cast<float4*>(&pl[rr * TR + s4]) = R.p[e];
         }
         if (tid < kC) L[tid] = R.l;
-        const float4 uv = R.u;
+        float u[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) u[r] = R.u[r];
         __syncthreads();
         if (ch + 1 < nch) gload(R, ch + 1);
-        if (tid < kC) ef[tid] = expf(L[kC - 1] - L[tid]);
+        if (tid < kC) {
+            ef[tid] = expf(L[kC - 1] - L[tid]);
+            el[tid] = expf(L[tid]);
+        }
 
-        // D = U - W S0 and Q S0 for row r, columns cq..cq+3
-        float wsum[4] = {}, qsum[4] = {};
-        for (int d = 0; d < DK; d += 4) {
-            const float4 wv = *reinterpret_cast<const float4*>(&wl[r * KR + d]);
-            const float4 qv = *reinterpret_cast<const float4*>(&ql[r * KR + d]);
-            const float wa[4] = {wv.x, wv.y, wv.z, wv.w}, qa[4] = {qv.x, qv.y, qv.z, qv.w};
+        // S0 as B operands: sb[b] holds S0[16 b + 4 lg + s][li], s = 0..3
+        float4 sb[NB];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float4 sv = *reinterpret_cast<const float4*>(&S[(d + e) * kSL + cq]);
-                const float sa[4] = {sv.x, sv.y, sv.z, sv.w};
+        for (int b = 0; b < NB; ++b) sb[b] = *reinterpret_cast<const float4*>(&st[li * KR + 16 * b + 4 * lg]);
+
+        // W S0 and Q S0 for rows 16 wid .. 16 wid + 15
+        f4 ws = f4z(), qs = f4z();
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    wsum[v] = fmaf(wa[e], sa[v], wsum[v]);
-                    qsum[v] = fmaf(qa[e], sa[v], qsum[v]);
-                }
-            }
+        for (int b = 0; b < NB; ++b) {
+            const float4 wa = *reinterpret_cast<const float4*>(&wl[(16 * wid + li) * KR + 16 * b + 4 * lg]);
+            const float4 qa = *reinterpret_cast<const float4*>(&ql[(16 * wid + li) * KR + 16 * b + 4 * lg]);
+            ws = mfma(wa.x, sb[b].x, ws);
+            ws = mfma(wa.y, sb[b].y, ws);
+            ws = mfma(wa.z, sb[b].z, ws);
+            ws = mfma(wa.w, sb[b].w, ws);
+            qs = mfma(qa.x, sb[b].x, qs);
+            qs = mfma(qa.y, sb[b].y, qs);
+            qs = mfma(qa.z, sb[b].z, qs);
+            qs = mfma(qa.w, sb[b].w, qs);
         }
-        {
-            *reinterpret_cast<float4*>(&dl[r * kSL + cq]) =
-                make_float4(uv.x - wsum[0], uv.y - wsum[1], uv.z - wsum[2], uv.w - wsum[3]);
-        }
+        // D = U - W S0 at (token 16 wid + 4 lg + r, column li), stored transposed
+        *reinterpret_cast<float4*>(&dlt[li * TR + 16 * wid + 4 * lg]) =
+            make_float4(u[0] - ws[0], u[1] - ws[1], u[2] - ws[2], u[3] - ws[3]);
         __syncthreads();
 
-        // y_r = e^(L_r) (Q S0)_r + sum_s P[r][s] d_s
+        // y = e^L (Q S0) + P D; P is lower triangular, so k blocks past this wave's rows add nothing
         {
-            const float g = expf(L[r]);
-            float yv[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) yv[v] = g * qsum[v];
-            for (int s = 0; s <= r; ++s) {
-                const float p = pl[r * 68 + s];
-                const float4 dv4 = *reinterpret_cast<const float4*>(&dl[s * kSL + cq]);
-                yv[0] = fmaf(p, dv4.x, yv[0]);
-                yv[1] = fmaf(p, dv4.y, yv[1]);
-                yv[2] = fmaf(p, dv4.z, yv[2]);
-                yv[3] = fmaf(p, dv4.w, yv[3]);
+            const float4 e4 = *reinterpret_cast<const float4*>(&el[16 * wid + 4 * lg]);
+            f4 y = {e4.x * qs[0], e4.y * qs[1], e4.z * qs[2], e4.w * qs[3]};
+            for (int b = 0; b <= wid; ++b) {
+                const float4 pa = *reinterpret_cast<const float4*>(&pl[(16 * wid + li) * TR + 16 * b + 4 * lg]);
+                const float4 db = *reinterpret_cast<const float4*>(&dlt[li * TR + 16 * b + 4 * lg]);
+                y = mfma(pa.x, db.x, y);
+                y = mfma(pa.y, db.y, y);
+                y = mfma(pa.z, db.z, y);
+                y = mfma(pa.w, db.w, y);
             }
-            if (r < n) {
-                float* y = a.y + (size_t)(t0 + r) * a.hv * dv + (size_t)j * dv + c0 + cq;
-                *reinterpret_cast<float4*>(y) = make_float4(yv[0] * a.out_scale, yv[1] * a.out_scale,
-                                                            yv[2] * a.out_scale, yv[3] * a.out_scale);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * wid + 4 * lg + r;
+                if (row < n) a.y[(size_t)(t0 + row) * a.hv * dv + (size_t)j * dv + c0 + li] = y[r] * a.out_scale;
             }
         }
 
-        // S <- e^(L_end) S0 + sum_s e^(L_end - L_s) k_s d_s^T
-        {
-            const float ge = expf(L[kC - 1]);
-            float sv[PER];
+        // S <- e^(L_end) S0 + K^T (ef D): this wave's d tiles t = wid, wid + 4, ...
+        f4 sn[(NB + 3) / 4];
+        const float ge = expf(L[kC - 1]);
 #pragma unroll
-            for (int v = 0; v < PER; ++v) sv[v] = ge * S[ud * kSL + uc + v];
-            for (int s = 0; s < kC; ++s) {
-                const float kf = kl[s * KR + ud] * ef[s];
+        for (int tt = 0; tt < (NB + 3) / 4; ++tt) {
+            const int t = wid + 4 * tt;
+            if (t >= NB) break;
+            const float4 s0 = *reinterpret_cast<const float4*>(&st[li * KR + 16 * t + 4 * lg]);
+            f4 acc = {ge * s0.x, ge * s0.y, ge * s0.z, ge * s0.w};
 #pragma unroll
-                for (int v = 0; v < PER; ++v) sv[v] = fmaf(kf, dl[s * kSL + uc + v], sv[v]);
+            for (int b = 0; b < kC / 16; ++b) {
+                // A = K^T: (d 16 t + li, token 16 b + 4 lg + s), four scalar reads of K rows
+                const float* kr = &kl[(16 * b + 4 * lg) * KR + 16 * t + li];
+                const float4 db = *reinterpret_cast<const float4*>(&dlt[li * TR + 16 * b + 4 * lg]);
+                const float4 fb = *reinterpret_cast<const float4*>(&ef[16 * b + 4 * lg]);
+                acc = mfma(kr[0], fb.x * db.x, acc);
+                acc = mfma(kr[KR], fb.y * db.y, acc);
+                acc = mfma(kr[2 * KR], fb.z * db.z, acc);
+                acc = mfma(kr[3 * KR], fb.w * db.w, acc);
             }
-            __syncthreads();  // every read of S0 above is done
+            sn[tt] = acc;
+        }
+        __syncthreads();  // every read of S0 is done
 #pragma unroll
-            for (int v = 0; v < PER; ++v) S[ud * kSL + uc + v] = sv[v];
+        for (int tt = 0; tt < (NB + 3) / 4; ++tt) {
+            const int t = wid + 4 * tt;
+            if (t >= NB) break;
+            *reinterpret_cast<float4*>(&st[li * KR + 16 * t + 4 * lg]) =
+                make_float4(sn[tt][0], sn[tt][1], sn[tt][2], sn[tt][3]);
         }
         __syncthreads();
     }
-    for (int e = tid; e < DK * kSL; e += 256) st[(e / kSL) * dv + c0 + (e % kSL)] = S[e];
+    for (int e = tid; e < DK * kSL; e += 256) gst[(e / kSL) * dv + c0 + (e % kSL)] = st[(e % kSL) * KR + e / kSL];
 }
 
 // yz[t, j, :] = f16(RMSNorm(y[t, j, :]; w) * silu(z[t, j, :])); one block per token.
