@@ -56,11 +56,12 @@ Q35_DEV uint32_t bf2_to_h2(uint32_t w) { return pack_h2(bf16_lo(w), bf16_hi(w));
 // same 64 up rows; a wave holds a gate tile and its up tile, so the epilogue
 // is elementwise in registers.
 
-constexpr int kBM = 256, kBN = 128, kBK = 64, kRow = kBK + 8;  // LDS row: 144 bytes
-constexpr int kGemmThreads = 512;
+constexpr int kBN = 128, kBK = 64, kRow = kBK + 8;  // LDS row: 144 bytes
 
-template <int MODE>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(PfGemmArgs a) {
+// BM rows of x per block (128 or 256), 2 BM threads: waves of 64 x 64.
+template <int MODE, int BM>
+__global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_kernel(PfGemmArgs a) {
+    constexpr int kBM = BM, kGemmThreads = 2 * BM, WPT = 512 / kGemmThreads;  // W chunks per thread
     __shared__ __align__(16) _Float16 xs[2][kBM * kRow];
     __shared__ __align__(16) _Float16 ws[2][kBN * kRow];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -87,19 +88,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(PfGemmArgs a) {
     // global -> register staging of one k tile (two stages in flight)
     struct Stage {
         uint4 xr[4];
-        uint4 wr;
-        uint32_t sc, bi;  // raw bf16 bits
+        uint4 wr[WPT];
+        uint32_t sc[WPT], bi[WPT];  // raw bf16 bits
     };
     // This thread's W row (fixed for the whole k loop): rows 64..127 of a SwiGLU
     // tile are the up rows of n0..n0+63; otherwise the row's segment picks the
     // matrix.  A row past the last one reads row 0 of the first matrix (always
     // present) and is masked to zero at the stash.
-    const uint8_t* wrow_p;
-    const uint16_t* srow_p;
-    const uint16_t* brow_p;
-    uint32_t wmsk;
-    {
-        const int row = tid >> 2, col = (tid & 3) * 16;
+    const uint8_t* wrow_p[WPT];
+    const uint16_t* srow_p[WPT];
+    const uint16_t* brow_p[WPT];
+    uint32_t wmsk[WPT];
+#pragma unroll
+    for (int wi = 0; wi < WPT; ++wi) {
+        const int c = tid + kGemmThreads * wi, row = c >> 2, col = (c & 3) * 16;
         const uint32_t gn = n0 + row;
         uint32_t q = 0, n = gn;
         if constexpr (MODE == kPfSwiglu) {
@@ -112,10 +114,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(PfGemmArgs a) {
         const bool live = (MODE == kPfSwiglu ? n : gn) < a.N;
         if (!live) q = 0;
         const size_t nn = live ? n : 0;
-        wrow_p = (q == 0 ? a.w[0] : q == 1 ? a.w[1] : q == 2 ? a.w[2] : a.w[3]) + nn * a.K + col;
-        srow_p = (q == 0 ? a.s[0] : q == 1 ? a.s[1] : q == 2 ? a.s[2] : a.s[3]) + nn * ng;
-        brow_p = (q == 0 ? a.b[0] : q == 1 ? a.b[1] : q == 2 ? a.b[2] : a.b[3]) + nn * ng;
-        wmsk = live ? 0xFFFFFFFFu : 0u;
+        wrow_p[wi] = (q == 0 ? a.w[0] : q == 1 ? a.w[1] : q == 2 ? a.w[2] : a.w[3]) + nn * a.K + col;
+        srow_p[wi] = (q == 0 ? a.s[0] : q == 1 ? a.s[1] : q == 2 ? a.s[2] : a.s[3]) + nn * ng;
+        brow_p[wi] = (q == 0 ? a.b[0] : q == 1 ? a.b[1] : q == 2 ? a.b[2] : a.b[3]) + nn * ng;
+        wmsk[wi] = live ? 0xFFFFFFFFu : 0u;
     }
     auto load = [&](Stage& g, uint32_t kt) {
 #pragma unroll
@@ -125,9 +127,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(PfGemmArgs a) {
             g.xr[i] = m < a.M ? *reinterpret_cast<const uint4*>(a.x + (size_t)m * a.K + kt * kBK + col)
                               : make_uint4(0, 0, 0, 0);
         }
-        g.wr = *reinterpret_cast<const uint4*>(wrow_p + kt * kBK);
-        g.sc = srow_p[kt];
-        g.bi = brow_p[kt];
+#pragma unroll
+        for (int wi = 0; wi < WPT; ++wi) {
+            g.wr[wi] = *reinterpret_cast<const uint4*>(wrow_p[wi] + kt * kBK);
+            g.sc[wi] = srow_p[wi][kt];
+            g.bi[wi] = brow_p[wi][kt];
+        }
     };
     // part q (0..3) of moving a staged tile into LDS: one x chunk, and four weights
     // dequantised (fp32 fma, one f16 rounding); spread over the MFMA steps
@@ -136,12 +141,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(PfGemmArgs a) {
             const int c = tid + kGemmThreads * q, row = c >> 3, col = (c & 7) * 8;
             *reinterpret_cast<uint4*>(&xs[buf][row * kRow + col]) = g.xr[q];
         }
-        const int row = tid >> 2, col = (tid & 3) * 16;
-        const uint32_t v = (q == 0 ? g.wr.x : q == 1 ? g.wr.y : q == 2 ? g.wr.z : g.wr.w) & wmsk;
-        const float sc = __uint_as_float((g.sc << 16) & wmsk), bi = __uint_as_float((g.bi << 16) & wmsk);
-        *reinterpret_cast<uint2*>(&ws[buf][row * kRow + col + 4 * q]) =
-            make_uint2(pack_h2(fmaf(sc, (float)(v & 0xFFu), bi), fmaf(sc, (float)((v >> 8) & 0xFFu), bi)),
-                       pack_h2(fmaf(sc, (float)((v >> 16) & 0xFFu), bi), fmaf(sc, (float)(v >> 24), bi)));
+#pragma unroll
+        for (int wi = 0; wi < WPT; ++wi) {
+            const int c = tid + kGemmThreads * wi, row = c >> 2, col = (c & 3) * 16;
+            const uint4 wr = g.wr[wi];
+            const uint32_t v = (q == 0 ? wr.x : q == 1 ? wr.y : q == 2 ? wr.z : wr.w) & wmsk[wi];
+            const float sc = __uint_as_float((g.sc[wi] << 16) & wmsk[wi]);
+            const float bi = __uint_as_float((g.bi[wi] << 16) & wmsk[wi]);
+            *reinterpret_cast<uint2*>(&ws[buf][row * kRow + col + 4 * q]) =
+                make_uint2(pack_h2(fmaf(sc, (float)(v & 0xFFu), bi), fmaf(sc, (float)((v >> 8) & 0xFFu), bi)),
+                           pack_h2(fmaf(sc, (float)((v >> 16) & 0xFFu), bi), fmaf(sc, (float)(v >> 24), bi)));
+        }
     };
     auto stash = [&](const Stage& g, int buf) {
 #pragma unroll
@@ -709,17 +719,19 @@ __global__ __launch_bounds__(256) void qk_rope_append_kernel(PfRopeArgs a) {
 }
 
 // Causal GQA attention over the bf16 cache for 32 tokens x G heads of one kv
-// head per block (one wave per q-head), key tiles of 32.  The tiles go to LDS
+// head per block (one wave per q-head), key tiles of 64.  The tiles go to LDS
 // as f16 (a bf16 value of the cache's range is exact in f16), the query is an
 // f16 row and the probabilities are rounded to f16, so the products are f16 x
 // f16 on the matrix cores with fp32 sums.  S^T = K Q^T puts one query per lane:
 // the softmax statistics are per lane (plus the partner lane l ^ 32), and the
 // probabilities in registers are already the B operand of O^T += V^T P^T.
 // Output: f16(attention * sigmoid(gate)).
+constexpr int kKT = 64;  // keys per tile
+
 template <int D, int G>
 __global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
-    constexpr int NT = 64 * G, KRW = D + 8, VRW = 32 + 4, DT = D / 32;
-    __shared__ __align__(16) uint16_t kt_s[32 * KRW];
+    constexpr int NT = 64 * G, KRW = D + 8, VRW = kKT + 4, DT = D / 32;
+    __shared__ __align__(16) uint16_t kt_s[kKT * KRW];
     __shared__ __align__(16) uint16_t vt_s[D * VRW];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, h2 = lane >> 5;
     const uint32_t g = blockIdx.y, h = g * G + wid;
@@ -743,23 +755,27 @@ __global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
     float m = -INFINITY, l = 0.f;
     // tile kt + 1 is fetched into registers while tile kt is in LDS
-    constexpr int KL = (32 * D / 8 + NT - 1) / NT, VL = (D + NT - 1) / NT;
+    constexpr int KL = (kKT * D / 8 + NT - 1) / NT;          // K: 16-byte chunks per thread
+    constexpr int VTASK = kKT / 4 * (D / 8);                  // V: (key quad, column octet) tasks
+    constexpr int VL = (VTASK + NT - 1) / NT;
     uint4 kr[KL], vr[VL][4];
     auto gload = [&](uint32_t k0) {
 #pragma unroll
         for (int i = 0; i < KL; ++i) {
             const int c = tid + NT * i, row = c / (D / 8), col = (c % (D / 8)) * 8;
-            kr[i] = (c < 32 * D / 8 && k0 + row < kend)
+            kr[i] = (c < kKT * D / 8 && k0 + row < kend)
                         ? *reinterpret_cast<const uint4*>(a.kc + (k0 + row) * rs + g * D + col)
                         : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < VL; ++i) {  // 8 key quads x D/8 column octets
-            const int c = tid + NT * i, b = c % (D / 8), q4 = c / (D / 8);
+        for (int i = 0; i < VL; ++i) {
+            // key quads vary fastest across lanes: the transposed LDS writes of a wave
+            // then fall on distinct banks but for one 2-way overlap
+            const int c = tid + NT * i, q4 = c % (kKT / 4), b = c / (kKT / 4);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const uint32_t key = k0 + 4 * q4 + u;
-                vr[i][u] = (c < D && key < kend)
+                vr[i][u] = (c < VTASK && key < kend)
                                ? *reinterpret_cast<const uint4*>(a.vc + key * rs + g * D + 8 * b)
                                : make_uint4(0, 0, 0, 0);
             }
@@ -769,14 +785,14 @@ __global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
 #pragma unroll
         for (int i = 0; i < KL; ++i) {
             const int c = tid + NT * i, row = c / (D / 8), col = (c % (D / 8)) * 8;
-            if (c < 32 * D / 8)
+            if (c < kKT * D / 8)
                 *reinterpret_cast<uint4*>(&kt_s[row * KRW + col]) =
                     make_uint4(bf2_to_h2(kr[i].x), bf2_to_h2(kr[i].y), bf2_to_h2(kr[i].z), bf2_to_h2(kr[i].w));
         }
 #pragma unroll
         for (int i = 0; i < VL; ++i) {
-            const int c = tid + NT * i, b = c % (D / 8), q4 = c / (D / 8);
-            if (c >= D) continue;
+            const int c = tid + NT * i, q4 = c % (kKT / 4), b = c / (kKT / 4);
+            if (c >= VTASK) continue;
             const uint32_t* p0 = reinterpret_cast<const uint32_t*>(&vr[i][0]);
             const uint32_t* p1 = reinterpret_cast<const uint32_t*>(&vr[i][1]);
             const uint32_t* p2 = reinterpret_cast<const uint32_t*>(&vr[i][2]);
@@ -791,30 +807,50 @@ __global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
             }
         }
     };
-    const uint32_t nkt = (kend + 31) / 32;
+    const uint32_t nkt = (kend + kKT - 1) / kKT;
     gload(0);
     for (uint32_t kt = 0; kt < nkt; ++kt) {
-        const uint32_t k0 = kt * 32;
+        const uint32_t k0 = kt * kKT;
         lstore();
         __syncthreads();
-        if (kt + 1 < nkt) gload(k0 + 32);
+        if (kt + 1 < nkt) gload(k0 + kKT);
 
-        f32x16 s;
+        // S^T for two 32-key halves: s[hf][r] is key k0 + 32 hf + 8 (r/4) + 4 h2 + r%4, query tq
+        // (the two halves' MFMA chains interleave, so no MFMA waits on the previous one)
+        f32x16 s[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+        for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            const half8 kv = *reinterpret_cast<const half8*>(&kt_s[(lane & 31) * KRW + ks * 16 + 8 * h2]);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kv, qv[ks], s, 0, 0, 0);
-        }
-        // s[r]: key k0 + 8 (r/4) + 4 h2 + r%4, query tq
+            for (int r = 0; r < 16; ++r) s[hf][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const half8 kv = *reinterpret_cast<const half8*>(
+                    &kt_s[(32 * hf + (lane & 31)) * KRW + ks * 16 + 8 * h2]);
+                s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kv, qv[ks], s[hf], 0, 0, 0);
+            }
+        // scale to base 2; only a tile reaching past the block's first query (the
+        // diagonal, block-uniform) needs the causal mask
         float mx = -INFINITY;
+        if (k0 + kKT - 1 <= a.cache_pos + t0 && k0 + kKT <= kend) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const uint32_t key = k0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            const bool ok = key <= a.cache_pos + tq && key < kend;
-            s[r] = ok ? s[r] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, s[r]);
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    s[hf][r] *= a.scale_log2;
+                    mx = fmaxf(mx, s[hf][r]);
+                }
+        } else {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const uint32_t key = k0 + 32 * hf + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                    const bool ok = key <= a.cache_pos + tq && key < kend;
+                    s[hf][r] = ok ? s[hf][r] * a.scale_log2 : -INFINITY;
+                    mx = fmaxf(mx, s[hf][r]);
+                }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         // the running maximum moves (and the accumulators are rescaled) only when
@@ -832,28 +868,28 @@ __global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
                 for (int r = 0; r < 16; ++r) o[dt][r] *= al;
         }
         float ps = 0.f;
+        half8 pb[4];  // k steps of 16 keys: step kk holds s[kk / 2][8 (kk % 2) + e]
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            s[r] = __builtin_amdgcn_exp2f(s[r] - m);
-            ps += s[r];
-        }
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(s[hf][r] - m);
+                ps += p;
+                pb[2 * hf + (r >> 3)][r & 7] = (_Float16)p;
+            }
         l += ps;
-        half8 pb[2];
+        // k steps outer, the DT independent accumulators inner
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pb[kk][e] = (_Float16)s[8 * kk + e];
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const uint16_t* vrow = &vt_s[(32 * dt + (lane & 31)) * VRW + 4 * h2];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 16 * kk);
-                const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 * kk + 8);
+            for (int dt = 0; dt < DT; ++dt) {
+                // keys 16 kk + 4 h2 + 0..3 and 16 kk + 8 + 4 h2 + 0..3, the order of pb[kk]
+                const uint16_t* vrow = &vt_s[(32 * dt + (lane & 31)) * VRW + 4 * h2 + 16 * kk];
+                const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+                const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
                 const half8 vv = __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
                 o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv, pb[kk], o[dt], 0, 0, 0);
             }
-        }
         __syncthreads();
     }
     l += __shfl_xor(l, 32);
@@ -882,9 +918,12 @@ __global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
 
 const void* pf_kernel_ptr(int i) {
     static const void* const k[] = {
-        reinterpret_cast<const void*>(pf::gemm_kernel<kPfF32>),
-        reinterpret_cast<const void*>(pf::gemm_kernel<kPfResid>),
-        reinterpret_cast<const void*>(pf::gemm_kernel<kPfSwiglu>),
+        reinterpret_cast<const void*>(pf::gemm_kernel<kPfF32, 128>),
+        reinterpret_cast<const void*>(pf::gemm_kernel<kPfResid, 128>),
+        reinterpret_cast<const void*>(pf::gemm_kernel<kPfSwiglu, 128>),
+        reinterpret_cast<const void*>(pf::gemm_kernel<kPfF32, 256>),
+        reinterpret_cast<const void*>(pf::gemm_kernel<kPfResid, 256>),
+        reinterpret_cast<const void*>(pf::gemm_kernel<kPfSwiglu, 256>),
         reinterpret_cast<const void*>(pf::rmsnorm_rows_kernel),
         reinterpret_cast<const void*>(pf::gdn_conv_kernel),
         reinterpret_cast<const void*>(pf::gdn_conv_state_kernel),
@@ -902,17 +941,22 @@ const void* pf_kernel_ptr(int i) {
     return i >= 0 && i < (int)(sizeof(k) / sizeof(k[0])) ? k[i] : nullptr;
 }
 
-hipError_t pf_gemm_launch(int mode, const PfGemmArgs& a, hipStream_t s) {
-    if (a.M == 0) return hipSuccess;
+template <int BM>
+static hipError_t gemm_launch_bm(int mode, const PfGemmArgs& a, hipStream_t s) {
     const uint32_t bn = mode == kPfSwiglu ? pf::kBN / 2 : pf::kBN;
-    const dim3 grid(((a.N + bn - 1) / bn) * ((a.M + pf::kBM - 1) / pf::kBM));
+    const dim3 grid(((a.N + bn - 1) / bn) * ((a.M + BM - 1) / BM));
     switch (mode) {
-        case kPfF32: pf::gemm_kernel<kPfF32><<<grid, pf::kGemmThreads, 0, s>>>(a); break;
-        case kPfResid: pf::gemm_kernel<kPfResid><<<grid, pf::kGemmThreads, 0, s>>>(a); break;
-        case kPfSwiglu: pf::gemm_kernel<kPfSwiglu><<<grid, pf::kGemmThreads, 0, s>>>(a); break;
+        case kPfF32: pf::gemm_kernel<kPfF32, BM><<<grid, 2 * BM, 0, s>>>(a); break;
+        case kPfResid: pf::gemm_kernel<kPfResid, BM><<<grid, 2 * BM, 0, s>>>(a); break;
+        case kPfSwiglu: pf::gemm_kernel<kPfSwiglu, BM><<<grid, 2 * BM, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t pf_gemm_launch(int mode, const PfGemmArgs& a, hipStream_t s) {
+    if (a.M == 0) return hipSuccess;
+    return gemm_launch_bm<256>(mode, a, s);
 }
 
 hipError_t pf_rmsnorm_launch(const void* x, bool x_f32, const uint16_t* w, uint16_t* out, uint32_t T,
