@@ -219,3 +219,44 @@ def test_prefill_full_then_decode_reads_the_prefilled_rows(rt, gen):
     torch.cuda.synchronize()
     ref, _, _ = O.prefill.prefill_full_attention(cfg, layer, kv, inv, x, pos)
     assert rel(rt.act_to_f32(scr.t["x_out"], cfg), ref[T]) < TOL_F32
+
+
+# --------------------------------------------------------------------------- other head shapes
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 8, 1), (128, 2, 2), (256, 2, 1)])
+def test_prefill_full_other_head_shapes(rt, gen, D, Hq, Hkv):
+    """The attention kernel's other instantiations: head dims 128 and 256 with one,
+    two and eight query heads per kv head (blocks of 64 to 512 threads)."""
+    from dataclasses import replace
+    pos, T = 7, 70
+    say(f"prefill full D={D} Hq={Hq} Hkv={Hkv} pos={pos} T={T}")
+    cfg = replace(synth.tiny("f32"), head_dim=D, num_heads=Hq, num_kv_heads=Hkv)
+    layer = synth.full_layer(gen, cfg, f"pf.fs{D}.{Hq}.{Hkv}")
+    cap = pos + T + 8
+    kv = synth.kv_cache(gen, cfg, f"pf.fs{D}", cap, pos)
+    kv["k"][pos + T:] = NAN_BF16
+    kv["v"][pos + T:] = NAN_BF16
+    x = gen.act(f"pf.fs.x{D}", (T, cfg.hidden), "f32")
+    before = {s: kv[s].copy() for s in ("k", "v")}
+    out, after = _full_run(rt, cfg, layer, kv, x, pos)
+    inv = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
+    ref, rkv, _ = O.prefill.prefill_full_attention(cfg, layer, kv, inv, x, pos)
+    assert np.isfinite(out).all()
+    assert _rows_rel(out, ref) < TOL_F32
+    _check_cache(after, before, rkv, pos, T)
+
+
+def test_prefill_gdn_head_dim_64(rt, gen):
+    from dataclasses import replace
+    T = 100
+    say(f"prefill GDN dk=dv=64 T={T}")
+    cfg = replace(synth.tiny("f32"), k_head_dim_lin=64, v_head_dim_lin=64)
+    layer = synth.gdn_layer(gen, cfg, "pf.g64")
+    st = synth.gdn_state(gen, cfg, "pf.g64", 0.2, 0.5)
+    x = gen.act("pf.g64.x", (T, cfg.hidden), "f32")
+    out, gst = _gdn_run(rt, cfg, layer, st, x)
+    ref, rst, _ = O.prefill.prefill_linear_attention(cfg, layer, st, x)
+    assert _rows_rel(out, ref) < TOL_F32
+    assert rel(gst["gdn_state"], rst["gdn_state"]) < TOL_F32
+    assert rel(gst["conv1d_state"], rst["conv1d_state"]) < TOL_F32
