@@ -117,6 +117,18 @@ def as_qm(w) -> QuantMatrix:
     return w if isinstance(w, QuantMatrix) else QuantMatrix(w)
 
 
+def stored(x, mode: str):
+    """A buffer the pages keep in bf16: unchanged in Mode A (the parity
+    authority, intermediates unrounded), rounded to bf16 in Mode B (diagnostic:
+    the residual stream, the smoothed qkv and every GEMV output are rounded where
+    the pages store them as bf16)."""
+    if mode == "A":
+        return np.asarray(x, dtype=np.float64)
+    if mode == "B":
+        return bf16_to_f64(f64_to_bf16(np.asarray(x, dtype=np.float64)))
+    raise ValueError(f"mode {mode!r} (A or B)")
+
+
 # --------------------------------------------------------------------------- elementwise / norms
 
 
@@ -291,7 +303,7 @@ def attention_decode(q: np.ndarray, k_cache_bf16: np.ndarray, v_cache_bf16: np.n
 # --------------------------------------------------------------------------- layers
 
 
-def mlp_residual(cfg, layer: dict, r: np.ndarray):
+def mlp_residual(cfg, layer: dict, r: np.ndarray, mode: str = "A"):
     """Post-norm, SwiGLU MLP and residual: the tail shared by both layer forwards.
 
     ``add_rms_norm`` then ``gate_proj.gemv_gate_up_with(up_proj)`` then
@@ -299,18 +311,21 @@ def mlp_residual(cfg, layer: dict, r: np.ndarray):
     x_out = r + W_down (silu(W_gate xn2) * (W_up xn2)),  xn2 = RMSNorm(r; post_ln).
     """
     xn2 = rms_norm(r, layer["post_ln"], cfg.rms_eps)
-    ga = as_qm(layer["gate_proj"]) @ xn2
-    up = as_qm(layer["up_proj"]) @ xn2
+    ga = stored(as_qm(layer["gate_proj"]) @ xn2, mode)
+    up = stored(as_qm(layer["up_proj"]) @ xn2, mode)
     h = silu(ga) * up
-    return r + as_qm(layer["down_proj"]) @ h, {"x_norm2": xn2, "gate_act": ga, "up_act": up}
+    x_out = r + stored(as_qm(layer["down_proj"]) @ h, mode)
+    return stored(x_out, mode), {"x_norm2": xn2, "gate_act": ga, "up_act": up}
 
 
-def forward_linear_attention(cfg, layer: dict, state: dict, x_in: np.ndarray):
+def forward_linear_attention(cfg, layer: dict, state: dict, x_in: np.ndarray, mode: str = "A"):
     """One token through one GDN layer (``forward_linear_attention``).
 
     state: {"conv1d_state": fp32 [C, K], "gdn_state": fp32 [Hv, dk, dv]}; a new
     dict is returned, the input is not modified.
     x_in: the residual stream in the activation dtype.
+    mode: "A" (default, the parity authority) or "B" (bf16 at the buffers the
+    pages store as bf16, see ``stored``).
 
     Returns (x_out float64, new_state, taps) where taps holds the named
     intermediates the page's dump hook exposes.
@@ -320,15 +335,16 @@ def forward_linear_attention(cfg, layer: dict, state: dict, x_in: np.ndarray):
     x = act_to_f64(x_in, cfg.act_dtype)
 
     xn = rms_norm(x, layer["input_ln"], cfg.rms_eps)
-    a = as_qm(layer["in_proj_a"]) @ xn
-    b = as_qm(layer["in_proj_b"]) @ xn
-    qkv = as_qm(layer["in_proj_qkv"]) @ xn
-    z = as_qm(layer["in_proj_z"]) @ xn
+    a = stored(as_qm(layer["in_proj_a"]) @ xn, mode)
+    b = stored(as_qm(layer["in_proj_b"]) @ xn, mode)
+    qkv = stored(as_qm(layer["in_proj_qkv"]) @ xn, mode)
+    z = stored(as_qm(layer["in_proj_z"]) @ xn, mode)
 
     conv_state, s = conv_update_silu(state["conv1d_state"], qkv, layer["conv1d_weight"])
     qk = 2 * Hk * dk
     s = s.copy()
     s[:qk] = l2_norm(s[:qk].reshape(2 * Hk, dk), 1e-6).reshape(-1)
+    s = stored(s, mode)
 
     g = gdn_gate(a, layer["dt_bias"], layer["a_log"])
     beta = gdn_beta(b)
@@ -345,9 +361,9 @@ def forward_linear_attention(cfg, layer: dict, state: dict, x_in: np.ndarray):
         S_new[j], y[j] = gated_delta_step(S_all[j], q[i], k[i], v[j], g[j], beta[j])
 
     yn = rms_norm(y, layer["norm_weight"], cfg.rms_eps)
-    out = as_qm(layer["out_proj"]) @ (silu(z) * yn.reshape(-1))
-    r = x + out
-    x_final, mt = mlp_residual(cfg, layer, r)
+    out = stored(as_qm(layer["out_proj"]) @ (silu(z) * yn.reshape(-1)), mode)
+    r = stored(x + out, mode)
+    x_final, mt = mlp_residual(cfg, layer, r, mode)
 
     taps = {"gdn_x_norm": xn, "gdn_qkv_pre": qkv, "gdn_qkv_smooth": s, "gdn_y": y.reshape(-1),
             "gdn_y_norm": yn.reshape(-1), "gdn_out": out, "gdn_x_resid": r,
@@ -357,11 +373,12 @@ def forward_linear_attention(cfg, layer: dict, state: dict, x_in: np.ndarray):
 
 
 def forward_full_attention(cfg, layer: dict, kv: dict, inv_freq: np.ndarray, x_in: np.ndarray,
-                           cache_pos: int, seq_len_attn: int | None = None):
+                           cache_pos: int, seq_len_attn: int | None = None, mode: str = "A"):
     """One token through one gated full-attention layer (``forward_full_attention``).
 
     kv: {"k": bf16 [cap, Hkv, D], "v": bf16 [cap, Hkv, D]}; a new dict with row
     ``cache_pos`` written is returned, the input is not modified.
+    mode: "A" (default) or "B" (bf16 at the pages' bf16 buffers, see ``stored``).
     Returns (x_out float64, new_kv, taps).
     """
     Hq, Hkv, D, R = cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, cfg.rotary_dim
@@ -370,9 +387,9 @@ def forward_full_attention(cfg, layer: dict, kv: dict, inv_freq: np.ndarray, x_i
     x = act_to_f64(x_in, cfg.act_dtype)
 
     xn = rms_norm(x, layer["input_ln"], cfg.rms_eps)
-    q_full = as_qm(layer["q_proj"]) @ xn
-    k = as_qm(layer["k_proj"]) @ xn
-    v = as_qm(layer["v_proj"]) @ xn
+    q_full = stored(as_qm(layer["q_proj"]) @ xn, mode)
+    k = stored(as_qm(layer["k_proj"]) @ xn, mode)
+    v = stored(as_qm(layer["v_proj"]) @ xn, mode)
 
     # per head [Q_h | gate_h]  (q_total comment, qwen35_qkv_split launch)
     qh = q_full.reshape(Hq, 2 * D)
@@ -391,9 +408,9 @@ def forward_full_attention(cfg, layer: dict, kv: dict, inv_freq: np.ndarray, x_i
 
     attn = attention_decode(qr, kc, vc, seq_len_attn)
     ga = attn * sigmoid(gate)
-    o = as_qm(layer["o_proj"]) @ ga.reshape(-1)
-    r = x + o
-    x_out, mt = mlp_residual(cfg, layer, r)
+    o = stored(as_qm(layer["o_proj"]) @ ga.reshape(-1), mode)
+    r = stored(x + o, mode)
+    x_out, mt = mlp_residual(cfg, layer, r, mode)
 
     taps = {"x_norm": xn, "q_full": q_full, "k": k, "v": v, "q_norm_out": qr.reshape(-1),
             "k_norm_out": kr.reshape(-1), "attn_out": attn.reshape(-1),

@@ -774,3 +774,39 @@ def test_bf16k_turbo4v_append_places_one_row():
     assert np.array_equal(out["k"][3], O.f64_to_bf16(k))
     back = T8.wht(T4.turbo4_dequantize(out["v"][3], out["v_scales"][3]))
     assert np.linalg.norm(back - v) / np.linalg.norm(v) < 0.2   # 4-bit Gaussian codebook: about 0.1
+
+
+# --------------------------------------------------------------------------- Mode B (diagnostic)
+
+
+def _bf16_exact(x):
+    x = np.asarray(x, dtype=np.float64)
+    return np.array_equal(O.bf16_to_f64(O.f64_to_bf16(x)), x)
+
+
+def test_mode_b_rounds_exactly_the_bf16_buffers(gen):
+    """Mode B keeps in bf16 what the pages store in bf16 (GEMV outputs, the smoothed
+    qkv, the residual stream) and stays within bf16 rounding of Mode A."""
+    cfg = synth.tiny("bf16")
+    layer = synth.gdn_layer(gen, cfg, "pin.mb")
+    st = synth.gdn_state(gen, cfg, "pin.mb", 0.1, 0.5)
+    x = gen.act("pin.mb.x", (cfg.hidden,), "bf16")
+    oa, sa, ta = O.forward_linear_attention(cfg, layer, st, x)
+    ob, sb, tb = O.forward_linear_attention(cfg, layer, st, x, mode="B")
+    for name in ("dt_raw", "b_raw", "gdn_qkv_pre", "z", "gdn_qkv_smooth", "gdn_out", "gdn_x_resid",
+                 "gate_act", "up_act"):
+        assert _bf16_exact(tb[name]), name
+        assert not _bf16_exact(ta[name]), name   # Mode A leaves them unrounded
+    assert _bf16_exact(ob)
+    assert np.linalg.norm(ob - oa) / np.linalg.norm(oa) < 1e-2
+    assert np.linalg.norm(sb["gdn_state"] - sa["gdn_state"]) / np.linalg.norm(sa["gdn_state"]) < 1e-2
+    full = synth.full_layer(gen, cfg, "pin.mbf")
+    kv = synth.kv_cache(gen, cfg, "pin.mbf", 8, 3)
+    inv = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
+    fa, _, fta = O.forward_full_attention(cfg, full, kv, inv, x, 3)
+    fb, _, ftb = O.forward_full_attention(cfg, full, kv, inv, x, 3, mode="B")
+    for name in ("q_full", "k", "v", "o", "x_resid", "gate_act", "up_act"):
+        assert _bf16_exact(ftb[name]), name
+    assert np.linalg.norm(fb - fa) / np.linalg.norm(fa) < 1e-2
+    with pytest.raises(ValueError):
+        O.forward_linear_attention(cfg, layer, st, x, mode="C")
