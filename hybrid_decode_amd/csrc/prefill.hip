@@ -50,11 +50,14 @@ Q35_DEV uint32_t bf2_to_h2(uint32_t w) { return pack_h2(bf16_lo(w), bf16_hi(w));
 // ====================================================================== GEMM
 //
 // out[m, n] = sum_k x[m, k] * W[n, k], W[n, k] = s[n, k/64] * code[n, k] + b[n, k/64]
-// (weights dequantised in fp32, rounded once to f16).  Block tile 256 (rows of
-// x) x 128 (rows of W) x 64 (one quantisation group); eight waves, each 64 x 64
-// as 2 x 2 MFMA tiles, so each dequantised weight serves 256 rows.  SwiGLU mode: the 128 W rows are 64 gate rows and the
-// same 64 up rows; a wave holds a gate tile and its up tile, so the epilogue
-// is elementwise in registers.
+// (weights dequantised in fp32, rounded once to f16).  Block tile BM (rows of x:
+// 256 as launched, 128 also built) x 128 (rows of W) x 64 (one quantisation
+// group); 2 BM threads in waves of 64 x 64 as 2 x 2 MFMA tiles, so each
+// dequantised weight serves BM rows.  k tiles pass through two register stages
+// and two LDS buffers: a tile's loads are waited for only where it is written
+// to LDS, a k step after they were issued.  SwiGLU mode: the 128 W rows are 64
+// gate rows and the same 64 up rows; a wave holds a gate tile and its up tile,
+// so the epilogue is elementwise in registers.
 
 constexpr int kBN = 128, kBK = 64, kRow = kBK + 8;  // LDS row: 144 bytes
 
