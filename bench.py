@@ -204,14 +204,16 @@ def prefill_gemm_rate(torch, B, rt, st, cfg, T, rounds=2):
     hidden), every layer's weights in turn; returns (us per launch, flops per launch)."""
     x = torch.zeros((T, cfg.hidden), dtype=torch.int16, device="cuda")
     y = torch.empty((T, cfg.intermediate), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.PREFILL_GEMM_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    wp, wn = ws.data_ptr(), B.PREFILL_GEMM_WORKSPACE_BYTES
     s = rt.stream_ptr()
-    B.q35_prefill_gemm(st.k, st.layers[0].q["gate_proj"].struct, x.data_ptr(), T, y.data_ptr(), s)
+    B.q35_prefill_gemm(st.k, st.layers[0].q["gate_proj"].struct, x.data_ptr(), T, y.data_ptr(), wp, wn, s)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(rounds):
         for L in st.layers:
-            B.q35_prefill_gemm(st.k, L.q["gate_proj"].struct, x.data_ptr(), T, y.data_ptr(), s)
+            B.q35_prefill_gemm(st.k, L.q["gate_proj"].struct, x.data_ptr(), T, y.data_ptr(), wp, wn, s)
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (rounds * len(st.layers))

@@ -19,6 +19,8 @@ Q35_ERR_UNSUPPORTED = 2
 Q35_ERR_OUT_OF_RANGE = 3
 Q35_ERR_HIP = 4
 Q35_ERR_NO_DEVICE = 5
+# q35_prefill_gemm's optional workspace (Q35_PREFILL_GEMM_WORKSPACE_BYTES)
+PREFILL_GEMM_WORKSPACE_BYTES = 32 << 20
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "OUT_OF_RANGE", 4: "HIP", 5: "NO_DEVICE"}
 
 Q35_ACT_BF16 = 0
@@ -197,7 +199,7 @@ def lib():
                                                   P(LinearAttentionState), vp, u32, vp, vp, sz, vp]),
             "q35_prefill_full_attention": (st, [vp, P(Qwen35ForwardConfig), P(FullAttentionLayer),
                                                 P(LayerKvCache), vp, vp, u32, u32, vp, vp, sz, vp]),
-            "q35_prefill_gemm": (st, [vp, P(Q35QuantWeight), vp, u32, vp, vp]),
+            "q35_prefill_gemm": (st, [vp, P(Q35QuantWeight), vp, u32, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -409,5 +411,5 @@ def q35_prefill_full_attention(kernels, cfg, layer, kv, inv_freq, x_in, n_tokens
                                             workspace_bytes, stream))
 
 
-def q35_prefill_gemm(kernels, w, x_f16, m: int, y, stream) -> None:
-    _check(lib().q35_prefill_gemm(kernels, C.byref(w), x_f16, m, y, stream))
+def q35_prefill_gemm(kernels, w, x_f16, m: int, y, workspace, workspace_bytes: int, stream) -> None:
+    _check(lib().q35_prefill_gemm(kernels, C.byref(w), x_f16, m, y, workspace, workspace_bytes, stream))

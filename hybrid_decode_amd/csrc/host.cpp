@@ -944,6 +944,7 @@ namespace {
 struct PfWs {
     size_t xh, qkv, z, fa, fb, qkvs, lg, beta, wc, uc, pc, lc, y, yz, r, h;  // GDN
     size_t qf, kf, vf, qb, ga;                                               // full (xh, r, h shared)
+    size_t part;                                                             // split GEMM partial tiles
     uint32_t nch;
     size_t bytes;
 };
@@ -983,7 +984,9 @@ PfWs pf_ws_layout(const Qwen35ForwardConfig& c, uint32_t T) {
     w.vf = take(o, t * kv_dim(c) * 4);
     w.qb = take(o, t * q_only(c) * 2);
     w.ga = take(o, t * q_only(c) * 2);
-    w.bytes = gdn > o ? gdn : o;
+    o = gdn > o ? gdn : o;
+    w.part = take(o, T ? kPfSplitBytes : 0);
+    w.bytes = o;
     return w;
 }
 
@@ -992,10 +995,17 @@ T* at_off(void* base, size_t off) {
     return reinterpret_cast<T*>(static_cast<char*>(base) + off);
 }
 
+// Where a GEMM launch may leave the partial tiles of a split last round (part
+// NULL: never split), and the compute units it plans the rounds for.
+struct PfSplit {
+    float* part;
+    uint32_t num_cu;
+};
+
 // One prefill GEMM launch.  F32 mode: up to four matrices stacked by rows, each
 // writing its own fp32 output (row stride = its rows); RESID and SWIGLU: ws[0]
 // (and ws[1] = up_proj for SWIGLU) into out with row stride ldo.
-q35_status pf_gemm(const char* what, int mode, const uint16_t* x, uint32_t M,
+q35_status pf_gemm(const PfSplit& sp, const char* what, int mode, const uint16_t* x, uint32_t M,
                    std::initializer_list<const Q35QuantWeight*> ws, std::initializer_list<void*> outs,
                    uint32_t ldo, const void* resid, bool resid_f32, bool out_f32, hipStream_t stream) {
     PfGemmArgs g{};
@@ -1019,7 +1029,8 @@ q35_status pf_gemm(const char* what, int mode, const uint16_t* x, uint32_t M,
     g.K = (*ws.begin())->k;
     g.resid_f32 = resid_f32 ? 1 : 0;
     g.out_f32 = out_f32 ? 1 : 0;
-    Q35_HIP(pf_gemm_launch(mode, g, stream), what);
+    g.part = sp.part;
+    Q35_HIP(pf_gemm_launch(mode, g, sp.num_cu, stream), what);
     return Q35_OK;
 }
 
@@ -1036,15 +1047,15 @@ q35_status pf_check_ws(const Qwen35ForwardConfig& c, uint32_t T, const void* ws,
 
 // the MLP half shared by both kinds: xn2 = RMSNorm(r), gate/up SwiGLU, down + r -> x_out
 template <class L>
-q35_status pf_mlp(const Qwen35ForwardConfig& c, const L& l, const PfWs& w, void* ws, uint32_t T,
-                  void* x_out, hipStream_t stream) {
+q35_status pf_mlp(const PfSplit& sp, const Qwen35ForwardConfig& c, const L& l, const PfWs& w, void* ws,
+                  uint32_t T, void* x_out, hipStream_t stream) {
     uint16_t* xh = at_off<uint16_t>(ws, w.xh);
     float* r = at_off<float>(ws, w.r);
     uint16_t* h = at_off<uint16_t>(ws, w.h);
     Q35_HIP(pf_rmsnorm_launch(r, true, l.post_ln, xh, T, c.hidden, c.rms_eps, stream), "prefill post norm");
-    Q35_TRY(pf_gemm("prefill gate/up", kPfSwiglu, xh, T, {&l.gate_proj, &l.up_proj}, {h}, c.intermediate,
+    Q35_TRY(pf_gemm(sp, "prefill gate/up", kPfSwiglu, xh, T, {&l.gate_proj, &l.up_proj}, {h}, c.intermediate,
                     nullptr, false, false, stream));
-    Q35_TRY(pf_gemm("prefill down", kPfResid, h, T, {&l.down_proj}, {x_out}, c.hidden, r, true,
+    Q35_TRY(pf_gemm(sp, "prefill down", kPfResid, h, T, {&l.down_proj}, {x_out}, c.hidden, r, true,
                     c.act_dtype == Q35_ACT_F32, stream));
     return Q35_OK;
 }
@@ -1083,6 +1094,7 @@ q35_status q35_prefill_linear_attention(const Qwen35Kernels* kernels,
     const uint32_t T = n_tokens, C = qkv_total(c);
     const bool f32 = c.act_dtype == Q35_ACT_F32;
     void* ws = workspace;
+    const PfSplit sp{at_off<float>(ws, w.part), (uint32_t)kernels->num_cu};
     const LinearAttentionLayer& l = *layer;
     uint16_t* xh = at_off<uint16_t>(ws, w.xh);
     float* qkv = at_off<float>(ws, w.qkv);
@@ -1091,8 +1103,9 @@ q35_status q35_prefill_linear_attention(const Qwen35Kernels* kernels,
     float* fb = at_off<float>(ws, w.fb);
 
     Q35_HIP(pf_rmsnorm_launch(x_in, f32, l.input_ln, xh, T, c.hidden, c.rms_eps, stream), "prefill input norm");
-    Q35_TRY(pf_gemm("prefill in_proj", kPfF32, xh, T, {&l.in_proj_qkv, &l.in_proj_z, &l.in_proj_a, &l.in_proj_b},
-                    {qkv, z, fa, fb}, 0, nullptr, false, true, stream));
+    Q35_TRY(pf_gemm(sp, "prefill in_proj", kPfF32, xh, T,
+                    {&l.in_proj_qkv, &l.in_proj_z, &l.in_proj_a, &l.in_proj_b}, {qkv, z, fa, fb}, 0, nullptr,
+                    false, true, stream));
 
     PfConvArgs cv{};
     cv.qkv = qkv;
@@ -1131,9 +1144,9 @@ q35_status q35_prefill_linear_attention(const Qwen35Kernels* kernels,
     Q35_HIP(pf_gdn_launch(cv, g, state->conv1d_state, stream), "prefill gated delta rule");
     uint16_t* yz = at_off<uint16_t>(ws, w.yz);
     Q35_HIP(pf_gdn_out_launch(g.y, z, l.norm_weight, yz, T, hv, dv, c.rms_eps, stream), "prefill gated norm");
-    Q35_TRY(pf_gemm("prefill out_proj", kPfResid, yz, T, {&l.out_proj}, {at_off<float>(ws, w.r)}, c.hidden,
+    Q35_TRY(pf_gemm(sp, "prefill out_proj", kPfResid, yz, T, {&l.out_proj}, {at_off<float>(ws, w.r)}, c.hidden,
                     x_in, f32, true, stream));
-    Q35_TRY(pf_mlp(c, l, w, ws, T, x_out, stream));
+    Q35_TRY(pf_mlp(sp, c, l, w, ws, T, x_out, stream));
     return ok();
 }
 
@@ -1163,13 +1176,14 @@ q35_status q35_prefill_full_attention(const Qwen35Kernels* kernels, const Qwen35
     const uint32_t T = n_tokens;
     const bool f32 = c.act_dtype == Q35_ACT_F32;
     void* ws = workspace;
+    const PfSplit sp{at_off<float>(ws, w.part), (uint32_t)kernels->num_cu};
     const FullAttentionLayer& l = *layer;
     uint16_t* xh = at_off<uint16_t>(ws, w.xh);
     float* qf = at_off<float>(ws, w.qf);
     float* kf = at_off<float>(ws, w.kf);
     float* vf = at_off<float>(ws, w.vf);
     Q35_HIP(pf_rmsnorm_launch(x_in, f32, l.input_ln, xh, T, c.hidden, c.rms_eps, stream), "prefill input norm");
-    Q35_TRY(pf_gemm("prefill q/k/v", kPfF32, xh, T, {&l.q_proj, &l.k_proj, &l.v_proj}, {qf, kf, vf}, 0, nullptr,
+    Q35_TRY(pf_gemm(sp, "prefill q/k/v", kPfF32, xh, T, {&l.q_proj, &l.k_proj, &l.v_proj}, {qf, kf, vf}, 0, nullptr,
                     false, true, stream));
     PfRopeArgs rp{};
     rp.q_full = qf;
@@ -1200,14 +1214,16 @@ q35_status q35_prefill_full_attention(const Qwen35Kernels* kernels, const Qwen35
     at.hkv = c.num_kv_heads;
     at.scale_log2 = 1.4426950408889634f / std::sqrt((float)c.head_dim);
     Q35_HIP(pf_attn_launch(rp, at, stream), "prefill attention");
-    Q35_TRY(pf_gemm("prefill o_proj", kPfResid, at.ga, T, {&l.o_proj}, {at_off<float>(ws, w.r)}, c.hidden,
+    Q35_TRY(pf_gemm(sp, "prefill o_proj", kPfResid, at.ga, T, {&l.o_proj}, {at_off<float>(ws, w.r)}, c.hidden,
                     x_in, f32, true, stream));
-    Q35_TRY(pf_mlp(c, l, w, ws, T, x_out, stream));
+    Q35_TRY(pf_mlp(sp, c, l, w, ws, T, x_out, stream));
     return ok();
 }
 
+static_assert(Q35_PREFILL_GEMM_WORKSPACE_BYTES == kPfSplitBytes, "split workspace size");
+
 q35_status q35_prefill_gemm(const Qwen35Kernels* kernels, const Q35QuantWeight* w, const uint16_t* x_f16,
-                            uint32_t m, float* y, hipStream_t stream) {
+                            uint32_t m, float* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     Q35_TRY(check_kernels(kernels));
     if (!w) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
     Q35_TRY(check_weight("w", *w, w->n, w->k));
@@ -1215,8 +1231,11 @@ q35_status q35_prefill_gemm(const Qwen35Kernels* kernels, const Q35QuantWeight* 
         return fail(Q35_ERR_INVALID_ARG, "w: shape [%u, %u] (k a nonzero multiple of 64)", w->n, w->k);
     Q35_TRY(need(x_f16, "x_f16"));
     Q35_TRY(need(y, "y", false));
+    if (workspace && ((reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < kPfSplitBytes))
+        return fail(Q35_ERR_INVALID_ARG, "workspace: %zu bytes, 256-byte aligned, needed (or NULL)", kPfSplitBytes);
     if (m == 0) return ok();
-    Q35_TRY(pf_gemm("prefill GEMM", kPfF32, x_f16, m, {w}, {y}, 0, nullptr, false, true, stream));
+    const PfSplit sp{static_cast<float*>(workspace), (uint32_t)kernels->num_cu};
+    Q35_TRY(pf_gemm(sp, "prefill GEMM", kPfF32, x_f16, m, {w}, {y}, 0, nullptr, false, true, stream));
     return ok();
 }
 

@@ -58,8 +58,31 @@ Q35_DEV uint32_t bf2_to_h2(uint32_t w) { return pack_h2(bf16_lo(w), bf16_hi(w));
 // to LDS, a k step after they were issued.  SwiGLU mode: the 128 W rows are 64
 // gate rows and the same 64 up rows; a wave holds a gate tile and its up tile,
 // so the epilogue is elementwise in registers.
+//
+// Wave quantisation.  A launch of n tiles on C compute units (one block each)
+// runs ceil(n / C) rounds; when the last round would be less than half full, its
+// tiles are cut into `split` ranges of k tiles, one block each, so that round
+// takes 1/split of the time.  Those blocks leave fp32 partial tiles in a
+// workspace and gemm_reduce_kernel adds the parts in order and applies the
+// epilogue.
 
 constexpr int kBN = 128, kBK = 64, kRow = kBK + 8;  // LDS row: 144 bytes
+
+// Tile t of a launch -> (row tile, column tile).  Consecutive blocks go to the 8
+// XCDs in turn, so block b runs on XCD b % 8.  When the row tiles divide evenly,
+// XCD x takes the row tiles x, x + 8, ... and sweeps all column tiles of one row
+// tile before the next: the blocks an XCD runs at once share their x tile in
+// that XCD's L2.
+Q35_DEV void tile_of(uint32_t t, uint32_t n_mt, uint32_t n_nt, uint32_t& mt, uint32_t& nt) {
+    if (n_mt % 8 == 0) {
+        const uint32_t slot = t / 8;
+        mt = t % 8 + 8 * (slot / n_nt);
+        nt = slot % n_nt;
+    } else {
+        mt = t / n_nt;
+        nt = t % n_nt;
+    }
+}
 
 // BM rows of x per block (128 or 256), 2 BM threads: waves of 64 x 64.
 template <int MODE, int BM>
@@ -69,24 +92,19 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_kernel(PfGemmArgs a) {
     __shared__ __align__(16) _Float16 ws[2][kBN * kRow];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wm = wid >> 1, wn = wid & 1;
-    // Tiles per XCD: consecutive blocks go to the 8 XCDs in turn, so block b runs
-    // on XCD b % 8.  When the row tiles divide evenly, XCD x takes the row tiles
-    // x, x + 8, ... and sweeps all column tiles of one row tile before the next:
-    // the blocks an XCD runs at once share their x tile in that XCD's L2.
     const uint32_t bn = MODE == kPfSwiglu ? kBN / 2 : kBN;
     const uint32_t n_nt = (a.N + bn - 1) / bn, n_mt = (a.M + kBM - 1) / kBM, b = blockIdx.x;
+    // blocks [0, n_full) take whole tiles; block n_full + split j + p takes k range
+    // p of tail tile n_full + j
+    const bool whole = b < a.n_full;
+    const uint32_t pb = whole ? 0 : b - a.n_full;
     uint32_t mt, nt;
-    if (n_mt % 8 == 0) {
-        const uint32_t slot = b / 8;
-        mt = b % 8 + 8 * (slot / n_nt);
-        nt = slot % n_nt;
-    } else {
-        mt = b / n_nt;
-        nt = b % n_nt;
-    }
+    tile_of(whole ? b : a.n_full + pb / a.split, n_mt, n_nt, mt, nt);
     const uint32_t m0 = mt * kBM;
     const uint32_t n0 = nt * bn;
-    const uint32_t nk = a.K / kBK, ng = a.K / 64;
+    const uint32_t nk_all = a.K / kBK, ng = a.K / 64;
+    const uint32_t k_lo = whole ? 0 : (pb % a.split) * nk_all / a.split;
+    const uint32_t nk = whole ? nk_all : (pb % a.split + 1) * nk_all / a.split - k_lo;
 
     // global -> register staging of one k tile (two stages in flight)
     struct Stage {
@@ -123,6 +141,7 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_kernel(PfGemmArgs a) {
         wmsk[wi] = live ? 0xFFFFFFFFu : 0u;
     }
     auto load = [&](Stage& g, uint32_t kt) {
+        kt += k_lo;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int c = tid + kGemmThreads * i, row = c >> 3, col = (c & 7) * 8;
@@ -218,7 +237,23 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_kernel(PfGemmArgs a) {
     }
 
     // epilogue: acc[i][j][r] is (row 8 (r/4) + 4 (lane/32) + r%4, column lane%32) of its tile
-    if constexpr (MODE == kPfSwiglu) {
+    if (!whole) {
+        // partial tile [kBM][kBN] in fp32, columns as the tile's W rows (SwiGLU:
+        // gate rows 0..63, up rows 64..127); rows past the last one of x are not
+        // written (the reduction skips them), columns past the matrix hold zeros
+        float* pp = a.part + (size_t)pb * (kBM * kBN);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = (MODE == kPfSwiglu ? 64 * j + 32 * wn : 64 * wn + 32 * j) + (lane & 31);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const uint32_t row = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (m0 + row < a.M) pp[row * kBN + col] = acc[i][j][r];
+                }
+        }
+    } else if constexpr (MODE == kPfSwiglu) {
         const uint32_t n = n0 + 32 * wn + (lane & 31);
         if (n < a.N) {
             uint16_t* out = static_cast<uint16_t*>(a.out[0]) + n;
@@ -255,6 +290,50 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_kernel(PfGemmArgs a) {
                         store_act(out, o, acc[i][j][r] + load_act(a.resid, o, a.resid_f32), a.out_f32);
                     }
                 }
+        }
+    }
+}
+
+// The tail tiles of a split launch: out = epilogue(sum of the `split` fp32 parts,
+// added in k order).  One thread per four consecutive columns of a tile row.
+template <int MODE, int BM>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(PfGemmArgs a) {
+    constexpr uint32_t kTile = BM * kBN, kPerTile = kTile / 4;
+    const uint32_t bn = MODE == kPfSwiglu ? kBN / 2 : kBN;
+    const uint32_t n_nt = (a.N + bn - 1) / bn, n_mt = (a.M + BM - 1) / BM;
+    const uint32_t g = blockIdx.x * 256 + threadIdx.x, j = g / kPerTile, e = g % kPerTile;
+    const uint32_t row = e / (kBN / 4), c4 = (e % (kBN / 4)) * 4;
+    if (MODE == kPfSwiglu && c4 >= kBN / 2) return;  // the up half is read with its gate half
+    uint32_t mt, nt;
+    tile_of(a.n_full + j, n_mt, n_nt, mt, nt);
+    const uint32_t m = mt * BM + row;
+    if (m >= a.M) return;
+    const float* pp = a.part + (size_t)j * a.split * kTile + row * kBN + c4;
+    float4 v = *reinterpret_cast<const float4*>(pp), u = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (MODE == kPfSwiglu) u = *reinterpret_cast<const float4*>(pp + kBN / 2);
+    for (uint32_t p = 1; p < a.split; ++p) {
+        const float4 w = *reinterpret_cast<const float4*>(pp + (size_t)p * kTile);
+        v.x += w.x, v.y += w.y, v.z += w.z, v.w += w.w;
+        if (MODE == kPfSwiglu) {
+            const float4 w2 = *reinterpret_cast<const float4*>(pp + (size_t)p * kTile + kBN / 2);
+            u.x += w2.x, u.y += w2.y, u.z += w2.z, u.w += w2.w;
+        }
+    }
+    const float vv[4] = {v.x, v.y, v.z, v.w}, uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint32_t n = nt * bn + c4 + c;
+        if (n >= a.N) break;
+        if constexpr (MODE == kPfSwiglu) {
+            static_cast<uint16_t*>(a.out[0])[(size_t)m * a.ldo[0] + n] = to_h(silu(vv[c]) * uu[c]);
+        } else if constexpr (MODE == kPfF32) {
+            const uint32_t q = (n >= a.seg_end[0]) + (n >= a.seg_end[1]) + (n >= a.seg_end[2]);
+            const uint32_t n1 = n - (q == 0 ? 0 : q == 1 ? a.seg_end[0] : q == 2 ? a.seg_end[1] : a.seg_end[2]);
+            float* out = static_cast<float*>(q == 0 ? a.out[0] : q == 1 ? a.out[1] : q == 2 ? a.out[2] : a.out[3]);
+            out[(size_t)m * (q == 0 ? a.ldo[0] : q == 1 ? a.ldo[1] : q == 2 ? a.ldo[2] : a.ldo[3]) + n1] = vv[c];
+        } else {
+            const size_t o = (size_t)m * a.ldo[0] + n;
+            store_act(a.out[0], o, vv[c] + load_act(a.resid, o, a.resid_f32), a.out_f32);
         }
     }
 }
@@ -927,6 +1006,9 @@ const void* pf_kernel_ptr(int i) {
         reinterpret_cast<const void*>(pf::gemm_kernel<kPfF32, 256>),
         reinterpret_cast<const void*>(pf::gemm_kernel<kPfResid, 256>),
         reinterpret_cast<const void*>(pf::gemm_kernel<kPfSwiglu, 256>),
+        reinterpret_cast<const void*>(pf::gemm_reduce_kernel<kPfF32, 256>),
+        reinterpret_cast<const void*>(pf::gemm_reduce_kernel<kPfResid, 256>),
+        reinterpret_cast<const void*>(pf::gemm_reduce_kernel<kPfSwiglu, 256>),
         reinterpret_cast<const void*>(pf::rmsnorm_rows_kernel),
         reinterpret_cast<const void*>(pf::gdn_conv_kernel),
         reinterpret_cast<const void*>(pf::gdn_conv_state_kernel),
@@ -944,22 +1026,45 @@ const void* pf_kernel_ptr(int i) {
     return i >= 0 && i < (int)(sizeof(k) / sizeof(k[0])) ? k[i] : nullptr;
 }
 
+// The split plan: with n tiles on num_cu compute units (one block each), a last
+// round of t = n % num_cu tiles with 2 t <= min(num_cu, kPfSplitBlocks) is cut
+// into split = min(that / t, 8, k tiles) ranges of k tiles.
 template <int BM>
-static hipError_t gemm_launch_bm(int mode, const PfGemmArgs& a, hipStream_t s) {
-    const uint32_t bn = mode == kPfSwiglu ? pf::kBN / 2 : pf::kBN;
-    const dim3 grid(((a.N + bn - 1) / bn) * ((a.M + BM - 1) / BM));
-    switch (mode) {
-        case kPfF32: pf::gemm_kernel<kPfF32, BM><<<grid, 2 * BM, 0, s>>>(a); break;
-        case kPfResid: pf::gemm_kernel<kPfResid, BM><<<grid, 2 * BM, 0, s>>>(a); break;
-        case kPfSwiglu: pf::gemm_kernel<kPfSwiglu, BM><<<grid, 2 * BM, 0, s>>>(a); break;
-        default: return hipErrorInvalidValue;
-    }
+static void gemm_plan(PfGemmArgs& a, uint32_t bn, uint32_t num_cu) {
+    const uint32_t n_tiles = ((a.N + bn - 1) / bn) * ((a.M + BM - 1) / BM);
+    a.n_full = n_tiles;
+    a.split = 1;
+    if (!a.part || num_cu == 0) return;
+    const uint32_t slots = num_cu < kPfSplitBlocks ? num_cu : kPfSplitBlocks, tail = n_tiles % num_cu;
+    if (tail == 0 || 2 * tail > slots) return;
+    uint32_t split = slots / tail;
+    if (split > 8) split = 8;
+    if (split > a.K / pf::kBK) split = a.K / pf::kBK;
+    if (split < 2) return;
+    a.n_full = n_tiles - tail;
+    a.split = split;
+}
+
+template <int MODE, int BM>
+static hipError_t gemm_launch_mode(PfGemmArgs a, uint32_t num_cu, hipStream_t s) {
+    const uint32_t bn = MODE == kPfSwiglu ? pf::kBN / 2 : pf::kBN;
+    gemm_plan<BM>(a, bn, num_cu);
+    const uint32_t n_tiles = ((a.N + bn - 1) / bn) * ((a.M + BM - 1) / BM), tail = n_tiles - a.n_full;
+    pf::gemm_kernel<MODE, BM><<<a.n_full + tail * a.split, 2 * BM, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || tail == 0) return e;
+    pf::gemm_reduce_kernel<MODE, BM><<<tail * (BM * pf::kBN / 4 / 256), 256, 0, s>>>(a);
     return hipGetLastError();
 }
 
-hipError_t pf_gemm_launch(int mode, const PfGemmArgs& a, hipStream_t s) {
+hipError_t pf_gemm_launch(int mode, const PfGemmArgs& a, uint32_t num_cu, hipStream_t s) {
     if (a.M == 0) return hipSuccess;
-    return gemm_launch_bm<256>(mode, a, s);
+    switch (mode) {
+        case kPfF32: return gemm_launch_mode<kPfF32, 256>(a, num_cu, s);
+        case kPfResid: return gemm_launch_mode<kPfResid, 256>(a, num_cu, s);
+        case kPfSwiglu: return gemm_launch_mode<kPfSwiglu, 256>(a, num_cu, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t pf_rmsnorm_launch(const void* x, bool x_f32, const uint16_t* w, uint16_t* out, uint32_t T,

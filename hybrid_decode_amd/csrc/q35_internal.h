@@ -270,8 +270,14 @@ struct PfGemmArgs {
     const void* resid;
     uint32_t M, N, K;
     uint32_t resid_f32, out_f32;
+    float* part;               // fp32 partial tiles of a split last round (NULL: never split)
+    uint32_t n_full, split;    // set by the launcher
 };
-hipError_t pf_gemm_launch(int mode, const PfGemmArgs& a, hipStream_t s);
+// Most blocks of split k ranges one launch holds: kPfSplitBlocks partial tiles of
+// 256 x 128 fp32 (32 MiB).
+constexpr uint32_t kPfSplitBlocks = 256;
+constexpr size_t kPfSplitBytes = (size_t)kPfSplitBlocks * 256 * 128 * 4;
+hipError_t pf_gemm_launch(int mode, const PfGemmArgs& a, uint32_t num_cu, hipStream_t s);
 // f16 rows of RMSNorm(x) for T rows of H (x fp32 or bf16)
 hipError_t pf_rmsnorm_launch(const void* x, bool x_f32, const uint16_t* w, uint16_t* out, uint32_t T,
                              uint32_t H, float eps, hipStream_t s);

@@ -646,11 +646,18 @@ q35_status q35_prefill_full_attention(const Qwen35Kernels* kernels, const Qwen35
  * The prefill's quantised-weight GEMM: y (fp32 [m, w->n]) = x W^T with x f16
  * [m, w->k] (16-byte aligned rows), W[n, k] = scale * code + bias evaluated in
  * fp32 and rounded to f16, products on the matrix cores with fp32 sums.
- * Exported so that it can be tested and timed on its own.  m == 0 enqueues
- * nothing.
+ * Exported so that it can be tested and timed on its own.  workspace: NULL, or
+ * device memory of Q35_PREFILL_GEMM_WORKSPACE_BYTES, 256-byte aligned,
+ * caller-owned and rewritten by the call: with it, a last round of tiles that
+ * would leave most compute units idle is cut along k into parts whose fp32
+ * sums are added in k order by a second kernel (the result then differs from
+ * the NULL case by fp32 rounding only).  A smaller or misaligned workspace:
+ * Q35_ERR_INVALID_ARG.  m == 0 enqueues nothing.
  */
+#define Q35_PREFILL_GEMM_WORKSPACE_BYTES ((size_t)32 << 20)
 q35_status q35_prefill_gemm(const Qwen35Kernels* kernels, const Q35QuantWeight* w,
-                            const uint16_t* x_f16, uint32_t m, float* y, hipStream_t stream);
+                            const uint16_t* x_f16, uint32_t m, float* y, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -280,7 +280,13 @@ def test_prefill_errors_before_any_launch(lib):
 def test_prefill_gemm_shape_errors(lib):
     w = B.Q35QuantWeight(0x1000, 0x2000, 0x3000, 8, 96)  # k not a multiple of 64
     with pytest.raises(B.Q35Error) as e:
-        B.q35_prefill_gemm(FAKE_KERNELS, w, 0x100, 4, 0x100, None)
+        B.q35_prefill_gemm(FAKE_KERNELS, w, 0x100, 4, 0x100, None, 0, None)
     assert e.value.status == B.Q35_ERR_INVALID_ARG
     w = B.Q35QuantWeight(0x1000, 0x2000, 0x3000, 8, 128)
-    B.q35_prefill_gemm(FAKE_KERNELS, w, 0x100, 0, 0x100, None)  # m == 0: nothing enqueued
+    # a workspace too small or misaligned for the split partial tiles
+    for ws, n in ((0x10000, B.PREFILL_GEMM_WORKSPACE_BYTES - 256), (0x10010, B.PREFILL_GEMM_WORKSPACE_BYTES)):
+        with pytest.raises(B.Q35Error) as e:
+            B.q35_prefill_gemm(FAKE_KERNELS, w, 0x100, 4, 0x100, ws, n, None)
+        assert e.value.status == B.Q35_ERR_INVALID_ARG and "workspace" in str(e.value)
+    B.q35_prefill_gemm(FAKE_KERNELS, w, 0x100, 0, 0x100, None, 0, None)  # m == 0: nothing enqueued
+    B.q35_prefill_gemm(FAKE_KERNELS, w, 0x100, 0, 0x100, 0x10000, B.PREFILL_GEMM_WORKSPACE_BYTES, None)

@@ -44,23 +44,56 @@ def _rows_rel(gpu, ref):
 # --------------------------------------------------------------------------- GEMM
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 64, 64), (77, 200, 256), (300, 384, 640), (129, 2560, 2560)])
-def test_prefill_gemm_matches_float64_on_the_same_f16_operands(rt, gen, m, n, k):
+def _gemm(rt, wq, x, m, n, split):
+    """q35_prefill_gemm of f16 x [m, k] by wq, fp32 out; with `split` it gets the
+    workspace that lets it cut a sparse last round of tiles along k."""
     from hybrid_decode_amd import binding as B
-    say(f"prefill GEMM m={m} n={n} k={k}")
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.PREFILL_GEMM_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda") if split else None
+    B.q35_prefill_gemm(rt.kernels(), wq.struct, xd.data_ptr(), m, y.data_ptr(),
+                       ws.data_ptr() if split else None, B.PREFILL_GEMM_WORKSPACE_BYTES if split else 0,
+                       rt.stream_ptr())
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("m,n,k", [(1, 64, 64), (77, 200, 256), (300, 384, 640), (129, 2560, 2560)])
+def test_prefill_gemm_matches_float64_on_the_same_f16_operands(rt, gen, m, n, k, split):
+    """With the workspace, every shape but the first (one k tile) has fewer tiles
+    than half the compute units, so all its tiles run as 4 or 8 k ranges."""
+    say(f"prefill GEMM m={m} n={n} k={k} split={split}")
     w = gen.quant(f"pf.gemm.{m}.{n}.{k}", n, k)
     x = gen.normal_f32(f"pf.gemm.x.{m}.{k}", (m, k)).astype(np.float16)
     ref = x.astype(np.float64) @ O.dequant(w).astype(np.float16).astype(np.float64).T
-    wq = rt.QuantWeightDev(w)
-    xd = torch.from_numpy(x.view(np.int16)).cuda()
-    y = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
-    B.q35_prefill_gemm(rt.kernels(), wq.struct, xd.data_ptr(), m, y.data_ptr(), rt.stream_ptr())
-    torch.cuda.synchronize()
-    got = y.cpu().numpy()
+    got = _gemm(rt, rt.QuantWeightDev(w), x, m, n, split)
     assert np.isfinite(got).all()
     # identical f16 operands: only the fp32 order of the sums differs
     assert rel(got, ref) < 1e-5
     assert _rows_rel(got, ref) < 1e-4
+
+
+def test_prefill_gemm_4096_rows_at_the_gate_proj_shape(rt, gen):
+    """The GEMM the benchmark times (4096 x 9216 x 2560: 1152 tiles, four whole
+    rounds on 256 compute units and a half round cut in two along k).  Sampled rows
+    in every row tile and on the tile edges against float64 on the same f16
+    operands; the whole output against the launch without a workspace (no split),
+    which differs by fp32 rounding only."""
+    m, n, k = 4096, 9216, 2560
+    say(f"prefill GEMM m={m} n={n} k={k}")
+    w = gen.quant("pf.gemm.big", n, k)
+    x = (0.5 * gen.normal_f32("pf.gemm.big.x", (m, k))).astype(np.float16)
+    wq = rt.QuantWeightDev(w)
+    got = _gemm(rt, wq, x, m, n, True)
+    plain = _gemm(rt, wq, x, m, n, False)
+    assert np.isfinite(got).all() and np.isfinite(plain).all()
+    rows = np.array(sorted({0, 1, 255, 256, 511, 1023, 1024, 2047, 2048, 3001, 3839, 3840, 4095}
+                           | set(range(17, m, 256))))
+    ref = x[rows].astype(np.float64) @ O.dequant(w).astype(np.float16).astype(np.float64).T
+    assert _rows_rel(got[rows], ref) < 1e-4
+    assert _rows_rel(plain[rows], ref) < 1e-4
+    assert _rows_rel(got, plain) < 1e-5
 
 
 # --------------------------------------------------------------------------- GDN layer
@@ -260,3 +293,135 @@ def test_prefill_gdn_head_dim_64(rt, gen):
     assert _rows_rel(out, ref) < TOL_F32
     assert rel(gst["gdn_state"], rst["gdn_state"]) < TOL_F32
     assert rel(gst["conv1d_state"], rst["conv1d_state"]) < TOL_F32
+
+
+# --------------------------------------------------------------------------- edge cases
+
+
+def test_prefill_zero_tokens_changes_nothing(rt, gen):
+    """n_tokens == 0 is an empty prompt: the call succeeds and touches neither the
+    state, the cache nor x_out."""
+    from hybrid_decode_amd import binding as B
+    say("prefill with zero tokens")
+    cfg = synth.tiny("f32")
+    cs = rt.cfg_struct(cfg)
+    ws, n = _workspace(B, cs, 1)
+    sentinel = torch.full((cfg.hidden,), 7.0, dtype=torch.float32, device="cuda")
+    xin = rt.to_dev(gen.act("pf.z.x", (1, cfg.hidden), "f32"))
+
+    layer = synth.gdn_layer(gen, cfg, "pf.z.g")
+    st = synth.gdn_state(gen, cfg, "pf.z.g", 0.2, 0.5)
+    L, S = rt.GdnLayerDev(layer), rt.GdnStateDev(st)
+    B.q35_prefill_linear_attention(rt.kernels(), cs, L.struct, S.struct, xin.data_ptr(), 0,
+                                   sentinel.data_ptr(), ws.data_ptr(), n, rt.stream_ptr())
+
+    layer = synth.full_layer(gen, cfg, "pf.z.f")
+    kv = synth.kv_cache(gen, cfg, "pf.z.f", 16, 5)
+    Lf, K = rt.FullLayerDev(layer), rt.KvCacheDev(kv)
+    inv = torch.from_numpy(O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)).cuda()
+    B.q35_prefill_full_attention(rt.kernels(), cs, Lf.struct, K.struct, inv.data_ptr(), xin.data_ptr(), 0,
+                                 5, sentinel.data_ptr(), ws.data_ptr(), n, rt.stream_ptr())
+    torch.cuda.synchronize()
+    after = S.to_host()
+    for k in ("gdn_state", "conv1d_state"):
+        assert np.array_equal(after[k], st[k]), k
+    kv_after = K.to_host()
+    for s in ("k", "v"):
+        assert np.array_equal(kv_after[s], kv[s]), s
+    assert bool((sentinel == 7.0).all())
+
+
+def test_prefill_full_fills_the_cache_to_capacity(rt, gen):
+    """cache_pos + n_tokens == capacity: the last row written is the cache's last
+    row (the largest prompt a cache takes)."""
+    say("prefill full tiny up to the cache capacity")
+    cfg = synth.tiny("f32")
+    layer = synth.full_layer(gen, cfg, "pf.cap")
+    pos, T = 24, 40
+    kv = synth.kv_cache(gen, cfg, "pf.cap", pos + T, pos)
+    x = gen.act("pf.cap.x", (T, cfg.hidden), "f32")
+    before = {s: kv[s].copy() for s in ("k", "v")}
+    out, after = _full_run(rt, cfg, layer, kv, x, pos)
+    inv = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
+    ref, rkv, _ = O.prefill.prefill_full_attention(cfg, layer, kv, inv, x, pos)
+    assert _rows_rel(out, ref) < TOL_F32
+    _check_cache(after, before, rkv, pos, T)
+
+
+# --------------------------------------------------------------------------- 4096-token prompts
+
+BIG_T, PREFIX = 4096, 300
+
+
+# One call of 4096 tokens against two of 2048: the projections split different
+# tail tiles along k (the tile count changes with the prompt length), so the two
+# differ by the fp32 order of those sums, which can move a bf16 output or cache
+# element by one rounding step (2^-8 relative): SPLIT_BF16 = 4e-3; the fp32 GDN
+# state only by fp32 rounding.
+SPLIT_BF16, SPLIT_F32 = 4e-3, 1e-5
+
+
+def _split_rel(a, b):
+    """Largest row-relative difference, and whether the two are bit-identical."""
+    return _rows_rel(a, b), bool(np.array_equal(a, b))
+
+
+def test_prefill_gdn_4b_4096_tokens(rt, gen):
+    """The benchmark's prompt through one 4B GDN layer (16 row tiles per GEMM, 64
+    chunks).  A token's output depends on the tokens before it only, so the first
+    300 outputs (two row tiles, four whole chunks and a ragged fifth) are checked
+    against the oracle's loop over those 300 tokens; all 4096 outputs and the final
+    state against the same prompt sent as two calls of 2048 tokens (SPLIT_*)."""
+    cfg = synth.qwen3_5_4b("bf16")
+    layer = synth.gdn_layer(gen, cfg, "pf.big.g")
+    st = synth.gdn_state(gen, cfg, "pf.big.g", 0.05, 0.5)
+    x = gen.act("pf.big.g.x", (BIG_T, cfg.hidden), "bf16")
+    say(f"prefill GDN 4B T={BIG_T} in one call")
+    out, gst = _gdn_run(rt, cfg, layer, st, x)
+    assert np.isfinite(out).all() and np.isfinite(gst["gdn_state"]).all()
+    say(f"prefill GDN 4B T={BIG_T} as two calls of {BIG_T // 2}")
+    o1, s1 = _gdn_run(rt, cfg, layer, st, x[:BIG_T // 2])
+    o2, s2 = _gdn_run(rt, cfg, layer, s1, x[BIG_T // 2:])
+    r_out, same_out = _split_rel(np.concatenate([o1, o2]), out)
+    r_st, same_st = _split_rel(s2["gdn_state"], gst["gdn_state"])
+    say(f"  split against one call: outputs rel {r_out:.1e} (bit-identical {same_out}), "
+        f"state rel {r_st:.1e} (bit-identical {same_st})")
+    assert r_out < SPLIT_BF16 and r_st < SPLIT_F32
+    assert rel(s2["conv1d_state"], gst["conv1d_state"]) < SPLIT_F32
+    ref, _, _ = O.prefill.prefill_linear_attention(cfg, layer, st, x[:PREFIX])
+    assert _rows_rel(out[:PREFIX], ref) < TOL_BF16
+
+
+def test_prefill_full_4b_4096_tokens(rt, gen):
+    """The benchmark's prompt through one 4B full-attention layer from an empty cache
+    of exactly 4096 rows (128 query tiles, up to 64 key tiles per tile): the first
+    300 outputs and cache rows against the oracle's loop over those tokens; all 4096
+    outputs and the whole cache against two calls of 2048 tokens, the second at
+    cache position 2048 (SPLIT_*)."""
+    cfg = synth.qwen3_5_4b("bf16")
+    layer = synth.full_layer(gen, cfg, "pf.big.f")
+    kv = synth.kv_cache(gen, cfg, "pf.big.f", BIG_T, 0)
+    x = gen.act("pf.big.f.x", (BIG_T, cfg.hidden), "bf16")
+    say(f"prefill full 4B T={BIG_T} in one call")
+    out, after = _full_run(rt, cfg, layer, kv, x, 0)
+    assert np.isfinite(out).all()
+    say(f"prefill full 4B T={BIG_T} as two calls of {BIG_T // 2}")
+    o1, kv1 = _full_run(rt, cfg, layer, kv, x[:BIG_T // 2], 0)
+    kv_mid = dict(kv)
+    kv_mid.update(kv1)
+    o2, kv2 = _full_run(rt, cfg, layer, kv_mid, x[BIG_T // 2:], BIG_T // 2)
+    r_out, same_out = _split_rel(np.concatenate([o1, o2]), out)
+    say(f"  split against one call: outputs rel {r_out:.1e} (bit-identical {same_out})")
+    assert r_out < SPLIT_BF16
+    for s in ("k", "v"):
+        r_kv, same_kv = _split_rel(O.bf16_to_f64(kv2[s]).reshape(BIG_T, -1),
+                                   O.bf16_to_f64(after[s]).reshape(BIG_T, -1))
+        say(f"  cache {s}: rel {r_kv:.1e} (bit-identical {same_kv})")
+        assert r_kv < SPLIT_BF16, s
+    inv = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
+    ref, rkv, _ = O.prefill.prefill_full_attention(cfg, layer, kv, inv, x[:PREFIX], 0)
+    assert _rows_rel(out[:PREFIX], ref) < TOL_BF16
+    for s in ("k", "v"):
+        g = O.bf16_to_f64(after[s][:PREFIX])
+        r = O.bf16_to_f64(rkv[s][:PREFIX])
+        assert rel(g, r) < 4e-3, s
