@@ -50,19 +50,18 @@ Q35_DEV uint32_t bf2_to_h2(uint32_t w) { return pack_h2(bf16_lo(w), bf16_hi(w));
 // ====================================================================== GEMM
 //
 // out[m, n] = sum_k x[m, k] * W[n, k], W[n, k] = s[n, k/64] * code[n, k] + b[n, k/64]
-// (weights dequantised in fp32, rounded once to f16).  Block tile BM (rows of x:
-// 256 as launched, 128 also built) x 128 (rows of W) x 64 (one quantisation
-// group); 2 BM threads in waves of 64 x 64 as 2 x 2 MFMA tiles, so each
-// dequantised weight serves BM rows.  k tiles pass through two register stages
+// (weights dequantised in fp32, rounded once to f16).  Block tile 256 (rows of
+// x) x 128 (rows of W) x 64 (one quantisation group); 512 threads in waves of
+// 64 x 64 as 2 x 2 MFMA tiles, so each dequantised weight serves 256 rows.  k tiles pass through two register stages
 // and two LDS buffers: a tile's loads are waited for only where it is written
 // to LDS, a k step after they were issued.  SwiGLU mode: the 128 W rows are 64
 // gate rows and the same 64 up rows; a wave holds a gate tile and its up tile,
 // so the epilogue is elementwise in registers.
 //
 // Wave quantisation.  A launch of n tiles on C compute units (one block each)
-// runs ceil(n / C) rounds; when the last round would be less than half full, its
-// tiles are cut into `split` ranges of k tiles, one block each, so that round
-// takes 1/split of the time.  Those blocks leave fp32 partial tiles in a
+// runs ceil(n / C) rounds; when the last round would be at most a quarter full,
+// its tiles are cut into `split` ranges of k tiles, one block each, so that
+// round takes about 1/split of the time.  Those blocks leave fp32 partial tiles in a
 // workspace and gemm_reduce_kernel adds the parts in order and applies the
 // epilogue.
 
@@ -84,10 +83,12 @@ Q35_DEV void tile_of(uint32_t t, uint32_t n_mt, uint32_t n_nt, uint32_t& mt, uin
     }
 }
 
-// BM rows of x per block (128 or 256), 2 BM threads: waves of 64 x 64.
+// BM = 256 rows of x per block, 512 threads: waves of 64 x 64; each thread stages
+// one 16-code chunk of W per k tile.
 template <int MODE, int BM>
-__global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_kernel(PfGemmArgs a) {
-    constexpr int kBM = BM, kGemmThreads = 2 * BM, WPT = 512 / kGemmThreads;  // W chunks per thread
+__global__ __launch_bounds__(2 * BM, 1) void gemm_kernel(PfGemmArgs a) {
+    static_assert(BM == 256, "one W chunk per thread per k tile");
+    constexpr int kBM = BM, kGemmThreads = 2 * BM;
     __shared__ __align__(16) _Float16 xs[2][kBM * kRow];
     __shared__ __align__(16) _Float16 ws[2][kBN * kRow];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -106,28 +107,29 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_kernel(PfGemmArgs a) {
     const uint32_t k_lo = whole ? 0 : (pb % a.split) * nk_all / a.split;
     const uint32_t nk = whole ? nk_all : (pb % a.split + 1) * nk_all / a.split - k_lo;
 
-    // global -> register staging of one k tile (two stages in flight)
+    // global -> register staging of one k tile (two stages in flight).  Named
+    // members, not arrays: a staged array may be moved to LDS by the compiler,
+    // which then waits for every load where it is issued.
     struct Stage {
-        uint4 xr[4];
-        uint4 wr[WPT];
-        uint32_t sc[WPT], bi[WPT];  // raw bf16 bits
+        uint4 x0, x1, x2, x3;  // four x chunks
+        uint4 w;               // sixteen weight codes
+        uint32_t sc, bi;       // raw bf16 bits
     };
     // This thread's W row (fixed for the whole k loop): rows 64..127 of a SwiGLU
     // tile are the up rows of n0..n0+63; otherwise the row's segment picks the
     // matrix.  A row past the last one reads row 0 of the first matrix (always
     // present) and is masked to zero at the stash.
-    const uint8_t* wrow_p[WPT];
-    const uint16_t* srow_p[WPT];
-    const uint16_t* brow_p[WPT];
-    uint32_t wmsk[WPT];
-#pragma unroll
-    for (int wi = 0; wi < WPT; ++wi) {
-        const int c = tid + kGemmThreads * wi, row = c >> 2, col = (c & 3) * 16;
-        const uint32_t gn = n0 + row;
+    const int wrow_t = tid >> 2, wcol_t = (tid & 3) * 16;
+    const uint8_t* wrow_p;
+    const uint16_t* srow_p;
+    const uint16_t* brow_p;
+    uint32_t wmsk;
+    {
+        const uint32_t gn = n0 + wrow_t;
         uint32_t q = 0, n = gn;
         if constexpr (MODE == kPfSwiglu) {
-            q = row >= kBN / 2 ? 1 : 0;
-            n = n0 + (q ? row - kBN / 2 : row);
+            q = wrow_t >= kBN / 2 ? 1 : 0;
+            n = n0 + (q ? wrow_t - kBN / 2 : wrow_t);
         } else if constexpr (MODE == kPfF32) {
             q = (gn >= a.seg_end[0]) + (gn >= a.seg_end[1]) + (gn >= a.seg_end[2]);
             n = gn - (q == 0 ? 0 : q == 1 ? a.seg_end[0] : q == 2 ? a.seg_end[1] : a.seg_end[2]);
@@ -135,49 +137,61 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_kernel(PfGemmArgs a) {
         const bool live = (MODE == kPfSwiglu ? n : gn) < a.N;
         if (!live) q = 0;
         const size_t nn = live ? n : 0;
-        wrow_p[wi] = (q == 0 ? a.w[0] : q == 1 ? a.w[1] : q == 2 ? a.w[2] : a.w[3]) + nn * a.K + col;
-        srow_p[wi] = (q == 0 ? a.s[0] : q == 1 ? a.s[1] : q == 2 ? a.s[2] : a.s[3]) + nn * ng;
-        brow_p[wi] = (q == 0 ? a.b[0] : q == 1 ? a.b[1] : q == 2 ? a.b[2] : a.b[3]) + nn * ng;
-        wmsk[wi] = live ? 0xFFFFFFFFu : 0u;
+        wrow_p = (q == 0 ? a.w[0] : q == 1 ? a.w[1] : q == 2 ? a.w[2] : a.w[3]) + nn * a.K + wcol_t;
+        srow_p = (q == 0 ? a.s[0] : q == 1 ? a.s[1] : q == 2 ? a.s[2] : a.s[3]) + nn * ng;
+        brow_p = (q == 0 ? a.b[0] : q == 1 ? a.b[1] : q == 2 ? a.b[2] : a.b[3]) + nn * ng;
+        wmsk = live ? 0xFFFFFFFFu : 0u;
+    }
+    // x rows past the last one repeat it: they feed only output rows that are never
+    // stored, and loads without a condition keep the compiler's wait counts exact
+    const uint16_t* xrow_p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = tid + kGemmThreads * i;
+        xrow_p[i] = a.x + (size_t)min(m0 + (c >> 3), a.M - 1) * a.K + (c & 7) * 8;
     }
     auto load = [&](Stage& g, uint32_t kt) {
         kt += k_lo;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + kGemmThreads * i, row = c >> 3, col = (c & 7) * 8;
-            const uint32_t m = m0 + row;
-            g.xr[i] = m < a.M ? *reinterpret_cast<const uint4*>(a.x + (size_t)m * a.K + kt * kBK + col)
-                              : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int wi = 0; wi < WPT; ++wi) {
-            g.wr[wi] = *reinterpret_cast<const uint4*>(wrow_p[wi] + kt * kBK);
-            g.sc[wi] = srow_p[wi][kt];
-            g.bi[wi] = brow_p[wi][kt];
-        }
+        const uint32_t ko = kt * kBK;
+        g.x0 = *reinterpret_cast<const uint4*>(xrow_p[0] + ko);
+        g.x1 = *reinterpret_cast<const uint4*>(xrow_p[1] + ko);
+        g.x2 = *reinterpret_cast<const uint4*>(xrow_p[2] + ko);
+        g.x3 = *reinterpret_cast<const uint4*>(xrow_p[3] + ko);
+        g.w = *reinterpret_cast<const uint4*>(wrow_p + ko);
+        g.sc = srow_p[kt];
+        g.bi = brow_p[kt];
     };
     // part q (0..3) of moving a staged tile into LDS: one x chunk, and four weights
     // dequantised (fp32 fma, one f16 rounding); spread over the MFMA steps
-    auto stash_part = [&](const Stage& g, int buf, int q) {
+    // (q is a compile-time constant throughout, so every member is picked statically)
+    auto stash_part = [&](const Stage& g, int buf, auto q_c) {
+        constexpr int q = decltype(q_c)::value;
+        uint4 xv;
+        uint32_t v;
+        if constexpr (q == 0) xv = g.x0, v = g.w.x;
+        if constexpr (q == 1) xv = g.x1, v = g.w.y;
+        if constexpr (q == 2) xv = g.x2, v = g.w.z;
+        if constexpr (q == 3) xv = g.x3, v = g.w.w;
         {
             const int c = tid + kGemmThreads * q, row = c >> 3, col = (c & 7) * 8;
-            *reinterpret_cast<uint4*>(&xs[buf][row * kRow + col]) = g.xr[q];
+            *reinterpret_cast<uint4*>(&xs[buf][row * kRow + col]) = xv;
         }
-#pragma unroll
-        for (int wi = 0; wi < WPT; ++wi) {
-            const int c = tid + kGemmThreads * wi, row = c >> 2, col = (c & 3) * 16;
-            const uint4 wr = g.wr[wi];
-            const uint32_t v = (q == 0 ? wr.x : q == 1 ? wr.y : q == 2 ? wr.z : wr.w) & wmsk[wi];
-            const float sc = __uint_as_float((g.sc[wi] << 16) & wmsk[wi]);
-            const float bi = __uint_as_float((g.bi[wi] << 16) & wmsk[wi]);
-            *reinterpret_cast<uint2*>(&ws[buf][row * kRow + col + 4 * q]) =
-                make_uint2(pack_h2(fmaf(sc, (float)(v & 0xFFu), bi), fmaf(sc, (float)((v >> 8) & 0xFFu), bi)),
-                           pack_h2(fmaf(sc, (float)((v >> 16) & 0xFFu), bi), fmaf(sc, (float)(v >> 24), bi)));
-        }
+        v &= wmsk;
+        const float sc = __uint_as_float((g.sc << 16) & wmsk);
+        const float bi = __uint_as_float((g.bi << 16) & wmsk);
+        *reinterpret_cast<uint2*>(&ws[buf][wrow_t * kRow + wcol_t + 4 * q]) =
+            make_uint2(pack_h2(fmaf(sc, (float)(v & 0xFFu), bi), fmaf(sc, (float)((v >> 8) & 0xFFu), bi)),
+                       pack_h2(fmaf(sc, (float)((v >> 16) & 0xFFu), bi), fmaf(sc, (float)(v >> 24), bi)));
     };
+    using c0 = std::integral_constant<int, 0>;
+    using c1 = std::integral_constant<int, 1>;
+    using c2 = std::integral_constant<int, 2>;
+    using c3 = std::integral_constant<int, 3>;
     auto stash = [&](const Stage& g, int buf) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) stash_part(g, buf, q);
+        stash_part(g, buf, c0{});
+        stash_part(g, buf, c1{});
+        stash_part(g, buf, c2{});
+        stash_part(g, buf, c3{});
     };
 
     f32x16 acc[2][2];
@@ -198,11 +212,9 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_kernel(PfGemmArgs a) {
     // MFMAs on LDS buffer CUR; with do_stash, the stash of the stage that feeds the
     // other buffer is interleaved, a quarter per k step
     Stage g0, g1;
-    auto compute = [&](auto cur_c, bool do_stash) {
-        constexpr int cur = decltype(cur_c)::value;
-        const Stage& nxt = cur == 0 ? g1 : g0;
-#pragma unroll
-        for (int ks = 0; ks < kBK / 16; ++ks) {
+    auto kstep = [&](auto cur_c, auto ks_c, bool do_stash) {
+        constexpr int cur = decltype(cur_c)::value, ks = decltype(ks_c)::value;
+        {
             half8 av[2], bv[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -216,25 +228,39 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void gemm_kernel(PfGemmArgs a) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
-            if (do_stash) stash_part(nxt, cur ^ 1, ks);
+            if (do_stash) {
+                if constexpr (cur == 0) stash_part(g1, 1, ks_c);
+                else stash_part(g0, 0, ks_c);
+            }
         }
+    };
+    auto compute = [&](auto cur_c, bool do_stash) {
+        kstep(cur_c, c0{}, do_stash);
+        kstep(cur_c, c1{}, do_stash);
+        kstep(cur_c, c2{}, do_stash);
+        kstep(cur_c, c3{}, do_stash);
     };
 
     // k tile kt sits in LDS buffer kt % 2 while tile kt + 1 waits in registers and
-    // tile kt + 2 is being fetched
+    // tile kt + 2 is being fetched.  Loads past the last tile repeat it (in bounds,
+    // never stashed), so every iteration issues the same loads; an odd last tile
+    // runs after the loop.
+    const c0 lds0;
+    const c1 lds1;
     load(g0, 0);
-    if (nk > 1) load(g1, 1);
+    load(g1, min(1u, nk - 1));
     stash(g0, 0);
     __syncthreads();
-    for (uint32_t kt = 0; kt < nk; kt += 2) {
-        if (kt + 2 < nk) load(g0, kt + 2);
-        compute(std::integral_constant<int, 0>{}, kt + 1 < nk);
+    uint32_t kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        load(g0, min(kt + 2, nk - 1));
+        compute(lds0, true);
         __syncthreads();
-        if (kt + 1 >= nk) break;
-        if (kt + 3 < nk) load(g1, kt + 3);
-        compute(std::integral_constant<int, 1>{}, kt + 2 < nk);
+        load(g1, min(kt + 3, nk - 1));
+        compute(lds1, kt + 2 < nk);
         __syncthreads();
     }
+    if (kt < nk) compute(lds0, false);
 
     // epilogue: acc[i][j][r] is (row 8 (r/4) + 4 (lane/32) + r%4, column lane%32) of its tile
     if (!whole) {
@@ -1000,9 +1026,6 @@ __global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
 
 const void* pf_kernel_ptr(int i) {
     static const void* const k[] = {
-        reinterpret_cast<const void*>(pf::gemm_kernel<kPfF32, 128>),
-        reinterpret_cast<const void*>(pf::gemm_kernel<kPfResid, 128>),
-        reinterpret_cast<const void*>(pf::gemm_kernel<kPfSwiglu, 128>),
         reinterpret_cast<const void*>(pf::gemm_kernel<kPfF32, 256>),
         reinterpret_cast<const void*>(pf::gemm_kernel<kPfResid, 256>),
         reinterpret_cast<const void*>(pf::gemm_kernel<kPfSwiglu, 256>),
@@ -1027,8 +1050,10 @@ const void* pf_kernel_ptr(int i) {
 }
 
 // The split plan: with n tiles on num_cu compute units (one block each), a last
-// round of t = n % num_cu tiles with 2 t <= min(num_cu, kPfSplitBlocks) is cut
-// into split = min(that / t, 8, k tiles) ranges of k tiles.
+// round of t = n % num_cu tiles with 4 t <= min(num_cu, kPfSplitBlocks) is cut
+// into split = min(that / t, 8, k tiles) ranges of k tiles.  (A last round over
+// a quarter full was measured faster whole: its tiles run faster than a full
+// round's, and the parts add partial-tile traffic and a second kernel.)
 template <int BM>
 static void gemm_plan(PfGemmArgs& a, uint32_t bn, uint32_t num_cu) {
     const uint32_t n_tiles = ((a.N + bn - 1) / bn) * ((a.M + BM - 1) / BM);
@@ -1036,7 +1061,7 @@ static void gemm_plan(PfGemmArgs& a, uint32_t bn, uint32_t num_cu) {
     a.split = 1;
     if (!a.part || num_cu == 0) return;
     const uint32_t slots = num_cu < kPfSplitBlocks ? num_cu : kPfSplitBlocks, tail = n_tiles % num_cu;
-    if (tail == 0 || 2 * tail > slots) return;
+    if (tail == 0 || 4 * tail > slots) return;
     uint32_t split = slots / tail;
     if (split > 8) split = 8;
     if (split > a.K / pf::kBK) split = a.K / pf::kBK;

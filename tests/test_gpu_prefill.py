@@ -61,8 +61,9 @@ def _gemm(rt, wq, x, m, n, split):
 @pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("m,n,k", [(1, 64, 64), (77, 200, 256), (300, 384, 640), (129, 2560, 2560)])
 def test_prefill_gemm_matches_float64_on_the_same_f16_operands(rt, gen, m, n, k, split):
-    """With the workspace, every shape but the first (one k tile) has fewer tiles
-    than half the compute units, so all its tiles run as 4 or 8 k ranges."""
+    """With the workspace, every shape but the first (one k tile) has at most a
+    quarter as many tiles as compute units, so all its tiles run as 4 or 8 k
+    ranges."""
     say(f"prefill GEMM m={m} n={n} k={k} split={split}")
     w = gen.quant(f"pf.gemm.{m}.{n}.{k}", n, k)
     x = gen.normal_f32(f"pf.gemm.x.{m}.{k}", (m, k)).astype(np.float16)
@@ -74,16 +75,18 @@ def test_prefill_gemm_matches_float64_on_the_same_f16_operands(rt, gen, m, n, k,
     assert _rows_rel(got, ref) < 1e-4
 
 
-def test_prefill_gemm_4096_rows_at_the_gate_proj_shape(rt, gen):
-    """The GEMM the benchmark times (4096 x 9216 x 2560: 1152 tiles, four whole
-    rounds on 256 compute units and a half round cut in two along k).  Sampled rows
-    in every row tile and on the tile edges against float64 on the same f16
-    operands; the whole output against the launch without a workspace (no split),
-    which differs by fp32 rounding only."""
-    m, n, k = 4096, 9216, 2560
+@pytest.mark.parametrize("n,k", [(9216, 2560), (2560, 9216)])
+def test_prefill_gemm_4096_rows_at_the_4b_shapes(rt, gen, n, k):
+    """The GEMMs of a 4096-token prompt: gate_proj's shape (the benchmark's; 1152
+    tiles, a half-full last round on 256 compute units, run whole) and down_proj's
+    (320 tiles: the quarter-full last round is cut in four along k).  Sampled
+    rows in every row tile and on the tile edges against float64 on the same f16
+    operands; the whole output against the launch without a workspace (never
+    split), which differs by fp32 rounding only."""
+    m = 4096
     say(f"prefill GEMM m={m} n={n} k={k}")
-    w = gen.quant("pf.gemm.big", n, k)
-    x = (0.5 * gen.normal_f32("pf.gemm.big.x", (m, k))).astype(np.float16)
+    w = gen.quant(f"pf.gemm.big.{n}", n, k)
+    x = (0.5 * gen.normal_f32(f"pf.gemm.big.x{k}", (m, k))).astype(np.float16)
     wq = rt.QuantWeightDev(w)
     got = _gemm(rt, wq, x, m, n, True)
     plain = _gemm(rt, wq, x, m, n, False)
