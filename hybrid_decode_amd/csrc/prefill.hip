@@ -455,16 +455,21 @@ __global__ __launch_bounds__(256) void gdn_conv_state_kernel(const float* qkv, f
 
 constexpr int kC = 64;
 
+// LDS holds at most 67 KB (DK = DV = 128), so two blocks share a CU: the Gram
+// products stream k and q through LDS in two halves of the head dimension, the
+// forward substitution reuses that space for its solved rows, A is kept once
+// (transposed), and the K columns of the right-hand side are read from memory.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void gdn_chunk_kernel(PfGdnArgs a) {
-    static_assert(DK + DV <= 256 && DK % 4 == 0, "chunk kernel: one thread per column of [V | K]");
-    constexpr int KR = DK + 4;
-    __shared__ __align__(16) float ks[kC * KR];
-    __shared__ __align__(16) float qs[kC * KR];
-    __shared__ __align__(16) float am[kC * 68];   // A, row-major
-    __shared__ __align__(16) float at[kC * 68];   // A, transposed
-    __shared__ float xsol[(kC - 16) * (DK + DV)];  // solved rows of the first three blocks
+    static_assert(DK + DV <= 256 && DK % 8 == 0, "chunk kernel: one thread per column of [V | K]");
+    constexpr int DH = DK / 2, KR = DH + 4;
+    constexpr int kGram = 2 * kC * KR, kSol = (kC - 16) * (DK + DV);
+    __shared__ __align__(16) float lds[kGram > kSol ? kGram : kSol];
+    __shared__ __align__(16) float at[kC * 68];   // A, transposed: at[s][r] = A[r][s]
     __shared__ float L[kC], bt[kC];
+    float* ks = lds;                 // Gram phase: half of k and q per pass
+    float* qs = lds + kC * KR;
+    float* xsol = lds;               // substitution: solved rows of the first three blocks
     const int tid = threadIdx.x;
     const uint32_t ch = blockIdx.x, j = blockIdx.y, nch = gridDim.x;
     const uint32_t i = j / (a.hv / a.hk);
@@ -472,17 +477,6 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(PfGdnArgs a) {
     const int n = (int)min((uint32_t)kC, a.T - t0);
     const uint32_t qoff = i * DK, koff = a.hk * DK + i * DK, voff = 2 * a.hk * DK + j * DV;
 
-    for (int c = tid; c < kC * DK / 4; c += 256) {
-        const int r = c / (DK / 4), d = (c % (DK / 4)) * 4;
-        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
-        if (r < n) {
-            const float* src = a.qkvs + (size_t)(t0 + r) * a.C;
-            kv = *reinterpret_cast<const float4*>(src + koff + d);
-            qv = *reinterpret_cast<const float4*>(src + qoff + d);
-        }
-        *reinterpret_cast<float4*>(&ks[r * KR + d]) = kv;
-        *reinterpret_cast<float4*>(&qs[r * KR + d]) = qv;
-    }
     if (tid < 64) {
         float lg = tid < n ? a.lg[(size_t)(t0 + tid) * a.hv + j] : 0.f;
         bt[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * a.hv + j] : 0.f;
@@ -493,29 +487,43 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(PfGdnArgs a) {
         }
         L[tid] = lg;
     }
-    __syncthreads();
 
     // Gram blocks: thread (rb, sb) -> rows 4 rb.., columns 4 sb..
     {
         const int rb = tid >> 4, sb = tid & 15;
         float kk[4][4] = {}, qk[4][4] = {};
-        for (int d = 0; d < DK; d += 4) {
-            float4 kr[4], qr[4], kc[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                kr[u] = *reinterpret_cast<const float4*>(&ks[(4 * rb + u) * KR + d]);
-                qr[u] = *reinterpret_cast<const float4*>(&qs[(4 * rb + u) * KR + d]);
-                kc[u] = *reinterpret_cast<const float4*>(&ks[(4 * sb + u) * KR + d]);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    kk[u][v] = fmaf(kr[u].x, kc[v].x, fmaf(kr[u].y, kc[v].y,
-                               fmaf(kr[u].z, kc[v].z, fmaf(kr[u].w, kc[v].w, kk[u][v]))));
-                    qk[u][v] = fmaf(qr[u].x, kc[v].x, fmaf(qr[u].y, kc[v].y,
-                               fmaf(qr[u].z, kc[v].z, fmaf(qr[u].w, kc[v].w, qk[u][v]))));
+        for (int h = 0; h < 2; ++h) {
+            for (int c = tid; c < kC * DH / 4; c += 256) {
+                const int r = c / (DH / 4), d = (c % (DH / 4)) * 4;
+                float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
+                if (r < n) {
+                    const float* src = a.qkvs + (size_t)(t0 + r) * a.C + h * DH;
+                    kv = *reinterpret_cast<const float4*>(src + koff + d);
+                    qv = *reinterpret_cast<const float4*>(src + qoff + d);
                 }
+                *reinterpret_cast<float4*>(&ks[r * KR + d]) = kv;
+                *reinterpret_cast<float4*>(&qs[r * KR + d]) = qv;
+            }
+            __syncthreads();
+            for (int d = 0; d < DH; d += 4) {
+                float4 kr[4], qr[4], kc[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    kr[u] = *reinterpret_cast<const float4*>(&ks[(4 * rb + u) * KR + d]);
+                    qr[u] = *reinterpret_cast<const float4*>(&qs[(4 * rb + u) * KR + d]);
+                    kc[u] = *reinterpret_cast<const float4*>(&ks[(4 * sb + u) * KR + d]);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        kk[u][v] = fmaf(kr[u].x, kc[v].x, fmaf(kr[u].y, kc[v].y,
+                                   fmaf(kr[u].z, kc[v].z, fmaf(kr[u].w, kc[v].w, kk[u][v]))));
+                        qk[u][v] = fmaf(qr[u].x, kc[v].x, fmaf(qr[u].y, kc[v].y,
+                                   fmaf(qr[u].z, kc[v].z, fmaf(qr[u].w, kc[v].w, qk[u][v]))));
+                    }
+            }
+            __syncthreads();
         }
         float* P = a.Pc + ((size_t)j * nch + ch) * kC * kC;
         float av[4][4];
@@ -530,8 +538,6 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(PfGdnArgs a) {
                 av[u][v] = s < r ? bt[r] * e * kk[u][v] : 0.f;
                 pv[v] = e * qk[u][v];
             }
-            *reinterpret_cast<float4*>(&am[r * 68 + 4 * sb]) =
-                make_float4(av[u][0], av[u][1], av[u][2], av[u][3]);
             *reinterpret_cast<float4*>(&P[r * kC + 4 * sb]) = make_float4(pv[0], pv[1], pv[2], pv[3]);
         }
 #pragma unroll
@@ -550,13 +556,14 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(PfGdnArgs a) {
         const size_t blk = (size_t)j * nch + ch;
         float* out = c < DV ? a.Uc + blk * kC * DV + c : a.Wc + blk * kC * DK + (c - DV);
         const int ld = c < DV ? DV : DK;
+        const uint32_t col = c < DV ? voff + c : koff + (c - DV);
         for (int rb = 0; rb < kC; rb += 16) {
             float x[16];
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 const int r = rb + u;
-                x[u] = c < DV ? (r < n ? bt[r] * a.qkvs[(size_t)(t0 + r) * a.C + voff + c] : 0.f)
-                              : bt[r] * expf(L[r]) * ks[r * KR + (c - DV)];
+                const float rhs = r < n ? a.qkvs[(size_t)(t0 + r) * a.C + col] : 0.f;
+                x[u] = c < DV ? bt[r] * rhs : bt[r] * expf(L[r]) * rhs;
             }
             for (int s = 0; s < rb; ++s) {
                 const float xv = xsol[s * (DK + DV) + c];
@@ -573,7 +580,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(PfGdnArgs a) {
 #pragma unroll
             for (int u = 1; u < 16; ++u)
 #pragma unroll
-                for (int v = 0; v < u; ++v) x[u] = fmaf(-am[(rb + u) * 68 + rb + v], x[v], x[u]);
+                for (int v = 0; v < u; ++v) x[u] = fmaf(-at[(rb + v) * 68 + rb + u], x[v], x[u]);
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 out[(size_t)(rb + u) * ld] = x[u];
