@@ -52,17 +52,18 @@ Q35_DEV uint32_t bf2_to_h2(uint32_t w) { return pack_h2(bf16_lo(w), bf16_hi(w));
 // out[m, n] = sum_k x[m, k] * W[n, k], W[n, k] = s[n, k/64] * code[n, k] + b[n, k/64]
 // (weights dequantised in fp32, rounded once to f16).  Block tile 256 (rows of
 // x) x 128 (rows of W) x 64 (one quantisation group); 512 threads in waves of
-// 64 x 64 as 2 x 2 MFMA tiles, so each dequantised weight serves 256 rows.  k tiles pass through two register stages
-// and two LDS buffers: a tile's loads are waited for only where it is written
-// to LDS, a k step after they were issued.  SwiGLU mode: the 128 W rows are 64
-// gate rows and the same 64 up rows; a wave holds a gate tile and its up tile,
-// so the epilogue is elementwise in registers.
+// 64 x 64 as 2 x 2 MFMA tiles, so each dequantised weight serves 256 rows.  k
+// tiles pass through two register stages and two LDS buffers: a tile's loads
+// are waited for only where it is written to LDS, a k step after they were
+// issued.  SwiGLU mode: the 128 W rows are 64 gate rows and the same 64 up
+// rows; a wave holds a gate tile and its up tile, so the epilogue is
+// elementwise in registers.
 //
 // Wave quantisation.  A launch of n tiles on C compute units (one block each)
 // runs ceil(n / C) rounds; when the last round would be at most a quarter full,
 // its tiles are cut into `split` ranges of k tiles, one block each, so that
-// round takes about 1/split of the time.  Those blocks leave fp32 partial tiles in a
-// workspace and gemm_reduce_kernel adds the parts in order and applies the
+// round takes about 1/split of the time.  Those blocks leave fp32 partial tiles
+// in a workspace and gemm_reduce_kernel adds the parts in order and applies the
 // epilogue.
 
 constexpr int kBN = 128, kBK = 64, kRow = kBK + 8;  // LDS row: 144 bytes
