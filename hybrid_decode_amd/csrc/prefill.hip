@@ -841,16 +841,24 @@ __global__ __launch_bounds__(256) void qk_rope_append_kernel(PfRopeArgs a) {
 // f16 on the matrix cores with fp32 sums.  S^T = K Q^T puts one query per lane:
 // the softmax statistics are per lane (plus the partner lane l ^ 32), and the
 // probabilities in registers are already the B operand of O^T += V^T P^T.
-// Output: f16(attention * sigmoid(gate)).
+// Output: f16(attention * sigmoid(gate)).  With D = 256 (and G <= 4) two waves
+// share a query head, each computing the scores (the same in both) and half of the output
+// columns: eight 32 x 32 accumulators per lane left too few registers for the
+// next key tile's loads to stay in flight.
 constexpr int kKT = 64;  // keys per tile
 
 template <int D, int G>
-__global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
-    constexpr int NT = 64 * G, KRW = D + 8, VRW = kKT + 4, DT = D / 32;
+constexpr int flash_wph() { return D == 256 && G <= 4 ? 2 : 1; }  // waves per query head
+
+template <int D, int G>
+__global__ __launch_bounds__((64 * G * flash_wph<D, G>())) void flash_kernel(PfAttnArgs a) {
+    constexpr int WPH = flash_wph<D, G>(), NT = 64 * G * WPH, KRW = D + 8, VRW = kKT + 4, DT = D / 32;
+    constexpr int DTW = DT / WPH;  // output column tiles of this wave
     __shared__ __align__(16) uint16_t kt_s[kKT * KRW];
     __shared__ __align__(16) uint16_t vt_s[D * VRW];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, h2 = lane >> 5;
-    const uint32_t g = blockIdx.y, h = g * G + wid;
+    const int half = wid % WPH;  // this wave's output columns: tiles half * DTW ..
+    const uint32_t g = blockIdx.y, h = g * G + wid / WPH;
     const uint32_t t0 = (gridDim.x - 1 - blockIdx.x) * 32;  // longest blocks first
     const uint32_t tq = t0 + (lane & 31);
     const uint32_t kend = a.cache_pos + min(t0 + 32, a.T);  // rows any query here may read
@@ -864,9 +872,9 @@ __global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
             w = *reinterpret_cast<const uint4*>(a.qb + ((size_t)tq * a.hq + h) * D + ks * 16 + 8 * h2);
         qv[ks] = __builtin_bit_cast(half8, w);
     }
-    f32x16 o[DT];
+    f32x16 o[DTW];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DTW; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
     float m = -INFINITY, l = 0.f;
@@ -874,26 +882,29 @@ __global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
     constexpr int KL = (kKT * D / 8 + NT - 1) / NT;          // K: 16-byte chunks per thread
     constexpr int VTASK = kKT / 4 * (D / 8);                  // V: (key quad, column octet) tasks
     constexpr int VL = (VTASK + NT - 1) / NT;
+    // Loads without a condition keep the compiler's wait counts exact, so tile
+    // kt + 1 stays in flight while tile kt is used: rows past kend (in the last
+    // tile only) repeat row kend - 1, finite values that the causal mask removes
+    // (keys past every query of the block) and that meet zero probabilities in
+    // P V; a thread whose chunk index is past the tile's loads a repeat of an
+    // earlier chunk and does not store it.
     uint4 kr[KL], vr[VL][4];
     auto gload = [&](uint32_t k0) {
 #pragma unroll
         for (int i = 0; i < KL; ++i) {
-            const int c = tid + NT * i, row = c / (D / 8), col = (c % (D / 8)) * 8;
-            kr[i] = (c < kKT * D / 8 && k0 + row < kend)
-                        ? *reinterpret_cast<const uint4*>(a.kc + (k0 + row) * rs + g * D + col)
-                        : make_uint4(0, 0, 0, 0);
+            const int c = (tid + NT * i) % (kKT * D / 8), row = c / (D / 8), col = (c % (D / 8)) * 8;
+            const uint32_t key = min(k0 + row, kend - 1);
+            kr[i] = *reinterpret_cast<const uint4*>(a.kc + key * rs + g * D + col);
         }
 #pragma unroll
         for (int i = 0; i < VL; ++i) {
             // key quads vary fastest across lanes: the transposed LDS writes of a wave
             // then fall on distinct banks but for one 2-way overlap
-            const int c = tid + NT * i, q4 = c % (kKT / 4), b = c / (kKT / 4);
+            const int c = (tid + NT * i) % VTASK, q4 = c % (kKT / 4), b = c / (kKT / 4);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const uint32_t key = k0 + 4 * q4 + u;
-                vr[i][u] = (c < VTASK && key < kend)
-                               ? *reinterpret_cast<const uint4*>(a.vc + key * rs + g * D + 8 * b)
-                               : make_uint4(0, 0, 0, 0);
+                const uint32_t key = min(k0 + 4 * q4 + u, kend - 1);
+                vr[i][u] = *reinterpret_cast<const uint4*>(a.vc + key * rs + g * D + 8 * b);
             }
         }
     };
@@ -929,7 +940,7 @@ __global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
         const uint32_t k0 = kt * kKT;
         lstore();
         __syncthreads();
-        if (kt + 1 < nkt) gload(k0 + kKT);
+        gload(min(k0 + kKT, (nkt - 1) * kKT));  // past the last tile: repeats it, unused
 
         // S^T for two 32-key halves: s[hf][r] is key k0 + 32 hf + 8 (r/4) + 4 h2 + r%4, query tq
         // (the two halves' MFMA chains interleave, so no MFMA waits on the previous one)
@@ -979,7 +990,7 @@ __global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
             m = mn;
             l *= al;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DTW; ++dt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[dt][r] *= al;
         }
@@ -998,9 +1009,10 @@ __global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
+            for (int dt = 0; dt < DTW; ++dt) {
                 // keys 16 kk + 4 h2 + 0..3 and 16 kk + 8 + 4 h2 + 0..3, the order of pb[kk]
-                const uint16_t* vrow = &vt_s[(32 * dt + (lane & 31)) * VRW + 4 * h2 + 16 * kk];
+                const int dg = half * DTW + dt;
+                const uint16_t* vrow = &vt_s[(32 * dg + (lane & 31)) * VRW + 4 * h2 + 16 * kk];
                 const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
                 const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
                 const half8 vv = __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -1014,10 +1026,10 @@ __global__ __launch_bounds__(64 * G) void flash_kernel(PfAttnArgs a) {
     const float* gate = a.q_full + (size_t)tq * a.hq * 2 * D + (size_t)h * 2 * D + D;
     uint16_t* out = a.ga + ((size_t)tq * a.hq + h) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DTW; ++dt)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-            const int d = 32 * dt + 8 * r4 + 4 * h2;
+            const int d = 32 * (half * DTW + dt) + 8 * r4 + 4 * h2;
             float v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -1155,7 +1167,7 @@ hipError_t pf_attn_launch(const PfRopeArgs& r, const PfAttnArgs& a, hipStream_t 
     dim3 grid((a.T + 31) / 32, a.hkv);
 #define Q35_PF_FLASH(DD, GG)                                                  \
     if (r.D == DD && G == GG) {                                               \
-        pf::flash_kernel<DD, GG><<<grid, 64 * GG, 0, s>>>(a);                 \
+        pf::flash_kernel<DD, GG><<<grid, 64 * GG * pf::flash_wph<DD, GG>(), 0, s>>>(a); \
         return hipGetLastError();                                             \
     }
     Q35_PF_FLASH(64, 1) Q35_PF_FLASH(64, 2) Q35_PF_FLASH(64, 4) Q35_PF_FLASH(64, 8)
