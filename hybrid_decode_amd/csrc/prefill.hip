@@ -244,8 +244,9 @@ __global__ __launch_bounds__(2 * BM, 1) void gemm_kernel(PfGemmArgs a) {
 
     // k tile kt sits in LDS buffer kt % 2 while tile kt + 1 waits in registers and
     // tile kt + 2 is being fetched.  Loads past the last tile repeat it (in bounds,
-    // never stashed), so every iteration issues the same loads; an odd last tile
-    // runs after the loop.
+    // never stashed), so every iteration issues the same loads, and the loop body
+    // stashes at every step (a straight line the scheduler can interleave); the
+    // last one or two tiles run after it.
     const c0 lds0;
     const c1 lds1;
     load(g0, 0);
@@ -253,15 +254,21 @@ __global__ __launch_bounds__(2 * BM, 1) void gemm_kernel(PfGemmArgs a) {
     stash(g0, 0);
     __syncthreads();
     uint32_t kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-        load(g0, min(kt + 2, nk - 1));
+    for (; kt + 2 < nk; kt += 2) {
+        load(g0, kt + 2);
         compute(lds0, true);
         __syncthreads();
         load(g1, min(kt + 3, nk - 1));
-        compute(lds1, kt + 2 < nk);
+        compute(lds1, true);
         __syncthreads();
     }
-    if (kt < nk) compute(lds0, false);
+    if (kt + 1 < nk) {  // tiles kt (LDS buffer 0) and kt + 1 (stage g1)
+        compute(lds0, true);
+        __syncthreads();
+        compute(lds1, false);
+    } else {            // tile kt
+        compute(lds0, false);
+    }
 
     // epilogue: acc[i][j][r] is (row 8 (r/4) + 4 (lane/32) + r%4, column lane%32) of its tile
     if (!whole) {
