@@ -11,10 +11,13 @@ Turbo2, Bf16KTurbo4V/3V/2V, ``k_is_rotated`` and the byte table of
 ``LayerKvCache::alloc``; ``full_attention.rs``: the symmetric and asymmetric
 Turbo branches of ``forward_full_attention``):
 
-* a quantised side stores b-bit indices into a Lloyd-Max codebook (b = 4, 3
-  or 2: 16, 8 or 4 levels; 3-bit indices go 8 to 3 bytes, 2-bit 4 to a byte)
-  and one FP8 E4M3 scale per group of 16 that keeps the group's L2 norm, in the
-  Walsh-Hadamard-rotated basis: ``max_seq * kv_dim * b / 8`` data bytes and
+* a quantised side holds, per element, a b-bit index into a Lloyd-Max
+  codebook (b = 4, 3 or 2, so 16, 8 or 4 levels; eight 3-bit indices share 3
+  bytes, four 2-bit indices share a byte), plus one E4M3 (FP8) scale for every
+  16 elements; the scale is chosen so that the dequantised group has the same
+  Euclidean length as the original, and all of it lives in the basis produced
+  by the Walsh-Hadamard rotation (mod.rs, ``MetalKvDtype::Turbo4``, ``Turbo3``,
+  ``Turbo2``): ``max_seq * kv_dim * b / 8`` data bytes and
   ``max_seq * kv_dim / 16`` scale bytes per side;
 * symmetric formats quantise K and V (the query is rotated before attention),
   asymmetric ones keep K in bf16, not rotated (the query is not rotated); V is

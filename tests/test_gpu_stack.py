@@ -1,7 +1,7 @@
 """GPU parity of the layer loop: the tiny two-layer hybrid at every step, and the
 32-layer 4B-shaped stack (real lm_head) at KV context 8192 and 65536, both
-layer by layer and through the persistent decode kernel (the benchmark's launch
-configuration), on sampled layers (each fed the GPU's own input to that layer),
+through the per-layer kernels replayed from one HIP graph (the benchmark's
+launch configuration) and through the persistent decode kernel, on sampled layers (each fed the GPU's own input to that layer),
 sampled logits and the greedy token, plus HIP-graph replay against eager
 execution and the two paths against each other."""
 import numpy as np
@@ -214,7 +214,8 @@ def test_stack_4b_ctx65536_sampled_layers_logits_and_token(rt):
 
 @pytest.fixture(scope="module")
 def persist8k(rt, stack8k):
-    """The same workload run by the persistent decode kernel (the benchmark's path)."""
+    """The same workload run by the persistent decode kernel (an alternative to the
+per-layer kernels that the benchmark replays)."""
     w, _ = stack8k
     say("persistent plan over the 8192-context stack")
     return _stack_from(rt, w, persistent=True)
