@@ -28,9 +28,16 @@ Readings taken where the pages are silent (each also stated at its function):
   no infinities, 0x7F and 0xFF are NaN;
 * T4 the cache layout follows the bf16 cache: data ``[capacity, Hkv, D]`` and
   scales ``[capacity, Hkv, D / 16]``, token-major;
-* T5 attention is exact over all positions: the pages' optional sparse-V
-  gate (a probability threshold whose reference point they do not give; 0
-  disables it) is not applied.
+* T5 the sparse-V gate: the Turbo attention launches take a threshold tau
+  (1e-3 unless the caller sets another; 0 turns the gate off) below which a
+  position's value row is left out.  The pages give the threshold, not what
+  it is compared with.  Reading: with w_t = exp(s_t - max_u s_u), the weight of
+  position t relative to the largest one, the softmax is taken over every
+  position as usual and only the value rows with w_t < tau are skipped:
+  out = sum over {t : w_t >= tau} of p_t V_t, p_t = w_t / sum_u w_u.  A
+  streaming kernel that compares against its running maximum instead (never
+  above the final one) skips a subset of these rows, so it differs from this
+  by at most sum over {t : w_t < tau} of p_t |V_t| per element.
 
 Parity pins live in ``tests/test_oracle_pins.py`` (Turbo8 section).
 """
@@ -45,6 +52,9 @@ from .qwen35 import (act_to_f64, as_qm, bf16_to_f64, f64_to_bf16, mlp_residual, 
 
 E4M3_MAX = 448.0
 GROUP = 16
+# The sparse-V threshold the Turbo branch uses when the caller does not set one
+# (full_attention.rs page, Turbo branch of forward_full_attention); 0 disables it.
+SPARSE_V_DEFAULT = 1e-3
 
 # --------------------------------------------------------------------------- rotation
 
@@ -149,11 +159,22 @@ def turbo8_dequantize(codes: np.ndarray, scales_bf16: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------- attention and layer
 
 
+def sparse_v_weights(s: np.ndarray, sparse_v: float):
+    """Softmax of the scores ``s`` over every position, and the weights with the
+    value rows the sparse-V gate skips set to zero (reading T5: a row is skipped
+    when ``exp(s_t - max s) < sparse_v``; 0 skips nothing).  Returns (p, p_kept)."""
+    w = np.exp(s - s.max())
+    p = w / w.sum()
+    return p, np.where(w >= sparse_v, p, 0.0)
+
+
 def attention_decode_turbo8(q: np.ndarray, kc: np.ndarray, ks: np.ndarray, vc: np.ndarray,
-                            vs: np.ndarray, seq_len: int) -> np.ndarray:
+                            vs: np.ndarray, seq_len: int,
+                            sparse_v: float = SPARSE_V_DEFAULT) -> np.ndarray:
     """GQA decode attention over a Turbo8 cache, in the pages' order: rotate each
     query head, attend with the dequantised rotated keys and values (scale
-    1/sqrt(D), softmax over positions [0, seq_len)), inverse-rotate the output.
+    1/sqrt(D), softmax over positions [0, seq_len), value rows gated by
+    ``sparse_v`` as in reading T5), inverse-rotate the output.
 
     q: [Hq, D] float64 (unrotated); kc/vc: uint8 [cap, Hkv, D]; ks/vs: bf16
     [cap, Hkv, D/16].  Returns [Hq, D] float64 in the unrotated basis.
@@ -168,9 +189,8 @@ def attention_decode_turbo8(q: np.ndarray, kc: np.ndarray, ks: np.ndarray, vc: n
     for h in range(Hq):
         g = h // rep
         s = K[:, g, :] @ qr[h] / math.sqrt(D)
-        p = np.exp(s - s.max())
-        p /= p.sum()
-        out[h] = p @ V[:, g, :]
+        _, pk = sparse_v_weights(s, sparse_v)
+        out[h] = pk @ V[:, g, :]
     return wht(out)
 
 
@@ -184,7 +204,8 @@ def turbo8_append(kv: dict, pos: int, k: np.ndarray, v: np.ndarray) -> dict:
 
 
 def forward_full_attention_turbo8(cfg, layer: dict, kv: dict, inv_freq: np.ndarray,
-                                  x_in: np.ndarray, cache_pos: int):
+                                  x_in: np.ndarray, cache_pos: int,
+                                  sparse_v: float = SPARSE_V_DEFAULT):
     """One token through one gated full-attention layer with a Turbo8 cache (the
     Turbo branch of ``forward_full_attention``): input RMSNorm, q/k/v projections,
     q/gate split, q/k RMSNorm, partial RoPE, rotated quantised append of k and v,
@@ -207,7 +228,7 @@ def forward_full_attention_turbo8(cfg, layer: dict, kv: dict, inv_freq: np.ndarr
     kr = rope_partial(kn, cache_pos, inv_freq, R)
     new_kv = turbo8_append(kv, cache_pos, kr, v.reshape(Hkv, D))
     attn = attention_decode_turbo8(qr, new_kv["k"], new_kv["k_scales"], new_kv["v"],
-                                   new_kv["v_scales"], cache_pos + 1)
+                                   new_kv["v_scales"], cache_pos + 1, sparse_v)
     ga = attn * sigmoid(gate)
     o = as_qm(layer["o_proj"]) @ ga.reshape(-1)
     r = x + o

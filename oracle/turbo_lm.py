@@ -46,8 +46,10 @@ Readings taken where the pages are silent (each also stated at its function):
 * V5 the rotation is the orthonormal Walsh-Hadamard transform of a head
   (reading T1 of the Turbo8 oracle); the quantiser's input is the rotated
   vector rounded to fp32;
-* V6 attention is exact over all positions (the pages' optional sparse-V gate
-  is not applied, as for Turbo8).
+* V6 the sparse-V gate follows reading T5 of the Turbo8 oracle: softmax over
+  every position, value rows whose weight relative to the largest,
+  exp(s_t - max s), is below the threshold (1e-3 unless set; 0 disables) are
+  left out.
 
 Parity pins live in ``tests/test_oracle_pins.py`` (Lloyd-Max formats section).
 """
@@ -60,7 +62,7 @@ import numpy as np
 
 from .qwen35 import (act_to_f64, as_qm, bf16_to_f64, f64_to_bf16, mlp_residual, rms_norm,
                      rope_partial, sigmoid)
-from .turbo8 import e4m3_decode, e4m3_encode, wht
+from .turbo8 import SPARSE_V_DEFAULT, e4m3_decode, e4m3_encode, sparse_v_weights, wht
 
 GROUP = 16
 
@@ -203,11 +205,13 @@ def turbo4_dequantize(packed, scales):
 # --------------------------------------------------------------------------- attention and layer
 
 
-def attention_decode(fmt: str, q: np.ndarray, kv: dict, seq_len: int) -> np.ndarray:
+def attention_decode(fmt: str, q: np.ndarray, kv: dict, seq_len: int,
+                     sparse_v: float = SPARSE_V_DEFAULT) -> np.ndarray:
     """GQA decode attention over a Lloyd-Max format cache: for a symmetric
     format the query is rotated and scored against the dequantised rotated
     keys, for an asymmetric one the unrotated query against the bf16 keys
-    (scale 1/sqrt(D), softmax over [0, seq_len)); the weights apply to the
+    (scale 1/sqrt(D), softmax over [0, seq_len)); the weights, with the rows
+    the sparse-V gate skips set to zero (reading V6), apply to the
     dequantised rotated values and the output is rotated back.
 
     q: [Hq, D] float64; kv: {"k", "v", "v_scales"} (+ "k_scales" when K is
@@ -228,14 +232,14 @@ def attention_decode(fmt: str, q: np.ndarray, kv: dict, seq_len: int) -> np.ndar
     for h in range(Hq):
         g = h // rep
         s = K[:, g, :] @ qq[h] / math.sqrt(D)
-        p = np.exp(s - s.max())
-        p /= p.sum()
-        out[h] = p @ V[:, g, :]
+        _, pk = sparse_v_weights(s, sparse_v)
+        out[h] = pk @ V[:, g, :]
     return wht(out)
 
 
-def attention_decode_bf16k_turbo4v(q, kc, vc, vs, seq_len):
-    return attention_decode("bf16k_turbo4v", q, {"k": kc, "v": vc, "v_scales": vs}, seq_len)
+def attention_decode_bf16k_turbo4v(q, kc, vc, vs, seq_len, sparse_v: float = SPARSE_V_DEFAULT):
+    return attention_decode("bf16k_turbo4v", q, {"k": kc, "v": vc, "v_scales": vs}, seq_len,
+                            sparse_v)
 
 
 def append(fmt: str, kv: dict, pos: int, k: np.ndarray, v: np.ndarray) -> dict:
@@ -257,7 +261,7 @@ def bf16k_turbo4v_append(kv, pos, k, v):
 
 
 def forward_full_attention(fmt: str, cfg, layer: dict, kv: dict, inv_freq: np.ndarray,
-                           x_in: np.ndarray, cache_pos: int):
+                           x_in: np.ndarray, cache_pos: int, sparse_v: float = SPARSE_V_DEFAULT):
     """One token through one gated full-attention layer with a Lloyd-Max format
     cache (the Turbo branches of ``forward_full_attention``): the bf16 layer's
     steps with the quantising append and the format's attention.
@@ -275,7 +279,7 @@ def forward_full_attention(fmt: str, cfg, layer: dict, kv: dict, inv_freq: np.nd
     qr = rope_partial(qn, cache_pos, inv_freq, R)
     kr = rope_partial(kn, cache_pos, inv_freq, R)
     new_kv = append(fmt, kv, cache_pos, kr, v.reshape(Hkv, D))
-    attn = attention_decode(fmt, qr, new_kv, cache_pos + 1)
+    attn = attention_decode(fmt, qr, new_kv, cache_pos + 1, sparse_v)
     ga = attn * sigmoid(gate)
     o = as_qm(layer["o_proj"]) @ ga.reshape(-1)
     r = x + o
@@ -287,5 +291,7 @@ def forward_full_attention(fmt: str, cfg, layer: dict, kv: dict, inv_freq: np.nd
     return x_out, new_kv, taps
 
 
-def forward_full_attention_bf16k_turbo4v(cfg, layer, kv, inv_freq, x_in, cache_pos):
-    return forward_full_attention("bf16k_turbo4v", cfg, layer, kv, inv_freq, x_in, cache_pos)
+def forward_full_attention_bf16k_turbo4v(cfg, layer, kv, inv_freq, x_in, cache_pos,
+                                         sparse_v: float = SPARSE_V_DEFAULT):
+    return forward_full_attention("bf16k_turbo4v", cfg, layer, kv, inv_freq, x_in, cache_pos,
+                                  sparse_v)

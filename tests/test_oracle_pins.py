@@ -593,7 +593,7 @@ def test_turbo8_attention_equals_sdpa_on_unrotated_dequantised_cache():
     ks = O.f64_to_bf16(rng.uniform(1e-3, 4e-3, (L + 3, Hkv, D // 16)))
     vs = O.f64_to_bf16(rng.uniform(1e-3, 4e-3, (L + 3, Hkv, D // 16)))
     q = rng.standard_normal((Hq, D)) * 4
-    got = T8.attention_decode_turbo8(q, kc, ks, vc, vs, L)
+    got = T8.attention_decode_turbo8(q, kc, ks, vc, vs, L, sparse_v=0.0)
     K = torch.from_numpy(T8.wht(T8.turbo8_dequantize(kc[:L], ks[:L]))).permute(1, 0, 2)
     V = torch.from_numpy(T8.wht(T8.turbo8_dequantize(vc[:L], vs[:L]))).permute(1, 0, 2)
     K = K.repeat_interleave(Hq // Hkv, dim=0)
@@ -736,7 +736,7 @@ def test_lloyd_max_format_attention_equals_sdpa(fmt):
         kv["k"] = O.f64_to_bf16(rng.standard_normal((L + 2, Hkv, D)))
         K = O.bf16_to_f64(kv["k"][:L])
     q = rng.standard_normal((Hq, D)) * 3
-    got = T4.attention_decode(fmt, q, kv, L)
+    got = T4.attention_decode(fmt, q, kv, L, sparse_v=0.0)
     V = T8.wht(T4.dequantize(kv["v"][:L], kv["v_scales"][:L], bits))
     Kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
     Vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
@@ -752,7 +752,7 @@ def test_turbo4v_attention_equals_sdpa_on_dequantised_values():
     vc = rng.integers(0, 256, (L + 2, Hkv, D // 2), dtype=np.uint8)
     vs = T8.e4m3_encode(rng.uniform(0.05, 2.0, (L + 2, Hkv, D // 16)).astype(np.float32))
     q = rng.standard_normal((Hq, D)) * 3
-    got = T4.attention_decode_bf16k_turbo4v(q, kc, vc, vs, L)
+    got = T4.attention_decode_bf16k_turbo4v(q, kc, vc, vs, L, sparse_v=0.0)
     K = torch.from_numpy(O.bf16_to_f64(kc[:L])).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
     V = torch.from_numpy(T8.wht(T4.turbo4_dequantize(vc[:L], vs[:L]))).permute(1, 0, 2)
     V = V.repeat_interleave(Hq // Hkv, dim=0)
