@@ -9,7 +9,10 @@
 //     S     <- S + k delta^T
 //     y      = S^T q / sqrt(dk)
 // Columns of S are independent, so the grid splits each head into tiles of
-// 16 columns.  With a = S_old^T k and b = S_old^T q the step is
+// 32 columns: a tile row is one 128-byte line, so every line of the state is
+// read and written by exactly one block (a 16-column tile left each line half
+// to a block on another XCD, and both XCDs' L2s fetched all of it).  With
+// a = S_old^T k and b = S_old^T q the step is
 //     delta = beta (v - g a),   y = (g b + (k.q) delta) / sqrt(dk),
 //     S'    = g S_old + k delta^T,
 // so one pass over the state computes both dot products, and one more writes
@@ -22,16 +25,17 @@
 namespace q35 {
 namespace {
 
-constexpr int kCT = 16;  // state columns per block
+constexpr int kCT = 32;  // state columns per block (one 128-byte line per row)
 
-// Threads: 2*DK.  Thread t holds state rows {2r, 2r+1} (r = t / 4) for the 4
-// columns 4c..4c+3 (c = t % 4) of the block's tile: two float4 per thread.
+// Threads: 2*DK.  Thread t holds state rows {2r, 2r+1} (r = t / 4) for the 8
+// columns 8c..8c+7 (c = t % 4) of the block's tile: four float4 per thread, all
+// issued before any arithmetic.
 template <int DK>
 __global__ __launch_bounds__(2 * DK) void gdn_kernel(GdnArgs a) {
     constexpr int DV = DK;
     constexpr int NT = 2 * DK, NW = (NT + 63) / 64;
     constexpr int NPR = NT / 16;  // 16-lane DPP rows; each sums 4 row pairs (8 state rows)
-    static_assert(NT >= 64 && kCT == 16, "at least one wave; a DPP row covers the 16 columns");
+    static_assert(NT >= 64 && kCT == 32 && DV % kCT == 0, "at least one wave; 4 lanes cover a tile row");
     __shared__ float dl[kCT];
     __shared__ float red[3][NW];
     __shared__ float part[NPR][2][kCT];  // per DPP row: a and b partials of the tile's columns
@@ -46,9 +50,17 @@ __global__ __launch_bounds__(2 * DK) void gdn_kernel(GdnArgs a) {
 
     // 1. every load is issued up front: the state tile, this thread's two q and
     //    k entries (raw; the L2 norms become two scalar factors), v, gate, beta
-    float* sbase = a.state + (size_t)h * DK * DV + col0 + 4 * cq;
-    const float4 S0 = *reinterpret_cast<const float4*>(sbase + (size_t)row0 * DV);
-    const float4 S1 = *reinterpret_cast<const float4*>(sbase + (size_t)(row0 + 1) * DV);
+    float* sbase = a.state + (size_t)h * DK * DV + col0 + 8 * cq;
+    float S[2][8];
+    {
+        const float4* p0 = reinterpret_cast<const float4*>(sbase + (size_t)row0 * DV);
+        const float4* p1 = reinterpret_cast<const float4*>(sbase + (size_t)(row0 + 1) * DV);
+        const float4 u0 = p0[0], u1 = p0[1], u2 = p1[0], u3 = p1[1];
+        S[0][0] = u0.x; S[0][1] = u0.y; S[0][2] = u0.z; S[0][3] = u0.w;
+        S[0][4] = u1.x; S[0][5] = u1.y; S[0][6] = u1.z; S[0][7] = u1.w;
+        S[1][0] = u2.x; S[1][1] = u2.y; S[1][2] = u2.z; S[1][3] = u2.w;
+        S[1][4] = u3.x; S[1][5] = u3.y; S[1][6] = u3.z; S[1][7] = u3.w;
+    }
     const float2 qr = *reinterpret_cast<const float2*>(a.qkv_conv + i * DK + row0);
     const float2 kr = *reinterpret_cast<const float2*>(a.qkv_conv + a.hk * DK + i * DK + row0);
     const float vv = a.qkv_conv[2 * a.hk * DK + h * DV + col0 + min(t, kCT - 1)];
@@ -56,20 +68,17 @@ __global__ __launch_bounds__(2 * DK) void gdn_kernel(GdnArgs a) {
     const float beta = a.beta[h];
 
     // 2. partial a = S^T k, b = S^T q (raw q, k) and the norms' sums, reduced
-    //    over the rows of each 16-lane DPP row (lanes of equal column quad)
-    float pa[4], pb[4];
-    pa[0] = fmaf(S0.x, kr.x, S1.x * kr.y);
-    pa[1] = fmaf(S0.y, kr.x, S1.y * kr.y);
-    pa[2] = fmaf(S0.z, kr.x, S1.z * kr.y);
-    pa[3] = fmaf(S0.w, kr.x, S1.w * kr.y);
-    pb[0] = fmaf(S0.x, qr.x, S1.x * qr.y);
-    pb[1] = fmaf(S0.y, qr.x, S1.y * qr.y);
-    pb[2] = fmaf(S0.z, qr.x, S1.z * qr.y);
-    pb[3] = fmaf(S0.w, qr.x, S1.w * qr.y);
-    // rotating a 16-lane row by 4 and then 8 keeps lane & 3 (the column quad):
+    //    over the rows of each 16-lane DPP row (lanes of equal column octet)
+    float pa[8], pb[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        pa[c] = fmaf(S[0][c], kr.x, S[1][c] * kr.y);
+        pb[c] = fmaf(S[0][c], qr.x, S[1][c] * qr.y);
+    }
+    // rotating a 16-lane row by 4 and then 8 keeps lane & 3 (the column octet):
     // every lane ends with the sum over the row's 4 row pairs for its columns
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 8; ++c) {
         pa[c] += dpp<0x124>(pa[c]);  // row_ror:4
         pb[c] += dpp<0x124>(pb[c]);
         pa[c] += dpp<0x128>(pa[c]);  // row_ror:8
@@ -84,12 +93,12 @@ __global__ __launch_bounds__(2 * DK) void gdn_kernel(GdnArgs a) {
         red[1][wid] = r1;
         red[2][wid] = r2;
     }
-    if ((lane & 15) < 4) {  // lanes 0..3 of each DPP row: column quads 0..3
+    if ((lane & 15) < 4) {  // lanes 0..3 of each DPP row: column octets 0..3
         const int pr = t >> 4;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            part[pr][0][4 * cq + c] = pa[c];
-            part[pr][1][4 * cq + c] = pb[c];
+        for (int c = 0; c < 8; ++c) {
+            part[pr][0][8 * cq + c] = pa[c];
+            part[pr][1][8 * cq + c] = pb[c];
         }
     }
     __syncthreads();
@@ -128,19 +137,20 @@ __global__ __launch_bounds__(2 * DK) void gdn_kernel(GdnArgs a) {
     __syncthreads();
 
     // 4. S' = g S + k delta^T (k normalised)
-    const float d0 = dl[4 * cq], d1 = dl[4 * cq + 1], d2 = dl[4 * cq + 2], d3 = dl[4 * cq + 3];
     const float k0 = kr.x * rk, k1 = kr.y * rk;
-    float4 o0, o1;
-    o0.x = fmaf(k0, d0, g * S0.x);
-    o0.y = fmaf(k0, d1, g * S0.y);
-    o0.z = fmaf(k0, d2, g * S0.z);
-    o0.w = fmaf(k0, d3, g * S0.w);
-    o1.x = fmaf(k1, d0, g * S1.x);
-    o1.y = fmaf(k1, d1, g * S1.y);
-    o1.z = fmaf(k1, d2, g * S1.z);
-    o1.w = fmaf(k1, d3, g * S1.w);
-    *reinterpret_cast<float4*>(sbase + (size_t)row0 * DV) = o0;
-    *reinterpret_cast<float4*>(sbase + (size_t)(row0 + 1) * DV) = o1;
+    float o[2][8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const float d = dl[8 * cq + c];
+        o[0][c] = fmaf(k0, d, g * S[0][c]);
+        o[1][c] = fmaf(k1, d, g * S[1][c]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        float4* p = reinterpret_cast<float4*>(sbase + (size_t)(row0 + j) * DV);
+        p[0] = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
+        p[1] = make_float4(o[j][4], o[j][5], o[j][6], o[j][7]);
+    }
 }
 
 }  // namespace
