@@ -7,9 +7,51 @@ import oracle as O
 TOL_BF16 = 2e-2    # bf16 activations
 TOL_F32 = 1e-3     # fp32 activations (tiny config) and the fp32 GDN state after 64 steps
 TOL_GEMV = 2e-5    # one fp32 GEMV against float64
+# Logits of the whole 32-layer 4B stack run by the oracle from the GPU's tokens
+# (its own residual stream, not fed the GPU's layer inputs).  The random-weight
+# stack amplifies any difference of rounding: the oracle itself, evaluated with
+# the pages' bf16 buffers rounded (Mode B) instead of unrounded (Mode A),
+# differs by 3.7e-2 in the first token's logits, and a relative perturbation of
+# 1e-4 of the first layer's output grows to 2.2e-2.  The bound is that spread
+# with margin; the per-layer checks (each layer fed the GPU's input) carry the
+# 2e-2 bf16 gate.
+TOL_STACK = 6e-2
 # one GEMV whose x is rounded to f16 (11 significant bits) before exact products:
 # the error is that rounding, ~2^-12 relative per element, averaged over the dot
 TOL_GEMV_F16 = 1e-3
+
+
+# Element-wise gate, applied beside the relative L2 one: no element may differ
+# from the oracle by more than one step of the output format at the oracle's
+# value (the rounding of a bf16 or fp32 store) plus ELEM_* times the RMS of the
+# oracle vector.  A single wrong element of typical size (about one RMS) fails
+# it, which a relative L2 bound of 2e-2 over 2560 elements would let pass.
+ELEM_BF16 = 0.15
+ELEM_F32 = 1e-2
+
+
+def fmt_step(ref, bits: int) -> np.ndarray:
+    """Spacing of a float format with ``bits`` significand bits (bf16 8, fp32 24)
+    at |ref|: 2^(e - bits + 1) for |ref| in [2^e, 2^(e+1))."""
+    ref = np.abs(np.asarray(ref, dtype=np.float64))
+    _, ex = np.frexp(ref)               # ref = m 2^ex, m in [0.5, 1)
+    return np.where(ref > 0, np.ldexp(1.0, ex - bits), 0.0)
+
+
+def elem_err(gpu, ref, bits: int = 8) -> float:
+    """max_i (|gpu_i - ref_i| - step(ref_i)) / rms(ref), the quantity ELEM_* bounds."""
+    gpu = np.asarray(gpu, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    rms = float(np.sqrt(np.mean(ref * ref))) or 1.0
+    return float(np.max(np.abs(gpu - ref) - fmt_step(ref, bits)) / rms)
+
+
+def check(gpu, ref, tol: float, elem: float, bits: int = 8, what=""):
+    """Both gates; returns (rel L2, element error) for reporting."""
+    r, e = rel(gpu, ref), elem_err(gpu, ref, bits)
+    assert r < tol, (what, "rel", r)
+    assert e < elem, (what, "elem", e)
+    return r, e
 
 
 def rel(gpu, ref) -> float:

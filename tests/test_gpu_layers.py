@@ -11,7 +11,7 @@ import torch
 import oracle as O
 import synth
 from synth import workloads
-from gpu_common import TOL_BF16, TOL_F32, rel, say
+from gpu_common import ELEM_BF16, ELEM_F32, TOL_BF16, TOL_F32, check, rel, say
 
 pytestmark = pytest.mark.gpu
 
@@ -53,9 +53,9 @@ def test_gdn_layer_tiny_fp32_every_step_and_tap(rt, gen):
         rt.forward_linear_attention(cfg, L, S, scr, xin, x_buf)
         torch.cuda.synchronize()
         ox, ost, taps = O.forward_linear_attention(cfg, layer, ost, x)
-        assert rel(rt.act_to_f32(x_buf, cfg), ox) < TOL_F32, t
+        check(rt.act_to_f32(x_buf, cfg), ox, TOL_F32, ELEM_F32, 24, t)
         for k, ok in GDN_TAPS.items():
-            assert rel(scr.t[k].cpu().numpy(), taps[ok]) < TOL_F32, (t, k)
+            check(scr.t[k].cpu().numpy(), taps[ok], TOL_F32, ELEM_F32, 24, (t, k))
         assert np.array_equal(rt.act_to_host(scr.t["x_final"], cfg), rt.act_to_host(x_buf, cfg))
         gst = S.to_host()
         assert rel(gst["gdn_state"], ost["gdn_state"]) < TOL_F32, t
@@ -121,9 +121,9 @@ def test_full_layer_tiny_fp32_every_step_tap_and_append(rt, gen):
         rt.forward_full_attention(cfg, Ld, scr, KVd, inv, pos, rt.to_dev(x), t)
         torch.cuda.synchronize()
         ox, okv, taps = O.forward_full_attention(cfg, layer, okv, inv_h, x, t)
-        assert rel(rt.act_to_f32(scr.t["x_out"], cfg), ox) < TOL_F32, t
+        check(rt.act_to_f32(scr.t["x_out"], cfg), ox, TOL_F32, ELEM_F32, 24, t)
         for k, ok in FULL_TAPS.items():
-            assert rel(scr.t[k].cpu().numpy(), taps[ok]) < TOL_F32, (t, k)
+            check(scr.t[k].cpu().numpy(), taps[ok], TOL_F32, ELEM_F32, 24, (t, k))
         after = KVd.to_host()
         for side in ("k", "v"):
             changed = np.nonzero(np.any(after[side] != before[side], axis=(1, 2)))[0].tolist()
@@ -145,16 +145,16 @@ def test_gdn_layer_4b_bf16_256_steps_and_state(rt, gen):
     scr = rt.GdnScratchDev(cfg)
     x_buf = rt.act_empty(cfg, cfg.hidden)
     ost = st
-    worst = 0.0
+    worst = worst_e = 0.0
     for t, x in enumerate(w["xs"]):
         if t % 32 == 0:
             say(f"4B GDN step {t}")
         rt.forward_linear_attention(cfg, L, S, scr, rt.to_dev(x), x_buf)
         ox, ost, _ = O.forward_linear_attention(cfg, layer, ost, x)
         torch.cuda.synchronize()
-        r = rel(rt.act_to_f32(x_buf, cfg), ox)
+        r, e = check(rt.act_to_f32(x_buf, cfg), ox, TOL_BF16, ELEM_BF16, 8, t)
         worst = max(worst, r)
-        assert r < TOL_BF16, (t, r)
+        worst_e = max(worst_e, e)
         if t == 63:
             gst = S.to_host()
             r_state = rel(gst["gdn_state"], ost["gdn_state"])
@@ -163,7 +163,7 @@ def test_gdn_layer_4b_bf16_256_steps_and_state(rt, gen):
             assert r_state < TOL_F32
             assert r_conv < TOL_F32
     gst = S.to_host()
-    say(f"4B GDN: worst output rel {worst:.2e}; after 256 steps state rel "
+    say(f"4B GDN: worst output rel {worst:.2e}, element error {worst_e:.3f} RMS; after 256 steps state rel "
         f"{rel(gst['gdn_state'], ost['gdn_state']):.2e}")
 
 
@@ -183,7 +183,7 @@ def test_full_layer_4b_bf16_64_steps_from_4096(rt, gen):
     inv_h = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
     okv = {"k": kv["k"].copy(), "v": kv["v"].copy()}
     outs = []
-    worst = 0.0
+    worst = worst_e = 0.0
     for i, x in enumerate(w["xs"]):
         t = start + i
         if i % 16 == 0:
@@ -194,10 +194,10 @@ def test_full_layer_4b_bf16_64_steps_from_4096(rt, gen):
         torch.cuda.synchronize()
         g = rt.act_to_f32(scr.t["x_out"], cfg)
         outs.append(g.copy())
-        r = rel(g, ox)
+        r, e = check(g, ox, TOL_BF16, ELEM_BF16, 8, t)
         worst = max(worst, r)
-        assert r < TOL_BF16, (t, r)
-    say(f"4B full attention: worst output rel {worst:.2e}")
+        worst_e = max(worst_e, e)
+    say(f"4B full attention: worst output rel {worst:.2e}, element error {worst_e:.3f} RMS")
     after = KVd.to_host()
     for side in ("k", "v"):
         assert np.array_equal(after[side][:start], kv[side][:start])          # prefill untouched

@@ -382,3 +382,17 @@ def test_turbo8_sparse_v_matches_the_same_rule():
         ref = T8.wht(((p * keep) @ V).numpy())
         assert np.allclose(got[h], ref, rtol=1e-10, atol=1e-12)
     assert 0 < kept < Hq * L
+
+
+def test_fp32_quant_matrix_is_within_fp32_rounding_of_brute_force(gen):
+    # the fp32 evaluation of the stack-sized GEMVs: the dense weights are the same
+    # exact fp32 values, the product carries fp32 accumulation error only
+    w = gen.quant("pin.qm32", 96, 2560)
+    x = gen.act("pin.qm32.x", (2560,), "f32").astype(np.float64)
+    q32 = O.QuantMatrix(w, np.float32)
+    assert q32.dense().dtype == np.float32
+    assert np.array_equal(q32.dense(), O.dequant(w))
+    ref = np.array([sum(float(a) * float(b) for a, b in zip(row, x)) for row in O.dequant(w)])
+    got = q32 @ x
+    assert got.dtype == np.float64
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 1e-5
