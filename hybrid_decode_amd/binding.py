@@ -43,7 +43,8 @@ EXPORTS = [
     "q35_kernels_resolve", "q35_kernels_release", "q35_kv_dtype_from_str", "q35_kv_cache_bytes",
     "q35_full_attention_workspace_bytes", "q35_forward_full_attention",
     "q35_forward_full_attention_devpos", "q35_forward_linear_attention", "q35_embed_lookup",
-    "q35_lm_head_workspace_bytes", "q35_lm_head_argmax", "q35_gate_up_swiglu", "q35_gemv",
+    "q35_lm_head_workspace_bytes", "q35_lm_head_argmax", "q35_lm_head_argmax_noalloc",
+    "q35_gate_up_swiglu", "q35_gemv",
     "q35_decode_workspace_bytes", "q35_decode_plan_create", "q35_decode_plan_release",
     "q35_decode_step", "q35_decode_check", "q35_decode_layer_input", "q35_decode_stage_layout",
     "q35_decode_stage_times", "q35_turbo8_quantize", "q35_fp8_e4m3_table",
@@ -177,6 +178,8 @@ def lib():
             "q35_lm_head_workspace_bytes": (st, [P(Qwen35ForwardConfig), P(sz)]),
             "q35_lm_head_argmax": (st, [vp, P(Qwen35ForwardConfig), vp, P(Q35QuantWeight), vp, vp,
                                         vp, sz, vp, vp, vp, u32, i32, vp, vp, vp]),
+            "q35_lm_head_argmax_noalloc": (st, [vp, P(Qwen35ForwardConfig), vp, P(Q35QuantWeight),
+                                                vp, vp, vp, vp, vp, u32, i32, vp, vp, vp]),
             "q35_gate_up_swiglu": (st, [vp, P(Qwen35ForwardConfig), vp, P(Q35QuantWeight),
                                         P(Q35QuantWeight), vp, vp, vp]),
             "q35_gemv": (st, [vp, P(Q35QuantWeight), vp, vp, u32, vp]),
@@ -310,6 +313,14 @@ def q35_lm_head_argmax(kernels, cfg, final_norm, lm_head, x, logits, workspace, 
                                     logits, workspace, workspace_bytes, tokens, positions,
                                     history, history_len, history_base, embed_table, x_next,
                                     stream))
+
+
+def q35_lm_head_argmax_noalloc(kernels, cfg, final_norm, lm_head, x, logits, tokens, positions,
+                               history, history_len, history_base, embed_table, x_next,
+                               stream) -> None:
+    _check(lib().q35_lm_head_argmax_noalloc(kernels, C.byref(cfg), final_norm, C.byref(lm_head), x,
+                                            logits, tokens, positions, history, history_len,
+                                            history_base, embed_table, x_next, stream))
 
 
 def q35_gate_up_swiglu(kernels, cfg, post_ln, gate_proj, up_proj, x_resid, mlp_act, stream) -> None:

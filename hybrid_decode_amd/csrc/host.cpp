@@ -21,6 +21,8 @@ struct Qwen35Kernels {
     int device;
     int num_cu;
     q35::LmLevels lm[5];  // Lloyd-Max codebooks of 2, 3 and 4 bits (computed at resolve)
+    void* scratch;        // this device's copy of the fixed workspace (no-alloc entry points)
+    size_t scratch_bytes;
 };
 
 namespace {
@@ -467,11 +469,21 @@ q35_status q35_kernels_resolve(int device, Qwen35Kernels** out) {
     probe(lm_finish_kernel_ptr(), "lm_head argmax");
     for (uint32_t d : {64u, 128u, 256u})
         for (uint32_t g : {1u, 2u, 4u, 8u}) probe(attn_combine_kernel_ptr(d, g), "attention merge");
+    // the fixed workspace's address on this device (it is current here)
+    void* scratch_ptr = nullptr;
+    size_t scratch_bytes = 0;
+    if (st == Q35_OK) {
+        const hipError_t e = static_scratch_address(&scratch_ptr, &scratch_bytes);
+        if (e != hipSuccess || !scratch_ptr)
+            st = fail(Q35_ERR_HIP, "fixed workspace address: %s", hipGetErrorString(e));
+    }
     (void)hipSetDevice(prev);
     if (st != Q35_OK) return st;
     Qwen35Kernels* k = new Qwen35Kernels;
     k->device = device;
     k->num_cu = prop.multiProcessorCount;
+    k->scratch = scratch_ptr;
+    k->scratch_bytes = scratch_bytes;
     for (int bits = 2; bits <= 4; ++bits) lloyd_max_normal(1 << bits, k->lm[bits].v);
     *out = k;
     return ok();
@@ -844,6 +856,28 @@ q35_status q35_lm_head_argmax(const Qwen35Kernels* kernels, const Qwen35ForwardC
     f.act_f32 = f32 ? 1 : 0;
     Q35_HIP(lm_finish_launch(f, stream), "lm_head argmax");
     return ok();
+}
+
+q35_status q35_lm_head_argmax_noalloc(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                                      const uint16_t* final_norm, const Q35QuantWeight* lm_head,
+                                      const void* x, float* logits, int32_t* tokens,
+                                      int32_t* positions, int32_t* history, uint32_t history_len,
+                                      int32_t history_base, const uint16_t* embed_table, void* x_next,
+                                      hipStream_t stream) {
+    Q35_TRY(check_kernels(kernels));
+    if (!cfg) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    Q35_TRY(q35_config_validate(cfg));
+    if (cfg->vocab == 0) return fail(Q35_ERR_INVALID_ARG, "vocab is 0");
+    const size_t need_bytes = lm_ws_layout(*cfg).total;
+    if (need_bytes > kernels->scratch_bytes)
+        return fail(Q35_ERR_OUT_OF_RANGE,
+                    "vocab %u needs %zu bytes of workspace, more than the fixed %zu bytes "
+                    "(use q35_lm_head_argmax with a caller workspace)",
+                    cfg->vocab, need_bytes, kernels->scratch_bytes);
+    // the per-block partials are written before they are read: nothing to clear
+    return q35_lm_head_argmax(kernels, cfg, final_norm, lm_head, x, logits, kernels->scratch,
+                              kernels->scratch_bytes, tokens, positions, history, history_len,
+                              history_base, embed_table, x_next, stream);
 }
 
 q35_status q35_gate_up_swiglu(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,

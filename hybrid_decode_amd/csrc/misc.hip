@@ -118,4 +118,18 @@ hipError_t embed_launch(const uint16_t* table, const int32_t* tokens, uint32_t v
 
 const void* embed_kernel_ptr() { return (const void*)&embed_kernel; }
 
+// Fixed workspace of the entry points that allocate nothing: each GPU the
+// library runs on holds one copy until the process ends.  Host code never
+// passes this name to a kernel (on the host it is a stand-in, not a device
+// address); static_scratch_address gives the device address, once per device,
+// with that device current.
+constexpr size_t kStaticScratchBytes = 64 * 1024;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+hipError_t static_scratch_address(void** ptr, size_t* bytes) {
+    *ptr = nullptr;
+    *bytes = kStaticScratchBytes;
+    return hipGetSymbolAddress(ptr, HIP_SYMBOL(scratch));
+}
+
 }  // namespace q35

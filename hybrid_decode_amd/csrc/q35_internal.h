@@ -183,6 +183,8 @@ const void* attn_combine_kernel_ptr(uint32_t head_dim, uint32_t group);
 hipError_t embed_launch(const uint16_t* table, const int32_t* tokens, uint32_t vocab,
                         uint32_t hidden, void* x_out, bool act_f32, hipStream_t stream);
 const void* embed_kernel_ptr();
+// Device address and size of the fixed workspace (the current device's copy).
+hipError_t static_scratch_address(void** ptr, size_t* bytes);
 
 // Greedy token from the lm_head's per-block partials, then the caller's
 // bookkeeping: history entry, position increment, next embedding.

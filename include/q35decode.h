@@ -416,6 +416,27 @@ q35_status q35_lm_head_argmax(const Qwen35Kernels* kernels, const Qwen35ForwardC
                               int32_t* history, uint32_t history_len, int32_t history_base,
                               const uint16_t* embed_table, void* x_next, hipStream_t stream);
 
+/*
+ * q35_lm_head_argmax without a workspace argument, for callers that cannot
+ * allocate (code under HIP graph capture, serving loops and harnesses that
+ * forbid hipMalloc).  Arguments, layout and results as q35_lm_head_argmax.
+ * The per-block partials go to a fixed 64 KiB device array that the library
+ * holds on each GPU until the process ends (its address is taken at
+ * q35_kernels_resolve); this call allocates nothing.  The partials never need
+ * more than 16 KiB (q35_lm_head_workspace_bytes: the launch is capped at a
+ * fixed number of blocks; the 248 320 vocabulary needs 15 872 bytes); a
+ * configuration that needed more than the array would return
+ * Q35_ERR_OUT_OF_RANGE.  Every call on one
+ * GPU shares that array: calls that overlap in time on one GPU (different
+ * streams without ordering) race and must not be issued.
+ */
+q35_status q35_lm_head_argmax_noalloc(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                                      const uint16_t* final_norm, const Q35QuantWeight* lm_head,
+                                      const void* x, float* logits, int32_t* tokens,
+                                      int32_t* positions, int32_t* history, uint32_t history_len,
+                                      int32_t history_base, const uint16_t* embed_table, void* x_next,
+                                      hipStream_t stream);
+
 /* ------------------------------------------------------------------ persistent decode */
 
 /*
