@@ -81,7 +81,8 @@ class Q35QuantWeight(C.Structure):
 
 class LayerKvCache(C.Structure):
     _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("capacity", C.c_uint32),
-                ("dtype", C.c_uint32), ("k_scales", C.c_void_p), ("v_scales", C.c_void_p)]
+                ("dtype", C.c_uint32), ("k_scales", C.c_void_p), ("v_scales", C.c_void_p),
+                ("sparse_v", C.c_float)]
 
 
 class FullAttentionLayer(C.Structure):

@@ -18,7 +18,9 @@
 //       (16 bytes each); the block's row slots each run an online softmax over
 //       their rows (base-2 exponent), then merge in LDS and the block writes
 //       one (max, sum, unnormalised output) triple per query head.  Each K/V
-//       row is read once for all G heads of its group (the GQA reuse).
+//       row is read once for all G heads of its group (the GQA reuse).  For
+//       the quantised formats the pages' sparse-V gate leaves out the value
+//       rows whose weight is below a threshold (see the loop).
 //   attn_merge_kernel    grid (q head, D/32), 256 threads: log-sum-exp merge
 //       of the chunk partials, the division by the total, the sigmoid gate.
 //
@@ -257,6 +259,7 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     __shared__ float red[(G < 4 ? G : 4) * RPI * D];  // per-slot outputs of up to 4 heads
     __shared__ float ov[ROTV ? G * D : 1];  // rotated V: merged accumulators, rotated back
     __shared__ float lut[LMV ? 16 : 1];     // Lloyd-Max formats: the codebook levels
+    __shared__ float bmax[G];               // sparse-V gate: running max of each head over the block
 
     const int32_t pos = attn_pos(a);
     if (pos < 0 || (uint32_t)pos >= a.capacity) return;
@@ -361,6 +364,7 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     if (t < D) vn[t] = ROTV ? vnew : bf16_to_f32(f32_to_bf16(vnew));
     if constexpr (LMV)
         if (t < 16) lut[t] = a.lm_levels[t];
+    if (t < G) bmax[t] = -INFINITY;
     if (t < (int)a.rotary / 2) {
         float sn, cs;
         sincosf((float)rope_pos * invf, &sn, &cs);
@@ -608,8 +612,7 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
             }
         }
     };
-    auto accumulate = [&](float pw, const float vv[8], float vscale) {
-        l += pw;
+    auto add_value = [&](float pw, const float vv[8], float vscale) {
 #pragma unroll
         for (int p = 0; p < G; ++p) {
             float pp = slot_bcast<G>(pw, p);
@@ -618,6 +621,23 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
             for (int e = 0; e < 8; ++e) acc[p][e] = fmaf(pp, vv[e], acc[p][e]);
         }
     };
+    auto accumulate = [&](float pw, const float vv[8], float vscale) {
+        l += pw;
+        add_value(pw, vv, vscale);
+    };
+    // Sparse-V gate of the quantised formats: the weight of every row enters the
+    // softmax sum, but a row's value is decoded and added only if some lane of
+    // the wave has s - r >= log2(sparse_v) for it.  r is the larger of the
+    // exact running maximum of the lane's row slot and the block's running
+    // maximum of its head, which the slots share through an LDS atomic max
+    // (m above is raised lazily and can lag by 8, which would weaken the gate
+    // by up to 2^8; a slot alone sees too few rows of a chunk).  Every value r
+    // can take is the maximum of rows already scored, never above the final
+    // maximum, so a row left out here has exp(s - max s) < sparse_v: the
+    // pages' rule would drop it too.
+    constexpr bool GATE = T8 || LMV;
+    const float lt = GATE ? a.sparse_v_log2 : -INFINITY;
+    float mrun = -INFINITY;
     auto batch = [&](const KT (&kd)[kUnroll], const VT (&vd)[kUnroll], const uint32_t (&ksd)[kUnroll],
                      const uint32_t (&vsd)[kUnroll], uint32_t tb) {
         float s[kUnroll];
@@ -633,12 +653,23 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) mx = fmaxf(mx, s[u]);
         rescale_to(mx);
+        float gref = -INFINITY;
+        if constexpr (GATE) {
+            mrun = fmaxf(mrun, mx);
+            if (j < G && mrun > -INFINITY)  // one lane per head of each row slot publishes
+                __hip_atomic_fetch_max(&bmax[hl], mrun, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            gref = fmaxf(mrun, __hip_atomic_load(&bmax[hl], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        }
         const float mref = m == -INFINITY ? 0.f : m;  // slot with no rows yet
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            float vv[8];
-            unpack_v(vd[u], vv);
-            accumulate(exp2f(s[u] - mref), vv, vscale_of(vsd[u]));
+            const float pw = exp2f(s[u] - mref);
+            l += pw;
+            if (!GATE || __builtin_amdgcn_ballot_w64(s[u] - gref >= lt) != 0) {
+                float vv[8];
+                unpack_v(vd[u], vv);
+                add_value(pw, vv, vscale_of(vsd[u]));
+            }
         }
     };
     // Reloads are unconditional (rows past the chunk read zero and move no

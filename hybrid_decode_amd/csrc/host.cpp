@@ -293,6 +293,8 @@ q35_status check_kv(const LayerKvCache& kv, bool allow_quantised) {
         if (kv.dtype == Q35_KV_TURBO8 &&
             ((reinterpret_cast<uintptr_t>(kv.k_scales) | reinterpret_cast<uintptr_t>(kv.v_scales)) & 1u))
             return fail(Q35_ERR_INVALID_ARG, "turbo8 scales not 2-byte aligned");
+        if (!(kv.sparse_v >= 0.0f && kv.sparse_v <= 3.0e38f))  // also rejects NaN and +inf
+            return fail(Q35_ERR_INVALID_ARG, "sparse_v %g must be finite and >= 0", (double)kv.sparse_v);
     } else {
         return fail(Q35_ERR_UNSUPPORTED, "KV dtype %u is not implemented on this path (%s)", kv.dtype,
                     allow_quantised ? "bf16 | turbo8 | turbo4/3/2 | bf16k_turbo4v/3v/2v" : "bf16");
@@ -624,6 +626,8 @@ static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35Fo
         a.max_chunks = attn_max_chunks(c, kv->capacity);
         a.eps = c.rms_eps;
         a.scale = 1.0f / std::sqrt((float)c.head_dim);
+        a.sparse_v_log2 = (kv->dtype == Q35_KV_BF16 || kv->sparse_v <= 0.0f) ? -INFINITY
+                                                                              : std::log2(kv->sparse_v);
         if (kv_lm_bits(kv->dtype)) std::memcpy(a.lm_levels, kernels->lm[kv_lm_bits(kv->dtype)].v, sizeof(a.lm_levels));
         uint32_t grid;
         if (cache_pos >= 0) {

@@ -158,6 +158,7 @@ struct AttnArgs {
     int32_t host_pos;        // >= 0: cache position from the host; < 0: read positions[0]
     float eps;
     float scale;
+    float sparse_v_log2;     // quantised formats: log2 of the sparse-V threshold (-inf: gate off)
     float lm_levels[16];     // Lloyd-Max formats: the codebook levels of the format's width
 };
 bool attn_dims_supported(uint32_t head_dim, uint32_t group);

@@ -139,7 +139,10 @@ class KvCacheDev:
     scale bytes [cap, Hkv, D/16] for each quantised side, "k" bf16 bits
     [cap, Hkv, D] for the asymmetric ones."""
 
-    def __init__(self, kv: dict, device="cuda"):
+    # the sparse-V threshold the pages' Turbo branch uses unless overridden
+    SPARSE_V_DEFAULT = 1e-3
+
+    def __init__(self, kv: dict, device="cuda", sparse_v: float = SPARSE_V_DEFAULT):
         if "kv_dtype" in kv:
             self.dtype = B.KV_DTYPES.index(kv["kv_dtype"])
         elif "k_scales" in kv:
@@ -154,8 +157,9 @@ class KvCacheDev:
         self.capacity = int(kv["k"].shape[0])
         self.k_scales = to_dev(kv["k_scales"], device) if "k_scales" in kv else None
         self.v_scales = to_dev(kv["v_scales"], device) if "v_scales" in kv else None
+        self.sparse_v = float(sparse_v)
         self.struct = B.LayerKvCache(ptr(self.k), ptr(self.v), self.capacity, self.dtype,
-                                     ptr(self.k_scales), ptr(self.v_scales))
+                                     ptr(self.k_scales), ptr(self.v_scales), self.sparse_v)
 
     def to_host(self) -> dict:
         """The arrays as NumPy, in the dtypes the generators use."""

@@ -181,6 +181,17 @@ q35_status q35_kv_cache_bytes(const Qwen35ForwardConfig* cfg, uint32_t dtype, ui
  *                  k as bf16 [capacity, num_kv_heads, head_dim], not rotated, with
  *                  k_scales NULL.  The append picks each index as the nearest level
  *                  to x / rms(group) and stores the scale ||x|| / ||level[idx]||.
+ * sparse_v: the sparse-V gate of the quantised formats (full_attention.rs: the
+ *   Turbo branches pass this threshold to their attention launches; the pages
+ *   use 1e-3 unless the caller overrides it, and 0 turns the gate off).  A
+ *   position's value row is left out of the weighted sum when its softmax
+ *   weight relative to the largest, exp(s_t - max s), is below sparse_v; the
+ *   softmax itself still covers every position.  The kernel compares against
+ *   its running maximum (never above the final one), so it leaves out a
+ *   subset of those rows, and only where every lane of a wave agrees: the
+ *   result differs from the exact rule by at most the weight of the rows that
+ *   rule drops.  Ignored for Q35_KV_BF16.  Must be finite and >= 0, else
+ *   Q35_ERR_INVALID_ARG.
  */
 typedef struct LayerKvCache {
     void* k;
@@ -189,6 +200,7 @@ typedef struct LayerKvCache {
     uint32_t dtype;
     void* k_scales;
     void* v_scales;
+    float sparse_v;
 } LayerKvCache;
 
 /* ------------------------------------------------------------------ full-attention layer */

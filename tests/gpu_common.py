@@ -72,3 +72,62 @@ def act_in(cfg, gen, name):
 
 def oracle_act(x, cfg):
     return O.act_to_f64(x, cfg.act_dtype)
+
+
+# --------------------------------------------------------------------------- sparse-V gate
+
+def _dequant_kv(fmt, kv, L):
+    """Stored rows [0, L) as the attention sees them: keys in the basis the query
+    is scored in, values rotated (the output is rotated back).  Returns (K, V,
+    query rotated?)."""
+    from oracle import turbo8 as T8
+    from oracle import turbo_lm as TL
+    if fmt == "turbo8":
+        K = T8.turbo8_dequantize(kv["k"][:L], kv["k_scales"][:L])
+        V = T8.turbo8_dequantize(kv["v"][:L], kv["v_scales"][:L])
+        return K, V, True
+    kq, bits = TL.FORMATS[fmt]
+    K = TL.dequantize(kv["k"][:L], kv["k_scales"][:L], bits) if kq else O.bf16_to_f64(kv["k"][:L])
+    V = TL.dequantize(kv["v"][:L], kv["v_scales"][:L], bits)
+    return K, V, kq
+
+
+def gated_attention_ref(fmt, q, kv, L, tau):
+    """The oracle's attention over a quantised cache with the sparse-V threshold tau."""
+    from oracle import turbo8 as T8
+    from oracle import turbo_lm as TL
+    if fmt == "turbo8":
+        return T8.attention_decode_turbo8(q, kv["k"], kv["k_scales"], kv["v"], kv["v_scales"], L,
+                                          sparse_v=tau)
+    return TL.attention_decode(fmt, q, kv, L, sparse_v=tau)
+
+
+def sparse_v_bound(fmt, q, kv, L, tau, rep):
+    """Per query head: the sum over the rows the oracle's gate drops of p_t ||V_t||
+    (p the softmax weight), and the number of dropped (row, head) pairs.  A
+    kernel that drops a subset of those rows lies within this L2 distance of
+    the oracle's gated output (the output rotation is orthonormal)."""
+    from oracle import turbo8 as T8
+    K, V, rot_q = _dequant_kv(fmt, kv, L)
+    D = q.shape[1]
+    out, n = [], 0
+    for h in range(q.shape[0]):
+        qq = T8.wht(q[h]) if rot_q else q[h]
+        s = K[:, h // rep, :] @ qq / np.sqrt(D)
+        p, pk = T8.sparse_v_weights(s, tau)
+        drop = pk == 0
+        n += int(drop.sum())
+        out.append(float(np.sum(p[drop] * np.linalg.norm(V[drop, h // rep, :], axis=1))))
+    return np.array(out), n
+
+
+def check_gated_attention(gpu, fmt, q, kv, L, tau, rep, tol):
+    """Per head: ||gpu - oracle(tau)|| <= tol ||oracle(tau)|| + the dropped weight
+    bound.  Returns (max error / norm, max bound / norm, dropped pairs)."""
+    ref = gated_attention_ref(fmt, q, kv, L, tau)
+    bound, ndrop = sparse_v_bound(fmt, q, kv, L, tau, rep)
+    g = np.asarray(gpu, dtype=np.float64).reshape(ref.shape)
+    err = np.linalg.norm(g - ref, axis=1)
+    scale = np.linalg.norm(ref, axis=1)
+    assert np.all(err <= tol * scale + bound * (1 + 1e-6)), (tau, err, bound)
+    return float((err / scale).max()), float((bound / scale).max()), ndrop

@@ -56,7 +56,7 @@ def test_struct_sizes_match_header_layout(lib):
     # 17 4-byte fields; the quantised-weight struct is 3 pointers + 2 u32
     assert ctypes.sizeof(B.Qwen35ForwardConfig) == 17 * 4
     assert ctypes.sizeof(B.Q35QuantWeight) == 32
-    assert ctypes.sizeof(B.LayerKvCache) == 40
+    assert ctypes.sizeof(B.LayerKvCache) == 48
 
 
 def test_tiny_config_validates(lib):
