@@ -99,7 +99,10 @@ class FullAttentionScratch(C.Structure):
                 ("x_out", C.c_void_p), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
                 ("x_norm", C.c_void_p), ("q_norm_out", C.c_void_p), ("k_norm_out", C.c_void_p),
                 ("attn_out", C.c_void_p), ("o", C.c_void_p), ("x_norm2", C.c_void_p),
-                ("gate_act", C.c_void_p), ("up_act", C.c_void_p)]
+                ("gate_act", C.c_void_p), ("up_act", C.c_void_p), ("status", C.c_void_p)]
+
+
+Q35_STATUS_POS_RANGE = 2
 
 
 class LinearAttentionLayer(C.Structure):

@@ -776,7 +776,17 @@ __global__ __launch_bounds__(kNT) void attn_merge_kernel(AttnArgs a) {
     __shared__ float stat[kNT / 64];
 
     const int32_t pos = attn_pos(a);
-    if (pos < 0 || (uint32_t)pos >= a.capacity) return;
+    if (pos < 0 || (uint32_t)pos >= a.capacity) {
+        // no attention for a position outside the cache: a zero output, and the
+        // caller's status word says so (the partial kernel wrote nothing)
+        if (cl == 0) {
+            a.gated_attn[h * D + d] = 0.f;
+            if (a.attn_out) a.attn_out[h * D + d] = 0.f;
+        }
+        if (a.status && blockIdx.x == 0 && blockIdx.y == 0 && t == 0)
+            __hip_atomic_fetch_or(a.status, Q35_STATUS_POS_RANGE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     const uint32_t nch = ((uint32_t)pos + a.chunk) / a.chunk;
 
     // partials of head h, dim d: part_acc[g][cc][i][d], chunk stride G*D floats

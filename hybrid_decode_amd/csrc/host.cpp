@@ -619,6 +619,7 @@ static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35Fo
         a.k_norm_out = s->k_norm_out;
         a.part_acc = reinterpret_cast<float*>(wsb + ws.acc_off);
         a.part_ml = reinterpret_cast<float*>(wsb + ws.ml_off);
+        a.status = s->status;
         a.capacity = kv->capacity;
         a.hq = c.num_heads;
         a.hkv = c.num_kv_heads;

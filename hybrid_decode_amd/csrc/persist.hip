@@ -27,6 +27,7 @@
 // the host reports the error.  The grid is one block per CU and launched
 // cooperatively, so all blocks are resident together.
 #include "gemv_core.h"
+#include "q35decode.h"
 #include "q35_device.h"
 #include "q35_internal.h"
 
@@ -81,7 +82,7 @@ struct PSync {
                 if (__ballot(!ok) == 0) break;
                 if (wall_clock64() - t0 > p->spin_ticks) {
                     failed = true;
-                    if (lane == 0) __hip_atomic_store(p->ctl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (lane == 0) __hip_atomic_fetch_or(p->ctl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
             }
@@ -520,6 +521,16 @@ Q35_DEV void st_merge(const AttnArgs& a, PSync& sy, uint32_t s) {
                 st_f32<true>(a.gated_attn, h * D + d, out * sigmoidf_(gate));
             }
         }
+    } else {
+        // positions[0] outside the cache: no attention this step.  The output is
+        // zero and the error word records it (q35_decode_check reports it).
+        for (uint32_t o = wave * gridDim.x + blockIdx.x; o < nout; o += gridDim.x * kPW)
+            if (lane == 0) {
+                if (a.attn_out) a.attn_out[o] = 0.f;
+                st_f32<true>(a.gated_attn, o, 0.f);
+            }
+        if (blockIdx.x == 0 && tid_x() == 0)
+            __hip_atomic_fetch_or(sy.p->ctl + 1, Q35_STATUS_POS_RANGE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     sy.arrive(s);
 }

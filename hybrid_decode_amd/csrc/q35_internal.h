@@ -148,6 +148,7 @@ struct AttnArgs {
     float* k_norm_out;       // optional tap (post-RoPE)
     float* part_acc;         // workspace: [Hkv][max_chunks][G][D]
     float* part_ml;          // workspace: [Hkv][max_chunks][G][2]
+    uint32_t* status;        // optional: Q35_STATUS_POS_RANGE is ORed in for a position out of range
     uint16_t* ks;            // Turbo8: bf16 K group scales [cap, Hkv, D/16] (kc then holds E4M3 codes)
     uint16_t* vs;            // Turbo8: bf16 V group scales; Lloyd-Max formats: E4M3 bytes [cap, Hkv, D/16]
                              // (kc/vc of a Lloyd-Max side hold packed indices [cap, Hkv, D*bits/8])

@@ -224,6 +224,8 @@ class FullScratchDev:
         self.t["workspace"] = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         s.workspace = ptr(self.t["workspace"])
         s.workspace_bytes = nbytes
+        self.t["status"] = torch.zeros(1, dtype=torch.int32, device=device)
+        s.status = ptr(self.t["status"])
         self.struct = s
 
 

@@ -236,7 +236,14 @@ typedef struct FullAttentionLayer {
  *   q_norm_out [q_only] (post-RoPE q), k_norm_out [kv_dim] (post-RoPE k),
  *   attn_out [q_only], o [hidden], x_norm2 [hidden], gate_act [intermediate],
  *   up_act [intermediate].
+ * Optional status (device uint32 [1], caller-owned, cleared by the caller):
+ *   the device-position entry (q35_forward_full_attention_devpos) ORs
+ *   Q35_STATUS_POS_RANGE into it when positions[0] lies outside
+ *   [0, capacity) at run time; that call then writes no KV row and its
+ *   attention output (gated_attn) is zero, so the step's result is not
+ *   the method's.  Without a status word the condition goes unreported.
  */
+#define Q35_STATUS_POS_RANGE 2u
 typedef struct FullAttentionScratch {
     float* q_full;
     float* k;
@@ -255,6 +262,7 @@ typedef struct FullAttentionScratch {
     float* x_norm2;
     float* gate_act;
     float* up_act;
+    uint32_t* status;
 } FullAttentionScratch;
 
 /* Workspace bytes one full-attention layer needs for caches of `capacity` tokens. */
@@ -531,9 +539,14 @@ void q35_decode_plan_release(Q35DecodePlan* plan);
 q35_status q35_decode_step(const Q35DecodePlan* plan, hipStream_t stream);
 
 /*
- * Synchronises the device and reads the plan's error word: 0 when every
- * inter-block wait so far completed; 1 when one gave up after its time limit
- * (the results of that step are invalid; create a new plan).
+ * Synchronises the device and reads the plan's error word, a set of bits
+ * accumulated over the plan's steps: 0 when every step ran as the method
+ * says; bit 0 (1) when an inter-block wait gave up after its time limit (the
+ * results of that step are invalid; create a new plan); bit 1
+ * (Q35_STATUS_POS_RANGE) when positions[0] lay outside [0, capacity) of a
+ * layer's cache, so that layer wrote no KV row and its attention output was
+ * zero (the token of that step is not the method's).  The kernel exits
+ * normally in both cases.
  */
 q35_status q35_decode_check(const Q35DecodePlan* plan, uint32_t* error_word);
 

@@ -26,7 +26,9 @@ TOL_GEMV_F16 = 1e-3
 # value (the rounding of a bf16 or fp32 store) plus ELEM_* times the RMS of the
 # oracle vector.  A single wrong element of typical size (about one RMS) fails
 # it, which a relative L2 bound of 2e-2 over 2560 elements would let pass.
-ELEM_BF16 = 0.15
+# Measured on MI355X: at most 0.002 RMS beyond one bf16 step for the 4B layers
+# (256 GDN steps, 64 full-attention steps, every layer of 16 stack tokens).
+ELEM_BF16 = 0.02
 ELEM_F32 = 1e-2
 
 

@@ -220,16 +220,33 @@ def test_full_layer_4b_bf16_64_steps_from_4096(rt, gen):
 
 
 def test_out_of_range_device_position_touches_nothing(rt, gen):
+    """A device position outside the cache writes no KV row, gives a zero
+    attention output and sets the position bit of the caller's status word;
+    a position inside leaves the word clear."""
+    from hybrid_decode_amd import binding as B
     cfg = synth.tiny("f32")
     layer = synth.full_layer(gen, cfg, "gpu.oor")
     kv = synth.kv_cache(gen, cfg, "gpu.oor", 8, 8)
     Ld, KVd = rt.FullLayerDev(layer), rt.KvCacheDev(kv)
     scr = rt.FullScratchDev(cfg, 8)
     inv = rt.inv_freq_dev(cfg)
+    x = rt.to_dev(gen.act("gpu.oor.x", (256,), "f32"))
     for p in (8, -1, 1 << 20):
         say(f"device position {p} with capacity 8")
+        scr.t["status"].zero_()
+        scr.t["gated_attn"].fill_(1.0)
         pos = torch.tensor([p], dtype=torch.int32, device="cuda")
-        rt.forward_full_attention(cfg, Ld, scr, KVd, inv, pos, rt.to_dev(gen.act("gpu.oor.x", (256,), "f32")), None)
+        rt.forward_full_attention(cfg, Ld, scr, KVd, inv, pos, x, None)
         torch.cuda.synchronize()
         h = KVd.to_host()
         assert np.array_equal(h["k"], kv["k"]) and np.array_equal(h["v"], kv["v"])
+        assert int(scr.t["status"].cpu()[0]) == B.Q35_STATUS_POS_RANGE
+        assert torch.count_nonzero(scr.t["gated_attn"]).item() == 0
+    say("device position 7 with capacity 8")
+    scr.t["status"].zero_()
+    kv2 = synth.kv_cache(gen, cfg, "gpu.oor", 8, 7)
+    KV2 = rt.KvCacheDev(kv2)
+    rt.forward_full_attention(cfg, Ld, scr, KV2, inv, torch.tensor([7], dtype=torch.int32, device="cuda"),
+                              x, None)
+    torch.cuda.synchronize()
+    assert int(scr.t["status"].cpu()[0]) == 0

@@ -59,6 +59,37 @@ def test_persistent_tiny_stack_16_tokens(rt, gen):
         assert rel(O.bf16_to_f64(h[side]), O.bf16_to_f64(kvs[1][side])) < 1e-2
 
 
+def test_persistent_plan_reports_a_position_past_the_cache(rt, gen):
+    """Stepping past a capacity-16 cache: the step at position 16 writes no KV
+    row, its attention output is zero, the kernel exits normally and the error
+    word carries the position bit (the earlier steps leave it clear)."""
+    from hybrid_decode_amd import binding as B
+    w = workloads.tiny_stack(gen, steps=1, capacity=16)
+    cfg, kinds = w["cfg"], w["kinds"]
+    Ls = [rt.GdnLayerDev(w["layers"][0]), rt.FullLayerDev(w["layers"][1])]
+    Ss = [rt.GdnStateDev(w["states"][0]), None]
+    KVs = [None, rt.KvCacheDev(w["kvs"][1])]
+    pos = torch.zeros(1, dtype=torch.int32, device="cuda")
+    plan = rt.DecodePlan(cfg, kinds, Ls, Ss, KVs, rt.inv_freq_dev(cfg), pos)
+    x = rt.to_dev(w["xs"][0])
+    for p in (14, 15):
+        say(f"persistent step at position {p} of 16")
+        plan.layer_input(0).copy_(x)
+        pos.fill_(p)
+        plan.step()
+        torch.cuda.synchronize()
+    assert plan.check() == 0
+    before = KVs[1].to_host()
+    say("persistent step at position 16 of 16")
+    plan.layer_input(0).copy_(x)
+    pos.fill_(16)
+    plan.step()
+    torch.cuda.synchronize()
+    assert plan.check() == B.Q35_STATUS_POS_RANGE
+    after = KVs[1].to_host()
+    assert np.array_equal(after["k"], before["k"]) and np.array_equal(after["v"], before["v"])
+
+
 def test_persistent_gdn_layer_4b_64_steps_and_state(rt, gen):
     """Config 2 through the persistent kernel (64 of its 256 steps)."""
     steps = 64
