@@ -12,7 +12,10 @@ from one replayed HIP graph.  Prints one JSON line (rank 0).
 With bf16 caches the line also carries "prefill": a prompt of --prefill-tokens
 tokens through the same stack with the multi-token prefill calls (timed after
 the decode, it overwrites the first cache rows), and the rate of its
-dequantising GEMM against the f16 matrix-core peak.
+dequantising GEMM against the f16 matrix-core peak.  "long_ctx" is decode at a
+long context (--long-ctx, default 65536 positions of KV in every full layer,
+--long-steps tokens) with the attention steps' own roofline.  "cpu_baseline"
+times whole tokens of the oracle on the host, weights dequantised once first.
 """
 import argparse
 import hashlib
@@ -119,45 +122,103 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(cfg, w, sample_note, kv="bf16"):
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def oracle_weights(w):
+    """Every quantised matrix of the stack as dense fp32, dequantised once
+    (the oracle's fp32 evaluation of stack-sized GEMVs); returns (layers, lm_head)."""
     import numpy as np
 
     import oracle as O
-    from synth import gdn_state
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    kinds = w["kinds"]
-    gi = kinds.index("gdn")
-    fi = kinds.index("full")
-    x = w["embed"][w["start_token"]]
+    ql = lambda l: {k: (O.QuantMatrix(v, np.float32) if isinstance(v, dict) and "codes" in v else v)
+                    for k, v in l.items()}
+    layers = [ql(l) for l in w["layers"]]
+    for l in layers:
+        for v in l.values():
+            if isinstance(v, O.QuantMatrix):
+                v.dense()
+    lm = O.QuantMatrix(w["lm_head"], np.float32)
+    lm.dense()
+    return layers, lm
+
+
+def oracle_token(cfg, w, layers, lm, states, kvs, token, pos, kv="bf16"):
+    """One whole token of the oracle: the layer loop, final norm, lm_head, greedy."""
+    import oracle as O
     inv = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
+    x = w["embed"][token]
+    for li, kind in enumerate(w["kinds"]):
+        if kind == "gdn":
+            y, states[li], _ = O.forward_linear_attention(cfg, layers[li], states[li], x)
+        elif kv == "bf16":
+            y, kvs[li], _ = O.forward_full_attention(cfg, layers[li], kvs[li], inv, x, pos)
+        elif kv == "turbo8":
+            from oracle import turbo8 as T8
+            y, kvs[li], _ = T8.forward_full_attention_turbo8(cfg, layers[li], kvs[li], inv, x, pos)
+        else:
+            from oracle import turbo_lm as TL
+            y, kvs[li], _ = TL.forward_full_attention(kv, cfg, layers[li], kvs[li], inv, x, pos)
+        x = O.f64_to_act(y, cfg.act_dtype)
+    return O.greedy(O.lm_head_logits(cfg, w["final_norm"], lm, O.act_to_f64(x, cfg.act_dtype)))
+
+
+def cpu_baseline(cfg, w, tokens, kv="bf16", n=3):
+    """The oracle as it stands, on whole tokens: dense fp32 weights cached once
+    (setup not timed), then n tokens at cache positions ctx, ctx + 1, ..., each
+    fed the token the GPU chose (teacher forcing); returns the baseline record
+    and the cached weights."""
     t0 = time.perf_counter()
-    O.forward_linear_attention(cfg, w["layers"][gi], w["states"][gi], x)
-    t_gdn = time.perf_counter() - t0
+    layers, lm = oracle_weights(w)
+    setup = time.perf_counter() - t0
+    states = list(w["states"])
+    kvs = [None if c is None else {k: v for k, v in c.items() if k not in ("capacity", "kv_dtype")}
+           for c in w["kvs"]]
     t0 = time.perf_counter()
-    kvd = {k: v for k, v in w["kvs"][fi].items() if k != "capacity"}
-    if kv == "turbo8":
-        from oracle import turbo8 as T8
-        T8.forward_full_attention_turbo8(cfg, w["layers"][fi], kvd, inv, x, w["ctx"])
-    elif kv != "bf16":
-        from oracle import turbo_lm as TL
-        kvd.pop("kv_dtype", None)
-        TL.forward_full_attention(kv, cfg, w["layers"][fi], kvd, inv, x, w["ctx"])
-    else:
-        O.forward_full_attention(cfg, w["layers"][fi], w["kvs"][fi], inv, x, w["ctx"])
-    t_full = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    logits = O.lm_head_logits(cfg, w["final_norm"], w["lm_head"], O.act_to_f64(x, "bf16"))
-    O.greedy(logits)
-    t_lm = time.perf_counter() - t0
-    n_gdn, n_full = kinds.count("gdn"), kinds.count("full")
-    t_tok = n_gdn * t_gdn + n_full * t_full + t_lm
-    return {"value": 1.0 / t_tok, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
-            "sample": sample_note.format(gdn=t_gdn, full=t_full, lm=t_lm, ng=n_gdn, nf=n_full),
-            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+    for i in range(n):
+        oracle_token(cfg, w, layers, lm, states, kvs, tokens[i], w["ctx"] + i, kv)
+    t_tok = (time.perf_counter() - t0) / n
+    rec = {"value": 1.0 / t_tok, "unit": "tok/s", "cores": blas_threads(), "kind": "oracle",
+           "sample": (f"{n} whole tokens of the oracle as it stands ({len(w['kinds'])} layers, final "
+                      f"norm, lm_head over {cfg.vocab}, greedy) at cache positions {w['ctx']}.."
+                      f"{w['ctx'] + n - 1} ({kv} KV), each fed the token the GPU chose; weights "
+                      f"dequantised once to fp32 ({setup:.0f} s, not timed), GEMVs in fp32 BLAS, "
+                      f"the rest float64: {t_tok:.2f} s per token"),
+           "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+    return rec, (layers, lm)
+
+
+def graph_kernel_nodes(graph):
+    """Kernel nodes of a captured graph (hipGraphGetNodes / hipGraphNodeGetType),
+    or None when the runtime cannot be queried."""
+    import ctypes as C
+    try:
+        import torch
+        try:
+            hip = C.CDLL("libamdhip64.so")
+        except OSError:
+            hip = C.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        h = C.c_void_p(graph.raw_cuda_graph())
+        n = C.c_size_t(0)
+        if hip.hipGraphGetNodes(h, None, C.byref(n)) != 0:
+            return None
+        nodes = (C.c_void_p * n.value)()
+        if hip.hipGraphGetNodes(h, nodes, C.byref(n)) != 0:
+            return None
+        count = 0
+        for nd in nodes:
+            t = C.c_int(-1)
+            if hip.hipGraphNodeGetType(C.c_void_p(nd), C.byref(t)) != 0:
+                return None
+            count += int(t.value == 0)  # hipGraphNodeTypeKernel
+        return count
+    except Exception:  # pragma: no cover
+        return None
 
 
 PEAK_MFMA_F16_TFLOPS = 2500.0
@@ -220,9 +281,10 @@ def prefill_gemm_rate(torch, B, rt, st, cfg, T, rounds=2):
     return us, 2.0 * T * cfg.intermediate * cfg.hidden
 
 
-def prefill_cpu_baseline(cfg, w, n=8):
+def prefill_cpu_baseline(cfg, w, layers, n=8):
     """The prefill oracle (the decode step looped over the tokens) on n tokens
-    through one GDN and one full-attention layer, composed over the stack."""
+    through one GDN and one full-attention layer (dense fp32 weights cached
+    beforehand), composed over the stack."""
     import numpy as np
 
     import oracle as O
@@ -233,17 +295,90 @@ def prefill_cpu_baseline(cfg, w, n=8):
     kv = {"k": np.zeros((n, cfg.num_kv_heads, cfg.head_dim), np.uint16),
           "v": np.zeros((n, cfg.num_kv_heads, cfg.head_dim), np.uint16)}
     t0 = time.perf_counter()
-    O.prefill.prefill_linear_attention(cfg, w["layers"][gi], w["states"][gi], x)
+    O.prefill.prefill_linear_attention(cfg, layers[gi], w["states"][gi], x)
     t_gdn = (time.perf_counter() - t0) / n
     t0 = time.perf_counter()
-    O.prefill.prefill_full_attention(cfg, w["layers"][fi], kv, inv, x, 0)
+    O.prefill.prefill_full_attention(cfg, layers[fi], kv, inv, x, 0)
     t_full = (time.perf_counter() - t0) / n
     t_tok = kinds.count("gdn") * t_gdn + kinds.count("full") * t_full
-    return 1.0 / t_tok, (f"float64 prefill oracle as it stands (the decode step looped over the "
-                         f"tokens; each call dequantises its layer once) on {n} tokens through one GDN "
-                         f"layer ({t_gdn:.3f}s/token) and one full layer at cache positions 0..{n - 1} "
-                         f"({t_full:.3f}s/token), composed over {kinds.count('gdn')} + "
-                         f"{kinds.count('full')} layers")
+    return 1.0 / t_tok, (f"prefill oracle as it stands (the decode step looped over the tokens; "
+                         f"dense fp32 weights cached, GEMVs in fp32 BLAS, the rest float64) on {n} "
+                         f"tokens through one GDN layer ({t_gdn:.3f}s/token) and one full layer at "
+                         f"cache positions 0..{n - 1} ({t_full:.3f}s/token), composed over "
+                         f"{kinds.count('gdn')} + {kinds.count('full')} layers")
+
+
+def long_context(torch, B, rt, synth, workloads, args, kv_bytes):
+    """Decode at a long context: the same 32-layer stack with every KV cache
+    filled to args.long_ctx positions, args.long_steps tokens from one replayed
+    graph; plus the attention steps alone (q35_attention_devpos: split, norms,
+    RoPE, append, split-K attention, merge and gate) timed on every full
+    layer's cache, the kernel the long context stresses."""
+    import numpy as np
+    ctx, K2, W2 = args.long_ctx, args.long_steps, 4
+    log(f"long context: generating the stack with KV at {ctx} positions")
+    w = workloads.stack_4b(synth.Gen(0), num_layers=args.layers, ctx=ctx, extra=W2 + K2 + 64, kv=args.kv)
+    cfg, kinds = w["cfg"], w["kinds"]
+    st = rt.DecodeStack(cfg, kinds, w["layers"], w["states"], w["kvs"], w["embed"], w["final_norm"],
+                        w["lm_head"], start_pos=ctx, start_token=w["start_token"],
+                        history_len=W2 + K2 + 8)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st.step(write_logits=False)
+    for _ in range(W2):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K2):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    tok_s = K2 / (ms / 1e3)
+    L_mid = ctx + W2 + K2 // 2 + 1
+    bpt = stack_bytes_per_token(cfg, st, kinds, L_mid, kv_bytes)
+    hist = st.history.cpu().numpy()[:W2 + K2]
+    assert np.all(hist >= 0) and np.all(hist < cfg.vocab), "decode produced invalid tokens"
+    log(f"long context {ctx}: {K2} tokens in {ms:.2f} ms: {ms / K2 * 1e3:.1f} us/token, {tok_s:.1f} tok/s, "
+        f"{bpt * tok_s / 1e9:.0f} GB/s")
+    # the attention steps alone, every full layer's cache in turn (the append
+    # rewrites row positions[0] with the same values each time)
+    s = rt.stream_ptr()
+    full = [i for i, k in enumerate(kinds) if k == "full"]
+    sc = st.full_scratch
+    call = lambda li: B.q35_attention_devpos(st.k, st.c, st.layers[li].struct, sc.struct,
+                                             st.kvs[li].struct, st.inv_freq.data_ptr(),
+                                             st.positions.data_ptr(), s)
+    for li in full:
+        call(li)
+    torch.cuda.synchronize()
+    R = 4
+    torch.cuda._sleep(100_000_000)
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for _ in range(R):
+        for li in full:
+            call(li)
+    a1.record()
+    torch.cuda.synchronize()
+    attn_us = a0.elapsed_time(a1) * 1e3 / (R * len(full))
+    L = int(st.positions.cpu()[0]) + 1
+    attn_bytes = int(L * cfg.kv_dim * 2 * kv_bytes)   # K and V rows read (the append included)
+    attn_gbs = attn_bytes / (attn_us * 1e-6) / 1e9
+    log(f"long context {ctx}: attention steps {attn_us:.1f} us per layer, {attn_gbs:.0f} GB/s")
+    out = {"ctx_start": ctx, "steps": K2, "warmup": W2, "value": round(tok_s, 2), "unit": "tok/s",
+           "ms_per_step": round(ms / K2, 4), "bytes_per_token": bpt,
+           "hbm_gbs": round(bpt * tok_s / 1e9, 1), "hbm_frac": round(bpt * tok_s / 1e9 / PEAK_HBM_GBS, 4),
+           "roofline": {"bound": "hbm",
+                        "kernel": "attn_partial_kernel + attn_merge_kernel (q35_attention_devpos)",
+                        "achieved": round(attn_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(attn_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                        "bytes_per_launch": attn_bytes, "us_per_launch": round(attn_us, 2)}}
+    del graph, st
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -257,6 +392,9 @@ def main():
     ap.add_argument("--dominant-rounds", type=int, default=4)
     ap.add_argument("--prefill-tokens", type=int, default=4096,
                     help="also time a prompt of this many tokens through the stack (0: skip)")
+    ap.add_argument("--long-ctx", type=int, default=65536,
+                    help="also time decode with every KV cache filled to this many positions (0: skip)")
+    ap.add_argument("--long-steps", type=int, default=32)
     ap.add_argument("--kv", choices=["bf16", "turbo8", "turbo4", "turbo3", "turbo2", "bf16k_turbo4v",
                                      "bf16k_turbo3v", "bf16k_turbo2v"], default="bf16",
                     help="KV cache format of the full-attention layers")
@@ -303,10 +441,12 @@ def main():
     log(f"resident weights {st.weight_bytes / 1e9:.3f} GB")
 
     # one decode token captured once, replayed every step
-    graph = torch.cuda.CUDAGraph()
+    graph = torch.cuda.CUDAGraph(keep_graph=True)
     with torch.cuda.graph(graph):
         st.step(write_logits=False)
-    log("graph captured")
+    launches = graph_kernel_nodes(graph)
+    graph.instantiate()
+    log(f"graph captured: {launches} kernel launches per token")
     for _ in range(W):
         graph.replay()
     torch.cuda.synchronize()
@@ -377,6 +517,9 @@ def main():
     log(f"device copy of {copy_bytes >> 20} MiB: {copy_gbs:.0f} GB/s (read + write)")
     traffic = measured_traffic()
 
+    gpu_tokens = [int(t) for t in hist[:4]]
+    first_token = w["start_token"]
+
     prefill = None
     if args.prefill_tokens > 0 and args.kv == "bf16":
         T = min(args.prefill_tokens, min(kv.capacity for kv in st.kvs if kv is not None))
@@ -412,7 +555,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",  # fp32 accumulation; x as f16 (HALF GEMV) or fp32, codes u8
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {
             "workload": (f"Qwen3.5-4B-shaped {args.layers}-layer hybrid stack "
@@ -423,7 +566,10 @@ def main():
             "intermediate": cfg.intermediate, "vocab": cfg.vocab, "batch": 1,
             "kv": args.kv,
             "storage": f"u8 codes + bf16 scale/bias per 64, bf16 activations, {kv_desc} KV, fp32 GDN state",
+            "arithmetic": ("GEMV products of f16 x (rounded per 16-element chunk) and exact f16 "
+                           "codes, fp32 sums; norms, softmax, recurrence and state in fp32"),
             "launch": "one HIP graph per token",
+            "launches_per_token": launches,
         },
         "bytes_per_token": bpt,
         "hbm_gbs": round(bpt * tok_s / 1e9, 1),
@@ -437,17 +583,20 @@ def main():
                      "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": dom_bytes, "us_per_launch": round(dom_us, 3)},
     }
+    if args.long_ctx > 0:
+        # the same stack with every KV cache filled to long_ctx positions
+        del graph, st
+        torch.cuda.empty_cache()
+        result["long_ctx"] = long_context(torch, B, rt, synth, workloads, args, kv_bytes)
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        note = ("float64 oracle as it stands (dequantises each matrix per call): one GDN layer "
-                "{gdn:.2f}s, one full-attention layer at ctx " + str(args.ctx) + " ({kv}) {full:.2f}s, "
-                "the lm_head + argmax {lm:.2f}s, each run once; tok/s = 1/({ng} GDN + {nf} full + "
-                "lm_head)").replace("{kv}", args.kv)
-        result["cpu_baseline"] = cpu_baseline(cfg, w, note, args.kv)
-        log(f"oracle: {result['cpu_baseline']['value']:.4f} tok/s")
+        log("timing the CPU oracle on whole tokens (weights dequantised once first)")
+        toks = [first_token] + gpu_tokens
+        result["cpu_baseline"], (olayers, _) = cpu_baseline(cfg, w, toks, args.kv)
+        log(f"oracle: {result['cpu_baseline']['value']:.4f} tok/s "
+            f"({result['cpu_baseline']['sample'].rsplit(': ', 1)[-1]})")
     if prefill is not None:
         if not args.no_cpu_baseline:
-            v, note = prefill_cpu_baseline(cfg, w)
+            v, note = prefill_cpu_baseline(cfg, w, olayers)
             prefill["cpu_baseline"] = {"value": v, "unit": "tok/s", "kind": "oracle", "sample": note,
                                        "cores": result["cpu_baseline"]["cores"]}
             log(f"prefill oracle: {v:.4f} tok/s")

@@ -44,6 +44,7 @@ EXPORTS = [
     "q35_full_attention_workspace_bytes", "q35_forward_full_attention",
     "q35_forward_full_attention_devpos", "q35_forward_linear_attention", "q35_embed_lookup",
     "q35_lm_head_workspace_bytes", "q35_lm_head_argmax", "q35_lm_head_argmax_noalloc",
+    "q35_attention_devpos",
     "q35_gate_up_swiglu", "q35_gemv",
     "q35_decode_workspace_bytes", "q35_decode_plan_create", "q35_decode_plan_release",
     "q35_decode_step", "q35_decode_check", "q35_decode_layer_input", "q35_decode_stage_layout",
@@ -182,6 +183,8 @@ def lib():
             "q35_lm_head_workspace_bytes": (st, [P(Qwen35ForwardConfig), P(sz)]),
             "q35_lm_head_argmax": (st, [vp, P(Qwen35ForwardConfig), vp, P(Q35QuantWeight), vp, vp,
                                         vp, sz, vp, vp, vp, u32, i32, vp, vp, vp]),
+            "q35_attention_devpos": (st, [vp, P(Qwen35ForwardConfig), P(FullAttentionLayer),
+                                          P(FullAttentionScratch), P(LayerKvCache), vp, vp, vp]),
             "q35_lm_head_argmax_noalloc": (st, [vp, P(Qwen35ForwardConfig), vp, P(Q35QuantWeight),
                                                 vp, vp, vp, vp, vp, u32, i32, vp, vp, vp]),
             "q35_gate_up_swiglu": (st, [vp, P(Qwen35ForwardConfig), vp, P(Q35QuantWeight),
@@ -317,6 +320,11 @@ def q35_lm_head_argmax(kernels, cfg, final_norm, lm_head, x, logits, workspace, 
                                     logits, workspace, workspace_bytes, tokens, positions,
                                     history, history_len, history_base, embed_table, x_next,
                                     stream))
+
+
+def q35_attention_devpos(kernels, cfg, layer, scratch, kv, inv_freq, positions, stream) -> None:
+    _check(lib().q35_attention_devpos(kernels, C.byref(cfg), C.byref(layer), C.byref(scratch),
+                                      C.byref(kv), inv_freq, positions, stream))
 
 
 def q35_lm_head_argmax_noalloc(kernels, cfg, final_norm, lm_head, x, logits, tokens, positions,

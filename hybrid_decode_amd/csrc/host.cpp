@@ -544,6 +544,61 @@ q35_status q35_full_attention_workspace_bytes(const Qwen35ForwardConfig* cfg, ui
     return ok();
 }
 
+// The attention steps of the full-attention forward (split, q/k norm, RoPE, KV
+// append, split-K attention, sigmoid gate) on the projections in the scratch.
+static q35_status launch_attention(const Qwen35Kernels* kernels, const Qwen35ForwardConfig& c,
+                                   const FullAttentionLayer* layer, const FullAttentionScratch* s,
+                                   const LayerKvCache* kv, const AttnWs& ws, const float* inv_freq,
+                                   const int32_t* positions, int64_t cache_pos,
+                                   uint32_t seq_len_attn, hipStream_t stream) {
+    AttnArgs a;
+    std::memset(&a, 0, sizeof(a));
+    const uint32_t G = c.num_heads / c.num_kv_heads;
+    uint8_t* wsb = static_cast<uint8_t*>(s->workspace);
+    a.q_full = s->q_full;
+    a.k = s->k;
+    a.v = s->v;
+    a.q_norm = layer->q_norm;
+    a.k_norm = layer->k_norm;
+    a.inv_freq = inv_freq;
+    a.positions = positions;
+    a.kc = static_cast<uint16_t*>(kv->k);
+    a.vc = static_cast<uint16_t*>(kv->v);
+    a.ks = static_cast<uint16_t*>(kv->k_scales);
+    a.vs = static_cast<uint16_t*>(kv->v_scales);
+    a.gated_attn = s->gated_attn;
+    a.attn_out = s->attn_out;
+    a.q_norm_out = s->q_norm_out;
+    a.k_norm_out = s->k_norm_out;
+    a.part_acc = reinterpret_cast<float*>(wsb + ws.acc_off);
+    a.part_ml = reinterpret_cast<float*>(wsb + ws.ml_off);
+    a.status = s->status;
+    a.capacity = kv->capacity;
+    a.hq = c.num_heads;
+    a.hkv = c.num_kv_heads;
+    a.rotary = c.rotary_dim;
+    a.max_chunks = attn_max_chunks(c, kv->capacity);
+    a.eps = c.rms_eps;
+    a.scale = 1.0f / std::sqrt((float)c.head_dim);
+    a.sparse_v_log2 = (kv->dtype == Q35_KV_BF16 || kv->sparse_v <= 0.0f) ? -INFINITY
+                                                                          : std::log2(kv->sparse_v);
+    if (kv_lm_bits(kv->dtype)) std::memcpy(a.lm_levels, kernels->lm[kv_lm_bits(kv->dtype)].v, sizeof(a.lm_levels));
+    uint32_t grid;
+    if (cache_pos >= 0) {
+        a.host_pos = (int32_t)cache_pos;
+        a.chunk = attn_chunk(c, seq_len_attn);
+        grid = (seq_len_attn + a.chunk - 1) / a.chunk;
+    } else {
+        a.host_pos = -1;
+        a.chunk = attn_chunk(c, kv->capacity);
+        grid = (kv->capacity + a.chunk - 1) / a.chunk;
+    }
+    if (grid > a.max_chunks) return fail(Q35_ERR_INVALID_ARG, "internal: %u chunks > %u", grid, a.max_chunks);
+    Q35_HIP(attn_launch(c.head_dim, G, a, grid, kv->dtype, stream), "attention");
+    (void)G;
+    return Q35_OK;
+}
+
 static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
                                     const FullAttentionLayer* layer,
                                     const FullAttentionScratch* s, const LayerKvCache* kv,
@@ -597,53 +652,8 @@ static q35_status forward_full_impl(const Qwen35Kernels* kernels, const Qwen35Fo
         Q35_TRY(b.launch((uint32_t)kernels->num_cu, stream, "q/k/v GEMV"));
     }
     // 2. split, q/k norm, RoPE, KV append, split-K attention, sigmoid gate
-    {
-        AttnArgs a;
-        std::memset(&a, 0, sizeof(a));
-        const uint32_t G = c.num_heads / c.num_kv_heads;
-        uint8_t* wsb = static_cast<uint8_t*>(s->workspace);
-        a.q_full = s->q_full;
-        a.k = s->k;
-        a.v = s->v;
-        a.q_norm = layer->q_norm;
-        a.k_norm = layer->k_norm;
-        a.inv_freq = inv_freq;
-        a.positions = positions;
-        a.kc = static_cast<uint16_t*>(kv->k);
-        a.vc = static_cast<uint16_t*>(kv->v);
-        a.ks = static_cast<uint16_t*>(kv->k_scales);
-        a.vs = static_cast<uint16_t*>(kv->v_scales);
-        a.gated_attn = s->gated_attn;
-        a.attn_out = s->attn_out;
-        a.q_norm_out = s->q_norm_out;
-        a.k_norm_out = s->k_norm_out;
-        a.part_acc = reinterpret_cast<float*>(wsb + ws.acc_off);
-        a.part_ml = reinterpret_cast<float*>(wsb + ws.ml_off);
-        a.status = s->status;
-        a.capacity = kv->capacity;
-        a.hq = c.num_heads;
-        a.hkv = c.num_kv_heads;
-        a.rotary = c.rotary_dim;
-        a.max_chunks = attn_max_chunks(c, kv->capacity);
-        a.eps = c.rms_eps;
-        a.scale = 1.0f / std::sqrt((float)c.head_dim);
-        a.sparse_v_log2 = (kv->dtype == Q35_KV_BF16 || kv->sparse_v <= 0.0f) ? -INFINITY
-                                                                              : std::log2(kv->sparse_v);
-        if (kv_lm_bits(kv->dtype)) std::memcpy(a.lm_levels, kernels->lm[kv_lm_bits(kv->dtype)].v, sizeof(a.lm_levels));
-        uint32_t grid;
-        if (cache_pos >= 0) {
-            a.host_pos = (int32_t)cache_pos;
-            a.chunk = attn_chunk(c, seq_len_attn);
-            grid = (seq_len_attn + a.chunk - 1) / a.chunk;
-        } else {
-            a.host_pos = -1;
-            a.chunk = attn_chunk(c, kv->capacity);
-            grid = (kv->capacity + a.chunk - 1) / a.chunk;
-        }
-        if (grid > a.max_chunks) return fail(Q35_ERR_INVALID_ARG, "internal: %u chunks > %u", grid, a.max_chunks);
-        Q35_HIP(attn_launch(c.head_dim, G, a, grid, kv->dtype, stream), "attention");
-        (void)G;
-    }
+    Q35_TRY(launch_attention(kernels, c, layer, s, kv, ws, inv_freq, positions, cache_pos, seq_len_attn,
+                             stream));
     // 3. o projection + residual
     {
         GemvBuild b(kOpOProj, q_only(c), f32);
@@ -682,6 +692,30 @@ q35_status q35_forward_full_attention_devpos(const Qwen35Kernels* kernels,
                                              hipStream_t stream, void** out) {
     return forward_full_impl(kernels, cfg, layer, scratch, kv, inv_freq, positions, x_in, -1, 0,
                              stream, out);
+}
+
+q35_status q35_attention_devpos(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                                const FullAttentionLayer* layer, const FullAttentionScratch* s,
+                                const LayerKvCache* kv, const float* inv_freq,
+                                const int32_t* positions, hipStream_t stream) {
+    Q35_TRY(check_kernels(kernels));
+    if (!cfg || !layer || !s || !kv) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    Q35_TRY(q35_config_validate(cfg));
+    const Qwen35ForwardConfig& c = *cfg;
+    Q35_TRY(check_kv(*kv, true));
+    Q35_TRY(need(inv_freq, "inv_freq", false));
+    Q35_TRY(need(positions, "positions", false));
+    Q35_TRY(check_full_layer(c, *layer));
+    Q35_TRY(need(s->q_full, "scratch.q_full"));
+    Q35_TRY(need(s->k, "scratch.k"));
+    Q35_TRY(need(s->v, "scratch.v"));
+    Q35_TRY(need(s->gated_attn, "scratch.gated_attn"));
+    Q35_TRY(need(s->workspace, "scratch.workspace"));
+    const AttnWs ws = attn_ws_layout(c, kv->capacity);
+    if (s->workspace_bytes < ws.total)
+        return fail(Q35_ERR_INVALID_ARG, "workspace %zu bytes < %zu required", s->workspace_bytes, ws.total);
+    Q35_TRY(launch_attention(kernels, c, layer, s, kv, ws, inv_freq, positions, -1, 0, stream));
+    return ok();
 }
 
 q35_status q35_forward_linear_attention(const Qwen35Kernels* kernels,

@@ -299,8 +299,9 @@ q35_status q35_forward_full_attention(const Qwen35Kernels* kernels, const Qwen35
  * Same as q35_forward_full_attention, but the cache position is read on the
  * device from positions[0] (seq_len_attn = positions[0] + 1), so one captured
  * HIP graph replays every decode step.  A device position outside
- * [0, capacity) skips the append and the attention (the output is then
- * meaningless but no memory outside the buffers is touched).
+ * [0, capacity) skips the append and the attention: the attention output is
+ * zero, no memory outside the buffers is touched, and scratch->status (when
+ * given) receives Q35_STATUS_POS_RANGE.
  */
 q35_status q35_forward_full_attention_devpos(const Qwen35Kernels* kernels,
                                              const Qwen35ForwardConfig* cfg,
@@ -309,6 +310,22 @@ q35_status q35_forward_full_attention_devpos(const Qwen35Kernels* kernels,
                                              const LayerKvCache* kv, const float* inv_freq,
                                              const int32_t* positions, const void* x_in,
                                              hipStream_t stream, void** out);
+
+/*
+ * Kernel-level export: the attention steps of forward_full_attention alone
+ * (full_attention.rs page: the q/gate split, the q/k RMSNorm, partial RoPE, the
+ * KV append, attention_decode and sigmoid_gate), on the projections already in
+ * scratch->q_full, k and v, with the cache position read from positions[0] as
+ * in q35_forward_full_attention_devpos.  Writes the appended row, the
+ * attention partials in scratch->workspace, scratch->gated_attn and the
+ * optional taps (q_norm_out, k_norm_out, attn_out) and status.  Two launches
+ * (per-chunk partials, then the merge with the gate).  Errors as
+ * q35_forward_full_attention_devpos.
+ */
+q35_status q35_attention_devpos(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                                const FullAttentionLayer* layer, const FullAttentionScratch* scratch,
+                                const LayerKvCache* kv, const float* inv_freq,
+                                const int32_t* positions, hipStream_t stream);
 
 /* ------------------------------------------------------------------ GDN layer */
 
