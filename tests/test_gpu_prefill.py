@@ -353,7 +353,7 @@ def test_prefill_full_fills_the_cache_to_capacity(rt, gen):
 
 # --------------------------------------------------------------------------- 4096-token prompts
 
-BIG_T, PREFIX = 4096, 300
+BIG_T = 4096
 
 
 # One call of 4096 tokens against two of 2048: the projections split different
@@ -369,12 +369,19 @@ def _split_rel(a, b):
     return _rows_rel(a, b), bool(np.array_equal(a, b))
 
 
+def _dense32(layer):
+    """The layer with its quantised matrices as fp32 dense matrices (the oracle's
+    fp32 evaluation of large GEMVs), so a 4096-token loop dequantises each once."""
+    return {k: (O.QuantMatrix(v, np.float32) if isinstance(v, dict) and "codes" in v else v)
+            for k, v in layer.items()}
+
+
 def test_prefill_gdn_4b_4096_tokens(rt, gen):
     """The benchmark's prompt through one 4B GDN layer (16 row tiles per GEMM, 64
-    chunks).  A token's output depends on the tokens before it only, so the first
-    300 outputs (two row tiles, four whole chunks and a ragged fifth) are checked
-    against the oracle's loop over those 300 tokens; all 4096 outputs and the final
-    state against the same prompt sent as two calls of 2048 tokens (SPLIT_*)."""
+    chunks): all 4096 outputs (bf16 bar) and the final GDN and conv states (fp32
+    bar) against the oracle's loop over the 4096 tokens; all 4096 outputs and the
+    final state also against the same
+    prompt sent as two calls of 2048 tokens (SPLIT_*)."""
     cfg = synth.qwen3_5_4b("bf16")
     layer = synth.gdn_layer(gen, cfg, "pf.big.g")
     st = synth.gdn_state(gen, cfg, "pf.big.g", 0.05, 0.5)
@@ -391,14 +398,22 @@ def test_prefill_gdn_4b_4096_tokens(rt, gen):
         f"state rel {r_st:.1e} (bit-identical {same_st})")
     assert r_out < SPLIT_BF16 and r_st < SPLIT_F32
     assert rel(s2["conv1d_state"], gst["conv1d_state"]) < SPLIT_F32
-    ref, _, _ = O.prefill.prefill_linear_attention(cfg, layer, st, x[:PREFIX])
-    assert _rows_rel(out[:PREFIX], ref) < TOL_BF16
+    say(f"oracle loop over {BIG_T} tokens")
+    ref, ost, _ = O.prefill.prefill_linear_attention(cfg, _dense32(layer), st, x)
+    r_all = _rows_rel(out, ref)
+    r_last = _rows_rel(out[-64:], ref[-64:])
+    r_gst = rel(gst["gdn_state"], ost["gdn_state"])
+    r_cst = rel(gst["conv1d_state"], ost["conv1d_state"])
+    say(f"  against the oracle: outputs rel {r_all:.2e} (last chunk {r_last:.2e}), GDN state rel "
+        f"{r_gst:.2e}, conv state rel {r_cst:.2e}")
+    # measured on MI355X: outputs 2.0e-3, GDN state 4.6e-4, conv state 2.8e-4
+    assert r_all < TOL_BF16 and r_gst < TOL_F32 and r_cst < TOL_F32
 
 
 def test_prefill_full_4b_4096_tokens(rt, gen):
     """The benchmark's prompt through one 4B full-attention layer from an empty cache
-    of exactly 4096 rows (128 query tiles, up to 64 key tiles per tile): the first
-    300 outputs and cache rows against the oracle's loop over those tokens; all 4096
+    of exactly 4096 rows (128 query tiles, up to 64 key tiles per tile): all 4096
+    outputs and cache rows against the oracle's loop over the 4096 tokens; all 4096
     outputs and the whole cache against two calls of 2048 tokens, the second at
     cache position 2048 (SPLIT_*)."""
     cfg = synth.qwen3_5_4b("bf16")
@@ -422,9 +437,13 @@ def test_prefill_full_4b_4096_tokens(rt, gen):
         say(f"  cache {s}: rel {r_kv:.1e} (bit-identical {same_kv})")
         assert r_kv < SPLIT_BF16, s
     inv = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
-    ref, rkv, _ = O.prefill.prefill_full_attention(cfg, layer, kv, inv, x[:PREFIX], 0)
-    assert _rows_rel(out[:PREFIX], ref) < TOL_BF16
+    say(f"oracle loop over {BIG_T} tokens")
+    ref, rkv, _ = O.prefill.prefill_full_attention(cfg, _dense32(layer), kv, inv, x, 0)
+    r_all = _rows_rel(out, ref)
+    say(f"  against the oracle: outputs rel {r_all:.2e} (last 64 rows {_rows_rel(out[-64:], ref[-64:]):.2e})")
+    assert r_all < TOL_BF16
     for s in ("k", "v"):
-        g = O.bf16_to_f64(after[s][:PREFIX])
-        r = O.bf16_to_f64(rkv[s][:PREFIX])
-        assert rel(g, r) < 4e-3, s
+        g = O.bf16_to_f64(after[s]).reshape(BIG_T, -1)
+        r = O.bf16_to_f64(rkv[s]).reshape(BIG_T, -1)
+        say(f"  cache {s} against the oracle: rel {_rows_rel(g, r):.2e}")
+        assert _rows_rel(g, r) < 4e-3, s
