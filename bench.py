@@ -395,6 +395,8 @@ def main():
     ap.add_argument("--long-ctx", type=int, default=65536,
                     help="also time decode with every KV cache filled to this many positions (0: skip)")
     ap.add_argument("--long-steps", type=int, default=32)
+    ap.add_argument("--path", choices=["layers", "xcd"], default="layers",
+                    help="decode launches: per-layer kernels, or the XCD-split plan (q35_xcd_*)")
     ap.add_argument("--kv", choices=["bf16", "turbo8", "turbo4", "turbo3", "turbo2", "bf16k_turbo4v",
                                      "bf16k_turbo3v", "bf16k_turbo2v"], default="bf16",
                     help="KV cache format of the full-attention layers")
@@ -436,9 +438,9 @@ def main():
     log(f"generated in {time.time() - t0:.1f}s; uploading")
     st = rt.DecodeStack(cfg, kinds, w["layers"], w["states"], w["kvs"], w["embed"],
                         w["final_norm"], w["lm_head"], start_pos=args.ctx,
-                        start_token=w["start_token"], history_len=W + K + 8)
+                        start_token=w["start_token"], history_len=W + K + 8, xcd=args.path == "xcd")
     torch.cuda.synchronize()
-    log(f"resident weights {st.weight_bytes / 1e9:.3f} GB")
+    log(f"resident weights {st.weight_bytes / 1e9:.3f} GB; decode path: {args.path}")
 
     # one decode token captured once, replayed every step
     graph = torch.cuda.CUDAGraph(keep_graph=True)
@@ -463,6 +465,9 @@ def main():
     bpt = stack_bytes_per_token(cfg, st, kinds, L_mid, kv_bytes)
     hist = st.history.cpu().numpy()[:W + K]
     assert np.all(hist >= 0) and np.all(hist < cfg.vocab), "decode produced invalid tokens"
+    if st.plan is not None:
+        err = st.plan.check()
+        assert err == 0, f"the decode plan reported error word {err:#x}"
     log(f"{K} tokens in {ms:.2f} ms: {ms_per_step * 1e3:.1f} us/token, {tok_s:.1f} tok/s, "
         f"{bpt * tok_s / 1e9:.0f} GB/s")
 

@@ -51,6 +51,8 @@ EXPORTS = [
     "q35_decode_stage_times", "q35_turbo8_quantize", "q35_fp8_e4m3_table",
     "q35_turbo_codebook", "q35_turbo_quantize", "q35_prefill_workspace_bytes",
     "q35_prefill_linear_attention", "q35_prefill_full_attention", "q35_prefill_gemm",
+    "q35_xcd_workspace_bytes", "q35_xcd_plan_create", "q35_xcd_plan_release", "q35_xcd_step",
+    "q35_xcd_check", "q35_xcd_layer_input", "q35_xcd_buffers",
 ]
 
 Q35_LAYER_LINEAR = 0
@@ -104,6 +106,7 @@ class FullAttentionScratch(C.Structure):
 
 
 Q35_STATUS_POS_RANGE = 2
+Q35_STATUS_XCD_MAP = 4
 
 
 class LinearAttentionLayer(C.Structure):
@@ -141,6 +144,13 @@ class Q35DecodeStackDesc(C.Structure):
                 ("lm_head", C.POINTER(Q35QuantWeight)), ("final_norm", C.c_void_p),
                 ("embed", C.c_void_p), ("tokens", C.c_void_p), ("logits", C.c_void_p),
                 ("history", C.c_void_p), ("history_len", C.c_uint32), ("history_base", C.c_int32)]
+
+
+class Q35XcdBuffers(C.Structure):
+    _fields_ = [("x_in", C.c_void_p), ("qkv_conv", C.c_void_p), ("z", C.c_void_p),
+                ("gate", C.c_void_p), ("beta", C.c_void_p), ("y", C.c_void_p),
+                ("out_parts", C.c_void_p), ("mlp_act", C.c_void_p), ("mlp_parts", C.c_void_p),
+                ("x_mid", C.c_void_p), ("x_resid", C.c_void_p)]
 
 
 DUMP_FN = C.CFUNCTYPE(None, C.c_void_p, C.c_char_p, C.c_void_p, C.c_uint32)
@@ -210,6 +220,14 @@ def lib():
             "q35_prefill_full_attention": (st, [vp, P(Qwen35ForwardConfig), P(FullAttentionLayer),
                                                 P(LayerKvCache), vp, vp, u32, u32, vp, vp, sz, vp]),
             "q35_prefill_gemm": (st, [vp, P(Q35QuantWeight), vp, u32, vp, vp, sz, vp]),
+            "q35_xcd_workspace_bytes": (st, [vp, P(Qwen35ForwardConfig), P(Q35DecodeStackDesc), P(sz)]),
+            "q35_xcd_plan_create": (st, [vp, P(Qwen35ForwardConfig), P(Q35DecodeStackDesc), vp, sz,
+                                         P(vp)]),
+            "q35_xcd_plan_release": (None, [vp]),
+            "q35_xcd_step": (st, [vp, vp]),
+            "q35_xcd_check": (st, [vp, P(u32)]),
+            "q35_xcd_layer_input": (st, [vp, u32, P(vp)]),
+            "q35_xcd_buffers": (st, [vp, P(Q35XcdBuffers)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -436,3 +454,42 @@ def q35_prefill_full_attention(kernels, cfg, layer, kv, inv_freq, x_in, n_tokens
 
 def q35_prefill_gemm(kernels, w, x_f16, m: int, y, workspace, workspace_bytes: int, stream) -> None:
     _check(lib().q35_prefill_gemm(kernels, C.byref(w), x_f16, m, y, workspace, workspace_bytes, stream))
+
+
+def q35_xcd_workspace_bytes(kernels, cfg, desc) -> int:
+    b = C.c_size_t()
+    _check(lib().q35_xcd_workspace_bytes(kernels, C.byref(cfg), C.byref(desc), C.byref(b)))
+    return b.value
+
+
+def q35_xcd_plan_create(kernels, cfg, desc, workspace, workspace_bytes) -> int:
+    h = C.c_void_p()
+    _check(lib().q35_xcd_plan_create(kernels, C.byref(cfg), C.byref(desc), workspace, workspace_bytes,
+                                     C.byref(h)))
+    return h.value
+
+
+def q35_xcd_plan_release(plan) -> None:
+    lib().q35_xcd_plan_release(plan)
+
+
+def q35_xcd_step(plan, stream) -> None:
+    _check(lib().q35_xcd_step(plan, stream))
+
+
+def q35_xcd_check(plan) -> int:
+    e = C.c_uint32()
+    _check(lib().q35_xcd_check(plan, C.byref(e)))
+    return e.value
+
+
+def q35_xcd_layer_input(plan, layer: int) -> int:
+    x = C.c_void_p()
+    _check(lib().q35_xcd_layer_input(plan, layer, C.byref(x)))
+    return x.value
+
+
+def q35_xcd_buffers(plan) -> Q35XcdBuffers:
+    b = Q35XcdBuffers()
+    _check(lib().q35_xcd_buffers(plan, C.byref(b)))
+    return b

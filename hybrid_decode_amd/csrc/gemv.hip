@@ -85,7 +85,8 @@ hipError_t gemv_launch(int op, uint32_t k, bool half, const GemvArgs& a, uint32_
     switch (op) {
         case kOpPlain: return gemv_launch_plain(op, k, half, xreg, a, blocks, stream);
         case kOpInGdn:
-        case kOpInFull: return gemv_launch_in(op, k, half, xreg, a, blocks, stream);
+        case kOpInFull:
+        case kOpInFullP: return gemv_launch_in(op, k, half, xreg, a, blocks, stream);
         case kOpOutGated:
         case kOpOProj: return gemv_launch_out(op, k, half, xreg, a, blocks, stream);
         case kOpGateUp:
@@ -99,7 +100,8 @@ const void* gemv_kernel_ptr(int op, uint32_t k, bool half, bool xreg) {
     switch (op) {
         case kOpPlain: return gemv_ptr_plain(op, k, half, xreg);
         case kOpInGdn:
-        case kOpInFull: return gemv_ptr_in(op, k, half, xreg);
+        case kOpInFull:
+        case kOpInFullP: return gemv_ptr_in(op, k, half, xreg);
         case kOpOutGated:
         case kOpOProj: return gemv_ptr_out(op, k, half, xreg);
         case kOpGateUp:

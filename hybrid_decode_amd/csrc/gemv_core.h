@@ -67,46 +67,29 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 template <int OP>
 struct Op;
-template <>
-struct Op<kOpPlain> {
-    static constexpr bool PAIRED = false;
-    static constexpr int PRO = kProLoadF32, NSEG = 1;
+// PRO: the prologue; NSEG: segments; EPI: the operation whose epilogues the
+// segments run, segment SI running that operation's segment esi(SI).
+template <int EPI_, int PRO_, int NSEG_, bool PAIRED_ = false>
+struct OpT {
+    static constexpr bool PAIRED = PAIRED_;
+    static constexpr int PRO = PRO_, NSEG = NSEG_, EPI = EPI_;
+    static constexpr int esi(int si) { return si; }
 };
-template <>
-struct Op<kOpInGdn> {  // segments: qkv (conv), z, a (gate), b (beta)
-    static constexpr bool PAIRED = false;
-    static constexpr int PRO = kProRmsAct, NSEG = 4;
+template <> struct Op<kOpPlain> : OpT<kOpPlain, kProLoadF32, 1> {};
+template <> struct Op<kOpInGdn> : OpT<kOpInGdn, kProRmsAct, 4> {};  // qkv (conv), z, a (gate), b (beta)
+template <> struct Op<kOpInFull> : OpT<kOpInFull, kProRmsAct, 3> {};  // q, k, v
+template <> struct Op<kOpOutGated> : OpT<kOpOutGated, kProGatedNorm, 1> {};
+template <> struct Op<kOpOProj> : OpT<kOpOProj, kProLoadF32, 1> {};
+template <> struct Op<kOpGateUp> : OpT<kOpGateUp, kProRmsF32, 1, true> {};
+template <> struct Op<kOpDown> : OpT<kOpDown, kProLoadF32, 1> {};
+template <> struct Op<kOpLmHead> : OpT<kOpLmHead, kProRmsAct, 1> {};
+template <> struct Op<kOpInFullP> : OpT<kOpInFull, kProRmsParts, 3> {};
+template <> struct Op<kOpInGdnX> : OpT<kOpInGdn, kProRmsParts, 6> {  // q, k, v (conv), z, a, b
+    static constexpr int esi(int si) { return si < 3 ? 0 : si - 2; }
 };
-template <>
-struct Op<kOpInFull> {  // segments: q, k, v
-    static constexpr bool PAIRED = false;
-    static constexpr int PRO = kProRmsAct, NSEG = 3;
-};
-template <>
-struct Op<kOpOutGated> {
-    static constexpr bool PAIRED = false;
-    static constexpr int PRO = kProGatedNorm, NSEG = 1;
-};
-template <>
-struct Op<kOpOProj> {
-    static constexpr bool PAIRED = false;
-    static constexpr int PRO = kProLoadF32, NSEG = 1;
-};
-template <>
-struct Op<kOpGateUp> {
-    static constexpr bool PAIRED = true;
-    static constexpr int PRO = kProRmsF32, NSEG = 1;
-};
-template <>
-struct Op<kOpDown> {
-    static constexpr bool PAIRED = false;
-    static constexpr int PRO = kProLoadF32, NSEG = 1;
-};
-template <>
-struct Op<kOpLmHead> {
-    static constexpr bool PAIRED = false;
-    static constexpr int PRO = kProRmsAct, NSEG = 1;
-};
+template <> struct Op<kOpGateUpX> : OpT<kOpGateUp, kProRmsParts, 1, true> {};
+template <> struct Op<kOpOutPart> : OpT<kOpPlain, kProGatedNorm, 1> {};
+template <> struct Op<kOpDownPart> : OpT<kOpPlain, kProLoadF32, 1> {};
 
 template <int K, bool PAIRED>
 struct Geo {
@@ -203,6 +186,8 @@ Q35_DEV void with_seg(const GemvArgs& a, uint32_t g, F&& f) {
         if constexpr (NSEG > 1) if (si == 1) f(a.seg[1], SegIdx<1>{});
         if constexpr (NSEG > 2) if (si == 2) f(a.seg[2], SegIdx<2>{});
         if constexpr (NSEG > 3) if (si == 3) f(a.seg[3], SegIdx<3>{});
+        if constexpr (NSEG > 4) if (si == 4) f(a.seg[4], SegIdx<4>{});
+        if constexpr (NSEG > 5) if (si == 5) f(a.seg[5], SegIdx<5>{});
     }
 }
 
@@ -237,7 +222,9 @@ struct ProRegs {
 #endif
 constexpr int kAuxXPersist = Q35_PERSIST_X_AUX;
 
-template <int K, int PRO, bool HALF, int NT, bool COH = false>
+// COH: x (and z) were written by other blocks of the same launch and are read
+// with cache policy XAUX (device-coherent, or L2 for blocks of one XCD).
+template <int K, int PRO, bool HALF, int NT, bool COH = false, int XAUX = kAuxXPersist>
 Q35_DEV void prologue_issue(const GemvPro& p, ProRegs<K, PRO, NT>& r) {
     constexpr int KC = K / 16, MC = pro_chunks<K, NT>();
     constexpr bool X_BF16 = (PRO == kProRmsAct) && HALF;  // the residual stream is bf16 for HALF
@@ -255,11 +242,11 @@ Q35_DEV void prologue_issue(const GemvPro& p, ProRegs<K, PRO, NT>& r) {
                 if constexpr (X_BF16) {
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
-                        r.x[m][j] = ld_b128<kAuxXPersist>(rx, 32u * cc + 16u * j);
+                        r.x[m][j] = ld_b128<XAUX>(rx, 32u * cc + 16u * j);
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        r.x[m][j] = ld_b128<kAuxXPersist>(rx, 64u * cc + 16u * j);
+                        r.x[m][j] = ld_b128<XAUX>(rx, 64u * cc + 16u * j);
                 }
                 if constexpr (PRO == kProRmsAct || PRO == kProRmsF32) {
                     r.w[m][0] = ld_b128<0>(rw, 32u * cc);
@@ -268,7 +255,7 @@ Q35_DEV void prologue_issue(const GemvPro& p, ProRegs<K, PRO, NT>& r) {
                 if constexpr (PRO == kProGatedNorm) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        r.z[m][j] = ld_b128<kAuxXPersist>(rz, 64u * cc + 16u * j);
+                        r.z[m][j] = ld_b128<XAUX>(rz, 64u * cc + 16u * j);
                     const uint32_t wo = ((16u * cc) % p.head_dim) * 2u;
                     r.w[m][0] = ld_b128<0>(rw, wo);
                     r.w[m][1] = ld_b128<0>(rw, wo + 16u);
@@ -418,12 +405,12 @@ Q35_DEV void read_chunk(const uint4* ximg, const float2* xab, int cc, float v[16
 // every row's dot product is multiplied by (1/rms for the RMS prologues, else 1).
 template <int K, int PRO, bool HALF, int NT>
 Q35_DEV float prologue_build(const GemvPro& p, const ProRegs<K, PRO, NT>& r, uint4* ximg,
-                             float2* xab, float* red) {
+                             float2* xab, float* red, bool lead) {
     constexpr int KC = K / 16, MC = pro_chunks<K, NT>(), NW = NT / 64;
     constexpr bool X_BF16 = (PRO == kProRmsAct) && HALF;
     constexpr bool RMS = (PRO == kProRmsAct || PRO == kProRmsF32);
     const int t = tid_x(), lane = t & 63, wid = t >> 6;
-    const bool tap = (p.tap != nullptr) && blockIdx.x == 0;
+    const bool tap = (p.tap != nullptr) && lead;
     float ss = 0.f;
 
 #pragma unroll
@@ -504,6 +491,154 @@ Q35_DEV float prologue_build(const GemvPro& p, const ProRegs<K, PRO, NT>& r, uin
     return post;
 }
 
+// ---------------------------------------------------------------- sum-of-partials prologue
+
+// kProRmsParts.  The residual stream arrives as a base vector plus up to eight
+// fp32 partial vectors (one per XCD of a column-split GEMV); x is their sum,
+// added in a fixed order (base, then partial 0, 1, ...), so every block forms
+// the same values.  Thread t owns quads (4 elements) t, t + NT, ...; the first
+// round of quads is loaded with the other early loads and later rounds (K/4 >
+// NT) where they are summed.  Out-of-range offsets (quads past the end,
+// partials past nparts) read zero through the buffer ranges, so the loads are
+// branch-free.  The sum goes to an fp32 staging area in LDS, then the image is
+// built from it as in the RMS prologues; block 0 writes the sum out.
+constexpr int kMaxParts = 8;
+
+template <int K, int NT>
+struct PartsRegs {
+    static constexpr int NQ = K / 4, MQ = (NQ + NT - 1) / NT, MC = pro_chunks<K, NT>();
+    uint4 b;              // base quad: 4 fp32, or 4 bf16 in .x/.y
+    uint4 p[kMaxParts];   // the partials' quads
+    uint4 w[MC][2];       // 16 bf16 norm weights per chunk
+};
+
+template <int K>
+Q35_DEV void parts_load(const GemvPro& p, int q, uint4& b, uint4 (&pp)[kMaxParts]) {
+    constexpr uint32_t NQ = K / 4, kPast = 0xFFFFFFF0u;
+    const bool live = (uint32_t)q < NQ;
+    if (p.x_f32) {
+        b = ld_b128<0>(rsrc(p.x, K * 4u), live ? 16u * q : kPast);
+    } else {
+        const uint2 h = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                      rsrc(p.x, K * 2u), live ? 8u * q : kPast, 0, 0));
+        b = make_uint4(h.x, h.y, 0u, 0u);
+    }
+    const auto rp = rsrc(p.parts, p.parts ? p.nparts * K * 4u : 0u);
+#pragma unroll
+    for (int i = 0; i < kMaxParts; ++i) pp[i] = ld_b128<0>(rp, live ? (i * K + 4u * q) * 4u : kPast);
+}
+
+template <int K, int NT>
+Q35_DEV void parts_issue(const GemvPro& p, PartsRegs<K, NT>& r) {
+    constexpr int KC = K / 16;
+    const int t = tid_x();
+    parts_load<K>(p, t, r.b, r.p);
+    const auto rw = rsrc(p.w, K * 2u);
+#pragma unroll
+    for (int m = 0; m < PartsRegs<K, NT>::MC; ++m) {
+        const int cc = t + NT * m;
+        const uint32_t off = cc < KC ? 32u * cc : 0xFFFFFFF0u;
+        r.w[m][0] = ld_b128<0>(rw, off);
+        r.w[m][1] = ld_b128<0>(rw, off + 16u);
+    }
+}
+
+template <int K, bool HALF, int NT>
+Q35_DEV float parts_build(const GemvPro& p, const PartsRegs<K, NT>& r, uint4* ximg, float2* xab,
+                          float* red, float* xs, bool lead) {
+    using PR = PartsRegs<K, NT>;
+    constexpr int KC = K / 16, NW = NT / 64;
+    const int t = tid_x(), lane = t & 63, wid = t >> 6;
+#pragma unroll
+    for (int m = 0; m < PR::MQ; ++m) {
+        const int q = t + NT * m;
+        uint4 b = r.b;
+        uint4 pp[kMaxParts];
+#pragma unroll
+        for (int i = 0; i < kMaxParts; ++i) pp[i] = r.p[i];
+        if (m > 0) parts_load<K>(p, q, b, pp);
+        if (q < PR::NQ) {
+            float v[4];
+            if (p.x_f32) {
+                v[0] = __uint_as_float(b.x);
+                v[1] = __uint_as_float(b.y);
+                v[2] = __uint_as_float(b.z);
+                v[3] = __uint_as_float(b.w);
+            } else {
+                v[0] = bf16_lo(b.x);
+                v[1] = bf16_hi(b.x);
+                v[2] = bf16_lo(b.y);
+                v[3] = bf16_hi(b.y);
+            }
+#pragma unroll
+            for (int i = 0; i < kMaxParts; ++i) {
+                v[0] += __uint_as_float(pp[i].x);
+                v[1] += __uint_as_float(pp[i].y);
+                v[2] += __uint_as_float(pp[i].z);
+                v[3] += __uint_as_float(pp[i].w);
+            }
+            uint32_t h[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                h[j] = f32_to_bf16(v[j]);
+                if (p.sum_bf16) v[j] = bf16_to_f32(h[j]);
+            }
+            reinterpret_cast<float4*>(xs)[q] = make_float4(v[0], v[1], v[2], v[3]);
+            if (p.sum_out && blockIdx.x == 0) {
+                if (p.sum_bf16)
+                    reinterpret_cast<uint2*>(p.sum_out)[q] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                else
+                    reinterpret_cast<float4*>(p.sum_out)[q] = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+    }
+    __syncthreads();
+    float ss = 0.f;
+#pragma unroll
+    for (int m = 0; m < PR::MC; ++m) {
+        const int cc = t + NT * m;
+        if (cc < KC) {
+            float v[16], wv[16];
+            const float4* x4 = reinterpret_cast<const float4*>(xs) + 4 * cc;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 u = x4[j];
+                v[4 * j] = u.x;
+                v[4 * j + 1] = u.y;
+                v[4 * j + 2] = u.z;
+                v[4 * j + 3] = u.w;
+            }
+            unpack_bf16x16(r.w[m], wv);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                ss = fmaf(v[j], v[j], ss);
+                v[j] *= wv[j];
+            }
+            write_chunk<K, HALF>(ximg, xab, cc, v, 1.0f);
+        }
+    }
+    const float s_w = wave_sum(ss);
+    if (lane == 0) red[wid] = s_w;
+    __syncthreads();
+    float ss_t = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) ss_t += red[i];
+    const float post = 1.0f / sqrtf(ss_t / (float)K + p.eps);
+    if (p.tap && lead) {
+#pragma unroll
+        for (int m = 0; m < PR::MC; ++m) {
+            const int cc = t + NT * m;
+            if (cc < KC) {
+                float v[16];
+                read_chunk<K, HALF>(ximg, xab, cc, v);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) p.tap[16 * cc + j] = v[j] * post;
+            }
+        }
+    }
+    return post;
+}
+
 // ---------------------------------------------------------------- epilogues
 
 // Operands an epilogue reads from memory (GemvSeg::pre16/8/4/2, element n),
@@ -519,17 +654,19 @@ struct EpiPre {
     uint32_t q2;  // bf16: residual, dt_bias
 };
 
-template <int OP, bool HALF>
+template <int OP_, bool HALF>
 constexpr int pre_mask() {  // which of the 16/8/4/2-byte operands the op's epilogues read
+    constexpr int OP = Op<OP_>::EPI;
     return OP == kOpInGdn ? (16 | 8 | 4 | 2)
          : (OP == kOpOutGated || OP == kOpOProj) ? (HALF ? 2 : 4)
          : OP == kOpDown ? 4
          : 0;
 }
 
-template <int OP, int SI, bool COH>
+template <int OP_, int SI_, bool COH>
 Q35_DEV void epilogue(const GemvArgs& a, const GemvSeg& s, uint32_t n, float v, float v2,
                       const EpiPre& e, float& best_v, int& best_i) {
+    constexpr int OP = Op<OP_>::EPI, SI = Op<OP_>::esi(SI_);
     if constexpr (OP == kOpPlain || OP == kOpInFull || (OP == kOpInGdn && SI == 1)) {
         st_f32<COH>(s.out, n, v);
     } else if constexpr (OP == kOpInGdn && SI == 0) {
@@ -614,13 +751,6 @@ Q35_DEV void argmax_partial(const GemvArgs& a, float best_v, int best_i, float* 
 
 // ---------------------------------------------------------------- the kernel
 
-// The body shared by the standalone kernels and the stages of the persistent
-// decode kernel.  rg: this wave's first row group; nw: the stride between its
-// row groups.  COH (persistent stages): x, the epilogue operands and the
-// outputs are exchanged with other blocks of the same launch, so they use
-// device-coherent loads and stores; the wave's first row group of weights is
-// issued before wait() (which returns once the stage's inputs are published),
-// and a wave with no row group issues no loads.
 // The registers of one row group in flight: codes, scales and biases of each
 // matrix, and the epilogue operands.
 template <int NC, int NC2>
@@ -630,25 +760,35 @@ struct RgBuf {
     EpiPre pre;
 };
 
-// The body shared by the standalone kernels and the stages of the persistent
-// decode kernel.  rg: this wave's first row group; nw: the stride between its
-// row groups.  COH (persistent stages): x, the epilogue operands and the outputs are exchanged with other
-// blocks of the same launch, so they use device-coherent loads and stores;
-// the wave's first row group of weights is issued before wait() (which
-// returns once the stage's inputs are published), and a wave with no row
-// group issues no loads.
-template <int K, int OP, bool HALF, bool XREG, int NT, bool COH, class Wait>
-Q35_DEV void gemv_body(const GemvArgs& a, uint32_t rg, uint32_t nw, Wait&& wait) {
+// The body shared by the standalone kernels, the stages of the persistent
+// decode kernel and those of the XCD-split kernel.  rg: this wave's first row
+// group; nw: the stride between its row groups; lead: this block writes the
+// prologue's tap; smem4: the block's LDS.
+// SYNC 0: standalone (or the first stage of a launch): x loads, then weights.
+// SYNC 1 (persistent stages): x, the epilogue operands and the outputs are
+// exchanged with other blocks of the launch through device-coherent loads and
+// stores.  SYNC 2 (XCD stages): x was written by blocks of the same XCD with
+// plain stores and is read with device-coherent loads.  With
+// SYNC 1 or 2 the wave's first row group of weights is issued before wait()
+// (which returns once the stage's inputs are published), and a wave with no
+// row group issues no loads.
+// KS: the row stride of the matrices in elements; K < KS reads a column slice
+// (the segment pointers then point at the slice's first column).
+template <int K, int OP, bool HALF, bool XREG, int NT, int SYNC, int KS = K, class Wait>
+Q35_DEV void gemv_body(const GemvArgs& a, uint32_t rg, uint32_t nw, Wait&& wait, bool lead, uint4* smem4) {
     using T = Op<OP>;
     constexpr bool PAIRED = T::PAIRED;
     using G = Geo<K, PAIRED>;
     constexpr int KC = G::KC, LR = G::LR, R = G::R, NC = G::NC;
-    constexpr int KG = K / 64;  // scale groups per row
+    constexpr int KGS = KS / 64;  // scale groups per row of the matrix
+    constexpr bool COH = SYNC == 1;
+    constexpr bool PARTS = T::PRO == kProRmsParts;
+    static_assert(KS % 64 == 0 && KS >= K, "row stride");
 
-    extern __shared__ uint4 smem4[];
     uint4* ximg = smem4;                                         // x image (f16: 2*KC, fp32: 4*KC)
     float2* xab = reinterpret_cast<float2*>(smem4 + (HALF ? 2 : 4) * KC);  // per-chunk (A, B)
     float* red = reinterpret_cast<float*>(xab + KC);
+    float* xs = red + kRedSlots;                                 // kProRmsParts: fp32 sum [K]
     const float4* xq = reinterpret_cast<const float4*>(smem4);
 
     const int lane = tid_x() & 63;
@@ -686,17 +826,17 @@ Q35_DEV void gemv_body(const GemvArgs& a, uint32_t rg, uint32_t nw, Wait&& wait)
         if constexpr (PM & 2)
             b.pre.q2 = __builtin_amdgcn_raw_buffer_load_b16(
                 pre_rsrc(pick<T::NSEG>(si, [&](int i) { return a.seg[i].pre2; }), 2u), n * 2u, 0, PRE_AUX);
-        const uint32_t cbytes = rows * (uint32_t)K, sbytes = rows * (uint32_t)KG * 2u;
-        const uint32_t coff = row0 * (uint32_t)K, soff = row0 * (uint32_t)KG * 2u;
+        const uint32_t cbytes = rows * (uint32_t)KS, sbytes = rows * (uint32_t)KGS * 2u;
+        const uint32_t coff = row0 * (uint32_t)KS, soff = row0 * (uint32_t)KGS * 2u;
         auto issue = [&](const void* c, const void* sc, const void* bi, u32x4_t* wd, uint32_t* sd,
                          uint32_t* bd) {
             const auto rc = rsrc(c, cbytes), rs = rsrc(sc, sbytes), rb = rsrc(bi, sbytes);
 #pragma unroll
             for (int i = 0; i < NC; ++i) {
                 const uint32_t cc = (uint32_t)li + LR * i;
-                wd[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, rloc * K + 16u * cc, coff, kAuxStream);
-                sd[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, (rloc * KG + (cc >> 2)) * 2u, soff, 0);
-                bd[i] = __builtin_amdgcn_raw_buffer_load_b16(rb, (rloc * KG + (cc >> 2)) * 2u, soff, 0);
+                wd[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, rloc * KS + 16u * cc, coff, kAuxStream);
+                sd[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, (rloc * KGS + (cc >> 2)) * 2u, soff, 0);
+                bd[i] = __builtin_amdgcn_raw_buffer_load_b16(rb, (rloc * KGS + (cc >> 2)) * 2u, soff, 0);
             }
         };
         issue(pick<T::NSEG>(si, [&](int i) { return a.seg[i].codes[0]; }),
@@ -707,8 +847,14 @@ Q35_DEV void gemv_body(const GemvArgs& a, uint32_t rg, uint32_t nw, Wait&& wait)
     };
 
     Buf b0;
-    ProRegs<K, T::PRO, NT> pr;
-    if constexpr (COH) {
+    ProRegs<K, PARTS ? kProLoadF32 : T::PRO, NT> pr;
+    PartsRegs<K, NT> prp;
+    if constexpr (PARTS) {
+        static_assert(SYNC == 0, "the partial sums come from an earlier launch");
+        parts_issue<K, NT>(a.pro, prp);
+        asm volatile("" ::: "memory");
+        load_rg(rg, rg < total, b0);
+    } else if constexpr (SYNC != 0) {
         // weights first (they do not depend on this launch), then the wait for
         // the stage's inputs, then x
 #ifdef Q35_PERSIST_PRE_WAVES
@@ -720,7 +866,7 @@ Q35_DEV void gemv_body(const GemvArgs& a, uint32_t rg, uint32_t nw, Wait&& wait)
         asm volatile("" ::: "memory");
         wait();
         if (!early && rg < total) load_rg(rg, true, b0);
-        prologue_issue<K, T::PRO, HALF, NT, true>(a.pro, pr);
+        prologue_issue<K, T::PRO, HALF, NT, true, SYNC == 1 ? kAuxXPersist : kAuxCoherent>(a.pro, pr);
     } else {
         // x loads first, then the first row groups' weights (vector loads complete in order)
         prologue_issue<K, T::PRO, HALF, NT>(a.pro, pr);
@@ -729,7 +875,11 @@ Q35_DEV void gemv_body(const GemvArgs& a, uint32_t rg, uint32_t nw, Wait&& wait)
     }
     asm volatile("" ::: "memory");
 
-    const float post = prologue_build<K, T::PRO, HALF, NT>(a.pro, pr, ximg, xab, red);
+    float post;
+    if constexpr (PARTS)
+        post = parts_build<K, HALF, NT>(a.pro, prp, ximg, xab, red, xs, lead);
+    else
+        post = prologue_build<K, T::PRO, HALF, NT>(a.pro, pr, ximg, xab, red, lead);
 
     float best_v = -INFINITY;
     int best_i = 0x7FFFFFFF;
@@ -781,22 +931,24 @@ Q35_DEV void gemv_body(const GemvArgs& a, uint32_t rg, uint32_t nw, Wait&& wait)
 
 template <int K, int OP, bool HALF, bool XREG, int NT>
 __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a) {
+    extern __shared__ uint4 smem4[];
     // wave-uniform by construction; readfirstlane lets the compiler keep the row
     // group (and so every buffer load's scalar offset) in SGPRs
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid_x() >> 6);
-    gemv_body<K, OP, HALF, XREG, NT, false>(a, blockIdx.x * (NT / 64) + wave, gridDim.x * (NT / 64),
-                                            [] {});
+    gemv_body<K, OP, HALF, XREG, NT, 0>(a, blockIdx.x * (NT / 64) + wave, gridDim.x * (NT / 64), [] {},
+                                        blockIdx.x == 0, smem4);
 }
 
-template <int K, bool HALF>
-constexpr size_t lds_bytes() {  // x image + per-chunk (A, B) + reduction slots
-    return (size_t)(K / 16) * ((HALF ? 2 : 4) * 16 + 8) + kRedSlots * sizeof(float);
+// x image + per-chunk (A, B) + reduction slots (+ the fp32 sum of kProRmsParts)
+template <int K, bool HALF, bool PARTS = false>
+constexpr size_t lds_bytes() {
+    return (size_t)(K / 16) * ((HALF ? 2 : 4) * 16 + 8) + kRedSlots * sizeof(float) + (PARTS ? K * 4 : 0);
 }
 
 template <int K, int OP, bool HALF, bool XREG>
 hipError_t launch_t(const GemvArgs& a, uint32_t blocks, hipStream_t stream) {
     constexpr int NT = gemv_threads(OP);
-    const size_t lds = lds_bytes<K, HALF>();
+    const size_t lds = lds_bytes<K, HALF, Op<OP>::PRO == kProRmsParts>();
     hipLaunchKernelGGL((gemv_kernel<K, OP, HALF, XREG, NT>), dim3(blocks), dim3(NT), lds, stream, a);
     return hipGetLastError();
 }

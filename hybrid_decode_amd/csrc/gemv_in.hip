@@ -1,4 +1,4 @@
-// GEMV instantiations: kOpInGdn, kOpInFull.
+// GEMV instantiations: kOpInGdn, kOpInFull, kOpInFullP.
 #include "gemv_core.h"
 
 namespace q35 {
@@ -20,6 +20,13 @@ hipError_t gemv_launch_in(int op, uint32_t k, bool half, bool xreg, const GemvAr
         Q35_W_HIDDEN(X)
 #undef X
     }
+    if (op == kOpInFullP) {
+#define X(KK)                                                                              \
+        if (k == KK) return half ? gemv::launch_t<KK, kOpInFullP, true, false>(a, blocks, stream) \
+                                 : gemv::launch_t<KK, kOpInFullP, false, false>(a, blocks, stream);
+        Q35_W_PARTS(X)
+#undef X
+    }
     return hipErrorInvalidValue;
 }
 
@@ -37,6 +44,13 @@ const void* gemv_ptr_in(int op, uint32_t k, bool half, bool xreg) {
         if (k == KK) return half ? gemv::kernel_ptr_t<KK, kOpInFull, true, false>()          \
                                  : gemv::kernel_ptr_t<KK, kOpInFull, false, false>();
         Q35_W_HIDDEN(X)
+#undef X
+    }
+    if (op == kOpInFullP) {
+#define X(KK)                                                                           \
+        if (k == KK) return half ? gemv::kernel_ptr_t<KK, kOpInFullP, true, false>()          \
+                                 : gemv::kernel_ptr_t<KK, kOpInFullP, false, false>();
+        Q35_W_PARTS(X)
 #undef X
     }
     return nullptr;

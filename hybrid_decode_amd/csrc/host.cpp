@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <initializer_list>
 #include <string>
 #include <vector>
@@ -467,6 +468,13 @@ q35_status q35_kernels_resolve(int device, Qwen35Kernels** out) {
             for (uint32_t f : {Q35_KV_BF16, Q35_KV_TURBO8, Q35_KV_BF16K_TURBO4V})
                 probe(attn_kernel_ptr(d, g, f), "attention");
     for (int i = 0; pf_kernel_ptr(i); ++i) probe(pf_kernel_ptr(i), "prefill");
+#define X(KK)                                                                  \
+    probe(gemv_kernel_ptr(kOpInFullP, KK, false, false), "q/k/v (partial sums)"); \
+    probe(gemv_kernel_ptr(kOpInFullP, KK, true, false), "q/k/v (partial sums)");
+    Q35_W_PARTS(X)
+#undef X
+    for (int launch : {kXcdMixer, kXcdMlp}) probe(xcd_kernel_ptr(1, launch), "XCD-split decode");
+    probe(xsum_kernel_ptr(), "residual sum");
     probe(embed_kernel_ptr(), "embed");
     probe(lm_finish_kernel_ptr(), "lm_head argmax");
     for (uint32_t d : {64u, 128u, 256u})
@@ -1721,6 +1729,493 @@ q35_status q35_decode_stage_times(const Q35DecodePlan* plan, uint64_t* ticks, ui
         return Q35_OK;
     }));
     if (ticks_per_second) *ticks_per_second = plan->clock_hz;
+    return ok();
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ XCD-split decode plan
+
+struct Q35XcdPlan {
+    int device;
+    int shape;
+    uint32_t blocks;
+    uint32_t n_layers;
+    uint32_t* ctl;  // [0] unused, [1] error word
+    uint32_t* sync;
+    uint32_t* probe;
+    uint64_t spin_ticks;
+    XStage* table;                                       // device copy of `stages`
+    std::vector<XStage> stages;                          // [launch stages][kXcds], in step order
+    std::vector<std::function<q35_status(hipStream_t)>> ops;  // one token's launches
+    void* x_first;
+    void* x_last;
+    Q35XcdBuffers bufs;
+};
+
+namespace {
+
+// The residual stream between launches: base + partial sums (fp32, in order).
+struct XRes {
+    const void* base;
+    bool base_f32;
+    const float* parts;
+    uint32_t nparts;
+};
+
+// Segment over rows [row0, row0 + rows) of w (and w2), columns from col0 on;
+// r rows per row group at the launch's K.
+GemvSeg& xseg(GemvArgs& a, const Q35QuantWeight& w, uint32_t row0, uint32_t rows, uint32_t col0, uint32_t r,
+              int32_t epi, const Q35QuantWeight* w2 = nullptr) {
+    GemvSeg& s = a.seg[a.nseg++];
+    const size_t kg = w.k / 64;
+    s.codes[0] = w.codes + (size_t)row0 * w.k + col0;
+    s.scales[0] = w.scales + row0 * kg + col0 / 64;
+    s.biases[0] = w.biases + row0 * kg + col0 / 64;
+    if (w2) {
+        s.codes[1] = w2->codes + (size_t)row0 * w2->k + col0;
+        s.scales[1] = w2->scales + row0 * kg + col0 / 64;
+        s.biases[1] = w2->biases + row0 * kg + col0 / 64;
+    }
+    s.rg_begin = a.total_rg;
+    s.rows = rows;
+    a.total_rg += rows / r;
+    s.rg_end = a.total_rg;
+    s.epi = epi;
+    return s;
+}
+
+void parts_pro(GemvPro& p, const XRes& in, const uint16_t* norm, float eps, bool round_bf16, void* sum_out) {
+    p.kind = kProRmsParts;
+    p.x = in.base;
+    p.x_f32 = in.base_f32 ? 1 : 0;
+    p.parts = in.parts;
+    p.nparts = in.nparts;
+    p.w = norm;
+    p.eps = eps;
+    p.sum_bf16 = round_bf16 ? 1 : 0;
+    p.sum_out = sum_out;
+}
+
+// Validates the stack for the XCD-split plan, lays out the workspace and (when
+// plan != nullptr) fills the plan.
+q35_status xcd_build(const Qwen35Kernels* k, const Qwen35ForwardConfig* cfg, const Q35DecodeStackDesc* d,
+                     uint8_t* ws, size_t* total, Q35XcdPlan* plan) {
+    Q35_TRY(check_kernels(k));
+    if (!cfg || !d) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    Q35_TRY(q35_config_validate(cfg));
+    const Qwen35ForwardConfig& c = *cfg;
+    const bool f32 = c.act_dtype == Q35_ACT_F32;
+    const int shape = xcd_shape_id(c.hidden, c.intermediate, z_dim(c), c.k_head_dim_lin, !f32);
+    if (!shape) return fail(Q35_ERR_UNSUPPORTED, "the XCD-split kernels are not built for these dimensions");
+    const uint32_t blocks = (uint32_t)k->num_cu;
+    const uint32_t nb = blocks / kXcds;
+    const uint32_t Hk = c.num_k_heads_lin, Hv = c.num_v_heads_lin, dk = c.k_head_dim_lin, dv = c.v_head_dim_lin;
+    if (blocks % kXcds != 0 || Hk % kXcds != 0 || Hv % kXcds != 0 || (Hv / kXcds) * (dv / 16) != nb ||
+        c.intermediate % kXcds != 0)
+        return fail(Q35_ERR_UNSUPPORTED, "%u compute units, %u/%u linear heads: no even split over %d XCDs",
+                    blocks, Hk, Hv, kXcds);
+    if (d->n_layers == 0 || !d->layers) return fail(Q35_ERR_INVALID_ARG, "empty stack");
+    Q35_TRY(need(d->positions, "positions", false));
+    const bool tail = d->lm_head != nullptr;
+    uint32_t max_cap = 0;
+    bool any_full = false;
+    for (uint32_t l = 0; l < d->n_layers; ++l) {
+        const Q35StackLayer& L = d->layers[l];
+        if (L.kind == Q35_LAYER_LINEAR) {
+            if (!L.linear || !L.state) return fail(Q35_ERR_INVALID_ARG, "layer %u: NULL weights/state", l);
+            Q35_TRY(check_linear_layer(c, *L.linear, *L.state));
+        } else if (L.kind == Q35_LAYER_FULL) {
+            if (!L.full || !L.kv) return fail(Q35_ERR_INVALID_ARG, "layer %u: NULL weights/cache", l);
+            Q35_TRY(check_full_layer(c, *L.full));
+            Q35_TRY(check_kv(*L.kv, true));
+            max_cap = std::max(max_cap, L.kv->capacity);
+            any_full = true;
+        } else {
+            return fail(Q35_ERR_INVALID_ARG, "layer %u: kind %u", l, L.kind);
+        }
+    }
+    if (any_full) Q35_TRY(need(d->inv_freq, "inv_freq", false));
+    if (tail) {
+        if (c.vocab == 0) return fail(Q35_ERR_INVALID_ARG, "vocab is 0");
+        Q35_TRY(check_weight("lm_head", *d->lm_head, c.vocab, c.hidden));
+        Q35_TRY(need(d->final_norm, "final_norm"));
+        Q35_TRY(need(d->tokens, "tokens", false));
+        if (!d->embed || !aligned16(d->embed) || c.hidden % 8 != 0)
+            return fail(Q35_ERR_INVALID_ARG, "embed NULL or not 16-byte aligned, or hidden %% 8 != 0");
+        Q35_TRY(opt(d->logits, "logits"));
+    }
+
+    const size_t act = f32 ? 4 : 2;
+    const uint32_t H = c.hidden, I = c.intermediate, qt = qkv_total(c), zd = z_dim(c);
+    uint32_t nxst = 0;
+    for (uint32_t l = 0; l < d->n_layers; ++l)
+        nxst += (d->layers[l].kind == Q35_LAYER_LINEAR ? kXcdStages[kXcdMixer] : 0) + kXcdStages[kXcdMlp];
+    Bump b{ws};
+    uint32_t* ctl = static_cast<uint32_t*>(b.take(256));
+    uint32_t* sync = static_cast<uint32_t*>(b.take(kXcds * 256));
+    // the placement probe's output: its own lines, never the counters' (another
+    // XCD's cached copy of a counter line could outlive the clear)
+    uint32_t* probe = static_cast<uint32_t*>(b.take(4u * blocks));
+    XStage* table = static_cast<XStage*>(b.take(sizeof(XStage) * kXcds * nxst));
+    void* x_first = b.take(act * H);
+    void* x_in = b.take(act * H);
+    void* x_last = b.take(act * H);
+    float* x_mid = b.f32(H);
+    float* x_res = b.f32(H);
+    float* pmix = b.f32((size_t)kXcds * H);
+    float* pmlp = b.f32((size_t)kXcds * H);
+    float* qkv = b.f32(qt);
+    float* z = b.f32(zd);
+    float* gate = b.f32(Hv);
+    float* beta = b.f32(Hv);
+    float* y = b.f32(zd);
+    float* h = b.f32(I);
+    FullAttentionScratch fs;
+    std::memset(&fs, 0, sizeof(fs));
+    AttnWs aws{};
+    if (any_full) {
+        fs.q_full = b.f32(q_total(c));
+        fs.k = b.f32(kv_dim(c));
+        fs.v = b.f32(kv_dim(c));
+        fs.gated_attn = b.f32(q_only(c));
+        aws = attn_ws_layout(c, max_cap);
+        fs.workspace = b.take(aws.total);
+        fs.workspace_bytes = aws.total;
+        fs.status = ctl ? ctl + 1 : nullptr;  // a position out of range is reported by q35_xcd_check
+    }
+    LmWs lws{};
+    void* lm_ws = nullptr;
+    if (tail) {
+        lws = lm_ws_layout(c);
+        lm_ws = b.take(lws.total);
+    }
+    *total = b.off;
+    if (!plan) return Q35_OK;
+
+    plan->shape = shape;
+    plan->blocks = blocks;
+    plan->n_layers = d->n_layers;
+    plan->ctl = ctl;
+    plan->sync = sync;
+    plan->probe = probe;
+    plan->table = table;
+    plan->x_first = x_first;
+    plan->x_last = x_last;
+    Q35XcdBuffers& bf = plan->bufs;
+    bf.x_in = x_in;
+    bf.qkv_conv = qkv;
+    bf.z = z;
+    bf.gate = gate;
+    bf.beta = beta;
+    bf.y = y;
+    bf.out_parts = pmix;
+    bf.mlp_act = h;
+    bf.mlp_parts = pmlp;
+    bf.x_mid = x_mid;
+    bf.x_resid = x_res;
+
+    std::vector<XStage>& tab = plan->stages;
+    auto& ops = plan->ops;
+    const uint32_t num_cu = blocks;
+    const uint32_t r_h = (uint32_t)gemv_rows_per_matrix_group(H, false);
+    const uint32_t r_gu = (uint32_t)gemv_rows_per_matrix_group(H, true);
+    const uint32_t r_z8 = (uint32_t)gemv_rows_per_matrix_group(zd / kXcds, false);
+    const uint32_t r_i8 = (uint32_t)gemv_rows_per_matrix_group(I / kXcds, false);
+    auto new_stage = [&](int kind) -> std::vector<XStage*> {
+        std::vector<XStage*> v;
+        const size_t at = tab.size();
+        tab.resize(at + kXcds);
+        for (int x = 0; x < kXcds; ++x) {
+            XStage& s = tab[at + x];
+            std::memset(&s, 0, sizeof(s));
+            s.kind = kind;
+            v.push_back(&s);
+        }
+        return v;
+    };
+    auto xcd_op = [&](int launch, size_t first_entry) {
+        XcdArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.table = table + first_entry;
+        a.sync = sync;
+        a.err = ctl + 1;
+        ops.push_back([plan, launch, a](hipStream_t s) mutable -> q35_status {
+            a.spin_ticks = plan->spin_ticks;
+            Q35_HIP(xcd_launch(plan->shape, launch, a, plan->blocks, s),
+                    launch == kXcdMixer ? "XCD mixer launch" : "XCD MLP launch");
+            return Q35_OK;
+        });
+    };
+    // gate/up over XCD x's rows from the residual `in`, its sum written to x_res;
+    // down over the matching columns into pmlp[x]
+    auto mlp = [&](const Q35QuantWeight& gp, const Q35QuantWeight& up, const Q35QuantWeight& dp,
+                   const uint16_t* post_ln, const XRes& in) {
+        const size_t first = tab.size();
+        const uint32_t i8 = I / kXcds;
+        auto s0 = new_stage(kXsGateUp);
+        for (int x = 0; x < kXcds; ++x) {
+            GemvArgs& g = s0[x]->g;
+            g.act_f32 = f32;
+            parts_pro(g.pro, in, post_ln, c.rms_eps, false, x_res);
+            xseg(g, gp, i8 * x, i8, 0, r_gu, kEpiSwiGLU, &up).out = h + i8 * x;
+        }
+        auto s1 = new_stage(kXsDownPart);
+        for (int x = 0; x < kXcds; ++x) {
+            GemvArgs& g = s1[x]->g;
+            g.act_f32 = f32;
+            g.pro.kind = kProLoadF32;
+            g.pro.x = h + i8 * x;
+            xseg(g, dp, 0, H, i8 * x, r_i8, kEpiStore).out = pmlp + (size_t)H * x;
+        }
+        xcd_op(kXcdMlp, first);
+    };
+
+    XRes in{x_first, f32, nullptr, 0};
+    for (uint32_t l = 0; l < d->n_layers; ++l) {
+        const Q35StackLayer& L = d->layers[l];
+        if (L.kind == Q35_LAYER_LINEAR) {
+            const LinearAttentionLayer& w = *L.linear;
+            const size_t first = tab.size();
+            const uint32_t qh = Hk * dk / kXcds, vh = Hv * dv / kXcds, ah = Hv / kXcds;
+            auto s0 = new_stage(kXsInGdn);
+            for (int x = 0; x < kXcds; ++x) {
+                GemvArgs& g = s0[x]->g;
+                g.act_f32 = f32;
+                parts_pro(g.pro, in, w.input_ln, c.rms_eps, !f32, x_in);
+                // q, k and v channels of the XCD's heads: conv + SiLU
+                const uint32_t ch[3] = {qh * x, Hk * dk + qh * x, 2 * Hk * dk + vh * x};
+                const uint32_t nch[3] = {qh, qh, vh};
+                for (int j = 0; j < 3; ++j) {
+                    GemvSeg& sq = xseg(g, w.in_proj_qkv, ch[j], nch[j], 0, r_h, kEpiConv);
+                    sq.out = qkv + ch[j];
+                    sq.state = L.state->conv1d_state + (size_t)ch[j] * 4;
+                    sq.pre16 = sq.state;
+                    sq.pre8 = w.conv1d_weight + (size_t)ch[j] * 4;
+                }
+                xseg(g, w.in_proj_z, vh * x, vh, 0, r_h, kEpiStore).out = z + vh * x;
+                GemvSeg& sa = xseg(g, w.in_proj_a, ah * x, ah, 0, r_h, kEpiGate);
+                sa.out = gate + ah * x;
+                sa.pre2 = w.dt_bias + ah * x;
+                sa.pre4 = w.a_log + ah * x;
+                xseg(g, w.in_proj_b, ah * x, ah, 0, r_h, kEpiBeta).out = beta + ah * x;
+            }
+            auto s1 = new_stage(kXsGdn);
+            for (int x = 0; x < kXcds; ++x) {
+                GdnArgs& g = s1[x]->d;
+                g.state = L.state->gdn_state;
+                g.qkv_conv = qkv;
+                g.gate = gate;
+                g.beta = beta;
+                g.y = y;
+                g.hk = Hk;
+                g.hv = Hv;
+                g.l2_eps = 1e-6f;
+                g.out_scale = 1.0f / std::sqrt((float)dk);
+            }
+            auto s2 = new_stage(kXsOutPart);
+            for (int x = 0; x < kXcds; ++x) {
+                GemvArgs& g = s2[x]->g;
+                g.act_f32 = f32;
+                g.pro.kind = kProGatedNorm;
+                g.pro.x = y + vh * x;
+                g.pro.z = z + vh * x;
+                g.pro.w = w.norm_weight;
+                g.pro.head_dim = dv;
+                g.pro.eps = c.rms_eps;
+                xseg(g, w.out_proj, 0, H, vh * x, r_z8, kEpiStore).out = pmix + (size_t)H * x;
+            }
+            xcd_op(kXcdMixer, first);
+            mlp(w.gate_proj, w.up_proj, w.down_proj, w.post_ln, XRes{x_in, f32, pmix, (uint32_t)kXcds});
+        } else {
+            const FullAttentionLayer& w = *L.full;
+            const LayerKvCache* kv = L.kv;
+            {
+                GemvBuild g(kOpInFullP, H, f32);
+                parts_pro(g.a.pro, in, w.input_ln, c.rms_eps, !f32, x_in);
+                g.add(w.q_proj, kEpiStore).out = fs.q_full;
+                g.add(w.k_proj, kEpiStore).out = fs.k;
+                g.add(w.v_proj, kEpiStore).out = fs.v;
+                ops.push_back([g, num_cu](hipStream_t s) mutable -> q35_status {
+                    return g.launch(num_cu, s, "q/k/v GEMV");
+                });
+            }
+            {
+                // the layer and cache descriptions are host structs read at creation: copied
+                const Qwen35Kernels* kk = k;
+                const Qwen35ForwardConfig cc = c;
+                const FullAttentionLayer wl = w;
+                const LayerKvCache kvc = *kv;
+                const float* inv = d->inv_freq;
+                const int32_t* pos = d->positions;
+                ops.push_back([kk, cc, wl, fs, kvc, aws, inv, pos](hipStream_t s) -> q35_status {
+                    return launch_attention(kk, cc, &wl, &fs, &kvc, aws, inv, pos, -1, 0, s);
+                });
+            }
+            {
+                GemvBuild g(kOpOProj, q_only(c), f32);
+                g.a.pro.kind = kProLoadF32;
+                g.a.pro.x = fs.gated_attn;
+                GemvSeg& so = g.add(w.o_proj, kEpiResidActIn);
+                so.out = x_mid;
+                (f32 ? so.pre4 : so.pre2) = x_in;
+                ops.push_back([g, num_cu](hipStream_t s) mutable -> q35_status {
+                    return g.launch(num_cu, s, "o_proj GEMV");
+                });
+            }
+            mlp(w.gate_proj, w.up_proj, w.down_proj, w.post_ln, XRes{x_mid, true, nullptr, 0});
+        }
+        in = XRes{x_res, true, pmlp, (uint32_t)kXcds};
+    }
+    // the last layer's output, whole, in the activation dtype
+    ops.push_back([x_res, pmlp, H, x_last, f32](hipStream_t s) -> q35_status {
+        Q35_HIP(xsum_launch(x_res, true, pmlp, kXcds, H, x_last, f32, s), "residual sum");
+        return Q35_OK;
+    });
+    if (tail) {
+        GemvBuild g(kOpLmHead, H, f32);
+        g.a.pro.kind = kProRmsAct;
+        g.a.pro.x_f32 = f32;
+        g.a.pro.x = x_last;
+        g.a.pro.w = d->final_norm;
+        g.a.pro.eps = c.rms_eps;
+        g.add(*d->lm_head, kEpiArgmax).out = d->logits;
+        uint8_t* wsb = static_cast<uint8_t*>(lm_ws);
+        g.a.am.part_val = reinterpret_cast<float*>(wsb + lws.val_off);
+        g.a.am.part_idx = reinterpret_cast<int32_t*>(wsb + lws.idx_off);
+        LmFinishArgs f;
+        std::memset(&f, 0, sizeof(f));
+        f.part_val = g.a.am.part_val;
+        f.part_idx = g.a.am.part_idx;
+        f.nparts = lws.blocks;
+        f.vocab = c.vocab;
+        f.tokens = d->tokens;
+        f.positions = d->positions;
+        f.history = d->history;
+        f.history_len = d->history ? d->history_len : 0;
+        f.history_base = d->history_base;
+        f.embed = d->embed;
+        f.x_next = x_first;
+        f.hidden = H;
+        f.act_f32 = f32 ? 1 : 0;
+        const uint32_t lm_blocks = lws.blocks;
+        ops.push_back([g, f, num_cu, lm_blocks](hipStream_t s) mutable -> q35_status {
+            Q35_TRY(g.launch(num_cu, s, "lm_head GEMV", lm_blocks));
+            Q35_HIP(lm_finish_launch(f, s), "lm_head argmax");
+            return Q35_OK;
+        });
+    }
+    if (tab.size() != (size_t)nxst * kXcds)
+        return fail(Q35_ERR_INVALID_ARG, "internal: %zu stage entries != %u", tab.size(), nxst * kXcds);
+    return Q35_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+q35_status q35_xcd_workspace_bytes(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                                   const Q35DecodeStackDesc* stack, size_t* bytes) {
+    if (!bytes) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    size_t total = 0;
+    Q35_TRY(xcd_build(kernels, cfg, stack, nullptr, &total, nullptr));
+    *bytes = total;
+    return ok();
+}
+
+q35_status q35_xcd_plan_create(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                               const Q35DecodeStackDesc* stack, void* workspace, size_t workspace_bytes,
+                               Q35XcdPlan** out) {
+    if (!out) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    *out = nullptr;
+    size_t total = 0;
+    Q35_TRY(xcd_build(kernels, cfg, stack, nullptr, &total, nullptr));
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(Q35_ERR_INVALID_ARG, "workspace NULL or not 256-byte aligned");
+    if (workspace_bytes < total)
+        return fail(Q35_ERR_INVALID_ARG, "workspace %zu bytes < %zu required", workspace_bytes, total);
+    Q35XcdPlan* plan = new Q35XcdPlan();
+    plan->device = kernels->device;
+    q35_status st = xcd_build(kernels, cfg, stack, static_cast<uint8_t*>(workspace), &total, plan);
+    if (st == Q35_OK) {
+        st = on_device(plan->device, [&]() -> q35_status {
+            int khz = 0;
+            Q35_HIP(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, plan->device),
+                    "hipDeviceGetAttribute");
+            if (khz <= 0) return fail(Q35_ERR_UNSUPPORTED, "no device wall clock");
+            plan->spin_ticks = (uint64_t)(kWaitLimitSeconds * (double)khz * 1000.0);
+            for (int launch : {kXcdMixer, kXcdMlp}) {
+                int per_cu = 0;
+                Q35_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, xcd_kernel_ptr(plan->shape, launch),
+                                                                     kXcdThreads, 0),
+                        "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+                if (per_cu != 1)
+                    return fail(Q35_ERR_UNSUPPORTED, "the XCD kernels fit %d blocks per CU, not one", per_cu);
+            }
+            // placement: XCD of block b = (b + c) % 8 for one c (the dispatcher's
+            // turn order; c may differ from launch to launch)
+            XcdArgs pa;
+            std::memset(&pa, 0, sizeof(pa));
+            pa.probe = plan->probe;
+            Q35_HIP(xcd_launch(plan->shape, kXcdMixer, pa, plan->blocks, nullptr), "XCD placement probe");
+            std::vector<uint32_t> where(plan->blocks);
+            Q35_HIP(hipMemcpy(where.data(), plan->probe, 4u * plan->blocks, hipMemcpyDeviceToHost), "probe read");
+            for (uint32_t i = 0; i < plan->blocks; ++i)
+                if (where[i] >= (uint32_t)kXcds || (where[i] + kXcds - i % kXcds) % kXcds != where[0])
+                    return fail(Q35_ERR_UNSUPPORTED, "block %u ran on XCD %u, block 0 on %u: not one residue "
+                                                     "class of the block index per XCD", i, where[i], where[0]);
+            Q35_HIP(hipMemcpy(plan->table, plan->stages.data(), plan->stages.size() * sizeof(XStage),
+                              hipMemcpyHostToDevice),
+                    "stage table upload");
+            Q35_HIP(hipMemset(plan->ctl, 0, 256), "sync word clear");
+            Q35_HIP(hipMemset(plan->sync, 0, kXcds * 256), "sync word clear");
+            if (stack->lm_head) {
+                Q35_HIP(embed_launch(stack->embed, stack->tokens, cfg->vocab, cfg->hidden, plan->x_first,
+                                     cfg->act_dtype == Q35_ACT_F32, nullptr),
+                        "first embedding");
+            }
+            Q35_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize");
+            return Q35_OK;
+        });
+    }
+    if (st != Q35_OK) {
+        delete plan;
+        return st;
+    }
+    *out = plan;
+    return ok();
+}
+
+void q35_xcd_plan_release(Q35XcdPlan* plan) { delete plan; }
+
+q35_status q35_xcd_step(const Q35XcdPlan* plan, hipStream_t stream) {
+    if (!plan) return fail(Q35_ERR_INVALID_ARG, "NULL plan");
+    for (const auto& op : plan->ops) Q35_TRY(op(stream));
+    return ok();
+}
+
+q35_status q35_xcd_check(const Q35XcdPlan* plan, uint32_t* error_word) {
+    if (!plan || !error_word) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    Q35_TRY(on_device(plan->device, [&]() -> q35_status {
+        Q35_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize");
+        Q35_HIP(hipMemcpy(error_word, plan->ctl + 1, 4, hipMemcpyDeviceToHost), "error word read");
+        return Q35_OK;
+    }));
+    return ok();
+}
+
+q35_status q35_xcd_layer_input(const Q35XcdPlan* plan, uint32_t layer, void** x) {
+    if (!plan || !x) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    if (layer != 0 && layer != plan->n_layers)
+        return fail(Q35_ERR_OUT_OF_RANGE, "layer %u: only the first input (0) and the last output (%u) are whole vectors",
+                    layer, plan->n_layers);
+    *x = layer == 0 ? plan->x_first : plan->x_last;
+    return ok();
+}
+
+q35_status q35_xcd_buffers(const Q35XcdPlan* plan, Q35XcdBuffers* bufs) {
+    if (!plan || !bufs) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
+    *bufs = plan->bufs;
     return ok();
 }
 

@@ -9,7 +9,7 @@ namespace q35 {
 
 // ------------------------------------------------------------------ GEMV family
 
-constexpr int kMaxSegs = 4;
+constexpr int kMaxSegs = 6;
 constexpr int kGemvThreads = 256;       // threads per block: streaming GEMVs, GDN in-projection
 constexpr int kGemvLayerThreads = 640;  // threads per block of the other per-layer GEMVs (one per CU)
 
@@ -18,6 +18,8 @@ enum : int32_t {
     kProRmsF32 = 1,     // x = RMSNorm(x_f32; w)
     kProGatedNorm = 2,  // x = RMSNorm_per_head(y; w) * silu(z)
     kProLoadF32 = 3,    // x = src
+    kProRmsParts = 4,   // x = RMSNorm(base + sum of nparts fp32 partial vectors; w), the sum optionally
+                        //     rounded to bf16 and written out by block 0
 };
 
 enum : int32_t {
@@ -61,6 +63,11 @@ struct GemvPro {
     uint32_t head_dim;
     float eps;
     float* tap;  // optional: the normalised x (before the silu(z) factor), block 0 writes it
+    // kProRmsParts (x is the base, fp32 when x_f32 else bf16)
+    const float* parts;  // [nparts][K] fp32
+    uint32_t nparts;     // 0..8
+    int32_t sum_bf16;    // round the sum to bf16 before the norm (a layer input held in bf16)
+    void* sum_out;       // optional: the sum, bf16 when sum_bf16 else fp32
 };
 
 struct GemvArgmax {
@@ -88,10 +95,20 @@ enum : int32_t {
     kOpGateUp = 5,    // RMSNorm(x_resid); paired gate/up -> silu(g) * u  (1)
     kOpDown = 6,      // x loaded; down + residual -> activation dtype    (1)
     kOpLmHead = 7,    // RMSNorm(x); logits + argmax                      (1)
+    // Variants of the above for the XCD-split decode: the residual stream
+    // arrives as a base plus per-XCD partial sums, and the GEMVs of one XCD
+    // cover its share of the rows (or of the columns, as a partial sum).
+    kOpInFullP = 8,   // kOpInFull with the kProRmsParts prologue          (3)
+    kOpInGdnX = 9,    // kOpInGdn over one XCD's rows: q, k, v (conv), z, a, b (6)
+    kOpGateUpX = 10,  // kOpGateUp with the kProRmsParts prologue           (1)
+    kOpOutPart = 11,  // gated norm prologue; out_proj column slice, y stored (1)
+    kOpDownPart = 12, // x loaded; down column slice, y stored            (1)
 };
 
 // GEMV widths compiled in, by role.
 #define Q35_W_HIDDEN(X) X(256) X(1024) X(2048) X(2560) X(3072) X(4096) X(5120) X(6144) X(8192)
+// Hidden widths of the sum-of-partials prologue: the XCD-split decode, built for K / 4 <= 640 threads.
+#define Q35_W_PARTS(X) X(256) X(1024) X(2048) X(2560)
 #define Q35_W_PROJ(X) X(128) X(256) X(512) X(1024) X(2048) X(4096) X(6144) X(8192)
 #define Q35_W_INTER(X) \
     X(512) X(1024) X(2048) X(3072) X(4096) X(5120) X(6144) X(8192) X(9216) X(12288)
@@ -253,6 +270,54 @@ int persist_shape_id(uint32_t hidden, uint32_t inter, uint32_t q_only, uint32_t 
 size_t persist_lds_bytes(int shape);
 const void* persist_kernel_ptr(int shape);
 hipError_t persist_launch(int shape, const PersistArgs& a, uint32_t blocks, hipStream_t stream);
+
+// ------------------------------------------------------------------ XCD-split decode
+
+// A launch runs a fixed sequence of stages; block b works for XCD b % 8 (the
+// hardware's placement of a one-block-per-CU grid, checked in the kernel) and
+// the blocks of one XCD meet at a counter in that XCD's L2 between stages.
+constexpr int kXcds = 8;
+constexpr int kXcdThreads = 1024;  // threads per block; one block per CU
+
+enum : int32_t {
+    kXsInGdn = 1,     // GEMV kOpInGdnX (first stage of a launch)
+    kXsGdn = 2,       // gated delta rule tiles of the XCD's v-heads
+    kXsOutPart = 3,   // GEMV kOpOutPart: out_proj over the XCD's y columns -> partial
+    kXsGateUp = 4,    // GEMV kOpGateUpX (first stage of a launch)
+    kXsDownPart = 5,  // GEMV kOpDownPart: down over the XCD's activation columns -> partial
+};
+
+struct XStage {  // one XCD's arguments of one stage
+    int32_t kind;
+    int32_t pad;
+    union {
+        GemvArgs g;
+        GdnArgs d;
+    };
+};
+
+struct XcdArgs {
+    const XStage* table;  // device, [stages of the launch][kXcds]
+    uint32_t* sync;       // [kXcds][64]: XCD x's counter at sync[64 x] (monotonic)
+    uint32_t* err;        // error word: bit 0 a wait expired, Q35_STATUS_XCD_MAP a block off its XCD
+    uint64_t spin_ticks;  // wall-clock ticks before a wait gives up
+    uint32_t* probe;      // non-NULL: each block writes its XCD id to probe[blockIdx.x] and exits
+};
+
+// The two launches: the GDN mixer (stages kXsInGdn, kXsGdn, kXsOutPart) and
+// the MLP (kXsGateUp, kXsDownPart); XcdArgs::table points at the launch's first stage.
+enum : int { kXcdMixer = 0, kXcdMlp = 1 };
+constexpr uint32_t kXcdStages[2] = {3, 2};
+
+// 1: the Qwen3.5-4B shapes with bf16 activations; 0: not built.
+int xcd_shape_id(uint32_t hidden, uint32_t inter, uint32_t z_dim, uint32_t dk, bool half);
+const void* xcd_kernel_ptr(int shape, int launch);
+hipError_t xcd_launch(int shape, int launch, const XcdArgs& a, uint32_t blocks, hipStream_t stream);
+// out = base + parts[0] + ... + parts[nparts-1] (fp32, in that order), stored in
+// the activation dtype: the residual stream of the XCD-split decode made whole.
+hipError_t xsum_launch(const void* base, bool base_f32, const float* parts, uint32_t nparts, uint32_t n,
+                       void* out, bool out_f32, hipStream_t stream);
+const void* xsum_kernel_ptr();
 
 // ------------------------------------------------------------------ prefill (T tokens per launch)
 

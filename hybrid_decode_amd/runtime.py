@@ -258,42 +258,49 @@ def inv_freq_dev(cfg, device="cuda") -> torch.Tensor:
 
 # --------------------------------------------------------------------------- persistent decode
 
+def _stack_desc(kinds, layers, states, kvs, inv_freq, positions, tail):
+    """Q35DecodeStackDesc of a stack (and the host array it points into)."""
+    import ctypes as C
+    n = len(kinds)
+    arr = (B.Q35StackLayer * n)()
+    for i, kind in enumerate(kinds):
+        if kind == "gdn":
+            arr[i].kind = B.Q35_LAYER_LINEAR
+            arr[i].linear = C.pointer(layers[i].struct)
+            arr[i].state = C.pointer(states[i].struct)
+        else:
+            arr[i].kind = B.Q35_LAYER_FULL
+            arr[i].full = C.pointer(layers[i].struct)
+            arr[i].kv = C.pointer(kvs[i].struct)
+    d = B.Q35DecodeStackDesc()
+    d.n_layers = n
+    d.layers = arr
+    d.inv_freq = ptr(inv_freq)
+    d.positions = ptr(positions)
+    if tail is not None:
+        d.lm_head = C.pointer(tail["lm_head"].struct)
+        d.final_norm = ptr(tail["final_norm"])
+        d.embed = ptr(tail["embed"])
+        d.tokens = ptr(tail["tokens"])
+        d.logits = ptr(tail.get("logits"))
+        d.history = ptr(tail.get("history"))
+        d.history_len = tail.get("history_len", 0)
+        d.history_base = tail.get("history_base", 0)
+    return arr, d
+
+
 class DecodePlan:
     """A stack's layers (and optionally its tail) run by the persistent decode
     kernel: ``step()`` is one cooperative launch per token."""
 
     def __init__(self, cfg, kinds, layers, states, kvs, inv_freq, positions, tail=None,
                  device: int = 0):
-        import ctypes as C
         self.cfg, self.kinds, self.device = cfg, list(kinds), device
         self.c = cfg_struct(cfg)
         self.k = kernels(device)
         n = len(kinds)
-        arr = (B.Q35StackLayer * n)()
-        for i, kind in enumerate(kinds):
-            if kind == "gdn":
-                arr[i].kind = B.Q35_LAYER_LINEAR
-                arr[i].linear = C.pointer(layers[i].struct)
-                arr[i].state = C.pointer(states[i].struct)
-            else:
-                arr[i].kind = B.Q35_LAYER_FULL
-                arr[i].full = C.pointer(layers[i].struct)
-                arr[i].kv = C.pointer(kvs[i].struct)
-        d = B.Q35DecodeStackDesc()
-        d.n_layers = n
-        d.layers = arr
-        d.inv_freq = ptr(inv_freq)
-        d.positions = ptr(positions)
+        arr, d = _stack_desc(kinds, layers, states, kvs, inv_freq, positions, tail)
         self.tail = tail
-        if tail is not None:
-            d.lm_head = C.pointer(tail["lm_head"].struct)
-            d.final_norm = ptr(tail["final_norm"])
-            d.embed = ptr(tail["embed"])
-            d.tokens = ptr(tail["tokens"])
-            d.logits = ptr(tail.get("logits"))
-            d.history = ptr(tail.get("history"))
-            d.history_len = tail.get("history_len", 0)
-            d.history_base = tail.get("history_base", 0)
         self._keep = (arr, d, layers, states, kvs, inv_freq, positions)
         nbytes = B.q35_decode_workspace_bytes(self.k, self.c, d)
         self.ws = torch.zeros(nbytes + 256, dtype=torch.uint8, device=f"cuda:{device}")
@@ -327,6 +334,54 @@ class DecodePlan:
             pass
 
 
+# --------------------------------------------------------------------------- XCD-split decode
+
+class XcdPlan:
+    """A stack's layers (and optionally its tail) with the steps that split over
+    the eight XCDs joined per launch: ``step()`` enqueues one token (two launches
+    per GDN layer, four per full-attention layer, then the tail)."""
+
+    def __init__(self, cfg, kinds, layers, states, kvs, inv_freq, positions, tail=None,
+                 device: int = 0):
+        self.cfg, self.kinds, self.device = cfg, list(kinds), device
+        self.c = cfg_struct(cfg)
+        self.k = kernels(device)
+        arr, d = _stack_desc(kinds, layers, states, kvs, inv_freq, positions, tail)
+        self.tail = tail
+        self._keep = (arr, d, layers, states, kvs, inv_freq, positions)
+        nbytes = B.q35_xcd_workspace_bytes(self.k, self.c, d)
+        self.ws = torch.zeros(nbytes + 256, dtype=torch.uint8, device=f"cuda:{device}")
+        off = (-self.ws.data_ptr()) % 256
+        self.plan = B.q35_xcd_plan_create(self.k, self.c, d, self.ws.data_ptr() + off, nbytes)
+        self._bufs = B.q35_xcd_buffers(self.plan)
+
+    def step(self, stream=None) -> None:
+        B.q35_xcd_step(self.plan, stream_ptr(stream))
+
+    def check(self) -> int:
+        """Error word of the plan (0: every wait completed, every block on its XCD)."""
+        return B.q35_xcd_check(self.plan)
+
+    def _view(self, p: int, n: int, dtype) -> torch.Tensor:
+        o = p - self.ws.data_ptr()
+        nb = n * torch.empty((), dtype=dtype).element_size()
+        return self.ws[o:o + nb].view(dtype)
+
+    def layer_input(self, layer: int) -> torch.Tensor:
+        """The first layer's input (0) or the last layer's output (n_layers), act [hidden]."""
+        return self._view(B.q35_xcd_layer_input(self.plan, layer), self.cfg.hidden, act_dtype(self.cfg))
+
+    def buffer(self, name: str, n: int, dtype=torch.float32) -> torch.Tensor:
+        """View of one of the plan's shared buffers (Q35XcdBuffers field `name`)."""
+        return self._view(getattr(self._bufs, name), n, dtype)
+
+    def __del__(self):
+        try:
+            B.q35_xcd_plan_release(self.plan)
+        except Exception:
+            pass
+
+
 # --------------------------------------------------------------------------- decode stack
 
 class DecodeStack:
@@ -340,7 +395,7 @@ class DecodeStack:
 
     def __init__(self, cfg, kinds, layers, states, kvs, embed, final_norm, lm_head, start_pos: int,
                  start_token: int, history_len: int = 0, device: int = 0, taps: bool = False,
-                 persistent: bool = False):
+                 persistent: bool = False, xcd: bool = False):
         dev = f"cuda:{device}"
         self.cfg, self.kinds, self.device = cfg, list(kinds), device
         self.c = cfg_struct(cfg)
@@ -370,20 +425,21 @@ class DecodeStack:
         B.q35_embed_lookup(self.k, self.c, ptr(self.embed), ptr(self.tokens), ptr(self.x_embed),
                            stream_ptr())
         self.plan = None
-        if persistent:
+        if persistent or xcd:
             tail = {"lm_head": self.lm_head, "final_norm": self.final_norm, "embed": self.embed,
                     "tokens": self.tokens, "logits": self.logits,
                     "history": self.history if history_len else None,
                     "history_len": history_len, "history_base": self.history_base}
-            self.plan = DecodePlan(cfg, self.kinds, self.layers, self.states, self.kvs,
-                                   self.inv_freq, self.positions, tail, device)
+            cls = XcdPlan if xcd else DecodePlan
+            self.plan = cls(cfg, self.kinds, self.layers, self.states, self.kvs,
+                            self.inv_freq, self.positions, tail, device)
 
     @property
     def weight_bytes(self) -> int:
         return sum(l.weight_bytes for l in self.layers) + self.lm_head.nbytes
 
     def step(self, stream=None, write_logits: bool = True) -> None:
-        if self.plan is not None:  # one persistent launch (logits always written when held)
+        if self.plan is not None:  # the plan's launches (logits always written when held)
             self.plan.step(stream)
             return
         s = stream_ptr(stream)

@@ -244,6 +244,9 @@ typedef struct FullAttentionLayer {
  *   the method's.  Without a status word the condition goes unreported.
  */
 #define Q35_STATUS_POS_RANGE 2u
+/* Error bit of the XCD-split plan: a block read an XCD id outside [0, 8) (its
+ * results are invalid). */
+#define Q35_STATUS_XCD_MAP 4u
 typedef struct FullAttentionScratch {
     float* q_full;
     float* k;
@@ -583,6 +586,86 @@ q35_status q35_decode_stage_layout(const Q35DecodePlan* plan, uint32_t* n_stages
  */
 q35_status q35_decode_stage_times(const Q35DecodePlan* plan, uint64_t* ticks, uint32_t n,
                                   uint64_t* ticks_per_second);
+
+/* ------------------------------------------------------------------ XCD-split decode plan
+ *
+ * The same token as the per-layer calls and the persistent plan (the layer
+ * forwards of the linear_attention.rs and full_attention.rs pages, then the
+ * final RMSNorm, lm_head and greedy token), launched so that the steps whose
+ * work splits over MI355X's eight XCDs share one launch: a GDN layer is two
+ * launches (mixer: in-projection, conv, gate/beta, gated delta rule, gated
+ * norm, out-projection; MLP: gate/up, SwiGLU, down), a full-attention layer
+ * four (q/k/v; attention; o_proj; MLP).  XCD x takes v-heads
+ * [Hv/8 x, Hv/8 (x+1)) of the mixer and intermediate rows
+ * [I/8 x, I/8 (x+1)) of the MLP; the out-projection and down then leave
+ * eight fp32 partial sums, which the next launch adds to the residual in a
+ * fixed order (base, partial 0, ..., partial 7).  The residual stream is
+ * rounded to the activation dtype where the per-layer calls store it (each
+ * layer's input and the stack's output).  Built for the Qwen3.5-4B shapes with
+ * bf16 activations on a device of 8 x 32 compute units whose one-block-per-CU
+ * grids place the blocks of one residue class of the block index mod 8 on each
+ * XCD (checked at creation; every block takes its share from the XCD id it reads).
+ * Any KV format of the per-layer calls.
+ */
+typedef struct Q35XcdPlan Q35XcdPlan;
+
+/* Device workspace q35_xcd_plan_create needs for this stack. */
+q35_status q35_xcd_workspace_bytes(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                                   const Q35DecodeStackDesc* stack, size_t* bytes);
+
+/*
+ * Validates the stack (as the per-layer calls do), checks the placement of a
+ * one-block-per-CU grid, writes the per-XCD stage table into the caller's
+ * device workspace (256-byte aligned; synchronous copy), clears the sync words
+ * and, with a tail, writes the embedding of tokens[0] into the first layer's
+ * input.  `kernels` and the stack's device arrays must outlive the plan; the
+ * host structs of the description are copied.  The workspace must not be used
+ * by anything else while the plan lives.  Errors: Q35_ERR_UNSUPPORTED (shapes,
+ * compute-unit count, placement), Q35_ERR_INVALID_ARG (as the per-layer calls;
+ * workspace too small), Q35_ERR_HIP.
+ */
+q35_status q35_xcd_plan_create(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
+                               const Q35DecodeStackDesc* stack, void* workspace, size_t workspace_bytes,
+                               Q35XcdPlan** out);
+void q35_xcd_plan_release(Q35XcdPlan* plan);
+
+/* One token at cache position positions[0] (read on the device): every layer,
+ * then the tail.  Enqueued on `stream`; capturable.  Steps of one plan must not
+ * overlap (one stream). */
+q35_status q35_xcd_step(const Q35XcdPlan* plan, hipStream_t stream);
+
+/*
+ * Synchronises the device and reads the plan's error word (bits accumulated
+ * over its steps): bit 0 (1) when a wait among the blocks of an XCD gave up
+ * after its time limit; Q35_STATUS_POS_RANGE when positions[0] lay outside a
+ * layer's cache; Q35_STATUS_XCD_MAP when a block read an XCD id outside [0, 8).  With any bit set the tokens since the plan was created are
+ * not the method's; create a new plan.  The kernels exit normally in every case.
+ */
+q35_status q35_xcd_check(const Q35XcdPlan* plan, uint32_t* error_word);
+
+/* Device pointer (act [hidden]) of the first layer's input (layer 0: without a
+ * tail the caller writes each token's input there before the step) or of the
+ * last layer's output (layer == n_layers).  Other layers' inputs are not held
+ * as whole vectors: Q35_ERR_OUT_OF_RANGE. */
+q35_status q35_xcd_layer_input(const Q35XcdPlan* plan, uint32_t layer, void** x);
+
+/* Device buffers of the plan, shared by all layers: after a step they hold the
+ * values of the last layer that wrote them (of the only layer, in a one-layer
+ * plan).  fp32 unless noted. */
+typedef struct Q35XcdBuffers {
+    void* x_in;        /* act [hidden]: the layer input, as summed and rounded */
+    float* qkv_conv;   /* [qkv_total_lin]: conv + SiLU output (GDN) */
+    float* z;          /* [Hv * dv] */
+    float* gate;       /* [Hv]: decay gate */
+    float* beta;       /* [Hv] */
+    float* y;          /* [Hv * dv]: recurrence output, before the gated norm */
+    float* out_parts;  /* [8][hidden]: out-projection partial sums (GDN) */
+    float* mlp_act;    /* [intermediate]: silu(gate) * up */
+    float* mlp_parts;  /* [8][hidden]: down partial sums */
+    float* x_mid;      /* [hidden]: x_in + o_proj output (full attention) */
+    float* x_resid;    /* [hidden]: the residual after the mixer (the MLP's base) */
+} Q35XcdBuffers;
+q35_status q35_xcd_buffers(const Q35XcdPlan* plan, Q35XcdBuffers* bufs);
 
 /* ------------------------------------------------------------------ kernel-level export */
 
