@@ -100,6 +100,10 @@ q35_status opt(const void* p, const char* what) {
 constexpr uint32_t kAttnTargetBlocks = 512;
 constexpr uint32_t kAttnMaxChunk = 2048;
 
+// Rows per block: the share of kAttnTargetBlocks blocks, rounded up to whole
+// iterations.  Measured at position 8192 (attention steps of 8 layers): chunks
+// of 96 rows (344 blocks) 17.8 us a layer, 64 rows (516 blocks) 21.0 us, 128
+// rows (260 blocks) 19.7 us; more blocks repeat the q prologue more often.
 uint32_t attn_chunk(const Qwen35ForwardConfig& c, uint32_t n) {
     const uint32_t rpi = attn_rows_per_iter(c.head_dim);
     uint64_t want = ((uint64_t)n * c.num_kv_heads + kAttnTargetBlocks - 1) / kAttnTargetBlocks;
