@@ -159,3 +159,63 @@ def test_prefill_in_two_pieces_equals_one_pass(gen):
     a2, kv2, _ = O.prefill.prefill_full_attention(cfgf, lay, kv1, inv, xf[4:], pos + 4)
     assert np.array_equal(outf, np.concatenate([a1, a2]))
     assert np.array_equal(kvf["k"], kv2["k"]) and np.array_equal(kvf["v"], kv2["v"])
+
+
+# --------------------------------------------------------------------------- quantised caches
+
+QUANT_FORMATS = ["turbo8", "turbo4", "turbo3", "turbo2", "bf16k_turbo4v", "bf16k_turbo3v", "bf16k_turbo2v"]
+
+
+def _quant_case(gen, fmt, T, cache_pos, cap):
+    cfg = synth.tiny("f32")
+    layer = synth.full_layer(gen, cfg, f"pfq.{fmt}")
+    if fmt == "turbo8":
+        kv = synth.kv_cache_turbo8(gen, cfg, f"pfq.{fmt}", cap, cache_pos)
+    else:
+        kv = synth.kv_cache_lm(gen, cfg, f"pfq.{fmt}", cap, cache_pos, fmt)
+    x = gen.act(f"pfq.{fmt}.x", (T, cfg.hidden), "f32")
+    inv = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
+    return cfg, layer, kv, x, inv
+
+
+def _turbo_forward(fmt, cfg, layer, kv, inv, x, pos, sparse_v):
+    if fmt == "turbo8":
+        return O.turbo8.forward_full_attention_turbo8(cfg, layer, kv, inv, x, pos, sparse_v=sparse_v)
+    return O.turbo_lm.forward_full_attention(fmt, cfg, layer, kv, inv, x, pos, sparse_v=sparse_v)
+
+
+@pytest.mark.parametrize("fmt", QUANT_FORMATS)
+def test_quantised_prefill_is_the_formats_decode_loop(gen, fmt):
+    """A prompt into a quantised cache is the format's decode step per token:
+    one token equals the step, the cache rows [pos, pos + T) are the only rows
+    written, and two pieces equal one pass (state carried through the cache)."""
+    T, pos, cap = 6, 9, 24
+    cfg, layer, kv, x, inv = _quant_case(gen, fmt, T, pos, cap)
+    for tau in (0.0, 0.05):
+        o1, kv1, _ = O.prefill.prefill_full_attention(cfg, layer, kv, inv, x[:1], pos, fmt=fmt, sparse_v=tau)
+        r1, rkv1, _ = _turbo_forward(fmt, cfg, layer, kv, inv, x[0], pos, tau)
+        assert np.array_equal(o1[0], r1)
+        for name in rkv1:
+            assert np.array_equal(kv1[name], rkv1[name]), name
+    out, new, _ = O.prefill.prefill_full_attention(cfg, layer, kv, inv, x, pos, fmt=fmt, sparse_v=0.0)
+    for name, a in new.items():
+        if not isinstance(a, np.ndarray) or a.ndim == 0 or a.shape[0] != cap:
+            continue
+        rows = np.nonzero(np.any((a != kv[name]).reshape(cap, -1), axis=1))[0]
+        assert set(rows.tolist()) <= set(range(pos, pos + T)), name
+        assert np.array_equal(a[:pos], kv[name][:pos]) and np.array_equal(a[pos + T:], kv[name][pos + T:])
+    a1, k1, _ = O.prefill.prefill_full_attention(cfg, layer, kv, inv, x[:2], pos, fmt=fmt, sparse_v=0.0)
+    a2, k2, _ = O.prefill.prefill_full_attention(cfg, layer, k1, inv, x[2:], pos + 2, fmt=fmt, sparse_v=0.0)
+    assert np.array_equal(out, np.concatenate([a1, a2]))
+    for name in new:
+        assert np.array_equal(np.asarray(new[name]), np.asarray(k2[name])), name
+
+
+def test_quantised_prefill_honours_the_sparse_v_threshold(gen):
+    T, pos, cap = 5, 40, 48
+    cfg, layer, kv, x, inv = _quant_case(gen, "turbo4", T, pos, cap)
+    o0, _, _ = O.prefill.prefill_full_attention(cfg, layer, kv, inv, x, pos, fmt="turbo4", sparse_v=0.0)
+    o3, _, _ = O.prefill.prefill_full_attention(cfg, layer, kv, inv, x, pos, fmt="turbo4", sparse_v=0.3)
+    assert not np.array_equal(o0, o3)
+    with pytest.raises(ValueError):
+        O.prefill.prefill_full_attention(cfg, layer, kv, inv, x, pos, fmt="turbo5")
