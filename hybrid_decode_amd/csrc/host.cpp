@@ -1029,6 +1029,7 @@ namespace {
 struct PfWs {
     size_t xh, qkv, z, fa, fb, qkvs, lg, beta, wc, uc, pc, lc, y, yz, r, h;  // GDN
     size_t qf, kf, vf, qb, ga;                                               // full (xh, r, h shared)
+    size_t gaf, pos;                                                         // full, quantised caches
     size_t part;                                                             // split GEMM partial tiles
     uint32_t nch;
     size_t bytes;
@@ -1069,6 +1070,8 @@ PfWs pf_ws_layout(const Qwen35ForwardConfig& c, uint32_t T) {
     w.vf = take(o, t * kv_dim(c) * 4);
     w.qb = take(o, t * q_only(c) * 2);
     w.ga = take(o, t * q_only(c) * 2);
+    w.gaf = take(o, t * q_only(c) * 4);
+    w.pos = take(o, t * 4);
     o = gdn > o ? gdn : o;
     w.part = take(o, T ? kPfSplitBytes : 0);
     w.bytes = o;
@@ -1245,19 +1248,27 @@ q35_status q35_prefill_full_attention(const Qwen35Kernels* kernels, const Qwen35
     if (!layer || !kv) return fail(Q35_ERR_INVALID_ARG, "NULL argument");
     const Qwen35ForwardConfig& c = *cfg;
     Q35_TRY(check_full_layer(c, *layer));
-    Q35_TRY(check_kv(*kv, false));
+    Q35_TRY(check_kv(*kv, true));
     Q35_TRY(need(inv_freq, "inv_freq", false));
     Q35_TRY(need(x_in, "x_in", false));
     Q35_TRY(need(x_out, "x_out", false));
     const uint32_t G = c.num_heads / c.num_kv_heads;
-    if (!pf_attn_dims_supported(c.head_dim, G))
+    const bool quant = kv->dtype != Q35_KV_BF16;
+    if (!quant && !pf_attn_dims_supported(c.head_dim, G))
         return fail(Q35_ERR_UNSUPPORTED, "prefill attention head_dim %u, group %u", c.head_dim, G);
+    if (quant && !attn_dims_supported(c.head_dim, G))
+        return fail(Q35_ERR_UNSUPPORTED, "attention head_dim %u, group %u", c.head_dim, G);
     if ((uint64_t)cache_pos + n_tokens > kv->capacity)
         return fail(Q35_ERR_OUT_OF_RANGE, "cache_pos %u + %u tokens > capacity %u", cache_pos, n_tokens,
                     kv->capacity);
     PfWs w;
     Q35_TRY(pf_check_ws(c, n_tokens, workspace, workspace_bytes, &w));
     if (n_tokens == 0) return ok();
+    // a quantised cache: the per-token attention's partials use the split-GEMM area
+    const AttnWs aws = attn_ws_layout(c, kv->capacity);
+    if (quant && aws.total > kPfSplitBytes)
+        return fail(Q35_ERR_UNSUPPORTED, "capacity %u: attention partials exceed the prefill workspace",
+                    kv->capacity);
     const uint32_t T = n_tokens;
     const bool f32 = c.act_dtype == Q35_ACT_F32;
     void* ws = workspace;
@@ -1270,6 +1281,32 @@ q35_status q35_prefill_full_attention(const Qwen35Kernels* kernels, const Qwen35
     Q35_HIP(pf_rmsnorm_launch(x_in, f32, l.input_ln, xh, T, c.hidden, c.rms_eps, stream), "prefill input norm");
     Q35_TRY(pf_gemm(sp, "prefill q/k/v", kPfF32, xh, T, {&l.q_proj, &l.k_proj, &l.v_proj}, {qf, kf, vf}, 0, nullptr,
                     false, true, stream));
+    uint16_t* ga = at_off<uint16_t>(ws, w.ga);
+    if (quant) {
+        // A quantised cache: each prompt token runs the decode attention steps (q/k
+        // norm, RoPE, the quantising append of its row, attention over the rows as
+        // stored, sparse-V gate, sigmoid gate), in token order; the projections
+        // around them stay batched.
+        int32_t* pos = at_off<int32_t>(ws, w.pos);
+        float* gaf = at_off<float>(ws, w.gaf);
+        Q35_HIP(pf_iota_launch(pos, T, (int32_t)cache_pos, stream), "prefill positions");
+        FullAttentionScratch s{};
+        s.workspace = at_off<void>(ws, w.part);
+        s.workspace_bytes = kPfSplitBytes;
+        for (uint32_t t = 0; t < T; ++t) {
+            s.q_full = qf + (size_t)t * q_total(c);
+            s.k = kf + (size_t)t * kv_dim(c);
+            s.v = vf + (size_t)t * kv_dim(c);
+            s.gated_attn = gaf + (size_t)t * q_only(c);
+            Q35_TRY(launch_attention(kernels, c, layer, &s, kv, aws, inv_freq, pos + t, (int64_t)cache_pos + t,
+                                     cache_pos + t + 1, stream));
+        }
+        Q35_HIP(pf_cast_f16_launch(gaf, ga, T * q_only(c), stream), "prefill attention output");
+        Q35_TRY(pf_gemm(sp, "prefill o_proj", kPfResid, ga, T, {&l.o_proj}, {at_off<float>(ws, w.r)}, c.hidden,
+                        x_in, f32, true, stream));
+        Q35_TRY(pf_mlp(sp, c, l, w, ws, T, x_out, stream));
+        return ok();
+    }
     PfRopeArgs rp{};
     rp.q_full = qf;
     rp.k = kf;
@@ -1292,7 +1329,7 @@ q35_status q35_prefill_full_attention(const Qwen35Kernels* kernels, const Qwen35
     at.q_full = qf;
     at.kc = rp.kc;
     at.vc = rp.vc;
-    at.ga = at_off<uint16_t>(ws, w.ga);
+    at.ga = ga;
     at.T = T;
     at.cache_pos = cache_pos;
     at.hq = c.num_heads;

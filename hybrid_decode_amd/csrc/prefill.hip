@@ -1047,9 +1047,36 @@ __global__ __launch_bounds__((64 * G * flash_wph<D, G>())) void flash_kernel(PfA
         }
 }
 
+// ---------------------------------------------------------------------- quantised caches
+
+// Cache positions base, base + 1, ... of the prompt's tokens (the per-token
+// attention of a quantised cache reads its RoPE position from memory).
+__global__ __launch_bounds__(256) void iota_kernel(int32_t* out, uint32_t n, int32_t base) {
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i < n) out[i] = base + (int32_t)i;
+}
+
+// fp32 -> f16 (round to nearest even), the o-projection GEMM's operand.
+__global__ __launch_bounds__(256) void cast_f16_kernel(const float* x, uint16_t* y, uint32_t n) {
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i < n) y[i] = __builtin_bit_cast(uint16_t, (_Float16)x[i]);
+}
+
 }  // namespace pf
 
 // ====================================================================== launchers
+
+hipError_t pf_iota_launch(int32_t* out, uint32_t n, int32_t base, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    pf::iota_kernel<<<(n + 255) / 256, 256, 0, s>>>(out, n, base);
+    return hipGetLastError();
+}
+
+hipError_t pf_cast_f16_launch(const float* x, uint16_t* y, uint32_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    pf::cast_f16_kernel<<<(n + 255) / 256, 256, 0, s>>>(x, y, n);
+    return hipGetLastError();
+}
 
 const void* pf_kernel_ptr(int i) {
     static const void* const k[] = {
@@ -1072,6 +1099,8 @@ const void* pf_kernel_ptr(int i) {
         reinterpret_cast<const void*>(pf::qk_rope_append_kernel),
         reinterpret_cast<const void*>(pf::flash_kernel<64, 2>),
         reinterpret_cast<const void*>(pf::flash_kernel<256, 4>),
+        reinterpret_cast<const void*>(pf::iota_kernel),
+        reinterpret_cast<const void*>(pf::cast_f16_kernel),
     };
     return i >= 0 && i < (int)(sizeof(k) / sizeof(k[0])) ? k[i] : nullptr;
 }

@@ -407,6 +407,10 @@ struct PfAttnArgs {
 };
 bool pf_attn_dims_supported(uint32_t head_dim, uint32_t group);
 hipError_t pf_attn_launch(const PfRopeArgs& r, const PfAttnArgs& a, hipStream_t s);
+// The prompt's cache positions base + i into out[n], and an fp32 -> f16 cast
+// (the per-token attention path of a quantised cache).
+hipError_t pf_iota_launch(int32_t* out, uint32_t n, int32_t base, hipStream_t s);
+hipError_t pf_cast_f16_launch(const float* x, uint16_t* y, uint32_t n, hipStream_t s);
 // the prefill kernels, i = 0, 1, ... until nullptr (for the load check at resolve)
 const void* pf_kernel_ptr(int i);
 

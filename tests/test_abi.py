@@ -264,12 +264,14 @@ def test_prefill_errors_before_any_launch(lib):
     with pytest.raises(B.Q35Error) as e:
         B.q35_prefill_full_attention(FAKE_KERNELS, c, full, kv, fake, fake, 100, 29, fake, fake, ws_bytes, None)
     assert e.value.status == B.Q35_ERR_OUT_OF_RANGE
-    # the prefill appends bf16 rows only
+    # a quantised cache so long that its attention partials exceed the split area
     kv.dtype = B.q35_kv_dtype_from_str("turbo8")
     kv.k_scales, kv.v_scales = fake, fake
+    kv.capacity = 1 << 23
     with pytest.raises(B.Q35Error) as e:
         B.q35_prefill_full_attention(FAKE_KERNELS, c, full, kv, fake, fake, 10, 0, fake, fake, ws_bytes, None)
-    assert e.value.status == B.Q35_ERR_UNSUPPORTED
+    assert e.value.status == B.Q35_ERR_UNSUPPORTED and "capacity" in str(e.value)
+    kv.capacity = 128
     # a NULL weight
     lin.in_proj_z.codes = None
     with pytest.raises(B.Q35Error) as e:

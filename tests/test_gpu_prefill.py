@@ -167,11 +167,12 @@ def test_prefill_gdn_then_decode_continues_the_state(rt, gen):
 # --------------------------------------------------------------------------- full-attention layer
 
 
-def _full_run(rt, cfg, layer, kv, x, pos):
+def _full_run(rt, cfg, layer, kv, x, pos, sparse_v=None):
     from hybrid_decode_amd import binding as B
     T = x.shape[0]
     cs = rt.cfg_struct(cfg)
-    L, K = rt.FullLayerDev(layer), rt.KvCacheDev(kv)
+    L = rt.FullLayerDev(layer)
+    K = rt.KvCacheDev(kv) if sparse_v is None else rt.KvCacheDev(kv, sparse_v=sparse_v)
     inv = torch.from_numpy(O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)).cuda()
     xin = rt.to_dev(x)
     xout = torch.empty_like(xin)
@@ -447,3 +448,87 @@ def test_prefill_full_4b_4096_tokens(rt, gen):
         r = O.bf16_to_f64(rkv[s]).reshape(BIG_T, -1)
         say(f"  cache {s} against the oracle: rel {_rows_rel(g, r):.2e}")
         assert _rows_rel(g, r) < 4e-3, s
+
+
+# --------------------------------------------------------------------------- quantised caches
+
+QFORMATS = ["turbo8", "turbo4", "turbo3", "turbo2", "bf16k_turbo4v", "bf16k_turbo3v", "bf16k_turbo2v"]
+
+
+def _qcache(gen, cfg, fmt, prefix, cap, filled):
+    if fmt == "turbo8":
+        return synth.kv_cache_turbo8(gen, cfg, prefix, cap, filled)
+    return synth.kv_cache_lm(gen, cfg, prefix, cap, filled, fmt)
+
+
+def _qrows(fmt, kv, side, rows):
+    """Dequantised (rotated-basis) rows of one side of a quantised cache, or the
+    bf16 keys of an asymmetric format."""
+    from oracle import turbo8 as T8, turbo_lm as TL
+    if fmt == "turbo8":
+        return T8.turbo8_dequantize(kv[side][rows], kv[side + "_scales"][rows])
+    kq, bits = TL.FORMATS[fmt]
+    if side == "k" and not kq:
+        return O.bf16_to_f64(kv["k"][rows])
+    return TL.dequantize(kv[side][rows], kv[side + "_scales"][rows], bits)
+
+
+def _check_qcache(fmt, after, before, ref, pos, T):
+    """Only rows [pos, pos + T) change, and each side holds the oracle's rows up
+    to the quantisation flips that the projections' f16 rounding can cause
+    (one step of a code in a few elements): rel 5e-2 per side."""
+    for name, a in after.items():
+        if not isinstance(a, np.ndarray) or a.ndim == 0:
+            continue
+        cap = a.shape[0]
+        changed = np.nonzero(np.any((a != before[name]).reshape(cap, -1), axis=1))[0]
+        assert set(changed.tolist()) <= set(range(pos, pos + T)), name
+    rows = slice(pos, pos + T)
+    for side in ("k", "v"):
+        r = rel(_qrows(fmt, after, side, rows), _qrows(fmt, ref, side, rows))
+        assert r < 5e-2, (fmt, side, r)
+
+
+@pytest.mark.parametrize("fmt", QFORMATS)
+def test_prefill_full_quantised_tiny(rt, gen, fmt):
+    """A prompt into a quantised cache (per-token attention, sparse-V off on both
+    sides) against the oracle's decode loop of the format."""
+    pos, T = 37, 48
+    say(f"prefill full tiny into {fmt} pos={pos} T={T}")
+    cfg = synth.tiny("f32")
+    layer = synth.full_layer(gen, cfg, f"pfq.{fmt}")
+    cap = pos + T + 16
+    kv = _qcache(gen, cfg, fmt, f"pfq.{fmt}", cap, pos)
+    x = gen.act(f"pfq.{fmt}.x", (T, cfg.hidden), "f32")
+    before = {k: np.array(v, copy=True) for k, v in kv.items() if isinstance(v, np.ndarray)}
+    out, after = _full_run(rt, cfg, layer, kv, x, pos, sparse_v=0.0)
+    inv = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
+    ref, rkv, _ = O.prefill.prefill_full_attention(cfg, layer, kv, inv, x, pos, fmt=fmt, sparse_v=0.0)
+    assert np.isfinite(out).all()
+    r = _rows_rel(out, ref)
+    say(f"  {fmt}: worst token rel {r:.2e}")
+    assert r < TOL_BF16
+    _check_qcache(fmt, after, before, rkv, pos, T)
+
+
+@pytest.mark.parametrize("fmt", ["turbo8", "bf16k_turbo4v", "turbo2"])
+def test_prefill_full_quantised_4b_after_4096_cached_rows(rt, gen, fmt):
+    """The 4B layer, a 16-token prompt after 4096 cached rows, the pages' default
+    sparse-V threshold on both sides."""
+    pos, T = 4096, 16
+    say(f"prefill full 4B into {fmt} pos={pos} T={T}")
+    cfg = synth.qwen3_5_4b("bf16")
+    layer = synth.full_layer(gen, cfg, f"pfq4.{fmt}")
+    cap = pos + T + 32
+    kv = _qcache(gen, cfg, fmt, f"pfq4.{fmt}", cap, pos)
+    x = gen.act(f"pfq4.{fmt}.x", (T, cfg.hidden), "bf16")
+    before = {k: np.array(v, copy=True) for k, v in kv.items() if isinstance(v, np.ndarray)}
+    out, after = _full_run(rt, cfg, layer, kv, x, pos)
+    inv = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
+    say("  oracle loop")
+    ref, rkv, _ = O.prefill.prefill_full_attention(cfg, _dense32(layer), kv, inv, x, pos, fmt=fmt)
+    assert np.isfinite(out).all()
+    r = _rows_rel(out, ref)
+    say(f"  {fmt}: worst token rel {r:.2e}")
+    assert r < TOL_BF16
+    _check_qcache(fmt, after, before, rkv, pos, T)
