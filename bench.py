@@ -381,6 +381,61 @@ def long_context(torch, B, rt, synth, workloads, args, kv_bytes):
     return out
 
 
+KV_FORMATS = ["bf16", "turbo8", "turbo4", "turbo3", "turbo2", "bf16k_turbo4v", "bf16k_turbo3v", "bf16k_turbo2v"]
+
+
+def attention_formats(torch, B, rt, synth, pos, rounds=8, copies=8):
+    """The attention steps alone (q35_attention_devpos) at cache position pos for
+    every KV format: `copies` device copies of one layer's synthetic cache (more
+    bytes than the last-level cache holds), each quantised format with the
+    sparse-V gate at the pages' default and off.  Host-event time per layer."""
+    from synth import qwen3_5_4b, full_layer, kv_cache, kv_cache_turbo8, kv_cache_lm
+    cfg = qwen3_5_4b("bf16")
+    g = synth.Gen(0)
+    cap = pos + 64
+    layer = rt.FullLayerDev(full_layer(g, cfg, "af.L"))
+    inv = rt.inv_freq_dev(cfg)
+    posd = torch.tensor([pos], dtype=torch.int32, device="cuda")
+    out = {"workload": f"attention steps of one Qwen3.5-4B full-attention layer at cache position {pos}, "
+                       f"{copies} cache copies in turn", "pos": pos, "formats": {}}
+    for fmt in KV_FORMATS:
+        log(f"attention at {pos}: {fmt}")
+        if fmt == "bf16":
+            kv = kv_cache(g, cfg, f"af.{fmt}", cap, pos)
+        elif fmt == "turbo8":
+            kv = kv_cache_turbo8(g, cfg, f"af.{fmt}", cap, pos)
+        else:
+            kv = kv_cache_lm(g, cfg, f"af.{fmt}", cap, pos, fmt)
+        res = {}
+        for tau in ([None] if fmt == "bf16" else [rt.KvCacheDev.SPARSE_V_DEFAULT, 0.0]):
+            kvs = [rt.KvCacheDev(kv) if tau is None else rt.KvCacheDev(kv, sparse_v=tau) for _ in range(copies)]
+            scr = rt.FullScratchDev(cfg, cap)
+            scr.t["q_full"].normal_()
+            scr.t["k"].normal_()
+            scr.t["v"].normal_()
+            s = rt.stream_ptr()
+
+            def run():
+                for kvd in kvs:
+                    B.q35_attention_devpos(rt.kernels(0), rt.cfg_struct(cfg), layer.struct, scr.struct,
+                                           kvd.struct, inv.data_ptr(), posd.data_ptr(), s)
+            run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(50_000_000)
+            e0.record()
+            for _ in range(rounds):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (rounds * copies)
+            res["default" if tau else ("off" if tau == 0.0 else "exact")] = round(us, 2)
+            del kvs, scr
+            torch.cuda.empty_cache()
+        out["formats"][fmt] = res
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -397,6 +452,9 @@ def main():
     ap.add_argument("--long-steps", type=int, default=32)
     ap.add_argument("--path", choices=["layers", "xcd"], default="layers",
                     help="decode launches: per-layer kernels, or the XCD-split plan (q35_xcd_*)")
+    ap.add_argument("--attn-formats", type=int, default=0, metavar="POS",
+                    help="only time the attention steps at cache position POS for every KV format "
+                         "(sparse-V gate at its default and off) and print one JSON line")
     ap.add_argument("--kv", choices=["bf16", "turbo8", "turbo4", "turbo3", "turbo2", "bf16k_turbo4v",
                                      "bf16k_turbo3v", "bf16k_turbo2v"], default="bf16",
                     help="KV cache format of the full-attention layers")
@@ -419,6 +477,9 @@ def main():
 
     torch.cuda.set_device(0)
     rt.kernels(0)
+    if args.attn_formats > 0:
+        print(json.dumps(attention_formats(torch, B, rt, synth, args.attn_formats)), flush=True)
+        return
     K, W = args.steps, args.warmup
     t0 = time.time()
     gen = synth.Gen(0)
