@@ -381,6 +381,104 @@ def long_context(torch, B, rt, synth, workloads, args, kv_bytes):
     return out
 
 
+def layer_configs(torch, B, rt, synth, workloads, rounds=5, copies=6):
+    """One 4B GDN layer for 256 sequential steps (GDN state N(0, 0.1), conv state
+    N(0, 1), a fresh N(0, 1) input row each step) and one 4B full-attention layer
+    for 64 steps at cache positions 4096..4159 (bf16 KV rows [0, 4096) N(0, 1)).
+    Step t runs on device copy t % copies of the layer's weights: identical
+    bytes at distinct addresses, more of them than the 256 MB last-level cache
+    holds, so every step streams its weights from HBM (the copies share one
+    state or one KV cache, so the results equal one copy's).  All steps of a run
+    are one captured HIP graph; per-step time from the median and the fastest of
+    `rounds` replays.  The same graph on one copy gives the cache-warm figure
+    (its weights fit in the last-level cache), reported beside it."""
+    import numpy as np
+    s_of = rt.stream_ptr
+    out = {}
+
+    def timed(graph, steps):
+        graph.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(rounds):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / steps)
+        return float(np.median(ts)), float(min(ts))
+
+    def entry(kind, workload, steps, bpstep, rot, warm):
+        (med, mn), (wmed, _) = rot, warm
+        gbs = bpstep / (med * 1e-6) / 1e9
+        log(f"{kind} layer, {steps} steps over {copies} weight copies: {med:.2f} us/step "
+            f"(min {mn:.2f}), {gbs:.0f} GB/s; one copy (cache-warm): {wmed:.2f} us/step")
+        return {"workload": workload, "steps": steps, "weight_copies": copies, "rounds": rounds,
+                "us_per_step": round(med, 2), "us_per_step_min": round(mn, 2),
+                "bytes_per_step": bpstep, "hbm_gbs": round(gbs, 1),
+                "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                "us_per_step_one_copy_cache_warm": round(wmed, 2)}
+
+    # GDN layer
+    w = workloads.gdn_layer_4b(synth.Gen(0))
+    cfg, H = w["cfg"], w["cfg"].hidden
+    k, c = rt.kernels(0), rt.cfg_struct(cfg)
+    Ls = [rt.GdnLayerDev(w["layer"]) for _ in range(copies)]
+    S, scr = rt.GdnStateDev(w["state"]), rt.GdnScratchDev(cfg)
+    xs = rt.to_dev(np.stack(w["xs"]))
+    xbuf = rt.act_empty(cfg, H)
+    steps = xs.shape[0]
+    graphs = []
+    for ncopy in (copies, 1):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for t in range(steps):
+                B.q35_forward_linear_attention(k, c, Ls[t % ncopy].struct, S.struct, scr.struct,
+                                               xs[t].data_ptr(), xbuf.data_ptr(), s_of())
+        graphs.append(g)
+    rot, warm = timed(graphs[0], steps), timed(graphs[1], steps)
+    bpstep = (Ls[0].weight_bytes + 2 * H * 2 * 2
+              + 2 * cfg.num_v_heads_lin * cfg.k_head_dim_lin * cfg.v_head_dim_lin * 4
+              + 2 * cfg.qkv_total_lin * cfg.conv_kernel_size * 4 + cfg.qkv_total_lin * cfg.conv_kernel_size * 2)
+    assert torch.isfinite(S.gdn_state).all(), "GDN state not finite"
+    out["gdn"] = entry("GDN", f"one Qwen3.5-4B-shaped GDN layer (int8 g64 weights, bf16 activations), "
+                              f"{steps} sequential single-token steps", steps, bpstep, rot, warm)
+    del graphs, Ls, S, scr, xs
+    torch.cuda.empty_cache()
+
+    # full-attention layer
+    w = workloads.full_layer_4b(synth.Gen(0))
+    cfg, start = w["cfg"], w["start"]
+    c = rt.cfg_struct(cfg)
+    Ls = [rt.FullLayerDev(w["layer"]) for _ in range(copies)]
+    kv = rt.KvCacheDev(w["kv"])
+    fs = rt.FullScratchDev(cfg, kv.capacity)
+    inv = rt.inv_freq_dev(cfg)
+    xs = rt.to_dev(np.stack(w["xs"]))
+    steps = xs.shape[0]
+    pos = torch.arange(start, start + steps, dtype=torch.int32, device="cuda")
+    graphs = []
+    for ncopy in (copies, 1):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for t in range(steps):
+                B.q35_forward_full_attention(k, c, Ls[t % ncopy].struct, fs.struct, kv.struct,
+                                             inv.data_ptr(), pos[t:t + 1].data_ptr(), xs[t].data_ptr(),
+                                             start + t, start + t + 1, s_of())
+        graphs.append(g)
+    rot, warm = timed(graphs[0], steps), timed(graphs[1], steps)
+    mean_len = start + (steps + 1) / 2.0   # rows attended per step, on average
+    bpstep = int(Ls[0].weight_bytes + 2 * H * 2 * 2 + mean_len * cfg.kv_dim * 2 * 2 + cfg.kv_dim * 2 * 2)
+    out["full"] = entry("full-attention", f"one Qwen3.5-4B-shaped gated full-attention layer (int8 g64 "
+                                          f"weights, bf16 activations, bf16 KV rows [0, {start}) N(0, 1)), "
+                                          f"{steps} steps at cache positions {start}..{start + steps - 1}",
+                        steps, bpstep, rot, warm)
+    del graphs, Ls, kv, fs, xs
+    torch.cuda.empty_cache()
+    return out
+
+
 KV_FORMATS = ["bf16", "turbo8", "turbo4", "turbo3", "turbo2", "bf16k_turbo4v", "bf16k_turbo3v", "bf16k_turbo2v"]
 
 
@@ -450,6 +548,8 @@ def main():
     ap.add_argument("--long-ctx", type=int, default=65536,
                     help="also time decode with every KV cache filled to this many positions (0: skip)")
     ap.add_argument("--long-steps", type=int, default=32)
+    ap.add_argument("--no-layer-configs", action="store_true",
+                    help="skip the single-layer runs (GDN 256 steps, full attention 64 steps, rotated weights)")
     ap.add_argument("--path", choices=["layers", "xcd"], default="layers",
                     help="decode launches: per-layer kernels, or the XCD-split plan (q35_xcd_*)")
     ap.add_argument("--attn-formats", type=int, default=0, metavar="POS",
@@ -654,6 +754,8 @@ def main():
         del graph, st
         torch.cuda.empty_cache()
         result["long_ctx"] = long_context(torch, B, rt, synth, workloads, args, kv_bytes)
+    if not args.no_layer_configs and args.kv == "bf16":
+        result["layer_configs"] = layer_configs(torch, B, rt, synth, workloads)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on whole tokens (weights dequantised once first)")
         toks = [first_token] + gpu_tokens

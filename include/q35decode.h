@@ -288,7 +288,8 @@ q35_status q35_full_attention_workspace_bytes(const Qwen35ForwardConfig* cfg, ui
  *   Turbo8 and Turbo4/3/2 the query heads, the new key and value are rotated
  *   before the quantising append and the attention output is rotated back; with
  *   Bf16K + TurboNV only the value is rotated (and the output rotated back).
- *   Attention is exact over all rows (the pages' sparse-V gate is not applied).
+ *   Attention covers all rows; with a quantised format, value rows below the
+ *   kv->sparse_v gate are left out of the weighted sum (see LayerKvCache).
  * x_in must not alias any scratch buffer.
  */
 q35_status q35_forward_full_attention(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
