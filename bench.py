@@ -281,6 +281,28 @@ def prefill_gemm_rate(torch, B, rt, st, cfg, T, rounds=2):
     return us, 2.0 * T * cfg.intermediate * cfg.hidden
 
 
+def library_gemm_rate(torch, M, N, K, reps=20):
+    """For reference: the ROCm BLAS f16 GEMM (torch.mm) on dense f16 operands of
+    the same shape, [M, K] x [K, N] with fp32 accumulation inside the library;
+    returns TFLOP/s.  Not part of the path (its weights would be twice the bytes
+    of the int8 codes); it places the dequantising GEMM against the vendor's."""
+    g = torch.Generator(device="cuda").manual_seed(0)
+    x = torch.randn((M, K), dtype=torch.float16, device="cuda", generator=g)
+    wt = torch.randn((K, N), dtype=torch.float16, device="cuda", generator=g)
+    for _ in range(3):
+        torch.mm(x, wt)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.mm(x, wt)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del x, wt
+    return 2.0 * M * N * K / (us * 1e-6) / 1e12
+
+
 def prefill_cpu_baseline(cfg, w, layers, n=8):
     """The prefill oracle (the decode step looped over the tokens) on n tokens
     through one GDN and one full-attention layer (dense fp32 weights cached
@@ -692,6 +714,8 @@ def main():
         pf_ms = prefill_stack(torch, B, rt, st, kinds, cfg, T)
         g_us, g_flops = prefill_gemm_rate(torch, B, rt, st, cfg, T)
         g_tf = g_flops / (g_us * 1e-6) / 1e12
+        lib_tf = library_gemm_rate(torch, T, cfg.intermediate, cfg.hidden)
+        log(f"library f16 GEMM (torch.mm) on the same shape: {lib_tf:.0f} TFLOP/s")
         log(f"prefill of {T} tokens through {len(kinds)} layers: {pf_ms:.2f} ms ({T / pf_ms * 1e3:.0f} tok/s); "
             f"GEMM {T}x{cfg.intermediate}x{cfg.hidden}: {g_us:.1f} us, {g_tf:.0f} TFLOP/s")
         prefill = {
@@ -702,7 +726,8 @@ def main():
                                                     f"{T} x {cfg.intermediate} x {cfg.hidden})",
                          "achieved": round(g_tf, 1), "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(g_tf / PEAK_MFMA_F16_TFLOPS, 4), "traffic": None,
-                         "flops_per_launch": g_flops, "us_per_launch": round(g_us, 2)},
+                         "flops_per_launch": g_flops, "us_per_launch": round(g_us, 2),
+                         "library_f16_gemm_tflops": round(lib_tf, 1)},
         }
 
     kv_desc = {"bf16": "bf16", "turbo8": "Turbo8 (WHT-rotated E4M3 + bf16 scale per 16)"}.get(args.kv)

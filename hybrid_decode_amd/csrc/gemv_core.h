@@ -217,14 +217,9 @@ struct ProRegs {
     uint4 w[MC][2];  // 16 bf16 norm weights
 };
 
-#ifndef Q35_PERSIST_X_AUX
-#define Q35_PERSIST_X_AUX kAuxCoherent
-#endif
-constexpr int kAuxXPersist = Q35_PERSIST_X_AUX;
-
 // COH: x (and z) were written by other blocks of the same launch and are read
 // with cache policy XAUX (device-coherent, or L2 for blocks of one XCD).
-template <int K, int PRO, bool HALF, int NT, bool COH = false, int XAUX = kAuxXPersist>
+template <int K, int PRO, bool HALF, int NT, bool COH = false, int XAUX = kAuxCoherent>
 Q35_DEV void prologue_issue(const GemvPro& p, ProRegs<K, PRO, NT>& r) {
     constexpr int KC = K / 16, MC = pro_chunks<K, NT>();
     constexpr bool X_BF16 = (PRO == kProRmsAct) && HALF;  // the residual stream is bf16 for HALF
@@ -857,16 +852,10 @@ Q35_DEV void gemv_body(const GemvArgs& a, uint32_t rg, uint32_t nw, Wait&& wait,
     } else if constexpr (SYNC != 0) {
         // weights first (they do not depend on this launch), then the wait for
         // the stage's inputs, then x
-#ifdef Q35_PERSIST_PRE_WAVES
-        const bool early = (tid_x() >> 6) < Q35_PERSIST_PRE_WAVES;
-#else
-        const bool early = true;
-#endif
-        if (early && rg < total) load_rg(rg, true, b0);
+        if (rg < total) load_rg(rg, true, b0);
         asm volatile("" ::: "memory");
         wait();
-        if (!early && rg < total) load_rg(rg, true, b0);
-        prologue_issue<K, T::PRO, HALF, NT, true, SYNC == 1 ? kAuxXPersist : kAuxCoherent>(a.pro, pr);
+        prologue_issue<K, T::PRO, HALF, NT, true, kAuxCoherent>(a.pro, pr);
     } else {
         // x loads first, then the first row groups' weights (vector loads complete in order)
         prologue_issue<K, T::PRO, HALF, NT>(a.pro, pr);
