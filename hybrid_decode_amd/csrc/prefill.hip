@@ -724,13 +724,20 @@ __global__ __launch_bounds__(256, 1) void gdn_scan_kernel(PfGdnArgs a) {
         {
             const float4 e4 = *reinterpret_cast<const float4*>(&el[16 * wid + 4 * lg]);
             f4 y = {e4.x * qs[0], e4.y * qs[1], e4.z * qs[2], e4.w * qs[3]};
-            for (int b = 0; b <= wid; ++b) {
-                const float4 pa = *reinterpret_cast<const float4*>(&pl[(16 * wid + li) * TR + 16 * b + 4 * lg]);
-                const float4 db = *reinterpret_cast<const float4*>(&dlt[li * TR + 16 * b + 4 * lg]);
-                y = mfma(pa.x, db.x, y);
-                y = mfma(pa.y, db.y, y);
-                y = mfma(pa.z, db.z, y);
-                y = mfma(pa.w, db.w, y);
+            // every k block's operands read first (in bounds for all four), then the chain
+            float4 pa[kC / 16], db[kC / 16];
+#pragma unroll
+            for (int b = 0; b < kC / 16; ++b) {
+                pa[b] = *reinterpret_cast<const float4*>(&pl[(16 * wid + li) * TR + 16 * b + 4 * lg]);
+                db[b] = *reinterpret_cast<const float4*>(&dlt[li * TR + 16 * b + 4 * lg]);
+            }
+#pragma unroll
+            for (int b = 0; b < kC / 16; ++b) {
+                if (b > wid) break;  // wave-uniform
+                y = mfma(pa[b].x, db[b].x, y);
+                y = mfma(pa[b].y, db[b].y, y);
+                y = mfma(pa[b].z, db[b].z, y);
+                y = mfma(pa[b].w, db[b].w, y);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -748,16 +755,28 @@ __global__ __launch_bounds__(256, 1) void gdn_scan_kernel(PfGdnArgs a) {
             if (t >= NB) break;
             const float4 s0 = *reinterpret_cast<const float4*>(&st[li * KR + 16 * t + 4 * lg]);
             f4 acc = {ge * s0.x, ge * s0.y, ge * s0.z, ge * s0.w};
+            // A = K^T: (d 16 t + li, token 16 b + 4 lg + s), scalar reads of K rows;
+            // all sixteen operand pairs are read before the chain, so one wait covers them
+            float ka[kC / 16][4];
+            float4 bb[kC / 16];
 #pragma unroll
             for (int b = 0; b < kC / 16; ++b) {
-                // A = K^T: (d 16 t + li, token 16 b + 4 lg + s), four scalar reads of K rows
                 const float* kr = &kl[(16 * b + 4 * lg) * KR + 16 * t + li];
+                ka[b][0] = kr[0];
+                ka[b][1] = kr[KR];
+                ka[b][2] = kr[2 * KR];
+                ka[b][3] = kr[3 * KR];
                 const float4 db = *reinterpret_cast<const float4*>(&dlt[li * TR + 16 * b + 4 * lg]);
                 const float4 fb = *reinterpret_cast<const float4*>(&ef[16 * b + 4 * lg]);
-                acc = mfma(kr[0], fb.x * db.x, acc);
-                acc = mfma(kr[KR], fb.y * db.y, acc);
-                acc = mfma(kr[2 * KR], fb.z * db.z, acc);
-                acc = mfma(kr[3 * KR], fb.w * db.w, acc);
+                bb[b] = make_float4(fb.x * db.x, fb.y * db.y, fb.z * db.z, fb.w * db.w);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int b = 0; b < kC / 16; ++b) {
+                acc = mfma(ka[b][0], bb[b].x, acc);
+                acc = mfma(ka[b][1], bb[b].y, acc);
+                acc = mfma(ka[b][2], bb[b].z, acc);
+                acc = mfma(ka[b][3], bb[b].w, acc);
             }
             sn[tt] = acc;
         }
