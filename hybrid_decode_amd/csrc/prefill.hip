@@ -485,9 +485,54 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(PfGdnArgs a) {
     const int n = (int)min((uint32_t)kC, a.T - t0);
     const uint32_t qoff = i * DK, koff = a.hk * DK + i * DK, voff = 2 * a.hk * DK + j * DV;
 
+    // this thread's column of the right-hand side [V | K] for the substitution
+    // below, 16 rows at a time: the first 16 are fetched now, behind the Gram
+    // products, and each row block fetches the next one's while it is solved
+    // (a resource over the chunk's rows returns zero past the last token;
+    // threads past the last column read values they never use)
+    const auto rX = rsrc(a.qkvs + (size_t)t0 * a.C, (uint32_t)n * a.C * 4u);
+    const uint32_t rcol = tid < DV ? voff + tid : koff + (tid - DV);
+    auto fetch16 = [&](float (&dst)[16], int rb) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            dst[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   rX, ((rb + u) * a.C + rcol) * 4u, 0, 0));
+    };
+    // one half of the head dimension of k and q for the Gram products: NH float4
+    // of each per thread, loaded into registers and then stashed in LDS; the
+    // second half is fetched while the first half's products run
+    constexpr int NH = kC * DH / 4 / 256;
+    static_assert(NH * 256 * 4 == kC * DH, "whole float4 per thread per half");
+    struct Half {
+        float4 k[NH], q[NH];
+    };
+    auto load_half = [&](Half& g, int h) {
+#pragma unroll
+        for (int e = 0; e < NH; ++e) {
+            const int c = tid + 256 * e, r = c / (DH / 4), d = (c % (DH / 4)) * 4;
+            g.k[e] = __builtin_bit_cast(float4, ld_b128<0>(rX, (r * a.C + koff + h * DH + d) * 4u));
+            g.q[e] = __builtin_bit_cast(float4, ld_b128<0>(rX, (r * a.C + qoff + h * DH + d) * 4u));
+        }
+    };
+    auto stash_half = [&](const Half& g) {
+#pragma unroll
+        for (int e = 0; e < NH; ++e) {
+            const int c = tid + 256 * e, r = c / (DH / 4), d = (c % (DH / 4)) * 4;
+            *reinterpret_cast<float4*>(&ks[r * KR + d]) = g.k[e];
+            *reinterpret_cast<float4*>(&qs[r * KR + d]) = g.q[e];
+        }
+    };
+
+    float lg = 0.f;
     if (tid < 64) {
-        float lg = tid < n ? a.lg[(size_t)(t0 + tid) * a.hv + j] : 0.f;
+        lg = tid < n ? a.lg[(size_t)(t0 + tid) * a.hv + j] : 0.f;
         bt[tid] = tid < n ? a.beta[(size_t)(t0 + tid) * a.hv + j] : 0.f;
+    }
+    Half h0, h1;
+    load_half(h0, 0);
+    float rhs[16];
+    fetch16(rhs, 0);
+    if (tid < 64) {
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {  // inclusive scan over the wave
             const float u = __shfl_up(lg, o);
@@ -500,19 +545,11 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(PfGdnArgs a) {
     {
         const int rb = tid >> 4, sb = tid & 15;
         float kk[4][4] = {}, qk[4][4] = {};
+#pragma unroll
         for (int h = 0; h < 2; ++h) {
-            for (int c = tid; c < kC * DH / 4; c += 256) {
-                const int r = c / (DH / 4), d = (c % (DH / 4)) * 4;
-                float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
-                if (r < n) {
-                    const float* src = a.qkvs + (size_t)(t0 + r) * a.C + h * DH;
-                    kv = *reinterpret_cast<const float4*>(src + koff + d);
-                    qv = *reinterpret_cast<const float4*>(src + qoff + d);
-                }
-                *reinterpret_cast<float4*>(&ks[r * KR + d]) = kv;
-                *reinterpret_cast<float4*>(&qs[r * KR + d]) = qv;
-            }
+            stash_half(h == 0 ? h0 : h1);
             __syncthreads();
+            if (h == 0) load_half(h1, 1);
             for (int d = 0; d < DH; d += 4) {
                 float4 kr[4], qr[4], kc[4];
 #pragma unroll
@@ -564,15 +601,14 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(PfGdnArgs a) {
         const size_t blk = (size_t)j * nch + ch;
         float* out = c < DV ? a.Uc + blk * kC * DV + c : a.Wc + blk * kC * DK + (c - DV);
         const int ld = c < DV ? DV : DK;
-        const uint32_t col = c < DV ? voff + c : koff + (c - DV);
         for (int rb = 0; rb < kC; rb += 16) {
-            float x[16];
+            float x[16], nxt[16];
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 const int r = rb + u;
-                const float rhs = r < n ? a.qkvs[(size_t)(t0 + r) * a.C + col] : 0.f;
-                x[u] = c < DV ? bt[r] * rhs : bt[r] * expf(L[r]) * rhs;
+                x[u] = c < DV ? bt[r] * rhs[u] : bt[r] * expf(L[r]) * rhs[u];
             }
+            fetch16(nxt, min(rb + 16, kC - 16));  // the last block refetches its own rows, unused
             for (int s = 0; s < rb; ++s) {
                 const float xv = xsol[s * (DK + DV) + c];
                 const float4* ar = reinterpret_cast<const float4*>(&at[s * 68 + rb]);
@@ -593,6 +629,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(PfGdnArgs a) {
             for (int u = 0; u < 16; ++u) {
                 out[(size_t)(rb + u) * ld] = x[u];
                 if (rb + 16 < kC) xsol[(rb + u) * (DK + DV) + c] = x[u];
+                rhs[u] = nxt[u];
             }
         }
     }
