@@ -398,22 +398,44 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const void* x, uint32
 // Q and K head, and the token's decay (as log g) and beta.
 __global__ __launch_bounds__(256) void gdn_conv_kernel(PfConvArgs a) {
     extern __shared__ float sq[];  // [nqk]
-    const uint32_t t = blockIdx.x;
+    // The blocks of a launch go to the eight XCDs in turn, so block b's XCD is
+    // fixed by b mod 8: that class takes a contiguous run of tokens, and the
+    // input rows that neighbouring tokens' windows share stay in its L2.  The
+    // grid is 8 ceil(T / 8) blocks; those past the last token return at once.
+    const uint32_t per = (a.T + 7) / 8;
+    const uint32_t t = (blockIdx.x % 8) * per + blockIdx.x / 8;
+    if (t >= a.T) return;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const size_t row = (size_t)t * a.C;
-    for (uint32_t c = tid; c < a.C; c += 256) {
-        float u = 0.f;
+    // four channels per pass: all their loads first (channels past the last
+    // one repeat it, unused), then the sums and stores
+    for (uint32_t c0 = tid; c0 < a.C; c0 += 4 * 256) {
+        uint2 wv[4];
+        float in[4][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int tau = (int)t - 3 + j;
-            const float in = tau >= 0 ? a.qkv[(size_t)tau * a.C + c] : a.conv_state[c * 4 + 4 + tau];
-            u = fmaf(bf16_to_f32(a.conv_w[c * 4 + j]), in, u);
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t c = min(c0 + 256 * k, a.C - 1);
+            wv[k] = *reinterpret_cast<const uint2*>(a.conv_w + (size_t)c * 4);  // 4 bf16 taps
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int tau = (int)t - 3 + j;
+                in[k][j] = tau >= 0 ? a.qkv[(size_t)tau * a.C + c] : a.conv_state[c * 4 + 4 + tau];
+            }
         }
-        const float s = silu(u);
-        if (c < a.nqk)
-            sq[c] = s;
-        else
-            a.qkvs[row + c] = s;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t c = c0 + 256 * k;
+            if (c >= a.C) break;
+            const float w[4] = {bf16_lo(wv[k].x), bf16_hi(wv[k].x), bf16_lo(wv[k].y), bf16_hi(wv[k].y)};
+            float u = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) u = fmaf(w[j], in[k][j], u);
+            const float sv = silu(u);
+            if (c < a.nqk)
+                sq[c] = sv;
+            else
+                a.qkvs[row + c] = sv;
+        }
     }
     if (tid < (int)a.hv) {
         const float av = a.a_raw[(size_t)t * a.hv + tid] + bf16_to_f32(a.dt_bias[tid]);
@@ -1216,7 +1238,7 @@ bool pf_gdn_dims_supported(uint32_t dk, uint32_t dv) {
 
 hipError_t pf_gdn_launch(const PfConvArgs& c, const PfGdnArgs& g, float* conv_state_out,
                          hipStream_t s) {
-    pf::gdn_conv_kernel<<<c.T, 256, c.nqk * sizeof(float), s>>>(c);
+    pf::gdn_conv_kernel<<<8 * ((c.T + 7) / 8), 256, c.nqk * sizeof(float), s>>>(c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     pf::gdn_conv_state_kernel<<<(c.C + 255) / 256, 256, 0, s>>>(c.qkv, conv_state_out, c.T, c.C);
