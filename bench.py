@@ -262,8 +262,13 @@ def prefill_stack(torch, B, rt, st, kinds, cfg, T, reps=3):
 
 def prefill_gemm_rate(torch, B, rt, st, cfg, T, rounds=2):
     """The prefill's dequantising GEMM at the gate_proj shape (T x intermediate x
-    hidden), every layer's weights in turn; returns (us per launch, flops per launch)."""
-    x = torch.zeros((T, cfg.hidden), dtype=torch.int16, device="cuda")
+    hidden), every layer's weights in turn, on seeded N(0, 1) f16 rows (the
+    matrix cores draw less power on zero operands and then clock higher, so
+    zero rows would overstate the rate); returns (us per launch, flops per launch)."""
+    import numpy as np
+    g = np.random.default_rng(11)
+    x = torch.from_numpy(g.standard_normal((T, cfg.hidden), dtype=np.float32).astype(np.float16)
+                         .view(np.int16)).to("cuda")
     y = torch.empty((T, cfg.intermediate), dtype=torch.float32, device="cuda")
     ws = torch.empty(B.PREFILL_GEMM_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
     wp, wn = ws.data_ptr(), B.PREFILL_GEMM_WORKSPACE_BYTES
