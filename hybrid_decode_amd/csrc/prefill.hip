@@ -59,6 +59,11 @@ Q35_DEV uint32_t bf2_to_h2(uint32_t w) { return pack_h2(bf16_lo(w), bf16_hi(w));
 // rows; a wave holds a gate tile and its up tile, so the epilogue is
 // elementwise in registers.
 //
+// W16: the weights arrive already dequantised (f16 [n, K], the same values
+// built the same way by dequant_kernel once per launch), and the stash copies
+// them: each weight tile is otherwise dequantised once for every 256-row tile
+// of x, which at T = 4096 cost the k loop about a fifth of its rate.
+//
 // Wave quantisation.  A launch of n tiles on C compute units (one block each)
 // runs ceil(n / C) rounds; when the last round would be at most a quarter full,
 // its tiles are cut into `split` ranges of k tiles, one block each, so that
@@ -86,7 +91,7 @@ Q35_DEV void tile_of(uint32_t t, uint32_t n_mt, uint32_t n_nt, uint32_t& mt, uin
 
 // BM = 256 rows of x per block, 512 threads: waves of 64 x 64; each thread stages
 // one 16-code chunk of W per k tile.
-template <int MODE, int BM>
+template <int MODE, int BM, bool W16 = false>
 __global__ __launch_bounds__(2 * BM, 1) void gemm_kernel(PfGemmArgs a) {
     static_assert(BM == 256, "one W chunk per thread per k tile");
     constexpr int kBM = BM, kGemmThreads = 2 * BM;
@@ -113,8 +118,9 @@ __global__ __launch_bounds__(2 * BM, 1) void gemm_kernel(PfGemmArgs a) {
     // which then waits for every load where it is issued.
     struct Stage {
         uint4 x0, x1, x2, x3;  // four x chunks
-        uint4 w;               // sixteen weight codes
-        uint32_t sc, bi;       // raw bf16 bits
+        uint4 w;               // sixteen weight codes (W16: the first eight f16 weights)
+        uint4 w2;              // W16: the last eight f16 weights
+        uint32_t sc, bi;       // raw bf16 bits (unused with W16)
     };
     // This thread's W row (fixed for the whole k loop): rows 64..127 of a SwiGLU
     // tile are the up rows of n0..n0+63; otherwise the row's segment picks the
@@ -138,7 +144,11 @@ __global__ __launch_bounds__(2 * BM, 1) void gemm_kernel(PfGemmArgs a) {
         const bool live = (MODE == kPfSwiglu ? n : gn) < a.N;
         if (!live) q = 0;
         const size_t nn = live ? n : 0;
-        wrow_p = (q == 0 ? a.w[0] : q == 1 ? a.w[1] : q == 2 ? a.w[2] : a.w[3]) + nn * a.K + wcol_t;
+        if constexpr (W16)
+            wrow_p = reinterpret_cast<const uint8_t*>((q == 0 ? a.wh[0] : q == 1 ? a.wh[1] : q == 2 ? a.wh[2] : a.wh[3]) +
+                                                      nn * a.K + wcol_t);
+        else
+            wrow_p = (q == 0 ? a.w[0] : q == 1 ? a.w[1] : q == 2 ? a.w[2] : a.w[3]) + nn * a.K + wcol_t;
         srow_p = (q == 0 ? a.s[0] : q == 1 ? a.s[1] : q == 2 ? a.s[2] : a.s[3]) + nn * ng;
         brow_p = (q == 0 ? a.b[0] : q == 1 ? a.b[1] : q == 2 ? a.b[2] : a.b[3]) + nn * ng;
         wmsk = live ? 0xFFFFFFFFu : 0u;
@@ -158,9 +168,14 @@ __global__ __launch_bounds__(2 * BM, 1) void gemm_kernel(PfGemmArgs a) {
         g.x1 = *reinterpret_cast<const uint4*>(xrow_p[1] + ko);
         g.x2 = *reinterpret_cast<const uint4*>(xrow_p[2] + ko);
         g.x3 = *reinterpret_cast<const uint4*>(xrow_p[3] + ko);
-        g.w = *reinterpret_cast<const uint4*>(wrow_p + ko);
-        g.sc = srow_p[kt];
-        g.bi = brow_p[kt];
+        if constexpr (W16) {
+            g.w = *reinterpret_cast<const uint4*>(wrow_p + 2 * ko);
+            g.w2 = *reinterpret_cast<const uint4*>(wrow_p + 2 * ko + 16);
+        } else {
+            g.w = *reinterpret_cast<const uint4*>(wrow_p + ko);
+            g.sc = srow_p[kt];
+            g.bi = brow_p[kt];
+        }
     };
     // part q (0..3) of moving a staged tile into LDS: one x chunk, and four weights
     // dequantised (fp32 fma, one f16 rounding); spread over the MFMA steps
@@ -177,12 +192,21 @@ __global__ __launch_bounds__(2 * BM, 1) void gemm_kernel(PfGemmArgs a) {
             const int c = tid + kGemmThreads * q, row = c >> 3, col = (c & 7) * 8;
             *reinterpret_cast<uint4*>(&xs[buf][row * kRow + col]) = xv;
         }
-        v &= wmsk;
-        const float sc = __uint_as_float((g.sc << 16) & wmsk);
-        const float bi = __uint_as_float((g.bi << 16) & wmsk);
-        *reinterpret_cast<uint2*>(&ws[buf][wrow_t * kRow + wcol_t + 4 * q]) =
-            make_uint2(pack_h2(fmaf(sc, (float)(v & 0xFFu), bi), fmaf(sc, (float)((v >> 8) & 0xFFu), bi)),
-                       pack_h2(fmaf(sc, (float)((v >> 16) & 0xFFu), bi), fmaf(sc, (float)(v >> 24), bi)));
+        if constexpr (W16) {
+            uint2 h;
+            if constexpr (q == 0) h = make_uint2(g.w.x, g.w.y);
+            if constexpr (q == 1) h = make_uint2(g.w.z, g.w.w);
+            if constexpr (q == 2) h = make_uint2(g.w2.x, g.w2.y);
+            if constexpr (q == 3) h = make_uint2(g.w2.z, g.w2.w);
+            *reinterpret_cast<uint2*>(&ws[buf][wrow_t * kRow + wcol_t + 4 * q]) = make_uint2(h.x & wmsk, h.y & wmsk);
+        } else {
+            v &= wmsk;
+            const float sc = __uint_as_float((g.sc << 16) & wmsk);
+            const float bi = __uint_as_float((g.bi << 16) & wmsk);
+            *reinterpret_cast<uint2*>(&ws[buf][wrow_t * kRow + wcol_t + 4 * q]) =
+                make_uint2(pack_h2(fmaf(sc, (float)(v & 0xFFu), bi), fmaf(sc, (float)((v >> 8) & 0xFFu), bi)),
+                           pack_h2(fmaf(sc, (float)((v >> 16) & 0xFFu), bi), fmaf(sc, (float)(v >> 24), bi)));
+        }
     };
     using c0 = std::integral_constant<int, 0>;
     using c1 = std::integral_constant<int, 1>;
@@ -370,6 +394,27 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(PfGemmArgs a) {
             store_act(a.out[0], o, vv[c] + load_act(a.resid, o, a.resid_f32), a.out_f32);
         }
     }
+}
+
+// out = f16(scale * code + bias) (fp32 fma, one rounding), 16 codes per thread:
+// element for element what gemm_kernel's stash builds from the codes.
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* codes, const uint16_t* scales,
+                                                      const uint16_t* biases, uint16_t* out,
+                                                      uint32_t n16, uint32_t K) {
+    const uint32_t i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n16) return;
+    const uint32_t per_row = K / 16, row = i / per_row, g = (i % per_row) / 4;
+    const uint4 c = reinterpret_cast<const uint4*>(codes)[i];
+    const float sc = bf16_to_f32(scales[(size_t)row * (K / 64) + g]);
+    const float bi = bf16_to_f32(biases[(size_t)row * (K / 64) + g]);
+    auto deq4 = [&](uint32_t v) {
+        return make_uint2(pack_h2(fmaf(sc, (float)(v & 0xFFu), bi), fmaf(sc, (float)((v >> 8) & 0xFFu), bi)),
+                          pack_h2(fmaf(sc, (float)((v >> 16) & 0xFFu), bi), fmaf(sc, (float)(v >> 24), bi)));
+    };
+    const uint2 a0 = deq4(c.x), a1 = deq4(c.y), a2 = deq4(c.z), a3 = deq4(c.w);
+    uint4* o = reinterpret_cast<uint4*>(out) + 2 * (size_t)i;
+    o[0] = make_uint4(a0.x, a0.y, a1.x, a1.y);
+    o[1] = make_uint4(a2.x, a2.y, a3.x, a3.y);
 }
 
 // ====================================================================== row norms
@@ -1179,6 +1224,10 @@ const void* pf_kernel_ptr(int i) {
         reinterpret_cast<const void*>(pf::flash_kernel<256, 4>),
         reinterpret_cast<const void*>(pf::iota_kernel),
         reinterpret_cast<const void*>(pf::cast_f16_kernel),
+        reinterpret_cast<const void*>(pf::gemm_kernel<kPfF32, 256, true>),
+        reinterpret_cast<const void*>(pf::gemm_kernel<kPfResid, 256, true>),
+        reinterpret_cast<const void*>(pf::gemm_kernel<kPfSwiglu, 256, true>),
+        reinterpret_cast<const void*>(pf::dequant_kernel),
     };
     return i >= 0 && i < (int)(sizeof(k) / sizeof(k[0])) ? k[i] : nullptr;
 }
@@ -1209,7 +1258,10 @@ static hipError_t gemm_launch_mode(PfGemmArgs a, uint32_t num_cu, hipStream_t s)
     const uint32_t bn = MODE == kPfSwiglu ? pf::kBN / 2 : pf::kBN;
     gemm_plan<BM>(a, bn, num_cu);
     const uint32_t n_tiles = ((a.N + bn - 1) / bn) * ((a.M + BM - 1) / BM), tail = n_tiles - a.n_full;
-    pf::gemm_kernel<MODE, BM><<<a.n_full + tail * a.split, 2 * BM, 0, s>>>(a);
+    if (a.wh[0])
+        pf::gemm_kernel<MODE, BM, true><<<a.n_full + tail * a.split, 2 * BM, 0, s>>>(a);
+    else
+        pf::gemm_kernel<MODE, BM, false><<<a.n_full + tail * a.split, 2 * BM, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || tail == 0) return e;
     pf::gemm_reduce_kernel<MODE, BM><<<tail * (BM * pf::kBN / 4 / 256), 256, 0, s>>>(a);
@@ -1224,6 +1276,14 @@ hipError_t pf_gemm_launch(int mode, const PfGemmArgs& a, uint32_t num_cu, hipStr
         case kPfSwiglu: return gemm_launch_mode<kPfSwiglu, 256>(a, num_cu, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t pf_dequant_launch(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases,
+                             uint32_t rows, uint32_t K, uint16_t* out, hipStream_t s) {
+    const uint32_t n16 = rows * (K / 16);
+    if (n16 == 0) return hipSuccess;
+    pf::dequant_kernel<<<(n16 + 255) / 256, 256, 0, s>>>(codes, scales, biases, out, n16, K);
+    return hipGetLastError();
 }
 
 hipError_t pf_rmsnorm_launch(const void* x, bool x_f32, const uint16_t* w, uint16_t* out, uint32_t T,

@@ -333,6 +333,7 @@ struct PfGemmArgs {
     const uint8_t* w[4];
     const uint16_t* s[4];
     const uint16_t* b[4];
+    const uint16_t* wh[4];     // the same matrices already dequantised to f16 [n, K] (NULL: from the codes)
     void* out[4];
     uint32_t ldo[4];
     uint32_t seg_end[4];       // cumulative; unused entries equal N
@@ -347,6 +348,10 @@ struct PfGemmArgs {
 constexpr uint32_t kPfSplitBlocks = 256;
 constexpr size_t kPfSplitBytes = (size_t)kPfSplitBlocks * 256 * 128 * 4;
 hipError_t pf_gemm_launch(int mode, const PfGemmArgs& a, uint32_t num_cu, hipStream_t s);
+// out (f16 [rows, K]) = scale * code + bias in fp32, rounded once to f16: the
+// values the GEMM would build from the codes (K a multiple of 64)
+hipError_t pf_dequant_launch(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases,
+                             uint32_t rows, uint32_t K, uint16_t* out, hipStream_t s);
 // f16 rows of RMSNorm(x) for T rows of H (x fp32 or bf16)
 hipError_t pf_rmsnorm_launch(const void* x, bool x_f32, const uint16_t* w, uint16_t* out, uint32_t T,
                              uint32_t H, float eps, hipStream_t s);

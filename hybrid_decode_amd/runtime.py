@@ -73,6 +73,7 @@ class QuantWeightDev:
         self.scales = to_dev(w["scales"], device)
         self.biases = to_dev(w["biases"], device)
         n, k = w["codes"].shape
+        self.n, self.k = n, k
         self.struct = B.Q35QuantWeight(ptr(self.codes), ptr(self.scales), ptr(self.biases), n, k)
 
     @property

@@ -753,7 +753,9 @@ q35_status q35_gemv(const Qwen35Kernels* kernels, const Q35QuantWeight* w, const
  * Workspace: device memory of at least q35_prefill_workspace_bytes(cfg,
  * n_tokens) bytes, 256-byte aligned, caller-owned, rewritten by every call (no
  * initialisation needed; shared by the two layer kinds, not by concurrent
- * calls).
+ * calls).  It includes room for the largest weight set of one projection as
+ * f16: from 4096 tokens on, each projection dequantises its weights there
+ * once (as q35_prefill_gemm does with a large enough workspace).
  */
 q35_status q35_prefill_workspace_bytes(const Qwen35ForwardConfig* cfg, uint32_t max_tokens,
                                        size_t* bytes);
@@ -799,11 +801,15 @@ q35_status q35_prefill_full_attention(const Qwen35Kernels* kernels, const Qwen35
  * [m, w->k] (16-byte aligned rows), W[n, k] = scale * code + bias evaluated in
  * fp32 and rounded to f16, products on the matrix cores with fp32 sums.
  * Exported so that it can be tested and timed on its own.  workspace: NULL, or
- * device memory of Q35_PREFILL_GEMM_WORKSPACE_BYTES, 256-byte aligned,
- * caller-owned and rewritten by the call: with it, a last round of tiles that
- * would leave most compute units idle is cut along k into parts whose fp32
- * sums are added in k order by a second kernel (the result then differs from
- * the NULL case by fp32 rounding only).  A smaller or misaligned workspace:
+ * device memory of at least Q35_PREFILL_GEMM_WORKSPACE_BYTES, 256-byte
+ * aligned, caller-owned and rewritten by the call: with it, a last round of
+ * tiles that would leave most compute units idle is cut along k into parts
+ * whose fp32 sums are added in k order by a second kernel (the result then
+ * differs from the NULL case by fp32 rounding only).  With at least
+ * Q35_PREFILL_GEMM_WORKSPACE_BYTES + 2 * w->n * w->k bytes, W is first
+ * written as f16 after that area and the product reads it from there instead
+ * of dequantising each tile of W once per 256 rows of x (the same f16 values,
+ * so the same result).  A smaller or misaligned workspace:
  * Q35_ERR_INVALID_ARG.  m == 0 enqueues nothing.
  */
 #define Q35_PREFILL_GEMM_WORKSPACE_BYTES ((size_t)32 << 20)

@@ -44,16 +44,17 @@ def _rows_rel(gpu, ref):
 # --------------------------------------------------------------------------- GEMM
 
 
-def _gemm(rt, wq, x, m, n, split):
+def _gemm(rt, wq, x, m, n, split, f16w=False):
     """q35_prefill_gemm of f16 x [m, k] by wq, fp32 out; with `split` it gets the
-    workspace that lets it cut a sparse last round of tiles along k."""
+    workspace that lets it cut a sparse last round of tiles along k, and with
+    `f16w` also the room to dequantise W to f16 once before the product."""
     from hybrid_decode_amd import binding as B
     xd = torch.from_numpy(x.view(np.int16)).cuda()
     y = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(B.PREFILL_GEMM_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda") if split else None
+    nb = B.PREFILL_GEMM_WORKSPACE_BYTES + (2 * wq.n * wq.k if f16w else 0)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if split else None
     B.q35_prefill_gemm(rt.kernels(), wq.struct, xd.data_ptr(), m, y.data_ptr(),
-                       ws.data_ptr() if split else None, B.PREFILL_GEMM_WORKSPACE_BYTES if split else 0,
-                       rt.stream_ptr())
+                       ws.data_ptr() if split else None, nb if split else 0, rt.stream_ptr())
     torch.cuda.synchronize()
     return y.cpu().numpy()
 
@@ -68,11 +69,16 @@ def test_prefill_gemm_matches_float64_on_the_same_f16_operands(rt, gen, m, n, k,
     w = gen.quant(f"pf.gemm.{m}.{n}.{k}", n, k)
     x = gen.normal_f32(f"pf.gemm.x.{m}.{k}", (m, k)).astype(np.float16)
     ref = x.astype(np.float64) @ O.dequant(w).astype(np.float16).astype(np.float64).T
-    got = _gemm(rt, rt.QuantWeightDev(w), x, m, n, split)
+    wq = rt.QuantWeightDev(w)
+    got = _gemm(rt, wq, x, m, n, split)
     assert np.isfinite(got).all()
     # identical f16 operands: only the fp32 order of the sums differs
     assert rel(got, ref) < 1e-5
     assert _rows_rel(got, ref) < 1e-4
+    if split:
+        # W dequantised to f16 once, up front: the same f16 values and the same
+        # sums in the same order, so the same bits
+        assert np.array_equal(_gemm(rt, wq, x, m, n, True, f16w=True), got)
 
 
 @pytest.mark.parametrize("n,k", [(9216, 2560), (2560, 9216)])
@@ -90,7 +96,9 @@ def test_prefill_gemm_4096_rows_at_the_4b_shapes(rt, gen, n, k):
     wq = rt.QuantWeightDev(w)
     got = _gemm(rt, wq, x, m, n, True)
     plain = _gemm(rt, wq, x, m, n, False)
+    f16w = _gemm(rt, wq, x, m, n, True, f16w=True)
     assert np.isfinite(got).all() and np.isfinite(plain).all()
+    assert np.array_equal(f16w, got), "W as f16 up front must give the same bits"
     rows = np.array(sorted({0, 1, 255, 256, 511, 1023, 1024, 2047, 2048, 3001, 3839, 3840, 4095}
                            | set(range(17, m, 256))))
     ref = x[rows].astype(np.float64) @ O.dequant(w).astype(np.float16).astype(np.float64).T
