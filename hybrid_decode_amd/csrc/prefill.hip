@@ -420,20 +420,30 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* codes, cons
 // ====================================================================== row norms
 
 // out[t, :] = f16(x[t, :] * w / sqrt(mean(x[t, :]^2) + eps)); one block per row.
+// PER >= H / 256 values per thread, all loaded before the sum and kept in
+// registers for the scaling (one read of the row).
+template <int PER>
 __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const void* x, uint32_t x_f32,
                                                            const uint16_t* w, uint16_t* out,
                                                            uint32_t H, float eps) {
     __shared__ float red[4];
     const size_t base = (size_t)blockIdx.x * H;
-    float ss = 0.f;
-    for (uint32_t i = threadIdx.x; i < H; i += 256) {
-        const float v = load_act(x, base + i, x_f32);
-        ss = fmaf(v, v, ss);
+    float v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const uint32_t i = threadIdx.x + 256 * u;
+        v[u] = i < H ? load_act(x, base + i, x_f32) : 0.f;
     }
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) ss = fmaf(v[u], v[u], ss);
     ss = block_sum<256>(ss, red);
     const float rs = 1.0f / sqrtf(ss / (float)H + eps);
-    for (uint32_t i = threadIdx.x; i < H; i += 256)
-        out[base + i] = to_h(load_act(x, base + i, x_f32) * rs * bf16_to_f32(w[i]));
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const uint32_t i = threadIdx.x + 256 * u;
+        if (i < H) out[base + i] = to_h(v[u] * rs * bf16_to_f32(w[i]));
+    }
 }
 
 // ====================================================================== GDN: conv, gates
@@ -898,19 +908,36 @@ __global__ __launch_bounds__(256, 1) void gdn_scan_kernel(PfGdnArgs a) {
 }
 
 // yz[t, j, :] = f16(RMSNorm(y[t, j, :]; w) * silu(z[t, j, :])); one block per token.
+// Wave wid takes heads wid, wid + 4, ...: eight of them at a time, with every
+// y and z value of the eight loaded before the sums (dv <= 128: two per lane).
 __global__ __launch_bounds__(256) void gdn_out_kernel(const float* y, const float* z,
                                                       const uint16_t* w, uint16_t* yz, uint32_t hv,
                                                       uint32_t dv, float eps) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const size_t row = (size_t)blockIdx.x * hv * dv;
-    for (uint32_t j = wid; j < hv; j += 4) {
-        float ss = 0.f;
-        for (uint32_t d = lane; d < dv; d += 64) ss = fmaf(y[row + j * dv + d], y[row + j * dv + d], ss);
-        ss = wave_sum(ss);
-        const float rs = 1.0f / sqrtf(ss / (float)dv + eps);
-        for (uint32_t d = lane; d < dv; d += 64) {
-            const size_t o = row + j * dv + d;
-            yz[o] = to_h(y[o] * rs * bf16_to_f32(w[d]) * silu(z[o]));
+    for (uint32_t j0 = wid; j0 < hv; j0 += 4 * 8) {
+        float yv[8][2], zv[8][2];
+#pragma unroll
+        for (int h = 0; h < 8; ++h)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const uint32_t j = j0 + 4 * h, d = lane + 64 * e;
+                const bool in = j < hv && d < dv;
+                const size_t o = row + (size_t)(in ? j : 0) * dv + (in ? d : 0);
+                yv[h][e] = in ? y[o] : 0.f;
+                zv[h][e] = in ? z[o] : 0.f;
+            }
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+            const uint32_t j = j0 + 4 * h;
+            if (j >= hv) break;  // wave-uniform
+            const float ss = wave_sum(fmaf(yv[h][0], yv[h][0], yv[h][1] * yv[h][1]));
+            const float rs = 1.0f / sqrtf(ss / (float)dv + eps);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const uint32_t d = lane + 64 * e;
+                if (d < dv) yz[row + j * dv + d] = to_h(yv[h][e] * rs * bf16_to_f32(w[d]) * silu(zv[h][e]));
+            }
         }
     }
 }
@@ -1209,7 +1236,10 @@ const void* pf_kernel_ptr(int i) {
         reinterpret_cast<const void*>(pf::gemm_reduce_kernel<kPfF32, 256>),
         reinterpret_cast<const void*>(pf::gemm_reduce_kernel<kPfResid, 256>),
         reinterpret_cast<const void*>(pf::gemm_reduce_kernel<kPfSwiglu, 256>),
-        reinterpret_cast<const void*>(pf::rmsnorm_rows_kernel),
+        reinterpret_cast<const void*>(pf::rmsnorm_rows_kernel<4>),
+        reinterpret_cast<const void*>(pf::rmsnorm_rows_kernel<8>),
+        reinterpret_cast<const void*>(pf::rmsnorm_rows_kernel<16>),
+        reinterpret_cast<const void*>(pf::rmsnorm_rows_kernel<32>),
         reinterpret_cast<const void*>(pf::gdn_conv_kernel),
         reinterpret_cast<const void*>(pf::gdn_conv_state_kernel),
         reinterpret_cast<const void*>(pf::gdn_chunk_kernel<32, 32>),
@@ -1288,7 +1318,16 @@ hipError_t pf_dequant_launch(const uint8_t* codes, const uint16_t* scales, const
 
 hipError_t pf_rmsnorm_launch(const void* x, bool x_f32, const uint16_t* w, uint16_t* out, uint32_t T,
                              uint32_t H, float eps, hipStream_t s) {
-    pf::rmsnorm_rows_kernel<<<T, 256, 0, s>>>(x, x_f32, w, out, H, eps);
+    if (H <= 4 * 256)
+        pf::rmsnorm_rows_kernel<4><<<T, 256, 0, s>>>(x, x_f32, w, out, H, eps);
+    else if (H <= 8 * 256)
+        pf::rmsnorm_rows_kernel<8><<<T, 256, 0, s>>>(x, x_f32, w, out, H, eps);
+    else if (H <= 16 * 256)
+        pf::rmsnorm_rows_kernel<16><<<T, 256, 0, s>>>(x, x_f32, w, out, H, eps);
+    else if (H <= 32 * 256)
+        pf::rmsnorm_rows_kernel<32><<<T, 256, 0, s>>>(x, x_f32, w, out, H, eps);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -1324,6 +1363,7 @@ hipError_t pf_gdn_launch(const PfConvArgs& c, const PfGdnArgs& g, float* conv_st
 
 hipError_t pf_gdn_out_launch(const float* y, const float* z, const uint16_t* w, uint16_t* yz,
                              uint32_t T, uint32_t hv, uint32_t dv, float eps, hipStream_t s) {
+    if (dv > 128) return hipErrorInvalidValue;  // two values per lane
     pf::gdn_out_kernel<<<T, 256, 0, s>>>(y, z, w, yz, hv, dv, eps);
     return hipGetLastError();
 }
