@@ -1182,17 +1182,23 @@ __global__ __launch_bounds__((64 * G * flash_wph<D, G>())) void flash_kernel(PfA
     const float inv = 1.0f / l;
     const float* gate = a.q_full + (size_t)tq * a.hq * 2 * D + (size_t)h * 2 * D + D;
     uint16_t* out = a.ga + ((size_t)tq * a.hq + h) * D;
+    // every gate value first: a store between two loads would make the second
+    // load's wait include the store (the vector memory counter counts both)
+    float4 gv[DTW][4];
+#pragma unroll
+    for (int dt = 0; dt < DTW; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+            gv[dt][r4] = *reinterpret_cast<const float4*>(gate + 32 * (half * DTW + dt) + 8 * r4 + 4 * h2);
 #pragma unroll
     for (int dt = 0; dt < DTW; ++dt)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const int d = 32 * (half * DTW + dt) + 8 * r4 + 4 * h2;
+            const float gt[4] = {gv[dt][r4].x, gv[dt][r4].y, gv[dt][r4].z, gv[dt][r4].w};
             float v[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float gt = gate[d + u];
-                v[u] = o[dt][4 * r4 + u] * inv / (1.0f + expf(-gt));
-            }
+            for (int u = 0; u < 4; ++u) v[u] = o[dt][4 * r4 + u] * inv / (1.0f + expf(-gt[u]));
             *reinterpret_cast<uint2*>(out + d) = make_uint2(pack_h2(v[0], v[1]), pack_h2(v[2], v[3]));
         }
 }
