@@ -760,7 +760,9 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
 
 // grid (Hq, D/32); thread t: dim d0 + t % 32, chunk lane t / 32.  Each thread
 // issues its first kPrefetch partial loads before the weights are known, so the
-// partials and the (max, sum) pairs arrive together.
+// partials and the (max, sum) pairs arrive together; the pairs are read from
+// memory once (kept in LDS for the weights) and the gate is requested with
+// them, so no load waits on an earlier result.
 constexpr int kMergeDims = 32;
 constexpr int kMergeLanes = kNT / kMergeDims;
 constexpr int kPrefetch = 16;
@@ -771,7 +773,7 @@ __global__ __launch_bounds__(kNT) void attn_merge_kernel(AttnArgs a) {
     const int dl = t % kMergeDims, cl = t / kMergeDims;
     const uint32_t h = blockIdx.x, g = h / G, i = h % G;
     const uint32_t d = blockIdx.y * kMergeDims + dl;
-    extern __shared__ float wsh[];  // [max_chunks] chunk weights
+    extern __shared__ float wsh[];  // [max_chunks] chunk maxima, then weights; then [max_chunks] sums
     __shared__ float red[kNT];
     __shared__ float stat[kNT / 64];
 
@@ -799,9 +801,16 @@ __global__ __launch_bounds__(kNT) void attn_merge_kernel(AttnArgs a) {
         pa[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(racc, cc * cstride + d * 4u, 0, 0));
     }
     const float* pml = a.part_ml + (size_t)g * a.max_chunks * 2 * G + 2 * i;
+    float* lsh = wsh + a.max_chunks;
 
     float mx = -INFINITY;
-    for (uint32_t cc = t; cc < nch; cc += kNT) mx = fmaxf(mx, pml[cc * 2 * G]);
+    for (uint32_t cc = t; cc < nch; cc += kNT) {
+        const float2 ml = *reinterpret_cast<const float2*>(pml + cc * 2 * G);
+        wsh[cc] = ml.x;
+        lsh[cc] = ml.y;
+        mx = fmaxf(mx, ml.x);
+    }
+    const float gate = a.q_full[(size_t)h * 2 * D + D + d];
     mx = wave_max(mx);
     if (lane == 0) red[wid] = mx;
     __syncthreads();
@@ -809,10 +818,10 @@ __global__ __launch_bounds__(kNT) void attn_merge_kernel(AttnArgs a) {
 #pragma unroll
     for (int w = 1; w < kNT / 64; ++w) M = fmaxf(M, red[w]);
     float tot = 0.f;
-    for (uint32_t cc = t; cc < nch; cc += kNT) {
-        const float w = exp2f(pml[cc * 2 * G] - M);
+    for (uint32_t cc = t; cc < nch; cc += kNT) {  // this thread's own chunks: no barrier needed
+        const float w = exp2f(wsh[cc] - M);
         wsh[cc] = w;
-        tot = fmaf(w, pml[cc * 2 * G + 1], tot);
+        tot = fmaf(w, lsh[cc], tot);
     }
     tot = block_sum<kNT>(tot, stat);  // its barriers also publish wsh (and free red)
 
@@ -832,7 +841,6 @@ __global__ __launch_bounds__(kNT) void attn_merge_kernel(AttnArgs a) {
         for (int c2 = 0; c2 < kMergeLanes; ++c2) o += red[c2 * kMergeDims + dl];
         o /= tot;
         if (a.attn_out) a.attn_out[h * D + d] = o;
-        const float gate = a.q_full[(size_t)h * 2 * D + D + d];
         a.gated_attn[h * D + d] = o * sigmoidf_(gate);
     }
 }
@@ -860,7 +868,7 @@ hipError_t launch_t(const AttnArgs& a, uint32_t grid_chunks, uint32_t fmt, hipSt
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_merge_kernel<D, G>), dim3(a.hq, D / kMergeDims), dim3(kNT),
-                       (size_t)a.max_chunks * sizeof(float), stream, a);
+                       (size_t)a.max_chunks * 2 * sizeof(float), stream, a);
     return hipGetLastError();
 }
 

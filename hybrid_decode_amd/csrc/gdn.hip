@@ -113,7 +113,10 @@ __global__ __launch_bounds__(2 * DK) void gdn_kernel(GdnArgs a) {
     const float rk = 1.0f / sqrtf(kk + a.l2_eps);
     kq *= rq * rk;
 
-    // 3. per column: delta and y
+    // 3. per column: delta and y (y is stored after the state: a store issued
+    //    here would make the wait before the state stores include its latency,
+    //    the vector memory counter counting stores as well as loads)
+    float yv = 0.f;
     if (t < kCT) {
         float av = 0.f, bv = 0.f;
 #pragma unroll
@@ -123,16 +126,7 @@ __global__ __launch_bounds__(2 * DK) void gdn_kernel(GdnArgs a) {
         }
         const float d = beta * (vv - g * av * rk);
         dl[t] = d;
-        a.y[h * DV + col0 + t] = (g * bv * rq + kq * d) * a.out_scale;
-    }
-    if (a.qkv_smooth) {
-        if (blockIdx.x == 0 && (h % rep) == 0 && own) {
-            a.qkv_smooth[i * DK + row0] = qr.x * rq;
-            a.qkv_smooth[i * DK + row0 + 1] = qr.y * rq;
-            a.qkv_smooth[a.hk * DK + i * DK + row0] = kr.x * rk;
-            a.qkv_smooth[a.hk * DK + i * DK + row0 + 1] = kr.y * rk;
-        }
-        if (t < kCT) a.qkv_smooth[2 * a.hk * DK + h * DV + col0 + t] = vv;
+        yv = (g * bv * rq + kq * d) * a.out_scale;
     }
     __syncthreads();
 
@@ -150,6 +144,16 @@ __global__ __launch_bounds__(2 * DK) void gdn_kernel(GdnArgs a) {
         float4* p = reinterpret_cast<float4*>(sbase + (size_t)(row0 + j) * DV);
         p[0] = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
         p[1] = make_float4(o[j][4], o[j][5], o[j][6], o[j][7]);
+    }
+    if (t < kCT) a.y[h * DV + col0 + t] = yv;
+    if (a.qkv_smooth) {
+        if (blockIdx.x == 0 && (h % rep) == 0 && own) {
+            a.qkv_smooth[i * DK + row0] = qr.x * rq;
+            a.qkv_smooth[i * DK + row0 + 1] = qr.y * rq;
+            a.qkv_smooth[a.hk * DK + i * DK + row0] = kr.x * rk;
+            a.qkv_smooth[a.hk * DK + i * DK + row0 + 1] = kr.y * rk;
+        }
+        if (t < kCT) a.qkv_smooth[2 * a.hk * DK + h * DV + col0 + t] = vv;
     }
 }
 
