@@ -397,6 +397,7 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     __syncthreads();
     if (a.q_norm_out && c == 0)
         for (int e = t; e < G * D; e += kNT) a.q_norm_out[(size_t)g * G * D + e] = qs[e];
+    uint16_t new_k = 0, new_v = 0;  // bf16 formats: this thread's element of the new row
     if constexpr (ROTQK) {
         if (has_new && a.k_norm_out)
             for (int d = t; d < D; d += kNT) a.k_norm_out[g * D + d] = qs[G * D + d];
@@ -448,13 +449,13 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     } else if (has_new) {
         if (a.k_norm_out)
             for (int d = t; d < D; d += kNT) a.k_norm_out[g * D + d] = qs[G * D + d];
-        uint16_t* krow = a.kc + ((size_t)pos * a.hkv + g) * D;
-        for (int d = t; d < D; d += kNT) {
-            const uint32_t kb = f32_to_bf16(qs[G * D + d]);
-            krow[d] = (uint16_t)kb;
-            if constexpr (!LMV)  // vn is already bf16-exact
-                a.vc[((size_t)pos * a.hkv + g) * D + d] = (uint16_t)f32_to_bf16(vn[d]);
-            qs[G * D + d] = bf16_to_f32(kb);  // attend to the row as stored
+        // the bf16 row is stored at the end of the kernel (the loop below attends
+        // to it from LDS): stores issued here would be counted by every later
+        // wait for the batch loads
+        if (t < D) {
+            new_k = (uint16_t)f32_to_bf16(qs[G * D + t]);
+            new_v = (uint16_t)f32_to_bf16(vn[t]);  // vn is already bf16-exact
+            qs[G * D + t] = bf16_to_f32(new_k);    // attend to the row as stored
         }
         if constexpr (LMV) {
             // the new v: rotated by wave 0, then quantised in groups of 16 (one
@@ -754,6 +755,13 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
             wht_regs<D>(x, lane);
 #pragma unroll
             for (int i = 0; i < D / 64; ++i) pacc[vi * D + lane * (D / 64) + i] = x[i];
+        }
+    }
+    if constexpr (!ROTQK) {
+        if (has_new && t < D) {
+            const size_t row = ((size_t)pos * a.hkv + g) * D;
+            a.kc[row + t] = new_k;
+            if constexpr (!LMV) a.vc[row + t] = new_v;
         }
     }
 }
