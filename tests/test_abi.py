@@ -245,6 +245,16 @@ def test_prefill_workspace_grows_with_tokens(lib):
     assert sizes[-1] % 256 == 0
 
 
+def test_prefill_workspace_holds_the_largest_projection_as_f16(lib):
+    """From 4096 tokens the projections dequantise their weights once into the
+    workspace: it must hold the largest set one launch reads (the 4B gate/up
+    pair, 2 x 9216 x 2560 f16) beyond what the activations need."""
+    c = B.q35_config_qwen3_5_4b()
+    one = B.q35_prefill_workspace_bytes(c, 1)
+    gate_up_f16 = 2 * c.intermediate * c.hidden * 2
+    assert one >= gate_up_f16 + (32 << 20)  # plus the split-GEMM partial tiles
+
+
 def test_prefill_errors_before_any_launch(lib):
     c, full, lin, fake = _prefill_layers()
     st = B.LinearAttentionState(fake, fake)
