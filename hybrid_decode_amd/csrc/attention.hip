@@ -36,6 +36,7 @@ namespace {
 
 constexpr int kNT = 256;
 constexpr int kUnroll = 4;                    // rows per row slot per batch
+constexpr int kMfRows = 64;                   // matrix-core path: rows per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
@@ -229,8 +230,8 @@ Q35_DEV void lm_append_group(const float v[16], const float* levels, const float
 // dequantised in the loop, and the block's unnormalised per-head accumulators
 // are rotated back before they are written (the transform is linear and its
 // own inverse, so the merge is unchanged).
-template <int D, int G, int F>
-__global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
+template <int D, int G, int F, bool MFT = false>
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void attn_partial_kernel(AttnArgs a) {
     static_assert(D <= kNT && D % 32 == 0, "one new-v element per thread; merge blocks of 32 dims");
     // row formats (F = a Q35_KV_* value): bf16; Turbo8 (K and V rotated, E4M3
     // with a bf16 scale per 16); the Lloyd-Max formats (LMB-bit codebook
@@ -242,22 +243,43 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
     constexpr bool LMV = LMB > 0;      // V in a Lloyd-Max format
     constexpr bool ROTQK = T8 || LMK;  // query and key rotated
     constexpr bool ROTV = T8 || LMV;
+    // MFT: Turbo8 rows at head dimension 128 or 256 through the matrix cores
+    // (tiles of 64 rows decoded once into LDS as f16; see the tile loop)
+    constexpr bool MF = MFT;
+    static_assert(!MF || (T8 && (D == 128 || D == 256)), "matrix-core tiles: Turbo8 at D 128 or 256");
+    constexpr int NG = D / 16;              // scale groups of 16 per row
+    constexpr int KTS = D + 8;              // MF: f16 per K row in LDS (8 of padding)
+    constexpr int VQS = 4 * (D + 16);       // MF: f16 per quad of V rows in LDS (16 slots of padding)
     using Geo = AGeo<D>;
     constexpr int LPR = Geo::LPR, RPI = Geo::RPI, B = Geo::B;
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     const int j = t % LPR;   // dim slice [8j, 8j+8)
     const int rs = t / LPR;  // row slot
-    const uint32_t g = blockIdx.y;
-    const uint32_t c = blockIdx.x;
+    // MF: the kv heads of a chunk run on one XCD (block b on XCD b % 8), so the
+    // group scales of a token, one 128-byte line for all heads, are fetched once
+    // into that XCD's L2; the grid is padded to whole groups of 8 chunks
+    uint32_t g = blockIdx.y, c = blockIdx.x;
+    if constexpr (MF) {
+        const uint32_t b = blockIdx.x + blockIdx.y * gridDim.x, q = b / 8u;
+        c = 8u * (q / a.hkv) + b % 8u;
+        g = q % a.hkv;
+    }
     const uint32_t T = a.chunk;
 
-    __shared__ float qs[(G + 1) * D];  // q heads of the group, then the new k
+    __shared__ __align__(16) float qs[(G + 1) * D];  // q heads of the group, then the new k
     __shared__ float vn[D];            // new v, bf16-rounded
     __shared__ float rsq[G + 1];
     __shared__ float2 rot[D / 2];      // (cos, sin) of pos * inv_freq[d], d < rotary / 2
     __shared__ float mls[RPI][2 * G];  // per-slot (max, sum)
-    __shared__ float red[(G < 4 ? G : 4) * RPI * D];  // per-slot outputs of up to 4 heads
-    __shared__ float ov[ROTV ? G * D : 1];  // rotated V: merged accumulators, rotated back
+    __shared__ float red[MF ? 1 : (G < 4 ? G : 4) * RPI * D];  // per-slot outputs of up to 4 heads
+    __shared__ float ov[(ROTV && !MF) ? G * D : 1];  // rotated V: merged accumulators, rotated back
+    // MF: the K tile, row-major, and the V tile in quads of rows: element
+    // 16 i + e of row r (group i, element e of the group) at slot NG e + i of
+    // quad r / 4, position r % 4, so a quad's 4 rows of one element are one
+    // 8-byte word and the decoders' stores spread over the banks.  After the
+    // loop the two hold the per-wave (max, sum) pairs and accumulators.
+    __shared__ __align__(16) _Float16 kt_s[MF ? kMfRows * KTS : 1];
+    __shared__ __align__(16) _Float16 vt_s[MF ? kMfRows / 4 * VQS : 1];
     __shared__ float lut[LMV ? 16 : 1];     // Lloyd-Max formats: the codebook levels
     __shared__ float bmax[G];               // sparse-V gate: running max of each head over the block
 
@@ -354,8 +376,30 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
             }
         }
     };
-    load_batch(kr[0], vr[0], ksr[0], vsr[0], t0);
-    load_batch(kr[1], vr[1], ksr[1], vsr[1], t0 + B);  // loads past the chunk return zero, unused
+    // MF: the decoders (thread t < 16 NG) each read 4 rows of one group of 16
+    // (codes and scale) of K and of V per tile
+    constexpr int ND = 16 * NG;
+    const bool dec = ND == kNT || t < ND;
+    const int gi = t % NG, rq = t / NG;  // decoder: group gi of the tile's rows 4 rq .. 4 rq + 3
+    uint4 kc4[4], vc4[4];
+    uint32_t ks4[4], vs4[4];
+    auto load_tile = [&](uint32_t tr) {  // tr: chunk-relative first row; rows past the chunk read zero
+        if (!dec) return;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t r = tr + 4u * rq + u;
+            kc4[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, r * krow_bytes + 16u * gi, 0, kAuxStream));
+            ks4[u] = __builtin_amdgcn_raw_buffer_load_b16(rks, r * ksrow_bytes + 2u * gi, 0, kAuxStream);
+            vc4[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, r * vrow_bytes + 16u * gi, 0, kAuxStream));
+            vs4[u] = __builtin_amdgcn_raw_buffer_load_b16(rvs, r * vsrow_bytes + 2u * gi, 0, kAuxStream);
+        }
+    };
+    if constexpr (MF) {
+        load_tile(0);
+    } else {
+        load_batch(kr[0], vr[0], ksr[0], vsr[0], t0);
+        load_batch(kr[1], vr[1], ksr[1], vsr[1], t0 + B);  // loads past the chunk return zero, unused
+    }
 
     // ---------------- prologue: q heads of this group and the new k, v
 #pragma unroll
@@ -479,6 +523,210 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(AttnArgs a) {
             }
         }
         __syncthreads();
+    }
+
+    if constexpr (MF) {
+        // ---------------- matrix-core tiles of kMfRows rows
+        // Per tile: the decoders turn the codes into f16 values (code times the
+        // group scale, rounded to nearest) in LDS, the row at `pos` from the
+        // values as stored in LDS; the next tile's loads then go out.  Wave w
+        // takes the tile's rows 16 w .. 16 w + 15: scores S (16 rows x 16
+        // columns, column h = query head h, zero for h >= G) as 16x16x32 MFMAs
+        // of K rows with q split into two f16 parts (high, then the rounding
+        // rest: products carry about 22 bits of q), an online softmax per head,
+        // and p V as 16x16x16 MFMAs with p in A (row = head, k = row of the
+        // tile), whose lane layout is the scores' output layout, so p stays in
+        // registers.  Lane L holds scores of rows 4 (L/16) + i, head L % 16,
+        // and accumulators of heads 4 (L/16) + i, V slot 16 dt + L % 16.
+        typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        const int hq = lane & 15, lq = lane >> 4;
+        // the B operands of the scores: q of head hq (columns h >= G repeat
+        // head h % G, never read back), elements 32 ks + 8 lq .. + 7, in f16
+        h8 qb[D / 32];
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qb[ks][e] = (_Float16)qs[(hq & (G - 1)) * D + 32 * ks + 8 * lq + e];
+        const float sscale = a.scale * kLog2e;  // scores in the base-2 exponent domain
+        const float lt = a.sparse_v_log2;
+        const uint32_t prow = (uint32_t)pos - t0;  // chunk-relative row of pos (out of range if not here)
+        float m = -INFINITY, l = 0.f, mrun = -INFINITY;
+        f4 O[D / 16];
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) O[dt] = f4{0.f, 0.f, 0.f, 0.f};
+
+        // 16 values of a group: 4 words of E4M3 codes times the group's bf16 scale
+        auto decode4 = [](uint32_t w, uint32_t sbits, float f[4]) {
+            const float sc = bf16_to_f32(sbits & 0xFFFFu);
+            const q35_float2_t p0 = e4m3x2_to_f32<false>(w), p1 = e4m3x2_to_f32<true>(w);
+            f[0] = p0.x * sc;
+            f[1] = p0.y * sc;
+            f[2] = p1.x * sc;
+            f[3] = p1.y * sc;
+        };
+        auto store_tile = [&](uint32_t tr) {
+            if (!dec) return;
+            // K: row by row, 16 elements as two 16-byte stores
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t kw[4] = {kc4[u].x, kc4[u].y, kc4[u].z, kc4[u].w};
+                float kf[16];
+#pragma unroll
+                for (int w4 = 0; w4 < 4; ++w4) decode4(kw[w4], ks4[u], kf + 4 * w4);
+                h8 k0, k1;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    k0[e] = (_Float16)kf[e];
+                    k1[e] = (_Float16)kf[8 + e];
+                }
+                _Float16* kd = kt_s + (4 * rq + u) * KTS + 16 * gi;
+                *reinterpret_cast<h8*>(kd) = k0;
+                *reinterpret_cast<h8*>(kd + 8) = k1;
+            }
+            // V: 4 elements of the 4 rows at a time, one 8-byte store per element
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4) {
+                float vf[4][4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t vw[4] = {vc4[u].x, vc4[u].y, vc4[u].z, vc4[u].w};
+                    decode4(vw[w4], vs4[u], vf[u]);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    *reinterpret_cast<h4*>(vt_s + rq * VQS + (NG * (4 * w4 + e) + gi) * 4) =
+                        h4{(_Float16)vf[0][e], (_Float16)vf[1][e], (_Float16)vf[2][e], (_Float16)vf[3][e]};
+            }
+        };
+
+        auto compute_tile = [&](uint32_t tr) {
+            f4 S = {0.f, 0.f, 0.f, 0.f};
+            const _Float16* ka = kt_s + (16 * wid + hq) * KTS + 8 * lq;
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+                const h8 kv = *reinterpret_cast<const h8*>(ka + 32 * ks);
+                S = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qb[ks], S, 0, 0, 0);
+            }
+            const uint32_t rb = tr + 16u * wid + 4u * lq;  // chunk-relative row of S[0]
+            float s[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[i] = rb + i < nrows ? S[i] * sscale : -INFINITY;
+            float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+            mx = fmaxf(mx, lane_xor<16>(mx));
+            mx = fmaxf(mx, lane_xor<32>(mx));  // the wave's max over the tile, head hq
+            mrun = fmaxf(mrun, mx);
+            // lazy rescale, as in the row-slot loop: only when some head's max
+            // grows by more than 8 (weights stay below 2^8, also in f16)
+            if (__builtin_amdgcn_ballot_w64(mx > m + 8.0f) != 0) {
+                const float mn = fmaxf(m, mx);
+                const float corr = mn == -INFINITY ? 1.0f : exp2f(m - mn);
+                m = mn;
+                l *= corr;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ci = __shfl(corr, 4 * lq + i);  // head 4 lq + i lives in lane 4 lq + i
+#pragma unroll
+                    for (int dt = 0; dt < D / 16; ++dt) O[dt][i] *= ci;
+                }
+            }
+            // every row's weight enters the sum; its value only if s - mrun >= lt
+            // (mrun: the exact running max of this wave's rows, never above
+            // the block's final max, so a dropped row's weight relative to the
+            // largest is below the threshold)
+            const float mref = m == -INFINITY ? 0.f : m;
+            h4 P;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = exp2f(s[i] - mref);
+                l += p;
+                P[i] = (_Float16)(s[i] - mrun >= lt ? p : 0.f);
+            }
+            const _Float16* vb = vt_s + (4 * wid + lq) * VQS + 4 * hq;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+                const h4 vv = *reinterpret_cast<const h4*>(vb + 64 * dt);
+                O[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(P, vv, O[dt], 0, 0, 0);
+            }
+        };
+
+        for (uint32_t tr = 0; tr < nrows; tr += kMfRows) {
+            __syncthreads();  // the previous tile is read
+            store_tile(tr);
+            if (tr + kMfRows < nrows) load_tile(tr + kMfRows);
+            if (has_new && prow - tr < (uint32_t)kMfRows) {
+                // the row at pos, from its values as stored (its codes in memory
+                // are being written by this block)
+                __syncthreads();
+                const uint32_t r = prow - tr;
+                for (int d = t; d < D; d += kNT) {
+                    const int sl = NG * (d % 16) + d / 16;  // V slot of element d
+                    kt_s[r * KTS + d] = (_Float16)qs[G * D + d];
+                    vt_s[(r / 4) * VQS + sl * 4 + r % 4] = (_Float16)vn[d];
+                }
+            }
+            __syncthreads();
+            compute_tile(tr);
+        }
+
+        // ---------------- merge the four waves, write this chunk's partials
+        l += lane_xor<16>(l);
+        l += lane_xor<32>(l);  // head hq's sum over the wave's rows
+        static_assert(4 * G * 2 * sizeof(float) <= sizeof(kt_s) && 4 * G * D * sizeof(float) <= sizeof(vt_s),
+                      "per-wave results fit the tiles");
+        float* wml = reinterpret_cast<float*>(kt_s);  // [wave][head] (max, sum)
+        float* wo = reinterpret_cast<float*>(vt_s);   // [wave][head][D] accumulators, scaled to the block max
+        __syncthreads();  // every wave is done with the tiles
+        if (lane < G) {
+            wml[(wid * G + lane) * 2] = m;
+            wml[(wid * G + lane) * 2 + 1] = l;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = 4 * lq + i;
+            if (h < G) {
+                float M = -INFINITY;
+#pragma unroll
+                for (int w = 0; w < kNT / 64; ++w) M = fmaxf(M, wml[(w * G + h) * 2]);  // wave 0 has a row
+                const float f = exp2f(wml[(wid * G + h) * 2] - M);
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt) {
+                    const int sl = 16 * dt + hq;              // V slot
+                    const int d = 16 * (sl % NG) + sl / NG;   // its element
+                    wo[(wid * G + h) * D + d] = O[dt][i] * f;
+                }
+            }
+        }
+        float* pacc = a.part_acc + ((size_t)g * a.max_chunks + c) * G * D;
+        float* pml = a.part_ml + ((size_t)g * a.max_chunks + c) * 2 * G;
+        if (t < G) {
+            float M = -INFINITY, tot = 0.f;
+#pragma unroll
+            for (int w = 0; w < kNT / 64; ++w) M = fmaxf(M, wml[(w * G + t) * 2]);
+#pragma unroll
+            for (int w = 0; w < kNT / 64; ++w) tot = fmaf(exp2f(wml[(w * G + t) * 2] - M), wml[(w * G + t) * 2 + 1], tot);
+            pml[2 * t] = M;
+            pml[2 * t + 1] = tot;
+        }
+        __syncthreads();
+        // each head's merged accumulator back to the original basis, one head per wave
+        for (int h = wid; h < G; h += kNT / 64) {
+            float x[D / 64];
+#pragma unroll
+            for (int i = 0; i < D / 64; ++i) {
+                const int d = lane * (D / 64) + i;
+                float o = 0.f;
+#pragma unroll
+                for (int w = 0; w < kNT / 64; ++w) o += wo[(w * G + h) * D + d];
+                x[i] = o;
+            }
+            wht_regs<D>(x, lane);
+#pragma unroll
+            for (int i = 0; i < D / 64; ++i) pacc[h * D + lane * (D / 64) + i] = x[i];
+        }
+        return;
     }
 
     // ---------------- batches of B rows: scores, online softmax, p V
@@ -853,8 +1101,20 @@ __global__ __launch_bounds__(kNT) void attn_merge_kernel(AttnArgs a) {
     }
 }
 
+// Turbo8 at head dimension 128 or 256 takes the matrix-core tiles once a
+// chunk holds a whole tile.
+template <int D, int F>
+constexpr bool kHasMfTiles = F == Q35_KV_TURBO8 && (D == 128 || D == 256);
+
 template <int D, int G, int F>
 void launch_partial(const AttnArgs& a, uint32_t grid_chunks, hipStream_t stream) {
+    if constexpr (kHasMfTiles<D, F>) {
+        if (a.chunk >= (uint32_t)kMfRows) {
+            hipLaunchKernelGGL((attn_partial_kernel<D, G, F, true>), dim3((grid_chunks + 7) / 8 * 8, a.hkv), dim3(kNT),
+                               0, stream, a);
+            return;
+        }
+    }
     hipLaunchKernelGGL((attn_partial_kernel<D, G, F>), dim3(grid_chunks, a.hkv), dim3(kNT), 0, stream, a);
 }
 
@@ -947,7 +1207,10 @@ hipError_t attn_launch(uint32_t head_dim, uint32_t group, const AttnArgs& a, uin
 }
 
 template <int D, int G>
-const void* partial_ptr(uint32_t fmt) {
+const void* partial_ptr(uint32_t fmt, bool tiles) {
+    if constexpr (kHasMfTiles<D, Q35_KV_TURBO8>)
+        if (tiles && fmt == Q35_KV_TURBO8) return (const void*)&attn_partial_kernel<D, G, Q35_KV_TURBO8, true>;
+    if (tiles) return nullptr;
 #define X(FF) \
     if (fmt == FF) return (const void*)&attn_partial_kernel<D, G, FF>;
     Q35_KV_FORMATS(X)
@@ -955,9 +1218,9 @@ const void* partial_ptr(uint32_t fmt) {
     return nullptr;
 }
 
-const void* attn_kernel_ptr(uint32_t head_dim, uint32_t group, uint32_t kv_dtype) {
+const void* attn_kernel_ptr(uint32_t head_dim, uint32_t group, uint32_t kv_dtype, bool tiles) {
 #define X(DD, GG) \
-    if (head_dim == DD && group == GG) return partial_ptr<DD, GG>(kv_dtype);
+    if (head_dim == DD && group == GG) return partial_ptr<DD, GG>(kv_dtype, tiles);
     Q35_ATTN_SHAPES(X)
 #undef X
     return nullptr;

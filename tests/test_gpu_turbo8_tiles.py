@@ -1,0 +1,88 @@
+"""GPU parity of the matrix-core tiles of Turbo8 decode attention (full_attention.rs
+page, the Turbo8 branch of `attention_decode`, with the sparse-V gate).
+
+At head dimension 128 or 256, once a split-K chunk holds at least 64 rows, the
+partial kernel decodes the chunk's rows 64 at a time into LDS and runs the
+scores and the weighted value sum on the matrix cores.  The cases below pick
+cache lengths whose chunks hold one to three such tiles with ragged tails,
+and positions whose row falls inside a later tile of its chunk (the appended
+row enters from the values as stored).  For each, one layer step runs with the
+gate off, at its default and at 0.3; the attention tap is compared with the
+oracle's attention over the cache as stored, with the kernel's own query: at
+threshold 0 within the fp32 tolerance, otherwise within it plus the weight of
+the rows the oracle's gate drops (the kernel drops a subset of those).
+
+Layer: hidden 256 (the projections are not what is tested here), the head
+geometry of each case; cache rows drawn as in the other Turbo8 tests (every
+finite E4M3 code, bf16 scales U(1e-3, 1e-2)).
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_common import TOL_F32, check_gated_attention, gated_attention_ref, rel, say
+
+pytestmark = pytest.mark.gpu
+
+# (head_dim, query heads, kv heads, rotary dims, positions)
+#   256 / 16 / 4: chunks of 64 rows at position 8191 (one tile each), 152 rows
+#                 at 19100 (pos at row 100: tile 1 of a 101-row chunk), 192 rows
+#                 at 24575 (three tiles, pos the last row)
+#   256 / 16 / 2: G = 8, chunks of 152 rows at 38900 (pos at row 140)
+#   128 / 8 / 2:  chunks of 64 rows at 700 (eleven chunks, the last ragged),
+#                 128 rows at 20000 (pos at row 32 of a chunk's first tile)
+#   128 / 4 / 4:  G = 1 at 5000
+CASES = [
+    (256, 16, 4, 64, (8191, 19100, 24575)),
+    (256, 16, 2, 64, (38900,)),
+    (128, 8, 2, 32, (700, 20000)),
+    (128, 4, 4, 32, (5000,)),
+]
+
+
+@pytest.fixture(scope="module")
+def rt():
+    from hybrid_decode_amd import runtime
+    runtime.kernels(0)
+    return runtime
+
+
+def _cfg(D, hq, hkv, rot):
+    return replace(synth.tiny("f32"), num_heads=hq, num_kv_heads=hkv, head_dim=D, rotary_dim=rot)
+
+
+@pytest.mark.parametrize("D,hq,hkv,rot,positions", CASES,
+                         ids=[f"d{c[0]}_g{c[1] // c[2]}" for c in CASES])
+def test_turbo8_tiles_match_the_oracle(rt, gen, D, hq, hkv, rot, positions):
+    cfg = _cfg(D, hq, hkv, rot)
+    layer = synth.full_layer(gen, cfg, f"gpu.t8mf.d{D}.g{hq // hkv}")
+    inv = rt.inv_freq_dev(cfg)
+    Ld = rt.FullLayerDev(layer)
+    rep = hq // hkv
+    for start in positions:
+        cap = start + 4
+        x = gen.act(f"gpu.t8mf.d{D}.g{rep}.x{start}", (cfg.hidden,), "f32")
+        attn = {}
+        for tau in (0.0, 1e-3, 0.3):
+            kv = synth.kv_cache_turbo8(gen, cfg, f"gpu.t8mf.d{D}.g{rep}.{start}", cap, start)
+            KVd = rt.KvCacheDev(kv, sparse_v=tau)
+            scr = rt.FullScratchDev(cfg, cap, taps=True)
+            pos = torch.tensor([start], dtype=torch.int32, device="cuda")
+            say(f"Turbo8 tiles: D {D}, G {rep}, Hkv {hkv}, position {start}, sparse_v {tau}")
+            rt.forward_full_attention(cfg, Ld, scr, KVd, inv, pos, rt.to_dev(x), start)
+            torch.cuda.synchronize()
+            after = KVd.to_host()
+            q = scr.t["q_norm_out"].cpu().numpy().astype(np.float64).reshape(hq, D)
+            g = scr.t["attn_out"].cpu().numpy().astype(np.float64).reshape(hq, D)
+            assert np.all(np.isfinite(g))
+            e, b, nd = check_gated_attention(g, "turbo8", q, after, start + 1, tau, rep, TOL_F32)
+            say(f"  error {e:.2e} of the norm (dropped-weight bound {b:.2e}, {nd} pairs dropped by the oracle)")
+            if tau == 0.0:
+                assert nd == 0
+                assert rel(g, gated_attention_ref("turbo8", q, after, start + 1, 0.0)) < TOL_F32
+            attn[tau] = g
+            del KVd, scr
+        assert rel(attn[0.3], attn[0.0]) > 1e-6   # the gate dropped rows
