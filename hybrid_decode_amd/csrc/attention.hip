@@ -243,10 +243,11 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
     constexpr bool LMV = LMB > 0;      // V in a Lloyd-Max format
     constexpr bool ROTQK = T8 || LMK;  // query and key rotated
     constexpr bool ROTV = T8 || LMV;
-    // MFT: Turbo8 rows at head dimension 128 or 256 through the matrix cores
-    // (tiles of 64 rows decoded once into LDS as f16; see the tile loop)
+    // MFT: the quantised formats at head dimension 128 or 256 through the
+    // matrix cores (tiles of 64 rows decoded once into LDS as f16; see the
+    // tile loop)
     constexpr bool MF = MFT;
-    static_assert(!MF || (T8 && (D == 128 || D == 256)), "matrix-core tiles: Turbo8 at D 128 or 256");
+    static_assert(!MF || ((T8 || LMV) && (D == 128 || D == 256)), "matrix-core tiles: quantised V at D 128 or 256");
     constexpr int NG = D / 16;              // scale groups of 16 per row
     constexpr int KTS = D + 8;              // MF: f16 per K row in LDS (8 of padding)
     constexpr int VQS = 4 * (D + 16);       // MF: f16 per quad of V rows in LDS (16 slots of padding)
@@ -377,21 +378,46 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
         }
     };
     // MF: the decoders (thread t < 16 NG) each read 4 rows of one group of 16
-    // (codes and scale) of K and of V per tile
+    // (data and scale) of K and of V per tile: KW / VW words of data per row
+    // (E4M3 codes: 4; 4- and 3-bit indices: 2, the 3-bit group's 6 bytes from
+    // the word boundary below them; 2-bit: 1; bf16 keys: 8)
     constexpr int ND = 16 * NG;
     const bool dec = ND == kNT || t < ND;
     const int gi = t % NG, rq = t / NG;  // decoder: group gi of the tile's rows 4 rq .. 4 rq + 3
-    uint4 kc4[4], vc4[4];
+    constexpr int KW = T8 ? 4 : LMK ? (LMB == 2 ? 1 : 2) : 8;
+    constexpr int VW = T8 ? 4 : (LMB == 2 ? 1 : 2);
+    uint32_t kc4[4][KW], vc4[4][VW];
     uint32_t ks4[4], vs4[4];
+    // byte offset of a row's group of 16 in its side (data of BITS bits per element)
+    auto grp_off = [&](uint32_t bits) { return (bits * 2u * (uint32_t)gi) & ~3u; };
+    auto load_words = [&](__amdgpu_buffer_rsrc_t rr, uint32_t off, uint32_t* w, auto nw) {
+        constexpr int N = decltype(nw)::value;
+        if constexpr (N == 8) {
+            const uint4 a0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, kAuxStream));
+            const uint4 a1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, off + 16u, 0, kAuxStream));
+            w[0] = a0.x, w[1] = a0.y, w[2] = a0.z, w[3] = a0.w, w[4] = a1.x, w[5] = a1.y, w[6] = a1.z, w[7] = a1.w;
+        } else if constexpr (N == 4) {
+            const uint4 a0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, kAuxStream));
+            w[0] = a0.x, w[1] = a0.y, w[2] = a0.z, w[3] = a0.w;
+        } else if constexpr (N == 2) {
+            const uint2 a0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, kAuxStream));
+            w[0] = a0.x, w[1] = a0.y;
+        } else {
+            w[0] = __builtin_amdgcn_raw_buffer_load_b32(rr, off, 0, kAuxStream);
+        }
+    };
     auto load_tile = [&](uint32_t tr) {  // tr: chunk-relative first row; rows past the chunk read zero
         if (!dec) return;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const uint32_t r = tr + 4u * rq + u;
-            kc4[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, r * krow_bytes + 16u * gi, 0, kAuxStream));
-            ks4[u] = __builtin_amdgcn_raw_buffer_load_b16(rks, r * ksrow_bytes + 2u * gi, 0, kAuxStream);
-            vc4[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, r * vrow_bytes + 16u * gi, 0, kAuxStream));
-            vs4[u] = __builtin_amdgcn_raw_buffer_load_b16(rvs, r * vsrow_bytes + 2u * gi, 0, kAuxStream);
+            load_words(rk, r * krow_bytes + grp_off(KBITS), kc4[u], std::integral_constant<int, KW>{});
+            if constexpr (T8) ks4[u] = __builtin_amdgcn_raw_buffer_load_b16(rks, r * ksrow_bytes + 2u * gi, 0, kAuxStream);
+            else if constexpr (LMK) ks4[u] = __builtin_amdgcn_raw_buffer_load_b8(rks, r * ksrow_bytes + gi, 0, kAuxStream);
+            else ks4[u] = 0;
+            load_words(rv, r * vrow_bytes + grp_off(VBITS), vc4[u], std::integral_constant<int, VW>{});
+            if constexpr (T8) vs4[u] = __builtin_amdgcn_raw_buffer_load_b16(rvs, r * vsrow_bytes + 2u * gi, 0, kAuxStream);
+            else vs4[u] = __builtin_amdgcn_raw_buffer_load_b8(rvs, r * vsrow_bytes + gi, 0, kAuxStream);
         }
     };
     if constexpr (MF) {
@@ -557,24 +583,42 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) O[dt] = f4{0.f, 0.f, 0.f, 0.f};
 
-        // 16 values of a group: 4 words of E4M3 codes times the group's bf16 scale
-        auto decode4 = [](uint32_t w, uint32_t sbits, float f[4]) {
-            const float sc = bf16_to_f32(sbits & 0xFFFFu);
-            const q35_float2_t p0 = e4m3x2_to_f32<false>(w), p1 = e4m3x2_to_f32<true>(w);
-            f[0] = p0.x * sc;
-            f[1] = p0.y * sc;
-            f[2] = p1.x * sc;
-            f[3] = p1.y * sc;
+        // elements 4 c .. 4 c + 3 of a row's group of 16, decoded: E4M3 codes
+        // times the bf16 group scale, codebook levels times the E4M3 group
+        // scale, or bf16 keys as they are
+        const uint32_t lsh = 8u * ((uint32_t)LMB * 2u * gi & 3u);  // 3-bit groups: bits below the group
+        auto dec4 = [&](const uint32_t* w, uint32_t sbits, int c, auto lmc, auto nwc, float f[4]) {
+            constexpr bool lm = decltype(lmc)::value;
+            constexpr int nw = decltype(nwc)::value;
+            if constexpr (nw == 8) {  // bf16
+                f[0] = bf16_lo(w[2 * c]);
+                f[1] = bf16_hi(w[2 * c]);
+                f[2] = bf16_lo(w[2 * c + 1]);
+                f[3] = bf16_hi(w[2 * c + 1]);
+            } else if constexpr (!lm) {  // Turbo8
+                const float sc = bf16_to_f32(sbits & 0xFFFFu);
+                const q35_float2_t p0 = e4m3x2_to_f32<false>(w[c]), p1 = e4m3x2_to_f32<true>(w[c]);
+                f[0] = p0.x * sc;
+                f[1] = p0.y * sc;
+                f[2] = p1.x * sc;
+                f[3] = p1.y * sc;
+            } else {
+                const float sc = e4m3x2_to_f32<false>(sbits & 0xFFu).x;
+                uint64_t bits = w[0];
+                if constexpr (nw == 2) bits = (((uint64_t)w[1] << 32) | bits) >> lsh;
+                bits >>= 4 * LMB * c;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) f[e] = lut[(uint32_t)(bits >> (LMB * e)) & ((1u << LMB) - 1u)] * sc;
+            }
         };
-        auto store_tile = [&](uint32_t tr) {
+        auto store_tile = [&]() {
             if (!dec) return;
             // K: row by row, 16 elements as two 16-byte stores
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const uint32_t kw[4] = {kc4[u].x, kc4[u].y, kc4[u].z, kc4[u].w};
                 float kf[16];
 #pragma unroll
-                for (int w4 = 0; w4 < 4; ++w4) decode4(kw[w4], ks4[u], kf + 4 * w4);
+                for (int w4 = 0; w4 < 4; ++w4) dec4(kc4[u], ks4[u], w4, std::bool_constant<LMK>{}, std::integral_constant<int, KW>{}, kf + 4 * w4);
                 h8 k0, k1;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -584,20 +628,19 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
                 _Float16* kd = kt_s + (4 * rq + u) * KTS + 16 * gi;
                 *reinterpret_cast<h8*>(kd) = k0;
                 *reinterpret_cast<h8*>(kd + 8) = k1;
+                if constexpr (LMB > 0) __builtin_amdgcn_sched_barrier(0);  // bounds the codebook reads in flight
             }
             // V: 4 elements of the 4 rows at a time, one 8-byte store per element
 #pragma unroll
             for (int w4 = 0; w4 < 4; ++w4) {
                 float vf[4][4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const uint32_t vw[4] = {vc4[u].x, vc4[u].y, vc4[u].z, vc4[u].w};
-                    decode4(vw[w4], vs4[u], vf[u]);
-                }
+                for (int u = 0; u < 4; ++u) dec4(vc4[u], vs4[u], w4, std::bool_constant<LMV>{}, std::integral_constant<int, VW>{}, vf[u]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     *reinterpret_cast<h4*>(vt_s + rq * VQS + (NG * (4 * w4 + e) + gi) * 4) =
                         h4{(_Float16)vf[0][e], (_Float16)vf[1][e], (_Float16)vf[2][e], (_Float16)vf[3][e]};
+                if constexpr (LMB > 0) __builtin_amdgcn_sched_barrier(0);
             }
         };
 
@@ -651,9 +694,11 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
             }
         };
 
+        // the next tile's loads go out once this one is decoded (two tiles
+        // in flight measured slower, also without spills)
         for (uint32_t tr = 0; tr < nrows; tr += kMfRows) {
             __syncthreads();  // the previous tile is read
-            store_tile(tr);
+            store_tile();
             if (tr + kMfRows < nrows) load_tile(tr + kMfRows);
             if (has_new && prow - tr < (uint32_t)kMfRows) {
                 // the row at pos, from its values as stored (its codes in memory
@@ -726,6 +771,8 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
             for (int i = 0; i < D / 64; ++i) pacc[h * D + lane * (D / 64) + i] = x[i];
         }
+        if constexpr (!ROTQK)  // bf16 keys: the new row's key, stored last as in the row-slot path
+            if (has_new && t < D) a.kc[((size_t)pos * a.hkv + g) * D + t] = new_k;
         return;
     }
 
@@ -1101,10 +1148,10 @@ __global__ __launch_bounds__(kNT) void attn_merge_kernel(AttnArgs a) {
     }
 }
 
-// Turbo8 at head dimension 128 or 256 takes the matrix-core tiles once a
-// chunk holds a whole tile.
+// The quantised formats at head dimension 128 or 256 take the matrix-core
+// tiles once a chunk holds a whole tile.
 template <int D, int F>
-constexpr bool kHasMfTiles = F == Q35_KV_TURBO8 && (D == 128 || D == 256);
+constexpr bool kHasMfTiles = (F == Q35_KV_TURBO8 || lm_bits(F) > 0) && (D == 128 || D == 256);
 
 template <int D, int G, int F>
 void launch_partial(const AttnArgs& a, uint32_t grid_chunks, hipStream_t stream) {
@@ -1208,9 +1255,14 @@ hipError_t attn_launch(uint32_t head_dim, uint32_t group, const AttnArgs& a, uin
 
 template <int D, int G>
 const void* partial_ptr(uint32_t fmt, bool tiles) {
-    if constexpr (kHasMfTiles<D, Q35_KV_TURBO8>)
-        if (tiles && fmt == Q35_KV_TURBO8) return (const void*)&attn_partial_kernel<D, G, Q35_KV_TURBO8, true>;
-    if (tiles) return nullptr;
+    if (tiles) {
+#define X(FF)                                 \
+    if constexpr (kHasMfTiles<D, FF>)         \
+        if (fmt == FF) return (const void*)&attn_partial_kernel<D, G, FF, true>;
+        Q35_KV_FORMATS(X)
+#undef X
+        return nullptr;
+    }
 #define X(FF) \
     if (fmt == FF) return (const void*)&attn_partial_kernel<D, G, FF>;
     Q35_KV_FORMATS(X)

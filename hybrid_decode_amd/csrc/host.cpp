@@ -472,7 +472,9 @@ q35_status q35_kernels_resolve(int device, Qwen35Kernels** out) {
             for (uint32_t f : {Q35_KV_BF16, Q35_KV_TURBO8, Q35_KV_BF16K_TURBO4V})
                 probe(attn_kernel_ptr(d, g, f), "attention");
     for (uint32_t d : {128u, 256u})
-        for (uint32_t g : {1u, 2u, 4u, 8u}) probe(attn_kernel_ptr(d, g, Q35_KV_TURBO8, true), "attention tiles");
+        for (uint32_t g : {1u, 2u, 4u, 8u})
+            for (uint32_t f : {Q35_KV_TURBO8, Q35_KV_TURBO4, Q35_KV_BF16K_TURBO4V})
+                probe(attn_kernel_ptr(d, g, f, true), "attention tiles");
     for (int i = 0; pf_kernel_ptr(i); ++i) probe(pf_kernel_ptr(i), "prefill");
 #define X(KK)                                                                  \
     probe(gemv_kernel_ptr(kOpInFullP, KK, false, false), "q/k/v (partial sums)"); \

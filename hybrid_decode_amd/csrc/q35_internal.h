@@ -186,7 +186,7 @@ uint32_t attn_rows_per_iter(uint32_t head_dim);
 hipError_t attn_launch(uint32_t head_dim, uint32_t group, const AttnArgs& a, uint32_t grid_chunks,
                        uint32_t kv_dtype, hipStream_t stream);
 // The partial kernel of a shape and KV format; tiles: the matrix-core tile
-// variant (Turbo8 at head dimension 128 or 256 only, else null).
+// variant (the quantised formats at head dimension 128 or 256 only, else null).
 const void* attn_kernel_ptr(uint32_t head_dim, uint32_t group, uint32_t kv_dtype, bool tiles = false);
 // Turbo8 group quantiser and E4M3 decoder of the attention kernels, over plain buffers.
 hipError_t turbo8_quantize_launch(const float* x, uint32_t n, uint8_t* codes, uint16_t* scales,
