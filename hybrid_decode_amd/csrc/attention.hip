@@ -282,6 +282,11 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
     __shared__ __align__(16) _Float16 kt_s[MF ? kMfRows * KTS : 1];
     __shared__ __align__(16) _Float16 vt_s[MF ? kMfRows / 4 * VQS : 1];
     __shared__ float lut[LMV ? 16 : 1];     // Lloyd-Max formats: the codebook levels
+    // MF, Lloyd-Max formats: the levels as f16, by pairs (4-bit: one index
+    // byte, 256 pairs; 3-bit: 6 index bits, 64 pairs) or by fours (2-bit: one
+    // index byte, 256 entries of two words); the first element in the low half
+    constexpr int PTW = (MF && LMV) ? (LMB == 2 ? 512 : LMB == 4 ? 256 : 64) : 1;
+    __shared__ __align__(8) uint32_t ptab[PTW];
     __shared__ float bmax[G];               // sparse-V gate: running max of each head over the block
 
     const int32_t pos = attn_pos(a);
@@ -434,6 +439,17 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
     if (t < D) vn[t] = ROTV ? vnew : bf16_to_f32(f32_to_bf16(vnew));
     if constexpr (LMV)
         if (t < 16) lut[t] = a.lm_levels[t];
+    if constexpr (MF && LMV) {
+        auto lv16 = [&](uint32_t i) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a.lm_levels[i]); };
+        if constexpr (LMB == 4) {
+            ptab[t] = lv16(t & 15u) | (lv16((uint32_t)t >> 4) << 16);
+        } else if constexpr (LMB == 3) {
+            if (t < 64) ptab[t] = lv16(t & 7u) | (lv16((uint32_t)t >> 3) << 16);
+        } else {
+            ptab[2 * t] = lv16(t & 3u) | (lv16((t >> 2) & 3u) << 16);
+            ptab[2 * t + 1] = lv16((t >> 4) & 3u) | (lv16((uint32_t)t >> 6) << 16);
+        }
+    }
     if (t < G) bmax[t] = -INFINITY;
     if (t < (int)a.rotary / 2) {
         float sn, cs;
@@ -566,6 +582,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
         // and accumulators of heads 4 (L/16) + i, V slot 16 dt + L % 16.
         typedef _Float16 h8 __attribute__((ext_vector_type(8)));
         typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
         typedef float f4 __attribute__((ext_vector_type(4)));
         const int hq = lane & 15, lq = lane >> 4;
         // the B operands of the scores: q of head hq (columns h >= G repeat
@@ -584,41 +601,66 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
         for (int dt = 0; dt < D / 16; ++dt) O[dt] = f4{0.f, 0.f, 0.f, 0.f};
 
         // elements 4 c .. 4 c + 3 of a row's group of 16, decoded: E4M3 codes
-        // times the bf16 group scale, codebook levels times the E4M3 group
-        // scale, or bf16 keys as they are
+        // times the bf16 group scale, or bf16 keys as they are
         const uint32_t lsh = 8u * ((uint32_t)LMB * 2u * gi & 3u);  // 3-bit groups: bits below the group
-        auto dec4 = [&](const uint32_t* w, uint32_t sbits, int c, auto lmc, auto nwc, float f[4]) {
-            constexpr bool lm = decltype(lmc)::value;
+        auto dec4 = [&](const uint32_t* w, uint32_t sbits, int c, auto nwc, float f[4]) {
             constexpr int nw = decltype(nwc)::value;
             if constexpr (nw == 8) {  // bf16
                 f[0] = bf16_lo(w[2 * c]);
                 f[1] = bf16_hi(w[2 * c]);
                 f[2] = bf16_lo(w[2 * c + 1]);
                 f[3] = bf16_hi(w[2 * c + 1]);
-            } else if constexpr (!lm) {  // Turbo8
+            } else {  // Turbo8
                 const float sc = bf16_to_f32(sbits & 0xFFFFu);
                 const q35_float2_t p0 = e4m3x2_to_f32<false>(w[c]), p1 = e4m3x2_to_f32<true>(w[c]);
                 f[0] = p0.x * sc;
                 f[1] = p0.y * sc;
                 f[2] = p1.x * sc;
                 f[3] = p1.y * sc;
-            } else {
-                const float sc = e4m3x2_to_f32<false>(sbits & 0xFFu).x;
-                uint64_t bits = w[0];
-                if constexpr (nw == 2) bits = (((uint64_t)w[1] << 32) | bits) >> lsh;
-                bits >>= 4 * LMB * c;
+            }
+        };
+        // a row's group of 16 in a Lloyd-Max format as 8 f16 pairs (elements
+        // 2 p, 2 p + 1 in word p): levels from the pair table times the E4M3
+        // group scale, in packed f16 (the level and the product each rounded
+        // to f16)
+        auto dec_lm = [&](const uint32_t* w, uint32_t sbyte, uint32_t o[8]) {
+            const _Float16 sh = (_Float16)e4m3x2_to_f32<false>(sbyte & 0xFFu).x;  // exact: E4M3 is a subset of f16
+            const h2 s2 = {sh, sh};
+            auto scaled = [&](uint32_t x) { return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, x) * s2); };
+            if constexpr (LMB == 4) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) f[e] = lut[(uint32_t)(bits >> (LMB * e)) & ((1u << LMB) - 1u)] * sc;
+                for (int p = 0; p < 8; ++p) o[p] = scaled(ptab[(w[p / 4] >> (8 * (p % 4))) & 0xFFu]);
+            } else if constexpr (LMB == 2) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint2 v = reinterpret_cast<const uint2*>(ptab)[(w[0] >> (8 * k)) & 0xFFu];
+                    o[2 * k] = scaled(v.x);
+                    o[2 * k + 1] = scaled(v.y);
+                }
+            } else {
+                const uint64_t bits = (((uint64_t)w[1] << 32) | w[0]) >> lsh;
+#pragma unroll
+                for (int p = 0; p < 8; ++p) o[p] = scaled(ptab[(uint32_t)(bits >> (6 * p)) & 0x3Fu]);
             }
         };
         auto store_tile = [&]() {
             if (!dec) return;
             // K: row by row, 16 elements as two 16-byte stores
+            if constexpr (LMK) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    uint32_t o[8];
+                    dec_lm(kc4[u], ks4[u], o);
+                    _Float16* kd = kt_s + (4 * rq + u) * KTS + 16 * gi;
+                    *reinterpret_cast<uint4*>(kd) = make_uint4(o[0], o[1], o[2], o[3]);
+                    *reinterpret_cast<uint4*>(kd + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+                }
+            } else
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 float kf[16];
 #pragma unroll
-                for (int w4 = 0; w4 < 4; ++w4) dec4(kc4[u], ks4[u], w4, std::bool_constant<LMK>{}, std::integral_constant<int, KW>{}, kf + 4 * w4);
+                for (int w4 = 0; w4 < 4; ++w4) dec4(kc4[u], ks4[u], w4, std::integral_constant<int, KW>{}, kf + 4 * w4);
                 h8 k0, k1;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -628,19 +670,32 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
                 _Float16* kd = kt_s + (4 * rq + u) * KTS + 16 * gi;
                 *reinterpret_cast<h8*>(kd) = k0;
                 *reinterpret_cast<h8*>(kd + 8) = k1;
-                if constexpr (LMB > 0) __builtin_amdgcn_sched_barrier(0);  // bounds the codebook reads in flight
             }
-            // V: 4 elements of the 4 rows at a time, one 8-byte store per element
+            // V: one 8-byte store per element (its 4 rows)
+            if constexpr (LMV) {
+                uint32_t o[4][8];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) dec_lm(vc4[u], vs4[u], o[u]);
+#pragma unroll
+                for (int p = 0; p < 8; ++p) {
+                    // low halves: element 2 p of rows 0..3; high halves: element 2 p + 1
+                    const uint2 lo = make_uint2(__builtin_amdgcn_perm(o[1][p], o[0][p], 0x05040100u),
+                                                __builtin_amdgcn_perm(o[3][p], o[2][p], 0x05040100u));
+                    const uint2 hi = make_uint2(__builtin_amdgcn_perm(o[1][p], o[0][p], 0x07060302u),
+                                                __builtin_amdgcn_perm(o[3][p], o[2][p], 0x07060302u));
+                    *reinterpret_cast<uint2*>(vt_s + rq * VQS + (NG * (2 * p) + gi) * 4) = lo;
+                    *reinterpret_cast<uint2*>(vt_s + rq * VQS + (NG * (2 * p + 1) + gi) * 4) = hi;
+                }
+            } else
 #pragma unroll
             for (int w4 = 0; w4 < 4; ++w4) {
                 float vf[4][4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) dec4(vc4[u], vs4[u], w4, std::bool_constant<LMV>{}, std::integral_constant<int, VW>{}, vf[u]);
+                for (int u = 0; u < 4; ++u) dec4(vc4[u], vs4[u], w4, std::integral_constant<int, VW>{}, vf[u]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     *reinterpret_cast<h4*>(vt_s + rq * VQS + (NG * (4 * w4 + e) + gi) * 4) =
                         h4{(_Float16)vf[0][e], (_Float16)vf[1][e], (_Float16)vf[2][e], (_Float16)vf[3][e]};
-                if constexpr (LMB > 0) __builtin_amdgcn_sched_barrier(0);
             }
         };
 
