@@ -643,8 +643,12 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
                 for (int p = 0; p < 8; ++p) o[p] = scaled(ptab[(uint32_t)(bits >> (6 * p)) & 0x3Fu]);
             }
         };
-        auto store_tile = [&]() {
-            if (!dec) return;
+        // Rows past the chunk: the first tile decodes them (their loads read
+        // zero); a later tile leaves a decoder's 4 rows as the previous tile
+        // left them when all 4 are past the chunk (finite values, masked out
+        // of the scores and given weight 0)
+        auto store_tile = [&](uint32_t tr) {
+            if (!dec || (tr > 0 && tr + 4u * rq >= nrows)) return;
             // K: row by row, 16 elements as two 16-byte stores
             if constexpr (LMK) {
 #pragma unroll
@@ -700,6 +704,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
         };
 
         auto compute_tile = [&](uint32_t tr) {
+            if (tr + 16u * wid >= nrows) return;  // none of the wave's rows is in the chunk
             f4 S = {0.f, 0.f, 0.f, 0.f};
             const _Float16* ka = kt_s + (16 * wid + hq) * KTS + 8 * lq;
 #pragma unroll
@@ -753,7 +758,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
         // in flight measured slower, also without spills)
         for (uint32_t tr = 0; tr < nrows; tr += kMfRows) {
             __syncthreads();  // the previous tile is read
-            store_tile();
+            store_tile(tr);
             if (tr + kMfRows < nrows) load_tile(tr + kMfRows);
             if (has_new && prow - tr < (uint32_t)kMfRows) {
                 // the row at pos, from its values as stored (its codes in memory
