@@ -223,6 +223,217 @@ Q35_DEV void lm_append_group(const float v[16], const float* levels, const float
     }
 }
 
+// Matrix-core tiles of a KV cache (head dimension 128 or 256; the attention
+// kernels use them for the quantised formats): kMfRows rows of one kv head loaded by the decoders (thread
+// t < 16 D/16, 4 rows of one group of 16 each: data and scale of K and of V)
+// into registers, then decoded into LDS as f16: K row-major (KTS halves per
+// row), V in quads of rows (element 16 i + e of a row at slot (D/16) e + i of
+// its quad, position row % 4), so a quad's 4 values of one element form one
+// 8-byte word and the decoders' stores spread over the banks.
+typedef _Float16 tile_h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 tile_h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 tile_h2 __attribute__((ext_vector_type(2)));
+
+template <int D, int F>
+struct KvTile {
+    static constexpr bool T8 = F == Q35_KV_TURBO8;
+    static constexpr int LMB = lm_bits(F);
+    static constexpr bool LMK = lm_k(F), LMV = LMB > 0;
+    static constexpr int NG = D / 16;              // scale groups of 16 per row
+    static constexpr int ND = 16 * NG;             // decoder threads
+    static constexpr int KTS = D + 8;              // f16 per K row in LDS (8 of padding)
+    static constexpr int VQS = 4 * (D + 16);       // f16 per quad of V rows (16 slots of padding)
+    static constexpr int KT_HALVES = kMfRows * KTS, VT_HALVES = kMfRows / 4 * VQS;
+    // bits per element of K and V data, bytes per group scale
+    static constexpr uint32_t KBITS = T8 ? 8u : LMK ? (uint32_t)LMB : 16u;
+    static constexpr uint32_t VBITS = T8 ? 8u : LMV ? (uint32_t)LMB : 16u;
+    // words of data per row and group (E4M3 codes: 4; 4- and 3-bit indices: 2,
+    // the 3-bit group's 6 bytes from the word boundary below them; 2-bit: 1;
+    // bf16 keys: 8)
+    static constexpr int KW = T8 ? 4 : LMK ? (LMB == 2 ? 1 : 2) : 8;
+    static constexpr int VW = T8 ? 4 : LMV ? (LMB == 2 ? 1 : 2) : 8;
+    // Lloyd-Max formats: the levels as f16, by pairs (4-bit: one index byte,
+    // 256 pairs; 3-bit: 6 index bits, 64 pairs) or by fours (2-bit: one index
+    // byte, 256 entries of two words); the first element in the low half
+    static constexpr int PTW = LMV ? (LMB == 2 ? 512 : LMB == 4 ? 256 : 64) : 1;
+
+    __amdgpu_buffer_rsrc_t rk, rv, rks, rvs;     // the sides from the first row of the range
+    uint32_t krow, vrow, ksrow, vsrow;           // bytes per cache row of each side
+    int gi, rq;                                  // decoder: group gi of the tile's rows 4 rq .. 4 rq + 3
+    bool dec;
+    uint32_t lsh;                                // 3-bit groups: bits below the group in its first word
+    uint32_t kc4[4][KW], vc4[4][VW], ks4[4], vs4[4];
+
+    Q35_DEV void init(int t, __amdgpu_buffer_rsrc_t k_, __amdgpu_buffer_rsrc_t v_, __amdgpu_buffer_rsrc_t ks_,
+                      __amdgpu_buffer_rsrc_t vs_, uint32_t hkv) {
+        rk = k_, rv = v_, rks = ks_, rvs = vs_;
+        krow = hkv * D * KBITS / 8u;
+        vrow = hkv * D * VBITS / 8u;
+        ksrow = hkv * (uint32_t)NG * (T8 ? 2u : LMK ? 1u : 0u);
+        vsrow = hkv * (uint32_t)NG * (T8 ? 2u : LMV ? 1u : 0u);
+        gi = t % NG;
+        rq = t / NG;
+        dec = ND == kNT || t < ND;
+        lsh = 8u * ((uint32_t)LMB * 2u * (uint32_t)gi & 3u);
+    }
+
+    template <int N>
+    static Q35_DEV void load_words(__amdgpu_buffer_rsrc_t rr, uint32_t off, uint32_t* w) {
+        if constexpr (N == 8) {
+            const uint4 a0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, kAuxStream));
+            const uint4 a1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, off + 16u, 0, kAuxStream));
+            w[0] = a0.x, w[1] = a0.y, w[2] = a0.z, w[3] = a0.w, w[4] = a1.x, w[5] = a1.y, w[6] = a1.z, w[7] = a1.w;
+        } else if constexpr (N == 4) {
+            const uint4 a0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, kAuxStream));
+            w[0] = a0.x, w[1] = a0.y, w[2] = a0.z, w[3] = a0.w;
+        } else if constexpr (N == 2) {
+            const uint2 a0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, kAuxStream));
+            w[0] = a0.x, w[1] = a0.y;
+        } else {
+            w[0] = __builtin_amdgcn_raw_buffer_load_b32(rr, off, 0, kAuxStream);
+        }
+    }
+
+    // the rows tr .. tr + kMfRows - 1 of the range into registers (rows past
+    // the range read zero)
+    Q35_DEV void load(uint32_t tr) {
+        if (!dec) return;
+        const uint32_t kg = (KBITS * 2u * (uint32_t)gi) & ~3u, vg = (VBITS * 2u * (uint32_t)gi) & ~3u;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t r = tr + 4u * rq + u;
+            load_words<KW>(rk, r * krow + kg, kc4[u]);
+            if constexpr (T8) ks4[u] = __builtin_amdgcn_raw_buffer_load_b16(rks, r * ksrow + 2u * gi, 0, kAuxStream);
+            else if constexpr (LMK) ks4[u] = __builtin_amdgcn_raw_buffer_load_b8(rks, r * ksrow + gi, 0, kAuxStream);
+            else ks4[u] = 0;
+            load_words<VW>(rv, r * vrow + vg, vc4[u]);
+            if constexpr (T8) vs4[u] = __builtin_amdgcn_raw_buffer_load_b16(rvs, r * vsrow + 2u * gi, 0, kAuxStream);
+            else if constexpr (LMV) vs4[u] = __builtin_amdgcn_raw_buffer_load_b8(rvs, r * vsrow + gi, 0, kAuxStream);
+            else vs4[u] = 0;
+        }
+    }
+
+    static Q35_DEV void fill_ptab(uint32_t* ptab, const float* levels, int t) {
+        if constexpr (LMV) {
+            auto lv16 = [&](uint32_t i) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)levels[i]); };
+            if constexpr (LMB == 4) {
+                ptab[t] = lv16(t & 15u) | (lv16((uint32_t)t >> 4) << 16);
+            } else if constexpr (LMB == 3) {
+                if (t < 64) ptab[t] = lv16(t & 7u) | (lv16((uint32_t)t >> 3) << 16);
+            } else {
+                ptab[2 * t] = lv16(t & 3u) | (lv16((t >> 2) & 3u) << 16);
+                ptab[2 * t + 1] = lv16((t >> 4) & 3u) | (lv16((uint32_t)t >> 6) << 16);
+            }
+        }
+    }
+
+    // elements 4 c .. 4 c + 3 of a row's group of 16: E4M3 codes times the
+    // bf16 group scale, or bf16 keys as they are
+    template <int NW>
+    static Q35_DEV void dec4(const uint32_t* w, uint32_t sbits, int c, float f[4]) {
+        if constexpr (NW == 8) {
+            f[0] = bf16_lo(w[2 * c]);
+            f[1] = bf16_hi(w[2 * c]);
+            f[2] = bf16_lo(w[2 * c + 1]);
+            f[3] = bf16_hi(w[2 * c + 1]);
+        } else {
+            const float sc = bf16_to_f32(sbits & 0xFFFFu);
+            const q35_float2_t p0 = e4m3x2_to_f32<false>(w[c]), p1 = e4m3x2_to_f32<true>(w[c]);
+            f[0] = p0.x * sc;
+            f[1] = p0.y * sc;
+            f[2] = p1.x * sc;
+            f[3] = p1.y * sc;
+        }
+    }
+
+    // a row's group of 16 in a Lloyd-Max format as 8 f16 pairs (elements
+    // 2 p, 2 p + 1 in word p): levels from the pair table times the E4M3 group
+    // scale, in packed f16 (the level and the product each rounded to f16)
+    Q35_DEV void dec_lm(const uint32_t* w, uint32_t sbyte, const uint32_t* ptab, uint32_t o[8]) const {
+        const _Float16 sh = (_Float16)e4m3x2_to_f32<false>(sbyte & 0xFFu).x;  // exact: E4M3 is a subset of f16
+        const tile_h2 s2 = {sh, sh};
+        auto scaled = [&](uint32_t x) { return __builtin_bit_cast(uint32_t, __builtin_bit_cast(tile_h2, x) * s2); };
+        if constexpr (LMB == 4) {
+#pragma unroll
+            for (int p = 0; p < 8; ++p) o[p] = scaled(ptab[(w[p / 4] >> (8 * (p % 4))) & 0xFFu]);
+        } else if constexpr (LMB == 2) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint2 v = reinterpret_cast<const uint2*>(ptab)[(w[0] >> (8 * k)) & 0xFFu];
+                o[2 * k] = scaled(v.x);
+                o[2 * k + 1] = scaled(v.y);
+            }
+        } else {
+            const uint64_t bits = (((uint64_t)w[1] << 32) | w[0]) >> lsh;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) o[p] = scaled(ptab[(uint32_t)(bits >> (6 * p)) & 0x3Fu]);
+        }
+    }
+
+    // The loaded rows into the LDS tiles.  Rows past the range (nrows): the
+    // first tile decodes them (their loads read zero); a later tile leaves a
+    // decoder's 4 rows as the previous tile left them when all 4 are past the
+    // range (finite values, which the callers mask out of the scores and give
+    // weight 0).
+    Q35_DEV void store(uint32_t tr, uint32_t nrows, _Float16* kt, _Float16* vt, const uint32_t* ptab) const {
+        if (!dec || (tr > 0 && tr + 4u * rq >= nrows)) return;
+        // K: row by row, 16 elements as two 16-byte stores
+        if constexpr (LMK) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                uint32_t o[8];
+                dec_lm(kc4[u], ks4[u], ptab, o);
+                _Float16* kd = kt + (4 * rq + u) * KTS + 16 * gi;
+                *reinterpret_cast<uint4*>(kd) = make_uint4(o[0], o[1], o[2], o[3]);
+                *reinterpret_cast<uint4*>(kd + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float kf[16];
+#pragma unroll
+                for (int w4 = 0; w4 < 4; ++w4) dec4<KW>(kc4[u], ks4[u], w4, kf + 4 * w4);
+                tile_h8 k0, k1;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    k0[e] = (_Float16)kf[e];
+                    k1[e] = (_Float16)kf[8 + e];
+                }
+                _Float16* kd = kt + (4 * rq + u) * KTS + 16 * gi;
+                *reinterpret_cast<tile_h8*>(kd) = k0;
+                *reinterpret_cast<tile_h8*>(kd + 8) = k1;
+            }
+        }
+        // V: one 8-byte store per element (its 4 rows)
+        if constexpr (LMV) {
+            uint32_t o[4][8];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) dec_lm(vc4[u], vs4[u], ptab, o[u]);
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                // low halves: element 2 p of rows 0..3; high halves: element 2 p + 1
+                const uint2 lo = make_uint2(__builtin_amdgcn_perm(o[1][p], o[0][p], 0x05040100u),
+                                            __builtin_amdgcn_perm(o[3][p], o[2][p], 0x05040100u));
+                const uint2 hi = make_uint2(__builtin_amdgcn_perm(o[1][p], o[0][p], 0x07060302u),
+                                            __builtin_amdgcn_perm(o[3][p], o[2][p], 0x07060302u));
+                *reinterpret_cast<uint2*>(vt + rq * VQS + (NG * (2 * p) + gi) * 4) = lo;
+                *reinterpret_cast<uint2*>(vt + rq * VQS + (NG * (2 * p + 1) + gi) * 4) = hi;
+            }
+        } else {
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4) {
+                float vf[4][4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) dec4<VW>(vc4[u], vs4[u], w4, vf[u]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    *reinterpret_cast<tile_h4*>(vt + rq * VQS + (NG * (4 * w4 + e) + gi) * 4) =
+                        tile_h4{(_Float16)vf[0][e], (_Float16)vf[1][e], (_Float16)vf[2][e], (_Float16)vf[3][e]};
+            }
+        }
+    }
+};
+
 // T8: Turbo8 cache (E4M3 codes [capacity, Hkv, D] with bf16 scales per 16
 // [capacity, Hkv, D/16], in the orthonormal Walsh-Hadamard basis of a head).
 // The prologue also rotates the G query heads and the new k and v, the block
@@ -282,11 +493,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
     __shared__ __align__(16) _Float16 kt_s[MF ? kMfRows * KTS : 1];
     __shared__ __align__(16) _Float16 vt_s[MF ? kMfRows / 4 * VQS : 1];
     __shared__ float lut[LMV ? 16 : 1];     // Lloyd-Max formats: the codebook levels
-    // MF, Lloyd-Max formats: the levels as f16, by pairs (4-bit: one index
-    // byte, 256 pairs; 3-bit: 6 index bits, 64 pairs) or by fours (2-bit: one
-    // index byte, 256 entries of two words); the first element in the low half
-    constexpr int PTW = (MF && LMV) ? (LMB == 2 ? 512 : LMB == 4 ? 256 : 64) : 1;
-    __shared__ __align__(8) uint32_t ptab[PTW];
+    __shared__ __align__(8) uint32_t ptab[MF ? KvTile<D, F>::PTW : 1];  // MF, Lloyd-Max formats: the level pair table
     __shared__ float bmax[G];               // sparse-V gate: running max of each head over the block
 
     const int32_t pos = attn_pos(a);
@@ -382,51 +589,11 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
             }
         }
     };
-    // MF: the decoders (thread t < 16 NG) each read 4 rows of one group of 16
-    // (data and scale) of K and of V per tile: KW / VW words of data per row
-    // (E4M3 codes: 4; 4- and 3-bit indices: 2, the 3-bit group's 6 bytes from
-    // the word boundary below them; 2-bit: 1; bf16 keys: 8)
-    constexpr int ND = 16 * NG;
-    const bool dec = ND == kNT || t < ND;
-    const int gi = t % NG, rq = t / NG;  // decoder: group gi of the tile's rows 4 rq .. 4 rq + 3
-    constexpr int KW = T8 ? 4 : LMK ? (LMB == 2 ? 1 : 2) : 8;
-    constexpr int VW = T8 ? 4 : (LMB == 2 ? 1 : 2);
-    uint32_t kc4[4][KW], vc4[4][VW];
-    uint32_t ks4[4], vs4[4];
-    // byte offset of a row's group of 16 in its side (data of BITS bits per element)
-    auto grp_off = [&](uint32_t bits) { return (bits * 2u * (uint32_t)gi) & ~3u; };
-    auto load_words = [&](__amdgpu_buffer_rsrc_t rr, uint32_t off, uint32_t* w, auto nw) {
-        constexpr int N = decltype(nw)::value;
-        if constexpr (N == 8) {
-            const uint4 a0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, kAuxStream));
-            const uint4 a1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, off + 16u, 0, kAuxStream));
-            w[0] = a0.x, w[1] = a0.y, w[2] = a0.z, w[3] = a0.w, w[4] = a1.x, w[5] = a1.y, w[6] = a1.z, w[7] = a1.w;
-        } else if constexpr (N == 4) {
-            const uint4 a0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, kAuxStream));
-            w[0] = a0.x, w[1] = a0.y, w[2] = a0.z, w[3] = a0.w;
-        } else if constexpr (N == 2) {
-            const uint2 a0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, kAuxStream));
-            w[0] = a0.x, w[1] = a0.y;
-        } else {
-            w[0] = __builtin_amdgcn_raw_buffer_load_b32(rr, off, 0, kAuxStream);
-        }
-    };
-    auto load_tile = [&](uint32_t tr) {  // tr: chunk-relative first row; rows past the chunk read zero
-        if (!dec) return;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t r = tr + 4u * rq + u;
-            load_words(rk, r * krow_bytes + grp_off(KBITS), kc4[u], std::integral_constant<int, KW>{});
-            if constexpr (T8) ks4[u] = __builtin_amdgcn_raw_buffer_load_b16(rks, r * ksrow_bytes + 2u * gi, 0, kAuxStream);
-            else if constexpr (LMK) ks4[u] = __builtin_amdgcn_raw_buffer_load_b8(rks, r * ksrow_bytes + gi, 0, kAuxStream);
-            else ks4[u] = 0;
-            load_words(rv, r * vrow_bytes + grp_off(VBITS), vc4[u], std::integral_constant<int, VW>{});
-            if constexpr (T8) vs4[u] = __builtin_amdgcn_raw_buffer_load_b16(rvs, r * vsrow_bytes + 2u * gi, 0, kAuxStream);
-            else vs4[u] = __builtin_amdgcn_raw_buffer_load_b8(rvs, r * vsrow_bytes + gi, 0, kAuxStream);
-        }
-    };
+    // MF: the tile loader; the first tile's loads go out now
+    [[maybe_unused]] KvTile<D, F> tio;
     if constexpr (MF) {
-        load_tile(0);
+        tio.init(t, rk, rv, rks, rvs, a.hkv);
+        tio.load(0);
     } else {
         load_batch(kr[0], vr[0], ksr[0], vsr[0], t0);
         load_batch(kr[1], vr[1], ksr[1], vsr[1], t0 + B);  // loads past the chunk return zero, unused
@@ -439,17 +606,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
     if (t < D) vn[t] = ROTV ? vnew : bf16_to_f32(f32_to_bf16(vnew));
     if constexpr (LMV)
         if (t < 16) lut[t] = a.lm_levels[t];
-    if constexpr (MF && LMV) {
-        auto lv16 = [&](uint32_t i) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a.lm_levels[i]); };
-        if constexpr (LMB == 4) {
-            ptab[t] = lv16(t & 15u) | (lv16((uint32_t)t >> 4) << 16);
-        } else if constexpr (LMB == 3) {
-            if (t < 64) ptab[t] = lv16(t & 7u) | (lv16((uint32_t)t >> 3) << 16);
-        } else {
-            ptab[2 * t] = lv16(t & 3u) | (lv16((t >> 2) & 3u) << 16);
-            ptab[2 * t + 1] = lv16((t >> 4) & 3u) | (lv16((uint32_t)t >> 6) << 16);
-        }
-    }
+    if constexpr (MF && LMV) KvTile<D, F>::fill_ptab(ptab, a.lm_levels, t);
     if (t < G) bmax[t] = -INFINITY;
     if (t < (int)a.rotary / 2) {
         float sn, cs;
@@ -582,7 +739,6 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
         // and accumulators of heads 4 (L/16) + i, V slot 16 dt + L % 16.
         typedef _Float16 h8 __attribute__((ext_vector_type(8)));
         typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
         typedef float f4 __attribute__((ext_vector_type(4)));
         const int hq = lane & 15, lq = lane >> 4;
         // the B operands of the scores: q of head hq (columns h >= G repeat
@@ -599,109 +755,6 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
         f4 O[D / 16];
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) O[dt] = f4{0.f, 0.f, 0.f, 0.f};
-
-        // elements 4 c .. 4 c + 3 of a row's group of 16, decoded: E4M3 codes
-        // times the bf16 group scale, or bf16 keys as they are
-        const uint32_t lsh = 8u * ((uint32_t)LMB * 2u * gi & 3u);  // 3-bit groups: bits below the group
-        auto dec4 = [&](const uint32_t* w, uint32_t sbits, int c, auto nwc, float f[4]) {
-            constexpr int nw = decltype(nwc)::value;
-            if constexpr (nw == 8) {  // bf16
-                f[0] = bf16_lo(w[2 * c]);
-                f[1] = bf16_hi(w[2 * c]);
-                f[2] = bf16_lo(w[2 * c + 1]);
-                f[3] = bf16_hi(w[2 * c + 1]);
-            } else {  // Turbo8
-                const float sc = bf16_to_f32(sbits & 0xFFFFu);
-                const q35_float2_t p0 = e4m3x2_to_f32<false>(w[c]), p1 = e4m3x2_to_f32<true>(w[c]);
-                f[0] = p0.x * sc;
-                f[1] = p0.y * sc;
-                f[2] = p1.x * sc;
-                f[3] = p1.y * sc;
-            }
-        };
-        // a row's group of 16 in a Lloyd-Max format as 8 f16 pairs (elements
-        // 2 p, 2 p + 1 in word p): levels from the pair table times the E4M3
-        // group scale, in packed f16 (the level and the product each rounded
-        // to f16)
-        auto dec_lm = [&](const uint32_t* w, uint32_t sbyte, uint32_t o[8]) {
-            const _Float16 sh = (_Float16)e4m3x2_to_f32<false>(sbyte & 0xFFu).x;  // exact: E4M3 is a subset of f16
-            const h2 s2 = {sh, sh};
-            auto scaled = [&](uint32_t x) { return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, x) * s2); };
-            if constexpr (LMB == 4) {
-#pragma unroll
-                for (int p = 0; p < 8; ++p) o[p] = scaled(ptab[(w[p / 4] >> (8 * (p % 4))) & 0xFFu]);
-            } else if constexpr (LMB == 2) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint2 v = reinterpret_cast<const uint2*>(ptab)[(w[0] >> (8 * k)) & 0xFFu];
-                    o[2 * k] = scaled(v.x);
-                    o[2 * k + 1] = scaled(v.y);
-                }
-            } else {
-                const uint64_t bits = (((uint64_t)w[1] << 32) | w[0]) >> lsh;
-#pragma unroll
-                for (int p = 0; p < 8; ++p) o[p] = scaled(ptab[(uint32_t)(bits >> (6 * p)) & 0x3Fu]);
-            }
-        };
-        // Rows past the chunk: the first tile decodes them (their loads read
-        // zero); a later tile leaves a decoder's 4 rows as the previous tile
-        // left them when all 4 are past the chunk (finite values, masked out
-        // of the scores and given weight 0)
-        auto store_tile = [&](uint32_t tr) {
-            if (!dec || (tr > 0 && tr + 4u * rq >= nrows)) return;
-            // K: row by row, 16 elements as two 16-byte stores
-            if constexpr (LMK) {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    uint32_t o[8];
-                    dec_lm(kc4[u], ks4[u], o);
-                    _Float16* kd = kt_s + (4 * rq + u) * KTS + 16 * gi;
-                    *reinterpret_cast<uint4*>(kd) = make_uint4(o[0], o[1], o[2], o[3]);
-                    *reinterpret_cast<uint4*>(kd + 8) = make_uint4(o[4], o[5], o[6], o[7]);
-                }
-            } else
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                float kf[16];
-#pragma unroll
-                for (int w4 = 0; w4 < 4; ++w4) dec4(kc4[u], ks4[u], w4, std::integral_constant<int, KW>{}, kf + 4 * w4);
-                h8 k0, k1;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    k0[e] = (_Float16)kf[e];
-                    k1[e] = (_Float16)kf[8 + e];
-                }
-                _Float16* kd = kt_s + (4 * rq + u) * KTS + 16 * gi;
-                *reinterpret_cast<h8*>(kd) = k0;
-                *reinterpret_cast<h8*>(kd + 8) = k1;
-            }
-            // V: one 8-byte store per element (its 4 rows)
-            if constexpr (LMV) {
-                uint32_t o[4][8];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) dec_lm(vc4[u], vs4[u], o[u]);
-#pragma unroll
-                for (int p = 0; p < 8; ++p) {
-                    // low halves: element 2 p of rows 0..3; high halves: element 2 p + 1
-                    const uint2 lo = make_uint2(__builtin_amdgcn_perm(o[1][p], o[0][p], 0x05040100u),
-                                                __builtin_amdgcn_perm(o[3][p], o[2][p], 0x05040100u));
-                    const uint2 hi = make_uint2(__builtin_amdgcn_perm(o[1][p], o[0][p], 0x07060302u),
-                                                __builtin_amdgcn_perm(o[3][p], o[2][p], 0x07060302u));
-                    *reinterpret_cast<uint2*>(vt_s + rq * VQS + (NG * (2 * p) + gi) * 4) = lo;
-                    *reinterpret_cast<uint2*>(vt_s + rq * VQS + (NG * (2 * p + 1) + gi) * 4) = hi;
-                }
-            } else
-#pragma unroll
-            for (int w4 = 0; w4 < 4; ++w4) {
-                float vf[4][4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) dec4(vc4[u], vs4[u], w4, std::integral_constant<int, VW>{}, vf[u]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    *reinterpret_cast<h4*>(vt_s + rq * VQS + (NG * (4 * w4 + e) + gi) * 4) =
-                        h4{(_Float16)vf[0][e], (_Float16)vf[1][e], (_Float16)vf[2][e], (_Float16)vf[3][e]};
-            }
-        };
 
         auto compute_tile = [&](uint32_t tr) {
             if (tr + 16u * wid >= nrows) return;  // none of the wave's rows is in the chunk
@@ -758,8 +811,8 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void a
         // in flight measured slower, also without spills)
         for (uint32_t tr = 0; tr < nrows; tr += kMfRows) {
             __syncthreads();  // the previous tile is read
-            store_tile(tr);
-            if (tr + kMfRows < nrows) load_tile(tr + kMfRows);
+            tio.store(tr, nrows, kt_s, vt_s, ptab);
+            if (tr + kMfRows < nrows) tio.load(tr + kMfRows);
             if (has_new && prow - tr < (uint32_t)kMfRows) {
                 // the row at pos, from its values as stored (its codes in memory
                 // are being written by this block)
@@ -1247,6 +1300,262 @@ hipError_t launch_t(const AttnArgs& a, uint32_t grid_chunks, uint32_t fmt, hipSt
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Prompt into a quantised cache (head dimension 128 or 256), two launches in
+// place of the decode steps of every prompt token: each token's row is
+// appended as the decode step would append it, then every token attends to the
+// rows [0, its position] as stored, so each sees the earlier prompt rows
+// quantised, as in token order.
+//
+// pfq_prep_kernel   grid (token, kv head g), 256 threads: the decode step's
+//     prologue for one token: RMSNorm and RoPE of the G query heads and the
+//     key, the Walsh-Hadamard rotation (query and key for the formats with
+//     rotated keys, the value always), the query heads as f16 into qh, the row
+//     quantised in groups of 16 into the cache (bf16 keys stored as bf16).
+template <int D, int G, int F>
+__global__ __launch_bounds__(kNT) void pfq_prep_kernel(PfQuantAttnArgs a) {
+    constexpr bool T8 = F == Q35_KV_TURBO8;
+    constexpr int LMB = lm_bits(F);
+    constexpr bool ROTQK = T8 || lm_k(F);
+    static_assert(T8 || LMB > 0, "quantised value rows");
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const uint32_t tok = blockIdx.x, g = blockIdx.y;
+    const uint32_t pos = a.cache_pos + tok;
+    __shared__ float qs[(G + 1) * D];  // q heads of the group, then the key
+    __shared__ float vn[D];
+    __shared__ float rsq[G + 1];
+    __shared__ float2 rot[D / 2];
+    __shared__ float lut[16];
+    const float* qf = a.q_full + (size_t)tok * a.hq * 2u * D;
+    const float* kf = a.k + (size_t)tok * a.hkv * D;
+    const float* vf = a.v + (size_t)tok * a.hkv * D;
+    for (int e = t; e < (G + 1) * D; e += kNT) {
+        const int i = e / D, d = e % D;
+        qs[e] = i < G ? qf[(size_t)(g * G + i) * 2 * D + d] : kf[g * D + d];
+    }
+    for (int d = t; d < D; d += kNT) vn[d] = vf[g * D + d];
+    if constexpr (LMB > 0)
+        if (t < 16) lut[t] = a.lm_levels[t];
+    if (t < (int)a.rotary / 2) {
+        float sn, cs;
+        sincosf((float)pos * a.inv_freq[t], &sn, &cs);
+        rot[t] = make_float2(cs, sn);
+    }
+    __syncthreads();
+    for (int i = wid; i < G + 1; i += kNT / 64) {
+        float ss = 0.f;
+        for (int d = lane; d < D; d += 64) ss = fmaf(qs[i * D + d], qs[i * D + d], ss);
+        ss = wave_sum(ss);
+        if (lane == 0) rsq[i] = 1.0f / sqrtf(ss / (float)D + a.eps);
+    }
+    __syncthreads();
+    for (int e = t; e < (G + 1) * D; e += kNT) {
+        const int i = e / D, d = e % D;
+        qs[e] = qs[e] * rsq[i] * bf16_to_f32(i < G ? a.q_norm[d] : a.k_norm[d]);
+    }
+    __syncthreads();
+    const int half = (int)a.rotary / 2;
+    for (int e = t; e < (G + 1) * half; e += kNT) {
+        const int i = e / half, d = e % half;
+        const float cs = rot[d].x, sn = rot[d].y;
+        const float x1 = qs[i * D + d], x2 = qs[i * D + d + half];
+        qs[i * D + d] = x1 * cs - x2 * sn;
+        qs[i * D + d + half] = x2 * cs + x1 * sn;
+    }
+    __syncthreads();
+    // rotations, one vector per wave: the G query heads and the key (rotated
+    // keys only), then the value
+    for (int vi = (ROTQK ? 0 : G + 1) + wid; vi < G + 2; vi += kNT / 64) {
+        float* xv = vi <= G ? qs + vi * D : vn;
+        float x[D / 64];
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) x[i] = xv[lane * (D / 64) + i];
+        wht_regs<D>(x, lane);
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) xv[lane * (D / 64) + i] = x[i];
+    }
+    __syncthreads();
+    for (int e = t; e < G * D; e += kNT)
+        a.qh[((size_t)tok * a.hq + (size_t)g * G) * D + e] = __builtin_bit_cast(uint16_t, (_Float16)qs[e]);
+    const size_t gi0 = ((size_t)pos * a.hkv + g) * (D / 16);  // group index of the row in the cache
+    if constexpr (!ROTQK)
+        if (t < D) static_cast<uint16_t*>(a.kc)[((size_t)pos * a.hkv + g) * D + t] = (uint16_t)f32_to_bf16(qs[G * D + t]);
+    constexpr int SIDES = ROTQK ? 2 : 1;  // groups of the key (rotated formats), then of the value
+    if (t < SIDES * (D / 16)) {
+        const int side = SIDES == 2 ? t / (D / 16) : 1, grp = t % (D / 16);
+        const float* src = (side ? vn : qs + G * D) + 16 * grp;
+        float v16[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v16[e] = src[e];
+        if constexpr (T8) {
+            uint32_t cw[4];
+            const uint32_t sb = turbo8_quantize16(v16, cw);
+            uint8_t* dst = static_cast<uint8_t*>(side ? a.vc : a.kc) + (gi0 + grp) * 16;
+            *reinterpret_cast<uint4*>(dst) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+            static_cast<uint16_t*>(side ? a.vs : a.ks)[gi0 + grp] = (uint16_t)sb;
+        } else {
+            float out16[16];
+            lm_append_group<LMB>(v16, a.lm_levels, lut, static_cast<uint8_t*>(side ? a.vc : a.kc),
+                                 static_cast<uint8_t*>(side ? a.vs : a.ks), gi0 + grp, out16);
+        }
+    }
+}
+
+// pfq_flash_kernel   grid (block of 64/G prompt tokens, kv head g), 256
+//     threads: causal attention of the block's tokens over the cache rows as
+//     stored, in the matrix-core tiles of the decode kernel (KvTile): each
+//     64-row tile is decoded once for all the block's tokens.  Wave w owns
+//     the 16 (token, head) columns 16 w .. 16 w + 15 (token 16 w / G + c / G,
+//     head c % G) across all tiles: scores S^T (16 rows x 16 columns) as
+//     16x16x32 f16 MFMAs of K rows against the f16 query heads, an online
+//     softmax per column (lazy rescale by 8 in base 2, the sparse-V gate
+//     against the column's exact running maximum), p V as 16x16x16 MFMAs with
+//     p in registers.  Then each column is divided by its sum, rotated back
+//     and multiplied by the sigmoid of its gate into ga (f16).  Blocks of the
+//     last tokens (the most rows) start first.
+template <int D, int G, int F>
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void pfq_flash_kernel(PfQuantAttnArgs a) {
+    using Tile = KvTile<D, F>;
+    constexpr int QB = 64 / G;  // prompt tokens per block
+    constexpr int NG = D / 16, KTS = Tile::KTS, VQS = Tile::VQS;
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int hq = lane & 15, lq = lane >> 4;
+    const uint32_t g = blockIdx.y;
+    const uint32_t tq0 = (gridDim.x - 1 - blockIdx.x) * QB;
+    const uint32_t tq1 = min(tq0 + (uint32_t)QB, a.T);
+    const uint32_t kend = a.cache_pos + tq1;  // rows [0, kend) are visible to some token of the block
+
+    // the K tile, then the V tile; after the loop the per-wave outputs
+    __shared__ __align__(16) _Float16 tiles[Tile::KT_HALVES + Tile::VT_HALVES];
+    __shared__ __align__(8) uint32_t ptab[Tile::PTW];
+    _Float16* kt_s = tiles;
+    _Float16* vt_s = tiles + Tile::KT_HALVES;
+
+    const size_t e0 = (size_t)g * D;  // element offset of head g in a cache row
+    Tile tio;
+    constexpr uint32_t SB = Tile::T8 ? 2u : 1u;  // bytes per group scale
+    const auto rks = Tile::T8 || Tile::LMK
+                         ? rsrc(static_cast<const uint8_t*>(a.ks) + (size_t)g * NG * SB, kend * a.hkv * NG * SB)
+                         : rsrc(a.vs, 0u);  // bf16 keys: no key scales, never read
+    tio.init(t, rsrc(static_cast<const uint8_t*>(a.kc) + e0 * Tile::KBITS / 8, kend * (a.hkv * D * Tile::KBITS / 8u)),
+             rsrc(static_cast<const uint8_t*>(a.vc) + e0 * Tile::VBITS / 8, kend * (a.hkv * D * Tile::VBITS / 8u)), rks,
+             rsrc(static_cast<const uint8_t*>(a.vs) + (size_t)g * NG * SB, kend * a.hkv * NG * SB), a.hkv);
+    tio.load(0);
+    if constexpr (Tile::LMV) Tile::fill_ptab(ptab, a.lm_levels, t);
+
+    // this lane's column: prompt token tok, head hh of the group
+    const int col = 16 * wid + hq;
+    const uint32_t tok = tq0 + (uint32_t)(col / G);
+    const int hh = col % G;
+    const bool live = tok < a.T;
+    const uint32_t last = a.cache_pos + (live ? tok : tq1 - 1);  // the column's last visible row
+    h8 qb[D / 32];
+    {
+        const uint16_t* qp = a.qh + ((size_t)(live ? tok : tq0) * a.hq + (size_t)g * G + hh) * D + 8 * lq;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) qb[ks] = __builtin_bit_cast(h8, *reinterpret_cast<const uint4*>(qp + 32 * ks));
+    }
+    const float sscale = a.scale * kLog2e;
+    const float lt = a.sparse_v_log2;
+    float m = -INFINITY, l = 0.f, mrun = -INFINITY;
+    f4 O[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) O[dt] = f4{0.f, 0.f, 0.f, 0.f};
+
+    for (uint32_t tr = 0; tr < kend; tr += kMfRows) {
+        __syncthreads();  // the previous tile is read
+        tio.store(tr, kend, kt_s, vt_s, ptab);
+        if (tr + kMfRows < kend) tio.load(tr + kMfRows);
+        __syncthreads();
+        // scores of the tile's 4 sub-tiles of 16 rows (lane: rows 4 lq + i of each)
+        float s[4][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+            f4 S = {0.f, 0.f, 0.f, 0.f};
+            if (tr + 16u * sub < kend) {
+                const _Float16* ka = kt_s + (16 * sub + hq) * KTS + 8 * lq;
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks)
+                    S = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const h8*>(ka + 32 * ks), qb[ks], S, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t r = tr + 16u * sub + 4u * lq + i;
+                s[sub][i] = r <= last ? S[i] * sscale : -INFINITY;
+                mx = fmaxf(mx, s[sub][i]);
+            }
+        }
+        mx = fmaxf(mx, lane_xor<16>(mx));
+        mx = fmaxf(mx, lane_xor<32>(mx));  // the column's max over the tile
+        mrun = fmaxf(mrun, mx);
+        if (__builtin_amdgcn_ballot_w64(mx > m + 8.0f) != 0) {
+            const float mn = fmaxf(m, mx);
+            const float corr = mn == -INFINITY ? 1.0f : exp2f(m - mn);
+            m = mn;
+            l *= corr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ci = __shfl(corr, 4 * lq + i);  // column 4 lq + i lives in lane 4 lq + i
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt) O[dt][i] *= ci;
+            }
+        }
+        const float mref = m == -INFINITY ? 0.f : m;
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+            if (tr + 16u * sub >= kend) break;
+            h4 P;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = exp2f(s[sub][i] - mref);
+                l += p;
+                P[i] = (_Float16)(s[sub][i] - mrun >= lt ? p : 0.f);
+            }
+            const _Float16* vb = vt_s + (4 * sub + lq) * VQS + 4 * hq;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+                O[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(P, *reinterpret_cast<const h4*>(vb + 64 * dt), O[dt], 0, 0, 0);
+        }
+    }
+
+    // ---------------- each column divided by its sum, rotated back, gated
+    l += lane_xor<16>(l);
+    l += lane_xor<32>(l);  // column hq's sum
+    static_assert(4 * 16 * D * sizeof(float) <= sizeof(tiles), "per-wave outputs fit the tiles");
+    float* wo = reinterpret_cast<float*>(tiles) + wid * 16 * D;  // [column][D]
+    __syncthreads();  // every wave is done with the tiles
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float inv = 1.0f / __shfl(l, 4 * lq + i);  // column 4 lq + i
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            const int sl = 16 * dt + hq;
+            wo[(4 * lq + i) * D + 16 * (sl % NG) + sl / NG] = O[dt][i] * inv;
+        }
+    }
+    __syncthreads();
+    for (int c = 0; c < 16; ++c) {
+        const int cc = 16 * wid + c;
+        const uint32_t tc = tq0 + (uint32_t)(cc / G);
+        if (tc >= a.T) break;
+        const uint32_t h = g * G + (uint32_t)(cc % G);
+        float x[D / 64];
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) x[i] = wo[c * D + lane * (D / 64) + i];
+        wht_regs<D>(x, lane);
+        const float* gate = a.q_full + ((size_t)tc * a.hq + h) * 2 * D + D;
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) {
+            const int d = lane * (D / 64) + i;
+            a.ga[((size_t)tc * a.hq + h) * D + d] = __builtin_bit_cast(uint16_t, (_Float16)(x[i] * sigmoidf_(gate[d])));
+        }
+    }
+}
+
 // Turbo8 group quantiser over a plain vector (kernel-level export): one thread
 // per group of 16.
 __global__ __launch_bounds__(256) void turbo8_quantize_kernel(const float* x, uint32_t groups,
@@ -1335,6 +1644,68 @@ const void* attn_kernel_ptr(uint32_t head_dim, uint32_t group, uint32_t kv_dtype
     if (head_dim == DD && group == GG) return partial_ptr<DD, GG>(kv_dtype, tiles);
     Q35_ATTN_SHAPES(X)
 #undef X
+    return nullptr;
+}
+
+namespace {
+template <int D, int G, int F>
+void pfq_launch(const PfQuantAttnArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((pfq_prep_kernel<D, G, F>), dim3(a.T, a.hkv), dim3(kNT), 0, stream, a);
+    constexpr uint32_t QB = 64 / G;
+    hipLaunchKernelGGL((pfq_flash_kernel<D, G, F>), dim3((a.T + QB - 1) / QB, a.hkv), dim3(kNT), 0, stream, a);
+}
+#define Q35_PFQ_SHAPES(X) X(128, 1) X(128, 2) X(128, 4) X(128, 8) X(256, 1) X(256, 2) X(256, 4) X(256, 8)
+#define Q35_QUANT_FORMATS(X)                                                                       \
+    X(Q35_KV_TURBO8) X(Q35_KV_TURBO4) X(Q35_KV_TURBO3) X(Q35_KV_TURBO2) X(Q35_KV_BF16K_TURBO4V) \
+    X(Q35_KV_BF16K_TURBO3V) X(Q35_KV_BF16K_TURBO2V)
+}  // namespace
+
+bool pf_quant_attn_supported(uint32_t head_dim, uint32_t group, uint32_t kv_dtype) {
+    bool fmt = false;
+#define X(FF) fmt |= kv_dtype == FF;
+    Q35_QUANT_FORMATS(X)
+#undef X
+#define X(DD, GG) if (fmt && head_dim == DD && group == GG) return true;
+    Q35_PFQ_SHAPES(X)
+#undef X
+    return false;
+}
+
+hipError_t pf_quant_attn_launch(uint32_t head_dim, uint32_t group, uint32_t kv_dtype, const PfQuantAttnArgs& a,
+                                hipStream_t stream) {
+    if (!pf_quant_attn_supported(head_dim, group, kv_dtype)) return hipErrorInvalidValue;
+    if (a.T == 0) return hipSuccess;
+#define XF(DD, GG, FF) \
+    if (head_dim == DD && group == GG && kv_dtype == FF) pfq_launch<DD, GG, FF>(a, stream);
+#define X(DD, GG)                   \
+    XF(DD, GG, Q35_KV_TURBO8)         \
+    XF(DD, GG, Q35_KV_TURBO4)         \
+    XF(DD, GG, Q35_KV_TURBO3)         \
+    XF(DD, GG, Q35_KV_TURBO2)         \
+    XF(DD, GG, Q35_KV_BF16K_TURBO4V)  \
+    XF(DD, GG, Q35_KV_BF16K_TURBO3V)  \
+    XF(DD, GG, Q35_KV_BF16K_TURBO2V)
+    Q35_PFQ_SHAPES(X)
+#undef X
+#undef XF
+    return hipGetLastError();
+}
+
+const void* pf_quant_kernel_ptr(uint32_t head_dim, uint32_t group, uint32_t kv_dtype, bool flash) {
+#define XF(DD, GG, FF)                                                                           \
+    if (head_dim == DD && group == GG && kv_dtype == FF)                                          \
+        return flash ? (const void*)&pfq_flash_kernel<DD, GG, FF> : (const void*)&pfq_prep_kernel<DD, GG, FF>;
+#define X(DD, GG)                   \
+    XF(DD, GG, Q35_KV_TURBO8)         \
+    XF(DD, GG, Q35_KV_TURBO4)         \
+    XF(DD, GG, Q35_KV_TURBO3)         \
+    XF(DD, GG, Q35_KV_TURBO2)         \
+    XF(DD, GG, Q35_KV_BF16K_TURBO4V)  \
+    XF(DD, GG, Q35_KV_BF16K_TURBO3V)  \
+    XF(DD, GG, Q35_KV_BF16K_TURBO2V)
+    Q35_PFQ_SHAPES(X)
+#undef X
+#undef XF
     return nullptr;
 }
 

@@ -476,6 +476,10 @@ q35_status q35_kernels_resolve(int device, Qwen35Kernels** out) {
             for (uint32_t f : {Q35_KV_TURBO8, Q35_KV_TURBO4, Q35_KV_BF16K_TURBO4V})
                 probe(attn_kernel_ptr(d, g, f, true), "attention tiles");
     for (int i = 0; pf_kernel_ptr(i); ++i) probe(pf_kernel_ptr(i), "prefill");
+    for (uint32_t d : {128u, 256u})
+        for (uint32_t g : {1u, 2u, 4u, 8u})
+            for (uint32_t f : {Q35_KV_TURBO8, Q35_KV_TURBO2, Q35_KV_BF16K_TURBO4V})
+                for (bool flash : {false, true}) probe(pf_quant_kernel_ptr(d, g, f, flash), "prefill attention (quantised)");
 #define X(KK)                                                                  \
     probe(gemv_kernel_ptr(kOpInFullP, KK, false, false), "q/k/v (partial sums)"); \
     probe(gemv_kernel_ptr(kOpInFullP, KK, true, false), "q/k/v (partial sums)");
@@ -1315,11 +1319,44 @@ q35_status q35_prefill_full_attention(const Qwen35Kernels* kernels, const Qwen35
     Q35_TRY(pf_gemm(sp, "prefill q/k/v", kPfF32, xh, T, {&l.q_proj, &l.k_proj, &l.v_proj}, {qf, kf, vf}, 0, nullptr,
                     false, true, stream));
     uint16_t* ga = at_off<uint16_t>(ws, w.ga);
+    if (quant && pf_quant_attn_supported(c.head_dim, G, kv->dtype)) {
+        // A quantised cache at head dimension 128 or 256: the prompt's rows are
+        // appended as its decode steps would append them, then every token
+        // attends to the rows as stored (two launches; see pfq_flash_kernel)
+        PfQuantAttnArgs qa;
+        std::memset(&qa, 0, sizeof(qa));
+        qa.q_full = qf;
+        qa.k = kf;
+        qa.v = vf;
+        qa.q_norm = l.q_norm;
+        qa.k_norm = l.k_norm;
+        qa.inv_freq = inv_freq;
+        qa.kc = kv->k;
+        qa.vc = kv->v;
+        qa.ks = kv->k_scales;
+        qa.vs = kv->v_scales;
+        qa.qh = at_off<uint16_t>(ws, w.qb);
+        qa.ga = ga;
+        qa.T = T;
+        qa.cache_pos = cache_pos;
+        qa.hq = c.num_heads;
+        qa.hkv = c.num_kv_heads;
+        qa.rotary = c.rotary_dim;
+        qa.eps = c.rms_eps;
+        qa.scale = 1.0f / std::sqrt((float)c.head_dim);
+        qa.sparse_v_log2 = kv->sparse_v <= 0.0f ? -INFINITY : std::log2(kv->sparse_v);
+        if (kv_lm_bits(kv->dtype)) std::memcpy(qa.lm_levels, kernels->lm[kv_lm_bits(kv->dtype)].v, sizeof(qa.lm_levels));
+        Q35_HIP(pf_quant_attn_launch(c.head_dim, G, kv->dtype, qa, stream), "prefill attention (quantised cache)");
+        Q35_TRY(pf_gemm(sp, "prefill o_proj", kPfResid, ga, T, {&l.o_proj}, {at_off<float>(ws, w.r)}, c.hidden,
+                        x_in, f32, true, stream));
+        Q35_TRY(pf_mlp(sp, c, l, w, ws, T, x_out, stream));
+        return ok();
+    }
     if (quant) {
-        // A quantised cache: each prompt token runs the decode attention steps (q/k
-        // norm, RoPE, the quantising append of its row, attention over the rows as
-        // stored, sparse-V gate, sigmoid gate), in token order; the projections
-        // around them stay batched.
+        // A quantised cache at the other head dimensions: each prompt token runs
+        // the decode attention steps (q/k norm, RoPE, the quantising append of its
+        // row, attention over the rows as stored, sparse-V gate, sigmoid gate), in
+        // token order; the projections around them stay batched.
         int32_t* pos = at_off<int32_t>(ws, w.pos);
         float* gaf = at_off<float>(ws, w.gaf);
         Q35_HIP(pf_iota_launch(pos, T, (int32_t)cache_pos, stream), "prefill positions");

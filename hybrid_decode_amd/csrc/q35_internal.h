@@ -412,6 +412,31 @@ struct PfAttnArgs {
     uint32_t T, cache_pos, hq, hkv;
     float scale_log2;
 };
+// A prompt into a quantised cache (head dimension 128 or 256): the rows of
+// the T tokens appended to the cache as the decode steps would append them,
+// then a causal attention of every token over the rows as stored (sparse-V
+// gate, sigmoid gate) into ga.  Two launches; qh is f16 scratch [T, hq, D].
+struct PfQuantAttnArgs {
+    const float* q_full;       // [T, hq * 2D]: q, then the gate, per head
+    const float* k;            // [T, hkv * D]
+    const float* v;            // [T, hkv * D]
+    const uint16_t* q_norm;
+    const uint16_t* k_norm;
+    const float* inv_freq;
+    void* kc;                  // the cache sides (formats as the decode attention's)
+    void* vc;
+    void* ks;                  // key group scales (null for bf16 keys)
+    void* vs;
+    uint16_t* qh;              // f16 [T, hq, D]: the prepared query heads
+    uint16_t* ga;              // f16 [T, hq * D]: gated attention output
+    uint32_t T, cache_pos, hq, hkv, rotary;
+    float eps, scale, sparse_v_log2;
+    float lm_levels[16];       // Lloyd-Max formats: the codebook levels of the format's width
+};
+bool pf_quant_attn_supported(uint32_t head_dim, uint32_t group, uint32_t kv_dtype);
+hipError_t pf_quant_attn_launch(uint32_t head_dim, uint32_t group, uint32_t kv_dtype, const PfQuantAttnArgs& a,
+                                hipStream_t stream);
+const void* pf_quant_kernel_ptr(uint32_t head_dim, uint32_t group, uint32_t kv_dtype, bool flash);
 bool pf_attn_dims_supported(uint32_t head_dim, uint32_t group);
 hipError_t pf_attn_launch(const PfRopeArgs& r, const PfAttnArgs& a, hipStream_t s);
 // The prompt's cache positions base + i into out[n], and an fp32 -> f16 cast

@@ -540,3 +540,35 @@ def test_prefill_full_quantised_4b_after_4096_cached_rows(rt, gen, fmt):
     say(f"  {fmt}: worst token rel {r:.2e}")
     assert r < TOL_BF16
     _check_qcache(fmt, after, before, rkv, pos, T)
+
+
+@pytest.mark.parametrize("fmt,sparse", [(f, 0.0) for f in QFORMATS] + [("turbo8", None), ("turbo4", None)])
+@pytest.mark.parametrize("D", [256, 128])
+def test_prefill_full_quantised_tiles(rt, gen, fmt, sparse, D):
+    """Head dimension 128 and 256 take the batched path: the prompt's rows
+    appended as its decode steps would append them, then one causal attention
+    of every token over the rows as stored.  70 prompt tokens after 100 cached
+    rows (query blocks of 64 / G tokens, the last one ragged; key tiles of 64
+    rows, the last one ragged), the sparse-V gate off on both sides or at the
+    pages' default on both (None), against the oracle's decode loop of the
+    format: the layer outputs within the bf16 bar and the cache rows as in the
+    other quantised prompt tests."""
+    from dataclasses import replace
+    pos, T = 100, 70
+    hq, hkv = (16, 4) if D == 256 else (8, 2)
+    cfg = replace(synth.tiny("f32"), num_heads=hq, num_kv_heads=hkv, head_dim=D, rotary_dim=D // 4)
+    say(f"prefill full into {fmt} tiles D={D} pos={pos} T={T} sparse_v={sparse}")
+    layer = synth.full_layer(gen, cfg, f"pfqt.{fmt}.{D}")
+    cap = pos + T + 16
+    kv = _qcache(gen, cfg, fmt, f"pfqt.{fmt}.{D}", cap, pos)
+    x = gen.act(f"pfqt.{fmt}.{D}.x", (T, cfg.hidden), "f32")
+    before = {k: np.array(v, copy=True) for k, v in kv.items() if isinstance(v, np.ndarray)}
+    kw = {} if sparse is None else {"sparse_v": sparse}
+    out, after = _full_run(rt, cfg, layer, kv, x, pos, **kw)
+    inv = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
+    ref, rkv, _ = O.prefill.prefill_full_attention(cfg, layer, kv, inv, x, pos, fmt=fmt, **kw)
+    assert np.isfinite(out).all()
+    r = _rows_rel(out, ref)
+    say(f"  {fmt} D={D}: worst token rel {r:.2e}")
+    assert r < TOL_BF16
+    _check_qcache(fmt, after, before, rkv, pos, T)
