@@ -9,7 +9,7 @@ from one replayed HIP graph.  Prints one JSON line (rank 0).
     python bench.py [--gpus 1] [--steps 128] [--warmup 8] [--ctx 8192] [--kv FORMAT]
                     [--prefill-tokens 4096]
 
-With bf16 caches the line also carries "prefill": a prompt of --prefill-tokens
+The line also carries "prefill": a prompt of --prefill-tokens
 tokens through the same stack with the multi-token prefill calls (timed after
 the decode, it overwrites the first cache rows), and the rate of its
 dequantising GEMM against the f16 matrix-core peak.  "long_ctx" is decode at a
@@ -717,7 +717,7 @@ def main():
     first_token = w["start_token"]
 
     prefill = None
-    if args.prefill_tokens > 0 and args.kv == "bf16":
+    if args.prefill_tokens > 0:
         T = min(args.prefill_tokens, min(kv.capacity for kv in st.kvs if kv is not None))
         pf_ms = prefill_stack(torch, B, rt, st, kinds, cfg, T)
         g_us, g_flops = prefill_gemm_rate(torch, B, rt, st, cfg, T)
@@ -729,7 +729,8 @@ def main():
         prefill = {
             "tokens": T, "ms": round(pf_ms, 3), "tok_s": round(T / pf_ms * 1e3, 1),
             "workload": (f"{T}-token prompt (synthetic bf16 rows) through the {len(kinds)}-layer stack, "
-                         f"full layers at cache positions 0..{T - 1}"),
+                         f"full layers at cache positions 0..{T - 1}"
+                         + ("" if args.kv == "bf16" else f", {args.kv} KV caches")),
             "roofline": {"bound": "mfma", "kernel": "q35_prefill_gemm: pf::dequant_kernel (W to f16) + "
                                                     "pf::gemm_kernel<0, 256, W16> (f16 GEMM, "
                                                     f"{T} x {cfg.intermediate} x {cfg.hidden}), per call",
