@@ -65,9 +65,13 @@ def stack8k(rt):
     return _make_stack(rt, 8192)
 
 
+def _kv_arrays(kv):
+    return [t for t in (kv.k, kv.v, kv.k_scales, kv.v_scales) if t is not None]
+
+
 def _snapshot(st):
     return ([None if s is None else (s.conv1d_state.clone(), s.gdn_state.clone()) for s in st.states],
-            [None if kv is None else (kv.k.clone(), kv.v.clone()) for kv in st.kvs],
+            [None if kv is None else [t.clone() for t in _kv_arrays(kv)] for kv in st.kvs],
             st.positions.clone(), st.tokens.clone(), st.x_embed.clone(),
             None if st.plan is None else st.plan.layer_input(0).clone())
 
@@ -82,8 +86,8 @@ def _restore(st, snap):
             s.gdn_state.copy_(v[1])
     for kv, v in zip(st.kvs, kk):
         if kv is not None:
-            kv.k.copy_(v[0])
-            kv.v.copy_(v[1])
+            for arr, saved in zip(_kv_arrays(kv), v):
+                arr.copy_(saved)
     st.positions.copy_(p)
     st.tokens.copy_(t)
     st.x_embed.copy_(x)
@@ -126,6 +130,9 @@ def _check_one_token(rt, w, st, sample_layers):
         say(f"oracle check of layer {li} ({kinds[li]})")
         if kinds[li] == "gdn":
             ox, _, _ = O.forward_linear_attention(cfg, w["layers"][li], w["states"][li], ins[li])
+        elif "k_scales" in w["kvs"][li]:
+            from oracle import turbo8 as T8
+            ox, _, _ = T8.forward_full_attention_turbo8(cfg, w["layers"][li], w["kvs"][li], inv_h, ins[li], pos)
         else:
             ox, _, _ = O.forward_full_attention(cfg, w["layers"][li], w["kvs"][li], inv_h, ins[li], pos)
         r, e = check(O.act_to_f64(outs[li], "bf16"), ox, TOL_BF16, ELEM_BF16, 8, li)
@@ -160,7 +167,24 @@ def test_stack_4b_ctx8192_sampled_layers_logits_and_token(rt, stack8k):
 
 
 def test_stack_4b_ctx8192_graph_replay_matches_eager(rt, stack8k):
-    w, st = stack8k
+    _graph_replay_matches_eager(rt, *stack8k)
+
+
+def test_stack_4b_ctx8192_turbo8_tiles(rt):
+    """Config 4 with Turbo8 caches: at capacity 8256 the full-attention layers run
+    the matrix-core tiles (72-row chunks, the kv heads of a chunk on one XCD)
+    from the device position.  One token layer by layer against the oracle
+    (sampled GDN and full-attention layers, each fed the GPU's input; the
+    pages' default sparse-V threshold on both sides), the lm_head and the
+    token; then graph replays against eager, bit for bit."""
+    say("generating the 32-layer 4B stack with Turbo8 caches at ctx 8192")
+    w = workloads.stack_4b(synth.Gen(0), num_layers=32, ctx=8192, extra=64, kv="turbo8")
+    st = _stack_from(rt, w)
+    _check_one_token(rt, w, st, sample_layers=(3, 15, 30, 31))
+    _graph_replay_matches_eager(rt, w, st)
+
+
+def _graph_replay_matches_eager(rt, w, st):
     snap = _snapshot(st)
     steps = 6
     say("eager decode of 6 tokens")
@@ -170,7 +194,7 @@ def test_stack_4b_ctx8192_graph_replay_matches_eager(rt, stack8k):
     eager_hist = st.history.cpu().numpy()[:steps].copy()
     eager_logits = st.logits.cpu().numpy().copy()
     eager_state = st.states[0].gdn_state.cpu().numpy().copy()
-    eager_k = st.kvs[3].k.cpu().numpy().copy()
+    eager_k = [t.cpu().numpy().copy() for t in _kv_arrays(st.kvs[3])]
     assert np.all(eager_hist >= 0)
     _restore(st, snap)
     say("capturing one decode step into a HIP graph")
@@ -193,7 +217,8 @@ def test_stack_4b_ctx8192_graph_replay_matches_eager(rt, stack8k):
     assert np.array_equal(st.history.cpu().numpy()[:steps], eager_hist)
     assert np.array_equal(st.logits.cpu().numpy(), eager_logits)
     assert np.array_equal(st.states[0].gdn_state.cpu().numpy(), eager_state)
-    assert np.array_equal(st.kvs[3].k.cpu().numpy(), eager_k)
+    for arr, e in zip(_kv_arrays(st.kvs[3]), eager_k):
+        assert np.array_equal(arr.cpu().numpy(), e)
     _restore(st, snap)
 
 
