@@ -1434,16 +1434,25 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void p
     _Float16* kt_s = tiles;
     _Float16* vt_s = tiles + Tile::KT_HALVES;
 
-    const size_t e0 = (size_t)g * D;  // element offset of head g in a cache row
-    Tile tio;
+    // head g's sides from cache row 0; each tile's loads go through buffer
+    // resources based at the tile's first row (32-bit offsets within 64 rows
+    // for any cache length), over the tile's rows below kend
     constexpr uint32_t SB = Tile::T8 ? 2u : 1u;  // bytes per group scale
-    const auto rks = Tile::T8 || Tile::LMK
-                         ? rsrc(static_cast<const uint8_t*>(a.ks) + (size_t)g * NG * SB, kend * a.hkv * NG * SB)
-                         : rsrc(a.vs, 0u);  // bf16 keys: no key scales, never read
-    tio.init(t, rsrc(static_cast<const uint8_t*>(a.kc) + e0 * Tile::KBITS / 8, kend * (a.hkv * D * Tile::KBITS / 8u)),
-             rsrc(static_cast<const uint8_t*>(a.vc) + e0 * Tile::VBITS / 8, kend * (a.hkv * D * Tile::VBITS / 8u)), rks,
-             rsrc(static_cast<const uint8_t*>(a.vs) + (size_t)g * NG * SB, kend * a.hkv * NG * SB), a.hkv);
-    tio.load(0);
+    const uint8_t* kb0 = static_cast<const uint8_t*>(a.kc) + (size_t)g * D * Tile::KBITS / 8;
+    const uint8_t* vb0 = static_cast<const uint8_t*>(a.vc) + (size_t)g * D * Tile::VBITS / 8;
+    const uint8_t* ksb0 = Tile::T8 || Tile::LMK ? static_cast<const uint8_t*>(a.ks) + (size_t)g * NG * SB : nullptr;
+    const uint8_t* vsb0 = static_cast<const uint8_t*>(a.vs) + (size_t)g * NG * SB;
+    Tile tio;
+    tio.init(t, rsrc(kb0, 0u), rsrc(vb0, 0u), rsrc(vsb0, 0u), rsrc(vsb0, 0u), a.hkv);
+    auto load_from = [&](uint32_t tr) {
+        const uint32_t n = min(kend - tr, (uint32_t)kMfRows);
+        tio.rk = rsrc(kb0 + (size_t)tr * tio.krow, n * tio.krow);
+        tio.rv = rsrc(vb0 + (size_t)tr * tio.vrow, n * tio.vrow);
+        if constexpr (Tile::T8 || Tile::LMK) tio.rks = rsrc(ksb0 + (size_t)tr * tio.ksrow, n * tio.ksrow);
+        tio.rvs = rsrc(vsb0 + (size_t)tr * tio.vsrow, n * tio.vsrow);
+        tio.load(0);
+    };
+    load_from(0);
     if constexpr (Tile::LMV) Tile::fill_ptab(ptab, a.lm_levels, t);
 
     // this lane's column: prompt token tok, head hh of the group
@@ -1468,7 +1477,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void p
     for (uint32_t tr = 0; tr < kend; tr += kMfRows) {
         __syncthreads();  // the previous tile is read
         tio.store(tr, kend, kt_s, vt_s, ptab);
-        if (tr + kMfRows < kend) tio.load(tr + kMfRows);
+        if (tr + kMfRows < kend) load_from(tr + kMfRows);
         __syncthreads();
         // scores of the tile's 4 sub-tiles of 16 rows (lane: rows 4 lq + i of each)
         float s[4][4];

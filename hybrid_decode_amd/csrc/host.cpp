@@ -1300,9 +1300,11 @@ q35_status q35_prefill_full_attention(const Qwen35Kernels* kernels, const Qwen35
     PfWs w;
     Q35_TRY(pf_check_ws(c, n_tokens, workspace, workspace_bytes, &w));
     if (n_tokens == 0) return ok();
-    // a quantised cache: the per-token attention's partials use the split-GEMM area
+    // a quantised cache the batched attention does not cover: the per-token
+    // attention's partials use the split-GEMM area
+    const bool quant_batched = quant && pf_quant_attn_supported(c.head_dim, G, kv->dtype);
     const AttnWs aws = attn_ws_layout(c, kv->capacity);
-    if (quant && aws.total > kPfSplitBytes)
+    if (quant && !quant_batched && aws.total > kPfSplitBytes)
         return fail(Q35_ERR_UNSUPPORTED, "capacity %u: attention partials exceed the prefill workspace",
                     kv->capacity);
     const uint32_t T = n_tokens;
@@ -1319,7 +1321,7 @@ q35_status q35_prefill_full_attention(const Qwen35Kernels* kernels, const Qwen35
     Q35_TRY(pf_gemm(sp, "prefill q/k/v", kPfF32, xh, T, {&l.q_proj, &l.k_proj, &l.v_proj}, {qf, kf, vf}, 0, nullptr,
                     false, true, stream));
     uint16_t* ga = at_off<uint16_t>(ws, w.ga);
-    if (quant && pf_quant_attn_supported(c.head_dim, G, kv->dtype)) {
+    if (quant_batched) {
         // A quantised cache at head dimension 128 or 256: the prompt's rows are
         // appended as its decode steps would append them, then every token
         // attends to the rows as stored (two launches; see pfq_flash_kernel)

@@ -780,15 +780,17 @@ q35_status q35_prefill_linear_attention(const Qwen35Kernels* kernels,
  * page, every step of forward_full_attention per token), the KV rows
  * [cache_pos, cache_pos + n_tokens) appended in the cache's format.  bf16: one
  * causal attention launch over the prompt.  A quantised format (the Turbo
- * branches, kv->sparse_v applied): the decode attention steps run once per
- * token in token order, each appending its quantised row and attending to the
- * rows as stored, as the decode loop would; the projections and the MLP stay
- * batched.  x_in and x_out: act [n_tokens, hidden], x_out may equal x_in;
- * inv_freq as in q35_forward_full_attention.  cache_pos + n_tokens >
+ * branches, kv->sparse_v applied): the result of the decode loop, each token
+ * appending its quantised row and attending to the rows [0, its position] as
+ * stored; at head_dim 128 and 256 in two launches (every row appended, then
+ * one causal attention over the rows as stored), otherwise the decode
+ * attention steps once per token in token order.  The projections and the
+ * MLP stay batched.  x_in and x_out: act [n_tokens, hidden], x_out may equal
+ * x_in; inv_freq as in q35_forward_full_attention.  cache_pos + n_tokens >
  * kv->capacity: Q35_ERR_OUT_OF_RANGE; a head_dim / group the attention kernels
- * do not cover, or a quantised cache whose attention partials exceed the
- * workspace's split-GEMM area (capacities past about four million tokens):
- * Q35_ERR_UNSUPPORTED.  n_tokens == 0 enqueues nothing.
+ * do not cover, or (per-token path) a quantised cache whose attention partials
+ * exceed the workspace's split-GEMM area (capacities past about four million
+ * tokens): Q35_ERR_UNSUPPORTED.  n_tokens == 0 enqueues nothing.
  */
 q35_status q35_prefill_full_attention(const Qwen35Kernels* kernels, const Qwen35ForwardConfig* cfg,
                                       const FullAttentionLayer* layer, const LayerKvCache* kv,

@@ -221,8 +221,10 @@ def test_gemv_shape_errors(lib):
     assert e.value.status == B.Q35_ERR_UNSUPPORTED
 
 
-def _prefill_layers():
+def _prefill_layers(head_dim=None):
     c = B.q35_config_qwen3_5_4b()
+    if head_dim is not None:
+        c.head_dim, c.rotary_dim = head_dim, head_dim // 4
     fake = 0x100000
 
     def qw(n, k):
@@ -274,12 +276,15 @@ def test_prefill_errors_before_any_launch(lib):
     with pytest.raises(B.Q35Error) as e:
         B.q35_prefill_full_attention(FAKE_KERNELS, c, full, kv, fake, fake, 100, 29, fake, fake, ws_bytes, None)
     assert e.value.status == B.Q35_ERR_OUT_OF_RANGE
-    # a quantised cache so long that its attention partials exceed the split area
+    # a quantised cache so long that the per-token path's attention partials
+    # exceed the split area (head_dim 64: the batched path covers 128 and 256)
+    c64, full64, _, _ = _prefill_layers(head_dim=64)
     kv.dtype = B.q35_kv_dtype_from_str("turbo8")
     kv.k_scales, kv.v_scales = fake, fake
-    kv.capacity = 1 << 23
+    kv.capacity = 1 << 25  # partials of 16385 chunks: 67 MB at head_dim 64
     with pytest.raises(B.Q35Error) as e:
-        B.q35_prefill_full_attention(FAKE_KERNELS, c, full, kv, fake, fake, 10, 0, fake, fake, ws_bytes, None)
+        B.q35_prefill_full_attention(FAKE_KERNELS, c64, full64, kv, fake, fake, 10, 0, fake, fake,
+                                     B.q35_prefill_workspace_bytes(c64, 100), None)
     assert e.value.status == B.Q35_ERR_UNSUPPORTED and "capacity" in str(e.value)
     kv.capacity = 128
     # a NULL weight
