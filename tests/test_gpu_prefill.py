@@ -572,3 +572,29 @@ def test_prefill_full_quantised_tiles(rt, gen, fmt, sparse, D):
     say(f"  {fmt} D={D}: worst token rel {r:.2e}")
     assert r < TOL_BF16
     _check_qcache(fmt, after, before, rkv, pos, T)
+
+
+@pytest.mark.parametrize("fmt,D,hq,hkv", [("turbo8", 128, 16, 2), ("turbo3", 128, 16, 2),
+                                          ("turbo8", 256, 8, 4), ("turbo8", 128, 4, 4)],
+                         ids=["turbo8-d128-g8", "turbo3-d128-g8", "turbo8-d256-g2", "turbo8-d128-g1"])
+def test_prefill_full_quantised_tiles_other_groups(rt, gen, fmt, D, hq, hkv):
+    """The batched path at the other query-group sizes (64 / G prompt tokens per
+    block: 8, 32 and 64), 90 tokens after 50 cached rows, the gate at the
+    pages' default on both sides, against the oracle's decode loop."""
+    from dataclasses import replace
+    pos, T = 50, 90
+    cfg = replace(synth.tiny("f32"), num_heads=hq, num_kv_heads=hkv, head_dim=D, rotary_dim=D // 4)
+    say(f"prefill full into {fmt} tiles D={D} G={hq // hkv} pos={pos} T={T}")
+    layer = synth.full_layer(gen, cfg, f"pfqg.{fmt}.{D}.{hq}")
+    cap = pos + T + 8
+    kv = _qcache(gen, cfg, fmt, f"pfqg.{fmt}.{D}.{hq}", cap, pos)
+    x = gen.act(f"pfqg.{fmt}.{D}.{hq}.x", (T, cfg.hidden), "f32")
+    before = {k: np.array(v, copy=True) for k, v in kv.items() if isinstance(v, np.ndarray)}
+    out, after = _full_run(rt, cfg, layer, kv, x, pos)
+    inv = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
+    ref, rkv, _ = O.prefill.prefill_full_attention(cfg, layer, kv, inv, x, pos, fmt=fmt)
+    assert np.isfinite(out).all()
+    r = _rows_rel(out, ref)
+    say(f"  {fmt} D={D} G={hq // hkv}: worst token rel {r:.2e}")
+    assert r < TOL_BF16
+    _check_qcache(fmt, after, before, rkv, pos, T)
