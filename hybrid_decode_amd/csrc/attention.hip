@@ -1,4 +1,5 @@
-// Gated GQA decode attention over a bf16 KV cache (gfx950), one token.
+// Gated GQA decode attention (gfx950), one token, over a bf16 or quantised KV
+// cache; and the attention of a prompt into a quantised cache.
 //
 // Covers the middle of the pages' full-attention forward (full_attention.rs
 // page: the q/gate split, the per-head q/k RMSNorm, partial RoPE, the KV
@@ -21,10 +22,17 @@
 //       row is read once for all G heads of its group (the GQA reuse).  For
 //       the quantised formats the pages' sparse-V gate leaves out the value
 //       rows whose weight is below a threshold (see the loop).
+//       At head dimension 128 and 256 the quantised formats take the
+//       matrix-core variant instead (MFT: 64-row tiles decoded once into
+//       LDS, scores and p V as MFMAs; same partials).
 //   attn_merge_kernel    grid (q head, D/32), 256 threads: log-sum-exp merge
 //       of the chunk partials, the division by the total, the sigmoid gate.
+// A prompt into a quantised cache (head dimension 128 and 256): the rows
+// appended (pfq_prep_kernel), then one causal attention over the rows as
+// stored in the same tiles (pfq_flash_kernel).
 //
-// Layouts: K/V caches bf16 [capacity, Hkv, D] (token-major).
+// Layouts: K/V caches token-major [capacity, Hkv, D] (bf16), with the
+// quantised formats' data and group scales in the same row order.
 #include <type_traits>
 
 #include "q35decode.h"
