@@ -598,3 +598,27 @@ def test_prefill_full_quantised_tiles_other_groups(rt, gen, fmt, D, hq, hkv):
     say(f"  {fmt} D={D} G={hq // hkv}: worst token rel {r:.2e}")
     assert r < TOL_BF16
     _check_qcache(fmt, after, before, rkv, pos, T)
+
+
+@pytest.mark.parametrize("pos,T", [(0, 1), (0, 64), (63, 1), (63, 65)])
+def test_prefill_full_quantised_tiles_edges(rt, gen, pos, T):
+    """Edges of the batched path (Turbo8, D 256, G 4): one token into an empty
+    cache (one key row), exactly one tile of tokens, one token whose row is
+    the last of the first tile, and a prompt whose query blocks straddle the
+    tile boundary; against the oracle's decode loop."""
+    from dataclasses import replace
+    cfg = replace(synth.tiny("f32"), num_heads=16, num_kv_heads=4, head_dim=256, rotary_dim=64)
+    say(f"prefill full into turbo8 tiles (edges) pos={pos} T={T}")
+    layer = synth.full_layer(gen, cfg, f"pfqe.{pos}.{T}")
+    cap = pos + T + 3
+    kv = _qcache(gen, cfg, "turbo8", f"pfqe.{pos}.{T}", cap, pos)
+    x = gen.act(f"pfqe.{pos}.{T}.x", (T, cfg.hidden), "f32")
+    before = {k: np.array(v, copy=True) for k, v in kv.items() if isinstance(v, np.ndarray)}
+    out, after = _full_run(rt, cfg, layer, kv, x, pos, sparse_v=0.0)
+    inv = O.rope_inv_freq(cfg.rope_theta, cfg.rotary_dim)
+    ref, rkv, _ = O.prefill.prefill_full_attention(cfg, layer, kv, inv, x, pos, fmt="turbo8", sparse_v=0.0)
+    assert np.isfinite(out).all()
+    r = _rows_rel(out, ref)
+    say(f"  worst token rel {r:.2e}")
+    assert r < TOL_BF16
+    _check_qcache("turbo8", after, before, rkv, pos, T)
