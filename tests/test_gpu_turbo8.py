@@ -27,7 +27,7 @@ import oracle as O
 from oracle import turbo8 as T8
 import synth
 from synth import workloads
-from gpu_common import TOL_BF16, TOL_F32, check_gated_attention, rel, say
+from gpu_common import ELEM_BF16, ELEM_F32, TOL_BF16, TOL_F32, check_gated_attention, elem_err, rel, say
 
 pytestmark = pytest.mark.gpu
 
@@ -193,6 +193,7 @@ def test_full_layer_tiny_turbo8_taps_append_and_attention(rt, gen):
         same = _check_row(after, before, t, scr, cfg, nkv)
         tol = TOL_F32 if same else TOL_BF16
         assert rel(rt.act_to_f32(scr.t["x_out"], cfg), ox) < tol, (t, same)
+        assert elem_err(rt.act_to_f32(scr.t["x_out"], cfg), ox, 24) < (ELEM_F32 if same else ELEM_BF16), (t, same)
         for k, ok in FULL_TAPS_POST.items():
             assert rel(scr.t[k].cpu().numpy(), taps[ok]) < tol, (t, k, same)
         # attention from the stored cache and the kernel's own query heads
@@ -230,6 +231,7 @@ def test_full_layer_4b_turbo8_from_4096(rt, gen):
         r = rel(rt.act_to_f32(scr.t["x_out"], cfg), ox)
         worst = max(worst, r)
         assert r < TOL_BF16, (t, r)
+        assert elem_err(rt.act_to_f32(scr.t["x_out"], cfg), ox, 8) < ELEM_BF16, t
         if i == 0:
             qk = scr.t["q_norm_out"].cpu().numpy().astype(np.float64).reshape(cfg.num_heads,
                                                                                cfg.head_dim)

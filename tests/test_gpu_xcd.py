@@ -15,7 +15,7 @@ import torch
 import oracle as O
 import synth
 from synth import workloads
-from gpu_common import ELEM_BF16, TOL_BF16, TOL_F32, TOL_GEMV_F16, TOL_STACK, check, rel, say
+from gpu_common import ELEM_BF16, TOL_BF16, TOL_F32, TOL_GEMV_F16, TOL_STACK, check, elem_err, rel, say
 
 pytestmark = pytest.mark.gpu
 
@@ -99,6 +99,7 @@ def test_xcd_full_layer_4b_64_steps_from_4096(rt, gen):
         r = rel(rt.act_to_f32(plan.layer_input(1), cfg), ox)
         worst = max(worst, r)
         assert r < TOL_BF16, (t, r)
+        assert elem_err(rt.act_to_f32(plan.layer_input(1), cfg), ox, 8) < ELEM_BF16, t
     say(f"XCD 4B full attention: worst output rel {worst:.2e}")
     after = KVd.to_host()
     for side in ("k", "v"):
