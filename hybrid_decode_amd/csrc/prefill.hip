@@ -270,7 +270,10 @@ __global__ __launch_bounds__(2 * BM, 1) void gemm_kernel(PfGemmArgs a) {
     // tile kt + 2 is being fetched.  Loads past the last tile repeat it (in bounds,
     // never stashed), so every iteration issues the same loads, and the loop body
     // stashes at every step (a straight line the scheduler can interleave); the
-    // last one or two tiles run after it.
+    // last one or two tiles run after it.  A scheduling barrier after each load
+    // keeps the loads at the head of their half: left free, the compiler sank
+    // them behind three of the four k steps, so the stash of the next half
+    // waited for them (the prefill GEMMs ran about 3 % slower).
     const c0 lds0;
     const c1 lds1;
     load(g0, 0);
@@ -280,9 +283,11 @@ __global__ __launch_bounds__(2 * BM, 1) void gemm_kernel(PfGemmArgs a) {
     uint32_t kt = 0;
     for (; kt + 2 < nk; kt += 2) {
         load(g0, kt + 2);
+        __builtin_amdgcn_sched_barrier(0);
         compute(lds0, true);
         __syncthreads();
         load(g1, min(kt + 3, nk - 1));
+        __builtin_amdgcn_sched_barrier(0);
         compute(lds1, true);
         __syncthreads();
     }
